@@ -1,0 +1,365 @@
+// Host side of the C ABI declared in include/dominotree.h.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <string>
+
+#include "../../include/dominotree.h"
+#include "kernels.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+dt_status fail(dt_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return s;
+}
+
+#define HIPCHK(expr)                                                                     \
+  do {                                                                                   \
+    hipError_t e_ = (expr);                                                              \
+    if (e_ != hipSuccess) return fail(DT_EHIP, "%s: %s", #expr, hipGetErrorString(e_)); \
+  } while (0)
+
+inline int round_up(int x, int m) { return (x + m - 1) / m * m; }
+
+}  // namespace
+
+struct dt_handle {
+  dt_dims dims{};
+  dt_params maxp{};
+  int device = 0;
+  int n_cu = 0;
+  int bf16 = 0;
+  size_t esz = 4;
+  const void* emb = nullptr;
+  // handle-owned weights
+  float* G = nullptr;       // [V, 3 ds]
+  void* tiles = nullptr;    // packed [W_hh ; W1_S^T]
+  float* b_hh = nullptr;    // [3 ds] or null
+  void* w1h_t = nullptr;    // [r, h]
+  void* w2t = nullptr;      // [V, r]
+  void* wlm_t = nullptr;    // [V, h] or null
+  int n_tiles = 0;
+  // workspace
+  uint64_t* chunk_cand = nullptr;
+  float4* chunk_stat = nullptr;
+  int32_t* cand_ids = nullptr;
+  float* cand_vals = nullptr;
+  int32_t* tokrank = nullptr;
+  float* lse = nullptr;
+  float* tail = nullptr;
+  float* P = nullptr;
+  float* state = nullptr;
+  void* act = nullptr;
+  float* gh = nullptr;
+  float* u = nullptr;
+  int32_t* rec = nullptr;
+  uint32_t* mbox_w = nullptr;
+  uint32_t* mbox_c = nullptr;
+  int* err = nullptr;
+  int* nanflag = nullptr;
+  size_t act_bytes = 0;
+  int max_workers = 0;
+};
+
+namespace {
+
+template <typename T>
+dt_status dalloc(T** p, size_t bytes) {
+  *p = nullptr;
+  if (bytes == 0) bytes = 16;
+  hipError_t e = hipMalloc(reinterpret_cast<void**>(p), bytes);
+  if (e != hipSuccess) return fail(DT_ENOMEM, "hipMalloc(%zu): %s", bytes, hipGetErrorString(e));
+  return DT_OK;
+}
+
+void free_all(dt_handle* h) {
+  void* ptrs[] = {h->G,       h->tiles,    h->b_hh,     h->w1h_t, h->w2t,      h->wlm_t,
+                  h->chunk_cand, h->chunk_stat, h->cand_ids, h->cand_vals, h->tokrank, h->lse,
+                  h->tail,    h->P,        h->state,    h->act,   h->gh,       h->u,
+                  h->rec,     h->mbox_w,   h->mbox_c,   h->err,   h->nanflag};
+  for (void* p : ptrs)
+    if (p) (void)hipFree(p);
+}
+
+dt_status check_dims(const dt_dims* d) {
+  if (d->vocab <= 0 || d->depths <= 0 || d->hidden <= 0 || d->emb_dim <= 0 || d->state_dim <= 0 ||
+      d->rank <= 0 || d->max_batch <= 0)
+    return fail(DT_EINVAL, "dims must be positive");
+  if (d->wdtype != DT_F32 && d->wdtype != DT_BF16) return fail(DT_EINVAL, "unknown wdtype %d", (int)d->wdtype);
+  if (d->max_batch > DT_MAX_BATCH) return fail(DT_EUNSUPPORTED, "max_batch %d > %d", d->max_batch, DT_MAX_BATCH);
+  if (d->depths > DT_MAX_DEPTHS) return fail(DT_EUNSUPPORTED, "depths %d > %d", d->depths, DT_MAX_DEPTHS);
+  if (d->vocab > DT_TOPM_MAX_CHUNKS * TOPM_CHUNK)
+    return fail(DT_EUNSUPPORTED, "vocab %d > %d", d->vocab, DT_TOPM_MAX_CHUNKS * TOPM_CHUNK);
+  if (d->wdtype == DT_BF16 && (d->emb_dim % 8 || d->hidden % 8))
+    return fail(DT_EUNSUPPORTED, "bf16 weights need emb_dim and hidden multiples of 8");
+  if (d->rank > 4096 || d->state_dim > 8192) return fail(DT_EUNSUPPORTED, "rank or state_dim too large");
+  return DT_OK;
+}
+
+dt_status check_params(const dt_params* p, int V, const dt_params* maxp) {
+  if (p->top_m < 1 || p->top_m > V) return fail(DT_EINVAL, "top_m %d outside 1..V", p->top_m);
+  if (p->top_m > DT_MAX_TOPM) return fail(DT_EUNSUPPORTED, "top_m %d > %d", p->top_m, DT_MAX_TOPM);
+  if (p->top_k < 1 || p->top_k > p->top_m) return fail(DT_EINVAL, "top_k %d outside 1..top_m", p->top_k);
+  if (p->budget < 1) return fail(DT_EINVAL, "budget %d < 1", p->budget);
+  if (p->budget > DT_MAX_BUDGET) return fail(DT_EUNSUPPORTED, "budget %d > %d", p->budget, DT_MAX_BUDGET);
+  if ((long)p->budget * (p->top_k - 1) + 1 > DT_MAX_FRONTIER)
+    return fail(DT_EUNSUPPORTED, "budget * (top_k - 1) + 1 > %d", DT_MAX_FRONTIER);
+  if (!(p->temperature > 0.f) || !std::isfinite(p->temperature))
+    return fail(DT_EINVAL, "temperature must be finite and > 0");
+  if (p->norm != DT_NORM_TOPM && p->norm != DT_NORM_FULLV) return fail(DT_EINVAL, "unknown norm");
+  if (p->flags & ~(DT_ACT_BF16 | DT_VALIDATE)) return fail(DT_EINVAL, "unknown flags 0x%x", p->flags);
+  if (maxp && (p->top_m > maxp->top_m || p->top_k > maxp->top_k || p->budget > maxp->budget))
+    return fail(DT_EINVAL, "params exceed the handle's max_params");
+  return DT_OK;
+}
+
+// tiles per worker: as few workers as fit beside the controllers
+int choose_tpw(const dt_handle* h, int B) {
+  const char* env = getenv("DT_TILES_PER_WORKER");
+  if (env && atoi(env) > 0) return atoi(env);
+  const int avail = h->n_cu - B;
+  int tpw = 2;
+  while ((h->n_tiles + tpw - 1) / tpw > avail) ++tpw;
+  return tpw;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* dt_last_error(void) { return g_err.c_str(); }
+
+const char* dt_version(void) { return "dominotree-mi355x 0.1 (gfx950)"; }
+
+dt_status dt_create(dt_handle** out, const dt_dims* dims, const dt_weights* w, const dt_params* maxp,
+                    void* stream_) {
+  if (!out) return fail(DT_EINVAL, "h is NULL");
+  *out = nullptr;
+  if (!dims || !w || !maxp) return fail(DT_EINVAL, "dims, weights and max_params are required");
+  dt_status s = check_dims(dims);
+  if (s != DT_OK) return s;
+  s = check_params(maxp, dims->vocab, nullptr);
+  if (s != DT_OK) return s;
+  if (!w->emb || !w->w_ih || !w->w_hh || !w->w1 || !w->w2) return fail(DT_EINVAL, "a required weight is NULL");
+  hipStream_t stream = reinterpret_cast<hipStream_t>(stream_);
+
+  dt_handle* h = new dt_handle();
+  h->dims = *dims;
+  h->maxp = *maxp;
+  h->bf16 = dims->wdtype == DT_BF16;
+  h->esz = h->bf16 ? 2 : 4;
+  h->emb = w->emb;
+  auto bail = [&](dt_status st) {
+    (void)hipStreamSynchronize(stream);
+    free_all(h);
+    delete h;
+    return st;
+  };
+  if (hipGetDevice(&h->device) != hipSuccess) return bail(fail(DT_EHIP, "hipGetDevice failed"));
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, h->device) != hipSuccess) return bail(fail(DT_EHIP, "no device properties"));
+  h->n_cu = prop.multiProcessorCount;
+  if (!prop.cooperativeLaunch) return bail(fail(DT_EUNSUPPORTED, "device lacks cooperative launch"));
+
+  const int V = dims->vocab, D = dims->depths, hd = dims->hidden, e = dims->emb_dim, ds = dims->state_dim,
+            r = dims->rank, Bm = dims->max_batch;
+  const int M = maxp->top_m, N = maxp->budget;
+  const size_t esz = h->esz;
+  const int rows_p = round_up(3 * ds + r, 16), kp = round_up(ds, 32);
+  h->n_tiles = rows_p / 16;
+  if (h->n_tiles + 1 > h->n_cu * 64) return bail(fail(DT_EUNSUPPORTED, "state_dim too large"));
+
+#define ALLOC(p, bytes)                 \
+  do {                                  \
+    dt_status st_ = dalloc(&(p), bytes); \
+    if (st_ != DT_OK) return bail(st_); \
+  } while (0)
+#define HIPB(expr)                                                                               \
+  do {                                                                                           \
+    hipError_t e_ = (expr);                                                                      \
+    if (e_ != hipSuccess) return bail(fail(DT_EHIP, "%s: %s", #expr, hipGetErrorString(e_))); \
+  } while (0)
+
+  // G = E W_ih^T + b_ih: the GRU input term of every token
+  ALLOC(h->G, (size_t)V * 3 * ds * sizeof(float));
+  if (h->bf16)
+    HIPB(dt::launch_gemm_bf16((const uint16_t*)w->emb, nullptr, (const uint16_t*)w->w_ih, w->b_ih, h->G, V,
+                              3 * ds, e, 3 * ds, stream));
+  else
+    HIPB(dt::launch_gemm_f32((const float*)w->emb, nullptr, (const float*)w->w_ih, w->b_ih, h->G, V, 3 * ds, e,
+                             3 * ds, stream));
+  ALLOC(h->tiles, (size_t)rows_p * kp * esz);
+  HIPB(dt::launch_pack_node_tiles(w->w_hh, w->w1, hd, ds, r, (int)esz, h->tiles, stream));
+  if (w->b_hh) {
+    ALLOC(h->b_hh, (size_t)3 * ds * sizeof(float));
+    HIPB(hipMemcpyAsync(h->b_hh, w->b_hh, (size_t)3 * ds * sizeof(float), hipMemcpyDeviceToDevice, stream));
+  }
+  ALLOC(h->w1h_t, (size_t)r * hd * esz);
+  HIPB(dt::launch_transpose(w->w1, h->w1h_t, hd, r, (int)esz, stream));  // rows 0..h-1 of W1
+  ALLOC(h->w2t, (size_t)V * r * esz);
+  HIPB(dt::launch_transpose(w->w2, h->w2t, r, V, (int)esz, stream));
+  if (w->w_lm) {
+    if (!h->bf16) return bail(fail(DT_EUNSUPPORTED, "the LM head needs bf16 weights"));
+    ALLOC(h->wlm_t, (size_t)V * hd * esz);
+    HIPB(dt::launch_transpose(w->w_lm, h->wlm_t, hd, V, (int)esz, stream));
+  }
+
+  // workspace for max_batch and max_params
+  const int S = dt::topm_chunks(V);
+  const size_t rows = (size_t)Bm * D;
+  ALLOC(h->chunk_cand, rows * S * M * sizeof(uint64_t));
+  ALLOC(h->chunk_stat, rows * S * sizeof(float4));
+  ALLOC(h->cand_ids, rows * M * sizeof(int32_t));
+  ALLOC(h->cand_vals, rows * M * sizeof(float));
+  ALLOC(h->tokrank, rows * M * sizeof(int32_t));
+  ALLOC(h->lse, rows * sizeof(float));
+  ALLOC(h->tail, rows * sizeof(float));
+  ALLOC(h->P, rows * r * sizeof(float));
+  const size_t nodes = (size_t)Bm * (N + 1);
+  ALLOC(h->state, nodes * round_up(ds, 32) * sizeof(float));
+  h->act_bytes = nodes * round_up(ds, 64) * esz;
+  ALLOC(h->act, h->act_bytes);
+  HIPB(hipMemsetAsync(h->act, 0, h->act_bytes, stream));
+  ALLOC(h->gh, nodes * round_up(3 * ds, 32) * sizeof(float));
+  ALLOC(h->u, nodes * round_up(r, 32) * sizeof(float));
+  ALLOC(h->rec, (size_t)Bm * (N + 2) * sizeof(int32_t));
+  h->max_workers = h->n_cu;
+  ALLOC(h->mbox_w, (size_t)h->max_workers * 32 * sizeof(uint32_t));
+  ALLOC(h->mbox_c, (size_t)DT_MAX_BATCH * 256 * sizeof(uint32_t));
+  ALLOC(h->err, 64);
+  ALLOC(h->nanflag, 64);
+  HIPB(hipMemsetAsync(h->err, 0, 64, stream));
+  HIPB(hipStreamSynchronize(stream));
+#undef ALLOC
+#undef HIPB
+  *out = h;
+  return DT_OK;
+}
+
+dt_status dt_build_trees(dt_handle* h, const dt_inputs* in, const dt_params* p, dt_outputs* out, void* stream_) {
+  if (!h || !in || !p || !out) return fail(DT_EINVAL, "h, in, p and out are required");
+  hipStream_t stream = reinterpret_cast<hipStream_t>(stream_);
+  const dt_dims& d = h->dims;
+  dt_status s = check_params(p, d.vocab, &h->maxp);
+  if (s != DT_OK) return s;
+  if (in->batch < 1 || in->batch > d.max_batch)
+    return fail(DT_EINVAL, "batch %d outside 1..%d", in->batch, d.max_batch);
+  if (!in->hidden) return fail(DT_EINVAL, "inputs.hidden is required");
+  if (!out->tokens || !out->parents || !out->depths || !out->scores || !out->n_nodes)
+    return fail(DT_EINVAL, "tokens, parents, depths, scores and n_nodes outputs are required");
+  if (!in->base_logits && !h->wlm_t) return fail(DT_EINVAL, "no base logits and no LM head weights");
+  if (h->bf16 && !(p->flags & DT_ACT_BF16))
+    return fail(DT_EUNSUPPORTED, "bf16 weights need DT_ACT_BF16 (bf16 GEMM operands)");
+
+  const int B = in->batch, D = d.depths, V = d.vocab, M = p->top_m, N = p->budget;
+  const int rows = B * D;
+
+  if ((p->flags & DT_VALIDATE) && in->base_logits) {
+    HIPCHK(hipMemsetAsync(h->nanflag, 0, sizeof(int), stream));
+    HIPCHK(dt::launch_nan_scan(in->base_logits, (size_t)rows * V, h->nanflag, stream));
+    int flag = 0;
+    HIPCHK(hipMemcpyAsync(&flag, h->nanflag, sizeof(int), hipMemcpyDeviceToHost, stream));
+    HIPCHK(hipStreamSynchronize(stream));
+    if (flag) return fail(DT_EINVAL, "base logits contain NaN");
+  }
+
+  // a1: per-depth candidates and LSE
+  if (in->base_logits) {
+    HIPCHK(dt::launch_topm(in->base_logits, rows, V, M, p->temperature, h->chunk_cand, h->chunk_stat,
+                           h->cand_ids, h->cand_vals, h->lse, h->tail, h->tokrank, out->cand_ids,
+                           out->cand_logits, out->lse, stream));
+  } else {
+    HIPCHK(dt::launch_lmhead_topm((const uint16_t*)in->hidden, (const uint16_t*)h->wlm_t, rows, V, d.hidden, M,
+                                  p->temperature, h->chunk_cand, h->chunk_stat, stream));
+    HIPCHK(dt::launch_topm_merge(h->chunk_cand, h->chunk_stat, rows, dt::topm_chunks(V), M, p->temperature,
+                                 h->cand_ids, h->cand_vals, h->lse, h->tail, h->tokrank, out->cand_ids,
+                                 out->cand_logits, out->lse, stream));
+  }
+  // a2: P = H W1_H (the path-independent half of W1 [H_d; S])
+  if (h->bf16)
+    HIPCHK(dt::launch_gemm_bf16((const uint16_t*)in->hidden, nullptr, (const uint16_t*)h->w1h_t, nullptr, h->P,
+                                rows, d.rank, d.hidden, d.rank, stream));
+  else
+    HIPCHK(dt::launch_gemm_f32((const float*)in->hidden, nullptr, (const float*)h->w1h_t, nullptr, h->P, rows,
+                               d.rank, d.hidden, d.rank, stream));
+
+  // a3-a8: the persistent builder
+  dt::TreeArgs a{};
+  a.B = B;
+  a.D = D;
+  a.ds = d.state_dim;
+  a.r = d.rank;
+  a.M = M;
+  a.k = p->top_k;
+  a.N = N;
+  a.T = p->temperature;
+  a.fullv = p->norm == DT_NORM_FULLV;
+  a.act_bf16 = (p->flags & DT_ACT_BF16) != 0;
+  a.n_tiles = h->n_tiles;
+  a.tiles_per_worker = choose_tpw(h, B);
+  a.n_workers = (h->n_tiles + a.tiles_per_worker - 1) / a.tiles_per_worker;
+  if (a.n_workers + B > h->n_cu || a.n_workers > h->max_workers)
+    return fail(DT_EUNSUPPORTED, "%d workers + %d requests exceed %d compute units", a.n_workers, B, h->n_cu);
+  a.tiles = h->tiles;
+  a.b_hh = h->b_hh;
+  a.G = h->G;
+  a.w2t = h->w2t;
+  a.P = h->P;
+  a.cand_ids = h->cand_ids;
+  a.cand_vals = h->cand_vals;
+  a.tail = h->tail;
+  a.tokrank = h->tokrank;
+  a.root = in->root_state;
+  a.state = h->state;
+  a.act = h->act;
+  a.gh = h->gh;
+  a.u = h->u;
+  a.rec = h->rec;
+  a.mbox_w = h->mbox_w;
+  a.mbox_c = h->mbox_c;
+  a.err = h->err;
+  a.tokens = out->tokens;
+  a.parents = out->parents;
+  a.depths = out->depths;
+  a.scores = out->scores;
+  a.n_nodes = out->n_nodes;
+  a.spin_limit = 1u << 21;
+  const size_t lds = dt::tree_lds_bytes(a, h->bf16);
+  if (lds > 160 * 1024) return fail(DT_EUNSUPPORTED, "builder needs %zu bytes of LDS", lds);
+  HIPCHK(dt::launch_fill_u32(h->mbox_w, 0u, (size_t)a.n_workers * 32, stream));
+  HIPCHK(dt::launch_fill_u32(h->mbox_c, 0u, (size_t)B * 256, stream));
+  HIPCHK(dt::launch_tree(a, h->bf16, lds, stream));
+  return DT_OK;
+}
+
+dt_status dt_sync_status(dt_handle* h, void* stream_) {
+  if (!h) return fail(DT_EINVAL, "h is NULL");
+  hipStream_t stream = reinterpret_cast<hipStream_t>(stream_);
+  HIPCHK(hipStreamSynchronize(stream));
+  int e = 0;
+  HIPCHK(hipMemcpy(&e, h->err, sizeof(int), hipMemcpyDeviceToHost));
+  if (e) return fail(DT_EDEVICE, "a builder wait ran out (device error word %d)", e);
+  return DT_OK;
+}
+
+dt_status dt_destroy(dt_handle* h) {
+  if (!h) return DT_OK;
+  (void)hipDeviceSynchronize();
+  free_all(h);
+  delete h;
+  return DT_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,88 @@
+// Internal launch interface of the builder's kernels (not part of the C ABI).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+// limits shared with include/dominotree.h
+#define DT_TOPM_MAX 64
+#define DT_TOPM_MAX_CHUNKS 128   // vocab up to 128 * 8192 = 1048576
+#define TOPM_CHUNK 8192
+
+namespace dt {
+
+inline int topm_chunks(int V) { return (V + TOPM_CHUNK - 1) / TOPM_CHUNK; }
+
+// ---- per-depth candidates (topm.hip)
+hipError_t launch_topm(const float* logits, int rows, int V, int M, float T, uint64_t* chunk_cand,
+                       float4* chunk_stat, int32_t* ids, float* vals, float* lse, float* tail,
+                       int32_t* tokrank, int32_t* user_ids, float* user_vals, float* user_lse,
+                       hipStream_t stream);
+hipError_t launch_topm_merge(const uint64_t* chunk_cand, const float4* chunk_stat, int rows, int S,
+                             int M, float T, int32_t* ids, float* vals, float* lse, float* tail,
+                             int32_t* tokrank, int32_t* user_ids, float* user_vals, float* user_lse,
+                             hipStream_t stream);
+hipError_t launch_nan_scan(const float* x, size_t n, int* flag, hipStream_t stream);
+
+// ---- dense products (gemm.hip)
+// C[m, n] = sum_k A[rowsel(m), k] * Bt[n, k] (+ bias[n]); A row-major [*, K],
+// Bt row-major [N, K]; rowsel = identity when `rows` is NULL.  fp32 output
+// with leading dimension ldc.
+hipError_t launch_gemm_bf16(const uint16_t* A, const int32_t* rows, const uint16_t* Bt, const float* bias,
+                            float* C, int M, int N, int K, int ldc, hipStream_t stream);
+hipError_t launch_gemm_f32(const float* A, const int32_t* rows, const float* Bt, const float* bias,
+                           float* C, int M, int N, int K, int ldc, hipStream_t stream);
+// LM head with the candidate epilogue: logits = H Wt^T never stored; writes the
+// per-(row, 8192-token chunk) candidate lists and LSE statistics that
+// launch_topm_merge consumes.
+hipError_t launch_lmhead_topm(const uint16_t* H, const uint16_t* Wt, int R, int V, int K, int M, float T,
+                              uint64_t* chunk_cand, float4* chunk_stat, hipStream_t stream);
+
+// ---- weight re-layout (prepack.hip)
+// out[c, r] = in[r, c] for a [R, C] matrix of 2- or 4-byte elements
+hipError_t launch_transpose(const void* in, void* out, int R, int C, int elem_bytes, hipStream_t stream);
+// Tiles of the per-node product [W_hh ; W1_S^T] ([3 ds + r] rows x ds) in the
+// builder's LDS order: tile t = rows 16t..16t+15; within a tile, for each
+// 32-wide k block, [k group 0..3][row 0..15] x 8 elements.
+hipError_t launch_pack_node_tiles(const void* w_hh, const void* w1, int h, int ds, int r, int elem_bytes,
+                                  void* out, hipStream_t stream);
+hipError_t launch_fill_u32(uint32_t* p, uint32_t v, size_t n, hipStream_t stream);
+
+// ---- the tree builder (tree.hip)
+struct TreeArgs {
+  // shapes and parameters
+  int B, D, ds, r, M, k, N;
+  float T;
+  int fullv;
+  int act_bf16;
+  int n_workers;        // worker blocks; block ids [0, n_workers) are workers
+  int tiles_per_worker;
+  int n_tiles;          // (3 ds + r) / 16
+  // read-only inputs
+  const void* tiles;       // packed [W_hh ; W1_S^T] tiles
+  const float* b_hh;       // [3 ds] or NULL
+  const float* G;          // [V, 3 ds]: W_ih E[v] + b_ih
+  const void* w2t;         // [V, r] (wdtype)
+  const float* P;          // [B, D, r]: H_d W1_H
+  const int32_t* cand_ids; // [B, D, M]
+  const float* cand_vals;  // [B, D, M]
+  const float* tail;       // [B, D]
+  const int32_t* tokrank;  // [B, D, M]
+  const float* root;       // [B, ds] or NULL
+  // write-once exchange buffers
+  float* state;            // [B, N + 1, ds]
+  void* act;               // [B, N + 1, ds] GEMM operand copy of the state (wdtype)
+  float* gh;               // [B, N + 1, 3 ds]
+  float* u;                // [B, N + 1, r]
+  int32_t* rec;            // [B, N + 2] node expanded at each step (-1: request finished)
+  uint32_t* mbox_w;        // [n_workers][32] controller -> worker mailboxes (one line each)
+  uint32_t* mbox_c;        // [B][256] worker -> controller mailboxes
+  int* err;                // device error word
+  // outputs
+  int32_t *tokens, *parents, *depths, *n_nodes;
+  float* scores;
+  unsigned spin_limit;
+};
+hipError_t launch_tree(const TreeArgs& a, int wdtype_bf16, size_t lds_bytes, hipStream_t stream);
+size_t tree_lds_bytes(const TreeArgs& a, int wdtype_bf16);
+
+}  // namespace dt

@@ -1,0 +1,278 @@
+// Per-depth candidate selection: the M largest base logits of each
+// (request, depth) row, ties to the lowest token id, plus the log-sum-exp of
+// base/T over the whole vocabulary and over the tokens left out ("tail").
+//
+// DominoTree technical summary, Componenti Core 2: the correction is applied
+// only to each depth's top-M marginal candidates.  The selection is pure
+// comparison on the fp32 inputs, so it is exact; only the two LSE values are
+// rounded.
+//
+// Two kernels.  topm_chunk: one 256-thread block per (row, chunk of 8192
+// tokens) reads its chunk once from HBM into LDS as order-preserving keys,
+// finds the chunk's M-th largest key with a 3-pass radix select (12, 12, 8
+// bits), collects the chunk's top-M (ties at the threshold in id order) and
+// the chunk's LSE statistics.  topm_merge: one block per row ranks the chunk
+// lists against each other and keeps the M best; the LSE statistics combine
+// exactly (a token left out of its chunk's list is left out of the row's).
+// The merge also serves the LM-head path, whose GEMM epilogue writes the same
+// chunk lists.
+#include "common.h"
+#include "kernels.h"
+
+namespace dt {
+
+constexpr int TOPM_THREADS = 256;
+constexpr int HBINS = 4096;
+
+__global__ __launch_bounds__(TOPM_THREADS) void topm_chunk_kernel(
+    const float* __restrict__ logits, int V, int S, int M, float T,
+    uint64_t* __restrict__ out_cand, float4* __restrict__ out_stat) {
+  __shared__ uint32_t keys[TOPM_CHUNK];
+  __shared__ uint32_t hist[HBINS];
+  __shared__ uint64_t sel[DT_TOPM_MAX];
+  __shared__ float red[4];
+  __shared__ int ired[4];
+  __shared__ int found_digit, found_above, sel_count, tie_last_s;
+
+  const int tid = threadIdx.x;
+  const int c = blockIdx.x;
+  const int row = blockIdx.y;
+  const int c0 = c * TOPM_CHUNK;
+  const int len = min(TOPM_CHUNK, V - c0);
+  const int Mc = min(M, len);
+  const float* src = logits + (size_t)row * (size_t)V + c0;
+
+  // 1. read the chunk once: keys into LDS, running max of the values
+  float vmax = -INFINITY;
+  if ((V & 3) == 0) {
+    const float4* s4 = reinterpret_cast<const float4*>(src);
+    const int n4 = len >> 2;
+    for (int i = tid; i < n4; i += TOPM_THREADS) {
+      float4 x = s4[i];
+      keys[4 * i + 0] = f32_key(x.x);
+      keys[4 * i + 1] = f32_key(x.y);
+      keys[4 * i + 2] = f32_key(x.z);
+      keys[4 * i + 3] = f32_key(x.w);
+      vmax = fmaxf(vmax, fmaxf(fmaxf(x.x, x.y), fmaxf(x.z, x.w)));
+    }
+  } else {
+    for (int i = tid; i < len; i += TOPM_THREADS) {
+      float x = src[i];
+      keys[i] = f32_key(x);
+      vmax = fmaxf(vmax, x);
+    }
+  }
+  const float m = block_max<TOPM_THREADS>(vmax, red) / T;
+
+  // 2. radix select of the Mc-th largest key
+  uint32_t prefix = 0, pmask = 0;
+  int need = Mc;
+#pragma unroll
+  for (int pass = 0; pass < 3; ++pass) {
+    const int sh = pass == 0 ? 20 : (pass == 1 ? 8 : 0);
+    const int width = pass == 2 ? 8 : 12;
+    const uint32_t dmask = (1u << width) - 1u;
+    const int nb = 1 << width;
+    for (int i = tid; i < nb; i += TOPM_THREADS) hist[i] = 0;
+    __syncthreads();
+    for (int i = tid; i < len; i += TOPM_THREADS) {
+      uint32_t k = keys[i];
+      if ((k & pmask) == prefix) atomicAdd(&hist[(k >> sh) & dmask], 1u);
+    }
+    __syncthreads();
+    // thread t owns bins [t*per, t*per + per); bins are scanned from the top
+    const int per = nb / TOPM_THREADS;
+    int mine = 0;
+    for (int b = 0; b < per; ++b) mine += (int)hist[tid * per + b];
+    int above = block_suffix_excl<TOPM_THREADS>(mine, ired);
+    for (int b = per - 1; b >= 0; --b) {
+      const int h = (int)hist[tid * per + b];
+      if (above < need && above + h >= need) {
+        found_digit = tid * per + b;
+        found_above = above;
+      }
+      above += h;
+    }
+    __syncthreads();
+    need -= found_above;
+    prefix |= (uint32_t)found_digit << sh;
+    pmask |= dmask << sh;
+    __syncthreads();
+  }
+  const uint32_t kstar = prefix;  // the Mc-th largest key; `need` of its ties are taken
+
+  // 3. every key above the threshold (order is fixed by the sort below)
+  if (tid == 0) {
+    sel_count = 0;
+    tie_last_s = -1;
+  }
+  __syncthreads();
+  for (int i = tid; i < len; i += TOPM_THREADS) {
+    const uint32_t k = keys[i];
+    if (k > kstar) sel[atomicAdd(&sel_count, 1)] = cand_pack(k, (uint32_t)(c0 + i));
+  }
+  __syncthreads();
+  // ties at the threshold: the `need` lowest ids, scanned in id order
+  int slot = Mc - need;
+  for (int b0 = 0; b0 < len && need > 0; b0 += TOPM_THREADS) {
+    const int i = b0 + tid;
+    const bool f = i < len && keys[i] == kstar;
+    int total;
+    const int r = block_rank_flag<TOPM_THREADS>(f, ired, &total);
+    if (f && r < need) {
+      sel[slot + r] = cand_pack(kstar, (uint32_t)(c0 + i));
+      if (r == need - 1) tie_last_s = i;
+    }
+    const int took = min(total, need);
+    slot += took;
+    need -= took;
+    __syncthreads();
+  }
+  const int tie_last = tie_last_s;
+
+  // 4. sort the chunk's list (value desc, id asc) in wave 0; pad with zeros
+  if (tid < 64) {
+    uint64_t v = tid < Mc ? sel[tid] : 0ull;
+    v = wave_sort_desc_u64(v);
+    if (tid < M) out_cand[((size_t)row * S + c) * M + tid] = v;
+  }
+
+  // 5. LSE statistics over the chunk and over its left-out tokens
+  float s_all = 0.f, s_tail = 0.f;
+  if (m > -INFINITY) {
+    for (int i = tid; i < len; i += TOPM_THREADS) {
+      const uint32_t k = keys[i];
+      const float e = __expf(key_f32(k) / T - m);
+      s_all += e;
+      const bool in = k > kstar || (k == kstar && i <= tie_last);
+      if (!in) s_tail += e;
+    }
+  }
+  s_all = block_sum<TOPM_THREADS>(s_all, red);
+  s_tail = block_sum<TOPM_THREADS>(s_tail, red);
+  if (tid == 0) out_stat[(size_t)row * S + c] = make_float4(m, s_all, s_tail, __int_as_float(Mc));
+}
+
+// Number of entries of a descending list greater than `key`.
+__device__ __forceinline__ int count_greater(const uint64_t* list, int n, uint64_t key) {
+  int lo = 0, hi = n;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (list[mid] > key) lo = mid + 1;
+    else hi = mid;
+  }
+  return lo;
+}
+
+__global__ __launch_bounds__(TOPM_THREADS) void topm_merge_kernel(
+    const uint64_t* __restrict__ cand, const float4* __restrict__ stat, int S, int M, float T,
+    int32_t* __restrict__ ids_out, float* __restrict__ vals_out, float* __restrict__ lse_out,
+    float* __restrict__ tail_out, int32_t* __restrict__ tokrank_out, int32_t* __restrict__ user_ids,
+    float* __restrict__ user_vals, float* __restrict__ user_lse) {
+  extern __shared__ uint64_t lists[];  // [S][M]
+  __shared__ int cnt[DT_TOPM_MAX_CHUNKS];
+  __shared__ float mc[DT_TOPM_MAX_CHUNKS], sc[DT_TOPM_MAX_CHUNKS], tc[DT_TOPM_MAX_CHUNKS];
+  __shared__ int out_ids[DT_TOPM_MAX];
+  __shared__ float red[4];
+
+  const int tid = threadIdx.x;
+  const int row = blockIdx.x;
+  const uint64_t* src = cand + (size_t)row * S * M;
+  for (int i = tid; i < S * M; i += TOPM_THREADS) lists[i] = src[i];
+  for (int i = tid; i < S; i += TOPM_THREADS) {
+    const float4 st = stat[(size_t)row * S + i];
+    mc[i] = st.x;
+    sc[i] = st.y;
+    tc[i] = st.z;
+    cnt[i] = __float_as_int(st.w);
+  }
+  __syncthreads();
+  float mloc = -INFINITY;
+  for (int i = tid; i < S; i += TOPM_THREADS) mloc = fmaxf(mloc, mc[i]);
+  const float mstar = block_max<TOPM_THREADS>(mloc, red);
+
+  float extra = 0.f;
+  for (int e = tid; e < S * M; e += TOPM_THREADS) {
+    const int c = e / M, i = e - c * M;
+    if (i >= cnt[c]) continue;
+    const uint64_t key = lists[e];
+    int rank = i;
+    for (int c2 = 0; c2 < S; ++c2)
+      if (c2 != c) rank += count_greater(lists + c2 * M, cnt[c2], key);
+    const float v = key_f32(cand_key(key));
+    if (rank < M) {
+      const int id = (int)cand_id(key);
+      out_ids[rank] = id;
+      ids_out[(size_t)row * M + rank] = id;
+      vals_out[(size_t)row * M + rank] = v;
+      if (user_ids) user_ids[(size_t)row * M + rank] = id;
+      if (user_vals) user_vals[(size_t)row * M + rank] = v;
+    } else if (mstar > -INFINITY) {
+      extra += __expf(v / T - mstar);
+    }
+  }
+  float s_all = 0.f, s_tail = 0.f;
+  if (mstar > -INFINITY) {
+    for (int i = tid; i < S; i += TOPM_THREADS) {
+      if (mc[i] > -INFINITY) {
+        const float f = __expf(mc[i] - mstar);
+        s_all += sc[i] * f;
+        s_tail += tc[i] * f;
+      }
+    }
+  }
+  s_all = block_sum<TOPM_THREADS>(s_all, red);
+  s_tail = block_sum<TOPM_THREADS>(s_tail + extra, red);
+  if (tid == 0) {
+    const float lse = (mstar > -INFINITY && s_all > 0.f) ? mstar + __logf(s_all) : -INFINITY;
+    const float tail = (mstar > -INFINITY && s_tail > 0.f) ? mstar + __logf(s_tail) : -INFINITY;
+    lse_out[row] = lse;
+    tail_out[row] = tail;
+    if (user_lse) user_lse[row] = lse;
+  }
+  __syncthreads();
+  // rank of each candidate's token id among the row's candidates (heap tie order)
+  for (int i = tid; i < M; i += TOPM_THREADS) {
+    int r = 0;
+    for (int j = 0; j < M; ++j) r += out_ids[j] < out_ids[i];
+    tokrank_out[(size_t)row * M + i] = r;
+  }
+}
+
+// NaN scan for DT_VALIDATE: sets *flag when any value is NaN.
+__global__ void nan_scan_kernel(const float* __restrict__ x, size_t n, int* __restrict__ flag) {
+  bool bad = false;
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
+    bad |= x[i] != x[i];
+  if (__any(bad) && (threadIdx.x & 63) == 0) atomicOr(flag, 1);
+}
+
+hipError_t launch_topm(const float* logits, int rows, int V, int M, float T, uint64_t* chunk_cand,
+                       float4* chunk_stat, int32_t* ids, float* vals, float* lse, float* tail,
+                       int32_t* tokrank, int32_t* user_ids, float* user_vals, float* user_lse,
+                       hipStream_t stream) {
+  const int S = topm_chunks(V);
+  hipLaunchKernelGGL(topm_chunk_kernel, dim3(S, rows), dim3(TOPM_THREADS), 0, stream, logits, V, S, M,
+                     T, chunk_cand, chunk_stat);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_topm_merge(chunk_cand, chunk_stat, rows, S, M, T, ids, vals, lse, tail, tokrank,
+                           user_ids, user_vals, user_lse, stream);
+}
+
+hipError_t launch_topm_merge(const uint64_t* chunk_cand, const float4* chunk_stat, int rows, int S,
+                             int M, float T, int32_t* ids, float* vals, float* lse, float* tail,
+                             int32_t* tokrank, int32_t* user_ids, float* user_vals, float* user_lse,
+                             hipStream_t stream) {
+  const size_t lds = (size_t)S * M * sizeof(uint64_t);
+  hipLaunchKernelGGL(topm_merge_kernel, dim3(rows), dim3(TOPM_THREADS), lds, stream, chunk_cand,
+                     chunk_stat, S, M, T, ids, vals, lse, tail, tokrank, user_ids, user_vals, user_lse);
+  return hipGetLastError();
+}
+
+hipError_t launch_nan_scan(const float* x, size_t n, int* flag, hipStream_t stream) {
+  hipLaunchKernelGGL(nan_scan_kernel, dim3(1024), dim3(256), 0, stream, x, n, flag);
+  return hipGetLastError();
+}
+
+}  // namespace dt

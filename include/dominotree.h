@@ -1,0 +1,192 @@
+/*
+ * dominotree.h -- C ABI of the MI355X (gfx950) conditional draft-tree builder.
+ *
+ * The library builds, for each request of a batch, the best-first draft tree
+ * of DominoTree: per-depth top-M candidates of the drafter's base logits, then
+ * a best-first loop that pops the frontier node with the highest cumulative
+ * path log-probability, advances Domino's GRU causal state along that node's
+ * path, applies the low-rank logit correction on the M candidate columns of the
+ * next depth only, log-softmaxes the corrected logits and pushes the k best
+ * children, until a fixed number of nodes has been popped.
+ *
+ * Sources (page title, then section):
+ *   [Domino, Method]  "Domino: decoupling causal modeling from autoregressive
+ *                     drafting in speculative decoding" (Chinese summary),
+ *                     section 核心方法 -- S = GRU(embeddings of the earlier
+ *                     draft tokens); dL = W2 SiLU(W1 [H_i; S]) with rank r;
+ *                     final logits = base + dL.
+ *   [Domino, Steps]   same page, 方法步骤详情 -- base logits are the frozen LM
+ *                     head applied to the parallel backbone's hidden states.
+ *   [DominoTree, 1]   "Riassunto Tecnico: DominoTree", Componenti Core 1 --
+ *                     best-first max-heap on cumulative path log-probability;
+ *                     children are scored by re-running the GRU correction on
+ *                     the node's own path; H_d is shared by every path.
+ *   [DominoTree, 2]   same page, Componenti Core 2 -- the correction is
+ *                     restricted to each depth's top-M marginal candidates
+ *                     (the r x M slice of W2) before the top-k children are
+ *                     chosen.
+ *   [DominoTree, 4]   same page, Componenti Core 4 -- fixed node budget.
+ *
+ * Conventions the pages leave open, fixed here (and in the CPU oracle):
+ *   - GRU gate rows are (reset, update, new) as in torch.nn.GRUCell; the reset
+ *     gate multiplies (W_hn S + b_hn); S' = (1 - z) n + z S.
+ *   - A child at depth d uses H_d and its parent's state; the root's children
+ *     use root_state and no GRU step is taken at the root.
+ *   - Scores: z_m = (base_m + dL_m) / T; log-prob = z_m - LSE(z_1..z_M)
+ *     (DT_NORM_TOPM) or z_m - LSE(z_1..z_M, tail) where tail is the LSE of
+ *     base/T over the tokens outside the candidates (DT_NORM_FULLV).
+ *   - Orders: candidates by (base logit desc, token id asc), +0 == -0, NaN
+ *     last; children by (z desc, token id asc), -inf log-probs never pushed;
+ *     pops by (score desc, depth asc, token id asc, parent index asc).
+ *   - The budget N counts non-root nodes; a node joins the tree when popped;
+ *     the N-th popped node and nodes at depth D are not expanded; a build ends
+ *     after N pops or when the frontier is empty.
+ *   - bf16 weights: every product accumulates in fp32; the GRU state is kept
+ *     in fp32 and rounded to bf16 (nearest-even) only as a matrix operand when
+ *     DT_ACT_BF16 is set; gates, SiLU, softmax and scores are fp32.
+ *
+ * Memory: every pointer in dt_weights, dt_inputs and dt_outputs is a DEVICE
+ * pointer on the handle's device; every struct is passed by HOST pointer.
+ * Tensors are dense row-major.  Streams are hipStream_t passed as void*
+ * (NULL = the null stream).
+ *
+ * Errors: every entry point returns a dt_status; dt_last_error() gives the
+ * calling thread's message for the last non-OK status.  Arguments are checked
+ * on the host before anything is enqueued; device-side failures (a bounded
+ * wait that ran out) are reported by the next dt_build_trees call on the
+ * handle or by dt_sync_status().
+ */
+#ifndef DOMINOTREE_H
+#define DOMINOTREE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  DT_OK = 0,
+  DT_EINVAL = -1,       /* a bad argument: NULL pointer, size out of range */
+  DT_EUNSUPPORTED = -2, /* valid but beyond this build's limits */
+  DT_ENOMEM = -3,       /* device allocation failed in dt_create */
+  DT_EHIP = -4,         /* a HIP runtime call failed (message has the text) */
+  DT_EDEVICE = -5       /* a kernel's bounded wait ran out (device fault) */
+} dt_status;
+
+typedef enum { DT_F32 = 0, DT_BF16 = 1 } dt_dtype;
+typedef enum { DT_NORM_TOPM = 0, DT_NORM_FULLV = 1 } dt_norm;
+
+/* dt_params.flags */
+#define DT_ACT_BF16 1u  /* round the GRU state to bf16 where it is a GEMM operand */
+#define DT_VALIDATE 2u  /* scan the base logits for NaN first (DT_EINVAL if any) */
+
+/* Limits of this build (DT_EUNSUPPORTED beyond them). */
+#define DT_MAX_BATCH 32
+#define DT_MAX_DEPTHS 31
+#define DT_MAX_TOPM 64
+#define DT_MAX_BUDGET 1024
+#define DT_MAX_FRONTIER 4096 /* budget * (top_k - 1) + 1 */
+
+typedef struct {
+  int32_t vocab;     /* V */
+  int32_t depths;    /* D = draft block size - 1 */
+  int32_t hidden;    /* h: rows of H_d, rows of the H half of W1 */
+  int32_t emb_dim;   /* e: embedding size (GRU input) */
+  int32_t state_dim; /* d_s: GRU state size */
+  int32_t rank;      /* r: correction rank */
+  int32_t max_batch; /* largest batch a build will be given */
+  dt_dtype wdtype;   /* dtype of emb, w_ih, w_hh, w1, w2, w_lm and hidden */
+} dt_dims;
+
+/* Weights, all device pointers of dtype dims.wdtype unless noted.
+ * emb is referenced, not copied: it must stay valid while the handle lives.
+ * The others are copied (re-laid out) by dt_create and may be freed after. */
+typedef struct {
+  const void* emb;   /* [V, e] token embeddings (GRU input E[token]) */
+  const void* w_ih;  /* [3 d_s, e] GRU input weights, row blocks (r, z, n) */
+  const void* w_hh;  /* [3 d_s, d_s] GRU state weights, row blocks (r, z, n) */
+  const float* b_ih; /* [3 d_s] fp32 or NULL (zeros) */
+  const float* b_hh; /* [3 d_s] fp32 or NULL (zeros) */
+  const void* w1;    /* [h + d_s, r]: u = [H_d; S] @ w1 (rows 0..h-1 act on H_d) */
+  const void* w2;    /* [r, V]: dL = a @ w2 */
+  const void* w_lm;  /* [h, V] LM head, or NULL (then base logits must be given) */
+} dt_weights;
+
+typedef struct {
+  int32_t top_m;     /* M, 1..min(V, DT_MAX_TOPM) */
+  int32_t top_k;     /* k, 1..M */
+  int32_t budget;    /* N, 1..DT_MAX_BUDGET, with N (k - 1) + 1 <= DT_MAX_FRONTIER */
+  float temperature; /* T > 0 */
+  dt_norm norm;
+  uint32_t flags;    /* DT_ACT_BF16 | DT_VALIDATE */
+} dt_params;
+
+typedef struct {
+  int32_t batch;            /* b, 1..dims.max_batch (<= DT_MAX_BATCH) */
+  const float* base_logits; /* [b, D, V] fp32, or NULL: computed as H @ w_lm */
+  const void* hidden;       /* [b, D, h] backbone hidden states H_1..H_D (wdtype) */
+  const float* root_state;  /* [b, d_s] fp32, or NULL (zeros) */
+} dt_inputs;
+
+/* Outputs (device pointers, caller-owned, sized for the batch and budget).
+ * Node 0 is the root: token -1, parent -1, depth 0, score 0.  Nodes 1..n are
+ * in pop order; slots past n_nodes hold token -1, parent -1, depth -1,
+ * score -inf.  The three cand_* / lse pointers are optional (NULL to skip):
+ * the per-depth candidates (sorted), their base logits and the LSE of base/T
+ * over the whole vocabulary. */
+typedef struct {
+  int32_t* tokens;   /* [b, N + 1] */
+  int32_t* parents;  /* [b, N + 1] */
+  int32_t* depths;   /* [b, N + 1] */
+  float* scores;     /* [b, N + 1] cumulative log-prob (natural log) */
+  int32_t* n_nodes;  /* [b] non-root nodes produced (N unless the frontier emptied) */
+  int32_t* cand_ids; /* [b, D, M] or NULL */
+  float* cand_logits;/* [b, D, M] or NULL */
+  float* lse;        /* [b, D] or NULL */
+} dt_outputs;
+
+typedef struct dt_handle dt_handle;
+
+/* Create a handle on the current HIP device: copy and re-lay-out the weights
+ * into handle-owned device memory (w2 -> [V, r]; w_lm -> [V, h]; GRU and W1
+ * in the builder's tile order) and allocate the workspace for dims.max_batch
+ * and for every params no larger than *max_params (top_m, top_k, budget).
+ * Enqueued on `stream` and synchronised before returning.
+ * Errors: DT_EINVAL (NULL h/dims/weights/max_params, non-positive sizes,
+ * missing required weight), DT_EUNSUPPORTED (limits, dims not multiples of
+ * the tile sizes: for bf16, e, d_s and h multiples of 32 and r of 16; d_s a
+ * multiple of 4), DT_ENOMEM, DT_EHIP.  On error *h is NULL. */
+dt_status dt_create(dt_handle** h, const dt_dims* dims, const dt_weights* w,
+                    const dt_params* max_params, void* stream);
+
+/* Build the trees of one batch [DominoTree, 1, 2, 4].  Enqueues the kernels on
+ * `stream` and returns: no host synchronisation and no allocation.  Results
+ * are valid once the stream reaches this point.  A handle must not be used by
+ * two builds at once (one workspace).  When in->base_logits is NULL the
+ * base logits are computed from in->hidden with w_lm [Domino, Steps] and are
+ * never written to memory (only their candidates and LSE are).
+ * Errors: DT_EINVAL (NULL pointers, batch out of range, params out of range
+ * or above the handle's max_params, NaN logits under DT_VALIDATE, w_lm
+ * missing with NULL base logits), DT_EUNSUPPORTED, DT_EHIP, DT_EDEVICE (a
+ * previous build's device wait ran out). */
+dt_status dt_build_trees(dt_handle* h, const dt_inputs* in, const dt_params* p,
+                         dt_outputs* out, void* stream);
+
+/* Synchronise `stream` and report a device-side failure of the handle's
+ * builds so far (DT_EDEVICE) or DT_OK. */
+dt_status dt_sync_status(dt_handle* h, void* stream);
+
+/* Free everything the handle owns (synchronises the device first). NULL is a no-op. */
+dt_status dt_destroy(dt_handle* h);
+
+/* Message of the calling thread's last non-OK status ("" if none). */
+const char* dt_last_error(void);
+
+/* Library version string. */
+const char* dt_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DOMINOTREE_H */

@@ -1,0 +1,125 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle."""
+import numpy as np
+import pytest
+
+from tests import gpu_util as gu
+from workloads import synth
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dev():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no HIP device")
+    import conditional_draft_tree_dominotree_amd as pkg
+    pkg.load_library()
+    return torch.device("cuda:0")
+
+
+def _assert_ok(reps):
+    for i, r in enumerate(reps):
+        assert r.ok, (i, r)
+
+
+def test_tiny_workload(dev):
+    spec, w, req = synth.workload("tiny")
+    tb = gu.make_builder(spec, w)
+    got = gu.run(tb, spec, req)
+    reps, trees = gu.compare(spec, w, req, got)
+    print(gu.summarize(reps))
+    _assert_ok(reps)
+    assert reps[0].exact
+    gu.check_candidates(spec, trees, got, [0])
+    tb.close()
+
+
+SMALL = [
+    # name, kwargs
+    ("base", dict(V=1000, D=5, h=32, e=24, ds=64, r=32, M=8, k=3, N=30)),
+    ("ragged_two_chunks", dict(V=8195, D=4, h=16, e=16, ds=32, r=16, M=12, k=4, N=25)),
+    ("batch3_fullv_T05", dict(V=3000, D=6, h=32, e=32, ds=64, r=48, M=16, k=4, N=40, B=3,
+                              norm="fullv", T=0.5)),
+    ("biases_root", dict(V=500, D=4, h=8, e=8, ds=12, r=8, M=6, k=2, N=20, biases=True,
+                         root_std=0.7)),
+    ("chain_k1", dict(V=700, D=6, h=16, e=16, ds=32, r=16, M=8, k=1, N=40)),
+    ("n1", dict(V=700, D=6, h=16, e=16, ds=32, r=16, M=8, k=4, N=1)),
+    ("m1", dict(V=300, D=5, h=16, e=16, ds=32, r=16, M=1, k=1, N=9)),
+    ("m_eq_v", dict(V=6, D=3, h=8, e=8, ds=4, r=4, M=6, k=6, N=100)),
+    ("m64_k8_b8", dict(V=20000, D=7, h=64, e=64, ds=128, r=64, M=64, k=8, N=120, B=8)),
+    ("deep_d31", dict(V=400, D=31, h=16, e=16, ds=32, r=16, M=4, k=2, N=80)),
+]
+
+
+@pytest.mark.parametrize("name,kw", SMALL, ids=[s[0] for s in SMALL])
+def test_small_fp32(dev, name, kw):
+    spec = synth.small(name, group=300 + len(name), **kw)
+    spec, w, req = synth.workload(spec)
+    tb = gu.make_builder(spec, w)
+    got = gu.run(tb, spec, req)
+    reps, trees = gu.compare(spec, w, req, got)
+    print(name, gu.summarize(reps))
+    _assert_ok(reps)
+    gu.check_candidates(spec, trees, got, range(spec.B))
+    tb.close()
+
+
+@pytest.mark.parametrize("B,M,k,N", [(1, 16, 4, 40), (5, 32, 8, 64), (32, 16, 4, 50)])
+def test_small_bf16(dev, B, M, k, N):
+    spec = synth.small(f"bf16_{B}_{M}", V=5000, D=8, h=64, e=96, ds=128, r=64, M=M, k=k, N=N,
+                       B=B, wdtype="bf16", group=400 + B, emb_std=0.5)
+    spec, w, req = synth.workload(spec)
+    tb = gu.make_builder(spec, w)
+    got = gu.run(tb, spec, req)
+    reps, trees = gu.compare(spec, w, req, got)
+    print(gu.summarize(reps))
+    _assert_ok(reps)
+    gu.check_candidates(spec, trees, got, range(spec.B))
+    tb.close()
+
+
+def test_candidates_with_ties_zero_and_inf(dev):
+    spec = synth.small("ties", V=20000, D=4, h=16, e=16, ds=32, r=16, M=40, k=4, N=20,
+                       group=500)
+    spec, w, req = synth.workload(spec)
+    base = req["base"].copy()
+    rng = np.random.default_rng(0)
+    base[0, 0, rng.choice(20000, 300, replace=False)] = 2.5         # many ties at the top
+    base[0, 1, :] = np.float32(-0.0)
+    base[0, 1, rng.choice(20000, 50, replace=False)] = np.float32(0.0)  # +0 and -0 tie
+    base[0, 2, :] = -np.inf
+    base[0, 2, [5, 19999, 8191, 8192]] = [1.0, 1.0, 0.5, 0.5]        # -inf fill, ties across chunks
+    base[0, 3, :] = 3.0                                              # all equal
+    tb = gu.make_builder(spec, w)
+    got = gu.run(tb, spec, req, base=base)
+    reps, trees = gu.compare(spec, w, req, got, base=base)
+    for d, dep in enumerate(trees[0].depths_info):
+        np.testing.assert_array_equal(got["cand_ids"][0, d], dep.cand, err_msg=f"depth {d}")
+    _assert_ok(reps)
+    tb.close()
+
+
+def test_validate_rejects_nan(dev):
+    import conditional_draft_tree_dominotree_amd as pkg
+    spec = synth.small("nan", V=600, D=3, h=8, e=8, ds=8, r=8, M=4, k=2, N=6, group=501)
+    spec, w, req = synth.workload(spec)
+    base = req["base"].copy()
+    base[0, 1, 17] = np.nan
+    tb = gu.make_builder(spec, w)
+    with pytest.raises(pkg.DtError) as ei:
+        gu.run(tb, spec, req, base=base, flags=pkg.DT_VALIDATE)
+    assert ei.value.status == pkg.binding.DT_EINVAL
+    tb.close()
+
+
+def test_runs_are_bitwise_reproducible(dev):
+    spec = synth.small("repro", V=4000, D=6, h=64, e=64, ds=128, r=64, M=32, k=8, N=60, B=6,
+                       wdtype="bf16", group=502, emb_std=0.5)
+    spec, w, req = synth.workload(spec)
+    tb = gu.make_builder(spec, w)
+    a = gu.run(tb, spec, req)
+    b = gu.run(tb, spec, req)
+    for key in a:
+        np.testing.assert_array_equal(a[key], b[key], err_msg=key)
+    tb.close()
