@@ -15,7 +15,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 DT_OK, DT_EINVAL, DT_EUNSUPPORTED, DT_ENOMEM, DT_EHIP, DT_EDEVICE = 0, -1, -2, -3, -4, -5
 DT_F32, DT_BF16 = 0, 1
 DT_NORM_TOPM, DT_NORM_FULLV = 0, 1
-DT_ACT_BF16, DT_VALIDATE = 1, 2
+DT_ACT_BF16, DT_VALIDATE, DT_TIMING = 1, 2, 4
 _STATUS = {0: "DT_OK", -1: "DT_EINVAL", -2: "DT_EUNSUPPORTED", -3: "DT_ENOMEM", -4: "DT_EHIP",
            -5: "DT_EDEVICE"}
 
@@ -54,8 +54,8 @@ class Outputs(C.Structure):
                 ("cand_logits", C.c_void_p), ("lse", C.c_void_p)]
 
 
-EXPORTS = ["dt_create", "dt_build_trees", "dt_sync_status", "dt_destroy", "dt_last_error",
-           "dt_version"]
+EXPORTS = ["dt_create", "dt_build_trees", "dt_sync_status", "dt_phase_times", "dt_destroy",
+           "dt_last_error", "dt_version"]
 _lib = None
 
 
@@ -80,6 +80,9 @@ def load_library():
                                    C.POINTER(Outputs), C.c_void_p]
     lib.dt_sync_status.restype = C.c_int
     lib.dt_sync_status.argtypes = [C.c_void_p, C.c_void_p]
+    lib.dt_phase_times.restype = C.c_int
+    lib.dt_phase_times.argtypes = [C.c_void_p, C.POINTER(C.c_float), C.c_int,
+                                   C.POINTER(C.c_int32)]
     lib.dt_destroy.restype = C.c_int
     lib.dt_destroy.argtypes = [C.c_void_p]
     lib.dt_last_error.restype = C.c_char_p
@@ -117,6 +120,14 @@ def dt_build_trees(handle: int, inputs: Inputs, params: Params, outputs: Outputs
 
 def dt_sync_status(handle: int, stream: int = 0):
     _check(load_library().dt_sync_status(C.c_void_p(handle), C.c_void_p(stream)))
+
+
+def dt_phase_times(handle: int) -> tuple:
+    """(mean ms per phase [candidates, P, mailbox reset, tree], builds averaged)."""
+    ms = (C.c_float * 4)()
+    cnt = C.c_int32()
+    _check(load_library().dt_phase_times(C.c_void_p(handle), ms, 4, C.byref(cnt)))
+    return list(ms), cnt.value
 
 
 def dt_destroy(handle: int):
@@ -204,3 +215,8 @@ class TreeBuilder:
 
     def sync_status(self):
         dt_sync_status(self.handle, self.stream.cuda_stream)
+
+    def phase_times(self) -> tuple:
+        """Mean [candidates, P, mailbox reset, tree] ms of the DT_TIMING builds
+        since the previous call, and how many builds were averaged."""
+        return dt_phase_times(self.handle)

@@ -71,6 +71,9 @@ struct dt_handle {
   int* nanflag = nullptr;
   size_t act_bytes = 0;
   int max_workers = 0;
+  static constexpr int RING = 256;   // timed builds kept for dt_phase_times
+  hipEvent_t ev[RING][5] = {};
+  int timed = 0;                      // timed builds since the last dt_phase_times
 };
 
 namespace {
@@ -91,6 +94,9 @@ void free_all(dt_handle* h) {
                   h->rec,     h->mbox_w,   h->mbox_c,   h->err,   h->nanflag};
   for (void* p : ptrs)
     if (p) (void)hipFree(p);
+  for (auto& set : h->ev)
+    for (hipEvent_t& e : set)
+      if (e) (void)hipEventDestroy(e);
 }
 
 dt_status check_dims(const dt_dims* d) {
@@ -119,7 +125,7 @@ dt_status check_params(const dt_params* p, int V, const dt_params* maxp) {
   if (!(p->temperature > 0.f) || !std::isfinite(p->temperature))
     return fail(DT_EINVAL, "temperature must be finite and > 0");
   if (p->norm != DT_NORM_TOPM && p->norm != DT_NORM_FULLV) return fail(DT_EINVAL, "unknown norm");
-  if (p->flags & ~(DT_ACT_BF16 | DT_VALIDATE)) return fail(DT_EINVAL, "unknown flags 0x%x", p->flags);
+  if (p->flags & ~(DT_ACT_BF16 | DT_VALIDATE | DT_TIMING)) return fail(DT_EINVAL, "unknown flags 0x%x", p->flags);
   if (maxp && (p->top_m > maxp->top_m || p->top_k > maxp->top_k || p->budget > maxp->budget))
     return fail(DT_EINVAL, "params exceed the handle's max_params");
   return DT_OK;
@@ -241,6 +247,8 @@ dt_status dt_create(dt_handle** out, const dt_dims* dims, const dt_weights* w, c
   ALLOC(h->err, 64);
   ALLOC(h->nanflag, 64);
   HIPB(hipMemsetAsync(h->err, 0, 64, stream));
+  for (auto& set : h->ev)
+    for (hipEvent_t& ev : set) HIPB(hipEventCreate(&ev));
   HIPB(hipStreamSynchronize(stream));
 #undef ALLOC
 #undef HIPB
@@ -265,6 +273,10 @@ dt_status dt_build_trees(dt_handle* h, const dt_inputs* in, const dt_params* p, 
 
   const int B = in->batch, D = d.depths, V = d.vocab, M = p->top_m, N = p->budget;
   const int rows = B * D;
+  const bool timing = (p->flags & DT_TIMING) != 0;
+  hipEvent_t* evs = h->ev[h->timed % dt_handle::RING];
+#define MARK(i) \
+  if (timing) HIPCHK(hipEventRecord(evs[i], stream))
 
   if ((p->flags & DT_VALIDATE) && in->base_logits) {
     HIPCHK(hipMemsetAsync(h->nanflag, 0, sizeof(int), stream));
@@ -276,6 +288,7 @@ dt_status dt_build_trees(dt_handle* h, const dt_inputs* in, const dt_params* p, 
   }
 
   // a1: per-depth candidates and LSE
+  MARK(0);
   if (in->base_logits) {
     HIPCHK(dt::launch_topm(in->base_logits, rows, V, M, p->temperature, h->chunk_cand, h->chunk_stat,
                            h->cand_ids, h->cand_vals, h->lse, h->tail, h->tokrank, out->cand_ids,
@@ -288,6 +301,7 @@ dt_status dt_build_trees(dt_handle* h, const dt_inputs* in, const dt_params* p, 
                                  out->cand_logits, out->lse, stream));
   }
   // a2: P = H W1_H (the path-independent half of W1 [H_d; S])
+  MARK(1);
   if (h->bf16)
     HIPCHK(dt::launch_gemm_bf16((const uint16_t*)in->hidden, nullptr, (const uint16_t*)h->w1h_t, nullptr, h->P,
                                 rows, d.rank, d.hidden, d.rank, stream));
@@ -338,9 +352,33 @@ dt_status dt_build_trees(dt_handle* h, const dt_inputs* in, const dt_params* p, 
   a.spin_limit = 1u << 21;
   const size_t lds = dt::tree_lds_bytes(a, h->bf16);
   if (lds > 160 * 1024) return fail(DT_EUNSUPPORTED, "builder needs %zu bytes of LDS", lds);
+  MARK(2);
   HIPCHK(dt::launch_fill_u32(h->mbox_w, 0u, (size_t)a.n_workers * 32, stream));
   HIPCHK(dt::launch_fill_u32(h->mbox_c, 0u, (size_t)B * 256, stream));
+  MARK(3);
   HIPCHK(dt::launch_tree(a, h->bf16, lds, stream));
+  MARK(4);
+  if (timing) ++h->timed;
+#undef MARK
+  return DT_OK;
+}
+
+dt_status dt_phase_times(dt_handle* h, float* ms, int n, int32_t* count) {
+  if (!h || !ms || !count) return fail(DT_EINVAL, "h, ms and count are required");
+  const int nb = h->timed < dt_handle::RING ? h->timed : dt_handle::RING;
+  double sum[4] = {0, 0, 0, 0};
+  for (int j = 0; j < nb; ++j) {
+    hipEvent_t* evs = h->ev[(h->timed - 1 - j) % dt_handle::RING];
+    HIPCHK(hipEventSynchronize(evs[4]));
+    for (int i = 0; i < 4; ++i) {
+      float t = 0.f;
+      HIPCHK(hipEventElapsedTime(&t, evs[i], evs[i + 1]));
+      sum[i] += t;
+    }
+  }
+  for (int i = 0; i < 4 && i < n; ++i) ms[i] = nb ? (float)(sum[i] / nb) : 0.f;
+  *count = nb;
+  h->timed = 0;
   return DT_OK;
 }
 

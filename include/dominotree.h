@@ -80,6 +80,7 @@ typedef enum { DT_NORM_TOPM = 0, DT_NORM_FULLV = 1 } dt_norm;
 /* dt_params.flags */
 #define DT_ACT_BF16 1u  /* round the GRU state to bf16 where it is a GEMM operand */
 #define DT_VALIDATE 2u  /* scan the base logits for NaN first (DT_EINVAL if any) */
+#define DT_TIMING 4u    /* record HIP events between the phases of the build (dt_phase_times) */
 
 /* Limits of this build (DT_EUNSUPPORTED beyond them). */
 #define DT_MAX_BATCH 32
@@ -119,7 +120,7 @@ typedef struct {
   int32_t budget;    /* N, 1..DT_MAX_BUDGET, with N (k - 1) + 1 <= DT_MAX_FRONTIER */
   float temperature; /* T > 0 */
   dt_norm norm;
-  uint32_t flags;    /* DT_ACT_BF16 | DT_VALIDATE */
+  uint32_t flags;    /* DT_ACT_BF16 | DT_VALIDATE | DT_TIMING */
 } dt_params;
 
 typedef struct {
@@ -176,6 +177,16 @@ dt_status dt_build_trees(dt_handle* h, const dt_inputs* in, const dt_params* p,
 /* Synchronise `stream` and report a device-side failure of the handle's
  * builds so far (DT_EDEVICE) or DT_OK. */
 dt_status dt_sync_status(dt_handle* h, void* stream);
+
+/* Mean durations, in milliseconds, of the phases of the builds made with
+ * DT_TIMING since the previous call (at most the last 256 of them), measured
+ * with HIP events recorded on each build's stream: ms[0] candidates (top-M +
+ * LSE, or the LM head with its candidate epilogue), ms[1] P = H W1_H, ms[2]
+ * mailbox reset, ms[3] the tree builder kernel.  Waits for those events,
+ * writes min(n, 4) values and the number of builds averaged to *count, then
+ * starts a new averaging window.
+ * Errors: DT_EINVAL (NULL h, ms or count), DT_EHIP. */
+dt_status dt_phase_times(dt_handle* h, float* ms, int n, int32_t* count);
 
 /* Free everything the handle owns (synchronises the device first). NULL is a no-op. */
 dt_status dt_destroy(dt_handle* h);

@@ -1,0 +1,88 @@
+"""GPU parity at the full workload sizes (Qwen3-4B / Qwen3-8B shapes).
+
+The oracle rebuilds a sample of requests one by one; every request of the
+batch is checked for the properties that hold at any size (exact candidates,
+valid tree structure, full budget, non-increasing scores in pop order).
+"""
+import numpy as np
+import pytest
+
+from tests import gpu_util as gu
+from workloads import synth
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dev():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no HIP device")
+    return torch.device("cuda:0")
+
+
+@pytest.fixture(scope="module")
+def q8b_builder(dev):
+    spec, w, _ = synth.workload("q8b_b32")
+    tb = gu.make_builder(spec, w, max_batch=32, max_m=64, max_k=8, max_n=256)
+    yield tb
+    tb.close()
+
+
+def _top_m_fast(row, M):
+    # (value desc, id asc) over the whole row, via a partition then an exact sort
+    kth = np.partition(row, row.size - M)[row.size - M]
+    idx = np.nonzero(row >= kth)[0]
+    order = np.lexsort((idx, -row[idx].astype(np.float64)))
+    return idx[order][:M]
+
+
+def _check_structure(spec, got):
+    for b in range(spec.B):
+        n = int(got["n_nodes"][b])
+        assert n == spec.N, (b, n)
+        par, dep, sc = got["parents"][b], got["depths"][b], got["scores"][b]
+        assert par[0] == -1 and dep[0] == 0 and sc[0] == 0
+        for i in range(1, n + 1):
+            assert 0 <= par[i] < i and dep[i] == dep[par[i]] + 1 <= spec.D
+        assert np.all(np.diff(sc[1:n + 1]) <= 1e-6)
+
+
+def _full_case(spec, w, req, tb, sample):
+    got = gu.run(tb, spec, req)
+    _check_structure(spec, got)
+    for b in range(spec.B):
+        for d in range(spec.D):
+            np.testing.assert_array_equal(got["cand_ids"][b, d], _top_m_fast(req["base"][b, d], spec.M),
+                                          err_msg=f"request {b} depth {d}")
+    reps, trees = gu.compare(spec, w, req, got, requests=sample)
+    gu.check_candidates(spec, trees, got, sample)
+    print(spec.name, gu.summarize(reps))
+    for b, r in zip(sample, reps):
+        assert r.ok, (b, r)
+    return got, reps
+
+
+def test_q4b_b1(dev):
+    spec, w, req = synth.workload("q4b_b1")
+    tb = gu.make_builder(spec, w)
+    _full_case(spec, w, req, tb, [0])
+    tb.close()
+
+
+def test_q8b_b1(dev, q8b_builder):
+    spec, w, req = synth.workload("q8b_b1")
+    _full_case(spec, w, req, q8b_builder, [0])
+
+
+def test_q8b_b32(dev, q8b_builder):
+    spec, w, req = synth.workload("q8b_b32")
+    _full_case(spec, w, req, q8b_builder, [0, 7, 19, 31])
+
+
+def test_q8b_b32_fullv_and_smaller_batch_reuse_handle(dev, q8b_builder):
+    # the same handle serves a smaller batch and the full-vocabulary normaliser
+    spec, w, req = synth.workload("q8b_b32")
+    small = spec.replace(B=5, norm="fullv", N=96)
+    req5 = {k: (v[:5] if v is not None else None) for k, v in req.items()}
+    _full_case(small, w, req5, q8b_builder, [0, 4])
