@@ -64,7 +64,6 @@ struct dt_handle {
   void* act = nullptr;
   float* gh = nullptr;
   float* u = nullptr;
-  int32_t* rec = nullptr;
   uint32_t* mbox_w = nullptr;
   uint32_t* mbox_c = nullptr;
   int* err = nullptr;
@@ -91,7 +90,7 @@ void free_all(dt_handle* h) {
   void* ptrs[] = {h->G,       h->tiles,    h->b_hh,     h->w1h_t, h->w2t,      h->wlm_t,
                   h->chunk_cand, h->chunk_stat, h->cand_ids, h->cand_vals, h->tokrank, h->lse,
                   h->tail,    h->P,        h->state,    h->act,   h->gh,       h->u,
-                  h->rec,     h->mbox_w,   h->mbox_c,   h->err,   h->nanflag};
+                  h->mbox_w,   h->mbox_c,   h->err,   h->nanflag};
   for (void* p : ptrs)
     if (p) (void)hipFree(p);
   for (auto& set : h->ev)
@@ -240,7 +239,6 @@ dt_status dt_create(dt_handle** out, const dt_dims* dims, const dt_weights* w, c
   HIPB(hipMemsetAsync(h->act, 0, h->act_bytes, stream));
   ALLOC(h->gh, nodes * round_up(3 * ds, 32) * sizeof(float));
   ALLOC(h->u, nodes * round_up(r, 32) * sizeof(float));
-  ALLOC(h->rec, (size_t)Bm * (N + 2) * sizeof(int32_t));
   h->max_workers = h->n_cu;
   ALLOC(h->mbox_w, (size_t)h->max_workers * 32 * sizeof(uint32_t));
   ALLOC(h->mbox_c, (size_t)DT_MAX_BATCH * 256 * sizeof(uint32_t));
@@ -340,7 +338,6 @@ dt_status dt_build_trees(dt_handle* h, const dt_inputs* in, const dt_params* p, 
   a.act = h->act;
   a.gh = h->gh;
   a.u = h->u;
-  a.rec = h->rec;
   a.mbox_w = h->mbox_w;
   a.mbox_c = h->mbox_c;
   a.err = h->err;

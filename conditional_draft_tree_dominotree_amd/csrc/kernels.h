@@ -68,12 +68,11 @@ struct TreeArgs {
   const float* tail;       // [B, D]
   const int32_t* tokrank;  // [B, D, M]
   const float* root;       // [B, ds] or NULL
-  // write-once exchange buffers
-  float* state;            // [B, N + 1, ds]
-  void* act;               // [B, N + 1, ds] GEMM operand copy of the state (wdtype)
-  float* gh;               // [B, N + 1, 3 ds]
-  float* u;                // [B, N + 1, r]
-  int32_t* rec;            // [B, N + 2] node expanded at each step (-1: request finished)
+  // write-once exchange buffers; act, gh and u are step-major: [step][request]
+  float* state;            // [B, N + 1, ds] by node
+  void* act;               // [N + 1, B, ds] GEMM operand copy of the expanded state (wdtype)
+  float* gh;               // [N + 1, B, 3 ds]
+  float* u;                // [N + 1, B, r]
   uint32_t* mbox_w;        // [n_workers][32] controller -> worker mailboxes (one line each)
   uint32_t* mbox_c;        // [B][256] worker -> controller mailboxes
   int* err;                // device error word

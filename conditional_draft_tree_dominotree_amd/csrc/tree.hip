@@ -69,6 +69,28 @@ __device__ __forceinline__ void st_dev_act<float>(float* p, float v, int act_bf1
   st_dev_f32(p, act_bf16 ? bf16_to_f32(f32_to_bf16(v)) : v);
 }
 
+__device__ __forceinline__ void st_dev_u32x2(void* p, uint32_t lo, uint32_t hi) {
+  typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+  u32x2 v = {lo, hi};
+  asm volatile("global_store_dwordx2 %0, %1, off sc1" ::"v"(p), "v"(v) : "memory");
+}
+
+// four consecutive operand values (the address is 8- or 16-byte aligned)
+template <typename W>
+__device__ __forceinline__ void st_dev_act4(W* p, floatx4 v, int act_bf16);
+template <>
+__device__ __forceinline__ void st_dev_act4<uint16_t>(uint16_t* p, floatx4 v, int) {
+  const uint32_t lo = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
+  const uint32_t hi = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
+  st_dev_u32x2(p, lo, hi);
+}
+template <>
+__device__ __forceinline__ void st_dev_act4<float>(float* p, floatx4 v, int act_bf16) {
+  if (act_bf16)
+    for (int q = 0; q < 4; ++q) v[q] = bf16_to_f32(f32_to_bf16(v[q]));
+  st_dev_f32x4(p, v);
+}
+
 template <typename W>
 __device__ __forceinline__ float w_to_f32(W v);
 template <>
@@ -98,7 +120,7 @@ __device__ __forceinline__ int key_parent(uint64_t k) { return 1023 - (int)((k >
 __device__ __forceinline__ int key_slot(uint64_t k) { return (int)((k >> 5) & 63); }
 
 // bounded wait on the words of one mailbox line; wave-uniform
-__device__ bool wait_mbox(const uint32_t* box, int nwords, uint32_t epoch, const int* err,
+__device__ __forceinline__ bool wait_mbox(const uint32_t* box, int nwords, uint32_t epoch, const int* err,
                           unsigned limit) {
   const int lane = threadIdx.x & 63;
   unsigned it = 0;
@@ -128,22 +150,26 @@ struct WorkerLds {
   }
 };
 
-__device__ __forceinline__ void worker_store_out(const TreeArgs& a, int b, int node, int row, float v) {
+// Exchange slots are step-major: the column request b publishes at step t
+// lives in slot t * B + b of act, gh and u.
+__device__ __forceinline__ size_t slot_of(const TreeArgs& a, int t, int b) { return (size_t)t * a.B + b; }
+
+__device__ __forceinline__ void worker_store_out(const TreeArgs& a, size_t slot, int row, float v) {
   const int ds3 = 3 * a.ds;
   if (row < ds3) {
-    st_dev_f32(a.gh + ((size_t)b * (a.N + 1) + node) * gh_stride(a.ds) + row, v + (a.b_hh ? a.b_hh[row] : 0.f));
+    st_dev_f32(a.gh + slot * gh_stride(a.ds) + row, v + (a.b_hh ? a.b_hh[row] : 0.f));
   } else if (row < ds3 + a.r) {
-    st_dev_f32(a.u + ((size_t)b * (a.N + 1) + node) * u_stride(a.r) + (row - ds3), v);
+    st_dev_f32(a.u + slot * u_stride(a.r) + (row - ds3), v);
   }
 }
 
 template <typename W>
-__device__ void worker_compute(const TreeArgs& a, const W* tiles_lds, const W* stage, int ncols,
+__device__ __forceinline__ void worker_compute(const TreeArgs& a, const W* tiles_lds, const W* stage, int ncols,
                                const int* colb, const int* coln, int my_tile0, int my_ntiles, int kp);
 
 // bf16: MFMA 16x16x32; wave w takes (tile, column block) pairs w, w+4, ...
 template <>
-__device__ void worker_compute<uint16_t>(const TreeArgs& a, const uint16_t* tiles_lds, const uint16_t* stage,
+__device__ __forceinline__ void worker_compute<uint16_t>(const TreeArgs& a, const uint16_t* tiles_lds, const uint16_t* stage,
                                          int ncols, const int* colb, const int* coln, int my_tile0,
                                          int my_ntiles, int kp) {
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
@@ -156,14 +182,30 @@ __device__ void worker_compute<uint16_t>(const TreeArgs& a, const uint16_t* tile
     const uint16_t* wt = tiles_lds + (size_t)tt * 16 * kp;
     const int col = cb * 16 + (lane & 15);
     const uint16_t* sc = stage + (size_t)col * kps + 8 * (lane >> 4);
-    for (int kb = 0; kb < nkb; ++kb) {
+    // two independent accumulation chains, 4 k blocks in flight
+    floatx4 acc2 = {0.f, 0.f, 0.f, 0.f};
+    int kb = 0;
+    for (; kb + 4 <= nkb; kb += 4) {
+      bf16x8 av[4], bv[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        av[q] = *reinterpret_cast<const bf16x8*>(wt + ((size_t)(kb + q) * 64 + lane) * 8);
+        bv[q] = *reinterpret_cast<const bf16x8*>(sc + (kb + q) * 32);
+      }
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[0], bv[0], acc, 0, 0, 0);
+      acc2 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[1], bv[1], acc2, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[2], bv[2], acc, 0, 0, 0);
+      acc2 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[3], bv[3], acc2, 0, 0, 0);
+    }
+    for (; kb < nkb; ++kb) {
       const bf16x8 av = *reinterpret_cast<const bf16x8*>(wt + ((size_t)kb * 64 + lane) * 8);
       const bf16x8 bv = *reinterpret_cast<const bf16x8*>(sc + kb * 32);
       acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, acc, 0, 0, 0);
     }
+    acc += acc2;
     // lane holds column (lane & 15), rows 4 (lane >> 4) + i of the tile
     if (col < ncols) {
-      const int b = colb[col], node = coln[col];
+      const size_t slot = (size_t)coln[col];
       const int row0 = (my_tile0 + tt) * 16 + 4 * (lane >> 4);
       const int ds3 = 3 * a.ds;
       if (row0 + 3 < ds3 && (ds3 & 3) == 0) {
@@ -175,9 +217,9 @@ __device__ void worker_compute<uint16_t>(const TreeArgs& a, const uint16_t* tile
           v[2] += bh[row0 + 2];
           v[3] += bh[row0 + 3];
         }
-        st_dev_f32x4(a.gh + ((size_t)b * (a.N + 1) + node) * gh_stride(a.ds) + row0, v);
+        st_dev_f32x4(a.gh + slot * gh_stride(a.ds) + row0, v);
       } else {
-        for (int i = 0; i < 4; ++i) worker_store_out(a, b, node, row0 + i, acc[i]);
+        for (int i = 0; i < 4; ++i) worker_store_out(a, slot, row0 + i, acc[i]);
       }
     }
   }
@@ -185,7 +227,7 @@ __device__ void worker_compute<uint16_t>(const TreeArgs& a, const uint16_t* tile
 
 // fp32: one (row, column) dot product per thread over the padded k
 template <>
-__device__ void worker_compute<float>(const TreeArgs& a, const float* tiles_lds, const float* stage, int ncols,
+__device__ __forceinline__ void worker_compute<float>(const TreeArgs& a, const float* tiles_lds, const float* stage, int ncols,
                                       const int* colb, const int* coln, int my_tile0, int my_ntiles,
                                       int kp) {
   const int kps = kp + STAGE_PAD;
@@ -201,12 +243,12 @@ __device__ void worker_compute<float>(const TreeArgs& a, const float* tiles_lds,
       const int kb = k >> 5, kg = (k >> 3) & 3, e = k & 7;
       s = fmaf(wt[(((size_t)kb * 4 + kg) * 16 + rr) * 8 + e], sc[k], s);
     }
-    worker_store_out(a, colb[col], coln[col], (my_tile0 + tt) * 16 + rr, s);
+    worker_store_out(a, (size_t)coln[col], (my_tile0 + tt) * 16 + rr, s);
   }
 }
 
 template <typename W>
-__device__ void worker_main(const TreeArgs& a, unsigned char* lds) {
+__device__ __forceinline__ void worker_main(const TreeArgs& a, unsigned char* lds) {
   const int w = blockIdx.x;
   const int tid = threadIdx.x;
   const int kp = k_padded(a.ds);
@@ -242,31 +284,48 @@ __device__ void worker_main(const TreeArgs& a, unsigned char* lds) {
     // active columns: requests whose controller has not finished
     if (tid < 64) {
       const int b = tid;
-      bool act = false;
-      int node = -1;
-      if (b < a.B && ld_dev_u32(mybox + b) != MBOX_DONE) {
-        node = (int)ld_dev_u32(a.rec + (size_t)b * (a.N + 2) + t);
-        act = node >= 0;
-      }
+      const bool act = b < a.B && ld_dev_u32(mybox + b) != MBOX_DONE;
       const unsigned long long m = __ballot(act);
       if (act) {
-        const int slot = __popcll(m & ((1ull << tid) - 1ull));
-        colb[slot] = b;
-        coln[slot] = node;
+        const int c = __popcll(m & ((1ull << tid) - 1ull));
+        colb[c] = b;
+        coln[c] = (int)slot_of(a, t, b);  // exchange slot of this column
       }
       if (tid == 0) *ncols_s = __popcll(m);
     }
     __syncthreads();
     const int ncols = *ncols_s;
     if (ncols == 0) return;  // every request is finished
-    // stage the GEMM operand copies of the expanded states (published, read once)
+    // stage the GEMM operand copies of the expanded states (published, read
+    // once).  Thread tid owns piece tid % per of columns tid / per + j * cpt;
+    // every load of a round is issued before any LDS store.
     {
       const int per = kp * (int)sizeof(W) / 16;  // 16-byte pieces per column
-      for (int i = tid; i < ncols * per; i += blockDim.x) {
-        const int c = i / per, p = i % per;
-        const W* src = reinterpret_cast<const W*>(a.act) + ((size_t)colb[c] * (a.N + 1) + coln[c]) * as;
-        *reinterpret_cast<uint4*>(stage + (size_t)c * kps + p * (16 / sizeof(W))) =
-            reinterpret_cast<const uint4*>(src)[p];
+      if (per <= 256 && 256 % per == 0) {
+        const int cpt = 256 / per;                 // columns per pass
+        const int pc = tid % per, c0 = tid / per;
+        constexpr int U = 16;
+        for (int cb = 0; cb < ncols; cb += U * cpt) {
+          uint4 v[U];
+#pragma unroll
+          for (int q = 0; q < U; ++q) {  // clamped: every lane loads a valid piece
+            const int c = min(cb + c0 + q * cpt, ncols - 1);
+            v[q] = reinterpret_cast<const uint4*>(reinterpret_cast<const W*>(a.act) + (size_t)coln[c] * as)[pc];
+          }
+          // unconditional stores (a clamped duplicate rewrites identical data),
+          // so that no load is sunk into a guarded block and serialised
+#pragma unroll
+          for (int q = 0; q < U; ++q) {
+            const int c = min(cb + c0 + q * cpt, ncols - 1);
+            *reinterpret_cast<uint4*>(stage + (size_t)c * kps + pc * (16 / sizeof(W))) = v[q];
+          }
+        }
+      } else {
+        for (int i = tid; i < ncols * per; i += blockDim.x) {
+          const int c = i / per, pc = i % per;
+          *reinterpret_cast<uint4*>(stage + (size_t)c * kps + pc * (16 / sizeof(W))) =
+              reinterpret_cast<const uint4*>(reinterpret_cast<const W*>(a.act) + (size_t)coln[c] * as)[pc];
+        }
       }
     }
     __syncthreads();
@@ -292,8 +351,11 @@ struct CtlLds {
   int* ntok;       // [N+1]
   int* npar;
   int* ndep;
+  int* nstep;      // [N+1] step at which a node was expanded
   float* nscore;
   float* av;       // [r]
+  void* w2s;       // [M][r] candidate rows of W2 for the next expansion (wdtype)
+  float* ps;       // [r] P row of the next expansion
   float* z;        // [64]
   float* logp;     // [64]
   int* okf;        // [64]
@@ -303,19 +365,20 @@ struct CtlLds {
   float* redf;     // [4]
 };
 
-__host__ __device__ inline size_t ctl_lds_bytes(int D, int M, int N, int r, int fcap) {
-  size_t s = 0;
+__host__ __device__ inline size_t ctl_lds_bytes(int D, int M, int N, int r, int fcap, int esz) {
+  size_t s = (size_t)M * r * esz + (size_t)r * 4 + 32;  // w2s, ps
   s += (size_t)fcap * 8;              // front (first: 8-byte aligned)
   s += (size_t)D * M * 4 * 3 + D * 4; // cid, cval, crank, tailv
-  s += (size_t)(N + 1) * 4 * 4;       // node records
+  s += (size_t)(N + 1) * 4 * 5;       // node records
   s += (size_t)r * 4 + 64 * 4 * 3;    // av, z, logp, okf
   s += 16 * 4 + 4 * 8 + 4 * 4 + 4 * 4 + 64;
   return s;
 }
 
-__device__ CtlLds ctl_carve(unsigned char* lds, int D, int M, int N, int r, int fcap) {
+__device__ __forceinline__ CtlLds ctl_carve(unsigned char* lds, int D, int M, int N, int r, int fcap, int esz) {
   CtlLds c;
   unsigned char* p = lds;
+  c.w2s = p; p += ((size_t)M * r * esz + 15) / 16 * 16;
   c.front = reinterpret_cast<uint64_t*>(p); p += (size_t)fcap * 8;
   c.red64 = reinterpret_cast<uint64_t*>(p); p += 4 * 8;
   c.cid = reinterpret_cast<int*>(p); p += (size_t)D * M * 4;
@@ -325,8 +388,10 @@ __device__ CtlLds ctl_carve(unsigned char* lds, int D, int M, int N, int r, int 
   c.ntok = reinterpret_cast<int*>(p); p += (size_t)(N + 1) * 4;
   c.npar = reinterpret_cast<int*>(p); p += (size_t)(N + 1) * 4;
   c.ndep = reinterpret_cast<int*>(p); p += (size_t)(N + 1) * 4;
+  c.nstep = reinterpret_cast<int*>(p); p += (size_t)(N + 1) * 4;
   c.nscore = reinterpret_cast<float*>(p); p += (size_t)(N + 1) * 4;
   c.av = reinterpret_cast<float*>(p); p += (size_t)r * 4;
+  c.ps = reinterpret_cast<float*>(p); p += (size_t)r * 4;
   c.z = reinterpret_cast<float*>(p); p += 64 * 4;
   c.logp = reinterpret_cast<float*>(p); p += 64 * 4;
   c.okf = reinterpret_cast<int*>(p); p += 64 * 4;
@@ -338,128 +403,224 @@ __device__ CtlLds ctl_carve(unsigned char* lds, int D, int M, int N, int r, int 
 
 __device__ __forceinline__ float sigm(float x) { return 1.0f / (1.0f + expf(-x)); }
 
+// Load the W2 rows of depth row dy's candidates and its P row into LDS.
+// Issued while the controller waits for the workers, so the expansion that
+// follows reads only LDS and the published u.
+template <typename W>
+__device__ __forceinline__ void ctl_prefetch(const TreeArgs& a, const CtlLds& c, int b, int dy) {
+  const int tid = threadIdx.x, M = a.M, r = a.r;
+  W* dst = reinterpret_cast<W*>(c.w2s);
+  const W* w2t = reinterpret_cast<const W*>(a.w2t);
+  const int per = r * (int)sizeof(W) / 16;   // 16-byte pieces per row
+  if ((r * (int)sizeof(W)) % 16 == 0 && per <= 256 && 256 % per == 0) {
+    const int rpt = 256 / per;                 // rows per pass
+    const int pc = tid % per, m0 = tid / per;
+    constexpr int U = 8;
+    for (int mb = 0; mb < M; mb += U * rpt) {
+      uint4 v[U];
+#pragma unroll
+      for (int q = 0; q < U; ++q) {  // clamped: every lane loads a valid piece
+        const int m = min(mb + m0 + q * rpt, M - 1);
+        v[q] = reinterpret_cast<const uint4*>(w2t + (size_t)c.cid[dy * M + m] * r)[pc];
+      }
+#pragma unroll
+      for (int q = 0; q < U; ++q) {  // unconditional: see the worker's staging
+        const int m = min(mb + m0 + q * rpt, M - 1);
+        reinterpret_cast<uint4*>(dst)[m * per + pc] = v[q];
+      }
+    }
+  } else {
+    for (int i = tid; i < M * r; i += blockDim.x) dst[i] = w2t[(size_t)c.cid[dy * M + i / r] * r + i % r];
+  }
+  const float* prow = a.P + ((size_t)b * a.D + dy) * r;
+  for (int j = tid; j < r; j += blockDim.x) c.ps[j] = prow[j];
+}
+
 // score the children of node y (depth dy < D) and push the k best
 template <typename W>
-__device__ void ctl_expand(const TreeArgs& a, const CtlLds& c, int b, int y) {
+__device__ __forceinline__ void ctl_expand(const TreeArgs& a, const CtlLds& c, int b, int y, int t) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int M = a.M, r = a.r;
   const int dy = c.ndep[y];        // children are at depth dy + 1; row dy of the tables
-  const float* urow = a.u + ((size_t)b * (a.N + 1) + y) * u_stride(r);
-  const float* prow = a.P + ((size_t)b * a.D + dy) * r;
+  const float* urow = a.u + slot_of(a, t, b) * u_stride(r);
   for (int j = tid; j < r; j += blockDim.x) {
-    const float x = urow[j] + prow[j];
+    const float x = urow[j] + c.ps[j];
     c.av[j] = x * sigm(x);  // SiLU
   }
   __syncthreads();
-  // dL_m = W2[:, cand_m] . a  (thread group per candidate, fixed order)
+  // dL_m = W2[:, cand_m] . a: tpc threads per candidate, each a contiguous
+  // slice of the rank, combined in a fixed order
   int tpc = 1;
-  while (tpc * 2 * M <= (int)blockDim.x && tpc < 64) tpc *= 2;  // threads per candidate
+  while (tpc * 2 * M <= (int)blockDim.x && tpc < 64) tpc *= 2;
   const int m = tid / tpc, part = tid % tpc;
+  const int len = (r + tpc - 1) / tpc;
   float dl = 0.f;
   if (m < M) {
-    const int id = c.cid[dy * M + m];
-    const W* wrow = reinterpret_cast<const W*>(a.w2t) + (size_t)id * r;
-    for (int j = part; j < r; j += tpc) dl = fmaf(w_to_f32<W>(wrow[j]), c.av[j], dl);
+    const W* wrow = reinterpret_cast<const W*>(c.w2s) + (size_t)m * r;
+    const int j0 = part * len, j1 = min(r, j0 + len);
+    constexpr int VE = 16 / sizeof(W);  // elements per 16-byte piece
+    if (j1 - j0 == len && len % VE == 0 && (r * (int)sizeof(W)) % 16 == 0) {
+      for (int j = j0; j < j1; j += VE) {
+        const uint4 wv = *reinterpret_cast<const uint4*>(wrow + j);
+        const W* we = reinterpret_cast<const W*>(&wv);
+#pragma unroll
+        for (int q = 0; q < VE; q += 4) {
+          const float4 av = *reinterpret_cast<const float4*>(c.av + j + q);
+          dl = fmaf(w_to_f32<W>(we[q]), av.x, dl);
+          dl = fmaf(w_to_f32<W>(we[q + 1]), av.y, dl);
+          dl = fmaf(w_to_f32<W>(we[q + 2]), av.z, dl);
+          dl = fmaf(w_to_f32<W>(we[q + 3]), av.w, dl);
+        }
+      }
+    } else {
+      for (int j = j0; j < j1; ++j) dl = fmaf(w_to_f32<W>(wrow[j]), c.av[j], dl);
+    }
   }
   for (int s = 1; s < tpc; s <<= 1) dl += __shfl_xor(dl, s);
   if (m < M && part == 0) c.z[m] = (c.cval[dy * M + m] + dl) / a.T + 0.0f;
   __syncthreads();
-  // log-softmax over the candidates (plus the base tail under fullv), wave 0
+  // wave 0, one candidate per lane: log-softmax over the candidates (plus the
+  // base tail under fullv), rank by (z desc, token asc), push the k best with
+  // a finite log-prob.  -inf log-probs rank after every finite one, so the
+  // children take ranks 0..n-1.
   if (tid < 64) {
-    const float zv = lane < M ? c.z[lane] : -INFINITY;
+    const bool has = lane < M;
+    const float zv = has ? c.z[lane] : -INFINITY;
+    const int idv = has ? c.cid[dy * M + lane] : 0x7FFFFFFF;
     float mx = wave_max(zv);
-    if (a.fullv) mx = fmaxf(mx, c.tailv[dy]);
-    float se = 0.f;
+    const float tl = a.fullv ? c.tailv[dy] : -INFINITY;
+    mx = fmaxf(mx, tl);
+    float lz = -INFINITY;
     if (mx > -INFINITY) {
-      se = wave_sum(lane < M ? expf(zv - mx) : 0.f);
-      if (a.fullv && c.tailv[dy] > -INFINITY) se += expf(c.tailv[dy] - mx);
+      float se = wave_sum(has ? expf(zv - mx) : 0.f);
+      if (tl > -INFINITY) se += expf(tl - mx);
+      lz = mx + logf(se);
     }
-    const float lz = mx > -INFINITY ? mx + logf(se) : -INFINITY;
-    if (lane < M) c.logp[lane] = zv - lz;
-  }
-  __syncthreads();
-  // rank by (z desc, token asc); the k best with a finite log-prob are pushed.
-  // -inf log-probs rank after every finite one, so the children take ranks 0..n-1.
-  if (tid < M) {
-    const float zm = c.z[tid];
-    const int idm = c.cid[dy * M + tid];
+    const float lp = zv - lz;
     int rank = 0;
     for (int q = 0; q < M; ++q) {
-      const float zq = c.z[q];
-      rank += (zq > zm) || (zq == zm && c.cid[dy * M + q] < idm);
+      const float zq = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(zv), q));
+      const int iq = __builtin_amdgcn_readlane(idv, q);
+      rank += (zq > zv) || (zq == zv && iq < idv);
     }
-    const float lp = c.logp[tid];
-    const bool ok = rank < a.k && isfinite(lp);
-    c.okf[tid] = ok;
-    if (ok) c.front[c.misc[0] + rank] = make_key(c.nscore[y] + lp, dy + 1, c.crank[dy * M + tid], y, tid);
-  }
-  __syncthreads();
-  if (tid == 0) {
-    int nch = 0;
-    for (int q = 0; q < M; ++q) nch += c.okf[q];
-    c.misc[0] += nch;
+    const bool ok = has && rank < a.k && isfinite(lp);
+    const int base = c.misc[0];
+    if (ok) c.front[base + rank] = make_key(c.nscore[y] + lp, dy + 1, c.crank[dy * M + lane], y, lane);
+    const unsigned long long bal = __ballot(ok);
+    if (lane == 0) c.misc[0] = base + __popcll(bal);
   }
   __syncthreads();
 }
 
-// pop the best frontier entry; returns false when the frontier is empty
-__device__ bool ctl_pop(const CtlLds& c, uint64_t* key_out) {
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int n = c.misc[0];
-  if (n == 0) return false;
-  uint64_t best = 0;
-  int pos = -1;
-  for (int i = tid; i < n; i += blockDim.x) {
-    const uint64_t k = c.front[i];
-    if (pos < 0 || k > best) {
-      best = k;
-      pos = i;
+// Wave 0 pops frontier entries in order, recording each as the next node,
+// until it finds one to expand (depth < D and index < N), the budget is met
+// or the frontier is empty.  Returns the node to expand or -1; updates *n.
+// Called by all threads; only wave 0 works, then one barrier.
+__device__ __forceinline__ int ctl_pop_until_expandable(const CtlLds& c, int D, int M, int N, int* n) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  if (tid < 64) {
+    int cnt = c.misc[0];
+    int nn = *n;
+    int next = -1;
+    while (nn < N && cnt > 0) {
+      uint64_t best = 0;
+      int pos = -1;
+      for (int i = lane; i < cnt; i += 64) {
+        const uint64_t k = c.front[i];
+        if (pos < 0 || k > best) {
+          best = k;
+          pos = i;
+        }
+      }
+      const uint64_t g = wave_max_u64(pos < 0 ? 0ull : best);
+      const unsigned long long hit = __ballot(pos >= 0 && best == g);  // keys are unique
+      const int src = __ffsll((long long)hit) - 1;
+      const int gpos = __shfl(pos, src);
+      const int i = nn + 1;
+      const int d = key_depth(g);
+      if (lane == 0) {
+        c.front[gpos] = c.front[cnt - 1];
+        c.ntok[i] = c.cid[(d - 1) * M + key_slot(g)];
+        c.npar[i] = key_parent(g);
+        c.ndep[i] = d;
+        c.nscore[i] = key_score(g);
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+      --cnt;
+      nn = i;
+      if (d < D && i < N) {
+        next = i;
+        break;
+      }
+    }
+    if (lane == 0) {
+      c.misc[0] = cnt;
+      c.misc[4] = nn;
+      c.misc[5] = next;
     }
   }
-  const uint64_t wbest = wave_max_u64(pos < 0 ? 0ull : best);
-  if (lane == 0) c.red64[wv] = wbest;
   __syncthreads();
-  uint64_t gbest = c.red64[0];
-  for (int i = 1; i < (int)(blockDim.x >> 6); ++i) gbest = c.red64[i] > gbest ? c.red64[i] : gbest;
-  if (pos >= 0 && best == gbest) c.misc[1] = pos;  // keys are unique
-  __syncthreads();
-  if (tid == 0) {
-    const int p = c.misc[1];
-    c.front[p] = c.front[n - 1];
-    c.misc[0] = n - 1;
-  }
-  __syncthreads();
-  *key_out = gbest;
-  return true;
+  *n = c.misc[4];
+  return c.misc[5];
 }
 
 template <typename W>
-__device__ void ctl_advance_state(const TreeArgs& a, int b, int y, int x, int tok) {
+__device__ __forceinline__ void ctl_advance_state(const TreeArgs& a, int b, int y, int x, int tok, int tx,
+                                                  int ty) {
+  // x was expanded at step tx; y is published for step ty
   // S_y = GRU(S_x, E[tok]) with W_ih E[tok] + b_ih = G[tok] and gh_x = W_hh S~_x + b_hh
   const int ds = a.ds;
   const float* gi = a.G + (size_t)tok * 3 * ds;
-  const float* gh = a.gh + ((size_t)b * (a.N + 1) + x) * gh_stride(ds);
+  const float* gh = a.gh + slot_of(a, tx, b) * gh_stride(ds);
   const float* sx = a.state + ((size_t)b * (a.N + 1) + x) * st_stride(ds);
   float* sy = a.state + ((size_t)b * (a.N + 1) + y) * st_stride(ds);
-  W* ay = reinterpret_cast<W*>(a.act) + ((size_t)b * (a.N + 1) + y) * act_stride(ds);
-  for (int j = threadIdx.x; j < ds; j += blockDim.x) {
-    const float rg = sigm(gi[j] + gh[j]);
-    const float zg = sigm(gi[ds + j] + gh[ds + j]);
-    const float ng = tanhf(gi[2 * ds + j] + rg * gh[2 * ds + j]);
-    const float s = (1.0f - zg) * ng + zg * sx[j];
-    st_dev_f32(sy + j, s);
-    st_dev_act<W>(ay + j, s, a.act_bf16);
+  W* ay = reinterpret_cast<W*>(a.act) + slot_of(a, ty, b) * act_stride(ds);
+  if ((ds & 3) == 0) {
+    for (int j = 4 * threadIdx.x; j < ds; j += 4 * blockDim.x) {
+      const float4 ir = *reinterpret_cast<const float4*>(gi + j);
+      const float4 iz = *reinterpret_cast<const float4*>(gi + ds + j);
+      const float4 in = *reinterpret_cast<const float4*>(gi + 2 * ds + j);
+      const float4 hr = *reinterpret_cast<const float4*>(gh + j);
+      const float4 hz = *reinterpret_cast<const float4*>(gh + ds + j);
+      const float4 hn = *reinterpret_cast<const float4*>(gh + 2 * ds + j);
+      const float4 sp = *reinterpret_cast<const float4*>(sx + j);
+      const float a0[4] = {ir.x, ir.y, ir.z, ir.w}, b0[4] = {hr.x, hr.y, hr.z, hr.w};
+      const float a1[4] = {iz.x, iz.y, iz.z, iz.w}, b1[4] = {hz.x, hz.y, hz.z, hz.w};
+      const float a2[4] = {in.x, in.y, in.z, in.w}, b2[4] = {hn.x, hn.y, hn.z, hn.w};
+      const float s0[4] = {sp.x, sp.y, sp.z, sp.w};
+      floatx4 o;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float rg = sigm(a0[q] + b0[q]);
+        const float zg = sigm(a1[q] + b1[q]);
+        const float ng = tanhf(a2[q] + rg * b2[q]);
+        o[q] = (1.0f - zg) * ng + zg * s0[q];
+      }
+      st_dev_f32x4(sy + j, o);
+      st_dev_act4<W>(ay + j, o, a.act_bf16);
+    }
+  } else {
+    for (int j = threadIdx.x; j < ds; j += blockDim.x) {
+      const float rg = sigm(gi[j] + gh[j]);
+      const float zg = sigm(gi[ds + j] + gh[ds + j]);
+      const float ng = tanhf(gi[2 * ds + j] + rg * gh[2 * ds + j]);
+      const float s = (1.0f - zg) * ng + zg * sx[j];
+      st_dev_f32(sy + j, s);
+      st_dev_act<W>(ay + j, s, a.act_bf16);
+    }
   }
   for (int j = ds + threadIdx.x; j < k_padded(ds); j += blockDim.x) st_dev_act<W>(ay + j, 0.f, 0);
 }
 
 template <typename W>
-__device__ void controller_main(const TreeArgs& a, unsigned char* lds) {
+__device__ __forceinline__ void controller_main(const TreeArgs& a, unsigned char* lds) {
   const int b = blockIdx.x - a.n_workers;
   const int tid = threadIdx.x;
   const int D = a.D, M = a.M, N = a.N;
   const int fcap = a.N * (a.k - 1) + 1;
-  CtlLds c = ctl_carve(lds, D, M, N, a.r, fcap);
+  CtlLds c = ctl_carve(lds, D, M, N, a.r, fcap, (int)sizeof(W));
 
   for (int i = tid; i < D * M; i += blockDim.x) {
     c.cid[i] = a.cand_ids[(size_t)b * D * M + i];
@@ -478,7 +639,7 @@ __device__ void controller_main(const TreeArgs& a, unsigned char* lds) {
   {
     const int ds = a.ds;
     float* s0 = a.state + (size_t)b * (N + 1) * st_stride(ds);
-    W* a0 = reinterpret_cast<W*>(a.act) + (size_t)b * (N + 1) * act_stride(ds);
+    W* a0 = reinterpret_cast<W*>(a.act) + slot_of(a, 0, b) * act_stride(ds);
     for (int j = tid; j < ds; j += blockDim.x) {
       const float v = a.root ? a.root[(size_t)b * ds + j] : 0.f;
       st_dev_f32(s0 + j, v);
@@ -486,7 +647,7 @@ __device__ void controller_main(const TreeArgs& a, unsigned char* lds) {
     }
     for (int j = ds + tid; j < k_padded(ds); j += blockDim.x) st_dev_act<W>(a0 + j, 0.f, 0);
   }
-  if (tid == 0) st_dev_u32(a.rec + (size_t)b * (N + 2), 0u);
+  if (tid == 0) c.nstep[0] = 0;
   stores_done();
   __syncthreads();
   if (tid < a.n_workers) st_dev_u32(a.mbox_w + (size_t)tid * 32 + b, 1u);  // step 0 posted
@@ -494,6 +655,7 @@ __device__ void controller_main(const TreeArgs& a, unsigned char* lds) {
   stores_done();
   __syncthreads();
 
+  ctl_prefetch<W>(a, c, b, 0);  // the root's children are at depth 1
   int y = 0;  // node expanded at this step
   int n = 0;  // non-root nodes popped (same value in every thread)
   bool failed = false;
@@ -508,35 +670,18 @@ __device__ void controller_main(const TreeArgs& a, unsigned char* lds) {
       failed = true;
       break;
     }
-    ctl_expand<W>(a, c, b, y);
+    ctl_expand<W>(a, c, b, y, t);
     // pop until a node to expand is found, the budget is met or the frontier is empty
-    int next = -1;
-    while (n < N) {
-      uint64_t key;
-      if (!ctl_pop(c, &key)) break;
-      const int i = n + 1;
-      const int d = key_depth(key), slot = key_slot(key);
-      if (tid == 0) {
-        c.ntok[i] = c.cid[(d - 1) * M + slot];
-        c.npar[i] = key_parent(key);
-        c.ndep[i] = d;
-        c.nscore[i] = key_score(key);
-      }
-      n = i;
-      if (d < D && i < N) {
-        next = i;
-        break;
-      }
-    }
-    __syncthreads();
+    const int next = ctl_pop_until_expandable(c, D, M, N, &n);
     if (next < 0) break;
-    ctl_advance_state<W>(a, b, next, c.npar[next], c.ntok[next]);
-    if (tid == 0) st_dev_u32(a.rec + (size_t)b * (N + 2) + t + 1, (uint32_t)next);
+    ctl_advance_state<W>(a, b, next, c.npar[next], c.ntok[next], c.nstep[c.npar[next]], t + 1);
+    if (tid == 0) c.nstep[next] = t + 1;
     stores_done();
     __syncthreads();
     for (int w = tid; w < a.n_workers; w += blockDim.x)
       st_dev_u32(a.mbox_w + (size_t)w * 32 + b, epoch + 1u);
     stores_done();
+    ctl_prefetch<W>(a, c, b, c.ndep[next]);  // overlaps the workers' step
     __syncthreads();
     y = next;
   }
@@ -567,7 +712,7 @@ size_t tree_lds_bytes(const TreeArgs& a, int wdtype_bf16) {
   const int kp = k_padded(a.ds);
   const size_t w = wdtype_bf16 ? WorkerLds<uint16_t>::bytes(a.tiles_per_worker, kp)
                                : WorkerLds<float>::bytes(a.tiles_per_worker, kp);
-  const size_t c = ctl_lds_bytes(a.D, a.M, a.N, a.r, a.N * (a.k - 1) + 1);
+  const size_t c = ctl_lds_bytes(a.D, a.M, a.N, a.r, a.N * (a.k - 1) + 1, wdtype_bf16 ? 2 : 4);
   return w > c ? w : c;
 }
 
