@@ -112,9 +112,54 @@ __global__ void gemm_f32_kernel(const float* __restrict__ A, const float* __rest
   C[(size_t)m * ldc + n] = s + (bias ? bias[n] : 0.f);
 }
 
+// Small outputs (few 128 x 128 tiles): one 32 x 32 output tile per block, the
+// four waves split K and their partial tiles are summed in LDS in a fixed
+// order.  Operands are read straight from global memory (16 bytes per lane).
+__global__ __launch_bounds__(256) void gemm_bf16_small_kernel(const uint16_t* __restrict__ A,
+                                                              const uint16_t* __restrict__ Bt,
+                                                              const float* __restrict__ bias,
+                                                              float* __restrict__ C, int M, int N, int K,
+                                                              int ldc) {
+  __shared__ float part[4][32 * 32];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int m0 = blockIdx.y * 32, n0 = blockIdx.x * 32;
+  const int kq = ((K + 15) / 16 + 3) / 4 * 16;  // k per wave, a multiple of 16
+  const int kb = w * kq, ke = min(K, kb + kq);
+  floatx16 acc;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) acc[e] = 0.f;
+  const int ar = m0 + (lane & 31), bc = n0 + (lane & 31), ko = 8 * (lane >> 5);
+  for (int k = kb; k < ke; k += 64) {
+    bf16x8 av[4], bv[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint4 a = load_row8(A, ar, M, k + 16 * q + ko, ke, K);
+      const uint4 b = load_row8(Bt, bc, N, k + 16 * q + ko, ke, K);
+      av[q] = *reinterpret_cast<const bf16x8*>(&a);
+      bv[q] = *reinterpret_cast<const bf16x8*>(&b);
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[q], bv[q], acc, 0, 0, 0);
+  }
+#pragma unroll
+  for (int e = 0; e < 16; ++e) part[w][(8 * (e >> 2) + 4 * (lane >> 5) + (e & 3)) * 32 + (lane & 31)] = acc[e];
+  __syncthreads();
+  for (int i = tid; i < 32 * 32; i += 256) {
+    const int row = m0 + i / 32, col = n0 + i % 32;
+    if (row < M && col < N)
+      C[(size_t)row * ldc + col] = ((part[0][i] + part[1][i]) + (part[2][i] + part[3][i])) + (bias ? bias[col] : 0.f);
+  }
+}
+
 hipError_t launch_gemm_bf16(const uint16_t* A, const int32_t* rows, const uint16_t* Bt, const float* bias,
                             float* C, int M, int N, int K, int ldc, hipStream_t stream) {
   if (rows != nullptr || (K & 7) != 0) return hipErrorInvalidValue;
+  const long tiles = (long)((N + GT - 1) / GT) * ((M + GT - 1) / GT);
+  if (tiles < 256) {
+    dim3 grid((N + 31) / 32, (M + 31) / 32);
+    hipLaunchKernelGGL(gemm_bf16_small_kernel, grid, dim3(256), 0, stream, A, Bt, bias, C, M, N, K, ldc);
+    return hipGetLastError();
+  }
   dim3 grid((N + GT - 1) / GT, (M + GT - 1) / GT);
   hipLaunchKernelGGL(gemm_bf16_kernel, grid, dim3(256), 0, stream, A, Bt, bias, C, M, N, K, ldc);
   return hipGetLastError();

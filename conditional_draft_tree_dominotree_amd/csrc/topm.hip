@@ -7,11 +7,15 @@
 // comparison on the fp32 inputs, so it is exact; only the two LSE values are
 // rounded.
 //
-// Two kernels.  topm_chunk: one 256-thread block per (row, chunk of 8192
-// tokens) reads its chunk once from HBM into LDS as order-preserving keys,
-// finds the chunk's M-th largest key with a 3-pass radix select (12, 12, 8
-// bits), collects the chunk's top-M (ties at the threshold in id order) and
-// the chunk's LSE statistics.  topm_merge: one block per row ranks the chunk
+// Kernels.  topm_chunk: one 256-thread block per (row, chunk of 8192 tokens)
+// reads its chunk once from HBM into registers (32 values per thread).  The
+// M-th largest of the 256 per-thread maxima is a lower bound of the chunk's
+// M-th largest value (at least M threads reach it), so the keys at or above
+// it -- typically a little more than M -- hold the chunk's top-M; they are
+// ranked exactly as (value desc, id asc) composites.  The chunk's LSE
+// statistics come from the same registers.  topm_fallback: when more than 512
+// keys reach that bound (many equal values), an exact 3-pass radix select
+// over the chunk in LDS redoes that chunk.  topm_merge: one block per row ranks the chunk
 // lists against each other and keeps the M best; the LSE statistics combine
 // exactly (a token left out of its chunk's list is left out of the row's).
 // The merge also serves the LM-head path, whose GEMM epilogue writes the same
@@ -24,15 +28,17 @@ namespace dt {
 constexpr int TOPM_THREADS = 256;
 constexpr int HBINS = 4096;
 
+constexpr int PER_THREAD = TOPM_CHUNK / TOPM_THREADS;  // 32 values per thread
+constexpr int FAST_CAP = 512;                          // candidates the fast path ranks
+
 __global__ __launch_bounds__(TOPM_THREADS) void topm_chunk_kernel(
     const float* __restrict__ logits, int V, int S, int M, float T,
     uint64_t* __restrict__ out_cand, float4* __restrict__ out_stat) {
-  __shared__ uint32_t keys[TOPM_CHUNK];
-  __shared__ uint32_t hist[HBINS];
-  __shared__ uint64_t sel[DT_TOPM_MAX];
+  __shared__ __attribute__((aligned(16))) uint64_t sel[FAST_CAP + 2];
+  __shared__ __attribute__((aligned(16))) uint32_t tmax[TOPM_THREADS];
   __shared__ float red[4];
-  __shared__ int ired[4];
-  __shared__ int found_digit, found_above, sel_count, tie_last_s;
+  __shared__ int sel_count;
+  __shared__ uint32_t tau_s;
 
   const int tid = threadIdx.x;
   const int c = blockIdx.x;
@@ -42,29 +48,154 @@ __global__ __launch_bounds__(TOPM_THREADS) void topm_chunk_kernel(
   const int Mc = min(M, len);
   const float* src = logits + (size_t)row * (size_t)V + c0;
 
-  // 1. read the chunk once: keys into LDS, running max of the values
-  float vmax = -INFINITY;
-  if ((V & 3) == 0) {
+  // 1. read the chunk once into registers: element tid*4 + 1024 j + e holds
+  //    float4 piece j of thread tid (coalesced); missing elements are -inf.
+  float x[PER_THREAD];
+  if ((V & 3) == 0 && len == TOPM_CHUNK) {
     const float4* s4 = reinterpret_cast<const float4*>(src);
-    const int n4 = len >> 2;
-    for (int i = tid; i < n4; i += TOPM_THREADS) {
-      float4 x = s4[i];
-      keys[4 * i + 0] = f32_key(x.x);
-      keys[4 * i + 1] = f32_key(x.y);
-      keys[4 * i + 2] = f32_key(x.z);
-      keys[4 * i + 3] = f32_key(x.w);
-      vmax = fmaxf(vmax, fmaxf(fmaxf(x.x, x.y), fmaxf(x.z, x.w)));
+#pragma unroll
+    for (int j = 0; j < PER_THREAD / 4; ++j) {
+      const float4 v = s4[j * TOPM_THREADS + tid];
+      x[4 * j] = v.x;
+      x[4 * j + 1] = v.y;
+      x[4 * j + 2] = v.z;
+      x[4 * j + 3] = v.w;
     }
   } else {
-    for (int i = tid; i < len; i += TOPM_THREADS) {
-      float x = src[i];
-      keys[i] = f32_key(x);
-      vmax = fmaxf(vmax, x);
-    }
+#pragma unroll
+    for (int j = 0; j < PER_THREAD / 4; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int i = (j * TOPM_THREADS + tid) * 4 + e;
+        x[4 * j + e] = i < len ? src[i] : -INFINITY;
+      }
+  }
+  auto idx_of = [&](int q) { return ((q >> 2) * TOPM_THREADS + tid) * 4 + (q & 3); };
+  float vmax = -INFINITY;
+  uint32_t kmax = 0;
+#pragma unroll
+  for (int q = 0; q < PER_THREAD; ++q) {
+    vmax = fmaxf(vmax, x[q]);
+    if (idx_of(q) < len) kmax = max(kmax, f32_key(x[q]));
   }
   const float m = block_max<TOPM_THREADS>(vmax, red) / T;
 
-  // 2. radix select of the Mc-th largest key
+  // 2. threshold: the Mc-th largest per-thread maximum bounds the chunk's
+  //    Mc-th largest key from below (at least Mc threads reach it)
+  tmax[tid] = kmax;
+  if (tid == 0) sel_count = 0;
+  __syncthreads();
+  {
+    // rank of this thread's maximum among all 256 (ties by thread index);
+    // 16-byte broadcast reads of the maxima
+    int rank = 0;
+    const uint4* t4 = reinterpret_cast<const uint4*>(tmax);
+#pragma unroll 8
+    for (int i = 0; i < TOPM_THREADS / 4; ++i) {
+      const uint4 o = t4[i];
+      rank += (o.x > kmax) || (o.x == kmax && 4 * i < tid);
+      rank += (o.y > kmax) || (o.y == kmax && 4 * i + 1 < tid);
+      rank += (o.z > kmax) || (o.z == kmax && 4 * i + 2 < tid);
+      rank += (o.w > kmax) || (o.w == kmax && 4 * i + 3 < tid);
+    }
+    if (rank == Mc - 1) tau_s = kmax;
+  }
+  __syncthreads();
+  const uint32_t tau = tau_s;
+#pragma unroll
+  for (int q = 0; q < PER_THREAD; ++q) {
+    const int i = idx_of(q);
+    const uint32_t k = f32_key(x[q]);
+    if (i < len && k >= tau) {
+      const int slot = atomicAdd(&sel_count, 1);
+      if (slot < FAST_CAP) sel[slot] = cand_pack(k, (uint32_t)(c0 + i));
+    }
+  }
+  __syncthreads();
+  const int cnt = sel_count;
+  if (cnt <= FAST_CAP) {
+    // 3a. rank the candidates exactly (composite keys are unique)
+    uint64_t mine[FAST_CAP / TOPM_THREADS];
+    int rk[FAST_CAP / TOPM_THREADS];
+#pragma unroll
+    for (int u = 0; u < FAST_CAP / TOPM_THREADS; ++u) {
+      const int e = tid + u * TOPM_THREADS;
+      mine[u] = e < cnt ? sel[e] : 0ull;
+      rk[u] = 0;
+    }
+    if (tid == 0 && (cnt & 1)) sel[cnt] = 0ull;  // pad to pairs (0 ranks below every key)
+    __syncthreads();
+    const ulonglong2* s2 = reinterpret_cast<const ulonglong2*>(sel);
+#pragma unroll 4
+    for (int i = 0; i < (cnt + 1) / 2; ++i) {
+      const ulonglong2 o = s2[i];
+#pragma unroll
+      for (int u = 0; u < FAST_CAP / TOPM_THREADS; ++u) rk[u] += (o.x > mine[u]) + (o.y > mine[u]);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < FAST_CAP / TOPM_THREADS; ++u) {
+      const int e = tid + u * TOPM_THREADS;
+      if (e < cnt && rk[u] < Mc) sel[rk[u]] = mine[u];  // ranks < Mc are distinct
+    }
+    __syncthreads();
+  } else {
+    // too many keys at the threshold (equal values): topm_fallback_kernel
+    // redoes this chunk exactly
+    if (tid == 0) out_stat[(size_t)row * S + c] = make_float4(0.f, 0.f, 0.f, __int_as_float(-1));
+    return;
+  }
+  // 4. the chunk's list, sorted (value desc, id asc), zero padded to M
+  if (tid < M) out_cand[((size_t)row * S + c) * M + tid] = tid < Mc ? sel[tid] : 0ull;
+
+  // 5. LSE statistics: the chunk's sum of exp(x/T - m), and the same sum over
+  //    its left-out tokens as the chunk sum minus the selected terms (the
+  //    selected values are the largest, so the difference keeps the tail to
+  //    within rounding of the chunk sum)
+  float s_all = 0.f;
+  const float vm = m * T;                      // the chunk's max value
+  const float l2t = 1.4426950408889634f / T;   // exp(y / T) = exp2(y * log2(e) / T)
+  if (m > -INFINITY) {
+#pragma unroll
+    for (int q = 0; q < PER_THREAD; ++q) s_all += exp2f((x[q] - vm) * l2t);  // -inf pads add 0
+  }
+  s_all = block_sum<TOPM_THREADS>(s_all, red);
+  if (tid == 0) {
+    float s_sel = 0.f;
+    if (m > -INFINITY)
+      for (int i = 0; i < Mc; ++i) s_sel += exp2f((key_f32(cand_key(sel[i])) - vm) * l2t);
+    out_stat[(size_t)row * S + c] = make_float4(m, s_all, fmaxf(s_all - s_sel, 0.f), __int_as_float(Mc));
+  }
+}
+
+// Exact per-chunk selection for the chunks the fast path could not rank
+// (more than FAST_CAP keys at or above its threshold: many equal values).
+// Every other block returns at once.  3-pass radix select (12, 12, 8 bits) of
+// the Mc-th largest key over the chunk in LDS, ties at the threshold taken in
+// id order.
+__global__ __launch_bounds__(TOPM_THREADS) void topm_fallback_kernel(
+    const float* __restrict__ logits, int V, int S, int M, float T,
+    uint64_t* __restrict__ out_cand, float4* __restrict__ out_stat) {
+  const int c = blockIdx.x, row = blockIdx.y;
+  if (__float_as_int(out_stat[(size_t)row * S + c].w) != -1) return;
+  __shared__ uint32_t keys[TOPM_CHUNK];
+  __shared__ uint32_t hist[HBINS];
+  __shared__ uint64_t sel[DT_TOPM_MAX];
+  __shared__ float red[4];
+  __shared__ int ired[4];
+  __shared__ int found_digit, found_above, sel_count, tie_last_s;
+  const int tid = threadIdx.x;
+  const int c0 = c * TOPM_CHUNK;
+  const int len = min(TOPM_CHUNK, V - c0);
+  const int Mc = min(M, len);
+  const float* src = logits + (size_t)row * (size_t)V + c0;
+  float vmax = -INFINITY;
+  for (int i = tid; i < len; i += TOPM_THREADS) {
+    const float x = src[i];
+    keys[i] = f32_key(x);
+    vmax = fmaxf(vmax, x);
+  }
+  const float m = block_max<TOPM_THREADS>(vmax, red) / T;
   uint32_t prefix = 0, pmask = 0;
   int need = Mc;
 #pragma unroll
@@ -76,11 +207,10 @@ __global__ __launch_bounds__(TOPM_THREADS) void topm_chunk_kernel(
     for (int i = tid; i < nb; i += TOPM_THREADS) hist[i] = 0;
     __syncthreads();
     for (int i = tid; i < len; i += TOPM_THREADS) {
-      uint32_t k = keys[i];
+      const uint32_t k = keys[i];
       if ((k & pmask) == prefix) atomicAdd(&hist[(k >> sh) & dmask], 1u);
     }
     __syncthreads();
-    // thread t owns bins [t*per, t*per + per); bins are scanned from the top
     const int per = nb / TOPM_THREADS;
     int mine = 0;
     for (int b = 0; b < per; ++b) mine += (int)hist[tid * per + b];
@@ -99,9 +229,7 @@ __global__ __launch_bounds__(TOPM_THREADS) void topm_chunk_kernel(
     pmask |= dmask << sh;
     __syncthreads();
   }
-  const uint32_t kstar = prefix;  // the Mc-th largest key; `need` of its ties are taken
-
-  // 3. every key above the threshold (order is fixed by the sort below)
+  const uint32_t kstar = prefix;
   if (tid == 0) {
     sel_count = 0;
     tie_last_s = -1;
@@ -112,7 +240,6 @@ __global__ __launch_bounds__(TOPM_THREADS) void topm_chunk_kernel(
     if (k > kstar) sel[atomicAdd(&sel_count, 1)] = cand_pack(k, (uint32_t)(c0 + i));
   }
   __syncthreads();
-  // ties at the threshold: the `need` lowest ids, scanned in id order
   int slot = Mc - need;
   for (int b0 = 0; b0 < len && need > 0; b0 += TOPM_THREADS) {
     const int i = b0 + tid;
@@ -129,23 +256,18 @@ __global__ __launch_bounds__(TOPM_THREADS) void topm_chunk_kernel(
     __syncthreads();
   }
   const int tie_last = tie_last_s;
-
-  // 4. sort the chunk's list (value desc, id asc) in wave 0; pad with zeros
   if (tid < 64) {
     uint64_t v = tid < Mc ? sel[tid] : 0ull;
     v = wave_sort_desc_u64(v);
     if (tid < M) out_cand[((size_t)row * S + c) * M + tid] = v;
   }
-
-  // 5. LSE statistics over the chunk and over its left-out tokens
   float s_all = 0.f, s_tail = 0.f;
   if (m > -INFINITY) {
     for (int i = tid; i < len; i += TOPM_THREADS) {
       const uint32_t k = keys[i];
       const float e = __expf(key_f32(k) / T - m);
       s_all += e;
-      const bool in = k > kstar || (k == kstar && i <= tie_last);
-      if (!in) s_tail += e;
+      if (!(k > kstar || (k == kstar && i <= tie_last))) s_tail += e;
     }
   }
   s_all = block_sum<TOPM_THREADS>(s_all, red);
@@ -253,6 +375,8 @@ hipError_t launch_topm(const float* logits, int rows, int V, int M, float T, uin
                        hipStream_t stream) {
   const int S = topm_chunks(V);
   hipLaunchKernelGGL(topm_chunk_kernel, dim3(S, rows), dim3(TOPM_THREADS), 0, stream, logits, V, S, M,
+                     T, chunk_cand, chunk_stat);
+  hipLaunchKernelGGL(topm_fallback_kernel, dim3(S, rows), dim3(TOPM_THREADS), 0, stream, logits, V, S, M,
                      T, chunk_cand, chunk_stat);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
