@@ -122,11 +122,14 @@ def dt_sync_status(handle: int, stream: int = 0):
     _check(load_library().dt_sync_status(C.c_void_p(handle), C.c_void_p(stream)))
 
 
+PHASES = ["lm_head", "candidates", "P", "mailbox_reset", "tree_kernel"]
+
+
 def dt_phase_times(handle: int) -> tuple:
-    """(mean ms per phase [candidates, P, mailbox reset, tree], builds averaged)."""
-    ms = (C.c_float * 4)()
+    """(mean ms per phase, in PHASES order, builds averaged)."""
+    ms = (C.c_float * len(PHASES))()
     cnt = C.c_int32()
-    _check(load_library().dt_phase_times(C.c_void_p(handle), ms, 4, C.byref(cnt)))
+    _check(load_library().dt_phase_times(C.c_void_p(handle), ms, len(PHASES), C.byref(cnt)))
     return list(ms), cnt.value
 
 
@@ -217,6 +220,7 @@ class TreeBuilder:
         dt_sync_status(self.handle, self.stream.cuda_stream)
 
     def phase_times(self) -> tuple:
-        """Mean [candidates, P, mailbox reset, tree] ms of the DT_TIMING builds
-        since the previous call, and how many builds were averaged."""
+        """Mean ms per phase (lm_head, candidates, P, mailbox_reset,
+        tree_kernel) of the DT_TIMING builds since the previous call, and
+        how many builds were averaged."""
         return dt_phase_times(self.handle)

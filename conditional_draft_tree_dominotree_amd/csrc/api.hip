@@ -50,6 +50,7 @@ struct dt_handle {
   void* w1h_t = nullptr;    // [r, h]
   void* w2t = nullptr;      // [V, r]
   void* wlm_t = nullptr;    // [V, h] or null
+  float* logits = nullptr;  // [max_batch, D, V] base logits computed by the LM head
   int n_tiles = 0;
   // workspace
   uint64_t* chunk_cand = nullptr;
@@ -71,7 +72,8 @@ struct dt_handle {
   size_t act_bytes = 0;
   int max_workers = 0;
   static constexpr int RING = 256;   // timed builds kept for dt_phase_times
-  hipEvent_t ev[RING][5] = {};
+  static constexpr int NPH = 5;       // timed phases
+  hipEvent_t ev[RING][NPH + 1] = {};
   int timed = 0;                      // timed builds since the last dt_phase_times
 };
 
@@ -87,7 +89,7 @@ dt_status dalloc(T** p, size_t bytes) {
 }
 
 void free_all(dt_handle* h) {
-  void* ptrs[] = {h->G,       h->tiles,    h->b_hh,     h->w1h_t, h->w2t,      h->wlm_t,
+  void* ptrs[] = {h->G,       h->tiles,    h->b_hh,     h->w1h_t, h->w2t,      h->wlm_t,  h->logits,
                   h->chunk_cand, h->chunk_stat, h->cand_ids, h->cand_vals, h->tokrank, h->lse,
                   h->tail,    h->P,        h->state,    h->act,   h->gh,       h->u,
                   h->mbox_w,   h->mbox_c,   h->err,   h->nanflag};
@@ -224,6 +226,7 @@ dt_status dt_create(dt_handle** out, const dt_dims* dims, const dt_weights* w, c
   // workspace for max_batch and max_params
   const int S = dt::topm_chunks(V);
   const size_t rows = (size_t)Bm * D;
+  if (h->wlm_t) ALLOC(h->logits, rows * V * sizeof(float));
   ALLOC(h->chunk_cand, rows * S * M * sizeof(uint64_t));
   ALLOC(h->chunk_stat, rows * S * sizeof(float4));
   ALLOC(h->cand_ids, rows * M * sizeof(int32_t));
@@ -285,21 +288,22 @@ dt_status dt_build_trees(dt_handle* h, const dt_inputs* in, const dt_params* p, 
     if (flag) return fail(DT_EINVAL, "base logits contain NaN");
   }
 
-  // a1: per-depth candidates and LSE
+  // a0 (LM head, when no base logits are given), then a1: candidates and LSE
   MARK(0);
-  if (in->base_logits) {
-    HIPCHK(dt::launch_topm(in->base_logits, rows, V, M, p->temperature, h->chunk_cand, h->chunk_stat,
-                           h->cand_ids, h->cand_vals, h->lse, h->tail, h->tokrank, out->cand_ids,
-                           out->cand_logits, out->lse, stream));
-  } else {
-    HIPCHK(dt::launch_lmhead_topm((const uint16_t*)in->hidden, (const uint16_t*)h->wlm_t, rows, V, d.hidden, M,
-                                  p->temperature, h->chunk_cand, h->chunk_stat, stream));
-    HIPCHK(dt::launch_topm_merge(h->chunk_cand, h->chunk_stat, rows, dt::topm_chunks(V), M, p->temperature,
-                                 h->cand_ids, h->cand_vals, h->lse, h->tail, h->tokrank, out->cand_ids,
-                                 out->cand_logits, out->lse, stream));
+  if (!in->base_logits) {
+    // L_base = H W_lm (Domino summary, 方法步骤详情), fp32 accumulate
+    HIPCHK(dt::launch_gemm_bf16((const uint16_t*)in->hidden, nullptr, (const uint16_t*)h->wlm_t, nullptr,
+                                h->logits, rows, V, d.hidden, V, stream));
+  }
+  MARK(1);
+  {
+    const float* logits = in->base_logits ? in->base_logits : h->logits;
+    HIPCHK(dt::launch_topm(logits, rows, V, M, p->temperature, h->chunk_cand, h->chunk_stat, h->cand_ids,
+                           h->cand_vals, h->lse, h->tail, h->tokrank, out->cand_ids, out->cand_logits, out->lse,
+                           stream));
   }
   // a2: P = H W1_H (the path-independent half of W1 [H_d; S])
-  MARK(1);
+  MARK(2);
   if (h->bf16)
     HIPCHK(dt::launch_gemm_bf16((const uint16_t*)in->hidden, nullptr, (const uint16_t*)h->w1h_t, nullptr, h->P,
                                 rows, d.rank, d.hidden, d.rank, stream));
@@ -349,12 +353,12 @@ dt_status dt_build_trees(dt_handle* h, const dt_inputs* in, const dt_params* p, 
   a.spin_limit = 1u << 21;
   const size_t lds = dt::tree_lds_bytes(a, h->bf16);
   if (lds > 160 * 1024) return fail(DT_EUNSUPPORTED, "builder needs %zu bytes of LDS", lds);
-  MARK(2);
+  MARK(3);
   HIPCHK(dt::launch_fill_u32(h->mbox_w, 0u, (size_t)a.n_workers * 32, stream));
   HIPCHK(dt::launch_fill_u32(h->mbox_c, 0u, (size_t)B * 256, stream));
-  MARK(3);
-  HIPCHK(dt::launch_tree(a, h->bf16, lds, stream));
   MARK(4);
+  HIPCHK(dt::launch_tree(a, h->bf16, lds, stream));
+  MARK(5);
   if (timing) ++h->timed;
 #undef MARK
   return DT_OK;
@@ -363,17 +367,17 @@ dt_status dt_build_trees(dt_handle* h, const dt_inputs* in, const dt_params* p, 
 dt_status dt_phase_times(dt_handle* h, float* ms, int n, int32_t* count) {
   if (!h || !ms || !count) return fail(DT_EINVAL, "h, ms and count are required");
   const int nb = h->timed < dt_handle::RING ? h->timed : dt_handle::RING;
-  double sum[4] = {0, 0, 0, 0};
+  double sum[dt_handle::NPH] = {};
   for (int j = 0; j < nb; ++j) {
     hipEvent_t* evs = h->ev[(h->timed - 1 - j) % dt_handle::RING];
-    HIPCHK(hipEventSynchronize(evs[4]));
-    for (int i = 0; i < 4; ++i) {
+    HIPCHK(hipEventSynchronize(evs[dt_handle::NPH]));
+    for (int i = 0; i < dt_handle::NPH; ++i) {
       float t = 0.f;
       HIPCHK(hipEventElapsedTime(&t, evs[i], evs[i + 1]));
       sum[i] += t;
     }
   }
-  for (int i = 0; i < 4 && i < n; ++i) ms[i] = nb ? (float)(sum[i] / nb) : 0.f;
+  for (int i = 0; i < dt_handle::NPH && i < n; ++i) ms[i] = nb ? (float)(sum[i] / nb) : 0.f;
   *count = nb;
   h->timed = 0;
   return DT_OK;

@@ -176,10 +176,3 @@ hipError_t launch_gemm_f32(const float* A, const int32_t* rows, const float* Bt,
 
 }  // namespace dt
 
-namespace dt {
-// The fused LM-head candidate epilogue is not built yet.
-hipError_t launch_lmhead_topm(const uint16_t*, const uint16_t*, int, int, int, int, float, uint64_t*, float4*,
-                              hipStream_t) {
-  return hipErrorNotSupported;
-}
-}  // namespace dt

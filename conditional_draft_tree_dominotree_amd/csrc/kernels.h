@@ -31,11 +31,6 @@ hipError_t launch_gemm_bf16(const uint16_t* A, const int32_t* rows, const uint16
                             float* C, int M, int N, int K, int ldc, hipStream_t stream);
 hipError_t launch_gemm_f32(const float* A, const int32_t* rows, const float* Bt, const float* bias,
                            float* C, int M, int N, int K, int ldc, hipStream_t stream);
-// LM head with the candidate epilogue: logits = H Wt^T never stored; writes the
-// per-(row, 8192-token chunk) candidate lists and LSE statistics that
-// launch_topm_merge consumes.
-hipError_t launch_lmhead_topm(const uint16_t* H, const uint16_t* Wt, int R, int V, int K, int M, float T,
-                              uint64_t* chunk_cand, float4* chunk_stat, hipStream_t stream);
 
 // ---- weight re-layout (prepack.hip)
 // out[c, r] = in[r, c] for a [R, C] matrix of 2- or 4-byte elements

@@ -180,11 +180,11 @@ dt_status dt_sync_status(dt_handle* h, void* stream);
 
 /* Mean durations, in milliseconds, of the phases of the builds made with
  * DT_TIMING since the previous call (at most the last 256 of them), measured
- * with HIP events recorded on each build's stream: ms[0] candidates (top-M +
- * LSE, or the LM head with its candidate epilogue), ms[1] P = H W1_H, ms[2]
- * mailbox reset, ms[3] the tree builder kernel.  Waits for those events,
- * writes min(n, 4) values and the number of builds averaged to *count, then
- * starts a new averaging window.
+ * with HIP events recorded on each build's stream: ms[0] the LM head (0 when
+ * base logits are given), ms[1] per-depth candidates (top-M + LSE), ms[2]
+ * P = H W1_H, ms[3] mailbox reset, ms[4] the tree builder kernel.  Waits for
+ * those events, writes min(n, 5) values and the number of builds averaged to
+ * *count, then starts a new averaging window.
  * Errors: DT_EINVAL (NULL h, ms or count), DT_EHIP. */
 dt_status dt_phase_times(dt_handle* h, float* ms, int n, int32_t* count);
 

@@ -23,7 +23,9 @@ def dev():
 
 @pytest.fixture(scope="module")
 def q8b_builder(dev):
-    spec, w, _ = synth.workload("q8b_b32")
+    # the LM-head workload draws the same Qwen3-8B-shaped head weights (same
+    # seed group) plus W_lm, so one handle serves every q8b workload
+    spec, w, _ = synth.workload("q8b_lm")
     tb = gu.make_builder(spec, w, max_batch=32, max_m=64, max_k=8, max_n=256)
     yield tb
     tb.close()
@@ -86,3 +88,27 @@ def test_q8b_b32_fullv_and_smaller_batch_reuse_handle(dev, q8b_builder):
     small = spec.replace(B=5, norm="fullv", N=96)
     req5 = {k: (v[:5] if v is not None else None) for k, v in req.items()}
     _full_case(small, w, req5, q8b_builder, [0, 4])
+
+
+def test_q8b_lm_pipeline(dev, q8b_builder):
+    from oracle import ref
+    spec, w, req = synth.workload("q8b_lm")
+    got = gu.run(q8b_builder, spec, req)          # base logits from H W_lm on the GPU
+    _check_structure(spec, got)
+    sample = [0, 31]
+    base = np.zeros((spec.B, spec.D, spec.V), np.float32)
+    for b in sample:
+        base[b] = ref.lm_head_logits(req["hidden"][b], w["w_lm"], True)
+    reps, trees = gu.compare(spec, w, req, got, requests=sample, base=base)
+    for b, t in zip(sample, trees):
+        for d, dep in enumerate(t.depths_info):
+            if not np.array_equal(got["cand_ids"][b, d], dep.cand):
+                assert dep.margin < 1e-4, (b, d, dep.margin)   # a near tie at the boundary
+            lse = got["lse"][b, d]
+            assert abs(lse - dep.lse) <= 1e-4 * max(1.0, abs(dep.lse)), (b, d, lse, dep.lse)
+            # the logits behind the candidates: GPU fp32 accumulation vs float64
+            np.testing.assert_allclose(got["cand_logits"][b, d], base[b, d, got["cand_ids"][b, d]],
+                                       rtol=0, atol=1e-4)
+    print(spec.name, gu.summarize(reps))
+    for b, r in zip(sample, reps):
+        assert r.ok, (b, r)
