@@ -235,7 +235,8 @@ dt_status dt_create(dt_handle** out, const dt_dims* dims, const dt_weights* w, c
   ALLOC(h->lse, rows * sizeof(float));
   ALLOC(h->tail, rows * sizeof(float));
   ALLOC(h->P, rows * r * sizeof(float));
-  const size_t nodes = (size_t)Bm * (N + 1);
+  // exchange slots: at most N + 1 steps of at most TREE_MAX_COLS expanded nodes
+  const size_t nodes = (size_t)(N + 1) * dt::TREE_MAX_COLS;
   ALLOC(h->state, nodes * round_up(ds, 32) * sizeof(float));
   h->act_bytes = nodes * round_up(ds, 64) * esz;
   ALLOC(h->act, h->act_bytes);
@@ -351,8 +352,9 @@ dt_status dt_build_trees(dt_handle* h, const dt_inputs* in, const dt_params* p, 
   a.scores = out->scores;
   a.n_nodes = out->n_nodes;
   a.spin_limit = 1u << 21;
-  const size_t lds = dt::tree_lds_bytes(a, h->bf16);
-  if (lds > 160 * 1024) return fail(DT_EUNSUPPORTED, "builder needs %zu bytes of LDS", lds);
+  const char* pops_env = getenv("DT_POPS");
+  const size_t lds = dt::plan_tree(a, h->bf16, pops_env ? atoi(pops_env) : 0);
+  if (lds == 0 || lds > 160 * 1024) return fail(DT_EUNSUPPORTED, "no builder schedule fits this shape in LDS");
   MARK(3);
   HIPCHK(dt::launch_fill_u32(h->mbox_w, 0u, (size_t)a.n_workers * 32, stream));
   HIPCHK(dt::launch_fill_u32(h->mbox_c, 0u, (size_t)B * 256, stream));

@@ -65,6 +65,31 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
   return v;
 }
 
+// Wave-wide max / sum through DPP row shifts (lane 15 of each row gathers its
+// row), then the four row results combined in a fixed order; the result is
+// the same in every lane.
+template <int CTRL>
+__device__ __forceinline__ float dpp_row(float identity, float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(identity), __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float lane_f(float v, int l) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+}
+__device__ __forceinline__ float wave_max_dpp(float v) {
+  v = fmaxf(v, dpp_row<0x111>(-INFINITY, v));  // row_shr:1
+  v = fmaxf(v, dpp_row<0x112>(-INFINITY, v));  // row_shr:2
+  v = fmaxf(v, dpp_row<0x114>(-INFINITY, v));  // row_shr:4
+  v = fmaxf(v, dpp_row<0x118>(-INFINITY, v));  // row_shr:8
+  return fmaxf(fmaxf(lane_f(v, 15), lane_f(v, 31)), fmaxf(lane_f(v, 47), lane_f(v, 63)));
+}
+__device__ __forceinline__ float wave_sum_dpp(float v) {
+  v += dpp_row<0x111>(0.f, v);
+  v += dpp_row<0x112>(0.f, v);
+  v += dpp_row<0x114>(0.f, v);
+  v += dpp_row<0x118>(0.f, v);
+  return (lane_f(v, 15) + lane_f(v, 31)) + (lane_f(v, 47) + lane_f(v, 63));
+}
+
 // Sort one value per lane of a wave in descending order (bitonic network).
 __device__ __forceinline__ uint64_t wave_sort_desc_u64(uint64_t v) {
   const int lane = threadIdx.x & 63;

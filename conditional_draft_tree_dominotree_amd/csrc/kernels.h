@@ -52,6 +52,13 @@ struct TreeArgs {
   int n_workers;        // worker blocks; block ids [0, n_workers) are workers
   int tiles_per_worker;
   int n_tiles;          // (3 ds + r) / 16
+  // schedule (set by plan_tree)
+  int p;                // nodes a request may expand per step (exchange columns per request)
+  int kc;               // state elements a worker stages per phase (kp / kc phases)
+  int xcap;             // node records per request (budget + root + speculation room)
+  int fcap;             // frontier entries per request
+  int qmax;             // frontier entries tested per pop round
+  int nslots;           // depth slots of W2 candidate rows in a controller's LDS
   // read-only inputs
   const void* tiles;       // packed [W_hh ; W1_S^T] tiles
   const float* b_hh;       // [3 ds] or NULL
@@ -63,11 +70,11 @@ struct TreeArgs {
   const float* tail;       // [B, D]
   const int32_t* tokrank;  // [B, D, M]
   const float* root;       // [B, ds] or NULL
-  // write-once exchange buffers; act, gh and u are step-major: [step][request]
-  float* state;            // [B, N + 1, ds] by node
-  void* act;               // [N + 1, B, ds] GEMM operand copy of the expanded state (wdtype)
-  float* gh;               // [N + 1, B, 3 ds]
-  float* u;                // [N + 1, B, r]
+  // write-once exchange slots, step-major: slot (t, b, j) = (t B + b) p + j
+  float* state;            // [slots, ds] fp32 GRU state of the node expanded in the slot
+  void* act;               // [slots, ds] its GEMM operand copy (wdtype)
+  float* gh;               // [slots, 3 ds]
+  float* u;                // [slots, r]
   uint32_t* mbox_w;        // [n_workers][32] controller -> worker mailboxes (one line each)
   uint32_t* mbox_c;        // [B][256] worker -> controller mailboxes
   int* err;                // device error word
@@ -76,7 +83,11 @@ struct TreeArgs {
   float* scores;
   unsigned spin_limit;
 };
+// Exchange columns a build may use per step (slots per step = B p <= this).
+constexpr int TREE_MAX_COLS = 64;
+// Fills the schedule fields of `a` (p from `pops`, 0 = automatic) and returns
+// the dynamic LDS bytes the launch needs, or 0 if the shape cannot be served.
+size_t plan_tree(TreeArgs& a, int wdtype_bf16, int pops);
 hipError_t launch_tree(const TreeArgs& a, int wdtype_bf16, size_t lds_bytes, hipStream_t stream);
-size_t tree_lds_bytes(const TreeArgs& a, int wdtype_bf16);
 
 }  // namespace dt

@@ -1,27 +1,43 @@
 // The conditional best-first tree builder: one persistent cooperative kernel.
 //
 // Method (DominoTree technical summary, Componenti Core 1, 2 and 4; Domino
-// summary, 核心方法): per request, pop the frontier node with the highest
-// cumulative log-prob, advance the GRU causal state along that node's path,
-// correct the next depth's M candidate logits with W2[:, cand] SiLU(W1 [H; S]),
-// log-softmax them, push the k best children; stop after N pops.
+// summary, 核心方法): per request, repeatedly take the frontier node with the
+// highest cumulative log-prob, advance the GRU causal state along that node's
+// path, correct the next depth's M candidate logits with
+// W2[:, cand] SiLU(W1 [H; S]), log-softmax them and push the k best children,
+// until N nodes have been taken.
+//
+// The tree this returns is the one the one-node-at-a-time loop returns: its N
+// nodes are the N best nodes of the whole k-restricted tree under the total
+// order (score desc, depth asc, token asc, parent's order asc), because a
+// child always comes after its parent in that order.  The kernel uses this to
+// expand up to p frontier nodes of a request per step instead of one:
+//   * a frontier entry f is taken into the request's record set X only if
+//     fewer than N + 1 records of X (the root included) precede it in the
+//     total order (otherwise it, and everything after it, can never be among
+//     the N best: X only grows);
+//   * the first node taken in a step is always one of the N best (every node
+//     that precedes it is already in X); the others are speculative and may
+//     later be pushed out by descendants of earlier ones;
+//   * the build ends when the frontier holds no entry that passes the test;
+//     the output is X ranked by the total order, cut after N + 1 records.
+// Speculation changes how much work is done, never the result.
 //
 // Roles (blocks of 256 threads, one per CU, launched cooperatively so that all
 // are resident):
 //   * worker blocks [0, n_workers): each keeps `tiles_per_worker` 16-row tiles
 //     of the per-node product Wc = [W_hh ; W1_S^T] ((3 d_s + r) x d_s) in LDS
 //     for the whole launch.  Each step it multiplies its rows by the GEMM
-//     operand copy of the states of the nodes being expanded (one column per
-//     request) with MFMA, and publishes gh = W_hh S~ + b_hh and u = W1_S^T S~.
+//     operand copies of the states expanded in that step (one column per
+//     expanded node) with MFMA, and publishes gh = W_hh S~ + b_hh and
+//     u = W1_S^T S~.
 //   * controller blocks [n_workers, n_workers + B): one per request.  It keeps
-//     the request's candidates, node records and frontier in LDS; scores the
-//     children of the node just expanded (a = SiLU(u + P_d), dL on the M
-//     candidate columns of W2, log-softmax, top-k), pushes them, pops the next
-//     node, and advances the GRU state for it elementwise from
-//     G[token] = W_ih E[token] + b_ih (a table folded once per handle) and its
-//     parent's gh.
-// The GRU input product never runs per node, and the per-node weights never
-// leave LDS; each step moves only states (d_s), gh (3 d_s) and u (r) per request.
+//     the request's candidates, node records and sorted frontier in LDS;
+//     scores the children of the nodes expanded in the step
+//     (a = SiLU(u + P_d), dL on the M candidate columns of W2, log-softmax,
+//     top-k), merges them into the frontier, takes the next nodes, and
+//     advances their GRU states elementwise from G[token] = W_ih E[token] +
+//     b_ih (a table folded once per handle) and their parents' gh.
 //
 // Exchange between blocks: every published value is written once per launch
 // to its own 128-byte-aligned slot with device-scope (sc1) stores; after the
@@ -30,12 +46,20 @@
 // and then reads the published slots.  Slots are never read before they are
 // published, so no cache holds a stale copy.  Every wait is bounded: when it
 // runs out the block sets the error word and leaves its loop.
+#include <algorithm>
+
 #include "common.h"
 #include "kernels.h"
 
 namespace dt {
 
 constexpr uint32_t MBOX_DONE = 0xFFFFFFFFu;
+constexpr int PMAX = 16;     // nodes per request per step
+constexpr int QCAP = 32;     // frontier entries tested per pop round
+constexpr int FCAPMAX = 6144;  // frontier entries per request
+constexpr int XMAX = 2047;   // records per request (11-bit parent field)
+constexpr int PPW = 2;       // (tile, column block) pairs per worker wave
+constexpr int GA = 4;        // states advanced together per controller thread
 
 // ---------------------------------------------------------------------------
 // device-scope memory operations
@@ -109,24 +133,39 @@ __host__ __device__ inline int gh_stride(int ds) { return round_up(3 * ds, 32); 
 __host__ __device__ inline int u_stride(int r) { return round_up(r, 32); }         // floats
 constexpr int STAGE_PAD = 8;  // extra elements per staged column (LDS bank spread)
 
-// frontier key: score | 31-depth | 63-tokrank | 1023-parent | slot
-__device__ __forceinline__ uint64_t make_key(float score, int depth, int tokrank, int parent, int slot) {
-  return ((uint64_t)f32_key(score) << 32) | ((uint64_t)(31 - depth) << 27) |
-         ((uint64_t)(63 - tokrank) << 21) | ((uint64_t)(1023 - parent) << 11) | ((uint64_t)slot << 5);
+// exchange slot of the j-th node a request expands at step t
+__device__ __forceinline__ size_t slot_of(const TreeArgs& a, int t, int b, int j) {
+  return ((size_t)t * a.B + b) * a.p + j;
 }
+
+// Frontier entry / record key, larger = earlier in the total order:
+//   [63:32] score | [31:27] 31 - depth | [26:21] 63 - token rank |
+//   [20:10] parent record | [9:4] candidate slot m
+// The upper 43 bits (score, depth, token) decide the order except between
+// nodes of equal score at the same depth with the same token, which the
+// parents' order decides (rec_better).  The parent field of a record's own key
+// goes stale when records are renumbered; rpar holds the current one.
+__device__ __forceinline__ uint64_t make_key(float score, int depth, int tokrank, int parent, int m) {
+  return ((uint64_t)f32_key(score) << 32) | ((uint64_t)(31 - depth) << 27) | ((uint64_t)(63 - tokrank) << 21) |
+         ((uint64_t)parent << 10) | ((uint64_t)m << 4);
+}
+__device__ __forceinline__ uint64_t key_u(uint64_t k) { return k >> 21; }
 __device__ __forceinline__ float key_score(uint64_t k) { return key_f32((uint32_t)(k >> 32)); }
 __device__ __forceinline__ int key_depth(uint64_t k) { return 31 - (int)((k >> 27) & 31); }
-__device__ __forceinline__ int key_parent(uint64_t k) { return 1023 - (int)((k >> 11) & 1023); }
-__device__ __forceinline__ int key_slot(uint64_t k) { return (int)((k >> 5) & 63); }
+__device__ __forceinline__ int key_parent(uint64_t k) { return (int)((k >> 10) & 2047); }
+__device__ __forceinline__ int key_m(uint64_t k) { return (int)((k >> 4) & 63); }
+__device__ __forceinline__ uint64_t key_with_parent(uint64_t k, int parent) {
+  return (k & ~(2047ull << 10)) | ((uint64_t)parent << 10);
+}
 
-// bounded wait on the words of one mailbox line; wave-uniform
-__device__ __forceinline__ bool wait_mbox(const uint32_t* box, int nwords, uint32_t epoch, const int* err,
-                          unsigned limit) {
+// bounded wait until every word of one mailbox line is >= need; wave-uniform
+__device__ __forceinline__ bool wait_mbox(const uint32_t* box, int nwords, uint32_t need, const int* err,
+                                          unsigned limit) {
   const int lane = threadIdx.x & 63;
   unsigned it = 0;
   while (true) {
     bool ok = true;
-    for (int i = lane; i < nwords; i += 64) ok &= ld_dev_u32(box + i) >= epoch;
+    for (int i = lane; i < nwords; i += 64) ok &= ld_dev_u32(box + i) >= need;
     if (__all(ok)) return true;
     if ((++it & 255) == 0) {
       if (ld_dev_u32(err) != 0) return false;
@@ -139,20 +178,22 @@ __device__ __forceinline__ bool wait_mbox(const uint32_t* box, int nwords, uint3
   }
 }
 
+// controller -> worker mailbox word: step epoch in the high bits, nodes expanded
+// by the request in that step in the low 5
+__device__ __forceinline__ uint32_t mbox_word(int epoch, int e) { return ((uint32_t)epoch << 5) | (uint32_t)e; }
+
 // ---------------------------------------------------------------------------
 // worker: per-step product of its Wc tiles with the expanded nodes' states
 
-template <typename W>
-struct WorkerLds {
-  // tiles [tpw][kp/32][4][16][8] elements, then the staged columns [32][kp + STAGE_PAD]
-  static size_t bytes(int tpw, int kp) {
-    return (size_t)tpw * 16 * kp * sizeof(W) + (size_t)32 * (kp + STAGE_PAD) * sizeof(W) + 1024;
-  }
-};
-
-// Exchange slots are step-major: the column request b publishes at step t
-// lives in slot t * B + b of act, gh and u.
-__device__ __forceinline__ size_t slot_of(const TreeArgs& a, int t, int b) { return (size_t)t * a.B + b; }
+// LDS: tiles [tpw][kp/32][4][16][8] elements, staged columns
+// [round_up(cols, 16)][kc + STAGE_PAD], then the column tables
+__host__ __device__ inline size_t worker_stage_offset(int tpw, int kp, int esz) {
+  return (size_t)tpw * 16 * kp * esz;
+}
+__host__ __device__ inline size_t worker_lds_bytes(int tpw, int kp, int kc, int cols, int esz) {
+  return worker_stage_offset(tpw, kp, esz) + (size_t)round_up(cols, 16) * (kc + STAGE_PAD) * esz +
+         (size_t)(2 * TREE_MAX_COLS + 64) * 4;
+}
 
 __device__ __forceinline__ void worker_store_out(const TreeArgs& a, size_t slot, int row, float v) {
   const int ds3 = 3 * a.ds;
@@ -163,102 +204,146 @@ __device__ __forceinline__ void worker_store_out(const TreeArgs& a, size_t slot,
   }
 }
 
+// Copy elements [k0, k0 + kc) of each active column's operand into the stage.
+// Thread tid owns 16-byte piece tid % per of columns tid / per + j * cpt;
+// every load of a batch is issued before any LDS store.
 template <typename W>
-__device__ __forceinline__ void worker_compute(const TreeArgs& a, const W* tiles_lds, const W* stage, int ncols,
-                               const int* colb, const int* coln, int my_tile0, int my_ntiles, int kp);
-
-// bf16: MFMA 16x16x32; wave w takes (tile, column block) pairs w, w+4, ...
-template <>
-__device__ __forceinline__ void worker_compute<uint16_t>(const TreeArgs& a, const uint16_t* tiles_lds, const uint16_t* stage,
-                                         int ncols, const int* colb, const int* coln, int my_tile0,
-                                         int my_ntiles, int kp) {
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  const int nkb = kp / 32;
-  const int ncb = (ncols + 15) / 16;
-  const int kps = kp + STAGE_PAD;
-  for (int pair = wv; pair < my_ntiles * ncb; pair += 4) {
-    const int tt = pair / ncb, cb = pair % ncb;
-    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-    const uint16_t* wt = tiles_lds + (size_t)tt * 16 * kp;
-    const int col = cb * 16 + (lane & 15);
-    const uint16_t* sc = stage + (size_t)col * kps + 8 * (lane >> 4);
-    // two independent accumulation chains, 4 k blocks in flight
-    floatx4 acc2 = {0.f, 0.f, 0.f, 0.f};
-    int kb = 0;
-    for (; kb + 4 <= nkb; kb += 4) {
-      bf16x8 av[4], bv[4];
+__device__ __forceinline__ void worker_stage(const TreeArgs& a, W* stage, const int* coln, int ncols, int k0,
+                                             int kc) {
+  const int tid = threadIdx.x;
+  const int as = act_stride(a.ds);
+  const int kcs = kc + STAGE_PAD;
+  const int per = kc * (int)sizeof(W) / 16;  // 16-byte pieces per column
+  const W* act = reinterpret_cast<const W*>(a.act);
+  if (per <= 256 && 256 % per == 0) {
+    const int cpt = 256 / per;  // columns per pass
+    const int pc = tid % per, c0 = tid / per;
+    constexpr int U = 16;
+    for (int cb = 0; cb < ncols; cb += U * cpt) {
+      uint4 v[U];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        av[q] = *reinterpret_cast<const bf16x8*>(wt + ((size_t)(kb + q) * 64 + lane) * 8);
-        bv[q] = *reinterpret_cast<const bf16x8*>(sc + (kb + q) * 32);
+      for (int q = 0; q < U; ++q) {  // clamped: every lane loads a valid piece
+        const int c = min(cb + c0 + q * cpt, ncols - 1);
+        v[q] = reinterpret_cast<const uint4*>(act + (size_t)coln[c] * as + k0)[pc];
       }
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[0], bv[0], acc, 0, 0, 0);
-      acc2 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[1], bv[1], acc2, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[2], bv[2], acc, 0, 0, 0);
-      acc2 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[3], bv[3], acc2, 0, 0, 0);
+      // unconditional stores (a clamped duplicate rewrites identical data),
+      // so that no load is sunk into a guarded block and serialised
+#pragma unroll
+      for (int q = 0; q < U; ++q) {
+        const int c = min(cb + c0 + q * cpt, ncols - 1);
+        *reinterpret_cast<uint4*>(stage + (size_t)c * kcs + pc * (16 / sizeof(W))) = v[q];
+      }
     }
-    for (; kb < nkb; ++kb) {
-      const bf16x8 av = *reinterpret_cast<const bf16x8*>(wt + ((size_t)kb * 64 + lane) * 8);
-      const bf16x8 bv = *reinterpret_cast<const bf16x8*>(sc + kb * 32);
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, acc, 0, 0, 0);
+  } else {
+    for (int i = tid; i < ncols * per; i += blockDim.x) {
+      const int c = i / per, pc = i % per;
+      *reinterpret_cast<uint4*>(stage + (size_t)c * kcs + pc * (16 / sizeof(W))) =
+          reinterpret_cast<const uint4*>(act + (size_t)coln[c] * as + k0)[pc];
     }
-    acc += acc2;
-    // lane holds column (lane & 15), rows 4 (lane >> 4) + i of the tile
-    if (col < ncols) {
-      const size_t slot = (size_t)coln[col];
-      const int row0 = (my_tile0 + tt) * 16 + 4 * (lane >> 4);
-      const int ds3 = 3 * a.ds;
-      if (row0 + 3 < ds3 && (ds3 & 3) == 0) {
-        const float* bh = a.b_hh;
-        floatx4 v = acc;
-        if (bh) {
-          v[0] += bh[row0];
-          v[1] += bh[row0 + 1];
-          v[2] += bh[row0 + 2];
-          v[3] += bh[row0 + 3];
+  }
+}
+
+// bf16: MFMA 16x16x32 over the k blocks [kb0, kb0 + nkb) staged in this phase;
+// wave w owns (tile, column block) pairs w, w + 4, ... (at most PPW)
+__device__ __forceinline__ void worker_mfma_phase(const uint16_t* tiles_lds, const uint16_t* stage, int kp,
+                                                  int kb0, int nkb, int kcs, int ncb, int pairs,
+                                                  floatx4 (&acc)[PPW][2]) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+#pragma unroll
+  for (int i = 0; i < PPW; ++i) {
+    const int pair = wv + 4 * i;
+    if (pair < pairs) {
+      const int tt = pair / ncb, cb = pair - tt * ncb;
+      const uint16_t* wt = tiles_lds + (size_t)tt * 16 * kp + (size_t)kb0 * 512;
+      const uint16_t* sc = stage + (size_t)(cb * 16 + (lane & 15)) * kcs + 8 * (lane >> 4);
+      int kb = 0;
+      for (; kb + 4 <= nkb; kb += 4) {
+        bf16x8 av[4], bv[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          av[q] = *reinterpret_cast<const bf16x8*>(wt + ((size_t)(kb + q) * 64 + lane) * 8);
+          bv[q] = *reinterpret_cast<const bf16x8*>(sc + (kb + q) * 32);
         }
-        st_dev_f32x4(a.gh + slot * gh_stride(a.ds) + row0, v);
-      } else {
-        for (int i = 0; i < 4; ++i) worker_store_out(a, slot, row0 + i, acc[i]);
+        acc[i][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[0], bv[0], acc[i][0], 0, 0, 0);
+        acc[i][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[1], bv[1], acc[i][1], 0, 0, 0);
+        acc[i][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[2], bv[2], acc[i][0], 0, 0, 0);
+        acc[i][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[3], bv[3], acc[i][1], 0, 0, 0);
+      }
+      for (; kb < nkb; ++kb) {
+        const bf16x8 av = *reinterpret_cast<const bf16x8*>(wt + ((size_t)kb * 64 + lane) * 8);
+        const bf16x8 bv = *reinterpret_cast<const bf16x8*>(sc + kb * 32);
+        acc[i][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, acc[i][0], 0, 0, 0);
       }
     }
   }
 }
 
-// fp32: one (row, column) dot product per thread over the padded k
-template <>
-__device__ __forceinline__ void worker_compute<float>(const TreeArgs& a, const float* tiles_lds, const float* stage, int ncols,
-                                      const int* colb, const int* coln, int my_tile0, int my_ntiles,
-                                      int kp) {
-  const int kps = kp + STAGE_PAD;
-  const int total = my_ntiles * 16 * ncols;
+__device__ __forceinline__ void worker_epilogue_bf16(const TreeArgs& a, const int* coln, int ncols, int tile0,
+                                                     int ncb, int pairs, floatx4 (&acc)[PPW][2]) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int ds3 = 3 * a.ds;
+#pragma unroll
+  for (int i = 0; i < PPW; ++i) {
+    const int pair = wv + 4 * i;
+    if (pair < pairs) {
+      const int tt = pair / ncb, cb = pair - tt * ncb;
+      const int col = cb * 16 + (lane & 15);
+      // lane holds column (lane & 15), rows 4 (lane >> 4) + q of the tile
+      if (col < ncols) {
+        const floatx4 s = acc[i][0] + acc[i][1];
+        const size_t slot = (size_t)coln[col];
+        const int row0 = (tile0 + tt) * 16 + 4 * (lane >> 4);
+        if (row0 + 3 < ds3 && (ds3 & 3) == 0) {
+          const float* bh = a.b_hh;
+          floatx4 v = s;
+          if (bh) {
+            v[0] += bh[row0];
+            v[1] += bh[row0 + 1];
+            v[2] += bh[row0 + 2];
+            v[3] += bh[row0 + 3];
+          }
+          st_dev_f32x4(a.gh + slot * gh_stride(a.ds) + row0, v);
+        } else {
+          for (int q = 0; q < 4; ++q) worker_store_out(a, slot, row0 + q, s[q]);
+        }
+      }
+    }
+  }
+}
+
+// fp32: one (row, column) dot product per thread over the staged k (one phase)
+__device__ __forceinline__ void worker_compute_f32(const TreeArgs& a, const float* tiles_lds, const float* stage,
+                                                   int ncols, const int* coln, int tile0, int ntiles, int kp,
+                                                   int kcs) {
+  const int total = ntiles * 16 * ncols;
   for (int idx = threadIdx.x; idx < total; idx += blockDim.x) {
     const int col = idx % ncols;
     const int rr = (idx / ncols) % 16;
     const int tt = idx / (ncols * 16);
     const float* wt = tiles_lds + (size_t)tt * 16 * kp;
-    const float* sc = stage + (size_t)col * kps;
+    const float* sc = stage + (size_t)col * kcs;
     float s = 0.f;
     for (int k = 0; k < kp; ++k) {
       const int kb = k >> 5, kg = (k >> 3) & 3, e = k & 7;
       s = fmaf(wt[(((size_t)kb * 4 + kg) * 16 + rr) * 8 + e], sc[k], s);
     }
-    worker_store_out(a, (size_t)coln[col], (my_tile0 + tt) * 16 + rr, s);
+    worker_store_out(a, (size_t)coln[col], (tile0 + tt) * 16 + rr, s);
   }
 }
 
 template <typename W>
 __device__ __forceinline__ void worker_main(const TreeArgs& a, unsigned char* lds) {
   const int w = blockIdx.x;
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63;
   const int kp = k_padded(a.ds);
+  const int kc = a.kc, kcs = kc + STAGE_PAD;
   const int tile0 = w * a.tiles_per_worker;
   const int ntiles = max(0, min(a.tiles_per_worker, a.n_tiles - tile0));
   W* tiles_lds = reinterpret_cast<W*>(lds);
-  W* stage = tiles_lds + (size_t)a.tiles_per_worker * 16 * kp;
-  int* colb = reinterpret_cast<int*>(stage + (size_t)32 * (kp + STAGE_PAD));
-  int* coln = colb + 32;
-  int* ncols_s = coln + 32;
+  W* stage = reinterpret_cast<W*>(lds + worker_stage_offset(a.tiles_per_worker, kp, (int)sizeof(W)));
+  int* coln = reinterpret_cast<int*>(stage + (size_t)round_up(a.B * a.p, 16) * kcs);
+  int* reqs = coln + TREE_MAX_COLS;  // requests with work this step
+  int* misc = reqs + TREE_MAX_COLS;  // [0] columns (-1: failed), [1] requests
 
   // the block's Wc tiles stay in LDS for the whole launch
   {
@@ -271,356 +356,828 @@ __device__ __forceinline__ void worker_main(const TreeArgs& a, unsigned char* ld
   __syncthreads();
 
   const uint32_t* mybox = a.mbox_w + (size_t)w * 32;
-  const int as = act_stride(a.ds);
-  const int kps = kp + STAGE_PAD;
   for (int t = 0;; ++t) {
     const uint32_t epoch = (uint32_t)t + 1u;
+    // wave 0: wait for every request's word of this step, then list the columns
     if (tid < 64) {
-      bool ok = wait_mbox(mybox, a.B, epoch, a.err, a.spin_limit);
-      if (tid == 0) *ncols_s = ok ? 0 : -1;
-    }
-    __syncthreads();
-    if (*ncols_s < 0) return;
-    // active columns: requests whose controller has not finished
-    if (tid < 64) {
-      const int b = tid;
-      const bool act = b < a.B && ld_dev_u32(mybox + b) != MBOX_DONE;
-      const unsigned long long m = __ballot(act);
-      if (act) {
-        const int c = __popcll(m & ((1ull << tid) - 1ull));
-        colb[c] = b;
-        coln[c] = (int)slot_of(a, t, b);  // exchange slot of this column
+      const bool ok = wait_mbox(mybox, a.B, epoch << 5, a.err, a.spin_limit);
+      const int b = lane;
+      uint32_t word = 0;
+      if (ok && b < a.B) word = ld_dev_u32(mybox + b);
+      const int e = (ok && b < a.B && word != MBOX_DONE) ? (int)(word & 31u) : 0;
+      // exclusive prefix of e over the lanes
+      int incl = e;
+      for (int d = 1; d < 64; d <<= 1) {
+        const int y = __shfl_up(incl, d);
+        if (lane >= d) incl += y;
       }
-      if (tid == 0) *ncols_s = __popcll(m);
+      const int base = incl - e;
+      for (int j = 0; j < e; ++j) coln[base + j] = (int)slot_of(a, t, b, j);
+      const unsigned long long has = __ballot(e > 0);
+      if (e > 0) reqs[__popcll(has & ((1ull << lane) - 1ull))] = b;
+      if (lane == 63) misc[0] = ok ? incl : -1;
+      if (lane == 0) misc[1] = __popcll(has);
     }
     __syncthreads();
-    const int ncols = *ncols_s;
-    if (ncols == 0) return;  // every request is finished
-    // stage the GEMM operand copies of the expanded states (published, read
-    // once).  Thread tid owns piece tid % per of columns tid / per + j * cpt;
-    // every load of a round is issued before any LDS store.
-    {
-      const int per = kp * (int)sizeof(W) / 16;  // 16-byte pieces per column
-      if (per <= 256 && 256 % per == 0) {
-        const int cpt = 256 / per;                 // columns per pass
-        const int pc = tid % per, c0 = tid / per;
-        constexpr int U = 16;
-        for (int cb = 0; cb < ncols; cb += U * cpt) {
-          uint4 v[U];
+    const int ncols = misc[0], nreq = misc[1];
+    if (ncols <= 0) return;  // a wait ran out, or every request is finished
+    const int ncb = (ncols + 15) / 16;
+    if constexpr (sizeof(W) == 2) {
+      const int pairs = ntiles * ncb;
+      floatx4 acc[PPW][2];
 #pragma unroll
-          for (int q = 0; q < U; ++q) {  // clamped: every lane loads a valid piece
-            const int c = min(cb + c0 + q * cpt, ncols - 1);
-            v[q] = reinterpret_cast<const uint4*>(reinterpret_cast<const W*>(a.act) + (size_t)coln[c] * as)[pc];
-          }
-          // unconditional stores (a clamped duplicate rewrites identical data),
-          // so that no load is sunk into a guarded block and serialised
-#pragma unroll
-          for (int q = 0; q < U; ++q) {
-            const int c = min(cb + c0 + q * cpt, ncols - 1);
-            *reinterpret_cast<uint4*>(stage + (size_t)c * kps + pc * (16 / sizeof(W))) = v[q];
-          }
-        }
-      } else {
-        for (int i = tid; i < ncols * per; i += blockDim.x) {
-          const int c = i / per, pc = i % per;
-          *reinterpret_cast<uint4*>(stage + (size_t)c * kps + pc * (16 / sizeof(W))) =
-              reinterpret_cast<const uint4*>(reinterpret_cast<const W*>(a.act) + (size_t)coln[c] * as)[pc];
-        }
+      for (int i = 0; i < PPW; ++i) acc[i][0] = acc[i][1] = floatx4{0.f, 0.f, 0.f, 0.f};
+      for (int k0 = 0; k0 < kp; k0 += kc) {
+        if (k0 > 0) __syncthreads();  // the previous phase's operands are consumed
+        worker_stage<W>(a, stage, coln, ncols, k0, kc);
+        __syncthreads();
+        worker_mfma_phase(reinterpret_cast<const uint16_t*>(tiles_lds), reinterpret_cast<const uint16_t*>(stage),
+                          kp, k0 / 32, kc / 32, kcs, ncb, pairs, acc);
       }
+      worker_epilogue_bf16(a, coln, ncols, tile0, ncb, pairs, acc);
+    } else {
+      worker_stage<W>(a, stage, coln, ncols, 0, kc);  // kc == kp for fp32
+      __syncthreads();
+      worker_compute_f32(a, reinterpret_cast<const float*>(tiles_lds), reinterpret_cast<const float*>(stage),
+                         ncols, coln, tile0, ntiles, kp, kcs);
     }
-    __syncthreads();
-    if (ntiles > 0) worker_compute<W>(a, tiles_lds, stage, ncols, colb, coln, tile0, ntiles, kp);
     stores_done();
     __syncthreads();
     // tell each active request's controller that this worker's rows are out
-    if (tid < ncols) st_dev_u32(a.mbox_c + (size_t)colb[tid] * 256 + w, epoch);
+    if (tid < nreq) st_dev_u32(a.mbox_c + (size_t)reqs[tid] * 256 + w, epoch);
     stores_done();
     __syncthreads();
   }
 }
 
 // ---------------------------------------------------------------------------
-// controller: one request's candidates, frontier, node records and GRU states
+// controller: one request's candidates, records, frontier and GRU states
 
-struct CtlLds {
-  int* cid;        // [D*M]
-  float* cval;     // [D*M]
-  int* crank;      // [D*M]
-  float* tailv;    // [D]
-  uint64_t* front; // [fcap]
-  int* ntok;       // [N+1]
-  int* npar;
-  int* ndep;
-  int* nstep;      // [N+1] step at which a node was expanded
-  float* nscore;
-  float* av;       // [r]
-  void* w2s;       // [M][r] candidate rows of W2 for the next expansion (wdtype)
-  float* ps;       // [r] P row of the next expansion
-  float* z;        // [64]
-  float* logp;     // [64]
-  int* okf;        // [64]
-  int* misc;       // [16]
-  uint64_t* red64; // [4]
-  int* redpos;     // [4]
-  float* redf;     // [4]
+#define LDS
+
+enum {
+  C_NF,      // frontier entries [fh, nf) of buffer fb
+  C_FH,
+  C_FB,
+  C_NX,      // records
+  C_E,       // nodes to expand in the next step
+  C_OK,
+  C_TAUSET,  // frontier entries with key_u < tau are known to be out
+  C_STOP,
+  C_NL,      // depth slots to load
+  C_G,       // where the best entry of an over-long tie group came from
+  C_NV,      // live new entries of a merge
+  C_MISC
 };
 
-__host__ __device__ inline size_t ctl_lds_bytes(int D, int M, int N, int r, int fcap, int esz) {
-  size_t s = (size_t)M * r * esz + (size_t)r * 4 + 32;  // w2s, ps
-  s += (size_t)fcap * 8;              // front (first: 8-byte aligned)
-  s += (size_t)D * M * 4 * 3 + D * 4; // cid, cval, crank, tailv
-  s += (size_t)(N + 1) * 4 * 5;       // node records
-  s += (size_t)r * 4 + 64 * 4 * 3;    // av, z, logp, okf
-  s += 16 * 4 + 4 * 8 + 4 * 4 + 4 * 4 + 64;
-  return s;
+// LDS arrays of a controller (32-bit LDS addresses)
+struct CtlLds {
+  LDS int* cid;         // [D*M] candidate token ids
+  LDS float* cval;      // [D*M] their base logits
+  LDS int* crank;       // [D*M] rank of each candidate's token id within its depth
+  LDS float* tailv;     // [D]
+  LDS uint64_t* rkey;   // [xcap] record keys; record 0 is the root
+  LDS int* rpar;        // [xcap] parent record (-1 for the root)
+  LDS int* rslot;       // [xcap] exchange slot holding the record's state (-1: not expanded)
+  LDS int* rrank;       // [xcap] position in the total order (compaction and output)
+  LDS uint64_t* trk;    // [xcap] compaction staging
+  LDS int* trp;         // [xcap]
+  LDS int* trs;         // [xcap]
+  LDS uint64_t* front;  // [2][fcap] frontier keys, sorted descending, in buffer misc[C_FB]
+  LDS uint64_t* nc;     // [p*k] children keys of this step (0 = none)
+  LDS uint64_t* ncs;    // [p*k] live children sorted descending
+  LDS int* pn;          // [p*k] their insertion points in the frontier
+  LDS unsigned char* w2s;  // [nslots][M][r + pad] W2 rows of the candidates of each slot's depth
+  LDS float* ps;        // [nslots][r] P rows
+  LDS int* wdep;        // [nslots] depth held by each slot (-1: none)
+  LDS int* wclaim;      // [nslots] slot used by a node of the next step
+  LDS int* lslots;      // [nslots] slots to load before the next step
+  LDS int* ex_rec;      // [p] records expanded in the step
+  LDS int* ex_ws;       // [p] their depth slots
+  LDS int* ex_dep;      // [p] their depths
+  LDS int* ex_tok;      // [p] their tokens
+  LDS int* ex_src;      // [p] exchange slots of their parents
+  LDS float* av;        // [p][r] SiLU(u + P)
+  LDS float* z;         // [p][64] corrected, tempered candidate logits
+  LDS int* cnt;         // [QCAP] records ahead of each tested frontier entry
+  LDS int* perm;        // [QCAP] tested entries in the total order
+  LDS int* acc;         // [QCAP] tested entries taken
+  LDS int* misc;        // [C_MISC]
+  LDS uint64_t* tau;    // [1]
+};
+
+enum {
+  L_CID, L_CVAL, L_CRANK, L_TAIL, L_RKEY, L_RPAR, L_RSLOT, L_RRANK, L_TRK, L_TRP, L_TRS, L_FRONT, L_NC, L_NCS,
+  L_PN, L_W2S, L_PS, L_WDEP, L_WCLAIM, L_LSLOTS, L_EXREC, L_EXWS, L_EXDEP, L_EXTOK, L_EXSRC, L_AV, L_Z, L_CNT,
+  L_PERM, L_ACC, L_MISC, L_TAU, L_COUNT
+};
+
+// elements per LDS row of W2 candidate weights: r plus 16 bytes, so that the
+// rows of consecutive candidates start in different banks
+__host__ __device__ inline int w2s_stride(int r, int esz) { return r + 16 / esz; }
+
+// byte offsets of the controller's LDS arrays; returns the total
+__host__ __device__ inline size_t ctl_offsets(const TreeArgs& a, int esz, size_t* off) {
+  const size_t DM = (size_t)a.D * a.M, pk = (size_t)a.p * a.k, X = (size_t)a.xcap, P = (size_t)a.p;
+  size_t sz[L_COUNT];
+  sz[L_CID] = DM * 4;
+  sz[L_CVAL] = DM * 4;
+  sz[L_CRANK] = DM * 4;
+  sz[L_TAIL] = (size_t)a.D * 4;
+  sz[L_RKEY] = X * 8;
+  sz[L_RPAR] = X * 4;
+  sz[L_RSLOT] = X * 4;
+  sz[L_RRANK] = X * 4;
+  sz[L_TRK] = X * 8;
+  sz[L_TRP] = X * 4;
+  sz[L_TRS] = X * 4;
+  sz[L_FRONT] = (size_t)2 * a.fcap * 8;
+  sz[L_NC] = pk * 8;
+  sz[L_NCS] = pk * 8;
+  sz[L_PN] = pk * 4;
+  sz[L_W2S] = (size_t)a.nslots * a.M * w2s_stride(a.r, esz) * esz;
+  sz[L_PS] = (size_t)a.nslots * a.r * 4;
+  sz[L_WDEP] = (size_t)a.nslots * 4;
+  sz[L_WCLAIM] = (size_t)a.nslots * 4;
+  sz[L_LSLOTS] = (size_t)a.nslots * 4;
+  sz[L_EXREC] = P * 4;
+  sz[L_EXWS] = P * 4;
+  sz[L_EXDEP] = P * 4;
+  sz[L_EXTOK] = P * 4;
+  sz[L_EXSRC] = P * 4;
+  sz[L_AV] = P * a.r * 4;
+  sz[L_Z] = P * 64 * 4;
+  sz[L_CNT] = QCAP * 4;
+  sz[L_PERM] = QCAP * 4;
+  sz[L_ACC] = QCAP * 4;
+  sz[L_MISC] = C_MISC * 4;
+  sz[L_TAU] = 8;
+  size_t o = 0;
+  for (int i = 0; i < L_COUNT; ++i) {
+    off[i] = o;
+    o += (sz[i] + 15) / 16 * 16;
+  }
+  return o;
 }
 
-__device__ __forceinline__ CtlLds ctl_carve(unsigned char* lds, int D, int M, int N, int r, int fcap, int esz) {
+__device__ __forceinline__ CtlLds ctl_carve(unsigned char* lds, const TreeArgs& a, int esz) {
+  size_t off[L_COUNT];
+  ctl_offsets(a, esz, off);
   CtlLds c;
-  unsigned char* p = lds;
-  c.w2s = p; p += ((size_t)M * r * esz + 15) / 16 * 16;
-  c.front = reinterpret_cast<uint64_t*>(p); p += (size_t)fcap * 8;
-  c.red64 = reinterpret_cast<uint64_t*>(p); p += 4 * 8;
-  c.cid = reinterpret_cast<int*>(p); p += (size_t)D * M * 4;
-  c.cval = reinterpret_cast<float*>(p); p += (size_t)D * M * 4;
-  c.crank = reinterpret_cast<int*>(p); p += (size_t)D * M * 4;
-  c.tailv = reinterpret_cast<float*>(p); p += (size_t)D * 4;
-  c.ntok = reinterpret_cast<int*>(p); p += (size_t)(N + 1) * 4;
-  c.npar = reinterpret_cast<int*>(p); p += (size_t)(N + 1) * 4;
-  c.ndep = reinterpret_cast<int*>(p); p += (size_t)(N + 1) * 4;
-  c.nstep = reinterpret_cast<int*>(p); p += (size_t)(N + 1) * 4;
-  c.nscore = reinterpret_cast<float*>(p); p += (size_t)(N + 1) * 4;
-  c.av = reinterpret_cast<float*>(p); p += (size_t)r * 4;
-  c.ps = reinterpret_cast<float*>(p); p += (size_t)r * 4;
-  c.z = reinterpret_cast<float*>(p); p += 64 * 4;
-  c.logp = reinterpret_cast<float*>(p); p += 64 * 4;
-  c.okf = reinterpret_cast<int*>(p); p += 64 * 4;
-  c.misc = reinterpret_cast<int*>(p); p += 16 * 4;
-  c.redpos = reinterpret_cast<int*>(p); p += 4 * 4;
-  c.redf = reinterpret_cast<float*>(p); p += 4 * 4;
+  c.cid = (LDS int*)(lds + off[L_CID]);
+  c.cval = (LDS float*)(lds + off[L_CVAL]);
+  c.crank = (LDS int*)(lds + off[L_CRANK]);
+  c.tailv = (LDS float*)(lds + off[L_TAIL]);
+  c.rkey = (LDS uint64_t*)(lds + off[L_RKEY]);
+  c.rpar = (LDS int*)(lds + off[L_RPAR]);
+  c.rslot = (LDS int*)(lds + off[L_RSLOT]);
+  c.rrank = (LDS int*)(lds + off[L_RRANK]);
+  c.trk = (LDS uint64_t*)(lds + off[L_TRK]);
+  c.trp = (LDS int*)(lds + off[L_TRP]);
+  c.trs = (LDS int*)(lds + off[L_TRS]);
+  c.front = (LDS uint64_t*)(lds + off[L_FRONT]);
+  c.nc = (LDS uint64_t*)(lds + off[L_NC]);
+  c.ncs = (LDS uint64_t*)(lds + off[L_NCS]);
+  c.pn = (LDS int*)(lds + off[L_PN]);
+  c.w2s = (LDS unsigned char*)(lds + off[L_W2S]);
+  c.ps = (LDS float*)(lds + off[L_PS]);
+  c.wdep = (LDS int*)(lds + off[L_WDEP]);
+  c.wclaim = (LDS int*)(lds + off[L_WCLAIM]);
+  c.lslots = (LDS int*)(lds + off[L_LSLOTS]);
+  c.ex_rec = (LDS int*)(lds + off[L_EXREC]);
+  c.ex_ws = (LDS int*)(lds + off[L_EXWS]);
+  c.ex_dep = (LDS int*)(lds + off[L_EXDEP]);
+  c.ex_tok = (LDS int*)(lds + off[L_EXTOK]);
+  c.ex_src = (LDS int*)(lds + off[L_EXSRC]);
+  c.av = (LDS float*)(lds + off[L_AV]);
+  c.z = (LDS float*)(lds + off[L_Z]);
+  c.cnt = (LDS int*)(lds + off[L_CNT]);
+  c.perm = (LDS int*)(lds + off[L_PERM]);
+  c.acc = (LDS int*)(lds + off[L_ACC]);
+  c.misc = (LDS int*)(lds + off[L_MISC]);
+  c.tau = (LDS uint64_t*)(lds + off[L_TAU]);
   return c;
 }
 
-__device__ __forceinline__ float sigm(float x) { return 1.0f / (1.0f + expf(-x)); }
-
-// Load the W2 rows of depth row dy's candidates and its P row into LDS.
-// Issued while the controller waits for the workers, so the expansion that
-// follows reads only LDS and the published u.
-template <typename W>
-__device__ __forceinline__ void ctl_prefetch(const TreeArgs& a, const CtlLds& c, int b, int dy) {
-  const int tid = threadIdx.x, M = a.M, r = a.r;
-  W* dst = reinterpret_cast<W*>(c.w2s);
-  const W* w2t = reinterpret_cast<const W*>(a.w2t);
-  const int per = r * (int)sizeof(W) / 16;   // 16-byte pieces per row
-  if ((r * (int)sizeof(W)) % 16 == 0 && per <= 256 && 256 % per == 0) {
-    const int rpt = 256 / per;                 // rows per pass
-    const int pc = tid % per, m0 = tid / per;
-    constexpr int U = 8;
-    for (int mb = 0; mb < M; mb += U * rpt) {
-      uint4 v[U];
-#pragma unroll
-      for (int q = 0; q < U; ++q) {  // clamped: every lane loads a valid piece
-        const int m = min(mb + m0 + q * rpt, M - 1);
-        v[q] = reinterpret_cast<const uint4*>(w2t + (size_t)c.cid[dy * M + m] * r)[pc];
-      }
-#pragma unroll
-      for (int q = 0; q < U; ++q) {  // unconditional: see the worker's staging
-        const int m = min(mb + m0 + q * rpt, M - 1);
-        reinterpret_cast<uint4*>(dst)[m * per + pc] = v[q];
-      }
-    }
-  } else {
-    for (int i = tid; i < M * r; i += blockDim.x) dst[i] = w2t[(size_t)c.cid[dy * M + i / r] * r + i % r];
-  }
-  const float* prow = a.P + ((size_t)b * a.D + dy) * r;
-  for (int j = tid; j < r; j += blockDim.x) c.ps[j] = prow[j];
+// the frontier buffer currently in use
+__device__ __forceinline__ LDS uint64_t* cur_front(const TreeArgs& a, const CtlLds& c) {
+  return c.front + (size_t)c.misc[C_FB] * a.fcap;
 }
 
-// score the children of node y (depth dy < D) and push the k best
-template <typename W>
-__device__ __forceinline__ void ctl_expand(const TreeArgs& a, const CtlLds& c, int b, int y, int t) {
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int M = a.M, r = a.r;
-  const int dy = c.ndep[y];        // children are at depth dy + 1; row dy of the tables
-  const float* urow = a.u + slot_of(a, t, b) * u_stride(r);
-  for (int j = tid; j < r; j += blockDim.x) {
-    const float x = urow[j] + c.ps[j];
-    c.av[j] = x * sigm(x);  // SiLU
+// Logistic function and tanh from the hardware exp2 and reciprocal (about
+// 1e-7 relative error; a tanh near 0 is accurate to about 1e-7 absolute).
+__device__ __forceinline__ float sigm(float x) {
+  return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.4426950408889634f * x));
+}
+__device__ __forceinline__ float tanh_(float x) { return 2.0f * sigm(2.0f * x) - 1.0f; }
+
+// Total order between two records of equal depth whose keys tie on
+// (score, depth, token): the parents' order decides, recursively.
+__device__ __forceinline__ bool rec_better(const CtlLds& c, int x, int y) {
+  for (int it = 0; it < 32; ++it) {
+    if (x == y || x < 0 || y < 0) return false;
+    const uint64_t ux = key_u(c.rkey[x]), uy = key_u(c.rkey[y]);
+    if (ux != uy) return ux > uy;
+    x = c.rpar[x];
+    y = c.rpar[y];
   }
-  __syncthreads();
-  // dL_m = W2[:, cand_m] . a: tpc threads per candidate, each a contiguous
-  // slice of the rank, combined in a fixed order
-  int tpc = 1;
-  while (tpc * 2 * M <= (int)blockDim.x && tpc < 64) tpc *= 2;
-  const int m = tid / tpc, part = tid % tpc;
-  const int len = (r + tpc - 1) / tpc;
-  float dl = 0.f;
-  if (m < M) {
-    const W* wrow = reinterpret_cast<const W*>(c.w2s) + (size_t)m * r;
-    const int j0 = part * len, j1 = min(r, j0 + len);
-    constexpr int VE = 16 / sizeof(W);  // elements per 16-byte piece
-    if (j1 - j0 == len && len % VE == 0 && (r * (int)sizeof(W)) % 16 == 0) {
-      for (int j = j0; j < j1; j += VE) {
-        const uint4 wv = *reinterpret_cast<const uint4*>(wrow + j);
-        const W* we = reinterpret_cast<const W*>(&wv);
+  return false;
+}
+
+// frontier entry f precedes frontier entry g in the total order
+__device__ __forceinline__ bool entry_better(const CtlLds& c, uint64_t f, uint64_t g) {
+  const uint64_t uf = key_u(f), ug = key_u(g);
+  if (uf != ug) return uf > ug;
+  return rec_better(c, key_parent(f), key_parent(g));
+}
+
+// rrank[x] = number of records that precede record x
+__device__ __forceinline__ void ctl_rank(const CtlLds& c, int nx) {
+  for (int x = threadIdx.x; x < nx; x += blockDim.x) {
+    const uint64_t xu = key_u(c.rkey[x]);
+    const int xp = c.rpar[x];
+    int r = 0, ties = 0;
+    for (int y = 0; y < nx; ++y) {
+      const uint64_t yu = key_u(c.rkey[y]);
+      r += yu > xu;
+      ties += yu == xu;
+    }
+    if (ties > 1)  // equal keys: the parents' order decides
+      for (int y = 0; y < nx; ++y)
+        if (y != x && key_u(c.rkey[y]) == xu && rec_better(c, c.rpar[y], xp)) ++r;
+    c.rrank[x] = r;
+  }
+}
+
+// Load the W2 candidate rows and the P row of each depth slot listed in
+// lslots.  Issued while the workers run the step, so that scoring reads LDS.
+template <typename W>
+__device__ __forceinline__ void ctl_prefetch(const TreeArgs& a, const CtlLds& c, int b) {
+  const int tid = threadIdx.x, M = a.M, r = a.r;
+  const int nl = c.misc[C_NL];
+  if (nl == 0) return;
+  const W* w2t = reinterpret_cast<const W*>(a.w2t);
+  const int rs = w2s_stride(r, (int)sizeof(W));
+  const int rows = nl * M;
+  const int per = r * (int)sizeof(W) / 16;   // 16-byte pieces per row
+  const int rsp = rs * (int)sizeof(W) / 16;  // pieces per LDS row
+  if ((r * (int)sizeof(W)) % 16 == 0 && per <= 256 && 256 % per == 0) {
+    const int rpt = 256 / per;  // rows per pass
+    const int pc = tid % per, r0 = tid / per;
+    constexpr int U = 8;
+    LDS uint4* dst4 = (LDS uint4*)c.w2s;
+    for (int rb = 0; rb < rows; rb += U * rpt) {
+      uint4 v[U];
+      int dst[U];
 #pragma unroll
-        for (int q = 0; q < VE; q += 4) {
-          const float4 av = *reinterpret_cast<const float4*>(c.av + j + q);
-          dl = fmaf(w_to_f32<W>(we[q]), av.x, dl);
-          dl = fmaf(w_to_f32<W>(we[q + 1]), av.y, dl);
-          dl = fmaf(w_to_f32<W>(we[q + 2]), av.z, dl);
-          dl = fmaf(w_to_f32<W>(we[q + 3]), av.w, dl);
-        }
+      for (int q = 0; q < U; ++q) {  // clamped: every lane loads a valid piece
+        const int row = min(rb + r0 + q * rpt, rows - 1);
+        const int li = row / M, m = row - li * M;
+        const int s = c.lslots[li];
+        dst[q] = (s * M + m) * rsp + pc;
+        v[q] = reinterpret_cast<const uint4*>(w2t + (size_t)c.cid[c.wdep[s] * M + m] * r)[pc];
       }
-    } else {
-      for (int j = j0; j < j1; ++j) dl = fmaf(w_to_f32<W>(wrow[j]), c.av[j], dl);
+#pragma unroll
+      for (int q = 0; q < U; ++q) dst4[dst[q]] = v[q];  // unconditional
+    }
+  } else {
+    LDS W* w2s = (LDS W*)c.w2s;
+    for (int i = tid; i < rows * r; i += blockDim.x) {
+      const int row = i / r, j = i % r;
+      const int s = c.lslots[row / M], m = row % M;
+      w2s[((size_t)s * M + m) * rs + j] = w2t[(size_t)c.cid[c.wdep[s] * M + m] * r + j];
     }
   }
-  for (int s = 1; s < tpc; s <<= 1) dl += __shfl_xor(dl, s);
-  if (m < M && part == 0) c.z[m] = (c.cval[dy * M + m] + dl) / a.T + 0.0f;
+  for (int i = tid; i < nl * r; i += blockDim.x) {
+    const int s = c.lslots[i / r], j = i % r;
+    c.ps[(size_t)s * r + j] = a.P[((size_t)b * a.D + c.wdep[s]) * r + j];
+  }
+}
+
+// Score the children of the e nodes expanded at step t and write the keys of
+// each node's k best into nc[j k .. j k + k) (0 where a child has no finite
+// log-prob).
+template <typename W>
+__device__ __forceinline__ void ctl_expand(const TreeArgs& a, const CtlLds& c, int b, int t, int e) {
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int M = a.M, r = a.r, k = a.k;
+  // a_j = SiLU(u_j + P_{d_j}); the u loads of all nodes are issued first
+  {
+    const int us = u_stride(r);
+    const float* ub = a.u + slot_of(a, t, b, 0) * us;  // the e slots are consecutive
+    for (int i = tid; i < r; i += blockDim.x) {
+      float uv[PMAX];
+#pragma unroll
+      for (int j = 0; j < PMAX; ++j)
+        if (j < e) uv[j] = ub[(size_t)j * us + i];
+#pragma unroll
+      for (int j = 0; j < PMAX; ++j)
+        if (j < e) {
+          const float x = uv[j] + c.ps[c.ex_ws[j] * r + i];
+          c.av[j * r + i] = x * sigm(x);
+        }
+    }
+  }
   __syncthreads();
-  // wave 0, one candidate per lane: log-softmax over the candidates (plus the
-  // base tail under fullv), rank by (z desc, token asc), push the k best with
-  // a finite log-prob.  -inf log-probs rank after every finite one, so the
-  // children take ranks 0..n-1.
-  if (tid < 64) {
+  // dL_{j,m} = W2[:, cand_m] . a_j: tpc threads per (node, candidate), each a
+  // contiguous slice of the rank, combined in a fixed order
+  {
+    const int nd = e * M;
+    int tpc = 1;
+    while (tpc * 2 * nd <= (int)blockDim.x && tpc < 64) tpc *= 2;
+    const int len = (r + tpc - 1) / tpc;
+    const int rs = w2s_stride(r, (int)sizeof(W));
+    constexpr int VE = 16 / sizeof(W);  // elements per 16-byte piece
+    for (int base = 0; base < nd * tpc; base += blockDim.x) {
+      const int idx = base + tid;
+      const int pr = idx / tpc, part = idx % tpc;
+      float dl = 0.f;
+      int j = 0, m = 0;
+      if (pr < nd) {
+        j = pr / M;
+        m = pr - j * M;
+        const LDS W* wrow = (const LDS W*)c.w2s + (c.ex_ws[j] * M + m) * rs;
+        const LDS float* avj = c.av + j * r;
+        const int j0 = part * len, j1 = min(r, j0 + len);
+        if (j1 - j0 == len && len % VE == 0 && (r * (int)sizeof(W)) % 16 == 0) {
+          for (int q0 = j0; q0 < j1; q0 += VE) {
+            const uint4 wv4 = *(const LDS uint4*)(wrow + q0);
+            const W* we = reinterpret_cast<const W*>(&wv4);
+#pragma unroll
+            for (int q = 0; q < VE; q += 4) {
+              const float4 a4 = *(const LDS float4*)(avj + q0 + q);
+              dl = fmaf(w_to_f32<W>(we[q]), a4.x, dl);
+              dl = fmaf(w_to_f32<W>(we[q + 1]), a4.y, dl);
+              dl = fmaf(w_to_f32<W>(we[q + 2]), a4.z, dl);
+              dl = fmaf(w_to_f32<W>(we[q + 3]), a4.w, dl);
+            }
+          }
+        } else {
+          for (int q = j0; q < j1; ++q) dl = fmaf(w_to_f32<W>(wrow[q]), avj[q], dl);
+        }
+      }
+      for (int s = 1; s < tpc; s <<= 1) dl += __shfl_xor(dl, s);
+      if (pr < nd && part == 0) c.z[j * 64 + m] = (c.cval[c.ex_dep[j] * M + m] + dl) / a.T + 0.0f;
+    }
+  }
+  __syncthreads();
+  // one wave per node, one candidate per lane: log-softmax over the candidates
+  // (plus the base tail under fullv), rank by (z desc, token asc), keep the k
+  // best with a finite log-prob.  -inf log-probs rank after every finite one.
+  for (int j = wv; j < e; j += 4) {
+    const int y = c.ex_rec[j];
+    const int dy = c.ex_dep[j];
+    const float yscore = key_score(c.rkey[y]);
     const bool has = lane < M;
-    const float zv = has ? c.z[lane] : -INFINITY;
+    const float zv = has ? c.z[j * 64 + lane] : -INFINITY;
     const int idv = has ? c.cid[dy * M + lane] : 0x7FFFFFFF;
-    float mx = wave_max(zv);
+    float mx = wave_max_dpp(zv);
     const float tl = a.fullv ? c.tailv[dy] : -INFINITY;
     mx = fmaxf(mx, tl);
     float lz = -INFINITY;
     if (mx > -INFINITY) {
-      float se = wave_sum(has ? expf(zv - mx) : 0.f);
+      float se = wave_sum_dpp(has ? expf(zv - mx) : 0.f);
       if (tl > -INFINITY) se += expf(tl - mx);
       lz = mx + logf(se);
     }
     const float lp = zv - lz;
+    // rank by the composite (value key, complemented id); absent lanes are 0
+    const uint64_t me = has ? cand_pack(f32_key(zv), (uint32_t)idv) : 0ull;
+    const uint32_t mlo = (uint32_t)me, mhi = (uint32_t)(me >> 32);
     int rank = 0;
     for (int q = 0; q < M; ++q) {
-      const float zq = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(zv), q));
-      const int iq = __builtin_amdgcn_readlane(idv, q);
-      rank += (zq > zv) || (zq == zv && iq < idv);
+      const uint64_t o = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)mhi, q) << 32) |
+                         (uint32_t)__builtin_amdgcn_readlane((int)mlo, q);
+      rank += o > me;
     }
-    const bool ok = has && rank < a.k && isfinite(lp);
-    const int base = c.misc[0];
-    if (ok) c.front[base + rank] = make_key(c.nscore[y] + lp, dy + 1, c.crank[dy * M + lane], y, lane);
-    const unsigned long long bal = __ballot(ok);
-    if (lane == 0) c.misc[0] = base + __popcll(bal);
+    const bool ok = has && isfinite(lp);
+    if (has && rank < k)
+      c.nc[j * k + rank] = ok ? make_key(yscore + lp, dy + 1, c.crank[dy * M + lane], y, lane) : 0ull;
+  }
+  if (tid == 0) c.misc[C_NV] = 0;
+  __syncthreads();
+}
+
+// Merge this step's children into the sorted frontier (written to the other
+// buffer), dropping entries that are known to be out (key_u < tau).  Keys are
+// unique, so positions follow from counts: a new entry lands at (its rank
+// among the new) + (old entries ahead of it); old entry i moves up by the new
+// entries ahead of it.  Also resets the pop state of the step.
+__device__ __forceinline__ void ctl_merge(const TreeArgs& a, const CtlLds& c, int nnew) {
+  const int tid = threadIdx.x;
+  const int fh = c.misc[C_FH], nf = c.misc[C_NF], fb = c.misc[C_FB];
+  const bool tauset = c.misc[C_TAUSET] != 0;
+  const uint64_t tau = *c.tau;
+  const LDS uint64_t* F = c.front + (size_t)fb * a.fcap + fh;
+  LDS uint64_t* O = c.front + (size_t)(1 - fb) * a.fcap;
+  // live old entries: a prefix of the sorted frontier
+  int na = nf - fh;
+  if (tauset) {
+    int lo = 0, hi = na;
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (key_u(F[mid]) >= tau) lo = mid + 1;
+      else hi = mid;
+    }
+    na = lo;
+  }
+  for (int i = tid; i < nnew; i += blockDim.x) {
+    const uint64_t key = c.nc[i];
+    if (key != 0 && (!tauset || key_u(key) >= tau)) {
+      int rn = 0;  // live new entries ahead (any key above a live one is live)
+      for (int q = 0; q < nnew; ++q) rn += c.nc[q] > key;
+      int lo = 0, hi = na;
+      while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (F[mid] > key) lo = mid + 1;
+        else hi = mid;
+      }
+      c.ncs[rn] = key;
+      c.pn[rn] = lo;
+      atomicAdd((int*)&c.misc[C_NV], 1);
+    }
+  }
+  __syncthreads();
+  const int nv = c.misc[C_NV];
+  // (k - 1) xcap + 1 bounds the frontier; the guard only keeps LDS intact
+  for (int i = tid; i < na; i += blockDim.x) {
+    int lo = 0, hi = nv;  // new entries with insertion point <= i go ahead of it
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (c.pn[mid] <= i) lo = mid + 1;
+      else hi = mid;
+    }
+    if (i + lo < a.fcap) O[i + lo] = F[i];
+  }
+  for (int rr = tid; rr < nv; rr += blockDim.x)
+    if (rr + c.pn[rr] < a.fcap) O[rr + c.pn[rr]] = c.ncs[rr];
+  if (tid == 0) {
+    if (na + nv > a.fcap) atomicOr(a.err, 4);
+    c.misc[C_FB] = 1 - fb;
+    c.misc[C_FH] = 0;
+    c.misc[C_NF] = min(na + nv, a.fcap);
+    c.misc[C_E] = 0;
+    c.misc[C_STOP] = 0;
+    c.misc[C_NL] = 0;
+    for (int s = 0; s < a.nslots; ++s) c.wclaim[s] = 0;
   }
   __syncthreads();
 }
 
-// Wave 0 pops frontier entries in order, recording each as the next node,
-// until it finds one to expand (depth < D and index < N), the budget is met
-// or the frontier is empty.  Returns the node to expand or -1; updates *n.
-// Called by all threads; only wave 0 works, then one barrier.
-__device__ __forceinline__ int ctl_pop_until_expandable(const CtlLds& c, int D, int M, int N, int* n) {
+// Keep the N + 1 first records (renumbered by rank, so X becomes sorted), remap
+// parents, and cut the frontier after the entries that can still get in:
+// every entry ranked below record N in key_u is out, and no other entry has a
+// dropped parent.
+__device__ __forceinline__ void ctl_compact(const TreeArgs& a, const CtlLds& c) {
+  const int tid = threadIdx.x, N = a.N;
+  const int nx = c.misc[C_NX];
+  ctl_rank(c, nx);
+  __syncthreads();
+  for (int x = tid; x < nx; x += blockDim.x) {
+    const int rk = c.rrank[x];
+    if (rk <= N) {
+      c.trk[rk] = c.rkey[x];
+      c.trp[rk] = c.rpar[x] >= 0 ? c.rrank[c.rpar[x]] : -1;
+      c.trs[rk] = c.rslot[x];
+    }
+    if (rk == N) {
+      const uint64_t u = key_u(c.rkey[x]);
+      if (!c.misc[C_TAUSET] || u > *c.tau) *c.tau = u;
+    }
+  }
+  __syncthreads();
+  const int fh = c.misc[C_FH], nf = c.misc[C_NF], fb = c.misc[C_FB];
+  const LDS uint64_t* F = c.front + (size_t)fb * a.fcap + fh;
+  LDS uint64_t* O = c.front + (size_t)(1 - fb) * a.fcap;
+  const uint64_t tauN = *c.tau;
+  int na = nf - fh;
+  {
+    int lo = 0, hi = na;
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (key_u(F[mid]) >= tauN) lo = mid + 1;
+      else hi = mid;
+    }
+    na = lo;
+  }
+  for (int i = tid; i < na; i += blockDim.x) O[i] = key_with_parent(F[i], c.rrank[key_parent(F[i])]);
+  const int nk = min(nx, N + 1);
+  for (int x = tid; x < nk; x += blockDim.x) {
+    c.rkey[x] = c.trk[x];
+    c.rpar[x] = c.trp[x];
+    c.rslot[x] = c.trs[x];
+  }
+  __syncthreads();
+  if (tid == 0) {
+    c.misc[C_NX] = nk;
+    c.misc[C_FB] = 1 - fb;
+    c.misc[C_FH] = 0;
+    c.misc[C_NF] = na;
+    c.misc[C_TAUSET] = 1;
+  }
+  __syncthreads();
+}
+
+// An over-long group of equal key_u at the head: rotate its best entry (in the
+// total order) to the head; it is then tested alone.  Thread 0 only.
+__device__ __forceinline__ void ctl_batch_group(const CtlLds& c, LDS uint64_t* F, int fh, int nf, uint64_t u) {
+  int g = fh;
+  for (int i = fh + 1; i < nf && key_u(F[i]) == u; ++i)
+    if (entry_better(c, F[i], F[g])) g = i;
+  const uint64_t best = F[g];
+  for (int i = g; i > fh; --i) F[i] = F[i - 1];
+  F[fh] = best;
+  c.misc[C_G] = g;  // where to put it back if it is neither taken nor out
+}
+
+// Take frontier entries for the next step (t + 1): up to p nodes to expand,
+// plus the depth-D leaves met on the way.  Returns the number to expand.
+__device__ __forceinline__ int ctl_pop(const TreeArgs& a, const CtlLds& c, int b, int t) {
   const int tid = threadIdx.x, lane = tid & 63;
-  if (tid < 64) {
-    int cnt = c.misc[0];
-    int nn = *n;
-    int next = -1;
-    while (nn < N && cnt > 0) {
-      uint64_t best = 0;
-      int pos = -1;
-      for (int i = lane; i < cnt; i += 64) {
-        const uint64_t k = c.front[i];
-        if (pos < 0 || k > best) {
-          best = k;
-          pos = i;
+  const int N = a.N, D = a.D, M = a.M;
+  for (int round = 0; round < 4 * XMAX; ++round) {
+    if (c.misc[C_NX] + a.qmax > a.xcap) {
+      if (c.misc[C_E] > 0) break;  // expand what was taken; compact next step
+      ctl_compact(a, c);
+    }
+    // the batch: the first Q entries, not ending inside a group of equal key_u
+    // (every thread computes the same Q from the same LDS words)
+    const int fh = c.misc[C_FH], nf = c.misc[C_NF], nx = c.misc[C_NX];
+    LDS uint64_t* F = cur_front(a, c) + fh;
+    int Q = min(min(nf - fh, a.qmax), a.xcap - nx);
+    bool group = false;
+    if (Q > 0 && Q < nf - fh && key_u(F[Q - 1]) == key_u(F[Q])) {
+      const uint64_t u = key_u(F[Q - 1]);
+      while (Q > 0 && key_u(F[Q - 1]) == u) --Q;
+      if (Q == 0) {
+        group = true;
+        Q = 1;
+        if (tid == 0) ctl_batch_group(c, F - fh, fh, nf, u);
+        __syncthreads();
+      }
+    }
+    if (Q <= 0) break;
+    // cnt[j] = records that precede entry j of the batch
+    {
+      int Qp = 1;
+      while (Qp < Q) Qp <<= 1;
+      const int S = min(64, 256 / Qp);
+      const int j = tid / S, s = tid % S;
+      int cv = 0, tie = 0;
+      uint64_t fu = 0;
+      if (j < Q) {
+        fu = key_u(F[j]);
+        for (int y = s; y < nx; y += S) {
+          const uint64_t yu = key_u(c.rkey[y]);
+          cv += yu > fu;
+          tie |= yu == fu;
+        }
+        if (tie) {  // equal keys: the parents' order decides
+          const int fp = key_parent(F[j]);
+          for (int y = s; y < nx; y += S)
+            if (key_u(c.rkey[y]) == fu && rec_better(c, c.rpar[y], fp)) ++cv;
         }
       }
-      const uint64_t g = wave_max_u64(pos < 0 ? 0ull : best);
-      const unsigned long long hit = __ballot(pos >= 0 && best == g);  // keys are unique
-      const int src = __ffsll((long long)hit) - 1;
-      const int gpos = __shfl(pos, src);
-      const int i = nn + 1;
-      const int d = key_depth(g);
+      for (int m = S >> 1; m >= 1; m >>= 1) cv += __shfl_xor(cv, m);
+      if (j < Q && s == 0) c.cnt[j] = cv;
+    }
+    __syncthreads();
+    // wave 0, lane jj = the jj-th batch entry in the total order: the taken
+    // entries are the longest prefix that is not out and fits the step
+    if (tid < 64) {
+      const bool has = lane < Q;
+      const bool tie = has && lane > 0 && key_u(F[lane]) == key_u(F[lane - 1]);
+      const bool anytie = __ballot(tie) != 0;
+      if (has) {
+        c.perm[lane] = lane;
+        c.acc[lane] = 0;
+      }
+      if (anytie && lane == 0)
+        for (int i = 1; i < Q; ++i) {  // insertion sort in the total order
+          const int v = c.perm[i];
+          int jj = i;
+          while (jj > 0 && entry_better(c, F[v], F[c.perm[jj - 1]])) {
+            c.perm[jj] = c.perm[jj - 1];
+            --jj;
+          }
+          c.perm[jj] = v;
+        }
+      const int j = has ? c.perm[lane] : 0;
+      const uint64_t key = has ? F[j] : 0ull;
+      const int d = key_depth(key);
+      const bool expd = has && d < D;
+      const bool out = has && c.cnt[j] + lane >= N + 1;
+      const int e0 = c.misc[C_E];
+      // depth slots: a depth is new if no slot holds it and no earlier lane has it
+      int held = 0, held_claimed = 0, nclaimed = 0;
+      for (int s = 0; s < a.nslots; ++s) {
+        const int ws = c.wdep[s], wc = c.wclaim[s];
+        held |= ws == d;
+        held_claimed |= ws == d && wc;
+        nclaimed += wc;
+      }
+      const unsigned long long bexp = __ballot(expd);
+      bool first = true;  // no earlier lane expands a node of the same depth
+      for (int q = 0; q < Q; ++q) {
+        const int dq = __builtin_amdgcn_readlane(d, q);
+        first &= !(q < lane && ((bexp >> q) & 1ull) && dq == d);
+      }
+      const unsigned long long le = lane == 63 ? ~0ull : ((2ull << lane) - 1ull);  // lanes <= lane
+      const unsigned long long bnew = __ballot(expd && first && !held);
+      const unsigned long long bhu = __ballot(expd && first && held && !held_claimed);
+      const int need = nclaimed + __popcll(bhu & le) + __popcll(bnew & le);
+      const bool fits = has && !out && (!expd || (e0 + __popcll(bexp & le) <= a.p && need <= a.nslots));
+      const unsigned long long bfail = __ballot(has && !fits);
+      const int A = bfail ? __ffsll((long long)bfail) - 1 : Q;
+      const bool isout = A < Q && ((__ballot(out) >> A) & 1ull);
+      const unsigned long long lowA = A >= 64 ? ~0ull : ((1ull << A) - 1ull);
+      // lane 0 claims the slots of the taken depths, then gives new depths free slots
       if (lane == 0) {
-        c.front[gpos] = c.front[cnt - 1];
-        c.ntok[i] = c.cid[(d - 1) * M + key_slot(g)];
-        c.npar[i] = key_parent(g);
-        c.ndep[i] = d;
-        c.nscore[i] = key_score(g);
+        uint32_t dm = 0;  // depths of the taken nodes to expand
+        for (unsigned long long mm = bexp & lowA; mm; mm &= mm - 1)
+          dm |= 1u << __builtin_amdgcn_readlane(d, __ffsll((long long)mm) - 1);
+        for (int s = 0; s < a.nslots; ++s)
+          if (c.wdep[s] >= 0 && ((dm >> c.wdep[s]) & 1u)) c.wclaim[s] = 1;
+        for (unsigned long long mm = bnew & lowA; mm; mm &= mm - 1) {
+          const int dq = __builtin_amdgcn_readlane(d, __ffsll((long long)mm) - 1);
+          for (int s = 0; s < a.nslots; ++s)
+            if (!c.wclaim[s]) {
+              c.wclaim[s] = 1;
+              c.wdep[s] = dq;
+              c.lslots[c.misc[C_NL]++] = s;
+              break;
+            }
+        }
       }
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-      --cnt;
-      nn = i;
-      if (d < D && i < N) {
-        next = i;
-        break;
+      // the taken lanes write their records and the tables of the next step
+      if (has && lane < A) {
+        const int x = nx + lane;
+        const int par = key_parent(key);
+        c.rkey[x] = key;
+        c.rpar[x] = par;
+        c.acc[j] = 1;
+        if (expd) {
+          const int ei = e0 + __popcll(bexp & le) - 1;
+          int ws = 0;
+          for (int s = 0; s < a.nslots; ++s)
+            if (c.wdep[s] == d) ws = s;
+          c.ex_rec[ei] = x;
+          c.ex_ws[ei] = ws;
+          c.ex_dep[ei] = d;
+          c.ex_tok[ei] = c.cid[(d - 1) * M + key_m(key)];
+          c.ex_src[ei] = c.rslot[par];
+          c.rslot[x] = (int)slot_of(a, t + 1, b, ei);
+        } else {
+          c.rslot[x] = -1;
+        }
+      }
+      if (lane == 0) {
+        if (group && A == 0 && !isout) {  // put the group's best entry back in key order
+          const int g = c.misc[C_G] - fh;
+          const uint64_t best = F[0];
+          for (int i = 0; i < g; ++i) F[i] = F[i + 1];
+          F[g] = best;
+        }
+        if (isout) {
+          const uint64_t u = key_u(F[c.perm[A]]);
+          if (!c.misc[C_TAUSET] || u > *c.tau) *c.tau = u;
+          c.misc[C_TAUSET] = 1;
+          c.misc[C_NF] = c.misc[C_FH] = 0;  // the rest of the frontier is out
+        } else {
+          if (anytie) {  // the taken entries may not be a key-order prefix
+            int wpos = Q;
+            for (int jj = Q - 1; jj >= 0; --jj)
+              if (!c.acc[jj]) F[--wpos] = F[jj];
+          }
+          c.misc[C_FH] = fh + A;
+        }
+        const int e1 = e0 + __popcll(bexp & lowA);
+        c.misc[C_E] = e1;
+        c.misc[C_NX] = nx + A;
+        c.misc[C_STOP] = isout || A < Q || e1 == a.p;
       }
     }
-    if (lane == 0) {
-      c.misc[0] = cnt;
-      c.misc[4] = nn;
-      c.misc[5] = next;
-    }
+    __syncthreads();
+    if (c.misc[C_STOP]) break;
   }
-  __syncthreads();
-  *n = c.misc[4];
-  return c.misc[5];
+  return c.misc[C_E];
 }
 
+// Advance the GRU state of each node taken for step t1 from its parent's:
+// S_y = GRU(S_x, E[tok]) with W_ih E[tok] + b_ih = G[tok] and
+// gh_x = W_hh S~_x + b_hh published by the workers at the parent's step.
+// The e nodes' float4 items are spread over the block; the loads of GA items
+// are issued before their stores.
 template <typename W>
-__device__ __forceinline__ void ctl_advance_state(const TreeArgs& a, int b, int y, int x, int tok, int tx,
-                                                  int ty) {
-  // x was expanded at step tx; y is published for step ty
-  // S_y = GRU(S_x, E[tok]) with W_ih E[tok] + b_ih = G[tok] and gh_x = W_hh S~_x + b_hh
+__device__ __forceinline__ void ctl_advance(const TreeArgs& a, const CtlLds& c, int b, int t1, int e) {
   const int ds = a.ds;
-  const float* gi = a.G + (size_t)tok * 3 * ds;
-  const float* gh = a.gh + slot_of(a, tx, b) * gh_stride(ds);
-  const float* sx = a.state + ((size_t)b * (a.N + 1) + x) * st_stride(ds);
-  float* sy = a.state + ((size_t)b * (a.N + 1) + y) * st_stride(ds);
-  W* ay = reinterpret_cast<W*>(a.act) + slot_of(a, ty, b) * act_stride(ds);
+  const size_t sl0 = slot_of(a, t1, b, 0);  // the e slots are consecutive
   if ((ds & 3) == 0) {
-    for (int j = 4 * threadIdx.x; j < ds; j += 4 * blockDim.x) {
-      const float4 ir = *reinterpret_cast<const float4*>(gi + j);
-      const float4 iz = *reinterpret_cast<const float4*>(gi + ds + j);
-      const float4 in = *reinterpret_cast<const float4*>(gi + 2 * ds + j);
-      const float4 hr = *reinterpret_cast<const float4*>(gh + j);
-      const float4 hz = *reinterpret_cast<const float4*>(gh + ds + j);
-      const float4 hn = *reinterpret_cast<const float4*>(gh + 2 * ds + j);
-      const float4 sp = *reinterpret_cast<const float4*>(sx + j);
-      const float a0[4] = {ir.x, ir.y, ir.z, ir.w}, b0[4] = {hr.x, hr.y, hr.z, hr.w};
-      const float a1[4] = {iz.x, iz.y, iz.z, iz.w}, b1[4] = {hz.x, hz.y, hz.z, hz.w};
-      const float a2[4] = {in.x, in.y, in.z, in.w}, b2[4] = {hn.x, hn.y, hn.z, hn.w};
-      const float s0[4] = {sp.x, sp.y, sp.z, sp.w};
-      floatx4 o;
+    const int n4 = ds >> 2;
+    const int total = e * n4;
+    for (int base = 0; base < total; base += GA * (int)blockDim.x) {
+      float4 ir[GA], iz[GA], in[GA], hr[GA], hz[GA], hn[GA], sp[GA];
+      int jv[GA], qv[GA];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const float rg = sigm(a0[q] + b0[q]);
-        const float zg = sigm(a1[q] + b1[q]);
-        const float ng = tanhf(a2[q] + rg * b2[q]);
-        o[q] = (1.0f - zg) * ng + zg * s0[q];
+      for (int g = 0; g < GA; ++g) {  // clamped: every lane loads valid addresses
+        const int item = min(base + g * (int)blockDim.x + (int)threadIdx.x, total - 1);
+        const int j = item / n4;
+        const int q = (item - j * n4) * 4;
+        jv[g] = j;
+        qv[g] = q;
+        int xs = c.ex_src[j];
+        if (xs < 0) {  // every parent was expanded; the guard keeps addresses valid
+          atomicOr(a.err, 8);
+          xs = 0;
+        }
+        const float* gi = a.G + (size_t)c.ex_tok[j] * 3 * ds + q;
+        const float* gh = a.gh + (size_t)xs * gh_stride(ds) + q;
+        ir[g] = *reinterpret_cast<const float4*>(gi);
+        iz[g] = *reinterpret_cast<const float4*>(gi + ds);
+        in[g] = *reinterpret_cast<const float4*>(gi + 2 * ds);
+        hr[g] = *reinterpret_cast<const float4*>(gh);
+        hz[g] = *reinterpret_cast<const float4*>(gh + ds);
+        hn[g] = *reinterpret_cast<const float4*>(gh + 2 * ds);
+        sp[g] = *reinterpret_cast<const float4*>(a.state + (size_t)xs * st_stride(ds) + q);
       }
-      st_dev_f32x4(sy + j, o);
-      st_dev_act4<W>(ay + j, o, a.act_bf16);
+#pragma unroll
+      for (int g = 0; g < GA; ++g) {
+        if (base + g * (int)blockDim.x + (int)threadIdx.x < total) {
+          const float a0[4] = {ir[g].x, ir[g].y, ir[g].z, ir[g].w}, b0[4] = {hr[g].x, hr[g].y, hr[g].z, hr[g].w};
+          const float a1[4] = {iz[g].x, iz[g].y, iz[g].z, iz[g].w}, b1[4] = {hz[g].x, hz[g].y, hz[g].z, hz[g].w};
+          const float a2[4] = {in[g].x, in[g].y, in[g].z, in[g].w}, b2[4] = {hn[g].x, hn[g].y, hn[g].z, hn[g].w};
+          const float s0[4] = {sp[g].x, sp[g].y, sp[g].z, sp[g].w};
+          floatx4 o;
+#pragma unroll
+          for (int qq = 0; qq < 4; ++qq) {
+            const float rg = sigm(a0[qq] + b0[qq]);
+            const float zg = sigm(a1[qq] + b1[qq]);
+            const float ng = tanh_(a2[qq] + rg * b2[qq]);
+            o[qq] = (1.0f - zg) * ng + zg * s0[qq];
+          }
+          const size_t sl = sl0 + jv[g];
+          st_dev_f32x4(a.state + sl * st_stride(ds) + qv[g], o);
+          st_dev_act4<W>(reinterpret_cast<W*>(a.act) + sl * act_stride(ds) + qv[g], o, a.act_bf16);
+        }
+      }
     }
   } else {
-    for (int j = threadIdx.x; j < ds; j += blockDim.x) {
-      const float rg = sigm(gi[j] + gh[j]);
-      const float zg = sigm(gi[ds + j] + gh[ds + j]);
-      const float ng = tanhf(gi[2 * ds + j] + rg * gh[2 * ds + j]);
-      const float s = (1.0f - zg) * ng + zg * sx[j];
-      st_dev_f32(sy + j, s);
-      st_dev_act<W>(ay + j, s, a.act_bf16);
+    for (int j = 0; j < e; ++j) {
+      const int xs = max(c.ex_src[j], 0);
+      const float* gi = a.G + (size_t)c.ex_tok[j] * 3 * ds;
+      const float* gh = a.gh + (size_t)xs * gh_stride(ds);
+      const float* sx = a.state + (size_t)xs * st_stride(ds);
+      float* sy = a.state + (sl0 + j) * st_stride(ds);
+      W* ay = reinterpret_cast<W*>(a.act) + (sl0 + j) * act_stride(ds);
+      for (int q = threadIdx.x; q < ds; q += blockDim.x) {
+        const float rg = sigm(gi[q] + gh[q]);
+        const float zg = sigm(gi[ds + q] + gh[ds + q]);
+        const float ng = tanh_(gi[2 * ds + q] + rg * gh[2 * ds + q]);
+        const float s = (1.0f - zg) * ng + zg * sx[q];
+        st_dev_f32(sy + q, s);
+        st_dev_act<W>(ay + q, s, a.act_bf16);
+      }
     }
   }
-  for (int j = ds + threadIdx.x; j < k_padded(ds); j += blockDim.x) st_dev_act<W>(ay + j, 0.f, 0);
+  const int kpad = k_padded(ds) - ds;  // zero k padding of the operand copies
+  for (int i = threadIdx.x; i < e * kpad; i += blockDim.x)
+    st_dev_act<W>(reinterpret_cast<W*>(a.act) + (sl0 + i / kpad) * act_stride(ds) + ds + i % kpad, 0.f, 0);
+}
+
+// outputs in the total order (node i = the record ranked i), padded past n
+__device__ __forceinline__ void ctl_output(const TreeArgs& a, const CtlLds& c, int b, bool failed) {
+  const int tid = threadIdx.x, N = a.N, M = a.M;
+  const int nx = c.misc[C_NX];
+  ctl_rank(c, nx);
+  __syncthreads();
+  const int n = min(N, nx - 1);
+  const size_t o = (size_t)b * (N + 1);
+  for (int x = tid; x < nx; x += blockDim.x) {
+    const int rk = c.rrank[x];
+    if (rk > N) continue;
+    const uint64_t key = c.rkey[x];
+    const bool root = x == 0;
+    const int d = key_depth(key);
+    a.tokens[o + rk] = root ? -1 : c.cid[(d - 1) * M + key_m(key)];
+    a.parents[o + rk] = root ? -1 : c.rrank[c.rpar[x]];
+    a.depths[o + rk] = d;
+    a.scores[o + rk] = key_score(key);
+  }
+  for (int i = n + 1 + tid; i <= N; i += blockDim.x) {
+    a.tokens[o + i] = -1;
+    a.parents[o + i] = -1;
+    a.depths[o + i] = -1;
+    a.scores[o + i] = -INFINITY;
+  }
+  if (tid == 0) a.n_nodes[b] = failed ? -1 : n;
 }
 
 template <typename W>
 __device__ __forceinline__ void controller_main(const TreeArgs& a, unsigned char* lds) {
   const int b = blockIdx.x - a.n_workers;
   const int tid = threadIdx.x;
-  const int D = a.D, M = a.M, N = a.N;
-  const int fcap = a.N * (a.k - 1) + 1;
-  CtlLds c = ctl_carve(lds, D, M, N, a.r, fcap, (int)sizeof(W));
+  const int D = a.D, M = a.M;
+  const CtlLds c = ctl_carve(lds, a, (int)sizeof(W));
 
   for (int i = tid; i < D * M; i += blockDim.x) {
     c.cid[i] = a.cand_ids[(size_t)b * D * M + i];
@@ -629,17 +1186,29 @@ __device__ __forceinline__ void controller_main(const TreeArgs& a, unsigned char
   }
   for (int i = tid; i < D; i += blockDim.x) c.tailv[i] = a.tail[(size_t)b * D + i];
   if (tid == 0) {
-    c.misc[0] = 0;  // frontier size
-    c.ntok[0] = -1;
-    c.npar[0] = -1;
-    c.ndep[0] = 0;
-    c.nscore[0] = 0.f;
+    // the root: score 0, depth 0; it precedes every other node
+    c.rkey[0] = make_key(0.f, 0, 0, 0, 0);
+    c.rpar[0] = -1;
+    c.rslot[0] = (int)slot_of(a, 0, b, 0);
+    c.misc[C_NX] = 1;
+    c.misc[C_NF] = c.misc[C_FH] = c.misc[C_FB] = 0;
+    c.misc[C_TAUSET] = 0;
+    *c.tau = 0;
+    for (int s = 0; s < a.nslots; ++s) c.wdep[s] = -1;
+    c.wdep[0] = 0;  // the root's children are at depth 1: row 0 of the tables
+    c.lslots[0] = 0;
+    c.misc[C_NL] = 1;
+    c.ex_rec[0] = 0;
+    c.ex_ws[0] = 0;
+    c.ex_dep[0] = 0;
+    c.misc[C_E] = 1;
   }
   // root state and its GEMM operand copy
   {
     const int ds = a.ds;
-    float* s0 = a.state + (size_t)b * (N + 1) * st_stride(ds);
-    W* a0 = reinterpret_cast<W*>(a.act) + slot_of(a, 0, b) * act_stride(ds);
+    const size_t sl = slot_of(a, 0, b, 0);
+    float* s0 = a.state + sl * st_stride(ds);
+    W* a0 = reinterpret_cast<W*>(a.act) + sl * act_stride(ds);
     for (int j = tid; j < ds; j += blockDim.x) {
       const float v = a.root ? a.root[(size_t)b * ds + j] : 0.f;
       st_dev_f32(s0 + j, v);
@@ -647,56 +1216,48 @@ __device__ __forceinline__ void controller_main(const TreeArgs& a, unsigned char
     }
     for (int j = ds + tid; j < k_padded(ds); j += blockDim.x) st_dev_act<W>(a0 + j, 0.f, 0);
   }
-  if (tid == 0) c.nstep[0] = 0;
   stores_done();
   __syncthreads();
-  if (tid < a.n_workers) st_dev_u32(a.mbox_w + (size_t)tid * 32 + b, 1u);  // step 0 posted
-  for (int w = tid + 256; w < a.n_workers; w += 256) st_dev_u32(a.mbox_w + (size_t)w * 32 + b, 1u);
+  for (int w = tid; w < a.n_workers; w += blockDim.x) st_dev_u32(a.mbox_w + (size_t)w * 32 + b, mbox_word(1, 1));
   stores_done();
+  ctl_prefetch<W>(a, c, b);
   __syncthreads();
 
-  ctl_prefetch<W>(a, c, b, 0);  // the root's children are at depth 1
-  int y = 0;  // node expanded at this step
-  int n = 0;  // non-root nodes popped (same value in every thread)
   bool failed = false;
   for (int t = 0;; ++t) {
+    const int e = c.misc[C_E];
     const uint32_t epoch = (uint32_t)t + 1u;
     if (tid < 64) {
       const bool ok = wait_mbox(a.mbox_c + (size_t)b * 256, a.n_workers, epoch, a.err, a.spin_limit);
-      if (tid == 0) c.misc[3] = ok;
+      if (tid == 0) c.misc[C_OK] = ok;
     }
     __syncthreads();
-    if (!c.misc[3]) {
+    if (!c.misc[C_OK]) {
       failed = true;
       break;
     }
-    ctl_expand<W>(a, c, b, y, t);
-    // pop until a node to expand is found, the budget is met or the frontier is empty
-    const int next = ctl_pop_until_expandable(c, D, M, N, &n);
-    if (next < 0) break;
-    ctl_advance_state<W>(a, b, next, c.npar[next], c.ntok[next], c.nstep[c.npar[next]], t + 1);
-    if (tid == 0) c.nstep[next] = t + 1;
+    ctl_expand<W>(a, c, b, t, e);
+    ctl_merge(a, c, e * a.k);
+    const int e2 = ctl_pop(a, c, b, t);
+    if (e2 == 0) break;
+    if (t + 1 > a.N) {  // cannot happen: every step takes one of the N best nodes
+      if (tid == 0) atomicOr(a.err, 2);
+      failed = true;
+      break;
+    }
+    ctl_advance<W>(a, c, b, t + 1, e2);
     stores_done();
     __syncthreads();
     for (int w = tid; w < a.n_workers; w += blockDim.x)
-      st_dev_u32(a.mbox_w + (size_t)w * 32 + b, epoch + 1u);
+      st_dev_u32(a.mbox_w + (size_t)w * 32 + b, mbox_word(t + 2, e2));
     stores_done();
-    ctl_prefetch<W>(a, c, b, c.ndep[next]);  // overlaps the workers' step
+    ctl_prefetch<W>(a, c, b);  // overlaps the workers' step
     __syncthreads();
-    y = next;
   }
   // release the workers from this request
   for (int w = tid; w < a.n_workers; w += blockDim.x) st_dev_u32(a.mbox_w + (size_t)w * 32 + b, MBOX_DONE);
   stores_done();
-  // outputs, padded past n
-  for (int i = tid; i <= N; i += blockDim.x) {
-    const bool in = i <= n;
-    a.tokens[(size_t)b * (N + 1) + i] = in ? c.ntok[i] : -1;
-    a.parents[(size_t)b * (N + 1) + i] = in ? c.npar[i] : -1;
-    a.depths[(size_t)b * (N + 1) + i] = in ? c.ndep[i] : -1;
-    a.scores[(size_t)b * (N + 1) + i] = in ? c.nscore[i] : -INFINITY;
-  }
-  if (tid == 0) a.n_nodes[b] = failed ? -1 : n;
+  ctl_output(a, c, b, failed);
 }
 
 template <typename W>
@@ -708,12 +1269,51 @@ __global__ __launch_bounds__(256) void tree_kernel(TreeArgs a) {
   else controller_main<W>(a, lds);
 }
 
-size_t tree_lds_bytes(const TreeArgs& a, int wdtype_bf16) {
+// ---------------------------------------------------------------------------
+// host side: schedule and launch
+
+size_t plan_tree(TreeArgs& a, int wdtype_bf16, int pops) {
+  const int esz = wdtype_bf16 ? 2 : 4;
+  const size_t lds_max = 160 * 1024;
   const int kp = k_padded(a.ds);
-  const size_t w = wdtype_bf16 ? WorkerLds<uint16_t>::bytes(a.tiles_per_worker, kp)
-                               : WorkerLds<float>::bytes(a.tiles_per_worker, kp);
-  const size_t c = ctl_lds_bytes(a.D, a.M, a.N, a.r, a.N * (a.k - 1) + 1, wdtype_bf16 ? 2 : 4);
-  return w > c ? w : c;
+  if (a.N + 1 > XMAX || a.M > 64 || a.k > a.M || a.D > 31) return 0;
+  // nodes per request per step: fill about TREE_MAX_COLS columns
+  int p = pops > 0 ? pops : TREE_MAX_COLS / a.B;
+  p = std::max(1, std::min(std::min(p, PMAX), TREE_MAX_COLS / a.B));
+  for (; p >= 1; --p) {
+    const int cols = a.B * p;
+    if (a.tiles_per_worker * ((cols + 15) / 16) > 4 * PPW) continue;
+    // worker staging phases: kc | kp, 32 | kc, stage within its share of LDS
+    int kc = kp;
+    const size_t stage_cap = wdtype_bf16 ? 68 * 1024 : lds_max - worker_stage_offset(a.tiles_per_worker, kp, esz) -
+                                                           (size_t)(2 * TREE_MAX_COLS + 64) * 4;
+    while ((size_t)round_up(cols, 16) * (kc + STAGE_PAD) * esz > stage_cap && kc % 64 == 0 && wdtype_bf16) kc /= 2;
+    const size_t wl = worker_lds_bytes(a.tiles_per_worker, kp, kc, cols, esz);
+    if (wl > lds_max) continue;
+    // controller: records for the budget, the root and speculation room; the
+    // frontier bound (k - 1) xcap + 1 must fit the merge's registers
+    int qmax = p == 1 ? 8 : QCAP;
+    int xcap = 0, fcap = 0;
+    for (; qmax >= 1; qmax /= 2) {
+      xcap = std::min(XMAX, a.N + 1 + 2 * qmax);
+      fcap = (a.k - 1) * xcap + 1;
+      if (fcap <= FCAPMAX) break;
+    }
+    if (qmax < 1) continue;
+    a.p = p;
+    a.kc = kc;
+    a.qmax = qmax;
+    a.xcap = xcap;
+    a.fcap = fcap;
+    // depth slots: as many as fit, at most p
+    size_t off[L_COUNT];
+    for (int ns = std::min(p, a.D); ns >= 1; --ns) {
+      a.nslots = ns;
+      const size_t cl = ctl_offsets(a, esz, off);
+      if (cl <= lds_max) return std::max(cl, wl);
+    }
+  }
+  return 0;
 }
 
 hipError_t launch_tree(const TreeArgs& a, int wdtype_bf16, size_t lds_bytes, hipStream_t stream) {
