@@ -54,6 +54,7 @@
 namespace dt {
 
 constexpr uint32_t MBOX_DONE = 0xFFFFFFFFu;
+constexpr int NT = 256;      // threads per block (every block of the builder)
 constexpr int PMAX = 16;     // nodes per request per step
 constexpr int QCAP = 32;     // frontier entries tested per pop round
 constexpr int FCAPMAX = 6144;  // frontier entries per request
@@ -131,7 +132,7 @@ __host__ __device__ inline int k_padded(int ds) { return round_up(ds, 32); }
 __host__ __device__ inline int st_stride(int ds) { return round_up(ds, 32); }      // floats
 __host__ __device__ inline int gh_stride(int ds) { return round_up(3 * ds, 32); }  // floats
 __host__ __device__ inline int u_stride(int r) { return round_up(r, 32); }         // floats
-constexpr int STAGE_PAD = 8;  // extra elements per staged column (LDS bank spread)
+constexpr int STAGE_PAD = 8;  // extra elements per staged column (bank spread)
 
 // exchange slot of the j-th node a request expands at step t
 __device__ __forceinline__ size_t slot_of(const TreeArgs& a, int t, int b, int j) {
@@ -206,7 +207,7 @@ __device__ __forceinline__ void worker_store_out(const TreeArgs& a, size_t slot,
 
 // Copy elements [k0, k0 + kc) of each active column's operand into the stage.
 // Thread tid owns 16-byte piece tid % per of columns tid / per + j * cpt;
-// every load of a batch is issued before any LDS store.
+// every load of a batch is issued before any store.
 template <typename W>
 __device__ __forceinline__ void worker_stage(const TreeArgs& a, W* stage, const int* coln, int ncols, int k0,
                                              int kc) {
@@ -235,7 +236,7 @@ __device__ __forceinline__ void worker_stage(const TreeArgs& a, W* stage, const 
       }
     }
   } else {
-    for (int i = tid; i < ncols * per; i += blockDim.x) {
+    for (int i = tid; i < ncols * per; i += NT) {
       const int c = i / per, pc = i % per;
       *reinterpret_cast<uint4*>(stage + (size_t)c * kcs + pc * (16 / sizeof(W))) =
           reinterpret_cast<const uint4*>(act + (size_t)coln[c] * as + k0)[pc];
@@ -316,7 +317,7 @@ __device__ __forceinline__ void worker_compute_f32(const TreeArgs& a, const floa
                                                    int ncols, const int* coln, int tile0, int ntiles, int kp,
                                                    int kcs) {
   const int total = ntiles * 16 * ncols;
-  for (int idx = threadIdx.x; idx < total; idx += blockDim.x) {
+  for (int idx = threadIdx.x; idx < total; idx += NT) {
     const int col = idx % ncols;
     const int rr = (idx / ncols) % 16;
     const int tt = idx / (ncols * 16);
@@ -345,13 +346,13 @@ __device__ __forceinline__ void worker_main(const TreeArgs& a, unsigned char* ld
   int* reqs = coln + TREE_MAX_COLS;  // requests with work this step
   int* misc = reqs + TREE_MAX_COLS;  // [0] columns (-1: failed), [1] requests
 
-  // the block's Wc tiles stay in LDS for the whole launch
+  // the block's Wc tiles stay in for the whole launch
   {
     const W* src = reinterpret_cast<const W*>(a.tiles) + (size_t)tile0 * 16 * kp;
     const size_t n16 = (size_t)ntiles * 16 * kp * sizeof(W) / 16;
     const uint4* s4 = reinterpret_cast<const uint4*>(src);
     uint4* d4 = reinterpret_cast<uint4*>(tiles_lds);
-    for (size_t i = tid; i < n16; i += blockDim.x) d4[i] = s4[i];
+    for (size_t i = tid; i < n16; i += NT) d4[i] = s4[i];
   }
   __syncthreads();
 
@@ -413,7 +414,6 @@ __device__ __forceinline__ void worker_main(const TreeArgs& a, unsigned char* ld
 // ---------------------------------------------------------------------------
 // controller: one request's candidates, records, frontier and GRU states
 
-#define LDS
 
 enum {
   C_NF,      // frontier entries [fh, nf) of buffer fb
@@ -430,88 +430,78 @@ enum {
   C_MISC
 };
 
-// LDS arrays of a controller (32-bit LDS addresses)
+// A node record and a candidate of a depth, as kept in LDS.
+struct Rec {
+  uint64_t key;  // record key; record 0 is the root
+  int par;       // parent record (-1 for the root)
+  int slot;      // exchange slot holding the record's state (-1: not expanded)
+};
+struct Cand {
+  int id;     // token id
+  int rank;   // rank of the token id within its depth
+  float val;  // base logit
+  int pad;
+};
+
+// Fixed-size per-step state at the start of a controller's (compile-time
+// offsets, so that accesses need no address registers).
+struct CtlFixed {
+  int misc[32];
+  uint64_t tau;        // frontier entries with key_u < tau are out (when C_TAUSET)
+  int cnt[QCAP];       // records ahead of each tested frontier entry
+  int perm[QCAP];      // tested entries in the total order
+  int acc[QCAP];       // tested entries taken
+  int ex_rec[PMAX];    // records expanded in the step
+  int ex_ws[PMAX];     // their depth slots
+  int ex_dep[PMAX];    // their depths
+  int ex_tok[PMAX];    // their tokens
+  int ex_src[PMAX];    // exchange slots of their parents
+  int wdep[PMAX];      // depth held by each W2 slot (-1: none)
+  int wclaim[PMAX];    // slot used by a node of the next step
+  int lslots[PMAX];    // slots to load before the next step
+  float z[PMAX * 64];  // corrected, tempered candidate logits
+};
+
+// LDS arrays of a controller
 struct CtlLds {
-  LDS int* cid;         // [D*M] candidate token ids
-  LDS float* cval;      // [D*M] their base logits
-  LDS int* crank;       // [D*M] rank of each candidate's token id within its depth
-  LDS float* tailv;     // [D]
-  LDS uint64_t* rkey;   // [xcap] record keys; record 0 is the root
-  LDS int* rpar;        // [xcap] parent record (-1 for the root)
-  LDS int* rslot;       // [xcap] exchange slot holding the record's state (-1: not expanded)
-  LDS int* rrank;       // [xcap] position in the total order (compaction and output)
-  LDS uint64_t* trk;    // [xcap] compaction staging
-  LDS int* trp;         // [xcap]
-  LDS int* trs;         // [xcap]
-  LDS uint64_t* front;  // [2][fcap] frontier keys, sorted descending, in buffer misc[C_FB]
-  LDS uint64_t* nc;     // [p*k] children keys of this step (0 = none)
-  LDS uint64_t* ncs;    // [p*k] live children sorted descending
-  LDS int* pn;          // [p*k] their insertion points in the frontier
-  LDS unsigned char* w2s;  // [nslots][M][r + pad] W2 rows of the candidates of each slot's depth
-  LDS float* ps;        // [nslots][r] P rows
-  LDS int* wdep;        // [nslots] depth held by each slot (-1: none)
-  LDS int* wclaim;      // [nslots] slot used by a node of the next step
-  LDS int* lslots;      // [nslots] slots to load before the next step
-  LDS int* ex_rec;      // [p] records expanded in the step
-  LDS int* ex_ws;       // [p] their depth slots
-  LDS int* ex_dep;      // [p] their depths
-  LDS int* ex_tok;      // [p] their tokens
-  LDS int* ex_src;      // [p] exchange slots of their parents
-  LDS float* av;        // [p][r] SiLU(u + P)
-  LDS float* z;         // [p][64] corrected, tempered candidate logits
-  LDS int* cnt;         // [QCAP] records ahead of each tested frontier entry
-  LDS int* perm;        // [QCAP] tested entries in the total order
-  LDS int* acc;         // [QCAP] tested entries taken
-  LDS int* misc;        // [C_MISC]
-  LDS uint64_t* tau;    // [1]
+  CtlFixed* f;
+  Cand* cand;           // [D*M]
+  float* tailv;         // [D]
+  Rec* rec;             // [xcap]
+  int* rrank;           // [xcap] position in the total order (compaction and output)
+  Rec* trec;            // [xcap] compaction staging
+  uint64_t* front;      // [2][fcap] frontier keys, sorted descending, in buffer misc[C_FB]
+  uint64_t* nc;         // [p*k] children keys of this step (0 = none)
+  uint64_t* ncs;        // [p*k] live children sorted descending
+  int* pn;              // [p*k] their insertion points in the frontier
+  unsigned char* w2s;   // [nslots][M][r + pad] W2 rows of the candidates of each slot's depth
+  float* ps;            // [nslots][r] P rows
+  float* av;            // [p][r] SiLU(u + P)
 };
 
-enum {
-  L_CID, L_CVAL, L_CRANK, L_TAIL, L_RKEY, L_RPAR, L_RSLOT, L_RRANK, L_TRK, L_TRP, L_TRS, L_FRONT, L_NC, L_NCS,
-  L_PN, L_W2S, L_PS, L_WDEP, L_WCLAIM, L_LSLOTS, L_EXREC, L_EXWS, L_EXDEP, L_EXTOK, L_EXSRC, L_AV, L_Z, L_CNT,
-  L_PERM, L_ACC, L_MISC, L_TAU, L_COUNT
-};
+enum { L_FIXED, L_CAND, L_TAIL, L_REC, L_RRANK, L_TREC, L_FRONT, L_NC, L_NCS, L_PN, L_W2S, L_PS, L_AV, L_COUNT };
 
-// elements per LDS row of W2 candidate weights: r plus 16 bytes, so that the
+// elements per row of W2 candidate weights: r plus 16 bytes, so that the
 // rows of consecutive candidates start in different banks
 __host__ __device__ inline int w2s_stride(int r, int esz) { return r + 16 / esz; }
 
-// byte offsets of the controller's LDS arrays; returns the total
+// byte offsets of the controller's arrays; returns the total
 __host__ __device__ inline size_t ctl_offsets(const TreeArgs& a, int esz, size_t* off) {
   const size_t DM = (size_t)a.D * a.M, pk = (size_t)a.p * a.k, X = (size_t)a.xcap, P = (size_t)a.p;
   size_t sz[L_COUNT];
-  sz[L_CID] = DM * 4;
-  sz[L_CVAL] = DM * 4;
-  sz[L_CRANK] = DM * 4;
+  sz[L_FIXED] = sizeof(CtlFixed);
+  sz[L_CAND] = DM * sizeof(Cand);
   sz[L_TAIL] = (size_t)a.D * 4;
-  sz[L_RKEY] = X * 8;
-  sz[L_RPAR] = X * 4;
-  sz[L_RSLOT] = X * 4;
+  sz[L_REC] = X * sizeof(Rec);
   sz[L_RRANK] = X * 4;
-  sz[L_TRK] = X * 8;
-  sz[L_TRP] = X * 4;
-  sz[L_TRS] = X * 4;
+  sz[L_TREC] = X * sizeof(Rec);
   sz[L_FRONT] = (size_t)2 * a.fcap * 8;
   sz[L_NC] = pk * 8;
   sz[L_NCS] = pk * 8;
   sz[L_PN] = pk * 4;
   sz[L_W2S] = (size_t)a.nslots * a.M * w2s_stride(a.r, esz) * esz;
   sz[L_PS] = (size_t)a.nslots * a.r * 4;
-  sz[L_WDEP] = (size_t)a.nslots * 4;
-  sz[L_WCLAIM] = (size_t)a.nslots * 4;
-  sz[L_LSLOTS] = (size_t)a.nslots * 4;
-  sz[L_EXREC] = P * 4;
-  sz[L_EXWS] = P * 4;
-  sz[L_EXDEP] = P * 4;
-  sz[L_EXTOK] = P * 4;
-  sz[L_EXSRC] = P * 4;
   sz[L_AV] = P * a.r * 4;
-  sz[L_Z] = P * 64 * 4;
-  sz[L_CNT] = QCAP * 4;
-  sz[L_PERM] = QCAP * 4;
-  sz[L_ACC] = QCAP * 4;
-  sz[L_MISC] = C_MISC * 4;
-  sz[L_TAU] = 8;
   size_t o = 0;
   for (int i = 0; i < L_COUNT; ++i) {
     off[i] = o;
@@ -524,44 +514,25 @@ __device__ __forceinline__ CtlLds ctl_carve(unsigned char* lds, const TreeArgs& 
   size_t off[L_COUNT];
   ctl_offsets(a, esz, off);
   CtlLds c;
-  c.cid = (LDS int*)(lds + off[L_CID]);
-  c.cval = (LDS float*)(lds + off[L_CVAL]);
-  c.crank = (LDS int*)(lds + off[L_CRANK]);
-  c.tailv = (LDS float*)(lds + off[L_TAIL]);
-  c.rkey = (LDS uint64_t*)(lds + off[L_RKEY]);
-  c.rpar = (LDS int*)(lds + off[L_RPAR]);
-  c.rslot = (LDS int*)(lds + off[L_RSLOT]);
-  c.rrank = (LDS int*)(lds + off[L_RRANK]);
-  c.trk = (LDS uint64_t*)(lds + off[L_TRK]);
-  c.trp = (LDS int*)(lds + off[L_TRP]);
-  c.trs = (LDS int*)(lds + off[L_TRS]);
-  c.front = (LDS uint64_t*)(lds + off[L_FRONT]);
-  c.nc = (LDS uint64_t*)(lds + off[L_NC]);
-  c.ncs = (LDS uint64_t*)(lds + off[L_NCS]);
-  c.pn = (LDS int*)(lds + off[L_PN]);
-  c.w2s = (LDS unsigned char*)(lds + off[L_W2S]);
-  c.ps = (LDS float*)(lds + off[L_PS]);
-  c.wdep = (LDS int*)(lds + off[L_WDEP]);
-  c.wclaim = (LDS int*)(lds + off[L_WCLAIM]);
-  c.lslots = (LDS int*)(lds + off[L_LSLOTS]);
-  c.ex_rec = (LDS int*)(lds + off[L_EXREC]);
-  c.ex_ws = (LDS int*)(lds + off[L_EXWS]);
-  c.ex_dep = (LDS int*)(lds + off[L_EXDEP]);
-  c.ex_tok = (LDS int*)(lds + off[L_EXTOK]);
-  c.ex_src = (LDS int*)(lds + off[L_EXSRC]);
-  c.av = (LDS float*)(lds + off[L_AV]);
-  c.z = (LDS float*)(lds + off[L_Z]);
-  c.cnt = (LDS int*)(lds + off[L_CNT]);
-  c.perm = (LDS int*)(lds + off[L_PERM]);
-  c.acc = (LDS int*)(lds + off[L_ACC]);
-  c.misc = (LDS int*)(lds + off[L_MISC]);
-  c.tau = (LDS uint64_t*)(lds + off[L_TAU]);
+  c.f = reinterpret_cast<CtlFixed*>(lds);
+  c.cand = reinterpret_cast<Cand*>(lds + off[L_CAND]);
+  c.tailv = reinterpret_cast<float*>(lds + off[L_TAIL]);
+  c.rec = reinterpret_cast<Rec*>(lds + off[L_REC]);
+  c.rrank = reinterpret_cast<int*>(lds + off[L_RRANK]);
+  c.trec = reinterpret_cast<Rec*>(lds + off[L_TREC]);
+  c.front = reinterpret_cast<uint64_t*>(lds + off[L_FRONT]);
+  c.nc = reinterpret_cast<uint64_t*>(lds + off[L_NC]);
+  c.ncs = reinterpret_cast<uint64_t*>(lds + off[L_NCS]);
+  c.pn = reinterpret_cast<int*>(lds + off[L_PN]);
+  c.w2s = lds + off[L_W2S];
+  c.ps = reinterpret_cast<float*>(lds + off[L_PS]);
+  c.av = reinterpret_cast<float*>(lds + off[L_AV]);
   return c;
 }
 
 // the frontier buffer currently in use
-__device__ __forceinline__ LDS uint64_t* cur_front(const TreeArgs& a, const CtlLds& c) {
-  return c.front + (size_t)c.misc[C_FB] * a.fcap;
+__device__ __forceinline__ uint64_t* cur_front(const TreeArgs& a, const CtlLds& c) {
+  return c.front + (size_t)c.f->misc[C_FB] * a.fcap;
 }
 
 // Logistic function and tanh from the hardware exp2 and reciprocal (about
@@ -576,10 +547,10 @@ __device__ __forceinline__ float tanh_(float x) { return 2.0f * sigm(2.0f * x) -
 __device__ __forceinline__ bool rec_better(const CtlLds& c, int x, int y) {
   for (int it = 0; it < 32; ++it) {
     if (x == y || x < 0 || y < 0) return false;
-    const uint64_t ux = key_u(c.rkey[x]), uy = key_u(c.rkey[y]);
+    const uint64_t ux = key_u(c.rec[x].key), uy = key_u(c.rec[y].key);
     if (ux != uy) return ux > uy;
-    x = c.rpar[x];
-    y = c.rpar[y];
+    x = c.rec[x].par;
+    y = c.rec[y].par;
   }
   return false;
 }
@@ -593,18 +564,18 @@ __device__ __forceinline__ bool entry_better(const CtlLds& c, uint64_t f, uint64
 
 // rrank[x] = number of records that precede record x
 __device__ __forceinline__ void ctl_rank(const CtlLds& c, int nx) {
-  for (int x = threadIdx.x; x < nx; x += blockDim.x) {
-    const uint64_t xu = key_u(c.rkey[x]);
-    const int xp = c.rpar[x];
+  for (int x = threadIdx.x; x < nx; x += NT) {
+    const uint64_t xu = key_u(c.rec[x].key);
+    const int xp = c.rec[x].par;
     int r = 0, ties = 0;
     for (int y = 0; y < nx; ++y) {
-      const uint64_t yu = key_u(c.rkey[y]);
+      const uint64_t yu = key_u(c.rec[y].key);
       r += yu > xu;
       ties += yu == xu;
     }
     if (ties > 1)  // equal keys: the parents' order decides
       for (int y = 0; y < nx; ++y)
-        if (y != x && key_u(c.rkey[y]) == xu && rec_better(c, c.rpar[y], xp)) ++r;
+        if (y != x && key_u(c.rec[y].key) == xu && rec_better(c, c.rec[y].par, xp)) ++r;
     c.rrank[x] = r;
   }
 }
@@ -614,18 +585,18 @@ __device__ __forceinline__ void ctl_rank(const CtlLds& c, int nx) {
 template <typename W>
 __device__ __forceinline__ void ctl_prefetch(const TreeArgs& a, const CtlLds& c, int b) {
   const int tid = threadIdx.x, M = a.M, r = a.r;
-  const int nl = c.misc[C_NL];
+  const int nl = c.f->misc[C_NL];
   if (nl == 0) return;
   const W* w2t = reinterpret_cast<const W*>(a.w2t);
   const int rs = w2s_stride(r, (int)sizeof(W));
   const int rows = nl * M;
   const int per = r * (int)sizeof(W) / 16;   // 16-byte pieces per row
-  const int rsp = rs * (int)sizeof(W) / 16;  // pieces per LDS row
+  const int rsp = rs * (int)sizeof(W) / 16;  // pieces per row
   if ((r * (int)sizeof(W)) % 16 == 0 && per <= 256 && 256 % per == 0) {
     const int rpt = 256 / per;  // rows per pass
     const int pc = tid % per, r0 = tid / per;
     constexpr int U = 8;
-    LDS uint4* dst4 = (LDS uint4*)c.w2s;
+    uint4* dst4 = (uint4*)c.w2s;
     for (int rb = 0; rb < rows; rb += U * rpt) {
       uint4 v[U];
       int dst[U];
@@ -633,24 +604,24 @@ __device__ __forceinline__ void ctl_prefetch(const TreeArgs& a, const CtlLds& c,
       for (int q = 0; q < U; ++q) {  // clamped: every lane loads a valid piece
         const int row = min(rb + r0 + q * rpt, rows - 1);
         const int li = row / M, m = row - li * M;
-        const int s = c.lslots[li];
+        const int s = c.f->lslots[li];
         dst[q] = (s * M + m) * rsp + pc;
-        v[q] = reinterpret_cast<const uint4*>(w2t + (size_t)c.cid[c.wdep[s] * M + m] * r)[pc];
+        v[q] = reinterpret_cast<const uint4*>(w2t + (size_t)c.cand[c.f->wdep[s] * M + m].id * r)[pc];
       }
 #pragma unroll
       for (int q = 0; q < U; ++q) dst4[dst[q]] = v[q];  // unconditional
     }
   } else {
-    LDS W* w2s = (LDS W*)c.w2s;
-    for (int i = tid; i < rows * r; i += blockDim.x) {
+    W* w2s = (W*)c.w2s;
+    for (int i = tid; i < rows * r; i += NT) {
       const int row = i / r, j = i % r;
-      const int s = c.lslots[row / M], m = row % M;
-      w2s[((size_t)s * M + m) * rs + j] = w2t[(size_t)c.cid[c.wdep[s] * M + m] * r + j];
+      const int s = c.f->lslots[row / M], m = row % M;
+      w2s[((size_t)s * M + m) * rs + j] = w2t[(size_t)c.cand[c.f->wdep[s] * M + m].id * r + j];
     }
   }
-  for (int i = tid; i < nl * r; i += blockDim.x) {
-    const int s = c.lslots[i / r], j = i % r;
-    c.ps[(size_t)s * r + j] = a.P[((size_t)b * a.D + c.wdep[s]) * r + j];
+  for (int i = tid; i < nl * r; i += NT) {
+    const int s = c.f->lslots[i / r], j = i % r;
+    c.ps[(size_t)s * r + j] = a.P[((size_t)b * a.D + c.f->wdep[s]) * r + j];
   }
 }
 
@@ -665,7 +636,7 @@ __device__ __forceinline__ void ctl_expand(const TreeArgs& a, const CtlLds& c, i
   {
     const int us = u_stride(r);
     const float* ub = a.u + slot_of(a, t, b, 0) * us;  // the e slots are consecutive
-    for (int i = tid; i < r; i += blockDim.x) {
+    for (int i = tid; i < r; i += NT) {
       float uv[PMAX];
 #pragma unroll
       for (int j = 0; j < PMAX; ++j)
@@ -673,7 +644,7 @@ __device__ __forceinline__ void ctl_expand(const TreeArgs& a, const CtlLds& c, i
 #pragma unroll
       for (int j = 0; j < PMAX; ++j)
         if (j < e) {
-          const float x = uv[j] + c.ps[c.ex_ws[j] * r + i];
+          const float x = uv[j] + c.ps[c.f->ex_ws[j] * r + i];
           c.av[j * r + i] = x * sigm(x);
         }
     }
@@ -682,30 +653,34 @@ __device__ __forceinline__ void ctl_expand(const TreeArgs& a, const CtlLds& c, i
   // dL_{j,m} = W2[:, cand_m] . a_j: tpc threads per (node, candidate), each a
   // contiguous slice of the rank, combined in a fixed order
   {
-    const int nd = e * M;
-    int tpc = 1;
-    while (tpc * 2 * nd <= (int)blockDim.x && tpc < 64) tpc *= 2;
-    const int len = (r + tpc - 1) / tpc;
+    // candidates padded to a power of two so that the index splits are shifts
+    int lm = 0;
+    while ((1 << lm) < M) ++lm;
+    const int nd = e << lm;
+    int lt = 0;  // log2 of the threads per (node, candidate)
+    while ((2 << lt) * nd <= NT && lt < 6) ++lt;
+    const int tpc = 1 << lt;
+    const int len = (r + tpc - 1) >> lt;
     const int rs = w2s_stride(r, (int)sizeof(W));
     constexpr int VE = 16 / sizeof(W);  // elements per 16-byte piece
-    for (int base = 0; base < nd * tpc; base += blockDim.x) {
+    const bool vec = (len % VE) == 0 && (r * (int)sizeof(W)) % 16 == 0 && (len << lt) == r;
+    for (int base = 0; base < nd * tpc; base += NT) {
       const int idx = base + tid;
-      const int pr = idx / tpc, part = idx % tpc;
+      const int pr = idx >> lt, part = idx & (tpc - 1);
+      const int j = pr >> lm, m = pr & ((1 << lm) - 1);
+      const bool valid = pr < nd && m < M;
       float dl = 0.f;
-      int j = 0, m = 0;
-      if (pr < nd) {
-        j = pr / M;
-        m = pr - j * M;
-        const LDS W* wrow = (const LDS W*)c.w2s + (c.ex_ws[j] * M + m) * rs;
-        const LDS float* avj = c.av + j * r;
+      if (valid) {
+        const W* wrow = (const W*)c.w2s + (c.f->ex_ws[j] * M + m) * rs;
+        const float* avj = c.av + j * r;
         const int j0 = part * len, j1 = min(r, j0 + len);
-        if (j1 - j0 == len && len % VE == 0 && (r * (int)sizeof(W)) % 16 == 0) {
+        if (vec) {
           for (int q0 = j0; q0 < j1; q0 += VE) {
-            const uint4 wv4 = *(const LDS uint4*)(wrow + q0);
+            const uint4 wv4 = *(const uint4*)(wrow + q0);
             const W* we = reinterpret_cast<const W*>(&wv4);
 #pragma unroll
             for (int q = 0; q < VE; q += 4) {
-              const float4 a4 = *(const LDS float4*)(avj + q0 + q);
+              const float4 a4 = *(const float4*)(avj + q0 + q);
               dl = fmaf(w_to_f32<W>(we[q]), a4.x, dl);
               dl = fmaf(w_to_f32<W>(we[q + 1]), a4.y, dl);
               dl = fmaf(w_to_f32<W>(we[q + 2]), a4.z, dl);
@@ -717,7 +692,7 @@ __device__ __forceinline__ void ctl_expand(const TreeArgs& a, const CtlLds& c, i
         }
       }
       for (int s = 1; s < tpc; s <<= 1) dl += __shfl_xor(dl, s);
-      if (pr < nd && part == 0) c.z[j * 64 + m] = (c.cval[c.ex_dep[j] * M + m] + dl) / a.T + 0.0f;
+      if (valid && part == 0) c.f->z[j * 64 + m] = (c.cand[c.f->ex_dep[j] * M + m].val + dl) / a.T + 0.0f;
     }
   }
   __syncthreads();
@@ -725,12 +700,12 @@ __device__ __forceinline__ void ctl_expand(const TreeArgs& a, const CtlLds& c, i
   // (plus the base tail under fullv), rank by (z desc, token asc), keep the k
   // best with a finite log-prob.  -inf log-probs rank after every finite one.
   for (int j = wv; j < e; j += 4) {
-    const int y = c.ex_rec[j];
-    const int dy = c.ex_dep[j];
-    const float yscore = key_score(c.rkey[y]);
+    const int y = c.f->ex_rec[j];
+    const int dy = c.f->ex_dep[j];
+    const float yscore = key_score(c.rec[y].key);
     const bool has = lane < M;
-    const float zv = has ? c.z[j * 64 + lane] : -INFINITY;
-    const int idv = has ? c.cid[dy * M + lane] : 0x7FFFFFFF;
+    const float zv = has ? c.f->z[j * 64 + lane] : -INFINITY;
+    const int idv = has ? c.cand[dy * M + lane].id : 0x7FFFFFFF;
     float mx = wave_max_dpp(zv);
     const float tl = a.fullv ? c.tailv[dy] : -INFINITY;
     mx = fmaxf(mx, tl);
@@ -752,9 +727,9 @@ __device__ __forceinline__ void ctl_expand(const TreeArgs& a, const CtlLds& c, i
     }
     const bool ok = has && isfinite(lp);
     if (has && rank < k)
-      c.nc[j * k + rank] = ok ? make_key(yscore + lp, dy + 1, c.crank[dy * M + lane], y, lane) : 0ull;
+      c.nc[j * k + rank] = ok ? make_key(yscore + lp, dy + 1, c.cand[dy * M + lane].rank, y, lane) : 0ull;
   }
-  if (tid == 0) c.misc[C_NV] = 0;
+  if (tid == 0) c.f->misc[C_NV] = 0;
   __syncthreads();
 }
 
@@ -765,11 +740,11 @@ __device__ __forceinline__ void ctl_expand(const TreeArgs& a, const CtlLds& c, i
 // entries ahead of it.  Also resets the pop state of the step.
 __device__ __forceinline__ void ctl_merge(const TreeArgs& a, const CtlLds& c, int nnew) {
   const int tid = threadIdx.x;
-  const int fh = c.misc[C_FH], nf = c.misc[C_NF], fb = c.misc[C_FB];
-  const bool tauset = c.misc[C_TAUSET] != 0;
-  const uint64_t tau = *c.tau;
-  const LDS uint64_t* F = c.front + (size_t)fb * a.fcap + fh;
-  LDS uint64_t* O = c.front + (size_t)(1 - fb) * a.fcap;
+  const int fh = c.f->misc[C_FH], nf = c.f->misc[C_NF], fb = c.f->misc[C_FB];
+  const bool tauset = c.f->misc[C_TAUSET] != 0;
+  const uint64_t tau = c.f->tau;
+  const uint64_t* F = c.front + (size_t)fb * a.fcap + fh;
+  uint64_t* O = c.front + (size_t)(1 - fb) * a.fcap;
   // live old entries: a prefix of the sorted frontier
   int na = nf - fh;
   if (tauset) {
@@ -781,7 +756,7 @@ __device__ __forceinline__ void ctl_merge(const TreeArgs& a, const CtlLds& c, in
     }
     na = lo;
   }
-  for (int i = tid; i < nnew; i += blockDim.x) {
+  for (int i = tid; i < nnew; i += NT) {
     const uint64_t key = c.nc[i];
     if (key != 0 && (!tauset || key_u(key) >= tau)) {
       int rn = 0;  // live new entries ahead (any key above a live one is live)
@@ -794,13 +769,13 @@ __device__ __forceinline__ void ctl_merge(const TreeArgs& a, const CtlLds& c, in
       }
       c.ncs[rn] = key;
       c.pn[rn] = lo;
-      atomicAdd((int*)&c.misc[C_NV], 1);
+      atomicAdd(&c.f->misc[C_NV], 1);
     }
   }
   __syncthreads();
-  const int nv = c.misc[C_NV];
-  // (k - 1) xcap + 1 bounds the frontier; the guard only keeps LDS intact
-  for (int i = tid; i < na; i += blockDim.x) {
+  const int nv = c.f->misc[C_NV];
+  // (k - 1) xcap + 1 bounds the frontier; the guard only keeps intact
+  for (int i = tid; i < na; i += NT) {
     int lo = 0, hi = nv;  // new entries with insertion point <= i go ahead of it
     while (lo < hi) {
       const int mid = (lo + hi) >> 1;
@@ -809,17 +784,17 @@ __device__ __forceinline__ void ctl_merge(const TreeArgs& a, const CtlLds& c, in
     }
     if (i + lo < a.fcap) O[i + lo] = F[i];
   }
-  for (int rr = tid; rr < nv; rr += blockDim.x)
+  for (int rr = tid; rr < nv; rr += NT)
     if (rr + c.pn[rr] < a.fcap) O[rr + c.pn[rr]] = c.ncs[rr];
   if (tid == 0) {
     if (na + nv > a.fcap) atomicOr(a.err, 4);
-    c.misc[C_FB] = 1 - fb;
-    c.misc[C_FH] = 0;
-    c.misc[C_NF] = min(na + nv, a.fcap);
-    c.misc[C_E] = 0;
-    c.misc[C_STOP] = 0;
-    c.misc[C_NL] = 0;
-    for (int s = 0; s < a.nslots; ++s) c.wclaim[s] = 0;
+    c.f->misc[C_FB] = 1 - fb;
+    c.f->misc[C_FH] = 0;
+    c.f->misc[C_NF] = min(na + nv, a.fcap);
+    c.f->misc[C_E] = 0;
+    c.f->misc[C_STOP] = 0;
+    c.f->misc[C_NL] = 0;
+    for (int s = 0; s < a.nslots; ++s) c.f->wclaim[s] = 0;
   }
   __syncthreads();
 }
@@ -830,26 +805,26 @@ __device__ __forceinline__ void ctl_merge(const TreeArgs& a, const CtlLds& c, in
 // dropped parent.
 __device__ __forceinline__ void ctl_compact(const TreeArgs& a, const CtlLds& c) {
   const int tid = threadIdx.x, N = a.N;
-  const int nx = c.misc[C_NX];
+  const int nx = c.f->misc[C_NX];
   ctl_rank(c, nx);
   __syncthreads();
-  for (int x = tid; x < nx; x += blockDim.x) {
+  for (int x = tid; x < nx; x += NT) {
     const int rk = c.rrank[x];
     if (rk <= N) {
-      c.trk[rk] = c.rkey[x];
-      c.trp[rk] = c.rpar[x] >= 0 ? c.rrank[c.rpar[x]] : -1;
-      c.trs[rk] = c.rslot[x];
+      c.trec[rk].key = c.rec[x].key;
+      c.trec[rk].par = c.rec[x].par >= 0 ? c.rrank[c.rec[x].par] : -1;
+      c.trec[rk].slot = c.rec[x].slot;
     }
     if (rk == N) {
-      const uint64_t u = key_u(c.rkey[x]);
-      if (!c.misc[C_TAUSET] || u > *c.tau) *c.tau = u;
+      const uint64_t u = key_u(c.rec[x].key);
+      if (!c.f->misc[C_TAUSET] || u > c.f->tau) c.f->tau = u;
     }
   }
   __syncthreads();
-  const int fh = c.misc[C_FH], nf = c.misc[C_NF], fb = c.misc[C_FB];
-  const LDS uint64_t* F = c.front + (size_t)fb * a.fcap + fh;
-  LDS uint64_t* O = c.front + (size_t)(1 - fb) * a.fcap;
-  const uint64_t tauN = *c.tau;
+  const int fh = c.f->misc[C_FH], nf = c.f->misc[C_NF], fb = c.f->misc[C_FB];
+  const uint64_t* F = c.front + (size_t)fb * a.fcap + fh;
+  uint64_t* O = c.front + (size_t)(1 - fb) * a.fcap;
+  const uint64_t tauN = c.f->tau;
   int na = nf - fh;
   {
     int lo = 0, hi = na;
@@ -860,34 +835,34 @@ __device__ __forceinline__ void ctl_compact(const TreeArgs& a, const CtlLds& c) 
     }
     na = lo;
   }
-  for (int i = tid; i < na; i += blockDim.x) O[i] = key_with_parent(F[i], c.rrank[key_parent(F[i])]);
+  for (int i = tid; i < na; i += NT) O[i] = key_with_parent(F[i], c.rrank[key_parent(F[i])]);
   const int nk = min(nx, N + 1);
-  for (int x = tid; x < nk; x += blockDim.x) {
-    c.rkey[x] = c.trk[x];
-    c.rpar[x] = c.trp[x];
-    c.rslot[x] = c.trs[x];
+  for (int x = tid; x < nk; x += NT) {
+    c.rec[x].key = c.trec[x].key;
+    c.rec[x].par = c.trec[x].par;
+    c.rec[x].slot = c.trec[x].slot;
   }
   __syncthreads();
   if (tid == 0) {
-    c.misc[C_NX] = nk;
-    c.misc[C_FB] = 1 - fb;
-    c.misc[C_FH] = 0;
-    c.misc[C_NF] = na;
-    c.misc[C_TAUSET] = 1;
+    c.f->misc[C_NX] = nk;
+    c.f->misc[C_FB] = 1 - fb;
+    c.f->misc[C_FH] = 0;
+    c.f->misc[C_NF] = na;
+    c.f->misc[C_TAUSET] = 1;
   }
   __syncthreads();
 }
 
 // An over-long group of equal key_u at the head: rotate its best entry (in the
 // total order) to the head; it is then tested alone.  Thread 0 only.
-__device__ __forceinline__ void ctl_batch_group(const CtlLds& c, LDS uint64_t* F, int fh, int nf, uint64_t u) {
+__device__ __forceinline__ void ctl_batch_group(const CtlLds& c, uint64_t* F, int fh, int nf, uint64_t u) {
   int g = fh;
   for (int i = fh + 1; i < nf && key_u(F[i]) == u; ++i)
     if (entry_better(c, F[i], F[g])) g = i;
   const uint64_t best = F[g];
   for (int i = g; i > fh; --i) F[i] = F[i - 1];
   F[fh] = best;
-  c.misc[C_G] = g;  // where to put it back if it is neither taken nor out
+  c.f->misc[C_G] = g;  // where to put it back if it is neither taken nor out
 }
 
 // Take frontier entries for the next step (t + 1): up to p nodes to expand,
@@ -896,14 +871,14 @@ __device__ __forceinline__ int ctl_pop(const TreeArgs& a, const CtlLds& c, int b
   const int tid = threadIdx.x, lane = tid & 63;
   const int N = a.N, D = a.D, M = a.M;
   for (int round = 0; round < 4 * XMAX; ++round) {
-    if (c.misc[C_NX] + a.qmax > a.xcap) {
-      if (c.misc[C_E] > 0) break;  // expand what was taken; compact next step
+    if (c.f->misc[C_NX] + a.qmax > a.xcap) {
+      if (c.f->misc[C_E] > 0) break;  // expand what was taken; compact next step
       ctl_compact(a, c);
     }
     // the batch: the first Q entries, not ending inside a group of equal key_u
-    // (every thread computes the same Q from the same LDS words)
-    const int fh = c.misc[C_FH], nf = c.misc[C_NF], nx = c.misc[C_NX];
-    LDS uint64_t* F = cur_front(a, c) + fh;
+    // (every thread computes the same Q from the same words)
+    const int fh = c.f->misc[C_FH], nf = c.f->misc[C_NF], nx = c.f->misc[C_NX];
+    uint64_t* F = cur_front(a, c) + fh;
     int Q = min(min(nf - fh, a.qmax), a.xcap - nx);
     bool group = false;
     if (Q > 0 && Q < nf - fh && key_u(F[Q - 1]) == key_u(F[Q])) {
@@ -928,18 +903,18 @@ __device__ __forceinline__ int ctl_pop(const TreeArgs& a, const CtlLds& c, int b
       if (j < Q) {
         fu = key_u(F[j]);
         for (int y = s; y < nx; y += S) {
-          const uint64_t yu = key_u(c.rkey[y]);
+          const uint64_t yu = key_u(c.rec[y].key);
           cv += yu > fu;
           tie |= yu == fu;
         }
         if (tie) {  // equal keys: the parents' order decides
           const int fp = key_parent(F[j]);
           for (int y = s; y < nx; y += S)
-            if (key_u(c.rkey[y]) == fu && rec_better(c, c.rpar[y], fp)) ++cv;
+            if (key_u(c.rec[y].key) == fu && rec_better(c, c.rec[y].par, fp)) ++cv;
         }
       }
       for (int m = S >> 1; m >= 1; m >>= 1) cv += __shfl_xor(cv, m);
-      if (j < Q && s == 0) c.cnt[j] = cv;
+      if (j < Q && s == 0) c.f->cnt[j] = cv;
     }
     __syncthreads();
     // wave 0, lane jj = the jj-th batch entry in the total order: the taken
@@ -949,29 +924,29 @@ __device__ __forceinline__ int ctl_pop(const TreeArgs& a, const CtlLds& c, int b
       const bool tie = has && lane > 0 && key_u(F[lane]) == key_u(F[lane - 1]);
       const bool anytie = __ballot(tie) != 0;
       if (has) {
-        c.perm[lane] = lane;
-        c.acc[lane] = 0;
+        c.f->perm[lane] = lane;
+        c.f->acc[lane] = 0;
       }
       if (anytie && lane == 0)
         for (int i = 1; i < Q; ++i) {  // insertion sort in the total order
-          const int v = c.perm[i];
+          const int v = c.f->perm[i];
           int jj = i;
-          while (jj > 0 && entry_better(c, F[v], F[c.perm[jj - 1]])) {
-            c.perm[jj] = c.perm[jj - 1];
+          while (jj > 0 && entry_better(c, F[v], F[c.f->perm[jj - 1]])) {
+            c.f->perm[jj] = c.f->perm[jj - 1];
             --jj;
           }
-          c.perm[jj] = v;
+          c.f->perm[jj] = v;
         }
-      const int j = has ? c.perm[lane] : 0;
+      const int j = has ? c.f->perm[lane] : 0;
       const uint64_t key = has ? F[j] : 0ull;
       const int d = key_depth(key);
       const bool expd = has && d < D;
-      const bool out = has && c.cnt[j] + lane >= N + 1;
-      const int e0 = c.misc[C_E];
+      const bool out = has && c.f->cnt[j] + lane >= N + 1;
+      const int e0 = c.f->misc[C_E];
       // depth slots: a depth is new if no slot holds it and no earlier lane has it
       int held = 0, held_claimed = 0, nclaimed = 0;
       for (int s = 0; s < a.nslots; ++s) {
-        const int ws = c.wdep[s], wc = c.wclaim[s];
+        const int ws = c.f->wdep[s], wc = c.f->wclaim[s];
         held |= ws == d;
         held_claimed |= ws == d && wc;
         nclaimed += wc;
@@ -997,14 +972,14 @@ __device__ __forceinline__ int ctl_pop(const TreeArgs& a, const CtlLds& c, int b
         for (unsigned long long mm = bexp & lowA; mm; mm &= mm - 1)
           dm |= 1u << __builtin_amdgcn_readlane(d, __ffsll((long long)mm) - 1);
         for (int s = 0; s < a.nslots; ++s)
-          if (c.wdep[s] >= 0 && ((dm >> c.wdep[s]) & 1u)) c.wclaim[s] = 1;
+          if (c.f->wdep[s] >= 0 && ((dm >> c.f->wdep[s]) & 1u)) c.f->wclaim[s] = 1;
         for (unsigned long long mm = bnew & lowA; mm; mm &= mm - 1) {
           const int dq = __builtin_amdgcn_readlane(d, __ffsll((long long)mm) - 1);
           for (int s = 0; s < a.nslots; ++s)
-            if (!c.wclaim[s]) {
-              c.wclaim[s] = 1;
-              c.wdep[s] = dq;
-              c.lslots[c.misc[C_NL]++] = s;
+            if (!c.f->wclaim[s]) {
+              c.f->wclaim[s] = 1;
+              c.f->wdep[s] = dq;
+              c.f->lslots[c.f->misc[C_NL]++] = s;
               break;
             }
         }
@@ -1013,54 +988,54 @@ __device__ __forceinline__ int ctl_pop(const TreeArgs& a, const CtlLds& c, int b
       if (has && lane < A) {
         const int x = nx + lane;
         const int par = key_parent(key);
-        c.rkey[x] = key;
-        c.rpar[x] = par;
-        c.acc[j] = 1;
+        c.rec[x].key = key;
+        c.rec[x].par = par;
+        c.f->acc[j] = 1;
         if (expd) {
           const int ei = e0 + __popcll(bexp & le) - 1;
           int ws = 0;
           for (int s = 0; s < a.nslots; ++s)
-            if (c.wdep[s] == d) ws = s;
-          c.ex_rec[ei] = x;
-          c.ex_ws[ei] = ws;
-          c.ex_dep[ei] = d;
-          c.ex_tok[ei] = c.cid[(d - 1) * M + key_m(key)];
-          c.ex_src[ei] = c.rslot[par];
-          c.rslot[x] = (int)slot_of(a, t + 1, b, ei);
+            if (c.f->wdep[s] == d) ws = s;
+          c.f->ex_rec[ei] = x;
+          c.f->ex_ws[ei] = ws;
+          c.f->ex_dep[ei] = d;
+          c.f->ex_tok[ei] = c.cand[(d - 1) * M + key_m(key)].id;
+          c.f->ex_src[ei] = c.rec[par].slot;
+          c.rec[x].slot = (int)slot_of(a, t + 1, b, ei);
         } else {
-          c.rslot[x] = -1;
+          c.rec[x].slot = -1;
         }
       }
       if (lane == 0) {
         if (group && A == 0 && !isout) {  // put the group's best entry back in key order
-          const int g = c.misc[C_G] - fh;
+          const int g = c.f->misc[C_G] - fh;
           const uint64_t best = F[0];
           for (int i = 0; i < g; ++i) F[i] = F[i + 1];
           F[g] = best;
         }
         if (isout) {
-          const uint64_t u = key_u(F[c.perm[A]]);
-          if (!c.misc[C_TAUSET] || u > *c.tau) *c.tau = u;
-          c.misc[C_TAUSET] = 1;
-          c.misc[C_NF] = c.misc[C_FH] = 0;  // the rest of the frontier is out
+          const uint64_t u = key_u(F[c.f->perm[A]]);
+          if (!c.f->misc[C_TAUSET] || u > c.f->tau) c.f->tau = u;
+          c.f->misc[C_TAUSET] = 1;
+          c.f->misc[C_NF] = c.f->misc[C_FH] = 0;  // the rest of the frontier is out
         } else {
           if (anytie) {  // the taken entries may not be a key-order prefix
             int wpos = Q;
             for (int jj = Q - 1; jj >= 0; --jj)
-              if (!c.acc[jj]) F[--wpos] = F[jj];
+              if (!c.f->acc[jj]) F[--wpos] = F[jj];
           }
-          c.misc[C_FH] = fh + A;
+          c.f->misc[C_FH] = fh + A;
         }
         const int e1 = e0 + __popcll(bexp & lowA);
-        c.misc[C_E] = e1;
-        c.misc[C_NX] = nx + A;
-        c.misc[C_STOP] = isout || A < Q || e1 == a.p;
+        c.f->misc[C_E] = e1;
+        c.f->misc[C_NX] = nx + A;
+        c.f->misc[C_STOP] = isout || A < Q || e1 == a.p;
       }
     }
     __syncthreads();
-    if (c.misc[C_STOP]) break;
+    if (c.f->misc[C_STOP]) break;
   }
-  return c.misc[C_E];
+  return c.f->misc[C_E];
 }
 
 // Advance the GRU state of each node taken for step t1 from its parent's:
@@ -1075,22 +1050,22 @@ __device__ __forceinline__ void ctl_advance(const TreeArgs& a, const CtlLds& c, 
   if ((ds & 3) == 0) {
     const int n4 = ds >> 2;
     const int total = e * n4;
-    for (int base = 0; base < total; base += GA * (int)blockDim.x) {
+    for (int base = 0; base < total; base += GA * (int)NT) {
       float4 ir[GA], iz[GA], in[GA], hr[GA], hz[GA], hn[GA], sp[GA];
       int jv[GA], qv[GA];
 #pragma unroll
       for (int g = 0; g < GA; ++g) {  // clamped: every lane loads valid addresses
-        const int item = min(base + g * (int)blockDim.x + (int)threadIdx.x, total - 1);
+        const int item = min(base + g * (int)NT + (int)threadIdx.x, total - 1);
         const int j = item / n4;
         const int q = (item - j * n4) * 4;
         jv[g] = j;
         qv[g] = q;
-        int xs = c.ex_src[j];
+        int xs = c.f->ex_src[j];
         if (xs < 0) {  // every parent was expanded; the guard keeps addresses valid
           atomicOr(a.err, 8);
           xs = 0;
         }
-        const float* gi = a.G + (size_t)c.ex_tok[j] * 3 * ds + q;
+        const float* gi = a.G + (size_t)c.f->ex_tok[j] * 3 * ds + q;
         const float* gh = a.gh + (size_t)xs * gh_stride(ds) + q;
         ir[g] = *reinterpret_cast<const float4*>(gi);
         iz[g] = *reinterpret_cast<const float4*>(gi + ds);
@@ -1102,7 +1077,7 @@ __device__ __forceinline__ void ctl_advance(const TreeArgs& a, const CtlLds& c, 
       }
 #pragma unroll
       for (int g = 0; g < GA; ++g) {
-        if (base + g * (int)blockDim.x + (int)threadIdx.x < total) {
+        if (base + g * (int)NT + (int)threadIdx.x < total) {
           const float a0[4] = {ir[g].x, ir[g].y, ir[g].z, ir[g].w}, b0[4] = {hr[g].x, hr[g].y, hr[g].z, hr[g].w};
           const float a1[4] = {iz[g].x, iz[g].y, iz[g].z, iz[g].w}, b1[4] = {hz[g].x, hz[g].y, hz[g].z, hz[g].w};
           const float a2[4] = {in[g].x, in[g].y, in[g].z, in[g].w}, b2[4] = {hn[g].x, hn[g].y, hn[g].z, hn[g].w};
@@ -1123,13 +1098,13 @@ __device__ __forceinline__ void ctl_advance(const TreeArgs& a, const CtlLds& c, 
     }
   } else {
     for (int j = 0; j < e; ++j) {
-      const int xs = max(c.ex_src[j], 0);
-      const float* gi = a.G + (size_t)c.ex_tok[j] * 3 * ds;
+      const int xs = max(c.f->ex_src[j], 0);
+      const float* gi = a.G + (size_t)c.f->ex_tok[j] * 3 * ds;
       const float* gh = a.gh + (size_t)xs * gh_stride(ds);
       const float* sx = a.state + (size_t)xs * st_stride(ds);
       float* sy = a.state + (sl0 + j) * st_stride(ds);
       W* ay = reinterpret_cast<W*>(a.act) + (sl0 + j) * act_stride(ds);
-      for (int q = threadIdx.x; q < ds; q += blockDim.x) {
+      for (int q = threadIdx.x; q < ds; q += NT) {
         const float rg = sigm(gi[q] + gh[q]);
         const float zg = sigm(gi[ds + q] + gh[ds + q]);
         const float ng = tanh_(gi[2 * ds + q] + rg * gh[2 * ds + q]);
@@ -1140,30 +1115,30 @@ __device__ __forceinline__ void ctl_advance(const TreeArgs& a, const CtlLds& c, 
     }
   }
   const int kpad = k_padded(ds) - ds;  // zero k padding of the operand copies
-  for (int i = threadIdx.x; i < e * kpad; i += blockDim.x)
+  for (int i = threadIdx.x; i < e * kpad; i += NT)
     st_dev_act<W>(reinterpret_cast<W*>(a.act) + (sl0 + i / kpad) * act_stride(ds) + ds + i % kpad, 0.f, 0);
 }
 
 // outputs in the total order (node i = the record ranked i), padded past n
 __device__ __forceinline__ void ctl_output(const TreeArgs& a, const CtlLds& c, int b, bool failed) {
   const int tid = threadIdx.x, N = a.N, M = a.M;
-  const int nx = c.misc[C_NX];
+  const int nx = c.f->misc[C_NX];
   ctl_rank(c, nx);
   __syncthreads();
   const int n = min(N, nx - 1);
   const size_t o = (size_t)b * (N + 1);
-  for (int x = tid; x < nx; x += blockDim.x) {
+  for (int x = tid; x < nx; x += NT) {
     const int rk = c.rrank[x];
     if (rk > N) continue;
-    const uint64_t key = c.rkey[x];
+    const uint64_t key = c.rec[x].key;
     const bool root = x == 0;
     const int d = key_depth(key);
-    a.tokens[o + rk] = root ? -1 : c.cid[(d - 1) * M + key_m(key)];
-    a.parents[o + rk] = root ? -1 : c.rrank[c.rpar[x]];
+    a.tokens[o + rk] = root ? -1 : c.cand[(d - 1) * M + key_m(key)].id;
+    a.parents[o + rk] = root ? -1 : c.rrank[c.rec[x].par];
     a.depths[o + rk] = d;
     a.scores[o + rk] = key_score(key);
   }
-  for (int i = n + 1 + tid; i <= N; i += blockDim.x) {
+  for (int i = n + 1 + tid; i <= N; i += NT) {
     a.tokens[o + i] = -1;
     a.parents[o + i] = -1;
     a.depths[o + i] = -1;
@@ -1179,29 +1154,29 @@ __device__ __forceinline__ void controller_main(const TreeArgs& a, unsigned char
   const int D = a.D, M = a.M;
   const CtlLds c = ctl_carve(lds, a, (int)sizeof(W));
 
-  for (int i = tid; i < D * M; i += blockDim.x) {
-    c.cid[i] = a.cand_ids[(size_t)b * D * M + i];
-    c.cval[i] = a.cand_vals[(size_t)b * D * M + i];
-    c.crank[i] = a.tokrank[(size_t)b * D * M + i];
+  for (int i = tid; i < D * M; i += NT) {
+    c.cand[i].id = a.cand_ids[(size_t)b * D * M + i];
+    c.cand[i].val = a.cand_vals[(size_t)b * D * M + i];
+    c.cand[i].rank = a.tokrank[(size_t)b * D * M + i];
   }
-  for (int i = tid; i < D; i += blockDim.x) c.tailv[i] = a.tail[(size_t)b * D + i];
+  for (int i = tid; i < D; i += NT) c.tailv[i] = a.tail[(size_t)b * D + i];
   if (tid == 0) {
     // the root: score 0, depth 0; it precedes every other node
-    c.rkey[0] = make_key(0.f, 0, 0, 0, 0);
-    c.rpar[0] = -1;
-    c.rslot[0] = (int)slot_of(a, 0, b, 0);
-    c.misc[C_NX] = 1;
-    c.misc[C_NF] = c.misc[C_FH] = c.misc[C_FB] = 0;
-    c.misc[C_TAUSET] = 0;
-    *c.tau = 0;
-    for (int s = 0; s < a.nslots; ++s) c.wdep[s] = -1;
-    c.wdep[0] = 0;  // the root's children are at depth 1: row 0 of the tables
-    c.lslots[0] = 0;
-    c.misc[C_NL] = 1;
-    c.ex_rec[0] = 0;
-    c.ex_ws[0] = 0;
-    c.ex_dep[0] = 0;
-    c.misc[C_E] = 1;
+    c.rec[0].key = make_key(0.f, 0, 0, 0, 0);
+    c.rec[0].par = -1;
+    c.rec[0].slot = (int)slot_of(a, 0, b, 0);
+    c.f->misc[C_NX] = 1;
+    c.f->misc[C_NF] = c.f->misc[C_FH] = c.f->misc[C_FB] = 0;
+    c.f->misc[C_TAUSET] = 0;
+    c.f->tau = 0;
+    for (int s = 0; s < a.nslots; ++s) c.f->wdep[s] = -1;
+    c.f->wdep[0] = 0;  // the root's children are at depth 1: row 0 of the tables
+    c.f->lslots[0] = 0;
+    c.f->misc[C_NL] = 1;
+    c.f->ex_rec[0] = 0;
+    c.f->ex_ws[0] = 0;
+    c.f->ex_dep[0] = 0;
+    c.f->misc[C_E] = 1;
   }
   // root state and its GEMM operand copy
   {
@@ -1209,30 +1184,30 @@ __device__ __forceinline__ void controller_main(const TreeArgs& a, unsigned char
     const size_t sl = slot_of(a, 0, b, 0);
     float* s0 = a.state + sl * st_stride(ds);
     W* a0 = reinterpret_cast<W*>(a.act) + sl * act_stride(ds);
-    for (int j = tid; j < ds; j += blockDim.x) {
+    for (int j = tid; j < ds; j += NT) {
       const float v = a.root ? a.root[(size_t)b * ds + j] : 0.f;
       st_dev_f32(s0 + j, v);
       st_dev_act<W>(a0 + j, v, a.act_bf16);
     }
-    for (int j = ds + tid; j < k_padded(ds); j += blockDim.x) st_dev_act<W>(a0 + j, 0.f, 0);
+    for (int j = ds + tid; j < k_padded(ds); j += NT) st_dev_act<W>(a0 + j, 0.f, 0);
   }
   stores_done();
   __syncthreads();
-  for (int w = tid; w < a.n_workers; w += blockDim.x) st_dev_u32(a.mbox_w + (size_t)w * 32 + b, mbox_word(1, 1));
+  for (int w = tid; w < a.n_workers; w += NT) st_dev_u32(a.mbox_w + (size_t)w * 32 + b, mbox_word(1, 1));
   stores_done();
   ctl_prefetch<W>(a, c, b);
   __syncthreads();
 
   bool failed = false;
   for (int t = 0;; ++t) {
-    const int e = c.misc[C_E];
+    const int e = c.f->misc[C_E];
     const uint32_t epoch = (uint32_t)t + 1u;
     if (tid < 64) {
       const bool ok = wait_mbox(a.mbox_c + (size_t)b * 256, a.n_workers, epoch, a.err, a.spin_limit);
-      if (tid == 0) c.misc[C_OK] = ok;
+      if (tid == 0) c.f->misc[C_OK] = ok;
     }
     __syncthreads();
-    if (!c.misc[C_OK]) {
+    if (!c.f->misc[C_OK]) {
       failed = true;
       break;
     }
@@ -1248,14 +1223,14 @@ __device__ __forceinline__ void controller_main(const TreeArgs& a, unsigned char
     ctl_advance<W>(a, c, b, t + 1, e2);
     stores_done();
     __syncthreads();
-    for (int w = tid; w < a.n_workers; w += blockDim.x)
+    for (int w = tid; w < a.n_workers; w += NT)
       st_dev_u32(a.mbox_w + (size_t)w * 32 + b, mbox_word(t + 2, e2));
     stores_done();
     ctl_prefetch<W>(a, c, b);  // overlaps the workers' step
     __syncthreads();
   }
   // release the workers from this request
-  for (int w = tid; w < a.n_workers; w += blockDim.x) st_dev_u32(a.mbox_w + (size_t)w * 32 + b, MBOX_DONE);
+  for (int w = tid; w < a.n_workers; w += NT) st_dev_u32(a.mbox_w + (size_t)w * 32 + b, MBOX_DONE);
   stores_done();
   ctl_output(a, c, b, failed);
 }
