@@ -132,12 +132,12 @@ dt_status check_params(const dt_params* p, int V, const dt_params* maxp) {
   return DT_OK;
 }
 
-// tiles per worker: as few workers as fit beside the controllers
+// tiles per worker: one per worker when the workers fit beside the controllers
 int choose_tpw(const dt_handle* h, int B) {
   const char* env = getenv("DT_TILES_PER_WORKER");
   if (env && atoi(env) > 0) return atoi(env);
   const int avail = h->n_cu - B;
-  int tpw = 2;
+  int tpw = 1;
   while ((h->n_tiles + tpw - 1) / tpw > avail) ++tpw;
   return tpw;
 }

@@ -84,7 +84,7 @@ struct TreeArgs {
   unsigned spin_limit;
 };
 // Exchange columns a build may use per step (slots per step = B p <= this).
-constexpr int TREE_MAX_COLS = 64;
+constexpr int TREE_MAX_COLS = 128;
 // Fills the schedule fields of `a` (p from `pops`, 0 = automatic) and returns
 // the dynamic LDS bytes the launch needs, or 0 if the shape cannot be served.
 size_t plan_tree(TreeArgs& a, int wdtype_bf16, int pops);

@@ -47,6 +47,7 @@
 // published, so no cache holds a stale copy.  Every wait is bounded: when it
 // runs out the block sets the error word and leaves its loop.
 #include <algorithm>
+#include <cstdlib>
 
 #include "common.h"
 #include "kernels.h"
@@ -80,6 +81,12 @@ __device__ __forceinline__ uint32_t ld_dev_u32(const void* p) {
   return v;
 }
 __device__ __forceinline__ void stores_done() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Keeps the instruction scheduler from moving anything across this point.  Put
+// between the loads of a batch and their uses, so that every load of the
+// batch is in flight at once instead of being sunk next to its use (which
+// the scheduler does under register pressure, one memory round trip each).
+__device__ __forceinline__ void keep_batch() { __builtin_amdgcn_sched_barrier(0); }
 
 __device__ __forceinline__ void st_dev_f32(float* p, float v) { st_dev_u32(p, __float_as_uint(v)); }
 
@@ -595,7 +602,7 @@ __device__ __forceinline__ void ctl_prefetch(const TreeArgs& a, const CtlLds& c,
   if ((r * (int)sizeof(W)) % 16 == 0 && per <= 256 && 256 % per == 0) {
     const int rpt = 256 / per;  // rows per pass
     const int pc = tid % per, r0 = tid / per;
-    constexpr int U = 8;
+    constexpr int U = 4;
     uint4* dst4 = (uint4*)c.w2s;
     for (int rb = 0; rb < rows; rb += U * rpt) {
       uint4 v[U];
@@ -641,6 +648,7 @@ __device__ __forceinline__ void ctl_expand(const TreeArgs& a, const CtlLds& c, i
 #pragma unroll
       for (int j = 0; j < PMAX; ++j)
         if (j < e) uv[j] = ub[(size_t)j * us + i];
+      keep_batch();
 #pragma unroll
       for (int j = 0; j < PMAX; ++j)
         if (j < e) {
@@ -1075,6 +1083,7 @@ __device__ __forceinline__ void ctl_advance(const TreeArgs& a, const CtlLds& c, 
         hn[g] = *reinterpret_cast<const float4*>(gh + 2 * ds);
         sp[g] = *reinterpret_cast<const float4*>(a.state + (size_t)xs * st_stride(ds) + q);
       }
+      keep_batch();
 #pragma unroll
       for (int g = 0; g < GA; ++g) {
         if (base + g * (int)NT + (int)threadIdx.x < total) {
@@ -1236,7 +1245,7 @@ __device__ __forceinline__ void controller_main(const TreeArgs& a, unsigned char
 }
 
 template <typename W>
-__global__ __launch_bounds__(256) void tree_kernel(TreeArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void tree_kernel(TreeArgs a) {
   extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
   // no cache line of an exchange slot may survive from an earlier launch
   __threadfence();
@@ -1293,10 +1302,20 @@ size_t plan_tree(TreeArgs& a, int wdtype_bf16, int pops) {
 
 hipError_t launch_tree(const TreeArgs& a, int wdtype_bf16, size_t lds_bytes, hipStream_t stream) {
   void* args[] = {const_cast<TreeArgs*>(&a)};
-  const dim3 grid(a.n_workers + a.B), block(256);
+  const dim3 grid(a.n_workers + a.B), block(NT);
   const void* fn = wdtype_bf16 ? (const void*)tree_kernel<uint16_t> : (const void*)tree_kernel<float>;
   hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_bytes);
   if (e != hipSuccess) return e;
+  const char* coop = getenv("DT_COOP");
+  if (coop && atoi(coop) == 0) {
+    // every block must be resident at once: one block per compute unit fits
+    int per_cu = 0, dev = 0, ncu = 0;
+    if ((e = hipGetDevice(&dev)) != hipSuccess) return e;
+    if ((e = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return e;
+    if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, NT, lds_bytes)) != hipSuccess) return e;
+    if ((long)per_cu * ncu < (long)grid.x) return hipErrorCooperativeLaunchTooLarge;
+    return hipLaunchKernel(fn, grid, block, args, lds_bytes, stream);
+  }
   return hipLaunchCooperativeKernel(fn, grid, block, args, (unsigned)lds_bytes, stream);
 }
 
