@@ -1,0 +1,64 @@
+"""Code-generation guards for the tree kernel (CPU: hipcc cross-compiles gfx950).
+
+The builder's step time is dominated by memory round trips, so two properties
+of the generated code matter as much as its arithmetic:
+  * no private (scratch) memory, and
+  * the worker's operand staging keeps its batch of 16-byte loads in flight
+    together (a schedule that waits after each load multiplies the staging
+    time by the batch size).
+Both depend on register pressure across the whole kernel, so any edit can flip
+them; these tests catch that without a GPU.
+"""
+import os
+import re
+import shutil
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+TREE = os.path.join(ROOT, "conditional_draft_tree_dominotree_amd", "csrc", "tree.hip")
+HIPCC = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
+
+
+@pytest.fixture(scope="module")
+def asm(tmp_path_factory):
+    if not os.path.exists(HIPCC):
+        pytest.skip("hipcc not available")
+    out = tmp_path_factory.mktemp("codegen") / "tree.s"
+    cmd = [HIPCC, "--offload-arch=gfx950", "-O3", "-std=c++17", "-Xclang", "-target-feature", "-Xclang",
+           "-packed-fp32-ops", "--cuda-device-only", "-S", "-o", str(out), TREE]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr[-2000:]
+    return out.read_text()
+
+
+def _kernel(asm_text, tmpl):
+    name = f"_ZN2dt11tree_kernelI{tmpl}EEvNS_8TreeArgsE"
+    lines = asm_text.split("\n")
+    start = next(i for i, l in enumerate(lines) if l.startswith(name + ":"))
+    end = next(i for i in range(start, len(lines)) if "s_endpgm" in lines[i])
+    meta = re.search(re.escape(name) + r"\.private_seg_size, (\d+)", asm_text)
+    return [l.strip() for l in lines[start:end]], (int(meta.group(1)) if meta else None)
+
+
+@pytest.mark.parametrize("tmpl", ["t", "f"])  # bf16 and fp32 weights
+def test_tree_kernel_uses_no_scratch(asm, tmpl):
+    body, priv = _kernel(asm, tmpl)
+    assert not any(l.startswith(("scratch_", "buffer_store_dword", "buffer_load_dword")) for l in body)
+    if priv is not None:
+        assert priv == 0
+
+
+def test_worker_staging_loads_are_batched(asm):
+    # the most 16-byte loads issued between two waits on vector memory
+    body, _ = _kernel(asm, "t")
+    runs, n = [], 0
+    for l in body:
+        if l.startswith("global_load_dwordx4"):
+            n += 1
+        elif l.startswith("s_waitcnt") and "vmcnt" in l:
+            if n:
+                runs.append(n)
+            n = 0
+    assert runs and max(runs) >= 8, f"staging loads are not batched: {runs}"
