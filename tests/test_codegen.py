@@ -50,15 +50,23 @@ def test_tree_kernel_uses_no_scratch(asm, tmpl):
         assert priv == 0
 
 
-def test_worker_staging_loads_are_batched(asm):
-    # the most 16-byte loads issued between two waits on vector memory
-    body, _ = _kernel(asm, "t")
+def _staging_runs(body):
+    # the worker's region: from its mailbox poll (the sleep before the first
+    # MFMA) to that MFMA; count the 16-byte loads issued between two waits on
+    # vector memory
+    first_mfma = next(i for i, l in enumerate(body) if l.startswith("v_mfma"))
+    poll = max(i for i, l in enumerate(body[:first_mfma]) if l.startswith("s_sleep"))
     runs, n = [], 0
-    for l in body:
+    for l in body[poll:first_mfma]:
         if l.startswith("global_load_dwordx4"):
             n += 1
         elif l.startswith("s_waitcnt") and "vmcnt" in l:
             if n:
                 runs.append(n)
             n = 0
+    return runs
+
+
+def test_worker_staging_loads_are_batched(asm):
+    runs = _staging_runs(_kernel(asm, "t")[0])
     assert runs and max(runs) >= 8, f"staging loads are not batched: {runs}"
