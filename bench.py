@@ -39,6 +39,40 @@ def tree_kernel_bytes(spec) -> float:
     return float(spec.N) * (per_step_weights + spec.B * per_request)
 
 
+TREE_SOURCES = ["csrc/tree.hip", "csrc/kernels.h", "csrc/common.h"]
+
+
+def tree_source_hash() -> str:
+    """sha256 of the sources the tree kernel is compiled from."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in TREE_SOURCES:
+        with open(os.path.join(ROOT, "conditional_draft_tree_dominotree_amd", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per tree-kernel launch from the committed rocprofv3 counter
+    summary (FETCH_SIZE + WRITE_SIZE, scaled by a plain copy of known size),
+    or None when there is none or the kernel's sources changed since."""
+    path = os.path.join(ROOT, "profiles", f"traffic_tree_kernel_{workload}.md")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    with open(path) as fh:
+        for line in fh:
+            if ":" in line and line.startswith("- "):
+                k, v = line[2:].split(":", 1)
+                fields[k.strip()] = v.strip().strip("`")
+    if fields.get("tree_source_sha256") != tree_source_hash():
+        return None
+    try:
+        return float(fields["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
 def to_dev(a):
     """A numpy array (bf16 stored as uint16 bits) as a contiguous device tensor."""
     import numpy as np
@@ -102,6 +136,8 @@ def main():
     ap.add_argument("--workload", default="q8b_b32")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="after the timed run, copy a MIB-MiB buffer 3 times (reference for HBM counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the builder has no multi-GPU path (requests shard "
@@ -188,7 +224,7 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBS,
-            "traffic": None,
+            "traffic": measured_traffic(spec.name),
             "algorithmic_bytes": ab,
         },
     }
@@ -220,6 +256,14 @@ def main():
                                 "ok": all(r.ok for r in reps),
                                 "max_abs_dscore": max(r.max_dscore for r in reps)}
     tb.close()
+    if args.copy_calibration > 0:
+        n = args.copy_calibration * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        res["copy_calibration_bytes"] = n * 4
     print(json.dumps(res))
 
 

@@ -8,18 +8,17 @@
 // rounded.
 //
 // Kernels.  topm_chunk: one 256-thread block per (row, chunk of 8192 tokens)
-// reads its chunk once from HBM into registers (32 values per thread).  The
-// M-th largest of the 256 per-thread maxima is a lower bound of the chunk's
-// M-th largest value (at least M threads reach it), so the keys at or above
-// it -- typically a little more than M -- hold the chunk's top-M; they are
-// ranked exactly as (value desc, id asc) composites.  The chunk's LSE
-// statistics come from the same registers.  topm_fallback: when more than 512
-// keys reach that bound (many equal values), an exact 3-pass radix select
-// over the chunk in LDS redoes that chunk.  topm_merge: one block per row ranks the chunk
-// lists against each other and keeps the M best; the LSE statistics combine
-// exactly (a token left out of its chunk's list is left out of the row's).
-// The merge also serves the LM-head path, whose GEMM epilogue writes the same
-// chunk lists.
+// reads its chunk once from HBM into registers (32 values per thread).  Each
+// wave sorts its 64 per-thread maxima and takes the ceil(M/4)-th largest; the
+// smallest of the four wave values bounds the chunk's M-th largest value from
+// below (at least M threads reach it), so the keys at or above it -- typically
+// a few more than M -- hold the chunk's top-M; they are ranked exactly as
+// (value desc, id asc) composites.  The chunk's LSE statistics come from the
+// same registers.  topm_fallback: when more than 512 keys reach that bound
+// (many equal values), an exact 3-pass radix select over the chunk in LDS
+// redoes that chunk.  topm_merge: one block per row ranks the chunk lists
+// against each other and keeps the M best; the LSE statistics combine exactly
+// (a token left out of its chunk's list is left out of the row's).
 #include "common.h"
 #include "kernels.h"
 
@@ -31,27 +30,32 @@ constexpr int HBINS = 4096;
 constexpr int PER_THREAD = TOPM_CHUNK / TOPM_THREADS;  // 32 values per thread
 constexpr int FAST_CAP = 512;                          // candidates the fast path ranks
 
-__global__ __launch_bounds__(TOPM_THREADS) void topm_chunk_kernel(
-    const float* __restrict__ logits, int V, int S, int M, float T,
-    uint64_t* __restrict__ out_cand, float4* __restrict__ out_stat) {
-  __shared__ __attribute__((aligned(16))) uint64_t sel[FAST_CAP + 2];
-  __shared__ __attribute__((aligned(16))) uint32_t tmax[TOPM_THREADS];
-  __shared__ float red[4];
-  __shared__ int sel_count;
-  __shared__ uint32_t tau_s;
+// Bitonic sort of one 32-bit value per lane of a wave, descending.
+__device__ __forceinline__ uint32_t wave_sort_desc_u32(uint32_t v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int k = 2; k <= 64; k <<= 1) {
+#pragma unroll
+    for (int j = k >> 1; j >= 1; j >>= 1) {
+      const uint32_t o = (uint32_t)__shfl_xor((int)v, j);
+      const bool lower = (lane & j) == 0;
+      const bool desc_block = (lane & k) == 0;  // the last (k = 64) block is descending
+      v = (lower == desc_block) ? max(v, o) : min(v, o);
+    }
+  }
+  return v;
+}
 
-  const int tid = threadIdx.x;
-  const int c = blockIdx.x;
-  const int row = blockIdx.y;
-  const int c0 = c * TOPM_CHUNK;
-  const int len = min(TOPM_CHUNK, V - c0);
-  const int Mc = min(M, len);
-  const float* src = logits + (size_t)row * (size_t)V + c0;
-
+template <bool FULL>
+__device__ __forceinline__ void topm_chunk_body(const float* __restrict__ src, int len, int c0, int Mc, int M,
+                                                float T, uint64_t* __restrict__ out_list,
+                                                float4* __restrict__ out_stat_p, uint64_t* sel, uint32_t* wb,
+                                                float* red, int* sel_count) {
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   // 1. read the chunk once into registers: element tid*4 + 1024 j + e holds
   //    float4 piece j of thread tid (coalesced); missing elements are -inf.
   float x[PER_THREAD];
-  if ((V & 3) == 0 && len == TOPM_CHUNK) {
+  if (FULL) {
     const float4* s4 = reinterpret_cast<const float4*>(src);
 #pragma unroll
     for (int j = 0; j < PER_THREAD / 4; ++j) {
@@ -76,96 +80,119 @@ __global__ __launch_bounds__(TOPM_THREADS) void topm_chunk_kernel(
 #pragma unroll
   for (int q = 0; q < PER_THREAD; ++q) {
     vmax = fmaxf(vmax, x[q]);
-    if (idx_of(q) < len) kmax = max(kmax, f32_key(x[q]));
+    if (FULL || idx_of(q) < len) kmax = max(kmax, f32_key(x[q]));
   }
-  const float m = block_max<TOPM_THREADS>(vmax, red) / T;
-
-  // 2. threshold: the Mc-th largest per-thread maximum bounds the chunk's
-  //    Mc-th largest key from below (at least Mc threads reach it)
-  tmax[tid] = kmax;
-  if (tid == 0) sel_count = 0;
-  __syncthreads();
-  {
-    // rank of this thread's maximum among all 256 (ties by thread index);
-    // 16-byte broadcast reads of the maxima
-    int rank = 0;
-    const uint4* t4 = reinterpret_cast<const uint4*>(tmax);
-#pragma unroll 8
-    for (int i = 0; i < TOPM_THREADS / 4; ++i) {
-      const uint4 o = t4[i];
-      rank += (o.x > kmax) || (o.x == kmax && 4 * i < tid);
-      rank += (o.y > kmax) || (o.y == kmax && 4 * i + 1 < tid);
-      rank += (o.z > kmax) || (o.z == kmax && 4 * i + 2 < tid);
-      rank += (o.w > kmax) || (o.w == kmax && 4 * i + 3 < tid);
-    }
-    if (rank == Mc - 1) tau_s = kmax;
+  // 2. threshold: in each wave the ceil(Mc/4)-th largest lane maximum; the
+  //    smallest of the four bounds the chunk's Mc-th largest key from below
+  //    (at least 4 ceil(Mc/4) >= Mc threads have a maximum at or above it)
+  const int m4 = (Mc + 3) >> 2;
+  const uint32_t sorted = wave_sort_desc_u32(kmax);
+  const uint32_t wbound = (uint32_t)__builtin_amdgcn_readlane((int)sorted, m4 - 1);
+  const float wmax = wave_max_dpp(vmax);
+  if (lane == 0) {
+    wb[wv] = wbound;
+    red[wv] = wmax;
   }
+  if (tid == 0) *sel_count = 0;
   __syncthreads();
-  const uint32_t tau = tau_s;
+  const uint32_t tau = min(min(wb[0], wb[1]), min(wb[2], wb[3]));
+  const float vm = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));  // the chunk's max value
 #pragma unroll
   for (int q = 0; q < PER_THREAD; ++q) {
-    const int i = idx_of(q);
     const uint32_t k = f32_key(x[q]);
-    if (i < len && k >= tau) {
-      const int slot = atomicAdd(&sel_count, 1);
-      if (slot < FAST_CAP) sel[slot] = cand_pack(k, (uint32_t)(c0 + i));
+    if ((FULL || idx_of(q) < len) && k >= tau) {
+      const int slot = atomicAdd(sel_count, 1);
+      if (slot < FAST_CAP) sel[slot] = cand_pack(k, (uint32_t)(c0 + idx_of(q)));
     }
   }
   __syncthreads();
-  const int cnt = sel_count;
-  if (cnt <= FAST_CAP) {
-    // 3a. rank the candidates exactly (composite keys are unique)
-    uint64_t mine[FAST_CAP / TOPM_THREADS];
-    int rk[FAST_CAP / TOPM_THREADS];
+  const int cnt = *sel_count;
+  if (cnt > FAST_CAP) {
+    // too many keys at the threshold (equal values): topm_fallback_kernel
+    // redoes this chunk exactly
+    if (tid == 0) *out_stat_p = make_float4(0.f, 0.f, 0.f, __int_as_float(-1));
+    return;
+  }
+  // 3. rank the candidates exactly (composite keys are unique)
+  uint64_t mine[FAST_CAP / TOPM_THREADS];
+  int rk[FAST_CAP / TOPM_THREADS];
 #pragma unroll
-    for (int u = 0; u < FAST_CAP / TOPM_THREADS; ++u) {
-      const int e = tid + u * TOPM_THREADS;
-      mine[u] = e < cnt ? sel[e] : 0ull;
-      rk[u] = 0;
+  for (int u = 0; u < FAST_CAP / TOPM_THREADS; ++u) {
+    const int e = tid + u * TOPM_THREADS;
+    mine[u] = e < cnt ? sel[e] : 0ull;
+    rk[u] = 0;
+  }
+  if (tid == 0 && (cnt & 1)) sel[cnt] = 0ull;  // pad to pairs (0 ranks below every key)
+  __syncthreads();
+  const ulonglong2* s2 = reinterpret_cast<const ulonglong2*>(sel);
+  if (cnt <= TOPM_THREADS) {
+    for (int i = 0; i < (cnt + 1) / 2; ++i) {
+      const ulonglong2 o = s2[i];
+      rk[0] += (o.x > mine[0]) + (o.y > mine[0]);
     }
-    if (tid == 0 && (cnt & 1)) sel[cnt] = 0ull;  // pad to pairs (0 ranks below every key)
-    __syncthreads();
-    const ulonglong2* s2 = reinterpret_cast<const ulonglong2*>(sel);
-#pragma unroll 4
+  } else {
     for (int i = 0; i < (cnt + 1) / 2; ++i) {
       const ulonglong2 o = s2[i];
 #pragma unroll
       for (int u = 0; u < FAST_CAP / TOPM_THREADS; ++u) rk[u] += (o.x > mine[u]) + (o.y > mine[u]);
     }
-    __syncthreads();
-#pragma unroll
-    for (int u = 0; u < FAST_CAP / TOPM_THREADS; ++u) {
-      const int e = tid + u * TOPM_THREADS;
-      if (e < cnt && rk[u] < Mc) sel[rk[u]] = mine[u];  // ranks < Mc are distinct
-    }
-    __syncthreads();
-  } else {
-    // too many keys at the threshold (equal values): topm_fallback_kernel
-    // redoes this chunk exactly
-    if (tid == 0) out_stat[(size_t)row * S + c] = make_float4(0.f, 0.f, 0.f, __int_as_float(-1));
-    return;
   }
+  __syncthreads();
+#pragma unroll
+  for (int u = 0; u < FAST_CAP / TOPM_THREADS; ++u) {
+    const int e = tid + u * TOPM_THREADS;
+    if (e < cnt && rk[u] < Mc) sel[rk[u]] = mine[u];  // ranks < Mc are distinct
+  }
+  __syncthreads();
   // 4. the chunk's list, sorted (value desc, id asc), zero padded to M
-  if (tid < M) out_cand[((size_t)row * S + c) * M + tid] = tid < Mc ? sel[tid] : 0ull;
+  if (tid < M) out_list[tid] = tid < Mc ? sel[tid] : 0ull;
 
   // 5. LSE statistics: the chunk's sum of exp(x/T - m), and the same sum over
   //    its left-out tokens as the chunk sum minus the selected terms (the
   //    selected values are the largest, so the difference keeps the tail to
   //    within rounding of the chunk sum)
+  const float m = vm / T;
+  const float l2t = 1.4426950408889634f / T;  // exp(y / T) = exp2(y * log2(e) / T)
   float s_all = 0.f;
-  const float vm = m * T;                      // the chunk's max value
-  const float l2t = 1.4426950408889634f / T;   // exp(y / T) = exp2(y * log2(e) / T)
-  if (m > -INFINITY) {
+  if (vm > -INFINITY) {
 #pragma unroll
-    for (int q = 0; q < PER_THREAD; ++q) s_all += exp2f((x[q] - vm) * l2t);  // -inf pads add 0
+    for (int q = 0; q < PER_THREAD; ++q) s_all += __builtin_amdgcn_exp2f((x[q] - vm) * l2t);  // -inf adds 0
   }
-  s_all = block_sum<TOPM_THREADS>(s_all, red);
+  s_all = wave_sum_dpp(s_all);
+  float s_sel = 0.f;
+  if (wv == 0) {
+    const float e = (lane < Mc && vm > -INFINITY) ? __builtin_amdgcn_exp2f((key_f32(cand_key(sel[lane])) - vm) * l2t)
+                                                  : 0.f;
+    s_sel = wave_sum_dpp(e);
+  }
+  __syncthreads();
+  if (lane == 0) red[wv] = s_all;
+  __syncthreads();
   if (tid == 0) {
-    float s_sel = 0.f;
-    if (m > -INFINITY)
-      for (int i = 0; i < Mc; ++i) s_sel += exp2f((key_f32(cand_key(sel[i])) - vm) * l2t);
-    out_stat[(size_t)row * S + c] = make_float4(m, s_all, fmaxf(s_all - s_sel, 0.f), __int_as_float(Mc));
+    const float tot = (red[0] + red[1]) + (red[2] + red[3]);
+    *out_stat_p = make_float4(m, tot, fmaxf(tot - s_sel, 0.f), __int_as_float(Mc));
   }
+}
+
+__global__ __launch_bounds__(TOPM_THREADS) void topm_chunk_kernel(
+    const float* __restrict__ logits, int V, int S, int M, float T,
+    uint64_t* __restrict__ out_cand, float4* __restrict__ out_stat) {
+  __shared__ __attribute__((aligned(16))) uint64_t sel[FAST_CAP + 2];
+  __shared__ uint32_t wb[4];
+  __shared__ float red[4];
+  __shared__ int sel_count;
+  const int c = blockIdx.x;
+  const int row = blockIdx.y;
+  const int c0 = c * TOPM_CHUNK;
+  const int len = min(TOPM_CHUNK, V - c0);
+  const int Mc = min(M, len);
+  const float* src = logits + (size_t)row * (size_t)V + c0;
+  uint64_t* list = out_cand + ((size_t)row * S + c) * M;
+  float4* stat = out_stat + (size_t)row * S + c;
+  if ((V & 3) == 0 && len == TOPM_CHUNK)
+    topm_chunk_body<true>(src, len, c0, Mc, M, T, list, stat, sel, wb, red, &sel_count);
+  else
+    topm_chunk_body<false>(src, len, c0, Mc, M, T, list, stat, sel, wb, red, &sel_count);
 }
 
 // Exact per-chunk selection for the chunks the fast path could not rank
