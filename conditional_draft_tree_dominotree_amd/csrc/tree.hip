@@ -47,7 +47,6 @@
 // published, so no cache holds a stale copy.  Every wait is bounded: when it
 // runs out the block sets the error word and leaves its loop.
 #include <algorithm>
-#include <cstdlib>
 
 #include "common.h"
 #include "kernels.h"
@@ -1306,16 +1305,6 @@ hipError_t launch_tree(const TreeArgs& a, int wdtype_bf16, size_t lds_bytes, hip
   const void* fn = wdtype_bf16 ? (const void*)tree_kernel<uint16_t> : (const void*)tree_kernel<float>;
   hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_bytes);
   if (e != hipSuccess) return e;
-  const char* coop = getenv("DT_COOP");
-  if (coop && atoi(coop) == 0) {
-    // every block must be resident at once: one block per compute unit fits
-    int per_cu = 0, dev = 0, ncu = 0;
-    if ((e = hipGetDevice(&dev)) != hipSuccess) return e;
-    if ((e = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return e;
-    if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, NT, lds_bytes)) != hipSuccess) return e;
-    if ((long)per_cu * ncu < (long)grid.x) return hipErrorCooperativeLaunchTooLarge;
-    return hipLaunchKernel(fn, grid, block, args, lds_bytes, stream);
-  }
   return hipLaunchCooperativeKernel(fn, grid, block, args, (unsigned)lds_bytes, stream);
 }
 
