@@ -1,6 +1,7 @@
 // Host side of the C ABI declared in include/dominotree.h.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -353,8 +354,12 @@ dt_status dt_build_trees(dt_handle* h, const dt_inputs* in, const dt_params* p, 
   a.n_nodes = out->n_nodes;
   a.spin_limit = 1u << 21;
   const char* pops_env = getenv("DT_POPS");
-  const size_t lds = dt::plan_tree(a, h->bf16, pops_env ? atoi(pops_env) : 0);
+  const char* workers_env = getenv("DT_WORKERS");  // "lds": workers stage operands in LDS
+  const size_t lds = dt::plan_tree(a, h->bf16, pops_env ? atoi(pops_env) : 0, std::min(h->n_cu - B, h->max_workers),
+                                   workers_env && !strcmp(workers_env, "lds"));
   if (lds == 0 || lds > 160 * 1024) return fail(DT_EUNSUPPORTED, "no builder schedule fits this shape in LDS");
+  if (a.n_workers + B > h->n_cu || a.n_workers > h->max_workers)
+    return fail(DT_EUNSUPPORTED, "%d workers + %d requests exceed %d compute units", a.n_workers, B, h->n_cu);
   MARK(3);
   HIPCHK(dt::launch_fill_u32(h->mbox_w, 0u, (size_t)a.n_workers * 32, stream));
   HIPCHK(dt::launch_fill_u32(h->mbox_c, 0u, (size_t)B * 256, stream));

@@ -55,6 +55,8 @@ struct TreeArgs {
   // schedule (set by plan_tree)
   int p;                // nodes a request may expand per step (exchange columns per request)
   int kc;               // state elements a worker stages per phase (kp / kc phases)
+  int regw;             // 0: workers stage operands in LDS; 1, 2: register workers, tiles per wave
+  int ncbmax;           // register workers: 16-column blocks per step
   int xcap;             // node records per request (budget + root + speculation room)
   int fcap;             // frontier entries per request
   int qmax;             // frontier entries tested per pop round
@@ -87,7 +89,10 @@ struct TreeArgs {
 constexpr int TREE_MAX_COLS = 128;
 // Fills the schedule fields of `a` (p from `pops`, 0 = automatic) and returns
 // the dynamic LDS bytes the launch needs, or 0 if the shape cannot be served.
-size_t plan_tree(TreeArgs& a, int wdtype_bf16, int pops);
+// With register workers (allowed unless `lds_workers`) it also sets
+// n_workers, at most `max_workers`; otherwise n_workers and tiles_per_worker
+// are the caller's.
+size_t plan_tree(TreeArgs& a, int wdtype_bf16, int pops, int max_workers, int lds_workers);
 hipError_t launch_tree(const TreeArgs& a, int wdtype_bf16, size_t lds_bytes, hipStream_t stream);
 
 }  // namespace dt

@@ -211,12 +211,45 @@ __device__ __forceinline__ void worker_store_out(const TreeArgs& a, size_t slot,
   }
 }
 
+// Sixteen 16-byte loads from base + off[q] (byte offsets), issued back to back
+// and completed together.  One asm block, so that register pressure elsewhere
+// in the kernel cannot make the compiler wait after each load.
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void load16_batch(const void* base, const unsigned (&off)[16], u32x4 (&v)[16]) {
+  asm volatile(
+      "global_load_dwordx4 %0, %16, %32\n\t"
+      "global_load_dwordx4 %1, %17, %32\n\t"
+      "global_load_dwordx4 %2, %18, %32\n\t"
+      "global_load_dwordx4 %3, %19, %32\n\t"
+      "global_load_dwordx4 %4, %20, %32\n\t"
+      "global_load_dwordx4 %5, %21, %32\n\t"
+      "global_load_dwordx4 %6, %22, %32\n\t"
+      "global_load_dwordx4 %7, %23, %32\n\t"
+      "global_load_dwordx4 %8, %24, %32\n\t"
+      "global_load_dwordx4 %9, %25, %32\n\t"
+      "global_load_dwordx4 %10, %26, %32\n\t"
+      "global_load_dwordx4 %11, %27, %32\n\t"
+      "global_load_dwordx4 %12, %28, %32\n\t"
+      "global_load_dwordx4 %13, %29, %32\n\t"
+      "global_load_dwordx4 %14, %30, %32\n\t"
+      "global_load_dwordx4 %15, %31, %32\n\t"
+      "s_waitcnt vmcnt(0)"
+      : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3]), "=&v"(v[4]), "=&v"(v[5]), "=&v"(v[6]), "=&v"(v[7]),
+        "=&v"(v[8]), "=&v"(v[9]), "=&v"(v[10]), "=&v"(v[11]), "=&v"(v[12]), "=&v"(v[13]), "=&v"(v[14]), "=&v"(v[15])
+      : "v"(off[0]), "v"(off[1]), "v"(off[2]), "v"(off[3]), "v"(off[4]), "v"(off[5]), "v"(off[6]), "v"(off[7]),
+        "v"(off[8]), "v"(off[9]), "v"(off[10]), "v"(off[11]), "v"(off[12]), "v"(off[13]), "v"(off[14]), "v"(off[15]),
+        "s"(base)
+      : "memory");
+}
+
 // Copy elements [k0, k0 + kc) of each active column's operand into the stage.
 // Thread tid owns 16-byte piece tid % per of columns tid / per + j * cpt;
-// every load of a batch is issued before any store.
+// every load of a batch is issued before any store.  slot0 is the first
+// exchange slot of the step (its columns lie in the next TREE_MAX_COLS slots,
+// so byte offsets from it fit 32 bits).
 template <typename W>
 __device__ __forceinline__ void worker_stage(const TreeArgs& a, W* stage, const int* coln, int ncols, int k0,
-                                             int kc) {
+                                             int kc, int slot0) {
   const int tid = threadIdx.x;
   const int as = act_stride(a.ds);
   const int kcs = kc + STAGE_PAD;
@@ -226,19 +259,21 @@ __device__ __forceinline__ void worker_stage(const TreeArgs& a, W* stage, const 
     const int cpt = 256 / per;  // columns per pass
     const int pc = tid % per, c0 = tid / per;
     constexpr int U = 16;
+    const W* base = act + (size_t)slot0 * as + k0;
     for (int cb = 0; cb < ncols; cb += U * cpt) {
-      uint4 v[U];
+      unsigned off[U];
+      u32x4 v[U];
 #pragma unroll
       for (int q = 0; q < U; ++q) {  // clamped: every lane loads a valid piece
         const int c = min(cb + c0 + q * cpt, ncols - 1);
-        v[q] = reinterpret_cast<const uint4*>(act + (size_t)coln[c] * as + k0)[pc];
+        off[q] = (unsigned)(((coln[c] - slot0) * as + pc * (16 / (int)sizeof(W))) * (int)sizeof(W));
       }
-      // unconditional stores (a clamped duplicate rewrites identical data),
-      // so that no load is sunk into a guarded block and serialised
+      load16_batch(base, off, v);
+      // unconditional stores (a clamped duplicate rewrites identical data)
 #pragma unroll
       for (int q = 0; q < U; ++q) {
         const int c = min(cb + c0 + q * cpt, ncols - 1);
-        *reinterpret_cast<uint4*>(stage + (size_t)c * kcs + pc * (16 / sizeof(W))) = v[q];
+        *reinterpret_cast<u32x4*>(stage + (size_t)c * kcs + pc * (16 / sizeof(W))) = v[q];
       }
     }
   } else {
@@ -338,6 +373,47 @@ __device__ __forceinline__ void worker_compute_f32(const TreeArgs& a, const floa
   }
 }
 
+// Wave 0 waits for every request's word of step t in worker w's mailbox, then
+// lists the step's columns (exchange slots, request-major) in coln and the
+// requests with work in reqs; misc[0] = columns (-1: a wait ran out),
+// misc[1] = requests.  Ends with a block barrier.
+__device__ __forceinline__ void worker_columns(const TreeArgs& a, int w, int t, int* coln, int* reqs, int* misc) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  const uint32_t epoch = (uint32_t)t + 1u;
+  if (tid < 64) {
+    const uint32_t* mybox = a.mbox_w + (size_t)w * 32;
+    const bool ok = wait_mbox(mybox, a.B, epoch << 5, a.err, a.spin_limit);
+    const int b = lane;
+    uint32_t word = 0;
+    if (ok && b < a.B) word = ld_dev_u32(mybox + b);
+    const int e = (ok && b < a.B && word != MBOX_DONE) ? (int)(word & 31u) : 0;
+    // exclusive prefix of e over the lanes
+    int incl = e;
+    for (int d = 1; d < 64; d <<= 1) {
+      const int y = __shfl_up(incl, d);
+      if (lane >= d) incl += y;
+    }
+    const int base = incl - e;
+    for (int j = 0; j < e; ++j) coln[base + j] = (int)slot_of(a, t, b, j);
+    const unsigned long long has = __ballot(e > 0);
+    if (e > 0) reqs[__popcll(has & ((1ull << lane) - 1ull))] = b;
+    if (lane == 63) misc[0] = ok ? incl : -1;
+    if (lane == 0) misc[1] = __popcll(has);
+  }
+  __syncthreads();
+}
+
+// Once this block's rows of the step are stored, tell each active request's
+// controller.
+__device__ __forceinline__ void worker_ack(const TreeArgs& a, int w, const int* reqs, int nreq, uint32_t epoch) {
+  const int tid = threadIdx.x;
+  stores_done();
+  __syncthreads();
+  if (tid < nreq) st_dev_u32(a.mbox_c + (size_t)reqs[tid] * 256 + w, epoch);
+  stores_done();
+  __syncthreads();
+}
+
 template <typename W>
 __device__ __forceinline__ void worker_main(const TreeArgs& a, unsigned char* lds) {
   const int w = blockIdx.x;
@@ -362,30 +438,9 @@ __device__ __forceinline__ void worker_main(const TreeArgs& a, unsigned char* ld
   }
   __syncthreads();
 
-  const uint32_t* mybox = a.mbox_w + (size_t)w * 32;
   for (int t = 0;; ++t) {
     const uint32_t epoch = (uint32_t)t + 1u;
-    // wave 0: wait for every request's word of this step, then list the columns
-    if (tid < 64) {
-      const bool ok = wait_mbox(mybox, a.B, epoch << 5, a.err, a.spin_limit);
-      const int b = lane;
-      uint32_t word = 0;
-      if (ok && b < a.B) word = ld_dev_u32(mybox + b);
-      const int e = (ok && b < a.B && word != MBOX_DONE) ? (int)(word & 31u) : 0;
-      // exclusive prefix of e over the lanes
-      int incl = e;
-      for (int d = 1; d < 64; d <<= 1) {
-        const int y = __shfl_up(incl, d);
-        if (lane >= d) incl += y;
-      }
-      const int base = incl - e;
-      for (int j = 0; j < e; ++j) coln[base + j] = (int)slot_of(a, t, b, j);
-      const unsigned long long has = __ballot(e > 0);
-      if (e > 0) reqs[__popcll(has & ((1ull << lane) - 1ull))] = b;
-      if (lane == 63) misc[0] = ok ? incl : -1;
-      if (lane == 0) misc[1] = __popcll(has);
-    }
-    __syncthreads();
+    worker_columns(a, w, t, coln, reqs, misc);
     const int ncols = misc[0], nreq = misc[1];
     if (ncols <= 0) return;  // a wait ran out, or every request is finished
     const int ncb = (ncols + 15) / 16;
@@ -396,24 +451,147 @@ __device__ __forceinline__ void worker_main(const TreeArgs& a, unsigned char* ld
       for (int i = 0; i < PPW; ++i) acc[i][0] = acc[i][1] = floatx4{0.f, 0.f, 0.f, 0.f};
       for (int k0 = 0; k0 < kp; k0 += kc) {
         if (k0 > 0) __syncthreads();  // the previous phase's operands are consumed
-        worker_stage<W>(a, stage, coln, ncols, k0, kc);
+        worker_stage<W>(a, stage, coln, ncols, k0, kc, (int)slot_of(a, t, 0, 0));
         __syncthreads();
         worker_mfma_phase(reinterpret_cast<const uint16_t*>(tiles_lds), reinterpret_cast<const uint16_t*>(stage),
                           kp, k0 / 32, kc / 32, kcs, ncb, pairs, acc);
       }
       worker_epilogue_bf16(a, coln, ncols, tile0, ncb, pairs, acc);
     } else {
-      worker_stage<W>(a, stage, coln, ncols, 0, kc);  // kc == kp for fp32
+      worker_stage<W>(a, stage, coln, ncols, 0, kc, (int)slot_of(a, t, 0, 0));  // kc == kp for fp32
       __syncthreads();
       worker_compute_f32(a, reinterpret_cast<const float*>(tiles_lds), reinterpret_cast<const float*>(stage),
                          ncols, coln, tile0, ntiles, kp, kcs);
     }
-    stores_done();
-    __syncthreads();
-    // tell each active request's controller that this worker's rows are out
-    if (tid < nreq) st_dev_u32(a.mbox_c + (size_t)reqs[tid] * 256 + w, epoch);
-    stores_done();
-    __syncthreads();
+    worker_ack(a, w, reqs, nreq, epoch);
+  }
+}
+
+
+// ---- register-resident worker (bf16, d_s padded to RKB * 32 = 1024)
+// Each wave owns TW tiles of [W_hh ; W1_S^T], held in registers as MFMA A
+// operands for the whole launch, and one 16-column block of each step: it
+// loads its columns' operands straight into B registers (one batch of RKB
+// 16-byte loads per lane, all in flight together) and runs RKB MFMAs per
+// tile.  No LDS staging: one memory round trip per step, and every byte of the
+// operands crosses the load path once per wave that multiplies it.
+// Wave task = w * 4 + wave: tile group task / ncbmax (tiles TW g .. TW g +
+// TW - 1), column block task % ncbmax.
+constexpr int RKB = 32;
+
+// RKB 16-byte loads at p + 64 q bytes (q < RKB): one lane's B operands of all
+// k blocks; issued back to back and completed together
+__device__ __forceinline__ void load_b_operands(const void* p, bf16x8 (&v)[RKB]) {
+  asm volatile(
+      "global_load_dwordx4 %0, %32, off\n\t"
+      "global_load_dwordx4 %1, %32, off offset:64\n\t"
+      "global_load_dwordx4 %2, %32, off offset:128\n\t"
+      "global_load_dwordx4 %3, %32, off offset:192\n\t"
+      "global_load_dwordx4 %4, %32, off offset:256\n\t"
+      "global_load_dwordx4 %5, %32, off offset:320\n\t"
+      "global_load_dwordx4 %6, %32, off offset:384\n\t"
+      "global_load_dwordx4 %7, %32, off offset:448\n\t"
+      "global_load_dwordx4 %8, %32, off offset:512\n\t"
+      "global_load_dwordx4 %9, %32, off offset:576\n\t"
+      "global_load_dwordx4 %10, %32, off offset:640\n\t"
+      "global_load_dwordx4 %11, %32, off offset:704\n\t"
+      "global_load_dwordx4 %12, %32, off offset:768\n\t"
+      "global_load_dwordx4 %13, %32, off offset:832\n\t"
+      "global_load_dwordx4 %14, %32, off offset:896\n\t"
+      "global_load_dwordx4 %15, %32, off offset:960\n\t"
+      "global_load_dwordx4 %16, %32, off offset:1024\n\t"
+      "global_load_dwordx4 %17, %32, off offset:1088\n\t"
+      "global_load_dwordx4 %18, %32, off offset:1152\n\t"
+      "global_load_dwordx4 %19, %32, off offset:1216\n\t"
+      "global_load_dwordx4 %20, %32, off offset:1280\n\t"
+      "global_load_dwordx4 %21, %32, off offset:1344\n\t"
+      "global_load_dwordx4 %22, %32, off offset:1408\n\t"
+      "global_load_dwordx4 %23, %32, off offset:1472\n\t"
+      "global_load_dwordx4 %24, %32, off offset:1536\n\t"
+      "global_load_dwordx4 %25, %32, off offset:1600\n\t"
+      "global_load_dwordx4 %26, %32, off offset:1664\n\t"
+      "global_load_dwordx4 %27, %32, off offset:1728\n\t"
+      "global_load_dwordx4 %28, %32, off offset:1792\n\t"
+      "global_load_dwordx4 %29, %32, off offset:1856\n\t"
+      "global_load_dwordx4 %30, %32, off offset:1920\n\t"
+      "global_load_dwordx4 %31, %32, off offset:1984\n\t"
+      "s_waitcnt vmcnt(0)"
+      : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3]), "=&v"(v[4]), "=&v"(v[5]), "=&v"(v[6]), "=&v"(v[7]),
+        "=&v"(v[8]), "=&v"(v[9]), "=&v"(v[10]), "=&v"(v[11]), "=&v"(v[12]), "=&v"(v[13]), "=&v"(v[14]),
+        "=&v"(v[15]), "=&v"(v[16]), "=&v"(v[17]), "=&v"(v[18]), "=&v"(v[19]), "=&v"(v[20]), "=&v"(v[21]),
+        "=&v"(v[22]), "=&v"(v[23]), "=&v"(v[24]), "=&v"(v[25]), "=&v"(v[26]), "=&v"(v[27]), "=&v"(v[28]),
+        "=&v"(v[29]), "=&v"(v[30]), "=&v"(v[31])
+      : "v"(p)
+      : "memory");
+}
+
+template <int TW>
+__device__ __forceinline__ void worker_regs(const TreeArgs& a, unsigned char* lds) {
+  const int w = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  int* coln = reinterpret_cast<int*>(lds);
+  int* reqs = coln + TREE_MAX_COLS;
+  int* misc = reqs + TREE_MAX_COLS;
+  const int kp = RKB * 32;
+  const int as = act_stride(a.ds);
+  const int task = w * 4 + wv;
+  const int tg = task / a.ncbmax, cb = task - tg * a.ncbmax;
+  const int tile0 = tg * TW;
+
+  // this wave's A operands: tile rows (lane & 15), k 8 (lane >> 4) + 32 kb
+  bf16x8 wa[TW][RKB];
+#pragma unroll
+  for (int i = 0; i < TW; ++i) {
+    const bool ok = tile0 + i < a.n_tiles;
+    const bf16x8* src = reinterpret_cast<const bf16x8*>(reinterpret_cast<const uint16_t*>(a.tiles) +
+                                                        (size_t)(ok ? tile0 + i : 0) * 16 * kp) + lane;
+#pragma unroll
+    for (int kb = 0; kb < RKB; ++kb) wa[i][kb] = src[kb * 64];
+  }
+
+  for (int t = 0;; ++t) {
+    const uint32_t epoch = (uint32_t)t + 1u;
+    worker_columns(a, w, t, coln, reqs, misc);
+    const int ncols = misc[0], nreq = misc[1];
+    if (ncols <= 0) return;  // a wait ran out, or every request is finished
+    if (tile0 < a.n_tiles && cb * 16 < ncols) {
+      const int col = cb * 16 + (lane & 15);
+      const size_t slot = (size_t)coln[min(col, ncols - 1)];
+      bf16x8 bv[RKB];
+      load_b_operands(reinterpret_cast<const uint16_t*>(a.act) + slot * as + 8 * (lane >> 4), bv);
+      floatx4 acc[TW][2];
+#pragma unroll
+      for (int i = 0; i < TW; ++i) acc[i][0] = acc[i][1] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kb = 0; kb < RKB; ++kb)
+#pragma unroll
+        for (int i = 0; i < TW; ++i)
+          acc[i][kb & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa[i][kb], bv[kb], acc[i][kb & 1], 0, 0, 0);
+      // lane holds column col, rows 4 (lane >> 4) + q of each tile
+      if (col < ncols) {
+        const int ds3 = 3 * a.ds;
+#pragma unroll
+        for (int i = 0; i < TW; ++i) {
+          if (tile0 + i >= a.n_tiles) continue;
+          const floatx4 sum = acc[i][0] + acc[i][1];
+          const int row0 = (tile0 + i) * 16 + 4 * (lane >> 4);
+          if (row0 + 3 < ds3 && (ds3 & 3) == 0) {
+            floatx4 v = sum;
+            if (a.b_hh) {
+              v[0] += a.b_hh[row0];
+              v[1] += a.b_hh[row0 + 1];
+              v[2] += a.b_hh[row0 + 2];
+              v[3] += a.b_hh[row0 + 3];
+            }
+            st_dev_f32x4(a.gh + slot * gh_stride(a.ds) + row0, v);
+          } else {
+            for (int q = 0; q < 4; ++q) worker_store_out(a, slot, row0 + q, sum[q]);
+          }
+        }
+      }
+    }
+    worker_ack(a, w, reqs, nreq, epoch);
   }
 }
 
@@ -1248,14 +1426,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
   // no cache line of an exchange slot may survive from an earlier launch
   __threadfence();
-  if ((int)blockIdx.x < a.n_workers) worker_main<W>(a, lds);
-  else controller_main<W>(a, lds);
+  if ((int)blockIdx.x < a.n_workers) {
+    if constexpr (sizeof(W) == 2) {
+      if (a.regw == 2) return worker_regs<2>(a, lds);
+      if (a.regw == 1) return worker_regs<1>(a, lds);
+    }
+    worker_main<W>(a, lds);
+  } else {
+    controller_main<W>(a, lds);
+  }
 }
 
 // ---------------------------------------------------------------------------
 // host side: schedule and launch
 
-size_t plan_tree(TreeArgs& a, int wdtype_bf16, int pops) {
+size_t plan_tree(TreeArgs& a, int wdtype_bf16, int pops, int max_workers, int lds_workers) {
   const int esz = wdtype_bf16 ? 2 : 4;
   const size_t lds_max = 160 * 1024;
   const int kp = k_padded(a.ds);
@@ -1263,16 +1448,29 @@ size_t plan_tree(TreeArgs& a, int wdtype_bf16, int pops) {
   // nodes per request per step: fill about TREE_MAX_COLS columns
   int p = pops > 0 ? pops : TREE_MAX_COLS / a.B;
   p = std::max(1, std::min(std::min(p, PMAX), TREE_MAX_COLS / a.B));
+  const int lds_n_workers = a.n_workers;
   for (; p >= 1; --p) {
     const int cols = a.B * p;
-    if (a.tiles_per_worker * ((cols + 15) / 16) > 4 * PPW) continue;
-    // worker staging phases: kc | kp, 32 | kc, stage within its share of LDS
+    const int ncb = (cols + 15) / 16;
+    // register workers: one tile per wave if that many blocks fit, else two
+    int regw = 0, n_workers = lds_n_workers;
+    if (wdtype_bf16 && kp == RKB * 32 && !lds_workers) {
+      for (int tw = 1; tw <= 2 && !regw; ++tw) {
+        const int nw = ((a.n_tiles + tw - 1) / tw * ncb + 3) / 4;
+        if (nw <= max_workers) regw = tw, n_workers = nw;
+      }
+    }
     int kc = kp;
-    const size_t stage_cap = wdtype_bf16 ? 68 * 1024 : lds_max - worker_stage_offset(a.tiles_per_worker, kp, esz) -
-                                                           (size_t)(2 * TREE_MAX_COLS + 64) * 4;
-    while ((size_t)round_up(cols, 16) * (kc + STAGE_PAD) * esz > stage_cap && kc % 64 == 0 && wdtype_bf16) kc /= 2;
-    const size_t wl = worker_lds_bytes(a.tiles_per_worker, kp, kc, cols, esz);
-    if (wl > lds_max) continue;
+    size_t wl = (size_t)(2 * TREE_MAX_COLS + 64) * 4;
+    if (!regw) {
+      if (a.tiles_per_worker * ncb > 4 * PPW) continue;
+      // worker staging phases: kc | kp, 32 | kc, stage within its share of LDS
+      const size_t stage_cap = wdtype_bf16 ? 68 * 1024 : lds_max - worker_stage_offset(a.tiles_per_worker, kp, esz) -
+                                                             (size_t)(2 * TREE_MAX_COLS + 64) * 4;
+      while ((size_t)round_up(cols, 16) * (kc + STAGE_PAD) * esz > stage_cap && kc % 64 == 0 && wdtype_bf16) kc /= 2;
+      wl = worker_lds_bytes(a.tiles_per_worker, kp, kc, cols, esz);
+      if (wl > lds_max) continue;
+    }
     // controller: records for the budget, the root and speculation room; the
     // frontier bound (k - 1) xcap + 1 must fit the merge's registers
     int qmax = p == 1 ? 8 : QCAP;
@@ -1285,6 +1483,9 @@ size_t plan_tree(TreeArgs& a, int wdtype_bf16, int pops) {
     if (qmax < 1) continue;
     a.p = p;
     a.kc = kc;
+    a.regw = regw;
+    a.ncbmax = ncb;
+    a.n_workers = n_workers;
     a.qmax = qmax;
     a.xcap = xcap;
     a.fcap = fcap;

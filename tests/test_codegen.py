@@ -50,23 +50,34 @@ def test_tree_kernel_uses_no_scratch(asm, tmpl):
         assert priv == 0
 
 
-def _staging_runs(body):
-    # the worker's region: from its mailbox poll (the sleep before the first
-    # MFMA) to that MFMA; count the 16-byte loads issued between two waits on
-    # vector memory
-    first_mfma = next(i for i, l in enumerate(body) if l.startswith("v_mfma"))
-    poll = max(i for i, l in enumerate(body[:first_mfma]) if l.startswith("s_sleep"))
-    runs, n = [], 0
-    for l in body[poll:first_mfma]:
+def _worker_region(body):
+    # from the worker's mailbox poll (the sleep before the first MFMA) to the
+    # last MFMA (only workers multiply on the matrix cores)
+    mfma = [i for i, l in enumerate(body) if l.startswith("v_mfma")]
+    poll = max(i for i, l in enumerate(body[:mfma[0]]) if l.startswith("s_sleep"))
+    return body[poll:mfma[-1] + 1]
+
+
+def _load_runs(body):
+    # runs of 16-byte loads issued between two waits on vector memory
+    runs, cur = [], []
+    for l in _worker_region(body):
         if l.startswith("global_load_dwordx4"):
-            n += 1
+            cur.append(l)
         elif l.startswith("s_waitcnt") and "vmcnt" in l:
-            if n:
-                runs.append(n)
-            n = 0
+            if cur:
+                runs.append(cur)
+            cur = []
     return runs
 
 
-def test_worker_staging_loads_are_batched(asm):
-    runs = _staging_runs(_kernel(asm, "t")[0])
-    assert runs and max(runs) >= 8, f"staging loads are not batched: {runs}"
+def test_lds_worker_staging_loads_are_batched(asm):
+    # the LDS worker's staging batch: 16 loads addressed from one base (saddr)
+    runs = [r for r in _load_runs(_kernel(asm, "t")[0]) if all(re.search(r", s\[\d+:\d+\]$", l) for l in r)]
+    assert runs and max(len(r) for r in runs) >= 16, f"staging loads are not batched: {[len(r) for r in runs]}"
+
+
+def test_register_worker_operand_loads_are_batched(asm):
+    # the register worker: all 32 k blocks of a lane's B operands in one batch
+    runs = [r for r in _load_runs(_kernel(asm, "t")[0]) if any("offset:1984" in l for l in r)]
+    assert runs and all(len(r) == 32 for r in runs), [len(r) for r in runs]

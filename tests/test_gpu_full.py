@@ -82,6 +82,14 @@ def test_q8b_b32(dev, q8b_builder):
     _full_case(spec, w, req, q8b_builder, [0, 7, 19, 31])
 
 
+def test_q8b_b32_lds_workers(dev, q8b_builder, monkeypatch):
+    # the workers that stage operands in LDS (the schedule for d_s other than
+    # 1024) at the full shape, on the same handle
+    monkeypatch.setenv("DT_WORKERS", "lds")
+    spec, w, req = synth.workload("q8b_b32")
+    _full_case(spec, w, req, q8b_builder, [0, 31])
+
+
 def test_q8b_b32_fullv_and_smaller_batch_reuse_handle(dev, q8b_builder):
     # the same handle serves a smaller batch and the full-vocabulary normaliser
     spec, w, req = synth.workload("q8b_b32")

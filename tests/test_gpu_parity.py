@@ -65,10 +65,13 @@ def test_small_fp32(dev, name, kw):
     tb.close()
 
 
-@pytest.mark.parametrize("B,M,k,N", [(1, 16, 4, 40), (5, 32, 8, 64), (32, 16, 4, 50)])
-def test_small_bf16(dev, B, M, k, N):
-    spec = synth.small(f"bf16_{B}_{M}", V=5000, D=8, h=64, e=96, ds=128, r=64, M=M, k=k, N=N,
-                       B=B, wdtype="bf16", group=400 + B, emb_std=0.5)
+# d_s = 1024 runs the register-resident workers (one or two tiles per wave),
+# other sizes the workers that stage operands in LDS
+@pytest.mark.parametrize("B,M,k,N,ds", [(1, 16, 4, 40, 128), (5, 32, 8, 64, 128), (32, 16, 4, 50, 128),
+                                        (1, 16, 4, 40, 1024), (3, 8, 3, 30, 1024), (32, 8, 4, 24, 1024)])
+def test_small_bf16(dev, B, M, k, N, ds):
+    spec = synth.small(f"bf16_{B}_{M}_{ds}", V=5000, D=8, h=64, e=96, ds=ds, r=64, M=M, k=k, N=N,
+                       B=B, wdtype="bf16", group=400 + B + (0 if ds == 128 else ds), emb_std=0.5)
     spec, w, req = synth.workload(spec)
     tb = gu.make_builder(spec, w)
     got = gu.run(tb, spec, req)
