@@ -470,58 +470,33 @@ __device__ __forceinline__ void worker_main(const TreeArgs& a, unsigned char* ld
 
 // ---- register-resident worker (bf16, d_s padded to RKB * 32 = 1024)
 // Each wave owns TW tiles of [W_hh ; W1_S^T], held in registers as MFMA A
-// operands for the whole launch, and one 16-column block of each step: it
-// loads its columns' operands straight into B registers (one batch of RKB
-// 16-byte loads per lane, all in flight together) and runs RKB MFMAs per
-// tile.  No LDS staging: one memory round trip per step, and every byte of the
-// operands crosses the load path once per wave that multiplies it.
-// Wave task = w * 4 + wave: tile group task / ncbmax (tiles TW g .. TW g +
-// TW - 1), column block task % ncbmax.
+// operands for the whole launch.  A block owns one 16-column block of each
+// step (block w: column block w % ncbmax) and its four waves four tile groups
+// (wave v: tile group 4 (w / ncbmax) + v, tiles TW g .. TW g + TW - 1).  Per
+// step the block stages its 16 columns' operands in LDS once (one batch of
+// eight 16-byte loads per thread, whole 128-byte lines) and every wave runs RKB
+// MFMAs per tile on them, so an operand byte crosses the load path once per
+// block rather than once per wave.
 constexpr int RKB = 32;
+constexpr int REGW_STAGE_OFFSET = 2048;  // after coln, reqs, misc
+constexpr int RSTRIDE = RKB * 32 + 8;  // staged column stride (elements): 16-byte skew per column
 
-// RKB 16-byte loads at p + 64 q bytes (q < RKB): one lane's B operands of all
-// k blocks; issued back to back and completed together
-__device__ __forceinline__ void load_b_operands(const void* p, bf16x8 (&v)[RKB]) {
+// Eight 16-byte loads from base + off[q] (byte offsets), issued back to back
+// and completed together (one asm block, like load16_batch).
+__device__ __forceinline__ void load8_batch(const void* base, const unsigned (&off)[8], u32x4 (&v)[8]) {
   asm volatile(
-      "global_load_dwordx4 %0, %32, off\n\t"
-      "global_load_dwordx4 %1, %32, off offset:64\n\t"
-      "global_load_dwordx4 %2, %32, off offset:128\n\t"
-      "global_load_dwordx4 %3, %32, off offset:192\n\t"
-      "global_load_dwordx4 %4, %32, off offset:256\n\t"
-      "global_load_dwordx4 %5, %32, off offset:320\n\t"
-      "global_load_dwordx4 %6, %32, off offset:384\n\t"
-      "global_load_dwordx4 %7, %32, off offset:448\n\t"
-      "global_load_dwordx4 %8, %32, off offset:512\n\t"
-      "global_load_dwordx4 %9, %32, off offset:576\n\t"
-      "global_load_dwordx4 %10, %32, off offset:640\n\t"
-      "global_load_dwordx4 %11, %32, off offset:704\n\t"
-      "global_load_dwordx4 %12, %32, off offset:768\n\t"
-      "global_load_dwordx4 %13, %32, off offset:832\n\t"
-      "global_load_dwordx4 %14, %32, off offset:896\n\t"
-      "global_load_dwordx4 %15, %32, off offset:960\n\t"
-      "global_load_dwordx4 %16, %32, off offset:1024\n\t"
-      "global_load_dwordx4 %17, %32, off offset:1088\n\t"
-      "global_load_dwordx4 %18, %32, off offset:1152\n\t"
-      "global_load_dwordx4 %19, %32, off offset:1216\n\t"
-      "global_load_dwordx4 %20, %32, off offset:1280\n\t"
-      "global_load_dwordx4 %21, %32, off offset:1344\n\t"
-      "global_load_dwordx4 %22, %32, off offset:1408\n\t"
-      "global_load_dwordx4 %23, %32, off offset:1472\n\t"
-      "global_load_dwordx4 %24, %32, off offset:1536\n\t"
-      "global_load_dwordx4 %25, %32, off offset:1600\n\t"
-      "global_load_dwordx4 %26, %32, off offset:1664\n\t"
-      "global_load_dwordx4 %27, %32, off offset:1728\n\t"
-      "global_load_dwordx4 %28, %32, off offset:1792\n\t"
-      "global_load_dwordx4 %29, %32, off offset:1856\n\t"
-      "global_load_dwordx4 %30, %32, off offset:1920\n\t"
-      "global_load_dwordx4 %31, %32, off offset:1984\n\t"
+      "global_load_dwordx4 %0, %8, %16\n\t"
+      "global_load_dwordx4 %1, %9, %16\n\t"
+      "global_load_dwordx4 %2, %10, %16\n\t"
+      "global_load_dwordx4 %3, %11, %16\n\t"
+      "global_load_dwordx4 %4, %12, %16\n\t"
+      "global_load_dwordx4 %5, %13, %16\n\t"
+      "global_load_dwordx4 %6, %14, %16\n\t"
+      "global_load_dwordx4 %7, %15, %16\n\t"
       "s_waitcnt vmcnt(0)"
-      : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3]), "=&v"(v[4]), "=&v"(v[5]), "=&v"(v[6]), "=&v"(v[7]),
-        "=&v"(v[8]), "=&v"(v[9]), "=&v"(v[10]), "=&v"(v[11]), "=&v"(v[12]), "=&v"(v[13]), "=&v"(v[14]),
-        "=&v"(v[15]), "=&v"(v[16]), "=&v"(v[17]), "=&v"(v[18]), "=&v"(v[19]), "=&v"(v[20]), "=&v"(v[21]),
-        "=&v"(v[22]), "=&v"(v[23]), "=&v"(v[24]), "=&v"(v[25]), "=&v"(v[26]), "=&v"(v[27]), "=&v"(v[28]),
-        "=&v"(v[29]), "=&v"(v[30]), "=&v"(v[31])
-      : "v"(p)
+      : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3]), "=&v"(v[4]), "=&v"(v[5]), "=&v"(v[6]), "=&v"(v[7])
+      : "v"(off[0]), "v"(off[1]), "v"(off[2]), "v"(off[3]), "v"(off[4]), "v"(off[5]), "v"(off[6]), "v"(off[7]),
+        "s"(base)
       : "memory");
 }
 
@@ -533,11 +508,11 @@ __device__ __forceinline__ void worker_regs(const TreeArgs& a, unsigned char* ld
   int* coln = reinterpret_cast<int*>(lds);
   int* reqs = coln + TREE_MAX_COLS;
   int* misc = reqs + TREE_MAX_COLS;
+  uint16_t* stage = reinterpret_cast<uint16_t*>(lds + REGW_STAGE_OFFSET);  // [16][RSTRIDE]
   const int kp = RKB * 32;
   const int as = act_stride(a.ds);
-  const int task = w * 4 + wv;
-  const int tg = task / a.ncbmax, cb = task - tg * a.ncbmax;
-  const int tile0 = tg * TW;
+  const int cb = w % a.ncbmax;
+  const int tile0 = ((w / a.ncbmax) * 4 + wv) * TW;
 
   // this wave's A operands: tile rows (lane & 15), k 8 (lane >> 4) + 32 kb
   bf16x8 wa[TW][RKB];
@@ -555,43 +530,62 @@ __device__ __forceinline__ void worker_regs(const TreeArgs& a, unsigned char* ld
     worker_columns(a, w, t, coln, reqs, misc);
     const int ncols = misc[0], nreq = misc[1];
     if (ncols <= 0) return;  // a wait ran out, or every request is finished
-    if (tile0 < a.n_tiles && cb * 16 < ncols) {
-      const int col = cb * 16 + (lane & 15);
-      const size_t slot = (size_t)coln[min(col, ncols - 1)];
-      bf16x8 bv[RKB];
-      load_b_operands(reinterpret_cast<const uint16_t*>(a.act) + slot * as + 8 * (lane >> 4), bv);
-      floatx4 acc[TW][2];
+    if (cb * 16 < ncols) {
+      // stage: thread piece tid + 256 q = column (tid >> 7) + 2 q, 16-byte piece tid & 127
+      const int slot0 = (int)slot_of(a, t, 0, 0);
+      const int pc = tid & 127;
+      unsigned off[8];
+      u32x4 v[8];
 #pragma unroll
-      for (int i = 0; i < TW; ++i) acc[i][0] = acc[i][1] = floatx4{0.f, 0.f, 0.f, 0.f};
+      for (int q = 0; q < 8; ++q) {
+        const int c = min(cb * 16 + (tid >> 7) + 2 * q, ncols - 1);  // clamped: always a valid column
+        off[q] = (unsigned)(((coln[c] - slot0) * as + pc * 8) * 2);
+      }
+      load8_batch(reinterpret_cast<const uint16_t*>(a.act) + (size_t)slot0 * as, off, v);
 #pragma unroll
-      for (int kb = 0; kb < RKB; ++kb)
+      for (int q = 0; q < 8; ++q)
+        *reinterpret_cast<u32x4*>(stage + ((tid >> 7) + 2 * q) * RSTRIDE + pc * 8) = v[q];
+      __syncthreads();
+      if (tile0 < a.n_tiles) {
+        // B operands: column (lane & 15), k 8 (lane >> 4) + 32 kb
+        const uint16_t* sb = stage + (lane & 15) * RSTRIDE + 8 * (lane >> 4);
+        floatx4 acc[TW][2];
 #pragma unroll
-        for (int i = 0; i < TW; ++i)
-          acc[i][kb & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa[i][kb], bv[kb], acc[i][kb & 1], 0, 0, 0);
-      // lane holds column col, rows 4 (lane >> 4) + q of each tile
-      if (col < ncols) {
-        const int ds3 = 3 * a.ds;
+        for (int i = 0; i < TW; ++i) acc[i][0] = acc[i][1] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int i = 0; i < TW; ++i) {
-          if (tile0 + i >= a.n_tiles) continue;
-          const floatx4 sum = acc[i][0] + acc[i][1];
-          const int row0 = (tile0 + i) * 16 + 4 * (lane >> 4);
-          if (row0 + 3 < ds3 && (ds3 & 3) == 0) {
-            floatx4 v = sum;
-            if (a.b_hh) {
-              v[0] += a.b_hh[row0];
-              v[1] += a.b_hh[row0 + 1];
-              v[2] += a.b_hh[row0 + 2];
-              v[3] += a.b_hh[row0 + 3];
+        for (int kb = 0; kb < RKB; ++kb) {
+          const bf16x8 bv = *reinterpret_cast<const bf16x8*>(sb + kb * 32);
+#pragma unroll
+          for (int i = 0; i < TW; ++i)
+            acc[i][kb & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa[i][kb], bv, acc[i][kb & 1], 0, 0, 0);
+        }
+        // lane holds column col, rows 4 (lane >> 4) + q of each tile
+        const int col = cb * 16 + (lane & 15);
+        if (col < ncols) {
+          const size_t slot = (size_t)coln[col];
+          const int ds3 = 3 * a.ds;
+#pragma unroll
+          for (int i = 0; i < TW; ++i) {
+            if (tile0 + i >= a.n_tiles) continue;
+            const floatx4 sum = acc[i][0] + acc[i][1];
+            const int row0 = (tile0 + i) * 16 + 4 * (lane >> 4);
+            if (row0 + 3 < ds3 && (ds3 & 3) == 0) {
+              floatx4 o = sum;
+              if (a.b_hh) {
+                o[0] += a.b_hh[row0];
+                o[1] += a.b_hh[row0 + 1];
+                o[2] += a.b_hh[row0 + 2];
+                o[3] += a.b_hh[row0 + 3];
+              }
+              st_dev_f32x4(a.gh + slot * gh_stride(a.ds) + row0, o);
+            } else {
+              for (int q = 0; q < 4; ++q) worker_store_out(a, slot, row0 + q, sum[q]);
             }
-            st_dev_f32x4(a.gh + slot * gh_stride(a.ds) + row0, v);
-          } else {
-            for (int q = 0; q < 4; ++q) worker_store_out(a, slot, row0 + q, sum[q]);
           }
         }
       }
     }
-    worker_ack(a, w, reqs, nreq, epoch);
+    worker_ack(a, w, reqs, nreq, epoch);  // its barrier also ends this step's stage reads
   }
 }
 
@@ -1456,12 +1450,12 @@ size_t plan_tree(TreeArgs& a, int wdtype_bf16, int pops, int max_workers, int ld
     int regw = 0, n_workers = lds_n_workers;
     if (wdtype_bf16 && kp == RKB * 32 && !lds_workers) {
       for (int tw = 1; tw <= 2 && !regw; ++tw) {
-        const int nw = ((a.n_tiles + tw - 1) / tw * ncb + 3) / 4;
+        const int nw = ((a.n_tiles + tw - 1) / tw + 3) / 4 * ncb;
         if (nw <= max_workers) regw = tw, n_workers = nw;
       }
     }
     int kc = kp;
-    size_t wl = (size_t)(2 * TREE_MAX_COLS + 64) * 4;
+    size_t wl = REGW_STAGE_OFFSET + (size_t)16 * RSTRIDE * 2;
     if (!regw) {
       if (a.tiles_per_worker * ncb > 4 * PPW) continue;
       // worker staging phases: kc | kp, 32 | kc, stage within its share of LDS

@@ -78,6 +78,6 @@ def test_lds_worker_staging_loads_are_batched(asm):
 
 
 def test_register_worker_operand_loads_are_batched(asm):
-    # the register worker: all 32 k blocks of a lane's B operands in one batch
-    runs = [r for r in _load_runs(_kernel(asm, "t")[0]) if any("offset:1984" in l for l in r)]
-    assert runs and all(len(r) == 32 for r in runs), [len(r) for r in runs]
+    # the register worker's staging: eight loads per thread in one batch
+    runs = [r for r in _load_runs(_kernel(asm, "t")[0]) if all(re.search(r", s\[\d+:\d+\]$", l) for l in r)]
+    assert any(len(r) == 8 for r in runs), [len(r) for r in runs]
