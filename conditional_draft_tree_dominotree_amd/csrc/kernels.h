@@ -55,7 +55,8 @@ struct TreeArgs {
   // schedule (set by plan_tree)
   int p;                // nodes a request may expand per step (exchange columns per request)
   int kc;               // state elements a worker stages per phase (kp / kc phases)
-  int regw;             // 0: workers stage operands in LDS; 1, 2: register workers, tiles per wave
+  int regw;             // 0: workers stage operands in LDS; register workers: 1 (1 tile per wave, 1
+                        // column block per block), 2 (2 tiles, 1 block), 3 (2 tiles, 2 blocks)
   int ncbmax;           // register workers: 16-column blocks per step
   int xcap;             // node records per request (budget + root + speculation room)
   int fcap;             // frontier entries per request
@@ -86,7 +87,7 @@ struct TreeArgs {
   unsigned spin_limit;
 };
 // Exchange columns a build may use per step (slots per step = B p <= this).
-constexpr int TREE_MAX_COLS = 128;
+constexpr int TREE_MAX_COLS = 256;
 // Fills the schedule fields of `a` (p from `pops`, 0 = automatic) and returns
 // the dynamic LDS bytes the launch needs, or 0 if the shape cannot be served.
 // With register workers (allowed unless `lds_workers`) it also sets

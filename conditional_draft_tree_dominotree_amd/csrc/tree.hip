@@ -132,7 +132,7 @@ __device__ __forceinline__ float w_to_f32<float>(float v) { return v; }
 // ---------------------------------------------------------------------------
 // layout helpers
 
-__host__ __device__ inline int round_up(int x, int m) { return (x + m - 1) / m * m; }
+__host__ __device__ constexpr int round_up(int x, int m) { return (x + m - 1) / m * m; }
 __host__ __device__ inline int act_stride(int ds) { return round_up(ds, 64); }     // elements
 __host__ __device__ inline int k_padded(int ds) { return round_up(ds, 32); }
 __host__ __device__ inline int st_stride(int ds) { return round_up(ds, 32); }      // floats
@@ -470,15 +470,15 @@ __device__ __forceinline__ void worker_main(const TreeArgs& a, unsigned char* ld
 
 // ---- register-resident worker (bf16, d_s padded to RKB * 32 = 1024)
 // Each wave owns TW tiles of [W_hh ; W1_S^T], held in registers as MFMA A
-// operands for the whole launch.  A block owns one 16-column block of each
-// step (block w: column block w % ncbmax) and its four waves four tile groups
-// (wave v: tile group 4 (w / ncbmax) + v, tiles TW g .. TW g + TW - 1).  Per
-// step the block stages its 16 columns' operands in LDS once (one batch of
-// eight 16-byte loads per thread, whole 128-byte lines) and every wave runs RKB
-// MFMAs per tile on them, so an operand byte crosses the load path once per
-// block rather than once per wave.
+// operands for the whole launch.  A block owns CPB 16-column blocks of each
+// step (block w: column blocks CPB (w % nb) + c, nb = ceil(ncbmax / CPB)) and
+// its four waves four tile groups (wave v: tile group 4 (w / nb) + v, tiles
+// TW g .. TW g + TW - 1).  Per step the block stages its columns' operands in
+// LDS once (one batch of 8 CPB 16-byte loads per thread, whole 128-byte lines)
+// and every wave runs RKB MFMAs per tile and column block on them, so an
+// operand byte crosses the load path once per block rather than once per wave.
 constexpr int RKB = 32;
-constexpr int REGW_STAGE_OFFSET = 2048;  // after coln, reqs, misc
+constexpr int REGW_STAGE_OFFSET = round_up((2 * TREE_MAX_COLS + 64) * 4, 256);  // after coln, reqs, misc
 constexpr int RSTRIDE = RKB * 32 + 8;  // staged column stride (elements): 16-byte skew per column
 
 // Eight 16-byte loads from base + off[q] (byte offsets), issued back to back
@@ -500,7 +500,7 @@ __device__ __forceinline__ void load8_batch(const void* base, const unsigned (&o
       : "memory");
 }
 
-template <int TW>
+template <int TW, int CPB>
 __device__ __forceinline__ void worker_regs(const TreeArgs& a, unsigned char* lds) {
   const int w = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -508,11 +508,12 @@ __device__ __forceinline__ void worker_regs(const TreeArgs& a, unsigned char* ld
   int* coln = reinterpret_cast<int*>(lds);
   int* reqs = coln + TREE_MAX_COLS;
   int* misc = reqs + TREE_MAX_COLS;
-  uint16_t* stage = reinterpret_cast<uint16_t*>(lds + REGW_STAGE_OFFSET);  // [16][RSTRIDE]
+  uint16_t* stage = reinterpret_cast<uint16_t*>(lds + REGW_STAGE_OFFSET);  // [16 CPB][RSTRIDE]
   const int kp = RKB * 32;
   const int as = act_stride(a.ds);
-  const int cb = w % a.ncbmax;
-  const int tile0 = ((w / a.ncbmax) * 4 + wv) * TW;
+  const int nb = (a.ncbmax + CPB - 1) / CPB;
+  const int col0 = (w % nb) * CPB * 16;  // first column of the block
+  const int tile0 = ((w / nb) * 4 + wv) * TW;
 
   // this wave's A operands: tile rows (lane & 15), k 8 (lane >> 4) + 32 kb
   bf16x8 wa[TW][RKB];
@@ -530,44 +531,59 @@ __device__ __forceinline__ void worker_regs(const TreeArgs& a, unsigned char* ld
     worker_columns(a, w, t, coln, reqs, misc);
     const int ncols = misc[0], nreq = misc[1];
     if (ncols <= 0) return;  // a wait ran out, or every request is finished
-    if (cb * 16 < ncols) {
+    if (col0 < ncols) {
       // stage: thread piece tid + 256 q = column (tid >> 7) + 2 q, 16-byte piece tid & 127
       const int slot0 = (int)slot_of(a, t, 0, 0);
       const int pc = tid & 127;
-      unsigned off[8];
-      u32x4 v[8];
+      const uint16_t* base = reinterpret_cast<const uint16_t*>(a.act) + (size_t)slot0 * as;
+      unsigned off[8 * CPB];
 #pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        const int c = min(cb * 16 + (tid >> 7) + 2 * q, ncols - 1);  // clamped: always a valid column
+      for (int q = 0; q < 8 * CPB; ++q) {
+        const int c = min(col0 + (tid >> 7) + 2 * q, ncols - 1);  // clamped: always a valid column
         off[q] = (unsigned)(((coln[c] - slot0) * as + pc * 8) * 2);
       }
-      load8_batch(reinterpret_cast<const uint16_t*>(a.act) + (size_t)slot0 * as, off, v);
+      if constexpr (CPB == 1) {
+        u32x4 v[8];
+        load8_batch(base, off, v);
 #pragma unroll
-      for (int q = 0; q < 8; ++q)
-        *reinterpret_cast<u32x4*>(stage + ((tid >> 7) + 2 * q) * RSTRIDE + pc * 8) = v[q];
+        for (int q = 0; q < 8; ++q) *reinterpret_cast<u32x4*>(stage + ((tid >> 7) + 2 * q) * RSTRIDE + pc * 8) = v[q];
+      } else {
+        u32x4 v[16];
+        load16_batch(base, off, v);
+#pragma unroll
+        for (int q = 0; q < 16; ++q) *reinterpret_cast<u32x4*>(stage + ((tid >> 7) + 2 * q) * RSTRIDE + pc * 8) = v[q];
+      }
       __syncthreads();
       if (tile0 < a.n_tiles) {
-        // B operands: column (lane & 15), k 8 (lane >> 4) + 32 kb
+        // B operands: column (lane & 15) of each column block, k 8 (lane >> 4) + 32 kb
         const uint16_t* sb = stage + (lane & 15) * RSTRIDE + 8 * (lane >> 4);
-        floatx4 acc[TW][2];
+        floatx4 acc[CPB][TW][2];
 #pragma unroll
-        for (int i = 0; i < TW; ++i) acc[i][0] = acc[i][1] = floatx4{0.f, 0.f, 0.f, 0.f};
+        for (int c = 0; c < CPB; ++c)
+#pragma unroll
+          for (int i = 0; i < TW; ++i) acc[c][i][0] = acc[c][i][1] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kb = 0; kb < RKB; ++kb) {
-          const bf16x8 bv = *reinterpret_cast<const bf16x8*>(sb + kb * 32);
+          bf16x8 bv[CPB];
 #pragma unroll
-          for (int i = 0; i < TW; ++i)
-            acc[i][kb & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa[i][kb], bv, acc[i][kb & 1], 0, 0, 0);
+          for (int c = 0; c < CPB; ++c) bv[c] = *reinterpret_cast<const bf16x8*>(sb + c * 16 * RSTRIDE + kb * 32);
+#pragma unroll
+          for (int c = 0; c < CPB; ++c)
+#pragma unroll
+            for (int i = 0; i < TW; ++i)
+              acc[c][i][kb & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa[i][kb], bv[c], acc[c][i][kb & 1], 0, 0, 0);
         }
         // lane holds column col, rows 4 (lane >> 4) + q of each tile
-        const int col = cb * 16 + (lane & 15);
-        if (col < ncols) {
+        const int ds3 = 3 * a.ds;
+#pragma unroll
+        for (int c = 0; c < CPB; ++c) {
+          const int col = col0 + c * 16 + (lane & 15);
+          if (col >= ncols) continue;
           const size_t slot = (size_t)coln[col];
-          const int ds3 = 3 * a.ds;
 #pragma unroll
           for (int i = 0; i < TW; ++i) {
             if (tile0 + i >= a.n_tiles) continue;
-            const floatx4 sum = acc[i][0] + acc[i][1];
+            const floatx4 sum = acc[c][i][0] + acc[c][i][1];
             const int row0 = (tile0 + i) * 16 + 4 * (lane >> 4);
             if (row0 + 3 < ds3 && (ds3 & 3) == 0) {
               floatx4 o = sum;
@@ -1422,8 +1438,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   __threadfence();
   if ((int)blockIdx.x < a.n_workers) {
     if constexpr (sizeof(W) == 2) {
-      if (a.regw == 2) return worker_regs<2>(a, lds);
-      if (a.regw == 1) return worker_regs<1>(a, lds);
+      if (a.regw == 1) return worker_regs<1, 1>(a, lds);
+      if (a.regw == 2) return worker_regs<2, 1>(a, lds);
+      if (a.regw == 3) return worker_regs<2, 2>(a, lds);
     }
     worker_main<W>(a, lds);
   } else {
@@ -1449,13 +1466,15 @@ size_t plan_tree(TreeArgs& a, int wdtype_bf16, int pops, int max_workers, int ld
     // register workers: one tile per wave if that many blocks fit, else two
     int regw = 0, n_workers = lds_n_workers;
     if (wdtype_bf16 && kp == RKB * 32 && !lds_workers) {
-      for (int tw = 1; tw <= 2 && !regw; ++tw) {
-        const int nw = ((a.n_tiles + tw - 1) / tw + 3) / 4 * ncb;
-        if (nw <= max_workers) regw = tw, n_workers = nw;
+      // (tiles per wave, column blocks per block): 1 = (1, 1), 2 = (2, 1), 3 = (2, 2)
+      for (int m = 1; m <= 3 && !regw; ++m) {
+        const int tw = m == 1 ? 1 : 2, cpb = m == 3 ? 2 : 1;
+        const int nw = ((a.n_tiles + tw - 1) / tw + 3) / 4 * ((ncb + cpb - 1) / cpb);
+        if (nw <= max_workers) regw = m, n_workers = nw;
       }
     }
     int kc = kp;
-    size_t wl = REGW_STAGE_OFFSET + (size_t)16 * RSTRIDE * 2;
+    size_t wl = REGW_STAGE_OFFSET + (size_t)(regw == 3 ? 32 : 16) * RSTRIDE * 2;
     if (!regw) {
       if (a.tiles_per_worker * ncb > 4 * PPW) continue;
       // worker staging phases: kc | kp, 32 | kc, stage within its share of LDS
