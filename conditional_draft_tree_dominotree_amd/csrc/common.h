@@ -90,6 +90,27 @@ __device__ __forceinline__ float wave_sum_dpp(float v) {
   return (lane_f(v, 15) + lane_f(v, 31)) + (lane_f(v, 47) + lane_f(v, 63));
 }
 
+// The same reductions over each half of the wave (lanes 0-31, 32-63); every
+// lane gets its half's result.  A half's order of operations is that of
+// wave_*_dpp when the other half holds the identity.
+__device__ __forceinline__ float half_max_dpp(float v) {
+  v = fmaxf(v, dpp_row<0x111>(-INFINITY, v));
+  v = fmaxf(v, dpp_row<0x112>(-INFINITY, v));
+  v = fmaxf(v, dpp_row<0x114>(-INFINITY, v));
+  v = fmaxf(v, dpp_row<0x118>(-INFINITY, v));
+  const float h0 = fmaxf(lane_f(v, 15), lane_f(v, 31)), h1 = fmaxf(lane_f(v, 47), lane_f(v, 63));
+  const float o0 = fmaxf(h0, -INFINITY), o1 = fmaxf(h1, -INFINITY);
+  return (threadIdx.x & 32) ? o1 : o0;
+}
+__device__ __forceinline__ float half_sum_dpp(float v) {
+  v += dpp_row<0x111>(0.f, v);
+  v += dpp_row<0x112>(0.f, v);
+  v += dpp_row<0x114>(0.f, v);
+  v += dpp_row<0x118>(0.f, v);
+  const float h0 = lane_f(v, 15) + lane_f(v, 31), h1 = lane_f(v, 47) + lane_f(v, 63);
+  return (threadIdx.x & 32) ? h1 + 0.f : h0 + 0.f;
+}
+
 // Sort one value per lane of a wave in descending order (bitonic network).
 __device__ __forceinline__ uint64_t wave_sort_desc_u64(uint64_t v) {
   const int lane = threadIdx.x & 63;

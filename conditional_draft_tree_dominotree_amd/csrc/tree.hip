@@ -60,7 +60,7 @@ constexpr int QCAP = 32;     // frontier entries tested per pop round
 constexpr int FCAPMAX = 6144;  // frontier entries per request
 constexpr int XMAX = 2047;   // records per request (11-bit parent field)
 constexpr int PPW = 2;       // (tile, column block) pairs per worker wave
-constexpr int GA = 4;        // states advanced together per controller thread
+constexpr int GA = 8;        // states advanced together per controller thread
 
 // ---------------------------------------------------------------------------
 // device-scope memory operations
@@ -71,8 +71,11 @@ __device__ __forceinline__ void st_dev_u32(void* p, uint32_t v) {
 __device__ __forceinline__ void st_dev_u16(void* p, uint32_t v) {
   asm volatile("global_store_short %0, %1, off sc1" ::"v"(p), "v"(v) : "memory");
 }
+// A store of more than 8 bytes reads its data registers after it issues; the
+// compiler does not see into the asm, so the asm itself waits out that window
+// before any following instruction may overwrite them.
 __device__ __forceinline__ void st_dev_f32x4(void* p, floatx4 v) {
-  asm volatile("global_store_dwordx4 %0, %1, off sc1" ::"v"(p), "v"(v) : "memory");
+  asm volatile("global_store_dwordx4 %0, %1, off sc1\n\ts_nop 1" ::"v"(p), "v"(v) : "memory");
 }
 __device__ __forceinline__ uint32_t ld_dev_u32(const void* p) {
   uint32_t v;
@@ -891,9 +894,45 @@ __device__ __forceinline__ void ctl_expand(const TreeArgs& a, const CtlLds& c, i
     }
   }
   __syncthreads();
-  // one wave per node, one candidate per lane: log-softmax over the candidates
-  // (plus the base tail under fullv), rank by (z desc, token asc), keep the k
-  // best with a finite log-prob.  -inf log-probs rank after every finite one.
+  // one half-wave (M <= 32) or wave per node, one candidate per lane:
+  // log-softmax over the candidates (plus the base tail under fullv), rank by
+  // (z desc, token asc), keep the k best with a finite log-prob.  -inf
+  // log-probs rank after every finite one.
+  if (M <= 32) {
+    const int half = lane >> 5, l32 = lane & 31;
+    for (int j0 = 2 * wv; j0 < e; j0 += 8) {
+      const int j = j0 + half;
+      const bool node = j < e;
+      const int jr = node ? j : j0;  // a valid node for the reads
+      const int y = c.f->ex_rec[jr];
+      const int dy = c.f->ex_dep[jr];
+      const float yscore = key_score(c.rec[y].key);
+      const bool has = node && l32 < M;
+      const float zv = has ? c.f->z[jr * 64 + l32] : -INFINITY;
+      const int idv = has ? c.cand[dy * M + l32].id : 0x7FFFFFFF;
+      const float tl = a.fullv ? c.tailv[dy] : -INFINITY;
+      const float mx = fmaxf(half_max_dpp(zv), tl);
+      const bool live = mx > -INFINITY;
+      float se = half_sum_dpp(has && live ? expf(zv - mx) : 0.f);
+      if (tl > -INFINITY) se += expf(tl - mx);
+      const float lz = live ? mx + logf(se) : -INFINITY;
+      const float lp = zv - lz;
+      const uint64_t me = has ? cand_pack(f32_key(zv), (uint32_t)idv) : 0ull;
+      const uint32_t mlo = (uint32_t)me, mhi = (uint32_t)(me >> 32);
+      int rank = 0;
+      for (int q = 0; q < M; ++q) {
+        const uint32_t h0 = (uint32_t)__builtin_amdgcn_readlane((int)mhi, q);
+        const uint32_t l0 = (uint32_t)__builtin_amdgcn_readlane((int)mlo, q);
+        const uint32_t h1 = (uint32_t)__builtin_amdgcn_readlane((int)mhi, q + 32);
+        const uint32_t l1 = (uint32_t)__builtin_amdgcn_readlane((int)mlo, q + 32);
+        const uint64_t o = half ? ((uint64_t)h1 << 32 | l1) : ((uint64_t)h0 << 32 | l0);
+        rank += o > me;
+      }
+      const bool ok = has && isfinite(lp);
+      if (has && rank < k)
+        c.nc[j * k + rank] = ok ? make_key(yscore + lp, dy + 1, c.cand[dy * M + l32].rank, y, l32) : 0ull;
+    }
+  } else
   for (int j = wv; j < e; j += 4) {
     const int y = c.f->ex_rec[j];
     const int dy = c.f->ex_dep[j];

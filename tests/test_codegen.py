@@ -81,3 +81,28 @@ def test_register_worker_operand_loads_are_batched(asm):
     # the register worker's staging: eight loads per thread in one batch
     runs = [r for r in _load_runs(_kernel(asm, "t")[0]) if all(re.search(r", s\[\d+:\d+\]$", l) for l in r)]
     assert any(len(r) == 8 for r in runs), [len(r) for r in runs]
+
+
+def _vregs(op):
+    m = re.match(r"v\[(\d+):(\d+)\]", op)
+    if m:
+        return set(range(int(m.group(1)), int(m.group(2)) + 1))
+    m = re.match(r"v(\d+)$", op)
+    return {int(m.group(1))} if m else set()
+
+
+@pytest.mark.parametrize("tmpl", ["t", "f"])
+def test_wide_store_data_not_overwritten_next(asm, tmpl):
+    # a vector store of more than 8 bytes reads its data registers a cycle
+    # after it issues: the next instruction must not write them
+    body = [l for l in _kernel(asm, tmpl)[0] if l and not l.startswith((";", "."))]
+    bad = []
+    for i, l in enumerate(body[:-1]):
+        if l.startswith(("global_store_dwordx3", "global_store_dwordx4", "buffer_store_dwordx4")):
+            data = _vregs(l.split(None, 1)[1].split(",")[1].strip())
+            nxt = body[i + 1]
+            if nxt.startswith("v_") and not nxt.startswith(("v_readlane", "v_cmp")):
+                dst = nxt.split(None, 1)[1].split(",")[0].strip()
+                if _vregs(dst) & data:
+                    bad.append((l, nxt))
+    assert not bad, bad[:5]
