@@ -848,9 +848,46 @@ __device__ __forceinline__ void ctl_expand(const TreeArgs& a, const CtlLds& c, i
     }
   }
   __syncthreads();
-  // dL_{j,m} = W2[:, cand_m] . a_j: tpc threads per (node, candidate), each a
-  // contiguous slice of the rank, combined in a fixed order
-  {
+  // dL_{j,m} = W2[:, cand_m] . a_j.  bf16 rows: a quad of threads per (node,
+  // 4 candidates), thread h of the quad taking elements 32 i + 8 h .. + 7 of
+  // all four rows (each a_j read serves four rows; a quad reads 64 consecutive
+  // bytes of a row), combined in a fixed order.
+  if (sizeof(W) == 2 && (M & 3) == 0 && (r & 31) == 0) {
+    const int G4 = M >> 2;
+    const int rs = w2s_stride(r, 2);
+    for (int base = 0; base < e * G4 * 4; base += NT) {
+      const int idx = base + tid, h = idx & 3, rest = idx >> 2;
+      const int j = rest / G4, g = rest - j * G4;
+      const bool valid = j < e;
+      const int jr = valid ? j : 0;
+      const float* avj = c.av + jr * r + 8 * h;
+      const uint16_t* w0 = reinterpret_cast<const uint16_t*>(c.w2s) + (size_t)(c.f->ex_ws[jr] * M + 4 * g) * rs + 8 * h;
+      float acc[4] = {0.f, 0.f, 0.f, 0.f};
+      for (int q0 = 0; q0 < r; q0 += 32) {
+        const float4 x0 = *reinterpret_cast<const float4*>(avj + q0);
+        const float4 x1 = *reinterpret_cast<const float4*>(avj + q0 + 4);
+        const float xa[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+#pragma unroll
+        for (int cc = 0; cc < 4; ++cc) {
+          const uint4 wv4 = *reinterpret_cast<const uint4*>(w0 + cc * rs + q0);
+          const uint32_t wd[4] = {wv4.x, wv4.y, wv4.z, wv4.w};
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            acc[cc] = fmaf(__uint_as_float(wd[q] << 16), xa[2 * q], acc[cc]);
+            acc[cc] = fmaf(__uint_as_float(wd[q] & 0xFFFF0000u), xa[2 * q + 1], acc[cc]);
+          }
+        }
+      }
+#pragma unroll
+      for (int cc = 0; cc < 4; ++cc) {
+        acc[cc] += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(acc[cc]), 0xB1, 0xF, 0xF, false));
+        acc[cc] += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(acc[cc]), 0x4E, 0xF, 0xF, false));
+      }
+      const float dl = h == 0 ? acc[0] : h == 1 ? acc[1] : h == 2 ? acc[2] : acc[3];
+      const int m = 4 * g + h;
+      if (valid) c.f->z[j * 64 + m] = (c.cand[c.f->ex_dep[j] * M + m].val + dl) / a.T + 0.0f;
+    }
+  } else {
     // candidates padded to a power of two so that the index splits are shifts
     int lm = 0;
     while ((1 << lm) < M) ++lm;
@@ -968,10 +1005,12 @@ __device__ __forceinline__ void ctl_expand(const TreeArgs& a, const CtlLds& c, i
 }
 
 // Merge this step's children into the sorted frontier (written to the other
-// buffer), dropping entries that are known to be out (key_u < tau).  Keys are
-// unique, so positions follow from counts: a new entry lands at (its rank
-// among the new) + (old entries ahead of it); old entry i moves up by the new
-// entries ahead of it.  Also resets the pop state of the step.
+// buffer), dropping new entries that are known to be out (key_u < tau); the
+// old entries are all live, since whatever raises tau also cuts the frontier
+// there.  Keys are unique.  First the live new entries are ranked among
+// themselves (S threads per entry), then each thread writes its share of the
+// merged order, found by a binary search on its first output's diagonal
+// (merge path).  Also resets the pop state of the step.
 __device__ __forceinline__ void ctl_merge(const TreeArgs& a, const CtlLds& c, int nnew) {
   const int tid = threadIdx.x;
   const int fh = c.f->misc[C_FH], nf = c.f->misc[C_NF], fb = c.f->misc[C_FB];
@@ -979,47 +1018,56 @@ __device__ __forceinline__ void ctl_merge(const TreeArgs& a, const CtlLds& c, in
   const uint64_t tau = c.f->tau;
   const uint64_t* F = c.front + (size_t)fb * a.fcap + fh;
   uint64_t* O = c.front + (size_t)(1 - fb) * a.fcap;
-  // live old entries: a prefix of the sorted frontier
-  int na = nf - fh;
-  if (tauset) {
-    int lo = 0, hi = na;
-    while (lo < hi) {
-      const int mid = (lo + hi) >> 1;
-      if (key_u(F[mid]) >= tau) lo = mid + 1;
-      else hi = mid;
-    }
-    na = lo;
-  }
-  for (int i = tid; i < nnew; i += NT) {
-    const uint64_t key = c.nc[i];
-    if (key != 0 && (!tauset || key_u(key) >= tau)) {
-      int rn = 0;  // live new entries ahead (any key above a live one is live)
-      for (int q = 0; q < nnew; ++q) rn += c.nc[q] > key;
-      int lo = 0, hi = na;
-      while (lo < hi) {
-        const int mid = (lo + hi) >> 1;
-        if (F[mid] > key) lo = mid + 1;
-        else hi = mid;
-      }
-      c.ncs[rn] = key;
-      c.pn[rn] = lo;
-      atomicAdd(&c.f->misc[C_NV], 1);
+  const int na = nf - fh;
+  {
+    int np = 1;
+    while (np < nnew) np <<= 1;
+    const int ls = NT / np >= 4 ? 2 : NT / np >= 2 ? 1 : 0;  // log2 of the threads per entry
+    const int S = 1 << ls;
+    for (int base = 0; base < (nnew << ls); base += NT) {
+      const int idx = base + tid, i = idx >> ls, s = idx & (S - 1);
+      const uint64_t key = i < nnew ? c.nc[i] : 0ull;
+      int rn = 0;  // new entries ahead (any key above a live one is live)
+      for (int q = s; q < nnew; q += S) rn += c.nc[q] > key;
+      if (ls >= 1) rn += __builtin_amdgcn_update_dpp(0, rn, 0xB1, 0xF, 0xF, false);  // lane ^ 1
+      if (ls >= 2) rn += __builtin_amdgcn_update_dpp(0, rn, 0x4E, 0xF, 0xF, false);  // lane ^ 2
+      const bool live = i < nnew && s == 0 && key != 0 && (!tauset || key_u(key) >= tau);
+      if (live) c.ncs[rn] = key;
+      const unsigned long long bl = __ballot(live);
+      if ((tid & 63) == 0 && bl) atomicAdd(&c.f->misc[C_NV], __popcll(bl));
     }
   }
   __syncthreads();
   const int nv = c.f->misc[C_NV];
-  // (k - 1) xcap + 1 bounds the frontier; the guard only keeps intact
-  for (int i = tid; i < na; i += NT) {
-    int lo = 0, hi = nv;  // new entries with insertion point <= i go ahead of it
-    while (lo < hi) {
-      const int mid = (lo + hi) >> 1;
-      if (c.pn[mid] <= i) lo = mid + 1;
-      else hi = mid;
+  const uint64_t* Nw = c.ncs;
+  {
+    // (k - 1) xcap + 1 bounds the frontier; the guard only keeps intact
+    const int total = min(na + nv, a.fcap);
+    const int L = (na + nv + NT - 1) / NT;
+    const int d0 = min(tid * L, total), d1 = min(d0 + L, total);
+    if (d0 < d1) {
+      // i old and d0 - i new entries precede output d0
+      int lo = max(0, d0 - nv), hi = min(d0, na);
+      while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (F[mid] > Nw[d0 - mid - 1]) lo = mid + 1;
+        else hi = mid;
+      }
+      int i = lo, j = d0 - lo;
+      uint64_t fi = i < na ? F[i] : 0ull, nj = j < nv ? Nw[j] : 0ull;
+      for (int d = d0; d < d1; ++d) {
+        const bool old = j >= nv || (i < na && fi > nj);
+        O[d] = old ? fi : nj;
+        if (old) {
+          ++i;
+          fi = i < na ? F[i] : 0ull;
+        } else {
+          ++j;
+          nj = j < nv ? Nw[j] : 0ull;
+        }
+      }
     }
-    if (i + lo < a.fcap) O[i + lo] = F[i];
   }
-  for (int rr = tid; rr < nv; rr += NT)
-    if (rr + c.pn[rr] < a.fcap) O[rr + c.pn[rr]] = c.ncs[rr];
   if (tid == 0) {
     if (na + nv > a.fcap) atomicOr(a.err, 4);
     c.f->misc[C_FB] = 1 - fb;
