@@ -111,6 +111,23 @@ __device__ __forceinline__ float half_sum_dpp(float v) {
   return (threadIdx.x & 32) ? h1 + 0.f : h0 + 0.f;
 }
 
+// Lane l gets lane l - 1's value (lane 0 gets 0).
+__device__ __forceinline__ uint32_t dpp_wave_shr1(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x138, 0xF, 0xF, false);  // wave_shr:1
+}
+
+// Inclusive OR-scan over the lanes of a wave: within each row of 16 by
+// doubling shifts, then each row takes the totals of the rows before it.
+__device__ __forceinline__ uint32_t wave_or_scan_incl(uint32_t v) {
+  v |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xF, 0xF, false);  // row_shr:1
+  v |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xF, 0xF, false);  // row_shr:2
+  v |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xF, 0xF, false);  // row_shr:4
+  v |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xF, 0xF, false);  // row_shr:8
+  v |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xA, 0xF, false);  // row_bcast:15 to rows 1, 3
+  v |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xC, 0xF, false);  // row_bcast:31 to rows 2, 3
+  return v;
+}
+
 // Sort one value per lane of a wave in descending order (bitonic network).
 __device__ __forceinline__ uint64_t wave_sort_desc_u64(uint64_t v) {
   const int lane = threadIdx.x & 63;

@@ -1203,8 +1203,110 @@ __device__ __forceinline__ int ctl_pop(const TreeArgs& a, const CtlLds& c, int b
     // entries are the longest prefix that is not out and fits the step
     if (tid < 64) {
       const bool has = lane < Q;
-      const bool tie = has && lane > 0 && key_u(F[lane]) == key_u(F[lane - 1]);
-      const bool anytie = __ballot(tie) != 0;
+      const uint64_t fl = has ? F[lane] : 0ull;
+      const uint64_t fprev = ((uint64_t)dpp_wave_shr1((uint32_t)(fl >> 32)) << 32) | dpp_wave_shr1((uint32_t)fl);
+      const bool anytie = __ballot(has && lane > 0 && key_u(fl) == key_u(fprev)) != 0;
+      if (!anytie) {
+        // key order is the total order: everything on registers and ballots
+        const int e0 = c.f->misc[C_E];
+        const int nl0 = c.f->misc[C_NL];
+        const int cl = has ? c.f->cnt[lane] : 0;
+        int wdl = lane < a.nslots ? c.f->wdep[lane] : -1;  // lane s: slot s
+        int wcl = lane < a.nslots ? c.f->wclaim[lane] : 0;
+        const uint64_t key = fl;
+        const int d = key_depth(key);
+        const bool expd = has && d < D;
+        const bool out = has && cl + lane >= N + 1;
+        // depths held by a slot, and by a claimed slot
+        uint32_t hm = 0, cm = 0;
+        int nclaimed = 0;
+        for (int s = 0; s < a.nslots; ++s) {
+          const int ws = __builtin_amdgcn_readlane(wdl, s), wc = __builtin_amdgcn_readlane(wcl, s);
+          if (ws >= 0) {
+            hm |= 1u << ws;
+            if (wc) cm |= 1u << ws;
+          }
+          nclaimed += wc;
+        }
+        const bool held = (hm >> d) & 1u, held_claimed = (cm >> d) & 1u;
+        const unsigned long long bexp = __ballot(expd);
+        // depths expanded by this lane and the earlier ones (inclusive), and by
+        // the earlier ones only
+        const uint32_t dmi = wave_or_scan_incl(expd ? 1u << d : 0u);
+        const uint32_t dmx = dpp_wave_shr1(dmi);
+        const bool first = !((dmx >> d) & 1u);
+        const unsigned long long le = lane == 63 ? ~0ull : ((2ull << lane) - 1ull);  // lanes <= lane
+        const unsigned long long bnew = __ballot(expd && first && !held);
+        const unsigned long long bhu = __ballot(expd && first && held && !held_claimed);
+        const int need = nclaimed + __popcll(bhu & le) + __popcll(bnew & le);
+        const bool fits = has && !out && (!expd || (e0 + __popcll(bexp & le) <= a.p && need <= a.nslots));
+        const unsigned long long bfail = __ballot(has && !fits);
+        const int A = bfail ? __ffsll((long long)bfail) - 1 : Q;
+        const bool isout = A < Q && ((__ballot(out) >> A) & 1ull);
+        const unsigned long long lowA = A >= 64 ? ~0ull : ((1ull << A) - 1ull);
+        // claim the slots of the taken depths, then give new depths free slots
+        const uint32_t dm = A > 0 ? (uint32_t)__builtin_amdgcn_readlane((int)dmi, A - 1) : 0u;
+        if (lane < a.nslots && wdl >= 0 && ((dm >> wdl) & 1u)) wcl = 1;
+        unsigned long long fm = __ballot(lane < a.nslots && !wcl);
+        int nl = nl0;
+        for (unsigned long long bn = bnew & lowA; bn; bn &= bn - 1) {
+          const int dq = __builtin_amdgcn_readlane(d, __ffsll((long long)bn) - 1);
+          const int sl = __ffsll((long long)fm) - 1;  // need <= nslots: a free slot exists
+          fm &= fm - 1;
+          if (lane == sl) {
+            wdl = dq;
+            wcl = 1;
+          }
+          if (lane == 0) c.f->lslots[nl] = sl;
+          ++nl;
+        }
+        if (lane < a.nslots) {
+          c.f->wdep[lane] = wdl;
+          c.f->wclaim[lane] = wcl;
+        }
+        // the taken lanes write their records and the tables of the next step
+        int ws = 0;  // the slot holding this lane's depth
+        for (int s = 0; s < a.nslots; ++s)
+          if (__builtin_amdgcn_readlane(wdl, s) == d) ws = s;
+        if (has && lane < A) {
+          const int x = nx + lane;
+          const int par = key_parent(key);
+          c.rec[x].key = key;
+          c.rec[x].par = par;
+          if (expd) {
+            const int ei = e0 + __popcll(bexp & le) - 1;
+            c.f->ex_rec[ei] = x;
+            c.f->ex_ws[ei] = ws;
+            c.f->ex_dep[ei] = d;
+            c.f->ex_tok[ei] = c.cand[(d - 1) * M + key_m(key)].id;
+            c.f->ex_src[ei] = c.rec[par].slot;
+            c.rec[x].slot = (int)slot_of(a, t + 1, b, ei);
+          } else {
+            c.rec[x].slot = -1;
+          }
+        }
+        if (lane == 0) {
+          if (group && A == 0 && !isout) {  // put the group's best entry back in key order
+            const int g = c.f->misc[C_G] - fh;
+            const uint64_t best = F[0];
+            for (int i = 0; i < g; ++i) F[i] = F[i + 1];
+            F[g] = best;
+          }
+          if (isout) {
+            const uint64_t u = key_u(F[A]);
+            if (!c.f->misc[C_TAUSET] || u > c.f->tau) c.f->tau = u;
+            c.f->misc[C_TAUSET] = 1;
+            c.f->misc[C_NF] = c.f->misc[C_FH] = 0;  // the rest of the frontier is out
+          } else {
+            c.f->misc[C_FH] = fh + A;
+          }
+          const int e1 = e0 + __popcll(bexp & lowA);
+          c.f->misc[C_E] = e1;
+          c.f->misc[C_NX] = nx + A;
+          c.f->misc[C_NL] = nl;
+          c.f->misc[C_STOP] = isout || A < Q || e1 == a.p;
+        }
+      } else {
       if (has) {
         c.f->perm[lane] = lane;
         c.f->acc[lane] = 0;
@@ -1312,6 +1414,7 @@ __device__ __forceinline__ int ctl_pop(const TreeArgs& a, const CtlLds& c, int b
         c.f->misc[C_E] = e1;
         c.f->misc[C_NX] = nx + A;
         c.f->misc[C_STOP] = isout || A < Q || e1 == a.p;
+      }
       }
     }
     __syncthreads();
