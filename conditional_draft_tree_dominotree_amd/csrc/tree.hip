@@ -503,6 +503,44 @@ __device__ __forceinline__ void load8_batch(const void* base, const unsigned (&o
       : "memory");
 }
 
+// Eight 16-byte LDS reads at p + off[q] (immediate byte offsets below), issued
+// back to back and completed together: the MFMA B operands of a group of k
+// blocks.  CPB = 2: k blocks 0..3 of column blocks 0 and 1 (the second column
+// block 16 staged columns = 33024 bytes further); CPB = 1: k blocks 0..7.
+template <int CPB>
+__device__ __forceinline__ void lds_read8_b(const uint16_t* p, bf16x8 (&v)[8]) {
+  const uint32_t a = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)p;
+  static_assert(16 * RSTRIDE * 2 == 33024, "column block stride");
+  if constexpr (CPB == 2)
+    asm volatile(
+        "ds_read_b128 %0, %8\n\t"
+        "ds_read_b128 %1, %8 offset:64\n\t"
+        "ds_read_b128 %2, %8 offset:128\n\t"
+        "ds_read_b128 %3, %8 offset:192\n\t"
+        "ds_read_b128 %4, %8 offset:33024\n\t"
+        "ds_read_b128 %5, %8 offset:33088\n\t"
+        "ds_read_b128 %6, %8 offset:33152\n\t"
+        "ds_read_b128 %7, %8 offset:33216\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3]), "=&v"(v[4]), "=&v"(v[5]), "=&v"(v[6]), "=&v"(v[7])
+        : "v"(a)
+        : "memory");
+  else
+    asm volatile(
+        "ds_read_b128 %0, %8\n\t"
+        "ds_read_b128 %1, %8 offset:64\n\t"
+        "ds_read_b128 %2, %8 offset:128\n\t"
+        "ds_read_b128 %3, %8 offset:192\n\t"
+        "ds_read_b128 %4, %8 offset:256\n\t"
+        "ds_read_b128 %5, %8 offset:320\n\t"
+        "ds_read_b128 %6, %8 offset:384\n\t"
+        "ds_read_b128 %7, %8 offset:448\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3]), "=&v"(v[4]), "=&v"(v[5]), "=&v"(v[6]), "=&v"(v[7])
+        : "v"(a)
+        : "memory");
+}
+
 template <int TW, int CPB>
 __device__ __forceinline__ void worker_regs(const TreeArgs& a, unsigned char* lds) {
   const int w = blockIdx.x;
@@ -565,16 +603,22 @@ __device__ __forceinline__ void worker_regs(const TreeArgs& a, unsigned char* ld
         for (int c = 0; c < CPB; ++c)
 #pragma unroll
           for (int i = 0; i < TW; ++i) acc[c][i][0] = acc[c][i][1] = floatx4{0.f, 0.f, 0.f, 0.f};
+        // groups of 8 / CPB k blocks: their B operands read in one batch
+        constexpr int KG = 8 / CPB;
 #pragma unroll
-        for (int kb = 0; kb < RKB; ++kb) {
-          bf16x8 bv[CPB];
+        for (int g = 0; g < RKB / KG; ++g) {
+          bf16x8 bv[8];  // [c KG + q]: column block c, k block g KG + q
+          lds_read8_b<CPB>(sb + g * KG * 32, bv);
 #pragma unroll
-          for (int c = 0; c < CPB; ++c) bv[c] = *reinterpret_cast<const bf16x8*>(sb + c * 16 * RSTRIDE + kb * 32);
+          for (int q = 0; q < KG; ++q) {
+            const int kb = g * KG + q;
 #pragma unroll
-          for (int c = 0; c < CPB; ++c)
+            for (int c = 0; c < CPB; ++c)
 #pragma unroll
-            for (int i = 0; i < TW; ++i)
-              acc[c][i][kb & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa[i][kb], bv[c], acc[c][i][kb & 1], 0, 0, 0);
+              for (int i = 0; i < TW; ++i)
+                acc[c][i][kb & 1] =
+                    __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa[i][kb], bv[c * KG + q], acc[c][i][kb & 1], 0, 0, 0);
+          }
         }
         // lane holds column col, rows 4 (lane >> 4) + q of each tile
         const int ds3 = 3 * a.ds;
