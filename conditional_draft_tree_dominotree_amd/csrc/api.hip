@@ -66,7 +66,8 @@ struct dt_handle {
   void* act = nullptr;
   float* gh = nullptr;
   float* u = nullptr;
-  uint32_t* mbox_w = nullptr;
+  int32_t* ninfo = nullptr;
+  uint32_t* mbox_w = nullptr;  // group flags, then the worker mailboxes
   uint32_t* mbox_c = nullptr;
   int* err = nullptr;
   int* nanflag = nullptr;
@@ -93,7 +94,7 @@ void free_all(dt_handle* h) {
   void* ptrs[] = {h->G,       h->tiles,    h->b_hh,     h->w1h_t, h->w2t,      h->wlm_t,  h->logits,
                   h->chunk_cand, h->chunk_stat, h->cand_ids, h->cand_vals, h->tokrank, h->lse,
                   h->tail,    h->P,        h->state,    h->act,   h->gh,       h->u,
-                  h->mbox_w,   h->mbox_c,   h->err,   h->nanflag};
+                  h->ninfo,   h->mbox_w,   h->mbox_c,   h->err,   h->nanflag};
   for (void* p : ptrs)
     if (p) (void)hipFree(p);
   for (auto& set : h->ev)
@@ -244,8 +245,9 @@ dt_status dt_create(dt_handle** out, const dt_dims* dims, const dt_weights* w, c
   HIPB(hipMemsetAsync(h->act, 0, h->act_bytes, stream));
   ALLOC(h->gh, nodes * round_up(3 * ds, 32) * sizeof(float));
   ALLOC(h->u, nodes * round_up(r, 32) * sizeof(float));
+  ALLOC(h->ninfo, nodes * 2 * sizeof(int32_t));
   h->max_workers = h->n_cu;
-  ALLOC(h->mbox_w, (size_t)h->max_workers * 32 * sizeof(uint32_t));
+  ALLOC(h->mbox_w, (dt::GFLAG_WORDS + (size_t)h->max_workers * 32) * sizeof(uint32_t));
   ALLOC(h->mbox_c, (size_t)DT_MAX_BATCH * 256 * sizeof(uint32_t));
   ALLOC(h->err, 64);
   ALLOC(h->nanflag, 64);
@@ -344,7 +346,9 @@ dt_status dt_build_trees(dt_handle* h, const dt_inputs* in, const dt_params* p, 
   a.act = h->act;
   a.gh = h->gh;
   a.u = h->u;
-  a.mbox_w = h->mbox_w;
+  a.ninfo = h->ninfo;
+  a.gflag = h->mbox_w;
+  a.mbox_w = h->mbox_w + dt::GFLAG_WORDS;
   a.mbox_c = h->mbox_c;
   a.err = h->err;
   a.tokens = out->tokens;
@@ -361,7 +365,7 @@ dt_status dt_build_trees(dt_handle* h, const dt_inputs* in, const dt_params* p, 
   if (a.n_workers + B > h->n_cu || a.n_workers > h->max_workers)
     return fail(DT_EUNSUPPORTED, "%d workers + %d requests exceed %d compute units", a.n_workers, B, h->n_cu);
   MARK(3);
-  HIPCHK(dt::launch_fill_u32(h->mbox_w, 0u, (size_t)a.n_workers * 32, stream));
+  HIPCHK(dt::launch_fill_u32(h->mbox_w, 0u, dt::GFLAG_WORDS + (size_t)a.n_workers * 32, stream));
   HIPCHK(dt::launch_fill_u32(h->mbox_c, 0u, (size_t)B * 256, stream));
   MARK(4);
   HIPCHK(dt::launch_tree(a, h->bf16, lds, stream));

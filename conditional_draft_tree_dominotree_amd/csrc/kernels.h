@@ -58,6 +58,7 @@ struct TreeArgs {
   int regw;             // 0: workers stage operands in LDS; register workers: 1 (1 tile per wave, 1
                         // column block per block), 2 (2 tiles, 1 block), 3 (2 tiles, 2 blocks)
   int ncbmax;           // register workers: 16-column blocks per step
+  int wadv;             // 1: the workers advance the GRU states of a step's nodes (register workers)
   int xcap;             // node records per request (budget + root + speculation room)
   int fcap;             // frontier entries per request
   int qmax;             // frontier entries tested per pop round
@@ -78,6 +79,8 @@ struct TreeArgs {
   void* act;               // [slots, ds] its GEMM operand copy (wdtype)
   float* gh;               // [slots, 3 ds]
   float* u;                // [slots, r]
+  int32_t* ninfo;          // [steps][TREE_MAX_COLS][2]: token and parent slot of each node to advance
+  uint32_t* gflag;         // [16][64] worker group flags (states of a step advanced)
   uint32_t* mbox_w;        // [n_workers][32] controller -> worker mailboxes (one line each)
   uint32_t* mbox_c;        // [B][256] worker -> controller mailboxes
   int* err;                // device error word
@@ -88,6 +91,7 @@ struct TreeArgs {
 };
 // Exchange columns a build may use per step (slots per step = B p <= this).
 constexpr int TREE_MAX_COLS = 256;
+constexpr int GFLAG_WORDS = 16 * 64;  // worker group flags, placed before the worker mailboxes
 // Fills the schedule fields of `a` (p from `pops`, 0 = automatic) and returns
 // the dynamic LDS bytes the launch needs, or 0 if the shape cannot be served.
 // With register workers (allowed unless `lds_workers`) it also sets

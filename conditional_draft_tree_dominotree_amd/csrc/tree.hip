@@ -132,6 +132,13 @@ __device__ __forceinline__ float w_to_f32<uint16_t>(uint16_t v) { return bf16_to
 template <>
 __device__ __forceinline__ float w_to_f32<float>(float v) { return v; }
 
+// Logistic function and tanh from the hardware exp2 and reciprocal (about
+// 1e-7 relative error; a tanh near 0 is accurate to about 1e-7 absolute).
+__device__ __forceinline__ float sigm(float x) {
+  return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.4426950408889634f * x));
+}
+__device__ __forceinline__ float tanh_(float x) { return 2.0f * sigm(2.0f * x) - 1.0f; }
+
 // ---------------------------------------------------------------------------
 // layout helpers
 
@@ -541,6 +548,66 @@ __device__ __forceinline__ void lds_read8_b(const uint16_t* p, bf16x8 (&v)[8]) {
         : "memory");
 }
 
+// Advance the GRU states of columns [c0, c0 + nc) of step t (d_s = 1024,
+// bf16 operand copies): S_y = GRU(S_x, E[tok]) with W_ih E[tok] + b_ih =
+// G[tok] and gh_x published by the workers at the parent's step.  The
+// group's nq blocks share the float4 items: block q takes items q NT + i +
+// k nq NT.  Token and parent slot come from the controller's node table.
+__device__ __forceinline__ void worker_advance(const TreeArgs& a, const int* coln, int t, int c0, int nc, int q,
+                                               int nq) {
+  constexpr int WG = 2;  // items per thread in flight
+  const int ds = a.ds, n4 = ds >> 2;
+  const int items = nc * n4;
+  const int slot0 = (int)slot_of(a, t, 0, 0);
+  const int32_t* info = a.ninfo + (size_t)t * TREE_MAX_COLS * 2;
+  for (int base = q * NT; base < items; base += nq * NT * WG) {
+    int tok[WG], src[WG], sl[WG], qv[WG];
+#pragma unroll
+    for (int g = 0; g < WG; ++g) {  // clamped: every lane reads valid entries
+      const int item = min(base + g * nq * NT + (int)threadIdx.x, items - 1);
+      const int cc = item / n4;
+      qv[g] = (item - cc * n4) * 4;
+      sl[g] = coln[c0 + cc];
+      const int2 in = *reinterpret_cast<const int2*>(info + (size_t)(sl[g] - slot0) * 2);
+      tok[g] = in.x;
+      src[g] = in.y;
+    }
+    float4 ir[WG], iz[WG], in_[WG], hr[WG], hz[WG], hn[WG], sp[WG];
+#pragma unroll
+    for (int g = 0; g < WG; ++g) {
+      const float* gi = a.G + (size_t)tok[g] * 3 * ds + qv[g];
+      const float* gh = a.gh + (size_t)src[g] * gh_stride(ds) + qv[g];
+      ir[g] = *reinterpret_cast<const float4*>(gi);
+      iz[g] = *reinterpret_cast<const float4*>(gi + ds);
+      in_[g] = *reinterpret_cast<const float4*>(gi + 2 * ds);
+      hr[g] = *reinterpret_cast<const float4*>(gh);
+      hz[g] = *reinterpret_cast<const float4*>(gh + ds);
+      hn[g] = *reinterpret_cast<const float4*>(gh + 2 * ds);
+      sp[g] = *reinterpret_cast<const float4*>(a.state + (size_t)src[g] * st_stride(ds) + qv[g]);
+    }
+    keep_batch();
+#pragma unroll
+    for (int g = 0; g < WG; ++g) {
+      if (base + g * nq * NT + (int)threadIdx.x < items) {
+        const float a0[4] = {ir[g].x, ir[g].y, ir[g].z, ir[g].w}, b0[4] = {hr[g].x, hr[g].y, hr[g].z, hr[g].w};
+        const float a1[4] = {iz[g].x, iz[g].y, iz[g].z, iz[g].w}, b1[4] = {hz[g].x, hz[g].y, hz[g].z, hz[g].w};
+        const float a2[4] = {in_[g].x, in_[g].y, in_[g].z, in_[g].w}, b2[4] = {hn[g].x, hn[g].y, hn[g].z, hn[g].w};
+        const float s0[4] = {sp[g].x, sp[g].y, sp[g].z, sp[g].w};
+        floatx4 o;
+#pragma unroll
+        for (int qq = 0; qq < 4; ++qq) {
+          const float rg = sigm(a0[qq] + b0[qq]);
+          const float zg = sigm(a1[qq] + b1[qq]);
+          const float ng = tanh_(a2[qq] + rg * b2[qq]);
+          o[qq] = (1.0f - zg) * ng + zg * s0[qq];
+        }
+        st_dev_f32x4(a.state + (size_t)sl[g] * st_stride(ds) + qv[g], o);
+        st_dev_act4<uint16_t>(reinterpret_cast<uint16_t*>(a.act) + (size_t)sl[g] * act_stride(ds) + qv[g], o, 1);
+      }
+    }
+  }
+}
+
 template <int TW, int CPB>
 __device__ __forceinline__ void worker_regs(const TreeArgs& a, unsigned char* lds) {
   const int w = blockIdx.x;
@@ -555,6 +622,7 @@ __device__ __forceinline__ void worker_regs(const TreeArgs& a, unsigned char* ld
   const int nb = (a.ncbmax + CPB - 1) / CPB;
   const int col0 = (w % nb) * CPB * 16;  // first column of the block
   const int tile0 = ((w / nb) * 4 + wv) * TW;
+  const int grp = w % nb, gq = w / nb, ngq = a.n_workers / nb;  // the blocks sharing these columns
 
   // this wave's A operands: tile rows (lane & 15), k 8 (lane >> 4) + 32 kb
   bf16x8 wa[TW][RKB];
@@ -573,6 +641,19 @@ __device__ __forceinline__ void worker_regs(const TreeArgs& a, unsigned char* ld
     const int ncols = misc[0], nreq = misc[1];
     if (ncols <= 0) return;  // a wait ran out, or every request is finished
     if (col0 < ncols) {
+      if (a.wadv && t > 0) {
+        // the group advances the states of its columns, then waits for all of it
+        worker_advance(a, coln, t, col0, min(16 * CPB, ncols - col0), gq, ngq);
+        stores_done();
+        __syncthreads();
+        if (tid == 0) st_dev_u32(a.gflag + grp * 64 + gq, epoch);
+        if (tid < 64) {
+          const bool ok = wait_mbox(a.gflag + grp * 64, ngq, epoch, a.err, a.spin_limit);
+          if (lane == 0) misc[2] = ok;
+        }
+        __syncthreads();
+        if (!misc[2]) return;
+      }
       // stage: thread piece tid + 256 q = column (tid >> 7) + 2 q, 16-byte piece tid & 127
       const int slot0 = (int)slot_of(a, t, 0, 0);
       const int pc = tid & 127;
@@ -775,13 +856,6 @@ __device__ __forceinline__ CtlLds ctl_carve(unsigned char* lds, const TreeArgs& 
 __device__ __forceinline__ uint64_t* cur_front(const TreeArgs& a, const CtlLds& c) {
   return c.front + (size_t)c.f->misc[C_FB] * a.fcap;
 }
-
-// Logistic function and tanh from the hardware exp2 and reciprocal (about
-// 1e-7 relative error; a tanh near 0 is accurate to about 1e-7 absolute).
-__device__ __forceinline__ float sigm(float x) {
-  return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.4426950408889634f * x));
-}
-__device__ __forceinline__ float tanh_(float x) { return 2.0f * sigm(2.0f * x) - 1.0f; }
 
 // Total order between two records of equal depth whose keys tie on
 // (score, depth, token): the parents' order decides, recursively.
@@ -1650,7 +1724,20 @@ __device__ __forceinline__ void controller_main(const TreeArgs& a, unsigned char
       failed = true;
       break;
     }
-    ctl_advance<W>(a, c, b, t + 1, e2);
+    if (a.wadv) {
+      // the workers advance the states: token and parent slot of each node
+      if (tid < e2) {
+        int xs = c.f->ex_src[tid];
+        if (xs < 0) {  // every parent was expanded; the guard keeps addresses valid
+          atomicOr(a.err, 8);
+          xs = 0;
+        }
+        const size_t sl = slot_of(a, t + 1, b, tid) - slot_of(a, t + 1, 0, 0);
+        st_dev_u32x2(a.ninfo + ((size_t)(t + 1) * TREE_MAX_COLS + sl) * 2, (uint32_t)c.f->ex_tok[tid], (uint32_t)xs);
+      }
+    } else {
+      ctl_advance<W>(a, c, b, t + 1, e2);
+    }
     stores_done();
     __syncthreads();
     for (int w = tid; w < a.n_workers; w += NT)
@@ -1699,12 +1786,13 @@ size_t plan_tree(TreeArgs& a, int wdtype_bf16, int pops, int max_workers, int ld
     const int ncb = (cols + 15) / 16;
     // register workers: one tile per wave if that many blocks fit, else two
     int regw = 0, n_workers = lds_n_workers;
-    if (wdtype_bf16 && kp == RKB * 32 && !lds_workers) {
+    if (wdtype_bf16 && a.ds == RKB * 32 && !lds_workers) {
       // (tiles per wave, column blocks per block): 1 = (1, 1), 2 = (2, 1), 3 = (2, 2)
       for (int m = 1; m <= 3 && !regw; ++m) {
         const int tw = m == 1 ? 1 : 2, cpb = m == 3 ? 2 : 1;
-        const int nw = ((a.n_tiles + tw - 1) / tw + 3) / 4 * ((ncb + cpb - 1) / cpb);
-        if (nw <= max_workers) regw = m, n_workers = nw;
+        const int ngq = ((a.n_tiles + tw - 1) / tw + 3) / 4;  // blocks per column group (64 flags each)
+        const int nw = ngq * ((ncb + cpb - 1) / cpb);
+        if (nw <= max_workers && ngq <= 64) regw = m, n_workers = nw;
       }
     }
     int kc = kp;
@@ -1732,6 +1820,7 @@ size_t plan_tree(TreeArgs& a, int wdtype_bf16, int pops, int max_workers, int ld
     a.kc = kc;
     a.regw = regw;
     a.ncbmax = ncb;
+    a.wadv = regw ? 1 : 0;
     a.n_workers = n_workers;
     a.qmax = qmax;
     a.xcap = xcap;
