@@ -56,7 +56,8 @@ struct TreeArgs {
   int p;                // nodes a request may expand per step (exchange columns per request)
   int kc;               // state elements a worker stages per phase (kp / kc phases)
   int regw;             // 0: workers stage operands in LDS; register workers: 1 (1 tile per wave, 1
-                        // column block per block), 2 (2 tiles, 1 block), 3 (2 tiles, 2 blocks)
+                        // column block per block), 2 (2 tiles, 1 block), 3 (2 tiles, 2 blocks),
+                        // 4 (2 tiles, 4 blocks)
   int ncbmax;           // register workers: 16-column blocks per step
   int wadv;             // 1: the workers advance the GRU states of a step's nodes (register workers)
   int xcap;             // node records per request (budget + root + speculation room)
@@ -90,7 +91,7 @@ struct TreeArgs {
   unsigned spin_limit;
 };
 // Exchange columns a build may use per step (slots per step = B p <= this).
-constexpr int TREE_MAX_COLS = 256;
+constexpr int TREE_MAX_COLS = 512;
 constexpr int GFLAG_WORDS = 16 * 64;  // worker group flags, placed before the worker mailboxes
 // Fills the schedule fields of `a` (p from `pops`, 0 = automatic) and returns
 // the dynamic LDS bytes the launch needs, or 0 if the shape cannot be served.

@@ -512,13 +512,29 @@ __device__ __forceinline__ void load8_batch(const void* base, const unsigned (&o
 
 // Eight 16-byte LDS reads at p + off[q] (immediate byte offsets below), issued
 // back to back and completed together: the MFMA B operands of a group of k
-// blocks.  CPB = 2: k blocks 0..3 of column blocks 0 and 1 (the second column
-// block 16 staged columns = 33024 bytes further); CPB = 1: k blocks 0..7.
+// blocks.  CPB = 4: k blocks 0, 1 of column blocks 0..3 (a column block is 16
+// staged columns = 33024 bytes; offsets stop at 65535, so blocks 2, 3 use a
+// second base); CPB = 2: k blocks 0..3 of column blocks 0, 1; CPB = 1: k
+// blocks 0..7.
 template <int CPB>
 __device__ __forceinline__ void lds_read8_b(const uint16_t* p, bf16x8 (&v)[8]) {
   const uint32_t a = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)p;
   static_assert(16 * RSTRIDE * 2 == 33024, "column block stride");
-  if constexpr (CPB == 2)
+  if constexpr (CPB == 4)
+    asm volatile(
+        "ds_read_b128 %0, %8\n\t"
+        "ds_read_b128 %1, %8 offset:64\n\t"
+        "ds_read_b128 %2, %8 offset:33024\n\t"
+        "ds_read_b128 %3, %8 offset:33088\n\t"
+        "ds_read_b128 %4, %9\n\t"
+        "ds_read_b128 %5, %9 offset:64\n\t"
+        "ds_read_b128 %6, %9 offset:33024\n\t"
+        "ds_read_b128 %7, %9 offset:33088\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3]), "=&v"(v[4]), "=&v"(v[5]), "=&v"(v[6]), "=&v"(v[7])
+        : "v"(a), "v"(a + 2u * 33024u)
+        : "memory");
+  else if constexpr (CPB == 2)
     asm volatile(
         "ds_read_b128 %0, %8\n\t"
         "ds_read_b128 %1, %8 offset:64\n\t"
@@ -555,7 +571,7 @@ __device__ __forceinline__ void lds_read8_b(const uint16_t* p, bf16x8 (&v)[8]) {
 // k nq NT.  Token and parent slot come from the controller's node table.
 __device__ __forceinline__ void worker_advance(const TreeArgs& a, const int* coln, int t, int c0, int nc, int q,
                                                int nq) {
-  constexpr int WG = 2;  // items per thread in flight
+  constexpr int WG = 3;  // items per thread in flight
   const int ds = a.ds, n4 = ds >> 2;
   const int items = nc * n4;
   const int slot0 = (int)slot_of(a, t, 0, 0);
@@ -658,32 +674,37 @@ __device__ __forceinline__ void worker_regs(const TreeArgs& a, unsigned char* ld
       const int slot0 = (int)slot_of(a, t, 0, 0);
       const int pc = tid & 127;
       const uint16_t* base = reinterpret_cast<const uint16_t*>(a.act) + (size_t)slot0 * as;
-      unsigned off[8 * CPB];
+      // batches of up to 16 loads (32 columns), each completed before the next
 #pragma unroll
-      for (int q = 0; q < 8 * CPB; ++q) {
-        const int c = min(col0 + (tid >> 7) + 2 * q, ncols - 1);  // clamped: always a valid column
-        off[q] = (unsigned)(((coln[c] - slot0) * as + pc * 8) * 2);
-      }
-      if constexpr (CPB == 1) {
-        u32x4 v[8];
-        load8_batch(base, off, v);
+      for (int h = 0; h < (CPB + 1) / 2; ++h) {
+        constexpr int NB = CPB == 1 ? 8 : 16;
+        unsigned off[NB];
 #pragma unroll
-        for (int q = 0; q < 8; ++q) *reinterpret_cast<u32x4*>(stage + ((tid >> 7) + 2 * q) * RSTRIDE + pc * 8) = v[q];
-      } else {
-        u32x4 v[16];
-        load16_batch(base, off, v);
+        for (int q = 0; q < NB; ++q) {
+          const int c = min(col0 + (tid >> 7) + 2 * (NB * h + q), ncols - 1);  // clamped: always a valid column
+          off[q] = (unsigned)(((coln[c] - slot0) * as + pc * 8) * 2);
+        }
+        u32x4 v[NB];
+        if constexpr (NB == 8) load8_batch(base, off, v);
+        else load16_batch(base, off, v);
 #pragma unroll
-        for (int q = 0; q < 16; ++q) *reinterpret_cast<u32x4*>(stage + ((tid >> 7) + 2 * q) * RSTRIDE + pc * 8) = v[q];
+        for (int q = 0; q < NB; ++q)
+          *reinterpret_cast<u32x4*>(stage + ((tid >> 7) + 2 * (NB * h + q)) * RSTRIDE + pc * 8) = v[q];
       }
       __syncthreads();
       if (tile0 < a.n_tiles) {
         // B operands: column (lane & 15) of each column block, k 8 (lane >> 4) + 32 kb
         const uint16_t* sb = stage + (lane & 15) * RSTRIDE + 8 * (lane >> 4);
-        floatx4 acc[CPB][TW][2];
+        // independent accumulation chains: two per (column block, tile) unless
+        // the column blocks give enough
+        constexpr int NACC = CPB >= 4 ? 1 : 2;
+        floatx4 acc[CPB][TW][NACC];
 #pragma unroll
         for (int c = 0; c < CPB; ++c)
 #pragma unroll
-          for (int i = 0; i < TW; ++i) acc[c][i][0] = acc[c][i][1] = floatx4{0.f, 0.f, 0.f, 0.f};
+          for (int i = 0; i < TW; ++i)
+#pragma unroll
+            for (int n = 0; n < NACC; ++n) acc[c][i][n] = floatx4{0.f, 0.f, 0.f, 0.f};
         // groups of 8 / CPB k blocks: their B operands read in one batch
         constexpr int KG = 8 / CPB;
 #pragma unroll
@@ -697,8 +718,8 @@ __device__ __forceinline__ void worker_regs(const TreeArgs& a, unsigned char* ld
             for (int c = 0; c < CPB; ++c)
 #pragma unroll
               for (int i = 0; i < TW; ++i)
-                acc[c][i][kb & 1] =
-                    __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa[i][kb], bv[c * KG + q], acc[c][i][kb & 1], 0, 0, 0);
+                acc[c][i][kb % NACC] =
+                    __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa[i][kb], bv[c * KG + q], acc[c][i][kb % NACC], 0, 0, 0);
           }
         }
         // lane holds column col, rows 4 (lane >> 4) + q of each tile
@@ -711,7 +732,8 @@ __device__ __forceinline__ void worker_regs(const TreeArgs& a, unsigned char* ld
 #pragma unroll
           for (int i = 0; i < TW; ++i) {
             if (tile0 + i >= a.n_tiles) continue;
-            const floatx4 sum = acc[c][i][0] + acc[c][i][1];
+            floatx4 sum = acc[c][i][0];
+            if constexpr (NACC == 2) sum = acc[c][i][0] + acc[c][i][1];
             const int row0 = (tile0 + i) * 16 + 4 * (lane >> 4);
             if (row0 + 3 < ds3 && (ds3 & 3) == 0) {
               floatx4 o = sum;
@@ -818,9 +840,9 @@ __host__ __device__ inline size_t ctl_offsets(const TreeArgs& a, int esz, size_t
   sz[L_RRANK] = X * 4;
   sz[L_TREC] = X * sizeof(Rec);
   sz[L_FRONT] = (size_t)2 * a.fcap * 8;
-  sz[L_NC] = pk * 8;
+  sz[L_NC] = (pk + 31) / 32 * 32 * 8;  // read in blocks of 32 keys
   sz[L_NCS] = pk * 8;
-  sz[L_PN] = pk * 4;
+  sz[L_PN] = 0;
   sz[L_W2S] = (size_t)a.nslots * a.M * w2s_stride(a.r, esz) * esz;
   sz[L_PS] = (size_t)a.nslots * a.r * 4;
   sz[L_AV] = P * a.r * 4;
@@ -943,6 +965,64 @@ __device__ __forceinline__ void ctl_prefetch(const TreeArgs& a, const CtlLds& c,
 // Score the children of the e nodes expanded at step t and write the keys of
 // each node's k best into nc[j k .. j k + k) (0 where a child has no finite
 // log-prob).
+// One lane's operands of two k steps of the correction products: 16 bytes at
+// w[c] and w[c] + 64 for four W2 rows, and 16 bytes at a + 0, 16, 128, 144 of
+// the node's activations, read from LDS in one batch completed together.
+__device__ __forceinline__ void lds_read_dl(const uint16_t* const (&w)[4], const float* av, u32x4 (&wv)[8],
+                                            float4 (&xv)[4]) {
+  uint32_t wa[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) wa[i] = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)w[i];
+  const uint32_t aa = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)av;
+  asm volatile(
+      "ds_read_b128 %0, %12\n\t"
+      "ds_read_b128 %1, %13\n\t"
+      "ds_read_b128 %2, %14\n\t"
+      "ds_read_b128 %3, %15\n\t"
+      "ds_read_b128 %4, %12 offset:64\n\t"
+      "ds_read_b128 %5, %13 offset:64\n\t"
+      "ds_read_b128 %6, %14 offset:64\n\t"
+      "ds_read_b128 %7, %15 offset:64\n\t"
+      "ds_read_b128 %8, %16\n\t"
+      "ds_read_b128 %9, %16 offset:16\n\t"
+      "ds_read_b128 %10, %16 offset:128\n\t"
+      "ds_read_b128 %11, %16 offset:144\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(wv[0]), "=&v"(wv[1]), "=&v"(wv[2]), "=&v"(wv[3]), "=&v"(wv[4]), "=&v"(wv[5]), "=&v"(wv[6]),
+        "=&v"(wv[7]), "=&v"(xv[0]), "=&v"(xv[1]), "=&v"(xv[2]), "=&v"(xv[3])
+      : "v"(wa[0]), "v"(wa[1]), "v"(wa[2]), "v"(wa[3]), "v"(aa)
+      : "memory");
+}
+
+// The 32 keys (256 bytes) at p, read from LDS in one batch of sixteen 16-byte
+// reads completed together.
+__device__ __forceinline__ void lds_read_keys32(const uint64_t* p, u32x4 (&v)[16]) {
+  const uint32_t a = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)p;
+  asm volatile(
+      "ds_read_b128 %0, %16\n\t"
+      "ds_read_b128 %1, %16 offset:16\n\t"
+      "ds_read_b128 %2, %16 offset:32\n\t"
+      "ds_read_b128 %3, %16 offset:48\n\t"
+      "ds_read_b128 %4, %16 offset:64\n\t"
+      "ds_read_b128 %5, %16 offset:80\n\t"
+      "ds_read_b128 %6, %16 offset:96\n\t"
+      "ds_read_b128 %7, %16 offset:112\n\t"
+      "ds_read_b128 %8, %16 offset:128\n\t"
+      "ds_read_b128 %9, %16 offset:144\n\t"
+      "ds_read_b128 %10, %16 offset:160\n\t"
+      "ds_read_b128 %11, %16 offset:176\n\t"
+      "ds_read_b128 %12, %16 offset:192\n\t"
+      "ds_read_b128 %13, %16 offset:208\n\t"
+      "ds_read_b128 %14, %16 offset:224\n\t"
+      "ds_read_b128 %15, %16 offset:240\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3]), "=&v"(v[4]), "=&v"(v[5]), "=&v"(v[6]), "=&v"(v[7]),
+        "=&v"(v[8]), "=&v"(v[9]), "=&v"(v[10]), "=&v"(v[11]), "=&v"(v[12]), "=&v"(v[13]), "=&v"(v[14]),
+        "=&v"(v[15])
+      : "v"(a)
+      : "memory");
+}
+
 template <typename W>
 __device__ __forceinline__ void ctl_expand(const TreeArgs& a, const CtlLds& c, int b, int t, int e) {
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
@@ -970,7 +1050,7 @@ __device__ __forceinline__ void ctl_expand(const TreeArgs& a, const CtlLds& c, i
   // 4 candidates), thread h of the quad taking elements 32 i + 8 h .. + 7 of
   // all four rows (each a_j read serves four rows; a quad reads 64 consecutive
   // bytes of a row), combined in a fixed order.
-  if (sizeof(W) == 2 && (M & 3) == 0 && (r & 31) == 0) {
+  if (sizeof(W) == 2 && (M & 3) == 0 && (r & 63) == 0) {
     const int G4 = M >> 2;
     const int rs = w2s_stride(r, 2);
     for (int base = 0; base < e * G4 * 4; base += NT) {
@@ -981,18 +1061,23 @@ __device__ __forceinline__ void ctl_expand(const TreeArgs& a, const CtlLds& c, i
       const float* avj = c.av + jr * r + 8 * h;
       const uint16_t* w0 = reinterpret_cast<const uint16_t*>(c.w2s) + (size_t)(c.f->ex_ws[jr] * M + 4 * g) * rs + 8 * h;
       float acc[4] = {0.f, 0.f, 0.f, 0.f};
-      for (int q0 = 0; q0 < r; q0 += 32) {
-        const float4 x0 = *reinterpret_cast<const float4*>(avj + q0);
-        const float4 x1 = *reinterpret_cast<const float4*>(avj + q0 + 4);
-        const float xa[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+      for (int q0 = 0; q0 < r; q0 += 64) {  // two k steps of 32 per LDS batch
+        const uint16_t* const wr[4] = {w0 + q0, w0 + rs + q0, w0 + 2 * rs + q0, w0 + 3 * rs + q0};
+        u32x4 wv[8];
+        float4 xv[4];
+        lds_read_dl(wr, avj + q0, wv, xv);
 #pragma unroll
-        for (int cc = 0; cc < 4; ++cc) {
-          const uint4 wv4 = *reinterpret_cast<const uint4*>(w0 + cc * rs + q0);
-          const uint32_t wd[4] = {wv4.x, wv4.y, wv4.z, wv4.w};
+        for (int st = 0; st < 2; ++st) {
+          const float xa[8] = {xv[2 * st].x, xv[2 * st].y, xv[2 * st].z, xv[2 * st].w,
+                               xv[2 * st + 1].x, xv[2 * st + 1].y, xv[2 * st + 1].z, xv[2 * st + 1].w};
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            acc[cc] = fmaf(__uint_as_float(wd[q] << 16), xa[2 * q], acc[cc]);
-            acc[cc] = fmaf(__uint_as_float(wd[q] & 0xFFFF0000u), xa[2 * q + 1], acc[cc]);
+          for (int cc = 0; cc < 4; ++cc) {
+            const uint32_t wd[4] = {wv[4 * st + cc].x, wv[4 * st + cc].y, wv[4 * st + cc].z, wv[4 * st + cc].w};
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              acc[cc] = fmaf(__uint_as_float(wd[q] << 16), xa[2 * q], acc[cc]);
+              acc[cc] = fmaf(__uint_as_float(wd[q] & 0xFFFF0000u), xa[2 * q + 1], acc[cc]);
+            }
           }
         }
       }
@@ -1054,38 +1139,72 @@ __device__ __forceinline__ void ctl_expand(const TreeArgs& a, const CtlLds& c, i
   // (z desc, token asc), keep the k best with a finite log-prob.  -inf
   // log-probs rank after every finite one.
   if (M <= 32) {
+    // half-wave h of wave w takes nodes 2 w + h and 2 w + h + 8 (e <= 16),
+    // both at once so that their latency chains overlap
     const int half = lane >> 5, l32 = lane & 31;
-    for (int j0 = 2 * wv; j0 < e; j0 += 8) {
-      const int j = j0 + half;
-      const bool node = j < e;
-      const int jr = node ? j : j0;  // a valid node for the reads
-      const int y = c.f->ex_rec[jr];
-      const int dy = c.f->ex_dep[jr];
-      const float yscore = key_score(c.rec[y].key);
-      const bool has = node && l32 < M;
-      const float zv = has ? c.f->z[jr * 64 + l32] : -INFINITY;
-      const int idv = has ? c.cand[dy * M + l32].id : 0x7FFFFFFF;
-      const float tl = a.fullv ? c.tailv[dy] : -INFINITY;
-      const float mx = fmaxf(half_max_dpp(zv), tl);
-      const bool live = mx > -INFINITY;
-      float se = half_sum_dpp(has && live ? expf(zv - mx) : 0.f);
-      if (tl > -INFINITY) se += expf(tl - mx);
-      const float lz = live ? mx + logf(se) : -INFINITY;
-      const float lp = zv - lz;
-      const uint64_t me = has ? cand_pack(f32_key(zv), (uint32_t)idv) : 0ull;
-      const uint32_t mlo = (uint32_t)me, mhi = (uint32_t)(me >> 32);
-      int rank = 0;
-      for (int q = 0; q < M; ++q) {
-        const uint32_t h0 = (uint32_t)__builtin_amdgcn_readlane((int)mhi, q);
-        const uint32_t l0 = (uint32_t)__builtin_amdgcn_readlane((int)mlo, q);
-        const uint32_t h1 = (uint32_t)__builtin_amdgcn_readlane((int)mhi, q + 32);
-        const uint32_t l1 = (uint32_t)__builtin_amdgcn_readlane((int)mlo, q + 32);
-        const uint64_t o = half ? ((uint64_t)h1 << 32 | l1) : ((uint64_t)h0 << 32 | l0);
-        rank += o > me;
+    const int hw = 2 * wv + half;
+    if (2 * wv < e) {
+      constexpr float L2E = 1.4426950408889634f, LN2 = 0.6931471805599453f;
+      int jr[2], y[2], dy[2];
+      bool node[2], has[2];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int j = hw + 8 * u;
+        node[u] = j < e;
+        jr[u] = node[u] ? j : 2 * wv;  // a valid node of this wave for the reads
+        has[u] = node[u] && l32 < M;
+        y[u] = c.f->ex_rec[jr[u]];
+        dy[u] = c.f->ex_dep[jr[u]];
       }
-      const bool ok = has && isfinite(lp);
-      if (has && rank < k)
-        c.nc[j * k + rank] = ok ? make_key(yscore + lp, dy + 1, c.cand[dy * M + l32].rank, y, l32) : 0ull;
+      float yscore[2], zv[2], tl[2];
+      int idv[2], crk[2];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        yscore[u] = key_score(c.rec[y[u]].key);
+        zv[u] = has[u] ? c.f->z[jr[u] * 64 + l32] : -INFINITY;
+        const Cand cd = c.cand[dy[u] * M + (has[u] ? l32 : 0)];
+        idv[u] = has[u] ? cd.id : 0x7FFFFFFF;
+        crk[u] = cd.rank;
+        tl[u] = a.fullv ? c.tailv[dy[u]] : -INFINITY;
+      }
+      float lz[2];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const float mx = fmaxf(half_max_dpp(zv[u]), tl[u]);
+        const bool live = mx > -INFINITY;
+        float se = half_sum_dpp(has[u] && live ? __builtin_amdgcn_exp2f((zv[u] - mx) * L2E) : 0.f);
+        if (tl[u] > -INFINITY) se += __builtin_amdgcn_exp2f((tl[u] - mx) * L2E);
+        lz[u] = live ? mx + __builtin_amdgcn_logf(se) * LN2 : -INFINITY;
+      }
+      // ranks among each node's candidates: the composites go to the node's
+      // own z row (read above), then every lane reads them back as broadcasts
+      uint64_t me[2];
+      uint64_t* kz[2];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        me[u] = has[u] ? cand_pack(f32_key(zv[u]), (uint32_t)idv[u]) : 0ull;
+        kz[u] = reinterpret_cast<uint64_t*>(c.f->z + jr[u] * 64);
+        if (node[u]) kz[u][l32] = me[u];
+      }
+      int rank[2] = {0, 0};
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        u32x4 kv[16];
+        lds_read_keys32(kz[u], kv);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const uint64_t k0 = ((uint64_t)kv[i].y << 32) | kv[i].x, k1 = ((uint64_t)kv[i].w << 32) | kv[i].z;
+          rank[u] += k0 > me[u];  // slots past M hold 0, which precedes nothing
+          rank[u] += k1 > me[u];
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const float lp = zv[u] - lz[u];
+        const bool ok = has[u] && isfinite(lp);
+        if (has[u] && rank[u] < k)
+          c.nc[(hw + 8 * u) * k + rank[u]] = ok ? make_key(yscore[u] + lp, dy[u] + 1, crk[u], y[u], l32) : 0ull;
+      }
     }
   } else
   for (int j = wv; j < e; j += 4) {
@@ -1118,6 +1237,8 @@ __device__ __forceinline__ void ctl_expand(const TreeArgs& a, const CtlLds& c, i
     if (has && rank < k)
       c.nc[j * k + rank] = ok ? make_key(yscore + lp, dy + 1, c.cand[dy * M + lane].rank, y, lane) : 0ull;
   }
+  // zero the new keys past e k up to a multiple of 32 (the merge reads blocks of 32)
+  for (int i = e * k + tid; i < (e * k + 31) / 32 * 32; i += NT) c.nc[i] = 0ull;
   if (tid == 0) c.f->misc[C_NV] = 0;
   __syncthreads();
 }
@@ -1145,8 +1266,21 @@ __device__ __forceinline__ void ctl_merge(const TreeArgs& a, const CtlLds& c, in
     for (int base = 0; base < (nnew << ls); base += NT) {
       const int idx = base + tid, i = idx >> ls, s = idx & (S - 1);
       const uint64_t key = i < nnew ? c.nc[i] : 0ull;
-      int rn = 0;  // new entries ahead (any key above a live one is live)
-      for (int q = s; q < nnew; q += S) rn += c.nc[q] > key;
+      // new entries ahead (any key above a live one is live): thread s of the
+      // group counts a contiguous share, 32 keys per LDS batch
+      const int CH = ((nnew + S - 1) / S + 31) & ~31;
+      const int qe = min(nnew, (s + 1) * CH);
+      int rn = 0;
+      for (int q0 = s * CH; q0 < qe; q0 += 32) {
+        u32x4 kv[16];
+        lds_read_keys32(c.nc + q0, kv);
+#pragma unroll
+        for (int i2 = 0; i2 < 16; ++i2) {
+          const uint64_t k0 = ((uint64_t)kv[i2].y << 32) | kv[i2].x, k1 = ((uint64_t)kv[i2].w << 32) | kv[i2].z;
+          rn += k0 > key;  // keys past nnew are 0, which precedes nothing
+          rn += k1 > key;
+        }
+      }
       if (ls >= 1) rn += __builtin_amdgcn_update_dpp(0, rn, 0xB1, 0xF, 0xF, false);  // lane ^ 1
       if (ls >= 2) rn += __builtin_amdgcn_update_dpp(0, rn, 0x4E, 0xF, 0xF, false);  // lane ^ 2
       const bool live = i < nnew && s == 0 && key != 0 && (!tauset || key_u(key) >= tau);
@@ -1762,6 +1896,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       if (a.regw == 1) return worker_regs<1, 1>(a, lds);
       if (a.regw == 2) return worker_regs<2, 1>(a, lds);
       if (a.regw == 3) return worker_regs<2, 2>(a, lds);
+      if (a.regw == 4) return worker_regs<2, 4>(a, lds);
     }
     worker_main<W>(a, lds);
   } else {
@@ -1787,16 +1922,16 @@ size_t plan_tree(TreeArgs& a, int wdtype_bf16, int pops, int max_workers, int ld
     // register workers: one tile per wave if that many blocks fit, else two
     int regw = 0, n_workers = lds_n_workers;
     if (wdtype_bf16 && a.ds == RKB * 32 && !lds_workers) {
-      // (tiles per wave, column blocks per block): 1 = (1, 1), 2 = (2, 1), 3 = (2, 2)
-      for (int m = 1; m <= 3 && !regw; ++m) {
-        const int tw = m == 1 ? 1 : 2, cpb = m == 3 ? 2 : 1;
+      // (tiles per wave, column blocks per block): 1 = (1, 1), 2 = (2, 1), 3 = (2, 2), 4 = (2, 4)
+      for (int m = 1; m <= 4 && !regw; ++m) {
+        const int tw = m == 1 ? 1 : 2, cpb = m == 4 ? 4 : m == 3 ? 2 : 1;
         const int ngq = ((a.n_tiles + tw - 1) / tw + 3) / 4;  // blocks per column group (64 flags each)
         const int nw = ngq * ((ncb + cpb - 1) / cpb);
         if (nw <= max_workers && ngq <= 64) regw = m, n_workers = nw;
       }
     }
     int kc = kp;
-    size_t wl = REGW_STAGE_OFFSET + (size_t)(regw == 3 ? 32 : 16) * RSTRIDE * 2;
+    size_t wl = REGW_STAGE_OFFSET + (size_t)(regw == 4 ? 64 : regw == 3 ? 32 : 16) * RSTRIDE * 2;
     if (!regw) {
       if (a.tiles_per_worker * ncb > 4 * PPW) continue;
       // worker staging phases: kc | kp, 32 | kc, stage within its share of LDS
