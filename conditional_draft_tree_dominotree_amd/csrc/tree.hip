@@ -1176,26 +1176,21 @@ __device__ __forceinline__ void ctl_expand(const TreeArgs& a, const CtlLds& c, i
         if (tl[u] > -INFINITY) se += __builtin_amdgcn_exp2f((tl[u] - mx) * L2E);
         lz[u] = live ? mx + __builtin_amdgcn_logf(se) * LN2 : -INFINITY;
       }
-      // ranks among each node's candidates: the composites go to the node's
-      // own z row (read above), then every lane reads them back as broadcasts
+      // ranks among each node's candidates: every lane compares its composite
+      // with the half-wave's others, rotated one lane at a time through the
+      // permute network (distinct lanes per read: no LDS bank conflicts)
       uint64_t me[2];
-      uint64_t* kz[2];
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        me[u] = has[u] ? cand_pack(f32_key(zv[u]), (uint32_t)idv[u]) : 0ull;
-        kz[u] = reinterpret_cast<uint64_t*>(c.f->z + jr[u] * 64);
-        if (node[u]) kz[u][l32] = me[u];
-      }
+      for (int u = 0; u < 2; ++u) me[u] = has[u] ? cand_pack(f32_key(zv[u]), (uint32_t)idv[u]) : 0ull;
       int rank[2] = {0, 0};
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        u32x4 kv[16];
-        lds_read_keys32(kz[u], kv);
+      for (int q = 1; q < 32; ++q) {
+        const int src = (((l32 + q) & 31) | (half << 5)) << 2;  // byte address of the source lane
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const uint64_t k0 = ((uint64_t)kv[i].y << 32) | kv[i].x, k1 = ((uint64_t)kv[i].w << 32) | kv[i].z;
-          rank[u] += k0 > me[u];  // slots past M hold 0, which precedes nothing
-          rank[u] += k1 > me[u];
+        for (int u = 0; u < 2; ++u) {
+          const uint32_t oh = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)(me[u] >> 32));
+          const uint32_t ol = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)(uint32_t)me[u]);
+          rank[u] += (((uint64_t)oh << 32) | ol) > me[u];  // lanes past M hold 0, which precedes nothing
         }
       }
 #pragma unroll
