@@ -72,6 +72,7 @@ struct dt_handle {
   int* err = nullptr;
   int* nanflag = nullptr;
   size_t act_bytes = 0;
+  uint32_t ebase = 0;  // epoch base of the next launch (mailboxes hold older epochs)
   int max_workers = 0;
   static constexpr int RING = 256;   // timed builds kept for dt_phase_times
   static constexpr int NPH = 5;       // timed phases
@@ -252,6 +253,8 @@ dt_status dt_create(dt_handle** out, const dt_dims* dims, const dt_weights* w, c
   ALLOC(h->err, 64);
   ALLOC(h->nanflag, 64);
   HIPB(hipMemsetAsync(h->err, 0, 64, stream));
+  HIPB(hipMemsetAsync(h->mbox_w, 0, (dt::GFLAG_WORDS + (size_t)h->max_workers * 32) * sizeof(uint32_t), stream));
+  HIPB(hipMemsetAsync(h->mbox_c, 0, (size_t)DT_MAX_BATCH * 256 * sizeof(uint32_t), stream));
   for (auto& set : h->ev)
     for (hipEvent_t& ev : set) HIPB(hipEventCreate(&ev));
   HIPB(hipStreamSynchronize(stream));
@@ -365,8 +368,15 @@ dt_status dt_build_trees(dt_handle* h, const dt_inputs* in, const dt_params* p, 
   if (a.n_workers + B > h->n_cu || a.n_workers > h->max_workers)
     return fail(DT_EUNSUPPORTED, "%d workers + %d requests exceed %d compute units", a.n_workers, B, h->n_cu);
   MARK(3);
-  HIPCHK(dt::launch_fill_u32(h->mbox_w, 0u, dt::GFLAG_WORDS + (size_t)a.n_workers * 32, stream));
-  HIPCHK(dt::launch_fill_u32(h->mbox_c, 0u, (size_t)B * 256, stream));
+  // mailboxes keep older epochs; clear them only when the epoch space wraps
+  const uint32_t span = dt::tree_epoch_span(a.N);
+  if (h->ebase + span >= dt::TREE_EPOCH_LIMIT) {
+    HIPCHK(dt::launch_fill_u32(h->mbox_w, 0u, dt::GFLAG_WORDS + (size_t)h->max_workers * 32, stream));
+    HIPCHK(dt::launch_fill_u32(h->mbox_c, 0u, (size_t)DT_MAX_BATCH * 256, stream));
+    h->ebase = 0;
+  }
+  a.ebase = h->ebase;
+  h->ebase += span;
   MARK(4);
   HIPCHK(dt::launch_tree(a, h->bf16, lds, stream));
   MARK(5);

@@ -89,10 +89,14 @@ struct TreeArgs {
   int32_t *tokens, *parents, *depths, *n_nodes;
   float* scores;
   unsigned spin_limit;
+  uint32_t ebase;          // epochs of this launch: ebase + 1 .. ebase + tree_epoch_span(N) - 1
 };
 // Exchange columns a build may use per step (slots per step = B p <= this).
 constexpr int TREE_MAX_COLS = 512;
 constexpr int GFLAG_WORDS = 16 * 64;  // worker group flags, placed before the worker mailboxes
+// Epochs a launch may use (at most N + 1 steps, the first post and the last).
+__host__ __device__ inline uint32_t tree_epoch_span(int N) { return (uint32_t)N + 8u; }
+constexpr uint32_t TREE_EPOCH_LIMIT = 1u << 27;  // mailbox words hold the epoch in 27 bits
 // Fills the schedule fields of `a` (p from `pops`, 0 = automatic) and returns
 // the dynamic LDS bytes the launch needs, or 0 if the shape cannot be served.
 // With register workers (allowed unless `lds_workers`) it also sets

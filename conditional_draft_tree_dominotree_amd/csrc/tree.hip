@@ -53,7 +53,7 @@
 
 namespace dt {
 
-constexpr uint32_t MBOX_DONE = 0xFFFFFFFFu;
+constexpr uint32_t MBOX_DONE_E = 31u;  // node count field of a request's last word (no more steps)
 constexpr int NT = 256;      // threads per block (every block of the builder)
 constexpr int PMAX = 16;     // nodes per request per step
 constexpr int QCAP = 32;     // frontier entries tested per pop round
@@ -196,8 +196,10 @@ __device__ __forceinline__ bool wait_mbox(const uint32_t* box, int nwords, uint3
 }
 
 // controller -> worker mailbox word: step epoch in the high bits, nodes expanded
-// by the request in that step in the low 5
-__device__ __forceinline__ uint32_t mbox_word(int epoch, int e) { return ((uint32_t)epoch << 5) | (uint32_t)e; }
+// by the request in that step in the low 5 (MBOX_DONE_E: the request is done).
+// Epochs run from ebase + 1 within a launch and only grow across launches, so
+// no mailbox needs clearing between builds.
+__device__ __forceinline__ uint32_t mbox_word(uint32_t epoch, uint32_t e) { return (epoch << 5) | e; }
 
 // ---------------------------------------------------------------------------
 // worker: per-step product of its Wc tiles with the expanded nodes' states
@@ -389,14 +391,14 @@ __device__ __forceinline__ void worker_compute_f32(const TreeArgs& a, const floa
 // misc[1] = requests.  Ends with a block barrier.
 __device__ __forceinline__ void worker_columns(const TreeArgs& a, int w, int t, int* coln, int* reqs, int* misc) {
   const int tid = threadIdx.x, lane = tid & 63;
-  const uint32_t epoch = (uint32_t)t + 1u;
+  const uint32_t epoch = a.ebase + (uint32_t)t + 1u;
   if (tid < 64) {
     const uint32_t* mybox = a.mbox_w + (size_t)w * 32;
     const bool ok = wait_mbox(mybox, a.B, epoch << 5, a.err, a.spin_limit);
     const int b = lane;
     uint32_t word = 0;
     if (ok && b < a.B) word = ld_dev_u32(mybox + b);
-    const int e = (ok && b < a.B && word != MBOX_DONE) ? (int)(word & 31u) : 0;
+    const int e = (ok && b < a.B && (word & 31u) != MBOX_DONE_E) ? (int)(word & 31u) : 0;
     // exclusive prefix of e over the lanes
     int incl = e;
     for (int d = 1; d < 64; d <<= 1) {
@@ -449,7 +451,7 @@ __device__ __forceinline__ void worker_main(const TreeArgs& a, unsigned char* ld
   __syncthreads();
 
   for (int t = 0;; ++t) {
-    const uint32_t epoch = (uint32_t)t + 1u;
+    const uint32_t epoch = a.ebase + (uint32_t)t + 1u;
     worker_columns(a, w, t, coln, reqs, misc);
     const int ncols = misc[0], nreq = misc[1];
     if (ncols <= 0) return;  // a wait ran out, or every request is finished
@@ -652,7 +654,7 @@ __device__ __forceinline__ void worker_regs(const TreeArgs& a, unsigned char* ld
   }
 
   for (int t = 0;; ++t) {
-    const uint32_t epoch = (uint32_t)t + 1u;
+    const uint32_t epoch = a.ebase + (uint32_t)t + 1u;
     worker_columns(a, w, t, coln, reqs, misc);
     const int ncols = misc[0], nreq = misc[1];
     if (ncols <= 0) return;  // a wait ran out, or every request is finished
@@ -1826,7 +1828,7 @@ __device__ __forceinline__ void controller_main(const TreeArgs& a, unsigned char
   }
   stores_done();
   __syncthreads();
-  for (int w = tid; w < a.n_workers; w += NT) st_dev_u32(a.mbox_w + (size_t)w * 32 + b, mbox_word(1, 1));
+  for (int w = tid; w < a.n_workers; w += NT) st_dev_u32(a.mbox_w + (size_t)w * 32 + b, mbox_word(a.ebase + 1, 1));
   stores_done();
   ctl_prefetch<W>(a, c, b);
   __syncthreads();
@@ -1834,7 +1836,7 @@ __device__ __forceinline__ void controller_main(const TreeArgs& a, unsigned char
   bool failed = false;
   for (int t = 0;; ++t) {
     const int e = c.f->misc[C_E];
-    const uint32_t epoch = (uint32_t)t + 1u;
+    const uint32_t epoch = a.ebase + (uint32_t)t + 1u;
     if (tid < 64) {
       const bool ok = wait_mbox(a.mbox_c + (size_t)b * 256, a.n_workers, epoch, a.err, a.spin_limit);
       if (tid == 0) c.f->misc[C_OK] = ok;
@@ -1870,13 +1872,14 @@ __device__ __forceinline__ void controller_main(const TreeArgs& a, unsigned char
     stores_done();
     __syncthreads();
     for (int w = tid; w < a.n_workers; w += NT)
-      st_dev_u32(a.mbox_w + (size_t)w * 32 + b, mbox_word(t + 2, e2));
+      st_dev_u32(a.mbox_w + (size_t)w * 32 + b, mbox_word(a.ebase + t + 2, e2));
     stores_done();
     ctl_prefetch<W>(a, c, b);  // overlaps the workers' step
     __syncthreads();
   }
   // release the workers from this request
-  for (int w = tid; w < a.n_workers; w += NT) st_dev_u32(a.mbox_w + (size_t)w * 32 + b, MBOX_DONE);
+  for (int w = tid; w < a.n_workers; w += NT)
+    st_dev_u32(a.mbox_w + (size_t)w * 32 + b, mbox_word(a.ebase + tree_epoch_span(a.N) - 1, MBOX_DONE_E));
   stores_done();
   ctl_output(a, c, b, failed);
 }
