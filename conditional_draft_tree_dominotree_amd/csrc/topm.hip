@@ -16,9 +16,11 @@
 // (value desc, id asc) composites.  The chunk's LSE statistics come from the
 // same registers.  topm_fallback: when more than 512 keys reach that bound
 // (many equal values), an exact 3-pass radix select over the chunk in LDS
-// redoes that chunk.  topm_merge: one block per row ranks the chunk lists
-// against each other and keeps the M best; the LSE statistics combine exactly
-// (a token left out of its chunk's list is left out of the row's).
+// redoes that chunk.  topm_merge: one block per row bounds the row's M-th key
+// from below by the M-th largest of the first few entries of every chunk list,
+// ranks the keys at or above the bound against each other and keeps the M
+// best; the LSE statistics combine exactly (a token left out of its chunk's
+// list is left out of the row's).
 #include "common.h"
 #include "kernels.h"
 
@@ -29,6 +31,8 @@ constexpr int HBINS = 4096;
 
 constexpr int PER_THREAD = TOPM_CHUNK / TOPM_THREADS;  // 32 values per thread
 constexpr int FAST_CAP = 512;                          // candidates the fast path ranks
+constexpr int MERGE_SUB = 320;   // merge: subset keys for the bound (S (M / S + 2) <= M + 2 S)
+constexpr int MERGE_CAP = 1024;  // merge: candidates ranked pairwise
 
 // Bitonic sort of one 32-bit value per lane of a wave, descending.
 __device__ __forceinline__ uint32_t wave_sort_desc_u32(uint32_t v) {
@@ -318,14 +322,18 @@ __global__ __launch_bounds__(TOPM_THREADS) void topm_merge_kernel(
     int32_t* __restrict__ ids_out, float* __restrict__ vals_out, float* __restrict__ lse_out,
     float* __restrict__ tail_out, int32_t* __restrict__ tokrank_out, int32_t* __restrict__ user_ids,
     float* __restrict__ user_vals, float* __restrict__ user_lse) {
-  extern __shared__ uint64_t lists[];  // [S][M]
+  extern __shared__ uint64_t lists[];  // [S][M], then [MERGE_CAP] candidates
   __shared__ int cnt[DT_TOPM_MAX_CHUNKS];
   __shared__ float mc[DT_TOPM_MAX_CHUNKS], sc[DT_TOPM_MAX_CHUNKS], tc[DT_TOPM_MAX_CHUNKS];
   __shared__ int out_ids[DT_TOPM_MAX];
   __shared__ float red[4];
+  __shared__ uint64_t sub[MERGE_SUB];
+  __shared__ int nsub, ncand;
+  __shared__ uint64_t lbound, kth;
 
   const int tid = threadIdx.x;
   const int row = blockIdx.x;
+  uint64_t* cands = lists + (size_t)S * M;
   const uint64_t* src = cand + (size_t)row * S * M;
   for (int i = tid; i < S * M; i += TOPM_THREADS) lists[i] = src[i];
   for (int i = tid; i < S; i += TOPM_THREADS) {
@@ -335,29 +343,98 @@ __global__ __launch_bounds__(TOPM_THREADS) void topm_merge_kernel(
     tc[i] = st.z;
     cnt[i] = __float_as_int(st.w);
   }
+  if (tid == 0) {
+    nsub = 0;
+    ncand = 0;
+    lbound = 0ull;
+    kth = 0ull;
+  }
   __syncthreads();
   float mloc = -INFINITY;
   for (int i = tid; i < S; i += TOPM_THREADS) mloc = fmaxf(mloc, mc[i]);
   const float mstar = block_max<TOPM_THREADS>(mloc, red);
 
-  float extra = 0.f;
+  // 1. a lower bound for the row's M-th largest key: the M-th largest of the
+  //    first tn entries of every (sorted) chunk list, a subset with at least M
+  //    keys whenever the lists hold tn each (else the bound is 0: every key)
+  const int tn = M / S + 2;
+  for (int e = tid; e < S * tn; e += TOPM_THREADS) {
+    const int c = e / tn, i = e - c * tn;
+    if (i < cnt[c]) {
+      const int slot = atomicAdd(&nsub, 1);
+      if (slot < MERGE_SUB) sub[slot] = lists[c * M + i];
+    }
+  }
+  __syncthreads();
+  const int U = min(nsub, MERGE_SUB);
+  for (int i = tid; i < U; i += TOPM_THREADS) {
+    const uint64_t key = sub[i];
+    int r = 0;
+#pragma unroll 8
+    for (int j = 0; j < U; ++j) r += sub[j] > key;
+    if (r == M - 1) lbound = key;  // keys are unique: one thread at most
+  }
+  __syncthreads();
+  // 2. the candidates: every key at or above the bound (a prefix of each list)
+  const uint64_t lb = lbound;
   for (int e = tid; e < S * M; e += TOPM_THREADS) {
     const int c = e / M, i = e - c * M;
-    if (i >= cnt[c]) continue;
     const uint64_t key = lists[e];
-    int rank = i;
-    for (int c2 = 0; c2 < S; ++c2)
-      if (c2 != c) rank += count_greater(lists + c2 * M, cnt[c2], key);
-    const float v = key_f32(cand_key(key));
-    if (rank < M) {
-      const int id = (int)cand_id(key);
-      out_ids[rank] = id;
-      ids_out[(size_t)row * M + rank] = id;
-      vals_out[(size_t)row * M + rank] = v;
-      if (user_ids) user_ids[(size_t)row * M + rank] = id;
-      if (user_vals) user_vals[(size_t)row * M + rank] = v;
-    } else if (mstar > -INFINITY) {
-      extra += __expf(v / T - mstar);
+    if (i < cnt[c] && key >= lb) {
+      const int slot = atomicAdd(&ncand, 1);
+      if (slot < MERGE_CAP) cands[slot] = key;
+    }
+  }
+  __syncthreads();
+  const int C = ncand;
+  if (C <= MERGE_CAP) {
+    // 3. exact ranks among the candidates; the M best are the row's list
+    for (int i = tid; i < C; i += TOPM_THREADS) {
+      const uint64_t key = cands[i];
+      int rank = 0;
+#pragma unroll 8
+      for (int j = 0; j < C; ++j) rank += cands[j] > key;
+      if (rank < M) {
+        const int id = (int)cand_id(key);
+        const float v = key_f32(cand_key(key));
+        out_ids[rank] = id;
+        ids_out[(size_t)row * M + rank] = id;
+        vals_out[(size_t)row * M + rank] = v;
+        if (user_ids) user_ids[(size_t)row * M + rank] = id;
+        if (user_vals) user_vals[(size_t)row * M + rank] = v;
+        if (rank == M - 1) kth = key;
+      }
+    }
+  } else {
+    // many keys at the bound: rank every list entry against the other lists
+    for (int e = tid; e < S * M; e += TOPM_THREADS) {
+      const int c = e / M, i = e - c * M;
+      if (i >= cnt[c]) continue;
+      const uint64_t key = lists[e];
+      int rank = i;
+      for (int c2 = 0; c2 < S; ++c2)
+        if (c2 != c) rank += count_greater(lists + c2 * M, cnt[c2], key);
+      if (rank < M) {
+        const int id = (int)cand_id(key);
+        const float v = key_f32(cand_key(key));
+        out_ids[rank] = id;
+        ids_out[(size_t)row * M + rank] = id;
+        vals_out[(size_t)row * M + rank] = v;
+        if (user_ids) user_ids[(size_t)row * M + rank] = id;
+        if (user_vals) user_vals[(size_t)row * M + rank] = v;
+        if (rank == M - 1) kth = key;
+      }
+    }
+  }
+  __syncthreads();
+  // 4. the list entries left out of the row's M (keys below the M-th) join the tail
+  const uint64_t km = kth;
+  float extra = 0.f;
+  if (mstar > -INFINITY) {
+    for (int e = tid; e < S * M; e += TOPM_THREADS) {
+      const int c = e / M, i = e - c * M;
+      const uint64_t key = lists[e];
+      if (i < cnt[c] && key < km) extra += __expf(key_f32(cand_key(key)) / T - mstar);
     }
   }
   float s_all = 0.f, s_tail = 0.f;
@@ -415,7 +492,7 @@ hipError_t launch_topm_merge(const uint64_t* chunk_cand, const float4* chunk_sta
                              int M, float T, int32_t* ids, float* vals, float* lse, float* tail,
                              int32_t* tokrank, int32_t* user_ids, float* user_vals, float* user_lse,
                              hipStream_t stream) {
-  const size_t lds = (size_t)S * M * sizeof(uint64_t);
+  const size_t lds = ((size_t)S * M + MERGE_CAP) * sizeof(uint64_t);
   hipLaunchKernelGGL(topm_merge_kernel, dim3(rows), dim3(TOPM_THREADS), lds, stream, chunk_cand,
                      chunk_stat, S, M, T, ids, vals, lse, tail, tokrank, user_ids, user_vals, user_lse);
   return hipGetLastError();
