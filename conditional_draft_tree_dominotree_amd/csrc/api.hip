@@ -73,6 +73,8 @@ struct dt_handle {
   int* nanflag = nullptr;
   size_t act_bytes = 0;
   uint32_t ebase = 0;  // epoch base of the next launch (mailboxes hold older epochs)
+  hipStream_t side = nullptr;  // runs P = H W1_H beside the candidate selection
+  hipEvent_t fork_ev = nullptr, join_ev = nullptr;
   int max_workers = 0;
   static constexpr int RING = 256;   // timed builds kept for dt_phase_times
   static constexpr int NPH = 5;       // timed phases
@@ -101,6 +103,9 @@ void free_all(dt_handle* h) {
   for (auto& set : h->ev)
     for (hipEvent_t& e : set)
       if (e) (void)hipEventDestroy(e);
+  if (h->fork_ev) (void)hipEventDestroy(h->fork_ev);
+  if (h->join_ev) (void)hipEventDestroy(h->join_ev);
+  if (h->side) (void)hipStreamDestroy(h->side);
 }
 
 dt_status check_dims(const dt_dims* d) {
@@ -257,6 +262,9 @@ dt_status dt_create(dt_handle** out, const dt_dims* dims, const dt_weights* w, c
   HIPB(hipMemsetAsync(h->mbox_c, 0, (size_t)DT_MAX_BATCH * 256 * sizeof(uint32_t), stream));
   for (auto& set : h->ev)
     for (hipEvent_t& ev : set) HIPB(hipEventCreate(&ev));
+  HIPB(hipStreamCreateWithFlags(&h->side, hipStreamNonBlocking));  // default priority
+  HIPB(hipEventCreateWithFlags(&h->fork_ev, hipEventDisableTiming));
+  HIPB(hipEventCreateWithFlags(&h->join_ev, hipEventDisableTiming));
   HIPB(hipStreamSynchronize(stream));
 #undef ALLOC
 #undef HIPB
@@ -295,8 +303,19 @@ dt_status dt_build_trees(dt_handle* h, const dt_inputs* in, const dt_params* p, 
     if (flag) return fail(DT_EINVAL, "base logits contain NaN");
   }
 
-  // a0 (LM head, when no base logits are given), then a1: candidates and LSE
+  // a2: P = H W1_H (the path-independent half of W1 [H_d; S]) needs only the
+  // hidden states: it runs on the side stream while the candidates are chosen
   MARK(0);
+  HIPCHK(hipEventRecord(h->fork_ev, stream));
+  HIPCHK(hipStreamWaitEvent(h->side, h->fork_ev, 0));
+  if (h->bf16)
+    HIPCHK(dt::launch_gemm_bf16((const uint16_t*)in->hidden, nullptr, (const uint16_t*)h->w1h_t, nullptr, h->P,
+                                rows, d.rank, d.hidden, d.rank, h->side));
+  else
+    HIPCHK(dt::launch_gemm_f32((const float*)in->hidden, nullptr, (const float*)h->w1h_t, nullptr, h->P, rows,
+                               d.rank, d.hidden, d.rank, h->side));
+  HIPCHK(hipEventRecord(h->join_ev, h->side));
+  // a0 (LM head, when no base logits are given), then a1: candidates and LSE
   if (!in->base_logits) {
     // L_base = H W_lm (Domino summary, 方法步骤详情), fp32 accumulate
     HIPCHK(dt::launch_gemm_bf16((const uint16_t*)in->hidden, nullptr, (const uint16_t*)h->wlm_t, nullptr,
@@ -309,14 +328,9 @@ dt_status dt_build_trees(dt_handle* h, const dt_inputs* in, const dt_params* p, 
                            h->cand_vals, h->lse, h->tail, h->tokrank, out->cand_ids, out->cand_logits, out->lse,
                            stream));
   }
-  // a2: P = H W1_H (the path-independent half of W1 [H_d; S])
+  // join: what P adds after the candidates are done
   MARK(2);
-  if (h->bf16)
-    HIPCHK(dt::launch_gemm_bf16((const uint16_t*)in->hidden, nullptr, (const uint16_t*)h->w1h_t, nullptr, h->P,
-                                rows, d.rank, d.hidden, d.rank, stream));
-  else
-    HIPCHK(dt::launch_gemm_f32((const float*)in->hidden, nullptr, (const float*)h->w1h_t, nullptr, h->P, rows,
-                               d.rank, d.hidden, d.rank, stream));
+  HIPCHK(hipStreamWaitEvent(stream, h->join_ev, 0));
 
   // a3-a8: the persistent builder
   dt::TreeArgs a{};

@@ -163,8 +163,10 @@ dt_status dt_create(dt_handle** h, const dt_dims* dims, const dt_weights* w,
 
 /* Build the trees of one batch [DominoTree, 1, 2, 4].  Enqueues the kernels on
  * `stream` and returns: no host synchronisation and no allocation.  Results
- * are valid once the stream reaches this point.  A handle must not be used by
- * two builds at once (one workspace).  When in->base_logits is NULL the
+ * are valid once the stream reaches this point.  P = H W1_H runs on a stream
+ * the handle owns (default priority), forked from and joined back into
+ * `stream` with events, beside the candidate selection.  A handle must not be
+ * used by two builds at once (one workspace).  When in->base_logits is NULL the
  * base logits are computed from in->hidden with w_lm [Domino, Steps] and are
  * never written to memory (only their candidates and LSE are).
  * Errors: DT_EINVAL (NULL pointers, batch out of range, params out of range
@@ -182,7 +184,9 @@ dt_status dt_sync_status(dt_handle* h, void* stream);
  * DT_TIMING since the previous call (at most the last 256 of them), measured
  * with HIP events recorded on each build's stream: ms[0] the LM head (0 when
  * base logits are given), ms[1] per-depth candidates (top-M + LSE), ms[2]
- * P = H W1_H, ms[3] mailbox reset, ms[4] the tree builder kernel.  Waits for
+ * the wait for P = H W1_H after the candidates (it runs beside them), ms[3]
+ * the builder's set-up (a mailbox clear only when the epoch space wraps),
+ * ms[4] the tree builder kernel.  Waits for
  * those events, writes min(n, 5) values and the number of builds averaged to
  * *count, then starts a new averaging window.
  * Errors: DT_EINVAL (NULL h, ms or count), DT_EHIP. */
