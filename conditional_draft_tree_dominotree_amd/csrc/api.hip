@@ -365,6 +365,7 @@ dt_status dt_build_trees(dt_handle* h, const dt_inputs* in, const dt_params* p, 
   a.u = h->u;
   a.ninfo = h->ninfo;
   a.gflag = h->mbox_w;
+  a.ready = h->mbox_w + 16 * 64;
   a.mbox_w = h->mbox_w + dt::GFLAG_WORDS;
   a.mbox_c = h->mbox_c;
   a.err = h->err;

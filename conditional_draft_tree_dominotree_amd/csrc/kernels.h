@@ -82,6 +82,7 @@ struct TreeArgs {
   float* u;                // [slots, r]
   int32_t* ninfo;          // [steps][TREE_MAX_COLS][2]: token and parent slot of each node to advance
   uint32_t* gflag;         // [16][64] worker group flags (states of a step advanced)
+  uint32_t* ready;         // [64] controller b: its start-up loads are done (the workers then load weights)
   uint32_t* mbox_w;        // [n_workers][32] controller -> worker mailboxes (one line each)
   uint32_t* mbox_c;        // [B][256] worker -> controller mailboxes
   int* err;                // device error word
@@ -93,7 +94,8 @@ struct TreeArgs {
 };
 // Exchange columns a build may use per step (slots per step = B p <= this).
 constexpr int TREE_MAX_COLS = 512;
-constexpr int GFLAG_WORDS = 16 * 64;  // worker group flags, placed before the worker mailboxes
+constexpr int GFLAG_WORDS = 16 * 64 + 64;  // worker group flags and controller ready flags, before the
+                                            // worker mailboxes
 // Epochs a launch may use (at most N + 1 steps, the first post and the last).
 __host__ __device__ inline uint32_t tree_epoch_span(int N) { return (uint32_t)N + 8u; }
 constexpr uint32_t TREE_EPOCH_LIMIT = 1u << 27;  // mailbox words hold the epoch in 27 bits

@@ -415,6 +415,18 @@ __device__ __forceinline__ void worker_columns(const TreeArgs& a, int w, int t, 
   __syncthreads();
 }
 
+// Workers load their weights only once every controller has its start-up
+// loads (candidates, first W2 rows): at launch the weight loads would
+// otherwise queue ahead of them.  Returns false if the wait ran out.
+__device__ __forceinline__ bool worker_wait_ready(const TreeArgs& a, int* misc) {
+  if (threadIdx.x < 64) {
+    const bool ok = wait_mbox(a.ready, a.B, a.ebase + 1, a.err, a.spin_limit);
+    if (threadIdx.x == 0) misc[2] = ok;
+  }
+  __syncthreads();
+  return misc[2] != 0;
+}
+
 // Once this block's rows of the step are stored, tell each active request's
 // controller.
 __device__ __forceinline__ void worker_ack(const TreeArgs& a, int w, const int* reqs, int nreq, uint32_t epoch) {
@@ -440,6 +452,7 @@ __device__ __forceinline__ void worker_main(const TreeArgs& a, unsigned char* ld
   int* reqs = coln + TREE_MAX_COLS;  // requests with work this step
   int* misc = reqs + TREE_MAX_COLS;  // [0] columns (-1: failed), [1] requests
 
+  if (!worker_wait_ready(a, misc)) return;
   // the block's Wc tiles stay in for the whole launch
   {
     const W* src = reinterpret_cast<const W*>(a.tiles) + (size_t)tile0 * 16 * kp;
@@ -450,7 +463,7 @@ __device__ __forceinline__ void worker_main(const TreeArgs& a, unsigned char* ld
   }
   __syncthreads();
 
-  for (int t = 0;; ++t) {
+  for (int t = a.root ? 0 : 1;; ++t) {  // zero roots: step 0 needs no product (set up by the controllers)
     const uint32_t epoch = a.ebase + (uint32_t)t + 1u;
     worker_columns(a, w, t, coln, reqs, misc);
     const int ncols = misc[0], nreq = misc[1];
@@ -642,6 +655,7 @@ __device__ __forceinline__ void worker_regs(const TreeArgs& a, unsigned char* ld
   const int tile0 = ((w / nb) * 4 + wv) * TW;
   const int grp = w % nb, gq = w / nb, ngq = a.n_workers / nb;  // the blocks sharing these columns
 
+  if (!worker_wait_ready(a, misc)) return;
   // this wave's A operands: tile rows (lane & 15), k 8 (lane >> 4) + 32 kb
   bf16x8 wa[TW][RKB];
 #pragma unroll
@@ -653,7 +667,7 @@ __device__ __forceinline__ void worker_regs(const TreeArgs& a, unsigned char* ld
     for (int kb = 0; kb < RKB; ++kb) wa[i][kb] = src[kb * 64];
   }
 
-  for (int t = 0;; ++t) {
+  for (int t = a.root ? 0 : 1;; ++t) {  // zero roots: step 0 needs no product (set up by the controllers)
     const uint32_t epoch = a.ebase + (uint32_t)t + 1u;
     worker_columns(a, w, t, coln, reqs, misc);
     const int ncols = misc[0], nreq = misc[1];
@@ -1825,20 +1839,30 @@ __device__ __forceinline__ void controller_main(const TreeArgs& a, unsigned char
       st_dev_act<W>(a0 + j, v, a.act_bf16);
     }
     for (int j = ds + tid; j < k_padded(ds); j += NT) st_dev_act<W>(a0 + j, 0.f, 0);
+    if (!a.root) {
+      // a zero root state: W_hh S + b_hh = b_hh and W1_S^T S = 0, without the workers
+      float* g0 = a.gh + sl * gh_stride(ds);
+      for (int j = tid; j < 3 * ds; j += NT) st_dev_f32(g0 + j, a.b_hh ? a.b_hh[j] : 0.f);
+      float* u0 = a.u + sl * u_stride(a.r);
+      for (int j = tid; j < a.r; j += NT) st_dev_f32(u0 + j, 0.f);
+    }
   }
   stores_done();
   __syncthreads();
-  for (int w = tid; w < a.n_workers; w += NT) st_dev_u32(a.mbox_w + (size_t)w * 32 + b, mbox_word(a.ebase + 1, 1));
+  if (a.root)
+    for (int w = tid; w < a.n_workers; w += NT) st_dev_u32(a.mbox_w + (size_t)w * 32 + b, mbox_word(a.ebase + 1, 1));
   stores_done();
   ctl_prefetch<W>(a, c, b);
   __syncthreads();
+  if (tid == 0) st_dev_u32(a.ready + b, a.ebase + 1);  // start-up loads done: workers may load weights
 
   bool failed = false;
   for (int t = 0;; ++t) {
     const int e = c.f->misc[C_E];
     const uint32_t epoch = a.ebase + (uint32_t)t + 1u;
     if (tid < 64) {
-      const bool ok = wait_mbox(a.mbox_c + (size_t)b * 256, a.n_workers, epoch, a.err, a.spin_limit);
+      const bool ok = (t == 0 && !a.root) ||  // zero roots: step 0's products are set up above
+                      wait_mbox(a.mbox_c + (size_t)b * 256, a.n_workers, epoch, a.err, a.spin_limit);
       if (tid == 0) c.f->misc[C_OK] = ok;
     }
     __syncthreads();
@@ -1887,8 +1911,10 @@ __device__ __forceinline__ void controller_main(const TreeArgs& a, unsigned char
 template <typename W>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void tree_kernel(TreeArgs a) {
   extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
-  // no cache line of an exchange slot may survive from an earlier launch
-  __threadfence();
+  // no cache line of an exchange slot may survive from an earlier launch: an
+  // acquire (cache invalidate) suffices; the writes of earlier kernels were
+  // released at their end
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   if ((int)blockIdx.x < a.n_workers) {
     if constexpr (sizeof(W) == 2) {
       if (a.regw == 1) return worker_regs<1, 1>(a, lds);

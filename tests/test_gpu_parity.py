@@ -82,6 +82,21 @@ def test_small_bf16(dev, B, M, k, N, ds):
     tb.close()
 
 
+def test_bf16_register_workers_with_root_and_biases(dev):
+    # a given root state: the workers compute step 0's products (with zero
+    # roots the controllers set them up and the workers start at step 1)
+    spec = synth.small("bf16_root", V=3000, D=6, h=64, e=96, ds=1024, r=64, M=8, k=3, N=30, B=4,
+                       wdtype="bf16", group=977, emb_std=0.5, biases=True, root_std=0.7)
+    spec, w, req = synth.workload(spec)
+    tb = gu.make_builder(spec, w)
+    got = gu.run(tb, spec, req)
+    reps, trees = gu.compare(spec, w, req, got)
+    print(gu.summarize(reps))
+    _assert_ok(reps)
+    gu.check_candidates(spec, trees, got, range(spec.B))
+    tb.close()
+
+
 def test_candidates_with_ties_zero_and_inf(dev):
     spec = synth.small("ties", V=20000, D=4, h=16, e=16, ds=32, r=16, M=40, k=4, N=20,
                        group=500)
