@@ -433,9 +433,8 @@ __device__ __forceinline__ void worker_ack(const TreeArgs& a, int w, const int* 
   const int tid = threadIdx.x;
   stores_done();
   __syncthreads();
+  // wave 0 only (nreq <= 64); the ack drains while it polls the next step
   if (tid < nreq) st_dev_u32(a.mbox_c + (size_t)reqs[tid] * 256 + w, epoch);
-  stores_done();
-  __syncthreads();
 }
 
 template <typename W>
@@ -1897,7 +1896,6 @@ __device__ __forceinline__ void controller_main(const TreeArgs& a, unsigned char
     __syncthreads();
     for (int w = tid; w < a.n_workers; w += NT)
       st_dev_u32(a.mbox_w + (size_t)w * 32 + b, mbox_word(a.ebase + t + 2, e2));
-    stores_done();
     ctl_prefetch<W>(a, c, b);  // overlaps the workers' step
     __syncthreads();
   }
