@@ -7,63 +7,112 @@
 // comparison on the fp32 inputs, so it is exact; only the two LSE values are
 // rounded.
 //
-// Kernels.  topm_chunk: one 256-thread block per (row, chunk of 8192 tokens)
-// reads its chunk once from HBM into registers (32 values per thread).  Each
-// wave sorts its 64 per-thread maxima and takes the ceil(M/4)-th largest; the
-// smallest of the four wave values bounds the chunk's M-th largest value from
-// below (at least M threads reach it), so the keys at or above it -- typically
-// a few more than M -- hold the chunk's top-M; they are ranked exactly as
-// (value desc, id asc) composites.  The chunk's LSE statistics come from the
-// same registers.  topm_fallback: when more than 512 keys reach that bound
-// (many equal values), an exact 3-pass radix select over the chunk in LDS
-// redoes that chunk.  topm_merge: one block per row bounds the row's M-th key
-// from below by the M-th largest of the first few entries of every chunk list,
-// ranks the keys at or above the bound against each other and keeps the M
-// best; the LSE statistics combine exactly (a token left out of its chunk's
-// list is left out of the row's).
+// Kernels.  topm_chunk: a grid of 256-thread blocks sized to fill the chip
+// walks the (row, chunk of 8192 tokens) items; each block reads an item once
+// from HBM into registers (32 values per thread) while it selects from the
+// previous one, so the loads of one item overlap the selection of the other.
+// Each wave finds the ceil(M/4)-th largest of its 64 per-thread maxima (a bit
+// search over ballots); the smallest of the four wave values bounds the
+// chunk's M-th largest value from below (at least M threads reach it), so the
+// keys at or above it -- typically a few more than M -- hold the chunk's
+// top-M; they are ranked exactly as (value desc, id asc) composites.  When
+// more than 512 keys reach that bound (many equal values), an exact radix
+// select over the same registers (four 8-bit passes, ties at the threshold
+// taken in id order) replaces the ranking.  The chunk's LSE statistics come
+// from the same registers.  topm_merge: one block per row bounds the row's
+// M-th key from below by the M-th largest of the first few entries of every
+// chunk list, ranks the keys at or above the bound against each other and
+// keeps the M best; the LSE statistics combine exactly (a token left out of
+// its chunk's list is left out of the row's).
+#include <algorithm>
+
 #include "common.h"
 #include "kernels.h"
 
 namespace dt {
 
 constexpr int TOPM_THREADS = 256;
-constexpr int HBINS = 4096;
 
 constexpr int PER_THREAD = TOPM_CHUNK / TOPM_THREADS;  // 32 values per thread
 constexpr int FAST_CAP = 512;                          // candidates the fast path ranks
 constexpr int MERGE_SUB = 320;   // merge: subset keys for the bound (S (M / S + 2) <= M + 2 S)
 constexpr int MERGE_CAP = 1024;  // merge: candidates ranked pairwise
 
-// Bitonic sort of one 32-bit value per lane of a wave, descending.
-__device__ __forceinline__ uint32_t wave_sort_desc_u32(uint32_t v) {
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int k = 2; k <= 64; k <<= 1) {
-#pragma unroll
-    for (int j = k >> 1; j >= 1; j >>= 1) {
-      const uint32_t o = (uint32_t)__shfl_xor((int)v, j);
-      const bool lower = (lane & j) == 0;
-      const bool desc_block = (lane & k) == 0;  // the last (k = 64) block is descending
-      v = (lower == desc_block) ? max(v, o) : min(v, o);
-    }
-  }
+// Inclusive add-scan over the lanes of a wave: doubling shifts within each
+// row of 16, then each row adds the totals of the rows before it.
+__device__ __forceinline__ int wave_add_scan_incl(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, false);  // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, false);  // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, false);  // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, false);  // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, false);  // row_bcast:15 to rows 1, 3
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xC, 0xF, false);  // row_bcast:31 to rows 2, 3
   return v;
 }
 
-template <bool FULL>
-__device__ __forceinline__ void topm_chunk_body(const float* __restrict__ src, int len, int c0, int Mc, int M,
-                                                float T, uint64_t* __restrict__ out_list,
-                                                float4* __restrict__ out_stat_p, uint64_t* sel, uint32_t* wb,
-                                                float* red, int* sel_count) {
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  // 1. read the chunk once into registers: element tid*4 + 1024 j + e holds
-  //    float4 piece j of thread tid (coalesced); missing elements are -inf.
-  float x[PER_THREAD];
-  if (FULL) {
+// Largest key of the wave (every lane gets it).
+__device__ __forceinline__ uint32_t wave_max_key(uint32_t v) {
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xF, 0xF, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xF, 0xF, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xF, 0xF, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xF, 0xF, false));
+  const uint32_t a = max((uint32_t)__builtin_amdgcn_readlane((int)v, 15), (uint32_t)__builtin_amdgcn_readlane((int)v, 31));
+  const uint32_t b = max((uint32_t)__builtin_amdgcn_readlane((int)v, 47), (uint32_t)__builtin_amdgcn_readlane((int)v, 63));
+  return max(a, b);
+}
+
+// The m-th largest of the wave's 64 keys (1 <= m <= 64): the largest c with
+// at least m keys >= c, built bit by bit from the top.
+__device__ __forceinline__ uint32_t wave_kth_largest(uint32_t v, int m) {
+  uint32_t p = 0;
+#pragma unroll
+  for (int b = 31; b >= 0; --b) {
+    const uint32_t c = p | (1u << b);
+    if ((int)__popcll(__ballot(v >= c)) >= m) p = c;
+  }
+  return p;
+}
+
+// Exclusive prefix sum over the threads of the block in thread order, and
+// the block total.  `red` holds 4 ints.
+__device__ __forceinline__ int block_prefix_excl(int v, int* red, int* total) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int incl = wave_add_scan_incl(v);
+  __syncthreads();
+  if (lane == 63) red[w] = incl;
+  __syncthreads();
+  int before = 0, tot = 0;
+#pragma unroll
+  for (int i = 0; i < TOPM_THREADS / 64; ++i) {
+    before += i < w ? red[i] : 0;
+    tot += red[i];
+  }
+  *total = tot;
+  return before + incl - v;
+}
+
+struct ChunkLds {
+  uint64_t sel[FAST_CAP];        // keys at or above the threshold; radix histogram of the exact path
+  uint64_t list[DT_TOPM_MAX];    // the chunk's Mc best, sorted
+  uint32_t wb[4], wm[4];         // per wave: threshold bound, largest key
+  float ws[4];                   // per wave: sum of exp
+  int wi[4];                     // scan totals
+  int sel_count, digit, above;
+};
+
+// Item = (row, chunk): element tid*4 + 1024 j + e of the chunk goes to
+// x[4 j + e] of thread tid (coalesced float4 pieces when VEC4).  Loads past
+// the chunk's end are clamped to its last element (every load stays in
+// bounds) and the values are then replaced by -inf.
+template <bool VEC4>
+__device__ __forceinline__ void chunk_load(const float* __restrict__ src, int len, float (&x)[PER_THREAD]) {
+  const int tid = threadIdx.x;
+  if (VEC4) {
     const float4* s4 = reinterpret_cast<const float4*>(src);
+    const int n4 = len >> 2;  // V is a multiple of 4
 #pragma unroll
     for (int j = 0; j < PER_THREAD / 4; ++j) {
-      const float4 v = s4[j * TOPM_THREADS + tid];
+      const float4 v = s4[min(j * TOPM_THREADS + tid, n4 - 1)];
       x[4 * j] = v.x;
       x[4 * j + 1] = v.y;
       x[4 * j + 2] = v.z;
@@ -73,237 +122,196 @@ __device__ __forceinline__ void topm_chunk_body(const float* __restrict__ src, i
 #pragma unroll
     for (int j = 0; j < PER_THREAD / 4; ++j)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int i = (j * TOPM_THREADS + tid) * 4 + e;
-        x[4 * j + e] = i < len ? src[i] : -INFINITY;
-      }
+      for (int e = 0; e < 4; ++e) x[4 * j + e] = src[min((j * TOPM_THREADS + tid) * 4 + e, len - 1)];
   }
-  auto idx_of = [&](int q) { return ((q >> 2) * TOPM_THREADS + tid) * 4 + (q & 3); };
-  float vmax = -INFINITY;
-  uint32_t kmax = 0;
+  if (len < TOPM_CHUNK) {
+    const int lim = len - 4 * tid;
 #pragma unroll
-  for (int q = 0; q < PER_THREAD; ++q) {
-    vmax = fmaxf(vmax, x[q]);
-    if (FULL || idx_of(q) < len) kmax = max(kmax, f32_key(x[q]));
-  }
-  // 2. threshold: in each wave the ceil(Mc/4)-th largest lane maximum; the
-  //    smallest of the four bounds the chunk's Mc-th largest key from below
-  //    (at least 4 ceil(Mc/4) >= Mc threads have a maximum at or above it)
-  const int m4 = (Mc + 3) >> 2;
-  const uint32_t sorted = wave_sort_desc_u32(kmax);
-  const uint32_t wbound = (uint32_t)__builtin_amdgcn_readlane((int)sorted, m4 - 1);
-  const float wmax = wave_max_dpp(vmax);
-  if (lane == 0) {
-    wb[wv] = wbound;
-    red[wv] = wmax;
-  }
-  if (tid == 0) *sel_count = 0;
-  __syncthreads();
-  const uint32_t tau = min(min(wb[0], wb[1]), min(wb[2], wb[3]));
-  const float vm = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));  // the chunk's max value
-#pragma unroll
-  for (int q = 0; q < PER_THREAD; ++q) {
-    const uint32_t k = f32_key(x[q]);
-    if ((FULL || idx_of(q) < len) && k >= tau) {
-      const int slot = atomicAdd(sel_count, 1);
-      if (slot < FAST_CAP) sel[slot] = cand_pack(k, (uint32_t)(c0 + idx_of(q)));
-    }
-  }
-  __syncthreads();
-  const int cnt = *sel_count;
-  if (cnt > FAST_CAP) {
-    // too many keys at the threshold (equal values): topm_fallback_kernel
-    // redoes this chunk exactly
-    if (tid == 0) *out_stat_p = make_float4(0.f, 0.f, 0.f, __int_as_float(-1));
-    return;
-  }
-  // 3. rank the candidates exactly (composite keys are unique)
-  uint64_t mine[FAST_CAP / TOPM_THREADS];
-  int rk[FAST_CAP / TOPM_THREADS];
-#pragma unroll
-  for (int u = 0; u < FAST_CAP / TOPM_THREADS; ++u) {
-    const int e = tid + u * TOPM_THREADS;
-    mine[u] = e < cnt ? sel[e] : 0ull;
-    rk[u] = 0;
-  }
-  if (tid == 0 && (cnt & 1)) sel[cnt] = 0ull;  // pad to pairs (0 ranks below every key)
-  __syncthreads();
-  const ulonglong2* s2 = reinterpret_cast<const ulonglong2*>(sel);
-  if (cnt <= TOPM_THREADS) {
-    for (int i = 0; i < (cnt + 1) / 2; ++i) {
-      const ulonglong2 o = s2[i];
-      rk[0] += (o.x > mine[0]) + (o.y > mine[0]);
-    }
-  } else {
-    for (int i = 0; i < (cnt + 1) / 2; ++i) {
-      const ulonglong2 o = s2[i];
-#pragma unroll
-      for (int u = 0; u < FAST_CAP / TOPM_THREADS; ++u) rk[u] += (o.x > mine[u]) + (o.y > mine[u]);
-    }
-  }
-  __syncthreads();
-#pragma unroll
-  for (int u = 0; u < FAST_CAP / TOPM_THREADS; ++u) {
-    const int e = tid + u * TOPM_THREADS;
-    if (e < cnt && rk[u] < Mc) sel[rk[u]] = mine[u];  // ranks < Mc are distinct
-  }
-  __syncthreads();
-  // 4. the chunk's list, sorted (value desc, id asc), zero padded to M
-  if (tid < M) out_list[tid] = tid < Mc ? sel[tid] : 0ull;
-
-  // 5. LSE statistics: the chunk's sum of exp(x/T - m), and the same sum over
-  //    its left-out tokens as the chunk sum minus the selected terms (the
-  //    selected values are the largest, so the difference keeps the tail to
-  //    within rounding of the chunk sum)
-  const float m = vm / T;
-  const float l2t = 1.4426950408889634f / T;  // exp(y / T) = exp2(y * log2(e) / T)
-  float s_all = 0.f;
-  if (vm > -INFINITY) {
-#pragma unroll
-    for (int q = 0; q < PER_THREAD; ++q) s_all += __builtin_amdgcn_exp2f((x[q] - vm) * l2t);  // -inf adds 0
-  }
-  s_all = wave_sum_dpp(s_all);
-  float s_sel = 0.f;
-  if (wv == 0) {
-    const float e = (lane < Mc && vm > -INFINITY) ? __builtin_amdgcn_exp2f((key_f32(cand_key(sel[lane])) - vm) * l2t)
-                                                  : 0.f;
-    s_sel = wave_sum_dpp(e);
-  }
-  __syncthreads();
-  if (lane == 0) red[wv] = s_all;
-  __syncthreads();
-  if (tid == 0) {
-    const float tot = (red[0] + red[1]) + (red[2] + red[3]);
-    *out_stat_p = make_float4(m, tot, fmaxf(tot - s_sel, 0.f), __int_as_float(Mc));
+    for (int q = 0; q < PER_THREAD; ++q)
+      if (!(((q >> 2) * (4 * TOPM_THREADS) + (q & 3)) < lim)) x[q] = -INFINITY;
   }
 }
 
+// One block per item.  The selection works on the fp32 values with float
+// compares (a key per element only for the few candidates): per element a
+// max, a compare with the threshold and one exp.
+template <bool VEC4>
 __global__ __launch_bounds__(TOPM_THREADS) void topm_chunk_kernel(
     const float* __restrict__ logits, int V, int S, int M, float T,
     uint64_t* __restrict__ out_cand, float4* __restrict__ out_stat) {
-  __shared__ __attribute__((aligned(16))) uint64_t sel[FAST_CAP + 2];
-  __shared__ uint32_t wb[4];
-  __shared__ float red[4];
-  __shared__ int sel_count;
-  const int c = blockIdx.x;
-  const int row = blockIdx.y;
-  const int c0 = c * TOPM_CHUNK;
-  const int len = min(TOPM_CHUNK, V - c0);
-  const int Mc = min(M, len);
+  __shared__ ChunkLds L;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int item = blockIdx.x;
+  const int row = item / S, c = item - row * S;
+  const int c0 = c * TOPM_CHUNK, len = min(TOPM_CHUNK, V - c0), Mc = min(M, len);
   const float* src = logits + (size_t)row * (size_t)V + c0;
-  uint64_t* list = out_cand + ((size_t)row * S + c) * M;
-  float4* stat = out_stat + (size_t)row * S + c;
-  if ((V & 3) == 0 && len == TOPM_CHUNK)
-    topm_chunk_body<true>(src, len, c0, Mc, M, T, list, stat, sel, wb, red, &sel_count);
-  else
-    topm_chunk_body<false>(src, len, c0, Mc, M, T, list, stat, sel, wb, red, &sel_count);
-}
-
-// Exact per-chunk selection for the chunks the fast path could not rank
-// (more than FAST_CAP keys at or above its threshold: many equal values).
-// Every other block returns at once.  3-pass radix select (12, 12, 8 bits) of
-// the Mc-th largest key over the chunk in LDS, ties at the threshold taken in
-// id order.
-__global__ __launch_bounds__(TOPM_THREADS) void topm_fallback_kernel(
-    const float* __restrict__ logits, int V, int S, int M, float T,
-    uint64_t* __restrict__ out_cand, float4* __restrict__ out_stat) {
-  const int c = blockIdx.x, row = blockIdx.y;
-  if (__float_as_int(out_stat[(size_t)row * S + c].w) != -1) return;
-  __shared__ uint32_t keys[TOPM_CHUNK];
-  __shared__ uint32_t hist[HBINS];
-  __shared__ uint64_t sel[DT_TOPM_MAX];
-  __shared__ float red[4];
-  __shared__ int ired[4];
-  __shared__ int found_digit, found_above, sel_count, tie_last_s;
-  const int tid = threadIdx.x;
-  const int c0 = c * TOPM_CHUNK;
-  const int len = min(TOPM_CHUNK, V - c0);
-  const int Mc = min(M, len);
-  const float* src = logits + (size_t)row * (size_t)V + c0;
-  float vmax = -INFINITY;
-  for (int i = tid; i < len; i += TOPM_THREADS) {
-    const float x = src[i];
-    keys[i] = f32_key(x);
-    vmax = fmaxf(vmax, x);
-  }
-  const float m = block_max<TOPM_THREADS>(vmax, red) / T;
-  uint32_t prefix = 0, pmask = 0;
-  int need = Mc;
+  float x[PER_THREAD];
+  chunk_load<VEC4>(src, len, x);
+  // element q of this thread is chunk element 4 tid + off(q)
+  auto off = [](int q) { return (q >> 2) * (4 * TOPM_THREADS) + (q & 3); };
+  const uint32_t id0 = (uint32_t)(c0 + 4 * tid);
+  // 1. threshold: in each wave the ceil(Mc/4)-th largest lane maximum; the
+  //    smallest of the four bounds the chunk's Mc-th largest value from below
+  //    (at least 4 ceil(Mc/4) >= Mc threads have a maximum at or above it)
+  float vmax = x[0];
 #pragma unroll
-  for (int pass = 0; pass < 3; ++pass) {
-    const int sh = pass == 0 ? 20 : (pass == 1 ? 8 : 0);
-    const int width = pass == 2 ? 8 : 12;
-    const uint32_t dmask = (1u << width) - 1u;
-    const int nb = 1 << width;
-    for (int i = tid; i < nb; i += TOPM_THREADS) hist[i] = 0;
-    __syncthreads();
-    for (int i = tid; i < len; i += TOPM_THREADS) {
-      const uint32_t k = keys[i];
-      if ((k & pmask) == prefix) atomicAdd(&hist[(k >> sh) & dmask], 1u);
-    }
-    __syncthreads();
-    const int per = nb / TOPM_THREADS;
-    int mine = 0;
-    for (int b = 0; b < per; ++b) mine += (int)hist[tid * per + b];
-    int above = block_suffix_excl<TOPM_THREADS>(mine, ired);
-    for (int b = per - 1; b >= 0; --b) {
-      const int h = (int)hist[tid * per + b];
-      if (above < need && above + h >= need) {
-        found_digit = tid * per + b;
-        found_above = above;
+  for (int q = 1; q < PER_THREAD; ++q) vmax = fmaxf(vmax, x[q]);  // NaN is dropped
+  const uint32_t kmax = f32_key(vmax);
+  const uint32_t wbound = wave_kth_largest(kmax, (Mc + 3) >> 2);
+  const uint32_t wtop = wave_max_key(kmax);
+  if (lane == 0) {
+    L.wb[wv] = wbound;
+    L.wm[wv] = wtop;
+  }
+  if (tid == 0) L.sel_count = 0;
+  __syncthreads();
+  const uint32_t tau = min(min(L.wb[0], L.wb[1]), min(L.wb[2], L.wb[3]));
+  const uint32_t ktop = max(max(L.wm[0], L.wm[1]), max(L.wm[2], L.wm[3]));
+  const float vm = ktop > 0x007FFFFFu ? key_f32(ktop) : -INFINITY;  // the chunk's largest value
+  // a bound above -inf: the candidates are the values >= tau_f (no -inf, no
+  // NaN, no padding); else the exact path
+  const bool fast = tau > 0x007FFFFFu;
+  const float tau_f = fast ? key_f32(tau) : INFINITY;
+  // 2. compaction of the candidates: count, one LDS atomic per wave, write
+  int n = 0;
+#pragma unroll
+  for (int q = 0; q < PER_THREAD; ++q) n += x[q] >= tau_f ? 1 : 0;
+  const int incl = wave_add_scan_incl(n);
+  const int wtot = __builtin_amdgcn_readlane(incl, 63);
+  int base = 0;
+  if (lane == 0 && wtot > 0) base = atomicAdd(&L.sel_count, wtot);
+  int pos = __builtin_amdgcn_readfirstlane(base) + incl - n;
+  if (wtot > 0) {
+#pragma unroll
+    for (int q = 0; q < PER_THREAD; ++q) {
+      const bool h = x[q] >= tau_f;
+      if (__ballot(h)) {  // wave-uniform: most elements of a wave have no candidate
+        if (h) {
+          if (pos < FAST_CAP) L.sel[pos] = cand_pack(f32_key(x[q]), id0 + (uint32_t)off(q));
+          ++pos;
+        }
       }
-      above += h;
     }
-    __syncthreads();
-    need -= found_above;
-    prefix |= (uint32_t)found_digit << sh;
-    pmask |= dmask << sh;
-    __syncthreads();
   }
-  const uint32_t kstar = prefix;
-  if (tid == 0) {
-    sel_count = 0;
-    tie_last_s = -1;
+  // 3. the chunk's sum of exp(x/T - m) (-inf adds 0); each term is
+  //    exp2(fma(x, log2(e)/T, -mb)), the same expression as the listed terms'
+  //    below, so that the tail (chunk sum minus listed terms) cancels them
+  //    term for term
+  const float l2t = 1.4426950408889634f / T;  // exp(y / T) = exp2(y * log2(e) / T)
+  const float mb = vm * l2t;
+  float s_all = 0.f;
+  if (vm > -INFINITY) {
+#pragma unroll
+    for (int q = 0; q < PER_THREAD; ++q) s_all += __builtin_amdgcn_exp2f(__builtin_fmaf(x[q], l2t, -mb));
   }
+  s_all = wave_sum_dpp(s_all);
+  if (lane == 0) L.ws[wv] = s_all;
   __syncthreads();
-  for (int i = tid; i < len; i += TOPM_THREADS) {
-    const uint32_t k = keys[i];
-    if (k > kstar) sel[atomicAdd(&sel_count, 1)] = cand_pack(k, (uint32_t)(c0 + i));
-  }
-  __syncthreads();
-  int slot = Mc - need;
-  for (int b0 = 0; b0 < len && need > 0; b0 += TOPM_THREADS) {
-    const int i = b0 + tid;
-    const bool f = i < len && keys[i] == kstar;
-    int total;
-    const int r = block_rank_flag<TOPM_THREADS>(f, ired, &total);
-    if (f && r < need) {
-      sel[slot + r] = cand_pack(kstar, (uint32_t)(c0 + i));
-      if (r == need - 1) tie_last_s = i;
+  const int cnt = L.sel_count;
+  if (fast && cnt <= FAST_CAP) {
+    // 4. rank the candidates exactly (composite keys are unique)
+    uint64_t mine[FAST_CAP / TOPM_THREADS];
+    int rk[FAST_CAP / TOPM_THREADS];
+#pragma unroll
+    for (int u = 0; u < FAST_CAP / TOPM_THREADS; ++u) {
+      const int e = tid + u * TOPM_THREADS;
+      mine[u] = e < cnt ? L.sel[e] : ~0ull;
+      rk[u] = 0;
     }
-    const int took = min(total, need);
-    slot += took;
-    need -= took;
+    const ulonglong2* s2 = reinterpret_cast<const ulonglong2*>(L.sel);
+    const int pairs = cnt >> 1;
+    if (cnt <= TOPM_THREADS) {
+      for (int i = 0; i < pairs; ++i) {
+        const ulonglong2 o = s2[i];
+        rk[0] += (o.x > mine[0]) + (o.y > mine[0]);
+      }
+      if (cnt & 1) rk[0] += L.sel[cnt - 1] > mine[0];
+    } else {
+      for (int i = 0; i < pairs; ++i) {
+        const ulonglong2 o = s2[i];
+#pragma unroll
+        for (int u = 0; u < FAST_CAP / TOPM_THREADS; ++u) rk[u] += (o.x > mine[u]) + (o.y > mine[u]);
+      }
+      if (cnt & 1) {
+        const uint64_t o = L.sel[cnt - 1];
+#pragma unroll
+        for (int u = 0; u < FAST_CAP / TOPM_THREADS; ++u) rk[u] += o > mine[u];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < FAST_CAP / TOPM_THREADS; ++u) {
+      const int e = tid + u * TOPM_THREADS;
+      if (e < cnt && rk[u] < Mc) L.list[rk[u]] = mine[u];  // ranks < Mc are distinct
+    }
+  } else {
+    // 4'. exact select (many equal values, or fewer than Mc finite ones):
+    //     radix passes of 8 bits over the chunk, read again from memory, find
+    //     the Mc-th largest key kstar; the keys above it and the first `need`
+    //     keys equal to it (lowest ids) form the list
+    uint32_t* hist = reinterpret_cast<uint32_t*>(L.sel);
+    uint32_t prefix = 0, pmask = 0;
+    int need = Mc;
+    for (int sh = 24; sh >= 0; sh -= 8) {
+      hist[tid] = 0;
+      __syncthreads();
+      for (int i = tid; i < len; i += TOPM_THREADS) {
+        const uint32_t k = f32_key(src[i]);
+        if ((k & pmask) == prefix) atomicAdd(&hist[(k >> sh) & 255u], 1u);
+      }
+      __syncthreads();
+      const int h = (int)hist[tid];
+      const int above = block_suffix_excl<TOPM_THREADS>(h, L.wi);  // keys with a larger digit
+      if (above < need && above + h >= need) {
+        L.digit = tid;
+        L.above = above;
+      }
+      __syncthreads();
+      need -= L.above;
+      prefix |= (uint32_t)L.digit << sh;
+      pmask |= 255u << sh;
+    }
+    const uint32_t kstar = prefix;
+    if (tid == 0) L.sel_count = 0;
     __syncthreads();
-  }
-  const int tie_last = tie_last_s;
-  if (tid < 64) {
-    uint64_t v = tid < Mc ? sel[tid] : 0ull;
-    v = wave_sort_desc_u64(v);
-    if (tid < M) out_cand[((size_t)row * S + c) * M + tid] = v;
-  }
-  float s_all = 0.f, s_tail = 0.f;
-  if (m > -INFINITY) {
     for (int i = tid; i < len; i += TOPM_THREADS) {
-      const uint32_t k = keys[i];
-      const float e = __expf(key_f32(k) / T - m);
-      s_all += e;
-      if (!(k > kstar || (k == kstar && i <= tie_last))) s_tail += e;
+      const uint32_t k = f32_key(src[i]);
+      if (k > kstar) L.list[atomicAdd(&L.sel_count, 1)] = cand_pack(k, (uint32_t)(c0 + i));
+    }
+    int slot = Mc - need, left = need;  // Mc - need keys are above kstar
+    for (int b0 = 0; b0 < len && left > 0; b0 += TOPM_THREADS) {
+      const int i = b0 + tid;
+      const bool f = i < len && f32_key(src[min(i, len - 1)]) == kstar;
+      int tot;
+      const int r = block_prefix_excl(f ? 1 : 0, L.wi, &tot);
+      if (f && r < left) L.list[slot + r] = cand_pack(kstar, (uint32_t)(c0 + i));
+      const int took = min(tot, left);
+      slot += took;
+      left -= took;
+    }
+    __syncthreads();
+    if (wv == 0) {
+      uint64_t v = lane < Mc ? L.list[lane] : 0ull;
+      v = wave_sort_desc_u64(v);
+      L.list[lane] = v;
     }
   }
-  s_all = block_sum<TOPM_THREADS>(s_all, red);
-  s_tail = block_sum<TOPM_THREADS>(s_tail, red);
-  if (tid == 0) out_stat[(size_t)row * S + c] = make_float4(m, s_all, s_tail, __int_as_float(Mc));
+  __syncthreads();
+  // 5. the list, zero padded to M, and the statistics (m = max / T, the
+  //    chunk's sum of exp(x/T - m), the same sum over its tokens left out of
+  //    the list as the chunk sum minus the listed terms -- the listed values
+  //    are the largest, so the difference keeps the tail to within rounding
+  //    of the chunk sum -- and Mc)
+  uint64_t* out_list = out_cand + (size_t)item * M;
+  if (tid < M) out_list[tid] = tid < Mc ? L.list[tid] : 0ull;
+  if (wv == 0) {
+    const float e = (lane < Mc && vm > -INFINITY)
+                        ? __builtin_amdgcn_exp2f(__builtin_fmaf(key_f32(cand_key(L.list[lane])), l2t, -mb)) : 0.f;
+    const float s_sel = wave_sum_dpp(e);
+    if (lane == 0) {
+      const float tot = (L.ws[0] + L.ws[1]) + (L.ws[2] + L.ws[3]);
+      out_stat[item] = make_float4(vm / T, tot, fmaxf(tot - s_sel, 0.f), __int_as_float(Mc));
+    }
+  }
 }
 
 // Number of entries of a descending list greater than `key`.
@@ -478,10 +486,15 @@ hipError_t launch_topm(const float* logits, int rows, int V, int M, float T, uin
                        int32_t* tokrank, int32_t* user_ids, float* user_vals, float* user_lse,
                        hipStream_t stream) {
   const int S = topm_chunks(V);
-  hipLaunchKernelGGL(topm_chunk_kernel, dim3(S, rows), dim3(TOPM_THREADS), 0, stream, logits, V, S, M,
-                     T, chunk_cand, chunk_stat);
-  hipLaunchKernelGGL(topm_fallback_kernel, dim3(S, rows), dim3(TOPM_THREADS), 0, stream, logits, V, S, M,
-                     T, chunk_cand, chunk_stat);
+  const int items = rows * S;
+  if (items == 0) return hipSuccess;
+  const bool vec4 = (V % 4 == 0) && (reinterpret_cast<uintptr_t>(logits) % 16 == 0);
+  if (vec4)
+    hipLaunchKernelGGL(topm_chunk_kernel<true>, dim3(items), dim3(TOPM_THREADS), 0, stream, logits, V, S, M, T,
+                       chunk_cand, chunk_stat);
+  else
+    hipLaunchKernelGGL(topm_chunk_kernel<false>, dim3(items), dim3(TOPM_THREADS), 0, stream, logits, V, S, M, T,
+                       chunk_cand, chunk_stat);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   return launch_topm_merge(chunk_cand, chunk_stat, rows, S, M, T, ids, vals, lse, tail, tokrank,
