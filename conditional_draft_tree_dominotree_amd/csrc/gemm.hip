@@ -9,9 +9,16 @@
 // the correction's first projection (H_d is shared by every path: DominoTree
 // technical summary, Componenti Core 1).
 //
-// bf16: a 128 x 128 block tile, 256 threads (2 x 2 waves of 64 x 64), MFMA
-// v_mfma_f32_32x32x16_bf16 with operands staged through LDS 32 k at a time.
-// fp32: one thread per output element (small shapes only).
+// bf16, large outputs (the LM head H W_lm, and the fold E W_ih^T): a 256 x 256
+// block tile, 256 threads (2 x 2 waves of 128 x 128, sixteen 32 x 32
+// accumulator tiles per wave), v_mfma_f32_32x32x16_bf16.  Operands go from
+// global memory straight into a four-stage LDS ring (32 k per stage, three
+// stages in flight while the fourth is read), one barrier per stage.  Blocks
+// are mapped to tiles XCD by XCD, so the blocks on one XCD (and its L2) cover
+// a contiguous run of tiles, those that share a tile of the larger operand
+// together.
+// bf16, other shapes: a 128 x 128 block tile (2 x 2 waves of 64 x 64), 32 k
+// per stage.  fp32: one thread per output element (small shapes only).
 #include "common.h"
 #include "kernels.h"
 
@@ -99,6 +106,164 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(const uint16_t* __restri
     }
 }
 
+constexpr int BT = 256;    // big tile (M and N)
+constexpr int BK = 32;     // k per stage: one 64-byte row piece per operand row
+constexpr int BNS = 4;     // stages in the LDS ring (three in flight while one is read)
+constexpr int BOPND = BT * BK;          // bf16 per operand per stage (16 KB)
+constexpr int BSTAGE = 2 * BOPND;       // bf16 per stage (A rows, then B rows)
+constexpr size_t BIG_LDS = (size_t)BNS * BSTAGE * sizeof(uint16_t);  // 131072 B
+
+typedef __attribute__((address_space(3))) void* lds_ptr;
+typedef const __attribute__((address_space(1))) void* glb_ptr;
+
+// LDS layout of one operand stage: row r (0..255) at r * 64 bytes, its four
+// 16-byte k pieces permuted by r's swizzle: piece c sits in slot c ^ swz(r),
+// swz(r) = ((r >> 1) & 3) ^ 3 ((r >> 3) & 1).  The 16-byte MFMA operand reads
+// of 16 consecutive rows then fall in 16 distinct 16-byte bank groups, and of
+// any 8 aligned rows in 8.
+__device__ __forceinline__ int big_swz(int r) { return ((r >> 1) & 3) ^ (((r >> 3) & 1) * 3); }
+
+// s_waitcnt vmcnt(n), the other counters left alone (gfx9 encoding)
+template <int n>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(n >= 0 && n < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (n & 15) | ((n >> 4) << 14));
+}
+
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_bf16_big_kernel(
+    const uint16_t* __restrict__ A, const uint16_t* __restrict__ Bt, const float* __restrict__ bias,
+    float* __restrict__ C, int M, int N, int K, int ldc, int tm, int tiles, int per_xcd) {
+  extern __shared__ __attribute__((aligned(16))) uint16_t glds[];
+  // blockIdx.x runs round-robin over the 8 XCDs: XCD x takes tiles
+  // [x per_xcd, (x + 1) per_xcd), the dimension with fewer tiles fastest (the
+  // blocks on an XCD then share the tile of the larger operand)
+  const int t = (int)(blockIdx.x & 7) * per_xcd + (int)(blockIdx.x >> 3);
+  if (t >= tiles) return;
+  const int tn = tiles / tm;
+  const int m0 = (tm <= tn ? t % tm : t / tn) * BT, n0 = (tm <= tn ? t / tm : t % tn) * BT;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = (w >> 1) * 128, wn = (w & 1) * 128;
+
+  // Operand loads go straight to LDS (global_load_lds_dwordx4): one wave
+  // instruction fills 1 KB = 16 rows x 64 bytes, lane l the slot (l & 3) of
+  // row l >> 2, so it fetches the k piece (l & 3) ^ swz(row).  Wave w fills
+  // row blocks 4w..4w+3 of each operand; rows past the matrix repeat its last
+  // row (their outputs are not stored).
+  const int lr = lane >> 2, lk = 8 * ((lane & 3) ^ big_swz(lr));
+  const uint16_t* a_base = A + (size_t)m0 * K;
+  const uint16_t* b_base = Bt + (size_t)n0 * K;
+  uint32_t a_off[4], b_off[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int r = 16 * (4 * w + q) + lr;
+    a_off[q] = (uint32_t)((min(m0 + r, M - 1) - m0) * K + lk);
+    b_off[q] = (uint32_t)((min(n0 + r, N - 1) - n0) * K + lk);
+  }
+  const int nk = K / BK;
+  auto issue = [&](int stage) {
+    // the stages past the last one load the last k block again (uniform
+    // wait counts; the buffer they fill is not read any more)
+    const int k0 = min(stage, nk - 1) * BK;
+    uint16_t* dst = glds + (stage % BNS) * BSTAGE + (4 * w) * 16 * BK;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      __builtin_amdgcn_global_load_lds((glb_ptr)(a_base + a_off[q] + k0), (lds_ptr)(dst + q * 16 * BK), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((glb_ptr)(b_base + b_off[q] + k0), (lds_ptr)(dst + BOPND + q * 16 * BK), 16,
+                                       0, 0);
+    }
+  };
+  // operand reads: lane reads row (lane & 31) of a 32-row block, k piece
+  // 2 h + (lane >> 5) (h = 0, 1: the two 16-k halves of a stage), at its
+  // swizzled slot
+  const int fr = lane & 31;
+  const int p0 = 8 * ((lane >> 5) ^ big_swz(fr & 15)), p1 = p0 ^ 16;
+  auto frags = [&](int stage, bf16x8 (&af)[2][4], bf16x8 (&bf)[2][4]) {
+    const uint16_t* sa = glds + (stage % BNS) * BSTAGE;
+    const uint16_t* sb = sa + BOPND;
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        af[h][x] = *reinterpret_cast<const bf16x8*>(&sa[(wm + 32 * x + fr) * BK + (h ? p1 : p0)]);
+        bf[h][x] = *reinterpret_cast<const bf16x8*>(&sb[(wn + 32 * x + fr) * BK + (h ? p1 : p0)]);
+      }
+  };
+  // this thread's loads of `stage` are in LDS (two later stages still in
+  // flight), then the barrier: every thread's are.  A bare s_barrier:
+  // __syncthreads' release fence would wait for every load in flight.  The
+  // empty asm statements keep memory accesses on their side of it.
+  auto stage_ready = [&]() {
+    __builtin_amdgcn_sched_barrier(0);
+    wait_vm<16>();
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  floatx16 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+
+  // Pipeline: while the MFMAs of stage i run, stage i + 1 is made ready, the
+  // loads of stage i + 4 go out into the buffer stage i used (its operands
+  // are in registers by then: the first MFMA of stage i waited for them) and
+  // the operands of stage i + 1 are read.
+  issue(0);
+  issue(1);
+  issue(2);
+  stage_ready();
+  issue(3);
+  bf16x8 fa[2][2][4], fb[2][2][4];
+  frags(0, fa[0], fb[0]);
+  auto step = [&](int i, bf16x8 (&ca)[2][4], bf16x8 (&cb)[2][4], bf16x8 (&na)[2][4], bf16x8 (&nb)[2][4]) {
+#pragma unroll
+    for (int y = 0; y < 4; ++y) acc[0][y] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ca[0][0], cb[0][y], acc[0][y], 0, 0, 0);
+    stage_ready();
+    issue(i + 4);
+    frags(i + 1, na, nb);
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int x = 0; x < 4; ++x)
+#pragma unroll
+        for (int y = 0; y < 4; ++y)
+          if (h || x) acc[x][y] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ca[h][x], cb[h][y], acc[x][y], 0, 0, 0);
+    // schedule: the stage's loads, then its LDS reads spread over the MFMAs
+#pragma unroll
+    for (int g = 0; g < 8; ++g) {
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 12, 0);
+  };
+  for (int i = 0; i < nk; i += 2) {
+    step(i, fa[0], fb[0], fa[1], fb[1]);
+    step(i + 1, fa[1], fb[1], fa[0], fb[0]);
+  }
+  wait_vm<0>();        // no load may still be writing LDS when the block ends
+  // D layout: lane holds column (lane & 31), rows 8 (e / 4) + 4 (lane >> 5) + (e % 4)
+#pragma unroll
+  for (int y = 0; y < 4; ++y) {
+    const int col = n0 + wn + 32 * y + fr;
+    if (col >= N) continue;
+    const float bv = bias ? bias[col] : 0.f;
+#pragma unroll
+    for (int x = 0; x < 4; ++x)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int row = m0 + wm + 32 * x + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+        if (row < M) C[(size_t)row * ldc + col] = acc[x][y][e] + bv;
+      }
+  }
+}
+
 __global__ void gemm_f32_kernel(const float* __restrict__ A, const float* __restrict__ Bt,
                                 const float* __restrict__ bias, float* __restrict__ C, int M, int N,
                                 int K, int ldc) {
@@ -154,6 +319,16 @@ __global__ __launch_bounds__(256) void gemm_bf16_small_kernel(const uint16_t* __
 hipError_t launch_gemm_bf16(const uint16_t* A, const int32_t* rows, const uint16_t* Bt, const float* bias,
                             float* C, int M, int N, int K, int ldc, hipStream_t stream) {
   if (rows != nullptr || (K & 7) != 0) return hipErrorInvalidValue;
+  const long big_tiles = (long)((N + BT - 1) / BT) * ((M + BT - 1) / BT);
+  if (K % (2 * BK) == 0 && K >= 2 * BK && big_tiles >= 256 && (size_t)BT * K < (1u << 31)) {
+    const int tm = (M + BT - 1) / BT, tiles = (int)big_tiles, per_xcd = (tiles + 7) / 8;
+    hipError_t e = hipFuncSetAttribute((const void*)gemm_bf16_big_kernel,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)BIG_LDS);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(gemm_bf16_big_kernel, dim3(8 * per_xcd), dim3(256), BIG_LDS, stream, A, Bt, bias, C, M,
+                       N, K, ldc, tm, tiles, per_xcd);
+    return hipGetLastError();
+  }
   const long tiles = (long)((N + GT - 1) / GT) * ((M + GT - 1) / GT);
   if (tiles < 256) {
     dim3 grid((N + 31) / 32, (M + 31) / 32);
