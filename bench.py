@@ -242,7 +242,7 @@ def main():
         # the LM head: a dense bf16 contraction, priced against the MFMA peak
         flops = 2.0 * spec.B * spec.D * spec.V * spec.h
         tf = flops / (phases[0] * 1e-3) / 1e12
-        res["roofline_lm_head"] = {"kernel": "gemm_bf16_kernel (H W_lm)", "bound": "mfma", "achieved": tf,
+        res["roofline_lm_head"] = {"kernel": "gemm_bf16_big_kernel (H W_lm)", "bound": "mfma", "achieved": tf,
                                    "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                                    "frac": tf / BF16_PEAK_TFLOPS, "traffic": None,
                                    "algorithmic_flops": flops}

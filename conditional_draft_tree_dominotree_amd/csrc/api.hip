@@ -50,7 +50,8 @@ struct dt_handle {
   float* b_hh = nullptr;    // [3 ds] or null
   void* w1h_t = nullptr;    // [r, h]
   void* w2t = nullptr;      // [V, r]
-  void* wlm_t = nullptr;    // [V, h] or null
+  void* wlm_t = nullptr;    // W_lm^T: tiled for the LM-head GEMM (wlm_tiled) or [V, h]; or null
+  bool wlm_tiled = false;
   float* logits = nullptr;  // [max_batch, D, V] base logits computed by the LM head
   int n_tiles = 0;
   // workspace
@@ -227,8 +228,16 @@ dt_status dt_create(dt_handle** out, const dt_dims* dims, const dt_weights* w, c
   HIPB(dt::launch_transpose(w->w2, h->w2t, r, V, (int)esz, stream));
   if (w->w_lm) {
     if (!h->bf16) return bail(fail(DT_EUNSUPPORTED, "the LM head needs bf16 weights"));
-    ALLOC(h->wlm_t, (size_t)V * hd * esz);
-    HIPB(dt::launch_transpose(w->w_lm, h->wlm_t, hd, V, (int)esz, stream));
+    if (dt::gemm_b_tiles_ok(V, hd)) {
+      // W_lm in the LM-head GEMM's tile order: each k stage of a 256-column
+      // tile is one contiguous 16 KB piece
+      h->wlm_tiled = true;
+      ALLOC(h->wlm_t, dt::gemm_b_tiles_elems(V, hd) * esz);
+      HIPB(dt::launch_pack_b_tiles((const uint16_t*)w->w_lm, (uint16_t*)h->wlm_t, hd, V, stream));
+    } else {
+      ALLOC(h->wlm_t, (size_t)V * hd * esz);
+      HIPB(dt::launch_transpose(w->w_lm, h->wlm_t, hd, V, (int)esz, stream));
+    }
   }
 
   // workspace for max_batch and max_params
@@ -318,8 +327,12 @@ dt_status dt_build_trees(dt_handle* h, const dt_inputs* in, const dt_params* p, 
   // a0 (LM head, when no base logits are given), then a1: candidates and LSE
   if (!in->base_logits) {
     // L_base = H W_lm (Domino summary, 方法步骤详情), fp32 accumulate
-    HIPCHK(dt::launch_gemm_bf16((const uint16_t*)in->hidden, nullptr, (const uint16_t*)h->wlm_t, nullptr,
-                                h->logits, rows, V, d.hidden, V, stream));
+    if (h->wlm_tiled)
+      HIPCHK(dt::launch_gemm_bf16_btiled((const uint16_t*)in->hidden, (const uint16_t*)h->wlm_t, h->logits, rows, V,
+                                         d.hidden, V, stream));
+    else
+      HIPCHK(dt::launch_gemm_bf16((const uint16_t*)in->hidden, nullptr, (const uint16_t*)h->wlm_t, nullptr,
+                                  h->logits, rows, V, d.hidden, V, stream));
   }
   MARK(1);
   {

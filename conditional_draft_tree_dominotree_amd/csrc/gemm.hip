@@ -16,7 +16,8 @@
 // stages in flight while the fourth is read), one barrier per stage.  Blocks
 // are mapped to tiles XCD by XCD, so the blocks on one XCD (and its L2) cover
 // a contiguous run of tiles, those that share a tile of the larger operand
-// together.
+// together.  For the LM head, W_lm is pre-tiled once per handle so that each
+// stage of a B tile is one contiguous, already swizzled 16 KB piece.
 // bf16, other shapes: a 128 x 128 block tile (2 x 2 waves of 64 x 64), 32 k
 // per stage.  fp32: one thread per output element (small shapes only).
 #include "common.h"
@@ -130,6 +131,10 @@ __device__ __forceinline__ void wait_vm() {
   __builtin_amdgcn_s_waitcnt(0x0F70 | (n & 15) | ((n >> 4) << 14));
 }
 
+// BTILED: Bt is in the tiled order of launch_pack_b_tiles ([N / 256][K / 32]
+// blocks of 256 rows x 32 k, swizzled, rows past N zero), so each stage of a
+// B tile is one contiguous 16 KB piece; otherwise Bt is row-major [N, K].
+template <bool BTILED>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_bf16_big_kernel(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ Bt, const float* __restrict__ bias,
     float* __restrict__ C, int M, int N, int K, int ldc, int tm, int tiles, int per_xcd) {
@@ -151,25 +156,29 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   // row blocks 4w..4w+3 of each operand; rows past the matrix repeat its last
   // row (their outputs are not stored).
   const int lr = lane >> 2, lk = 8 * ((lane & 3) ^ big_swz(lr));
+  const int nk = K / BK;
   const uint16_t* a_base = A + (size_t)m0 * K;
-  const uint16_t* b_base = Bt + (size_t)n0 * K;
+  // tiled B: this tile's nk stage blocks, wave w's 4 KB of each, lane l's 16 bytes
+  const uint16_t* b_base = BTILED ? Bt + (size_t)(n0 / BT) * nk * BOPND + (4 * w) * 16 * BK + 8 * lane
+                                  : Bt + (size_t)n0 * K;
   uint32_t a_off[4], b_off[4];
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const int r = 16 * (4 * w + q) + lr;
     a_off[q] = (uint32_t)((min(m0 + r, M - 1) - m0) * K + lk);
-    b_off[q] = (uint32_t)((min(n0 + r, N - 1) - n0) * K + lk);
+    b_off[q] = BTILED ? (uint32_t)(q * 16 * BK) : (uint32_t)((min(n0 + r, N - 1) - n0) * K + lk);
   }
-  const int nk = K / BK;
   auto issue = [&](int stage) {
     // the stages past the last one load the last k block again (uniform
     // wait counts; the buffer they fill is not read any more)
-    const int k0 = min(stage, nk - 1) * BK;
+    const int ks = min(stage, nk - 1);
+    const int k0 = ks * BK;
+    const int kb = BTILED ? ks * BOPND : k0;
     uint16_t* dst = glds + (stage % BNS) * BSTAGE + (4 * w) * 16 * BK;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       __builtin_amdgcn_global_load_lds((glb_ptr)(a_base + a_off[q] + k0), (lds_ptr)(dst + q * 16 * BK), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds((glb_ptr)(b_base + b_off[q] + k0), (lds_ptr)(dst + BOPND + q * 16 * BK), 16,
+      __builtin_amdgcn_global_load_lds((glb_ptr)(b_base + b_off[q] + kb), (lds_ptr)(dst + BOPND + q * 16 * BK), 16,
                                        0, 0);
     }
   };
@@ -189,13 +198,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         bf[h][x] = *reinterpret_cast<const bf16x8*>(&sb[(wn + 32 * x + fr) * BK + (h ? p1 : p0)]);
       }
   };
-  // this thread's loads of `stage` are in LDS (two later stages still in
-  // flight), then the barrier: every thread's are.  A bare s_barrier:
+  // this thread's loads of `stage` are in LDS (the BNS - 2 later stages
+  // still in flight), then the barrier: every thread's are.  A bare s_barrier:
   // __syncthreads' release fence would wait for every load in flight.  The
   // empty asm statements keep memory accesses on their side of it.
   auto stage_ready = [&]() {
     __builtin_amdgcn_sched_barrier(0);
-    wait_vm<16>();
+    wait_vm<8 * (BNS - 2)>();
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
@@ -211,21 +220,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
   // Pipeline: while the MFMAs of stage i run, stage i + 1 is made ready, the
-  // loads of stage i + 4 go out into the buffer stage i used (its operands
+  // loads of stage i + BNS go out into the buffer stage i used (its operands
   // are in registers by then: the first MFMA of stage i waited for them) and
   // the operands of stage i + 1 are read.
-  issue(0);
-  issue(1);
-  issue(2);
+#pragma unroll
+  for (int st = 0; st < BNS - 1; ++st) issue(st);
   stage_ready();
-  issue(3);
+  issue(BNS - 1);
   bf16x8 fa[2][2][4], fb[2][2][4];
   frags(0, fa[0], fb[0]);
   auto step = [&](int i, bf16x8 (&ca)[2][4], bf16x8 (&cb)[2][4], bf16x8 (&na)[2][4], bf16x8 (&nb)[2][4]) {
 #pragma unroll
     for (int y = 0; y < 4; ++y) acc[0][y] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ca[0][0], cb[0][y], acc[0][y], 0, 0, 0);
     stage_ready();
-    issue(i + 4);
+    issue(i + BNS);
     frags(i + 1, na, nb);
 #pragma unroll
     for (int h = 0; h < 2; ++h)
@@ -322,11 +330,11 @@ hipError_t launch_gemm_bf16(const uint16_t* A, const int32_t* rows, const uint16
   const long big_tiles = (long)((N + BT - 1) / BT) * ((M + BT - 1) / BT);
   if (K % (2 * BK) == 0 && K >= 2 * BK && big_tiles >= 256 && (size_t)BT * K < (1u << 31)) {
     const int tm = (M + BT - 1) / BT, tiles = (int)big_tiles, per_xcd = (tiles + 7) / 8;
-    hipError_t e = hipFuncSetAttribute((const void*)gemm_bf16_big_kernel,
+    hipError_t e = hipFuncSetAttribute((const void*)gemm_bf16_big_kernel<false>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)BIG_LDS);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(gemm_bf16_big_kernel, dim3(8 * per_xcd), dim3(256), BIG_LDS, stream, A, Bt, bias, C, M,
-                       N, K, ldc, tm, tiles, per_xcd);
+    hipLaunchKernelGGL(gemm_bf16_big_kernel<false>, dim3(8 * per_xcd), dim3(256), BIG_LDS, stream, A, Bt, bias, C,
+                       M, N, K, ldc, tm, tiles, per_xcd);
     return hipGetLastError();
   }
   const long tiles = (long)((N + GT - 1) / GT) * ((M + GT - 1) / GT);
@@ -337,6 +345,53 @@ hipError_t launch_gemm_bf16(const uint16_t* A, const int32_t* rows, const uint16
   }
   dim3 grid((N + GT - 1) / GT, (M + GT - 1) / GT);
   hipLaunchKernelGGL(gemm_bf16_kernel, grid, dim3(256), 0, stream, A, Bt, bias, C, M, N, K, ldc);
+  return hipGetLastError();
+}
+
+bool gemm_b_tiles_ok(int N, int K) { return K >= 2 * BK && K % (2 * BK) == 0 && (size_t)BT * K < (1u << 31) && N > 0; }
+
+hipError_t launch_gemm_bf16_btiled(const uint16_t* A, const uint16_t* Btiled, float* C, int M, int N, int K,
+                                   int ldc, hipStream_t stream) {
+  if (!gemm_b_tiles_ok(N, K) || M <= 0) return hipErrorInvalidValue;
+  const int tm = (M + BT - 1) / BT, tiles = tm * ((N + BT - 1) / BT), per_xcd = (tiles + 7) / 8;
+  hipError_t e = hipFuncSetAttribute((const void*)gemm_bf16_big_kernel<true>,
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)BIG_LDS);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(gemm_bf16_big_kernel<true>, dim3(8 * per_xcd), dim3(256), BIG_LDS, stream, A, Btiled,
+                     (const float*)nullptr, C, M, N, K, ldc, tm, tiles, per_xcd);
+  return hipGetLastError();
+}
+
+// Bt tiled from W [K, N] (row-major, the math layout x W): block (nt, s) holds
+// rows n = 256 nt .. 256 nt + 255 of W^T, k = 32 s .. 32 s + 31, row r at
+// r * 32 elements with its k piece c (8 elements) in slot c ^ big_swz(r);
+// rows past N are zero.  One thread per row of a block: 32 coalesced reads of
+// W's rows, 64 contiguous bytes written.
+__global__ __launch_bounds__(256) void pack_b_tiles_kernel(const uint16_t* __restrict__ W, uint16_t* __restrict__ out,
+                                                           int K, int N) {
+  const int nt = blockIdx.x, st = blockIdx.y, r = threadIdx.x;
+  const int n = nt * BT + r;
+  uint16_t v[BK];
+#pragma unroll
+  for (int k = 0; k < BK; ++k) v[k] = n < N ? W[(size_t)(st * BK + k) * N + n] : (uint16_t)0;
+  uint16_t* o = out + ((size_t)nt * (K / BK) + st) * BOPND + (size_t)r * BK;
+  const int sw = big_swz(r & 15);
+#pragma unroll
+  for (int c = 0; c < BK / 8; ++c) {
+    uint4 q;
+    q.x = v[8 * c + 0] | ((uint32_t)v[8 * c + 1] << 16);
+    q.y = v[8 * c + 2] | ((uint32_t)v[8 * c + 3] << 16);
+    q.z = v[8 * c + 4] | ((uint32_t)v[8 * c + 5] << 16);
+    q.w = v[8 * c + 6] | ((uint32_t)v[8 * c + 7] << 16);
+    *reinterpret_cast<uint4*>(o + 8 * (c ^ sw)) = q;
+  }
+}
+
+size_t gemm_b_tiles_elems(int N, int K) { return (size_t)((N + BT - 1) / BT) * BT * K; }
+
+hipError_t launch_pack_b_tiles(const uint16_t* W, uint16_t* out, int K, int N, hipStream_t stream) {
+  if (!gemm_b_tiles_ok(N, K)) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(pack_b_tiles_kernel, dim3((N + BT - 1) / BT, K / BK), dim3(256), 0, stream, W, out, K, N);
   return hipGetLastError();
 }
 

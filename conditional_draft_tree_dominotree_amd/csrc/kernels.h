@@ -29,6 +29,14 @@ hipError_t launch_nan_scan(const float* x, size_t n, int* flag, hipStream_t stre
 // with leading dimension ldc.
 hipError_t launch_gemm_bf16(const uint16_t* A, const int32_t* rows, const uint16_t* Bt, const float* bias,
                             float* C, int M, int N, int K, int ldc, hipStream_t stream);
+// The same product with Bt pre-tiled by launch_pack_b_tiles (from W = Bt^T,
+// [K, N] row-major); needs gemm_b_tiles_ok(N, K) (K a multiple of 64).  The
+// tiled copy holds gemm_b_tiles_elems(N, K) bf16.
+bool gemm_b_tiles_ok(int N, int K);
+size_t gemm_b_tiles_elems(int N, int K);
+hipError_t launch_pack_b_tiles(const uint16_t* W, uint16_t* out, int K, int N, hipStream_t stream);
+hipError_t launch_gemm_bf16_btiled(const uint16_t* A, const uint16_t* Btiled, float* C, int M, int N, int K,
+                                   int ldc, hipStream_t stream);
 hipError_t launch_gemm_f32(const float* A, const int32_t* rows, const float* Bt, const float* bias,
                            float* C, int M, int N, int K, int ldc, hipStream_t stream);
 
