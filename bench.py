@@ -195,6 +195,26 @@ def main():
     torch.cuda.synchronize()
     tb.sync_status()
     phases, nb = tb.phase_times()
+    # the verification inputs of the built trees (ancestor mask, positions,
+    # flattened tokens), timed on the builder's stream beside the build
+    prefix = torch.zeros(spec.B, dtype=torch.int32, device="cuda")
+    anchor = torch.zeros(spec.B, dtype=torch.int32, device="cuda")
+    vo = pkg.tree_attention_inputs(out["parents"], out["depths"], out["n_nodes"], tokens=out["tokens"],
+                                   prefix_len=prefix, anchor=anchor, stream=stream)
+    from conditional_draft_tree_dominotree_amd import binding
+    view = binding.TreeView(spec.B, spec.N + 1, out["parents"].data_ptr(), out["depths"].data_ptr(),
+                            out["tokens"].data_ptr(), out["n_nodes"].data_ptr(), prefix.data_ptr(),
+                            anchor.data_ptr())
+    vouts = binding.VerifyOutputs(vo["mask"].data_ptr(), vo["positions"].data_ptr(), vo["tokens"].data_ptr(),
+                                  vo["bad"].data_ptr())
+    v0, v1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    v0.record(stream)
+    for _ in range(args.steps):
+        binding.dt_tree_attention_inputs(view, vouts, stream.cuda_stream)
+    v1.record(stream)
+    torch.cuda.synchronize()
+    assert int(vo["bad"].sum().item()) == 0
+    verify_ms = v0.elapsed_time(v1) / args.steps
     n_nodes = out["n_nodes"].cpu().numpy()
     assert np.all(n_nodes == spec.N), n_nodes
 
@@ -227,6 +247,8 @@ def main():
         "round_ms_events": ev_ms,
         "phases_ms": {"lm_head": phases[0], "candidates": phases[1], "P_join": phases[2],
                       "builder_setup": phases[3], "tree_kernel": tree_ms, "builds_averaged": nb},
+        "verify_inputs": {"ms": verify_ms, "launch": "dt_tree_attention_inputs",
+                          "bytes": spec.B * (spec.N + 1) * 4 * (5 + (spec.N + 32) // 32) + spec.B * 12},
         "roofline": {
             "kernel": "tree_kernel",
             "bound": "hbm",

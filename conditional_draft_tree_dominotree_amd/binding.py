@@ -1,8 +1,9 @@
 """ctypes binding of libdominotree.so (argument marshalling only).
 
-The functions dt_create / dt_build_trees / dt_sync_status / dt_destroy /
-dt_last_error / dt_version mirror include/dominotree.h one to one; the
-TreeBuilder class wraps them for torch device tensors.  Every step of the
+The functions dt_create / dt_build_trees / dt_sync_status / dt_phase_times /
+dt_destroy / dt_tree_attention_inputs / dt_last_error / dt_version mirror
+include/dominotree.h one to one; TreeBuilder and tree_attention_inputs wrap
+them for torch device tensors.  Every step of the
 build runs in the HIP library: when it is not built, loading fails loudly.
 """
 from __future__ import annotations
@@ -54,8 +55,19 @@ class Outputs(C.Structure):
                 ("cand_logits", C.c_void_p), ("lse", C.c_void_p)]
 
 
+class TreeView(C.Structure):
+    _fields_ = [("batch", C.c_int32), ("cols", C.c_int32), ("parents", C.c_void_p),
+                ("depths", C.c_void_p), ("tokens", C.c_void_p), ("n_nodes", C.c_void_p),
+                ("prefix_len", C.c_void_p), ("anchor", C.c_void_p)]
+
+
+class VerifyOutputs(C.Structure):
+    _fields_ = [("mask", C.c_void_p), ("positions", C.c_void_p), ("tokens", C.c_void_p),
+                ("bad", C.c_void_p)]
+
+
 EXPORTS = ["dt_create", "dt_build_trees", "dt_sync_status", "dt_phase_times", "dt_destroy",
-           "dt_last_error", "dt_version"]
+           "dt_last_error", "dt_version", "dt_tree_attention_inputs"]
 _lib = None
 
 
@@ -89,6 +101,8 @@ def load_library():
     lib.dt_last_error.argtypes = []
     lib.dt_version.restype = C.c_char_p
     lib.dt_version.argtypes = []
+    lib.dt_tree_attention_inputs.restype = C.c_int
+    lib.dt_tree_attention_inputs.argtypes = [C.POINTER(TreeView), C.POINTER(VerifyOutputs), C.c_void_p]
     _lib = lib
     return lib
 
@@ -135,6 +149,10 @@ def dt_phase_times(handle: int) -> tuple:
 
 def dt_destroy(handle: int):
     _check(load_library().dt_destroy(C.c_void_p(handle)))
+
+
+def dt_tree_attention_inputs(view: TreeView, out: VerifyOutputs, stream: int = 0):
+    _check(load_library().dt_tree_attention_inputs(C.byref(view), C.byref(out), C.c_void_p(stream)))
 
 
 # ----------------------------------------------------------------------------
@@ -224,3 +242,30 @@ class TreeBuilder:
         tree_kernel) of the DT_TIMING builds since the previous call, and
         how many builds were averaged."""
         return dt_phase_times(self.handle)
+
+
+def tree_attention_inputs(parents, depths, n_nodes, tokens=None, prefix_len=None, anchor=None,
+                          stream=None) -> dict:
+    """Tree-attention inputs of built trees (torch int32 device tensors in the
+    builder's output layout, [b, cols]).  Returns device tensors: mask
+    [b, cols, ceil(cols / 32)] int32 (bit patterns of the uint32 words),
+    positions [b, cols], tokens [b, cols] (when `tokens` is given) and bad [b]."""
+    import torch
+    b, cols = parents.shape
+    for name, t in (("parents", parents), ("depths", depths), ("n_nodes", n_nodes),
+                    ("tokens", tokens), ("prefix_len", prefix_len), ("anchor", anchor)):
+        if t is not None and (not t.is_cuda or not t.is_contiguous() or t.dtype != torch.int32):
+            raise ValueError(f"{name} must be a contiguous int32 device tensor")
+    dev = parents.device
+    words = (cols + 31) // 32
+    o = {"mask": torch.empty((b, cols, words), dtype=torch.int32, device=dev),
+         "positions": torch.empty((b, cols), dtype=torch.int32, device=dev),
+         "bad": torch.empty((b,), dtype=torch.int32, device=dev)}
+    if tokens is not None:
+        o["tokens"] = torch.empty((b, cols), dtype=torch.int32, device=dev)
+    view = TreeView(b, cols, _ptr(parents), _ptr(depths), _ptr(tokens), _ptr(n_nodes),
+                    _ptr(prefix_len), _ptr(anchor))
+    vo = VerifyOutputs(_ptr(o["mask"]), _ptr(o["positions"]), _ptr(o.get("tokens")), _ptr(o["bad"]))
+    st = stream if stream is not None else torch.cuda.current_stream()
+    dt_tree_attention_inputs(view, vo, st.cuda_stream)
+    return o

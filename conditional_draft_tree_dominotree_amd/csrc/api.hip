@@ -450,4 +450,19 @@ dt_status dt_destroy(dt_handle* h) {
   return DT_OK;
 }
 
+dt_status dt_tree_attention_inputs(const dt_tree_view* trees, const dt_verify_outputs* out, void* stream) {
+  if (!trees || !out) return fail(DT_EINVAL, "NULL trees or out");
+  if (trees->batch < 1) return fail(DT_EINVAL, "batch %d < 1", trees->batch);
+  if (trees->cols < 1) return fail(DT_EINVAL, "cols %d < 1", trees->cols);
+  if (trees->cols > DT_MAX_BUDGET + 1)
+    return fail(DT_EUNSUPPORTED, "cols %d > %d", trees->cols, DT_MAX_BUDGET + 1);
+  if (!trees->parents || !trees->depths || !trees->n_nodes) return fail(DT_EINVAL, "NULL parents, depths or n_nodes");
+  if (!out->mask || !out->positions) return fail(DT_EINVAL, "NULL mask or positions");
+  if (out->tokens && !trees->tokens) return fail(DT_EINVAL, "flattened tokens need the trees' tokens");
+  HIPCHK(dt::launch_tree_attention(trees->batch, trees->cols, trees->parents, trees->depths, trees->tokens,
+                                   trees->n_nodes, trees->prefix_len, trees->anchor, out->mask, out->positions,
+                                   out->tokens, out->bad, (hipStream_t)stream));
+  return DT_OK;
+}
+
 }  // extern "C"

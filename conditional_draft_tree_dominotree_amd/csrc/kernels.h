@@ -40,6 +40,18 @@ hipError_t launch_gemm_bf16_btiled(const uint16_t* A, const uint16_t* Btiled, fl
 hipError_t launch_gemm_f32(const float* A, const int32_t* rows, const float* Bt, const float* bias,
                            float* C, int M, int N, int K, int ldc, hipStream_t stream);
 
+// ---- tree-attention inputs (verify.hip)
+constexpr int DT_VERIFY_MAX_COLS = 1025;  // budget + 1 at the largest budget
+// One block per tree: the ancestor mask [batch, cols, ceil(cols / 32)] (bit
+// j % 32 of word j / 32 of row i set when node j is i or an ancestor of i),
+// positions [batch, cols] (prefix + depth), flattened tokens [batch, cols]
+// (the anchor at node 0) and a per-tree flag for trees that break the
+// builder's invariants.  tokens/flat, prefix_len, anchor and bad may be NULL.
+hipError_t launch_tree_attention(int batch, int cols, const int32_t* parents, const int32_t* depths,
+                                 const int32_t* tokens, const int32_t* n_nodes, const int32_t* prefix_len,
+                                 const int32_t* anchor, uint32_t* mask, int32_t* positions, int32_t* flat,
+                                 int32_t* bad, hipStream_t stream);
+
 // ---- weight re-layout (prepack.hip)
 // out[c, r] = in[r, c] for a [R, C] matrix of 2- or 4-byte elements
 hipError_t launch_transpose(const void* in, void* out, int R, int C, int elem_bytes, hipStream_t stream);

@@ -150,9 +150,10 @@ typedef struct {
 typedef struct dt_handle dt_handle;
 
 /* Create a handle on the current HIP device: copy and re-lay-out the weights
- * into handle-owned device memory (w2 -> [V, r]; w_lm -> [V, h]; GRU and W1
- * in the builder's tile order) and allocate the workspace for dims.max_batch
- * and for every params no larger than *max_params (top_m, top_k, budget).
+ * into handle-owned device memory (w2 -> [V, r]; w_lm -> the LM-head GEMM's
+ * tile order; GRU and W1 in the builder's tile order) and allocate the
+ * workspace for dims.max_batch and for every params no larger than
+ * *max_params (top_m, top_k, budget).
  * Enqueued on `stream` and synchronised before returning.
  * Errors: DT_EINVAL (NULL h/dims/weights/max_params, non-positive sizes,
  * missing required weight), DT_EUNSUPPORTED (limits, dims not multiples of
@@ -167,8 +168,8 @@ dt_status dt_create(dt_handle** h, const dt_dims* dims, const dt_weights* w,
  * the handle owns (default priority), forked from and joined back into
  * `stream` with events, beside the candidate selection.  A handle must not be
  * used by two builds at once (one workspace).  When in->base_logits is NULL the
- * base logits are computed from in->hidden with w_lm [Domino, Steps] and are
- * never written to memory (only their candidates and LSE are).
+ * base logits are computed from in->hidden with w_lm [Domino, Steps] into a
+ * handle-owned fp32 workspace, from which the candidates and LSE are taken.
  * Errors: DT_EINVAL (NULL pointers, batch out of range, params out of range
  * or above the handle's max_params, NaN logits under DT_VALIDATE, w_lm
  * missing with NULL base logits), DT_EUNSUPPORTED, DT_EHIP, DT_EDEVICE (a
@@ -191,6 +192,44 @@ dt_status dt_sync_status(dt_handle* h, void* stream);
  * *count, then starts a new averaging window.
  * Errors: DT_EINVAL (NULL h, ms or count), DT_EHIP. */
 dt_status dt_phase_times(dt_handle* h, float* ms, int n, int32_t* count);
+
+/* ---- Verification inputs ------------------------------------------------
+ * The drafted tree is verified with the standard tree attention of
+ * DDTree/SpecInfer: a causal mask built from each node's ancestors
+ * ("Riassunto Tecnico: DominoTree", Componenti Core 5).  The view below reads
+ * trees in dt_outputs' layout (row stride cols = N + 1); every pointer is a
+ * DEVICE pointer. */
+typedef struct {
+  int32_t batch;              /* b >= 1 */
+  int32_t cols;               /* row stride of the arrays: N + 1, 1..DT_MAX_BUDGET + 1 */
+  const int32_t* parents;     /* [b, cols] (dt_outputs.parents) */
+  const int32_t* depths;      /* [b, cols] */
+  const int32_t* tokens;      /* [b, cols], or NULL (then no flattened tokens) */
+  const int32_t* n_nodes;     /* [b] */
+  const int32_t* prefix_len;  /* [b] committed prefix length, or NULL (0) */
+  const int32_t* anchor;      /* [b] last committed token (the root), or NULL (-1) */
+} dt_tree_view;
+
+typedef struct {
+  uint32_t* mask;      /* [b, cols, ceil(cols / 32)]: bit j % 32 of word j / 32 of
+                          row i is set when node j is node i or an ancestor of it
+                          (root included); rows and columns past n_nodes are 0 */
+  int32_t* positions;  /* [b, cols]: prefix_len + depth, -1 past n_nodes */
+  int32_t* tokens;     /* [b, cols] or NULL: the anchor at 0, node tokens at
+                          1..n_nodes, -1 past n_nodes */
+  int32_t* bad;        /* [b] or NULL: 1 when a tree breaks the builder's
+                          invariants (n_nodes outside 0..cols-1, a parent not
+                          smaller than its child, a path not ending at the
+                          root, a depth other than the path length), else 0 */
+} dt_verify_outputs;
+
+/* Build the tree-attention inputs of b trees on `stream` (one kernel, no
+ * synchronisation, no allocation).  A bad tree's mask rows hold the nodes
+ * that its walk reached before the break; its positions use the given depths.
+ * Errors: DT_EINVAL (NULL trees/out, NULL required pointers, batch or cols
+ * below 1, out->tokens without trees->tokens), DT_EUNSUPPORTED (cols above
+ * DT_MAX_BUDGET + 1), DT_EHIP. */
+dt_status dt_tree_attention_inputs(const dt_tree_view* trees, const dt_verify_outputs* out, void* stream);
 
 /* Free everything the handle owns (synchronises the device first). NULL is a no-op. */
 dt_status dt_destroy(dt_handle* h);

@@ -90,3 +90,23 @@ def test_unknown_flags_are_einval(lib):
     h = ctypes.c_void_p()
     assert lib.dt_create(ctypes.byref(h), ctypes.byref(d), ctypes.byref(w), ctypes.byref(p),
                          None) == binding.DT_EINVAL
+
+
+@pytest.mark.parametrize("view,out,code", [
+    ((0, 9, 16, 16, 16, 16), (16, 16, None), binding.DT_EINVAL),           # batch 0
+    ((2, 0, 16, 16, 16, 16), (16, 16, None), binding.DT_EINVAL),           # cols 0
+    ((2, 1026, 16, 16, 16, 16), (16, 16, None), binding.DT_EUNSUPPORTED),  # cols > N_max + 1
+    ((2, 9, None, 16, 16, 16), (16, 16, None), binding.DT_EINVAL),         # no parents
+    ((2, 9, 16, None, 16, 16), (16, 16, None), binding.DT_EINVAL),         # no depths
+    ((2, 9, 16, 16, 16, None), (16, 16, None), binding.DT_EINVAL),         # no n_nodes
+    ((2, 9, 16, 16, 16, 16), (None, 16, None), binding.DT_EINVAL),         # no mask
+    ((2, 9, 16, 16, 16, 16), (16, None, None), binding.DT_EINVAL),         # no positions
+    ((2, 9, 16, 16, None, 16), (16, 16, 16), binding.DT_EINVAL),           # flat tokens need tokens
+])
+def test_tree_attention_argument_errors(lib, view, out, code):
+    b, cols, par, dep, tok, nn = view
+    v = binding.TreeView(b, cols, par, dep, tok, nn, None, None)
+    o = binding.VerifyOutputs(out[0], out[1], out[2], None)
+    assert lib.dt_tree_attention_inputs(ctypes.byref(v), ctypes.byref(o), None) == code
+    assert pkg.dt_last_error()
+    assert lib.dt_tree_attention_inputs(None, None, None) == binding.DT_EINVAL
