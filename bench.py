@@ -215,6 +215,21 @@ def main():
     torch.cuda.synchronize()
     assert int(vo["bad"].sum().item()) == 0
     verify_ms = v0.elapsed_time(v1) / args.steps
+    # the greedy chain head over the whole vocabulary on the same weights and
+    # inputs, for the whole batch and for its first request alone
+    chain_ms = {}
+    for nb in ((spec.B, 1) if spec.B > 1 else (1,)):
+        hid_b = hidden[:nb].contiguous()
+        base_b = base[:nb].contiguous() if base is not None else None
+        co = tb.chain(hid_b, base_b)
+        c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        c0.record(stream)
+        for _ in range(args.steps):
+            tb.chain(hid_b, base_b, out=co)
+        c1.record(stream)
+        torch.cuda.synchronize()
+        tb.sync_status()
+        chain_ms[f"batch_{nb}"] = c0.elapsed_time(c1) / args.steps
     n_nodes = out["n_nodes"].cpu().numpy()
     assert np.all(n_nodes == spec.N), n_nodes
 
@@ -247,6 +262,7 @@ def main():
         "round_ms_events": ev_ms,
         "phases_ms": {"lm_head": phases[0], "candidates": phases[1], "P_join": phases[2],
                       "builder_setup": phases[3], "tree_kernel": tree_ms, "builds_averaged": nb},
+        "chain_head_ms": dict(chain_ms, positions=spec.D, launch="dt_draft_chain (greedy, full vocabulary)"),
         "verify_inputs": {"ms": verify_ms, "launch": "dt_tree_attention_inputs",
                           "bytes": spec.B * (spec.N + 1) * 4 * (5 + (spec.N + 32) // 32) + spec.B * 12},
         "roofline": {

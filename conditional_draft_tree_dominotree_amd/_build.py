@@ -9,7 +9,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "libdominotree.so")
 OBJ = os.path.join(PKG, "_build")
-SOURCES = ["api.hip", "topm.hip", "gemm.hip", "prepack.hip", "tree.hip", "verify.hip"]
+SOURCES = ["api.hip", "topm.hip", "gemm.hip", "prepack.hip", "tree.hip", "verify.hip", "chain.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

@@ -67,7 +67,7 @@ class VerifyOutputs(C.Structure):
 
 
 EXPORTS = ["dt_create", "dt_build_trees", "dt_sync_status", "dt_phase_times", "dt_destroy",
-           "dt_last_error", "dt_version", "dt_tree_attention_inputs"]
+           "dt_last_error", "dt_version", "dt_tree_attention_inputs", "dt_draft_chain"]
 _lib = None
 
 
@@ -101,6 +101,9 @@ def load_library():
     lib.dt_last_error.argtypes = []
     lib.dt_version.restype = C.c_char_p
     lib.dt_version.argtypes = []
+    lib.dt_draft_chain.restype = C.c_int
+    lib.dt_draft_chain.argtypes = [C.c_void_p, C.POINTER(Inputs), C.c_uint32, C.c_void_p, C.c_void_p,
+                                   C.c_void_p]
     lib.dt_tree_attention_inputs.restype = C.c_int
     lib.dt_tree_attention_inputs.argtypes = [C.POINTER(TreeView), C.POINTER(VerifyOutputs), C.c_void_p]
     _lib = lib
@@ -149,6 +152,11 @@ def dt_phase_times(handle: int) -> tuple:
 
 def dt_destroy(handle: int):
     _check(load_library().dt_destroy(C.c_void_p(handle)))
+
+
+def dt_draft_chain(handle: int, inputs: Inputs, flags: int, tokens: int, logits, stream: int = 0):
+    _check(load_library().dt_draft_chain(C.c_void_p(handle), C.byref(inputs), C.c_uint32(flags),
+                                         C.c_void_p(tokens), C.c_void_p(logits), C.c_void_p(stream)))
 
 
 def dt_tree_attention_inputs(view: TreeView, out: VerifyOutputs, stream: int = 0):
@@ -232,6 +240,25 @@ class TreeBuilder:
                        _ptr(o["n_nodes"]), _ptr(o.get("cand_ids")), _ptr(o.get("cand_logits")),
                        _ptr(o.get("lse")))
         dt_build_trees(self.handle, inp, prm, outs, self.stream.cuda_stream)
+        return o
+
+    def chain(self, hidden, base_logits=None, root_state=None, *, flags=None, out=None):
+        """Enqueue the greedy chain head (dt_draft_chain) on the builder's
+        stream; returns {"tokens": [b, D] int32, "logits": [b, D] float32}."""
+        torch = self.torch
+        if flags is None:
+            flags = DT_ACT_BF16 if self.wdtype == DT_BF16 else 0
+        for name, t in (("hidden", hidden), ("base_logits", base_logits), ("root_state", root_state)):
+            if t is not None and (not t.is_cuda or not t.is_contiguous()):
+                raise ValueError(f"{name} must be a contiguous device tensor")
+        b, D = hidden.shape[0], self.dims.depths
+        dev = self._keep["w_ih"].device
+        o = out if out is not None else {
+            "tokens": torch.empty((b, D), dtype=torch.int32, device=dev),
+            "logits": torch.empty((b, D), dtype=torch.float32, device=dev)}
+        inp = Inputs(b, _ptr(base_logits), _ptr(hidden), _ptr(root_state))
+        dt_draft_chain(self.handle, inp, flags, _ptr(o["tokens"]), _ptr(o.get("logits")),
+                       self.stream.cuda_stream)
         return o
 
     def sync_status(self):

@@ -53,6 +53,7 @@ struct dt_handle {
   void* wlm_t = nullptr;    // W_lm^T: tiled for the LM-head GEMM (wlm_tiled) or [V, h]; or null
   bool wlm_tiled = false;
   float* logits = nullptr;  // [max_batch, D, V] base logits computed by the LM head
+  void* wc_rm = nullptr;    // [3 ds + r, ds] row-major [W_hh ; W1_S^T] (the chain head)
   int n_tiles = 0;
   // workspace
   uint64_t* chunk_cand = nullptr;
@@ -72,6 +73,10 @@ struct dt_handle {
   uint32_t* mbox_c = nullptr;
   int* err = nullptr;
   int* nanflag = nullptr;
+  float* chain_gu = nullptr;     // chain head: [max_batch, 3 ds + r]
+  float* chain_s = nullptr;      // [max_batch, ds]
+  void* chain_sop = nullptr;     // [max_batch, ds] (wdtype)
+  uint64_t* chain_part = nullptr;  // [max_batch, chain_blocks(V)]
   size_t act_bytes = 0;
   uint32_t ebase = 0;  // epoch base of the next launch (mailboxes hold older epochs)
   hipStream_t side = nullptr;  // runs P = H W1_H beside the candidate selection
@@ -98,7 +103,8 @@ void free_all(dt_handle* h) {
   void* ptrs[] = {h->G,       h->tiles,    h->b_hh,     h->w1h_t, h->w2t,      h->wlm_t,  h->logits,
                   h->chunk_cand, h->chunk_stat, h->cand_ids, h->cand_vals, h->tokrank, h->lse,
                   h->tail,    h->P,        h->state,    h->act,   h->gh,       h->u,
-                  h->ninfo,   h->mbox_w,   h->mbox_c,   h->err,   h->nanflag};
+                  h->ninfo,   h->mbox_w,   h->mbox_c,   h->err,   h->nanflag, h->wc_rm,
+                  h->chain_gu, h->chain_s, h->chain_sop, h->chain_part};
   for (void* p : ptrs)
     if (p) (void)hipFree(p);
   for (auto& set : h->ev)
@@ -239,6 +245,16 @@ dt_status dt_create(dt_handle** out, const dt_dims* dims, const dt_weights* w, c
       HIPB(dt::launch_transpose(w->w_lm, h->wlm_t, hd, V, (int)esz, stream));
     }
   }
+
+  // the chain head's row-major [W_hh ; W1_S^T] and its workspace
+  ALLOC(h->wc_rm, (size_t)(3 * ds + r) * ds * esz);
+  HIPB(hipMemcpyAsync(h->wc_rm, w->w_hh, (size_t)3 * ds * ds * esz, hipMemcpyDeviceToDevice, stream));
+  HIPB(dt::launch_transpose((const char*)w->w1 + (size_t)hd * r * esz, (char*)h->wc_rm + (size_t)3 * ds * ds * esz,
+                            ds, r, (int)esz, stream));
+  ALLOC(h->chain_gu, (size_t)Bm * (3 * ds + r) * sizeof(float));
+  ALLOC(h->chain_s, (size_t)Bm * ds * sizeof(float));
+  ALLOC(h->chain_sop, (size_t)Bm * ds * esz);
+  ALLOC(h->chain_part, (size_t)Bm * dt::chain_blocks(V) * sizeof(uint64_t));
 
   // workspace for max_batch and max_params
   const int S = dt::topm_chunks(V);
@@ -447,6 +463,61 @@ dt_status dt_destroy(dt_handle* h) {
   (void)hipDeviceSynchronize();
   free_all(h);
   delete h;
+  return DT_OK;
+}
+
+dt_status dt_draft_chain(dt_handle* h, const dt_inputs* in, uint32_t flags, int32_t* tokens, float* logits,
+                         void* stream_) {
+  if (!h || !in || !tokens) return fail(DT_EINVAL, "h, in and tokens are required");
+  const dt_dims& d = h->dims;
+  if (in->batch < 1 || in->batch > d.max_batch)
+    return fail(DT_EINVAL, "batch %d outside 1..%d", in->batch, d.max_batch);
+  if (!in->hidden) return fail(DT_EINVAL, "hidden is required");
+  if (!in->base_logits && !h->wlm_t) return fail(DT_EINVAL, "no base logits and no LM head weights");
+  if (flags & ~(uint32_t)DT_ACT_BF16) return fail(DT_EINVAL, "unknown flags 0x%x", flags);
+  if (h->bf16 && !(flags & DT_ACT_BF16))
+    return fail(DT_EUNSUPPORTED, "bf16 weights need DT_ACT_BF16 (bf16 GEMM operands)");
+  if (!h->bf16 && (flags & DT_ACT_BF16)) return fail(DT_EUNSUPPORTED, "DT_ACT_BF16 needs bf16 weights");
+  if (d.rank > dt::CHAIN_MAX_RANK || d.rank % 8)
+    return fail(DT_EUNSUPPORTED, "the chain head needs rank <= %d and a multiple of 8", dt::CHAIN_MAX_RANK);
+  hipStream_t stream = reinterpret_cast<hipStream_t>(stream_);
+  const int B = in->batch, D = d.depths, V = d.vocab, rows = B * D;
+  // P = H W1_H for every position (the path-independent half of W1 [H_d; S])
+  if (h->bf16)
+    HIPCHK(dt::launch_gemm_bf16((const uint16_t*)in->hidden, nullptr, (const uint16_t*)h->w1h_t, nullptr, h->P,
+                                rows, d.rank, d.hidden, d.rank, stream));
+  else
+    HIPCHK(dt::launch_gemm_f32((const float*)in->hidden, nullptr, (const float*)h->w1h_t, nullptr, h->P, rows,
+                               d.rank, d.hidden, d.rank, stream));
+  if (!in->base_logits) {
+    if (h->wlm_tiled)
+      HIPCHK(dt::launch_gemm_bf16_btiled((const uint16_t*)in->hidden, (const uint16_t*)h->wlm_t, h->logits, rows, V,
+                                         d.hidden, V, stream));
+    else
+      HIPCHK(dt::launch_gemm_bf16((const uint16_t*)in->hidden, nullptr, (const uint16_t*)h->wlm_t, nullptr,
+                                  h->logits, rows, V, d.hidden, V, stream));
+  }
+  dt::ChainArgs c{};
+  c.B = B;
+  c.D = D;
+  c.V = V;
+  c.ds = d.state_dim;
+  c.r = d.rank;
+  c.bf16 = h->bf16;
+  c.w2t = h->w2t;
+  c.wc = h->wc_rm;
+  c.G = h->G;
+  c.b_hh = h->b_hh;
+  c.base = in->base_logits ? in->base_logits : h->logits;
+  c.P = h->P;
+  c.root = in->root_state;
+  c.gu = h->chain_gu;
+  c.s = h->chain_s;
+  c.s_op = h->chain_sop;
+  c.part = h->chain_part;
+  c.tokens = tokens;
+  c.logits = logits;
+  HIPCHK(dt::launch_chain(c, stream));
   return DT_OK;
 }
 

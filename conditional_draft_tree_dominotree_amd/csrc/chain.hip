@@ -1,0 +1,240 @@
+// Greedy Domino chain head over the whole vocabulary: for each draft position
+// d = 1..D, dL = W2 SiLU(W1 [H_d; S]) on every token, the pick
+// x_d = argmax(base_d + dL) (ties to the lowest id), then S <- GRU(S, E[x_d])
+// ("Domino：在投机解码中将因果建模与自回归草稿解耦", 核心方法 and 方法步骤详情:
+// the head corrects each position's block-parallel base logits with a GRU
+// state advanced from the previously drafted token).
+//
+// Per position, three launches on the caller's stream:
+//   1. [W_hh S~ | W1_S^T S~] for the batch (the dense-product kernels), S~ the
+//      state as a matrix operand;
+//   2. chain_correct: one thread per vocabulary row; a = SiLU(P_d + W1_S^T S~)
+//      for every request sits in LDS as [j][b] (one 16-byte broadcast read
+//      serves four requests), the thread requests its whole W2^T row at once
+//      (32 x 16 bytes in registers for bf16) and keeps one accumulator per
+//      request; each block writes, per request, its best (corrected logit,
+//      token) composite;
+//   3. chain_pick: one block per request reduces the block composites to the
+//      pick and advances the GRU state with G[pick] = E W_ih^T + b_ih (the
+//      handle's table) and the product of step 1.
+#include "common.h"
+#include "kernels.h"
+
+namespace dt {
+
+constexpr int CT = 256;  // threads per block (one vocabulary row each)
+
+// Row pieces of 8 elements held in registers at once: a whole bf16 row of
+// rank <= 256 (32 x 16 bytes; half of it with 32 requests), an fp32 row 64
+// elements at a time.
+template <typename T>
+struct RowPiece;
+template <>
+struct RowPiece<uint16_t> {
+  typedef uint4 type;
+  static constexpr int CHUNK = 256;
+  static __device__ __forceinline__ void unpack(const uint4& q, float (&w)[8]) {
+    const uint32_t u[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      w[2 * i] = __uint_as_float(u[i] << 16);
+      w[2 * i + 1] = __uint_as_float(u[i] & 0xFFFF0000u);
+    }
+  }
+};
+struct F8 {
+  float4 a, b;
+};
+template <>
+struct RowPiece<float> {
+  typedef F8 type;
+  static constexpr int CHUNK = 64;
+  static __device__ __forceinline__ void unpack(const F8& q, float (&w)[8]) {
+    w[0] = q.a.x; w[1] = q.a.y; w[2] = q.a.z; w[3] = q.a.w;
+    w[4] = q.b.x; w[5] = q.b.y; w[6] = q.b.z; w[7] = q.b.w;
+  }
+};
+
+// One vocabulary row per thread (the grid covers V).  NB: requests handled,
+// a multiple of 4 and >= B.  The row's W2^T pieces are all requested before
+// the first is used, so a thread waits for memory once per chunk.
+template <typename T, int NB>
+__global__ __launch_bounds__(CT) void chain_correct_kernel(const T* __restrict__ w2t, const float* __restrict__ base,
+                                                           const float* __restrict__ P,
+                                                           const float* __restrict__ gu, int B, int D, int d,
+                                                           int V, int r, int gstride, int goff,
+                                                           uint64_t* __restrict__ part) {
+  typedef typename RowPiece<T>::type Piece;
+  // 32 accumulators leave room for half a bf16 row at a time
+  constexpr int CH = (NB >= 32 && RowPiece<T>::CHUNK > 128) ? 128 : RowPiece<T>::CHUNK;
+  __shared__ __attribute__((aligned(16))) float a[CHAIN_MAX_RANK * NB];
+  __shared__ uint64_t wbest[CT / 64][NB];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  for (int t = tid; t < r * NB; t += CT) {
+    const int j = t / NB, b = t - j * NB;
+    float v = 0.f;
+    if (b < B) {
+      const float u = P[((size_t)b * D + d) * r + j] + gu[(size_t)b * gstride + goff + j];
+      v = u / (1.f + expf(-u));  // SiLU
+    }
+    a[t] = v;
+  }
+  __syncthreads();
+  const int v = blockIdx.x * CT + tid;
+  const int vr = min(v, V - 1);  // rows past V compute on the last row and are not kept
+  float acc[NB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) acc[b] = 0.f;
+  const Piece* row = reinterpret_cast<const Piece*>(w2t + (size_t)vr * r);
+  for (int c0 = 0; c0 < r; c0 += CH) {
+    Piece q[CH / 8];
+#pragma unroll
+    for (int i = 0; i < CH / 8; ++i)
+      if (c0 + 8 * i < r) q[i] = row[c0 / 8 + i];
+#pragma unroll
+    for (int i = 0; i < CH / 8; ++i) {
+      if (c0 + 8 * i < r) {
+        float w[8];
+        RowPiece<T>::unpack(q[i], w);
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) {
+          const float4* aj = reinterpret_cast<const float4*>(&a[(c0 + 8 * i + jj) * NB]);
+#pragma unroll
+          for (int g = 0; g < NB / 4; ++g) {
+            const float4 av = aj[g];
+            acc[4 * g] = fmaf(w[jj], av.x, acc[4 * g]);
+            acc[4 * g + 1] = fmaf(w[jj], av.y, acc[4 * g + 1]);
+            acc[4 * g + 2] = fmaf(w[jj], av.z, acc[4 * g + 2]);
+            acc[4 * g + 3] = fmaf(w[jj], av.w, acc[4 * g + 3]);
+          }
+        }
+      }
+    }
+  }
+  // per request: the block's best (corrected logit desc, token asc)
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    if (b < B) {
+      const float z = base[((size_t)b * D + d) * V + vr] + acc[b];
+      const uint64_t m = wave_max_u64(v < V ? cand_pack(f32_key(z), (uint32_t)v) : 0ull);
+      if (lane == 0) wbest[wv][b] = m;
+    }
+  }
+  __syncthreads();
+  if (tid < B) {
+    uint64_t m = wbest[0][tid];
+#pragma unroll
+    for (int w = 1; w < CT / 64; ++w) m = wbest[w][tid] > m ? wbest[w][tid] : m;
+    part[(size_t)tid * gridDim.x + blockIdx.x] = m;
+  }
+}
+
+template <typename T>
+__global__ __launch_bounds__(CT) void chain_pick_kernel(const uint64_t* __restrict__ part, int nblk, int V,
+                                                        const float* __restrict__ G, const float* __restrict__ gu,
+                                                        const float* __restrict__ b_hh, int gstride, int ds,
+                                                        int D, int d, int advance, float* __restrict__ s,
+                                                        T* __restrict__ s_op, int32_t* __restrict__ tokens,
+                                                        float* __restrict__ logits) {
+  __shared__ uint64_t wm[CT / 64];
+  __shared__ uint64_t pick;
+  const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  uint64_t m = 0ull;
+  for (int i = tid; i < nblk; i += CT) {
+    const uint64_t c = part[(size_t)b * nblk + i];
+    m = c > m ? c : m;
+  }
+  m = wave_max_u64(m);
+  if (lane == 0) wm[wv] = m;
+  __syncthreads();
+  if (tid == 0) {
+    uint64_t x = wm[0];
+    for (int w = 1; w < CT / 64; ++w) x = wm[w] > x ? wm[w] : x;
+    pick = x;
+    tokens[(size_t)b * D + d] = (int32_t)cand_id(x);
+    if (logits) logits[(size_t)b * D + d] = key_f32(cand_key(x));
+  }
+  __syncthreads();
+  if (!advance) return;
+  // S <- GRU(S, E[x]): gate rows (r, z, n), the reset gate on (W_hn S + b_hn)
+  const float* gi = G + (size_t)min(cand_id(pick), (uint32_t)(V - 1)) * 3 * ds;
+  const float* gh = gu + (size_t)b * gstride;
+  for (int i = tid; i < ds; i += CT) {
+    const float hr = gh[i] + (b_hh ? b_hh[i] : 0.f);
+    const float hz = gh[ds + i] + (b_hh ? b_hh[ds + i] : 0.f);
+    const float hn = gh[2 * ds + i] + (b_hh ? b_hh[2 * ds + i] : 0.f);
+    const float rg = 1.f / (1.f + expf(-(gi[i] + hr)));
+    const float zg = 1.f / (1.f + expf(-(gi[ds + i] + hz)));
+    const float ng = tanhf(gi[2 * ds + i] + rg * hn);
+    const float sp = s[(size_t)b * ds + i];
+    const float sn = (1.f - zg) * ng + zg * sp;
+    s[(size_t)b * ds + i] = sn;
+    if constexpr (sizeof(T) == 2) s_op[(size_t)b * ds + i] = f32_to_bf16(sn);  // bf16 operand, nearest-even
+    else s_op[(size_t)b * ds + i] = sn;
+  }
+}
+
+template <typename T>
+__global__ void chain_init_kernel(const float* __restrict__ root, int n, float* __restrict__ s, T* __restrict__ s_op) {
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) {
+    const float v = root ? root[i] : 0.f;
+    s[i] = v;
+    if constexpr (sizeof(T) == 2) s_op[i] = f32_to_bf16(v);
+    else s_op[i] = v;
+  }
+}
+
+int chain_blocks(int V) { return (V + CT - 1) / CT; }
+
+hipError_t launch_chain(const ChainArgs& c, hipStream_t stream) {
+  if (c.B < 1 || c.B > 32 || c.r < 8 || c.r > CHAIN_MAX_RANK || c.r % 8) return hipErrorInvalidValue;
+  const int nblk = chain_blocks(c.V), gstride = 3 * c.ds + c.r, goff = 3 * c.ds;
+  const int n = c.B * c.ds;
+  if (c.bf16)
+    hipLaunchKernelGGL(chain_init_kernel<uint16_t>, dim3((n + 255) / 256), dim3(256), 0, stream, c.root, n, c.s,
+                       (uint16_t*)c.s_op);
+  else
+    hipLaunchKernelGGL(chain_init_kernel<float>, dim3((n + 255) / 256), dim3(256), 0, stream, c.root, n, c.s,
+                       (float*)c.s_op);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  for (int d = 0; d < c.D; ++d) {
+    // 1. [W_hh S~ | W1_S^T S~]
+    e = c.bf16 ? launch_gemm_bf16((const uint16_t*)c.s_op, nullptr, (const uint16_t*)c.wc, nullptr, c.gu, c.B,
+                                  gstride, c.ds, gstride, stream)
+               : launch_gemm_f32((const float*)c.s_op, nullptr, (const float*)c.wc, nullptr, c.gu, c.B, gstride,
+                                 c.ds, gstride, stream);
+    if (e != hipSuccess) return e;
+    // 2. corrected logits of every token, block-wise best per request
+#define CHAIN_CORRECT(T, NB)                                                                                  \
+  hipLaunchKernelGGL((chain_correct_kernel<T, NB>), dim3(nblk), dim3(CT), 0, stream, (const T*)c.w2t, c.base, \
+                     c.P, c.gu, c.B, c.D, d, c.V, c.r, gstride, goff, c.part)
+    if (c.bf16) {
+      if (c.B <= 4) CHAIN_CORRECT(uint16_t, 4);
+      else if (c.B <= 8) CHAIN_CORRECT(uint16_t, 8);
+      else if (c.B <= 16) CHAIN_CORRECT(uint16_t, 16);
+      else CHAIN_CORRECT(uint16_t, 32);
+    } else {
+      if (c.B <= 4) CHAIN_CORRECT(float, 4);
+      else if (c.B <= 8) CHAIN_CORRECT(float, 8);
+      else if (c.B <= 16) CHAIN_CORRECT(float, 16);
+      else CHAIN_CORRECT(float, 32);
+    }
+#undef CHAIN_CORRECT
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    // 3. the pick, then the state for the next position
+    const int adv = d + 1 < c.D;
+    if (c.bf16)
+      hipLaunchKernelGGL(chain_pick_kernel<uint16_t>, dim3(c.B), dim3(CT), 0, stream, c.part, nblk, c.V, c.G, c.gu,
+                         c.b_hh, gstride, c.ds, c.D, d, adv, c.s, (uint16_t*)c.s_op, c.tokens, c.logits);
+    else
+      hipLaunchKernelGGL(chain_pick_kernel<float>, dim3(c.B), dim3(CT), 0, stream, c.part, nblk, c.V, c.G, c.gu,
+                         c.b_hh, gstride, c.ds, c.D, d, adv, c.s, (float*)c.s_op, c.tokens, c.logits);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+}  // namespace dt

@@ -52,6 +52,27 @@ hipError_t launch_tree_attention(int batch, int cols, const int32_t* parents, co
                                  const int32_t* anchor, uint32_t* mask, int32_t* positions, int32_t* flat,
                                  int32_t* bad, hipStream_t stream);
 
+// ---- greedy chain head over the whole vocabulary (chain.hip)
+constexpr int CHAIN_MAX_RANK = 256;
+struct ChainArgs {
+  int B, D, V, ds, r, bf16;  // bf16: weights and the state operand in bf16
+  const void* w2t;      // [V, r] (wdtype)
+  const void* wc;       // [3 ds + r, ds] row-major: W_hh rows, then W1_S^T
+  const float* G;       // [V, 3 ds] = E W_ih^T + b_ih
+  const float* b_hh;    // [3 ds] or null
+  const float* base;    // [B, D, V]
+  const float* P;       // [B, D, r] = H W1_H
+  const float* root;    // [B, ds] or null
+  float* gu;            // [B, 3 ds + r] workspace
+  float* s;             // [B, ds] workspace (state)
+  void* s_op;           // [B, ds] workspace (state as a matrix operand, wdtype)
+  uint64_t* part;       // [B, chain_blocks(V)] workspace
+  int32_t* tokens;      // [B, D]
+  float* logits;        // [B, D] or null
+};
+int chain_blocks(int V);
+hipError_t launch_chain(const ChainArgs& c, hipStream_t stream);
+
 // ---- weight re-layout (prepack.hip)
 // out[c, r] = in[r, c] for a [R, C] matrix of 2- or 4-byte elements
 hipError_t launch_transpose(const void* in, void* out, int R, int C, int elem_bytes, hipStream_t stream);

@@ -193,6 +193,24 @@ dt_status dt_sync_status(dt_handle* h, void* stream);
  * Errors: DT_EINVAL (NULL h, ms or count), DT_EHIP. */
 dt_status dt_phase_times(dt_handle* h, float* ms, int n, int32_t* count);
 
+/* ---- Greedy chain head ----------------------------------------------------
+ * The Domino head as a chain over the whole vocabulary [Domino, Method;
+ * Domino, Steps]: for each draft position d = 1..D in turn,
+ *   dL_d = W2^T SiLU(W1^T [H_d; S]) for every token, x_d = argmax(base_d + dL_d)
+ *   (ties to the lowest token id), then S <- GRU(S, E[x_d]),
+ * starting from S = root_state (zeros when NULL).  Uses the handle's weights
+ * and workspace (not at the same time as a dt_build_trees on the handle);
+ * in->base_logits NULL computes the base logits with w_lm as dt_build_trees
+ * does.  flags: DT_ACT_BF16 (required with bf16 weights, refused with fp32).
+ * Outputs (device, caller-owned): tokens [b, D]; logits [b, D] or NULL, the
+ * corrected logit base + dL of each pick.  Enqueued on `stream`, no
+ * synchronisation, no allocation.
+ * Errors: DT_EINVAL (NULL h/in/tokens/hidden, batch outside 1..max_batch,
+ * unknown flags, no base logits and no w_lm), DT_EUNSUPPORTED (rank above 256
+ * or not a multiple of 8, the DT_ACT_BF16 rule), DT_EHIP. */
+dt_status dt_draft_chain(dt_handle* h, const dt_inputs* in, uint32_t flags, int32_t* tokens, float* logits,
+                         void* stream);
+
 /* ---- Verification inputs ------------------------------------------------
  * The drafted tree is verified with the standard tree attention of
  * DDTree/SpecInfer: a causal mask built from each node's ancestors

@@ -110,3 +110,8 @@ def test_tree_attention_argument_errors(lib, view, out, code):
     assert lib.dt_tree_attention_inputs(ctypes.byref(v), ctypes.byref(o), None) == code
     assert pkg.dt_last_error()
     assert lib.dt_tree_attention_inputs(None, None, None) == binding.DT_EINVAL
+
+
+def test_chain_null_arguments_are_einval(lib):
+    assert lib.dt_draft_chain(None, None, 0, None, None, None) == binding.DT_EINVAL
+    assert "required" in pkg.dt_last_error()

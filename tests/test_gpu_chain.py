@@ -1,0 +1,105 @@
+"""GPU parity of the greedy chain head (dt_draft_chain) with the oracle
+(oracle/chain.py): the picked tokens bit-exact up to the first position
+where the oracle's own pick had a runner-up within the float tolerance (a
+near tie; the chains may then part), the corrected logits of the matched
+picks within 1e-4 (fp32 weights) or 2e-2 (bf16 weights)."""
+import numpy as np
+import pytest
+
+from oracle import chain, ref
+from tests import gpu_util as gu
+from workloads import synth
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dev():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no HIP device")
+    return torch.device("cuda:0")
+
+
+def compare(spec, w, req, got, requests, base=None):
+    bf16 = spec.wdtype == "bf16"
+    tol = gu.TOL_BF16 if bf16 else gu.TOL_F32
+    head = ref.make_head(w, bf16, spec.act_bf16)
+    exact, ties = 0, 0
+    for b in requests:
+        hid = ref.hidden_values(req["hidden"][b], bf16)
+        bl = base[b] if base is not None else req["base"][b]
+        toks, logits, margins = chain.greedy_chain(head, bl, hid, req["root"][b])
+        for d in range(spec.D):
+            if got["tokens"][b, d] != toks[d]:
+                assert margins[d] < tol, (b, d, got["tokens"][b, d], toks[d], margins[d])
+                ties += 1
+                break
+            assert abs(float(got["logits"][b, d]) - logits[d]) <= tol, (b, d, got["logits"][b, d], logits[d])
+        else:
+            exact += 1
+    return exact, ties
+
+
+def run_chain(tb, spec, req, base=None):
+    hidden = gu.to_dev(req["hidden"])
+    if base is None and spec.logits != "lmhead":
+        base = req["base"]
+    root = gu.to_dev(req["root"]) if spec.root_std > 0 else None
+    o = tb.chain(hidden, gu.to_dev(base), root)
+    tb.sync_status()
+    return {k: v.cpu().numpy() for k, v in o.items()}
+
+
+def test_tiny(dev):
+    spec, w, req = synth.workload("tiny")
+    tb = gu.make_builder(spec, w)
+    got = run_chain(tb, spec, req)
+    tb.close()
+    exact, ties = compare(spec, w, req, got, range(spec.B))
+    assert exact == spec.B, (exact, ties)
+
+
+def test_tiny_batch_root_state_and_ties(dev):
+    # several requests with their own root states; one depth with an exact
+    # tie in the base logits and W2 = 0 there is no correction to break it
+    spec, w, req = synth.workload("tiny")
+    rng = np.random.default_rng(5)
+    B = 7
+    req = {"base": np.repeat(req["base"], B, 0) + rng.normal(0, 1, (B, spec.D, spec.V)).astype(np.float32),
+           "hidden": np.repeat(req["hidden"], B, 0), "root": rng.normal(0, 1, (B, spec.ds)).astype(np.float32)}
+    w0 = dict(w)
+    w0["w2"] = np.zeros_like(w["w2"])
+    req["base"][3, 4, 10] = req["base"][3, 4, 900] = req["base"][3, 4].max() + 1.0
+    spec = spec.replace(B=B, root_std=1.0)
+    for weights in (w, w0):
+        tb = gu.make_builder(spec, weights)
+        got = run_chain(tb, spec, req)
+        tb.close()
+        exact, ties = compare(spec, weights, req, got, range(B))
+        assert exact == B, (exact, ties)
+    assert got["tokens"][3, 4] == 10
+
+
+@pytest.mark.parametrize("name,sample", [("q4b_b1", [0]), ("q8b_b1", [0]), ("q8b_b32", [0, 13, 31])])
+def test_full_shapes(dev, name, sample):
+    spec, w, req = synth.workload(name)
+    tb = gu.make_builder(spec, w)
+    got = run_chain(tb, spec, req)
+    tb.close()
+    assert got["tokens"].shape == (spec.B, spec.D)
+    assert np.all((got["tokens"] >= 0) & (got["tokens"] < spec.V))
+    exact, ties = compare(spec, w, req, got, sample)
+    print(name, f"{exact}/{len(sample)} chains exact, near-ties {ties}")
+    assert exact + ties == len(sample)
+
+
+def test_lm_head_route(dev):
+    spec, w, req = synth.workload("q8b_lm")
+    tb = gu.make_builder(spec, w)
+    got = run_chain(tb, spec, req)
+    tb.close()
+    base = np.zeros((spec.B, spec.D, spec.V), np.float32)
+    base[0] = ref.lm_head_logits(req["hidden"][0], w["w_lm"], True)
+    exact, ties = compare(spec, w, req, got, [0], base=base)
+    assert exact + ties == 1
