@@ -67,7 +67,7 @@ class VerifyOutputs(C.Structure):
 
 
 EXPORTS = ["dt_create", "dt_build_trees", "dt_sync_status", "dt_phase_times", "dt_destroy",
-           "dt_last_error", "dt_version", "dt_tree_attention_inputs", "dt_draft_chain"]
+           "dt_last_error", "dt_version", "dt_tree_attention_inputs", "dt_draft_chain", "dt_fold_state"]
 _lib = None
 
 
@@ -104,6 +104,9 @@ def load_library():
     lib.dt_draft_chain.restype = C.c_int
     lib.dt_draft_chain.argtypes = [C.c_void_p, C.POINTER(Inputs), C.c_uint32, C.c_void_p, C.c_void_p,
                                    C.c_void_p]
+    lib.dt_fold_state.restype = C.c_int
+    lib.dt_fold_state.argtypes = [C.c_void_p, C.c_int32, C.c_int32, C.c_void_p, C.c_void_p, C.c_void_p,
+                                  C.c_uint32, C.c_void_p]
     lib.dt_tree_attention_inputs.restype = C.c_int
     lib.dt_tree_attention_inputs.argtypes = [C.POINTER(TreeView), C.POINTER(VerifyOutputs), C.c_void_p]
     _lib = lib
@@ -157,6 +160,13 @@ def dt_destroy(handle: int):
 def dt_draft_chain(handle: int, inputs: Inputs, flags: int, tokens: int, logits, stream: int = 0):
     _check(load_library().dt_draft_chain(C.c_void_p(handle), C.byref(inputs), C.c_uint32(flags),
                                          C.c_void_p(tokens), C.c_void_p(logits), C.c_void_p(stream)))
+
+
+def dt_fold_state(handle: int, batch: int, n_tokens: int, tokens: int, prev_state, state_out: int,
+                  flags: int, stream: int = 0):
+    _check(load_library().dt_fold_state(C.c_void_p(handle), batch, n_tokens, C.c_void_p(tokens),
+                                        C.c_void_p(prev_state), C.c_void_p(state_out), C.c_uint32(flags),
+                                        C.c_void_p(stream)))
 
 
 def dt_tree_attention_inputs(view: TreeView, out: VerifyOutputs, stream: int = 0):
@@ -259,6 +269,24 @@ class TreeBuilder:
         inp = Inputs(b, _ptr(base_logits), _ptr(hidden), _ptr(root_state))
         dt_draft_chain(self.handle, inp, flags, _ptr(o["tokens"]), _ptr(o.get("logits")),
                        self.stream.cuda_stream)
+        return o
+
+    def fold_state(self, tokens, prev_state=None, *, flags=None, out=None):
+        """S <- GRU(S, E[t]) over tokens [b, L] (int32 device tensor) from
+        prev_state ([b, d_s] float32 or None = zeros); returns [b, d_s]."""
+        torch = self.torch
+        if flags is None:
+            flags = DT_ACT_BF16 if self.wdtype == DT_BF16 else 0
+        for name, t in (("tokens", tokens), ("prev_state", prev_state)):
+            if t is not None and (not t.is_cuda or not t.is_contiguous()):
+                raise ValueError(f"{name} must be a contiguous device tensor")
+        if tokens.dtype != torch.int32:
+            raise ValueError("tokens must be int32")
+        b, L = tokens.shape
+        o = out if out is not None else torch.empty((b, self.dims.state_dim), dtype=torch.float32,
+                                                    device=tokens.device)
+        dt_fold_state(self.handle, b, L, _ptr(tokens), _ptr(prev_state), _ptr(o), flags,
+                      self.stream.cuda_stream)
         return o
 
     def sync_status(self):

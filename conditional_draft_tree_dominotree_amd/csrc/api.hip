@@ -521,6 +521,33 @@ dt_status dt_draft_chain(dt_handle* h, const dt_inputs* in, uint32_t flags, int3
   return DT_OK;
 }
 
+dt_status dt_fold_state(dt_handle* h, int32_t batch, int32_t n_tokens, const int32_t* tokens,
+                        const float* prev_state, float* state_out, uint32_t flags, void* stream) {
+  if (!h || !tokens || !state_out) return fail(DT_EINVAL, "h, tokens and state_out are required");
+  if (batch < 1 || batch > h->dims.max_batch)
+    return fail(DT_EINVAL, "batch %d outside 1..%d", batch, h->dims.max_batch);
+  if (n_tokens < 1) return fail(DT_EINVAL, "n_tokens %d < 1", n_tokens);
+  if (flags & ~(uint32_t)DT_ACT_BF16) return fail(DT_EINVAL, "unknown flags 0x%x", flags);
+  if (h->bf16 && !(flags & DT_ACT_BF16))
+    return fail(DT_EUNSUPPORTED, "bf16 weights need DT_ACT_BF16 (bf16 GEMM operands)");
+  if (!h->bf16 && (flags & DT_ACT_BF16)) return fail(DT_EUNSUPPORTED, "DT_ACT_BF16 needs bf16 weights");
+  dt::ChainArgs c{};
+  c.B = batch;
+  c.V = h->dims.vocab;
+  c.ds = h->dims.state_dim;
+  c.r = h->dims.rank;
+  c.bf16 = h->bf16;
+  c.wc = h->wc_rm;
+  c.G = h->G;
+  c.b_hh = h->b_hh;
+  c.root = prev_state;
+  c.gu = h->chain_gu;
+  c.s = h->chain_s;
+  c.s_op = h->chain_sop;
+  HIPCHK(dt::launch_fold(c, tokens, n_tokens, state_out, reinterpret_cast<hipStream_t>(stream)));
+  return DT_OK;
+}
+
 dt_status dt_tree_attention_inputs(const dt_tree_view* trees, const dt_verify_outputs* out, void* stream) {
   if (!trees || !out) return fail(DT_EINVAL, "NULL trees or out");
   if (trees->batch < 1) return fail(DT_EINVAL, "batch %d < 1", trees->batch);

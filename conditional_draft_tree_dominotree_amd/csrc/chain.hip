@@ -129,6 +129,29 @@ __global__ __launch_bounds__(CT) void chain_correct_kernel(const T* __restrict__
   }
 }
 
+// S <- GRU(S, x) for one request, the input term gi = W_ih x + b_ih given
+// (a row of G): gate rows (r, z, n), the reset gate on (W_hn S + b_hn),
+// S' = (1 - z) n + z S; S' also goes to s_op (bf16, nearest-even, or fp32)
+// and, when given, to out.  One block; gh = W_hh S~ (no bias).
+template <typename T>
+__device__ __forceinline__ void gru_advance(const float* __restrict__ gi, const float* __restrict__ gh,
+                                            const float* __restrict__ b_hh, int ds, float* __restrict__ s,
+                                            T* __restrict__ s_op, float* __restrict__ out) {
+  for (int i = threadIdx.x; i < ds; i += blockDim.x) {
+    const float hr = gh[i] + (b_hh ? b_hh[i] : 0.f);
+    const float hz = gh[ds + i] + (b_hh ? b_hh[ds + i] : 0.f);
+    const float hn = gh[2 * ds + i] + (b_hh ? b_hh[2 * ds + i] : 0.f);
+    const float rg = 1.f / (1.f + expf(-(gi[i] + hr)));
+    const float zg = 1.f / (1.f + expf(-(gi[ds + i] + hz)));
+    const float ng = tanhf(gi[2 * ds + i] + rg * hn);
+    const float sn = (1.f - zg) * ng + zg * s[i];
+    s[i] = sn;
+    if constexpr (sizeof(T) == 2) s_op[i] = f32_to_bf16(sn);  // bf16 operand, nearest-even
+    else s_op[i] = sn;
+    if (out) out[i] = sn;
+  }
+}
+
 template <typename T>
 __global__ __launch_bounds__(CT) void chain_pick_kernel(const uint64_t* __restrict__ part, int nblk, int V,
                                                         const float* __restrict__ G, const float* __restrict__ gu,
@@ -156,22 +179,22 @@ __global__ __launch_bounds__(CT) void chain_pick_kernel(const uint64_t* __restri
   }
   __syncthreads();
   if (!advance) return;
-  // S <- GRU(S, E[x]): gate rows (r, z, n), the reset gate on (W_hn S + b_hn)
-  const float* gi = G + (size_t)min(cand_id(pick), (uint32_t)(V - 1)) * 3 * ds;
-  const float* gh = gu + (size_t)b * gstride;
-  for (int i = tid; i < ds; i += CT) {
-    const float hr = gh[i] + (b_hh ? b_hh[i] : 0.f);
-    const float hz = gh[ds + i] + (b_hh ? b_hh[ds + i] : 0.f);
-    const float hn = gh[2 * ds + i] + (b_hh ? b_hh[2 * ds + i] : 0.f);
-    const float rg = 1.f / (1.f + expf(-(gi[i] + hr)));
-    const float zg = 1.f / (1.f + expf(-(gi[ds + i] + hz)));
-    const float ng = tanhf(gi[2 * ds + i] + rg * hn);
-    const float sp = s[(size_t)b * ds + i];
-    const float sn = (1.f - zg) * ng + zg * sp;
-    s[(size_t)b * ds + i] = sn;
-    if constexpr (sizeof(T) == 2) s_op[(size_t)b * ds + i] = f32_to_bf16(sn);  // bf16 operand, nearest-even
-    else s_op[(size_t)b * ds + i] = sn;
-  }
+  gru_advance<T>(G + (size_t)min(cand_id(pick), (uint32_t)(V - 1)) * 3 * ds, gu + (size_t)b * gstride, b_hh, ds,
+                 s + (size_t)b * ds, s_op + (size_t)b * ds, nullptr);
+}
+
+// Fold one committed token per request into the state: S <- GRU(S, E[token])
+// (token ids clamped to 0..V-1); `out`, when given, also receives S.
+template <typename T>
+__global__ __launch_bounds__(CT) void fold_step_kernel(const int32_t* __restrict__ tokens, int L, int t, int V,
+                                                       const float* __restrict__ G, const float* __restrict__ gu,
+                                                       const float* __restrict__ b_hh, int gstride, int ds,
+                                                       float* __restrict__ s, T* __restrict__ s_op,
+                                                       float* __restrict__ out) {
+  const int b = blockIdx.x;
+  const int tok = min(max(tokens[(size_t)b * L + t], 0), V - 1);
+  gru_advance<T>(G + (size_t)tok * 3 * ds, gu + (size_t)b * gstride, b_hh, ds, s + (size_t)b * ds,
+                 s_op + (size_t)b * ds, out ? out + (size_t)b * ds : nullptr);
 }
 
 template <typename T>
@@ -185,6 +208,35 @@ __global__ void chain_init_kernel(const float* __restrict__ root, int n, float* 
 }
 
 int chain_blocks(int V) { return (V + CT - 1) / CT; }
+
+hipError_t launch_fold(const ChainArgs& c, const int32_t* tokens, int L, float* out, hipStream_t stream) {
+  if (c.B < 1 || L < 1) return hipErrorInvalidValue;
+  const int gstride = 3 * c.ds + c.r, n = c.B * c.ds;
+  if (c.bf16)
+    hipLaunchKernelGGL(chain_init_kernel<uint16_t>, dim3((n + 255) / 256), dim3(256), 0, stream, c.root, n, c.s,
+                       (uint16_t*)c.s_op);
+  else
+    hipLaunchKernelGGL(chain_init_kernel<float>, dim3((n + 255) / 256), dim3(256), 0, stream, c.root, n, c.s,
+                       (float*)c.s_op);
+  hipError_t e = hipGetLastError();
+  for (int t = 0; t < L && e == hipSuccess; ++t) {
+    // W_hh S~ (the first 3 ds rows of the row-major [W_hh ; W1_S^T])
+    e = c.bf16 ? launch_gemm_bf16((const uint16_t*)c.s_op, nullptr, (const uint16_t*)c.wc, nullptr, c.gu, c.B,
+                                  3 * c.ds, c.ds, gstride, stream)
+               : launch_gemm_f32((const float*)c.s_op, nullptr, (const float*)c.wc, nullptr, c.gu, c.B, 3 * c.ds,
+                                 c.ds, gstride, stream);
+    if (e != hipSuccess) return e;
+    float* o = t + 1 == L ? out : nullptr;
+    if (c.bf16)
+      hipLaunchKernelGGL(fold_step_kernel<uint16_t>, dim3(c.B), dim3(CT), 0, stream, tokens, L, t, c.V, c.G, c.gu,
+                         c.b_hh, gstride, c.ds, c.s, (uint16_t*)c.s_op, o);
+    else
+      hipLaunchKernelGGL(fold_step_kernel<float>, dim3(c.B), dim3(CT), 0, stream, tokens, L, t, c.V, c.G, c.gu,
+                         c.b_hh, gstride, c.ds, c.s, (float*)c.s_op, o);
+    e = hipGetLastError();
+  }
+  return e;
+}
 
 hipError_t launch_chain(const ChainArgs& c, hipStream_t stream) {
   if (c.B < 1 || c.B > 32 || c.r < 8 || c.r > CHAIN_MAX_RANK || c.r % 8) return hipErrorInvalidValue;

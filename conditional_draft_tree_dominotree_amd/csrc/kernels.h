@@ -72,6 +72,9 @@ struct ChainArgs {
 };
 int chain_blocks(int V);
 hipError_t launch_chain(const ChainArgs& c, hipStream_t stream);
+// S <- GRU(S, E[t]) over tokens[b, 0..L-1] from c.root (zeros when null),
+// written to out [B, ds]; uses c's weights and workspaces (gu, s, s_op).
+hipError_t launch_fold(const ChainArgs& c, const int32_t* tokens, int L, float* out, hipStream_t stream);
 
 // ---- weight re-layout (prepack.hip)
 // out[c, r] = in[r, c] for a [R, C] matrix of 2- or 4-byte elements

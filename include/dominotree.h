@@ -211,6 +211,23 @@ dt_status dt_phase_times(dt_handle* h, float* ms, int n, int32_t* count);
 dt_status dt_draft_chain(dt_handle* h, const dt_inputs* in, uint32_t flags, int32_t* tokens, float* logits,
                          void* stream);
 
+/* ---- Folding committed tokens into the causal state ------------------------
+ * The causal state before a draft block is the GRU over the tokens committed
+ * so far [Domino, Method: S_{i-1} = GRU(embeddings of the tokens before i)].
+ * For each request, S <- GRU(S, E[t]) over tokens[b, 0..n_tokens-1] in order,
+ * starting from prev_state (zeros when NULL), and the result goes to
+ * state_out: pass it as root_state to dt_build_trees / dt_draft_chain, or as
+ * prev_state to the next fold (the state carried across rounds).
+ * tokens [b, n_tokens] int32 (ids clamped to 0..V-1), prev_state and
+ * state_out [b, d_s] fp32, all device pointers (state_out may equal
+ * prev_state).  flags: DT_ACT_BF16 as for dt_draft_chain.  Uses the handle's
+ * workspace (not at the same time as another call on the handle).
+ * Errors: DT_EINVAL (NULL h/tokens/state_out, batch outside 1..max_batch,
+ * n_tokens < 1, unknown flags), DT_EUNSUPPORTED (the DT_ACT_BF16 rule),
+ * DT_EHIP. */
+dt_status dt_fold_state(dt_handle* h, int32_t batch, int32_t n_tokens, const int32_t* tokens,
+                        const float* prev_state, float* state_out, uint32_t flags, void* stream);
+
 /* ---- Verification inputs ------------------------------------------------
  * The drafted tree is verified with the standard tree attention of
  * DDTree/SpecInfer: a causal mask built from each node's ancestors

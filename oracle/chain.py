@@ -46,3 +46,13 @@ def greedy_chain(head: ref.Head, base: np.ndarray, hidden: np.ndarray, root: np.
         if d + 1 < D:
             s = ref.gru_step(head, s, head.emb(x))
     return np.array(tokens), np.array(logits), np.array(margins)
+
+
+def fold_state(head: ref.Head, prev: np.ndarray, tokens) -> np.ndarray:
+    """The causal state after the committed tokens: S <- GRU(S, E[t]) for each
+    token in order, from `prev` [Domino, Method: the state is a GRU over the
+    embeddings of the tokens before the position]."""
+    s = np.asarray(prev, np.float64)
+    for t in tokens:
+        s = ref.gru_step(head, s, head.emb(int(t)))
+    return s

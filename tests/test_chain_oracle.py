@@ -54,3 +54,25 @@ def test_vocabulary_relabelling():
     assert np.all(m0 > 1e-9)                 # distinct maxima: the relabelling is exact
     np.testing.assert_array_equal(perm[t0], t1)
     np.testing.assert_allclose(l0, l1, rtol=0, atol=1e-12)
+
+
+def test_fold_state_is_repeated_grucell():
+    # library special case: torch.nn.GRUCell in float64 applied token by token
+    import torch
+    spec, w, req = tiny()
+    head = ref.make_head(w, False, False)
+    rng = np.random.default_rng(4)
+    prev = rng.normal(0, 1, spec.ds)
+    toks = rng.integers(0, spec.V, 5)
+    got = chain.fold_state(head, prev, toks)
+    cell = torch.nn.GRUCell(spec.e, spec.ds, bias=True).double()
+    with torch.no_grad():
+        cell.weight_ih.copy_(torch.from_numpy(np.asarray(w["w_ih"], np.float64)))
+        cell.weight_hh.copy_(torch.from_numpy(np.asarray(w["w_hh"], np.float64)))
+        cell.bias_ih.zero_()
+        cell.bias_hh.zero_()
+        h = torch.from_numpy(prev)[None]
+        for t in toks:
+            h = cell(torch.from_numpy(np.asarray(w["emb"][t], np.float64))[None], h)
+    np.testing.assert_allclose(got, h[0].numpy(), rtol=0, atol=1e-12)
+    np.testing.assert_array_equal(chain.fold_state(head, prev, []), prev)

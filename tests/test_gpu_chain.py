@@ -103,3 +103,53 @@ def test_lm_head_route(dev):
     base[0] = ref.lm_head_logits(req["hidden"][0], w["w_lm"], True)
     exact, ties = compare(spec, w, req, got, [0], base=base)
     assert exact + ties == 1
+
+
+@pytest.mark.parametrize("name,L", [("tiny", 1), ("tiny", 6), ("q8b_b1", 3)])
+def test_fold_state(dev, name, L):
+    import torch
+    from oracle import chain as ochain
+    spec, w, req = synth.workload(name)
+    bf16 = spec.wdtype == "bf16"
+    head = ref.make_head(w, bf16, spec.act_bf16)
+    rng = np.random.default_rng(L)
+    B = 5
+    toks = rng.integers(0, spec.V, (B, L)).astype(np.int32)
+    prev = rng.normal(0, 0.5, (B, spec.ds)).astype(np.float32)
+    tb = gu.make_builder(spec, w, max_batch=B)
+    got = tb.fold_state(torch.from_numpy(toks).cuda(), torch.from_numpy(prev).cuda())
+    zero = tb.fold_state(torch.from_numpy(toks[:, :1].copy()).cuda())
+    tb.sync_status()
+    got, zero = got.cpu().numpy(), zero.cpu().numpy()
+    tb.close()
+    tol = 2e-3 if bf16 else 1e-5
+    for b in range(B):
+        want = ochain.fold_state(head, prev[b].astype(np.float64), toks[b])
+        np.testing.assert_allclose(got[b], want, rtol=0, atol=tol, err_msg=f"request {b}")
+        want0 = ochain.fold_state(head, np.zeros(spec.ds), toks[b, :1])
+        np.testing.assert_allclose(zero[b], want0, rtol=0, atol=tol, err_msg=f"request {b} from zeros")
+
+
+def test_fold_then_build(dev):
+    # the folded state as the root state of a build: the tree equals the
+    # oracle's tree from the oracle's folded state
+    import torch
+    from oracle import certify
+    from oracle import chain as ochain
+    spec, w, req = synth.workload("tiny")
+    head = ref.make_head(w, False, False)
+    toks = np.array([[5, 77, 1000]], np.int32)
+    tb = gu.make_builder(spec, w)
+    root = tb.fold_state(torch.from_numpy(toks).cuda())
+    out = tb.build(gu.to_dev(req["hidden"]), gu.to_dev(req["base"]), root, top_m=spec.M, top_k=spec.k,
+                   budget=spec.N, temperature=spec.T)
+    tb.sync_status()
+    got = {k: v.cpu().numpy() for k, v in out.items()}
+    tb.close()
+    root_o = ochain.fold_state(head, np.zeros(spec.ds), toks[0])
+    hid = req["hidden"][0].astype(np.float64)
+    t = ref.build_tree(head, req["base"][0], hid, root_o, spec.M, spec.k, spec.N, spec.T, spec.norm)
+    other = {k: got[k][0] for k in ("tokens", "parents", "depths", "scores")}
+    other["n_nodes"] = int(got["n_nodes"][0])
+    rep = certify.compare(t, head, hid, root_o, other, spec.k, spec.T, spec.norm, spec.N, gu.TOL_F32)
+    assert rep.ok and rep.exact, rep
