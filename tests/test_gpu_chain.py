@@ -153,3 +153,18 @@ def test_fold_then_build(dev):
     other["n_nodes"] = int(got["n_nodes"][0])
     rep = certify.compare(t, head, hid, root_o, other, spec.k, spec.T, spec.norm, spec.N, gu.TOL_F32)
     assert rep.ok and rep.exact, rep
+
+
+@pytest.mark.parametrize("B", [6, 9, 32])
+def test_small_fp32_batches(dev, B):
+    # every request-group width of the correction kernel (8, 16, 32), fp32
+    # weights, a vocabulary that is not a multiple of the block size, random
+    # root states
+    spec = synth.small(f"chain_b{B}", group=700 + B, V=3001, D=5, h=32, e=24, ds=64, r=32, M=8, k=2, N=10,
+                       B=B, root_std=0.5)
+    spec, w, req = synth.workload(spec)
+    tb = gu.make_builder(spec, w)
+    got = run_chain(tb, spec, req)
+    tb.close()
+    exact, ties = compare(spec, w, req, got, range(B))
+    assert exact == B, (exact, ties)

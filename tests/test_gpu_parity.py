@@ -49,6 +49,7 @@ SMALL = [
     ("m_eq_v", dict(V=6, D=3, h=8, e=8, ds=4, r=4, M=6, k=6, N=100)),
     ("m64_k8_b8", dict(V=20000, D=7, h=64, e=64, ds=128, r=64, M=64, k=8, N=120, B=8)),
     ("deep_d31", dict(V=400, D=31, h=16, e=16, ds=32, r=16, M=4, k=2, N=80)),
+    ("max_budget_n1024", dict(V=1500, D=12, h=16, e=16, ds=32, r=16, M=16, k=4, N=1024, B=2)),
 ]
 
 
