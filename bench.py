@@ -218,9 +218,9 @@ def main():
     # the greedy chain head over the whole vocabulary on the same weights and
     # inputs, for the whole batch and for its first request alone
     chain_ms = {}
-    for nb in ((spec.B, 1) if spec.B > 1 else (1,)):
-        hid_b = hidden[:nb].contiguous()
-        base_b = base[:nb].contiguous() if base is not None else None
+    for cb in ((spec.B, 1) if spec.B > 1 else (1,)):
+        hid_b = hidden[:cb].contiguous()
+        base_b = base[:cb].contiguous() if base is not None else None
         co = tb.chain(hid_b, base_b)
         c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         c0.record(stream)
@@ -229,7 +229,7 @@ def main():
         c1.record(stream)
         torch.cuda.synchronize()
         tb.sync_status()
-        chain_ms[f"batch_{nb}"] = c0.elapsed_time(c1) / args.steps
+        chain_ms[f"batch_{cb}"] = c0.elapsed_time(c1) / args.steps
     n_nodes = out["n_nodes"].cpu().numpy()
     assert np.all(n_nodes == spec.N), n_nodes
 

@@ -285,18 +285,21 @@ __global__ void gemm_f32_kernel(const float* __restrict__ A, const float* __rest
   C[(size_t)m * ldc + n] = s + (bias ? bias[n] : 0.f);
 }
 
-// Small outputs (few 128 x 128 tiles): one 32 x 32 output tile per block, the
-// four waves split K and their partial tiles are summed in LDS in a fixed
-// order.  Operands are read straight from global memory (16 bytes per lane).
-__global__ __launch_bounds__(256) void gemm_bf16_small_kernel(const uint16_t* __restrict__ A,
-                                                              const uint16_t* __restrict__ Bt,
-                                                              const float* __restrict__ bias,
-                                                              float* __restrict__ C, int M, int N, int K,
-                                                              int ldc) {
-  __shared__ float part[4][32 * 32];
+// Small outputs (few 128 x 128 tiles): one 32 x 32 output tile per block of
+// sixteen waves; the waves split K (a multiple of 16 each, at most four
+// 64-k steps at K = 4096) so that each wave's operand loads are few and go
+// out together, and their partial tiles are summed in LDS in a fixed order.
+// Operands are read straight from global memory (16 bytes per lane).
+constexpr int SW = 16;  // waves per block
+__global__ __launch_bounds__(64 * SW) void gemm_bf16_small_kernel(const uint16_t* __restrict__ A,
+                                                                  const uint16_t* __restrict__ Bt,
+                                                                  const float* __restrict__ bias,
+                                                                  float* __restrict__ C, int M, int N, int K,
+                                                                  int ldc) {
+  __shared__ float part[SW][32 * 32];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int m0 = blockIdx.y * 32, n0 = blockIdx.x * 32;
-  const int kq = ((K + 15) / 16 + 3) / 4 * 16;  // k per wave, a multiple of 16
+  const int kq = ((K + 15) / 16 + SW - 1) / SW * 16;  // k per wave, a multiple of 16
   const int kb = w * kq, ke = min(K, kb + kq);
   floatx16 acc;
 #pragma unroll
@@ -317,11 +320,17 @@ __global__ __launch_bounds__(256) void gemm_bf16_small_kernel(const uint16_t* __
 #pragma unroll
   for (int e = 0; e < 16; ++e) part[w][(8 * (e >> 2) + 4 * (lane >> 5) + (e & 3)) * 32 + (lane & 31)] = acc[e];
   __syncthreads();
-  for (int i = tid; i < 32 * 32; i += 256) {
-    const int row = m0 + i / 32, col = n0 + i % 32;
-    if (row < M && col < N)
-      C[(size_t)row * ldc + col] = ((part[0][i] + part[1][i]) + (part[2][i] + part[3][i])) + (bias ? bias[col] : 0.f);
-  }
+  // one output element per thread: the sixteen partials summed pairwise
+  const int i = tid;
+  float t[SW];
+#pragma unroll
+  for (int x = 0; x < SW; ++x) t[x] = part[x][i];
+#pragma unroll
+  for (int h = SW / 2; h >= 1; h >>= 1)
+#pragma unroll
+    for (int x = 0; x < h; ++x) t[x] = t[x] + t[x + h];
+  const int row = m0 + i / 32, col = n0 + i % 32;
+  if (row < M && col < N) C[(size_t)row * ldc + col] = t[0] + (bias ? bias[col] : 0.f);
 }
 
 hipError_t launch_gemm_bf16(const uint16_t* A, const int32_t* rows, const uint16_t* Bt, const float* bias,
@@ -340,7 +349,7 @@ hipError_t launch_gemm_bf16(const uint16_t* A, const int32_t* rows, const uint16
   const long tiles = (long)((N + GT - 1) / GT) * ((M + GT - 1) / GT);
   if (tiles < 256) {
     dim3 grid((N + 31) / 32, (M + 31) / 32);
-    hipLaunchKernelGGL(gemm_bf16_small_kernel, grid, dim3(256), 0, stream, A, Bt, bias, C, M, N, K, ldc);
+    hipLaunchKernelGGL(gemm_bf16_small_kernel, grid, dim3(64 * SW), 0, stream, A, Bt, bias, C, M, N, K, ldc);
     return hipGetLastError();
   }
   dim3 grid((N + GT - 1) / GT, (M + GT - 1) / GT);
