@@ -129,6 +129,99 @@ __global__ __launch_bounds__(CT) void chain_correct_kernel(const T* __restrict__
   }
 }
 
+// bf16 weights: the product W2^T a on the matrix cores.  a (fp32) is split
+// into a_hi = bf16(a) and a_lo = bf16(a - a_hi), and dL = W2^T a_hi +
+// W2^T a_lo is two v_mfma_f32_32x32x16_bf16 per 16 k with fp32
+// accumulation: each product is exact, and what a_hi + a_lo leaves out of a
+// is below 2^-16 of it.  A wave takes 32-row tiles of W2^T (the MFMA A
+// operand, read straight from memory, a tile's sixteen 16-byte loads per lane
+// issued together and the next tile's before this tile's MFMAs) against the
+// 32 request columns of a (the B operand, bf16 rows padded in LDS); the
+// accumulator lane holds request (lane & 31) for 16 rows, so the best
+// (corrected logit, token) per request is kept per lane.
+typedef __bf16 chain_bf16x8 __attribute__((ext_vector_type(8)));
+typedef float chain_floatx16 __attribute__((ext_vector_type(16)));
+constexpr int MT = 2;                 // 32-row tiles per wave
+constexpr int MROWS = 4 * MT * 32;    // rows per block
+constexpr int AROW = CHAIN_MAX_RANK + 8;  // bf16 per LDS row of a_hi / a_lo (padded)
+
+__global__ __launch_bounds__(CT) void chain_correct_mfma_kernel(const uint16_t* __restrict__ w2t,
+                                                                const float* __restrict__ base,
+                                                                const float* __restrict__ P,
+                                                                const float* __restrict__ gu, int B, int D, int d,
+                                                                int V, int r, int gstride, int goff,
+                                                                uint64_t* __restrict__ part) {
+  __shared__ __attribute__((aligned(16))) uint16_t ahi[32 * AROW];
+  __shared__ __attribute__((aligned(16))) uint16_t alo[32 * AROW];
+  __shared__ uint64_t wbest[CT / 64][32];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  for (int t = tid; t < 32 * r; t += CT) {
+    const int b = t / r, j = t - b * r;
+    float v = 0.f;
+    if (b < B) {
+      const float u = P[((size_t)b * D + d) * r + j] + gu[(size_t)b * gstride + goff + j];
+      v = u / (1.f + expf(-u));  // SiLU
+    }
+    const uint16_t hi = f32_to_bf16(v);
+    ahi[b * AROW + j] = hi;
+    alo[b * AROW + j] = f32_to_bf16(v - bf16_to_f32(hi));
+  }
+  __syncthreads();
+  const int fr = lane & 31, fk = 8 * (lane >> 5);
+  const int ks = r / 16;  // 16-k steps
+  const int vbase = blockIdx.x * MROWS + wv * MT * 32;
+  uint64_t best = 0ull;
+  uint4 q[2][CHAIN_MAX_RANK / 16];
+  auto load_tile = [&](int tile, uint4 (&dst)[CHAIN_MAX_RANK / 16]) {
+    const int vr = min(vbase + tile * 32 + fr, V - 1);
+    const uint16_t* row = w2t + (size_t)vr * r + fk;
+#pragma unroll
+    for (int s = 0; s < CHAIN_MAX_RANK / 16; ++s)
+      if (s < ks) dst[s] = *reinterpret_cast<const uint4*>(row + 16 * s);
+  };
+  load_tile(0, q[0]);
+#pragma unroll
+  for (int tile = 0; tile < MT; ++tile) {
+    if (tile + 1 < MT) load_tile(tile + 1, q[(tile + 1) & 1]);
+    chain_floatx16 acc;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[e] = 0.f;
+#pragma unroll
+    for (int s = 0; s < CHAIN_MAX_RANK / 16; ++s) {
+      if (s < ks) {
+        const chain_bf16x8 av = *reinterpret_cast<const chain_bf16x8*>(&q[tile & 1][s]);
+        const chain_bf16x8 bh = *reinterpret_cast<const chain_bf16x8*>(&ahi[fr * AROW + 16 * s + fk]);
+        const chain_bf16x8 bl = *reinterpret_cast<const chain_bf16x8*>(&alo[fr * AROW + 16 * s + fk]);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bh, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bl, acc, 0, 0, 0);
+      }
+    }
+    // lane: request fr, rows 8 (e / 4) + 4 (lane >> 5) + (e % 4) of the tile
+    if (fr < B) {
+      const float* brow = base + ((size_t)fr * D + d) * V;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int v = vbase + tile * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+        if (v < V) {
+          const uint64_t c = cand_pack(f32_key(brow[v] + acc[e]), (uint32_t)v);
+          best = c > best ? c : best;
+        }
+      }
+    }
+  }
+  // lanes l and l + 32 hold the same request
+  const uint64_t o = shfl_xor_u64(best, 32);
+  best = o > best ? o : best;
+  if (lane < 32) wbest[wv][lane] = best;
+  __syncthreads();
+  if (tid < B) {
+    uint64_t m = wbest[0][tid];
+#pragma unroll
+    for (int w = 1; w < CT / 64; ++w) m = wbest[w][tid] > m ? wbest[w][tid] : m;
+    part[(size_t)tid * gridDim.x + blockIdx.x] = m;
+  }
+}
+
 // S <- GRU(S, x) for one request, the input term gi = W_ih x + b_ih given
 // (a row of G): gate rows (r, z, n), the reset gate on (W_hn S + b_hn),
 // S' = (1 - z) n + z S; S' also goes to s_op (bf16, nearest-even, or fp32)
@@ -208,6 +301,7 @@ __global__ void chain_init_kernel(const float* __restrict__ root, int n, float* 
 }
 
 int chain_blocks(int V) { return (V + CT - 1) / CT; }
+int chain_mfma_blocks(int V) { return (V + MROWS - 1) / MROWS; }
 
 hipError_t launch_fold(const ChainArgs& c, const int32_t* tokens, int L, float* out, hipStream_t stream) {
   if (c.B < 1 || L < 1) return hipErrorInvalidValue;
@@ -261,7 +355,10 @@ hipError_t launch_chain(const ChainArgs& c, hipStream_t stream) {
 #define CHAIN_CORRECT(T, NB)                                                                                  \
   hipLaunchKernelGGL((chain_correct_kernel<T, NB>), dim3(nblk), dim3(CT), 0, stream, (const T*)c.w2t, c.base, \
                      c.P, c.gu, c.B, c.D, d, c.V, c.r, gstride, goff, c.part)
-    if (c.bf16) {
+    if (c.bf16 && c.r % 16 == 0) {
+      hipLaunchKernelGGL(chain_correct_mfma_kernel, dim3(chain_mfma_blocks(c.V)), dim3(CT), 0, stream,
+                         (const uint16_t*)c.w2t, c.base, c.P, c.gu, c.B, c.D, d, c.V, c.r, gstride, goff, c.part);
+    } else if (c.bf16) {
       if (c.B <= 4) CHAIN_CORRECT(uint16_t, 4);
       else if (c.B <= 8) CHAIN_CORRECT(uint16_t, 8);
       else if (c.B <= 16) CHAIN_CORRECT(uint16_t, 16);
@@ -277,11 +374,12 @@ hipError_t launch_chain(const ChainArgs& c, hipStream_t stream) {
     if (e != hipSuccess) return e;
     // 3. the pick, then the state for the next position
     const int adv = d + 1 < c.D;
+    const int np = (c.bf16 && c.r % 16 == 0) ? chain_mfma_blocks(c.V) : nblk;
     if (c.bf16)
-      hipLaunchKernelGGL(chain_pick_kernel<uint16_t>, dim3(c.B), dim3(CT), 0, stream, c.part, nblk, c.V, c.G, c.gu,
+      hipLaunchKernelGGL(chain_pick_kernel<uint16_t>, dim3(c.B), dim3(CT), 0, stream, c.part, np, c.V, c.G, c.gu,
                          c.b_hh, gstride, c.ds, c.D, d, adv, c.s, (uint16_t*)c.s_op, c.tokens, c.logits);
     else
-      hipLaunchKernelGGL(chain_pick_kernel<float>, dim3(c.B), dim3(CT), 0, stream, c.part, nblk, c.V, c.G, c.gu,
+      hipLaunchKernelGGL(chain_pick_kernel<float>, dim3(c.B), dim3(CT), 0, stream, c.part, np, c.V, c.G, c.gu,
                          c.b_hh, gstride, c.ds, c.D, d, adv, c.s, (float*)c.s_op, c.tokens, c.logits);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
