@@ -157,9 +157,14 @@ def main():
     pkg.load_library()   # fails loudly when the HIP library is missing
     assert torch.cuda.is_available(), "bench.py needs a HIP device"
     spec, w, req = synth.workload(args.workload)
-    tb = pkg.TreeBuilder({k: to_dev(v) for k, v in w.items()}, vocab=spec.V, depths=spec.D,
+    wdev = {k: to_dev(v) for k, v in w.items()}
+    torch.cuda.synchronize()
+    tc0 = time.perf_counter()
+    tb = pkg.TreeBuilder(wdev, vocab=spec.V, depths=spec.D,
                          hidden=spec.h, emb_dim=spec.e, state_dim=spec.ds, rank=spec.r,
                          max_batch=spec.B, max_top_m=spec.M, max_top_k=spec.k, max_budget=spec.N)
+    torch.cuda.synchronize()
+    create_s = time.perf_counter() - tc0   # tables and prepack, once per weight set
     hidden = to_dev(req["hidden"])
     base = to_dev(req["base"]) if req["base"] is not None else None
     norm = pkg.DT_NORM_FULLV if spec.norm == "fullv" else pkg.DT_NORM_TOPM
@@ -195,6 +200,36 @@ def main():
     torch.cuda.synchronize()
     tb.sync_status()
     phases, nb = tb.phase_times()
+    # round-time distribution: ROUNDS builds one by one with events around
+    # each, warm (nothing in between) and cold (a 512 MB buffer written
+    # between builds, which evicts the caches: MALL and L2); the buffer
+    # write doubles as a measure of the box's achievable HBM bandwidth
+    ROUNDS = 50
+    scratch = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    dist = {}
+    for mode in ("warm", "cold"):
+        ts = []
+        for _ in range(ROUNDS):
+            if mode == "cold":
+                scratch.fill_(1)
+            r0, r1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            r0.record(stream)
+            step()
+            r1.record(stream)
+            torch.cuda.synchronize()
+            ts.append(r0.elapsed_time(r1))
+        ts = np.array(ts)
+        dist[mode] = {"median_ms": float(np.median(ts)), "p10_ms": float(np.percentile(ts, 10)),
+                      "p90_ms": float(np.percentile(ts, 90))}
+    f0, f1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    f0.record()
+    for _ in range(10):
+        scratch.fill_(2)
+    f1.record()
+    torch.cuda.synchronize()
+    fill_gbs = 10 * scratch.numel() / (f0.elapsed_time(f1) * 1e-3) / 1e9
+    del scratch
+    tb.sync_status()
     # the verification inputs of the built trees (ancestor mask, positions,
     # flattened tokens), timed on the builder's stream beside the build
     prefix = torch.zeros(spec.B, dtype=torch.int32, device="cuda")
@@ -262,6 +297,9 @@ def main():
         "round_ms_events": ev_ms,
         "phases_ms": {"lm_head": phases[0], "candidates": phases[1], "P_join": phases[2],
                       "builder_setup": phases[3], "tree_kernel": tree_ms, "builds_averaged": nb},
+        "round_ms_distribution": dict(dist, rounds=ROUNDS),
+        "handle_create_s": create_s,
+        "hbm_write_gbs_measured": fill_gbs,
         "chain_head_ms": dict(chain_ms, positions=spec.D, launch="dt_draft_chain (greedy, full vocabulary)"),
         "verify_inputs": {"ms": verify_ms, "launch": "dt_tree_attention_inputs",
                           "bytes": spec.B * (spec.N + 1) * 4 * (5 + (spec.N + 32) // 32) + spec.B * 12},
@@ -274,6 +312,7 @@ def main():
             "frac": achieved / HBM_PEAK_GBS,
             "traffic": measured_traffic(spec.name),
             "algorithmic_bytes": ab,
+            "frac_vs_measured_write_bw": achieved / fill_gbs,
         },
     }
     if base is None:
