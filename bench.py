@@ -295,7 +295,7 @@ def main():
         },
         "us_per_tree": wall_ms * 1e3 / spec.B,
         "round_ms_events": ev_ms,
-        "phases_ms": {"lm_head": phases[0], "candidates": phases[1], "P_join": phases[2],
+        "phases_ms": {"lm_head_or_P": phases[0], "candidates": phases[1], "P_join": phases[2],
                       "builder_setup": phases[3], "tree_kernel": tree_ms, "builds_averaged": nb},
         "round_ms_distribution": dict(dist, rounds=ROUNDS),
         "handle_create_s": create_s,

@@ -142,7 +142,7 @@ def dt_sync_status(handle: int, stream: int = 0):
     _check(load_library().dt_sync_status(C.c_void_p(handle), C.c_void_p(stream)))
 
 
-PHASES = ["lm_head", "candidates", "P", "mailbox_reset", "tree_kernel"]
+PHASES = ["lm_head_or_P", "candidates", "P_join", "builder_setup", "tree_kernel"]
 
 
 def dt_phase_times(handle: int) -> tuple:
@@ -293,9 +293,9 @@ class TreeBuilder:
         dt_sync_status(self.handle, self.stream.cuda_stream)
 
     def phase_times(self) -> tuple:
-        """Mean ms per phase (lm_head, candidates, P, mailbox_reset,
-        tree_kernel) of the DT_TIMING builds since the previous call, and
-        how many builds were averaged."""
+        """Mean ms per phase (PHASES order: the LM head or P, candidates, the
+        wait for P, builder set-up, tree kernel) of the DT_TIMING builds since
+        the previous call, and how many builds were averaged."""
         return dt_phase_times(self.handle)
 
 

@@ -329,17 +329,25 @@ dt_status dt_build_trees(dt_handle* h, const dt_inputs* in, const dt_params* p, 
   }
 
   // a2: P = H W1_H (the path-independent half of W1 [H_d; S]) needs only the
-  // hidden states: it runs on the side stream while the candidates are chosen
+  // hidden states.  Beside the LM-head GEMM (on the handle's side stream) it
+  // costs nothing; with base logits given it runs first on the caller's
+  // stream (measured: beside the candidate selection the two contend for
+  // memory and P ends ~10 us after it; alone first it takes ~12 us and the
+  // selection ~10 us less)
   MARK(0);
-  HIPCHK(hipEventRecord(h->fork_ev, stream));
-  HIPCHK(hipStreamWaitEvent(h->side, h->fork_ev, 0));
+  const bool p_inline = in->base_logits != nullptr;
+  hipStream_t ps = p_inline ? stream : h->side;
+  if (!p_inline) {
+    HIPCHK(hipEventRecord(h->fork_ev, stream));
+    HIPCHK(hipStreamWaitEvent(h->side, h->fork_ev, 0));
+  }
   if (h->bf16)
     HIPCHK(dt::launch_gemm_bf16((const uint16_t*)in->hidden, nullptr, (const uint16_t*)h->w1h_t, nullptr, h->P,
-                                rows, d.rank, d.hidden, d.rank, h->side));
+                                rows, d.rank, d.hidden, d.rank, ps));
   else
     HIPCHK(dt::launch_gemm_f32((const float*)in->hidden, nullptr, (const float*)h->w1h_t, nullptr, h->P, rows,
-                               d.rank, d.hidden, d.rank, h->side));
-  HIPCHK(hipEventRecord(h->join_ev, h->side));
+                               d.rank, d.hidden, d.rank, ps));
+  if (!p_inline) HIPCHK(hipEventRecord(h->join_ev, h->side));
   // a0 (LM head, when no base logits are given), then a1: candidates and LSE
   if (!in->base_logits) {
     // L_base = H W_lm (Domino summary, 方法步骤详情), fp32 accumulate
@@ -359,7 +367,7 @@ dt_status dt_build_trees(dt_handle* h, const dt_inputs* in, const dt_params* p, 
   }
   // join: what P adds after the candidates are done
   MARK(2);
-  HIPCHK(hipStreamWaitEvent(stream, h->join_ev, 0));
+  if (!p_inline) HIPCHK(hipStreamWaitEvent(stream, h->join_ev, 0));
 
   // a3-a8: the persistent builder
   dt::TreeArgs a{};

@@ -164,9 +164,10 @@ dt_status dt_create(dt_handle** h, const dt_dims* dims, const dt_weights* w,
 
 /* Build the trees of one batch [DominoTree, 1, 2, 4].  Enqueues the kernels on
  * `stream` and returns: no host synchronisation and no allocation.  Results
- * are valid once the stream reaches this point.  P = H W1_H runs on a stream
+ * are valid once the stream reaches this point.  P = H W1_H runs first on
+ * `stream` when base logits are given; with the LM head it runs on a stream
  * the handle owns (default priority), forked from and joined back into
- * `stream` with events, beside the candidate selection.  A handle must not be
+ * `stream` with events, beside the LM-head GEMM.  A handle must not be
  * used by two builds at once (one workspace).  When in->base_logits is NULL the
  * base logits are computed from in->hidden with w_lm [Domino, Steps] into a
  * handle-owned fp32 workspace, from which the candidates and LSE are taken.
@@ -183,9 +184,9 @@ dt_status dt_sync_status(dt_handle* h, void* stream);
 
 /* Mean durations, in milliseconds, of the phases of the builds made with
  * DT_TIMING since the previous call (at most the last 256 of them), measured
- * with HIP events recorded on each build's stream: ms[0] the LM head (0 when
- * base logits are given), ms[1] per-depth candidates (top-M + LSE), ms[2]
- * the wait for P = H W1_H after the candidates (it runs beside them), ms[3]
+ * with HIP events recorded on each build's stream: ms[0] the LM head, or
+ * P = H W1_H when base logits are given, ms[1] per-depth candidates (top-M +
+ * LSE), ms[2] the wait for P after them (LM head only), ms[3]
  * the builder's set-up (a mailbox clear only when the epoch space wraps),
  * ms[4] the tree builder kernel.  Waits for
  * those events, writes min(n, 5) values and the number of builds averaged to
