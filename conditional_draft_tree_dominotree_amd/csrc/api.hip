@@ -52,6 +52,7 @@ struct dt_handle {
   void* w2t = nullptr;      // [V, r]
   void* wlm_t = nullptr;    // W_lm^T: tiled for the LM-head GEMM (wlm_tiled) or [V, h]; or null
   bool wlm_tiled = false;
+  uint16_t* a_tiles = nullptr;  // H in the LM-head GEMM's tile order (per call)
   float* logits = nullptr;  // [max_batch, D, V] base logits computed by the LM head
   void* wc_rm = nullptr;    // [3 ds + r, ds] row-major [W_hh ; W1_S^T] (the chain head)
   int n_tiles = 0;
@@ -104,7 +105,7 @@ void free_all(dt_handle* h) {
                   h->chunk_cand, h->chunk_stat, h->cand_ids, h->cand_vals, h->tokrank, h->lse,
                   h->tail,    h->P,        h->state,    h->act,   h->gh,       h->u,
                   h->ninfo,   h->mbox_w,   h->mbox_c,   h->err,   h->nanflag, h->wc_rm,
-                  h->chain_gu, h->chain_s, h->chain_sop, h->chain_part};
+                  h->chain_gu, h->chain_s, h->chain_sop, h->chain_part, h->a_tiles};
   for (void* p : ptrs)
     if (p) (void)hipFree(p);
   for (auto& set : h->ev)
@@ -239,6 +240,7 @@ dt_status dt_create(dt_handle** out, const dt_dims* dims, const dt_weights* w, c
       // tile is one contiguous 16 KB piece
       h->wlm_tiled = true;
       ALLOC(h->wlm_t, dt::gemm_b_tiles_elems(V, hd) * esz);
+      ALLOC(h->a_tiles, dt::gemm_a_tiles_elems(Bm * D, hd) * esz);
       HIPB(dt::launch_pack_b_tiles((const uint16_t*)w->w_lm, (uint16_t*)h->wlm_t, hd, V, stream));
     } else {
       ALLOC(h->wlm_t, (size_t)V * hd * esz);
@@ -353,7 +355,7 @@ dt_status dt_build_trees(dt_handle* h, const dt_inputs* in, const dt_params* p, 
     // L_base = H W_lm (Domino summary, 方法步骤详情), fp32 accumulate
     if (h->wlm_tiled)
       HIPCHK(dt::launch_gemm_bf16_btiled((const uint16_t*)in->hidden, (const uint16_t*)h->wlm_t, h->logits, rows, V,
-                                         d.hidden, V, stream));
+                                         d.hidden, V, h->a_tiles, stream));
     else
       HIPCHK(dt::launch_gemm_bf16((const uint16_t*)in->hidden, nullptr, (const uint16_t*)h->wlm_t, nullptr,
                                   h->logits, rows, V, d.hidden, V, stream));
@@ -500,7 +502,7 @@ dt_status dt_draft_chain(dt_handle* h, const dt_inputs* in, uint32_t flags, int3
   if (!in->base_logits) {
     if (h->wlm_tiled)
       HIPCHK(dt::launch_gemm_bf16_btiled((const uint16_t*)in->hidden, (const uint16_t*)h->wlm_t, h->logits, rows, V,
-                                         d.hidden, V, stream));
+                                         d.hidden, V, h->a_tiles, stream));
     else
       HIPCHK(dt::launch_gemm_bf16((const uint16_t*)in->hidden, nullptr, (const uint16_t*)h->wlm_t, nullptr,
                                   h->logits, rows, V, d.hidden, V, stream));
