@@ -55,6 +55,7 @@ struct dt_handle {
   uint16_t* a_tiles = nullptr;  // H in the LM-head GEMM's tile order (per call)
   float* logits = nullptr;  // [max_batch, D, V] base logits computed by the LM head
   void* wc_rm = nullptr;    // [3 ds + r, ds] row-major [W_hh ; W1_S^T] (the chain head)
+  void* w2f = nullptr;      // bf16 W2^T in the chain head's MFMA fragment order, or null
   int n_tiles = 0;
   // workspace
   uint64_t* chunk_cand = nullptr;
@@ -105,7 +106,7 @@ void free_all(dt_handle* h) {
                   h->chunk_cand, h->chunk_stat, h->cand_ids, h->cand_vals, h->tokrank, h->lse,
                   h->tail,    h->P,        h->state,    h->act,   h->gh,       h->u,
                   h->ninfo,   h->mbox_w,   h->mbox_c,   h->err,   h->nanflag, h->wc_rm,
-                  h->chain_gu, h->chain_s, h->chain_sop, h->chain_part, h->a_tiles};
+                  h->chain_gu, h->chain_s, h->chain_sop, h->chain_part, h->a_tiles, h->w2f};
   for (void* p : ptrs)
     if (p) (void)hipFree(p);
   for (auto& set : h->ev)
@@ -253,6 +254,10 @@ dt_status dt_create(dt_handle** out, const dt_dims* dims, const dt_weights* w, c
   HIPB(hipMemcpyAsync(h->wc_rm, w->w_hh, (size_t)3 * ds * ds * esz, hipMemcpyDeviceToDevice, stream));
   HIPB(dt::launch_transpose((const char*)w->w1 + (size_t)hd * r * esz, (char*)h->wc_rm + (size_t)3 * ds * ds * esz,
                             ds, r, (int)esz, stream));
+  if (h->bf16 && r % 16 == 0 && r <= dt::CHAIN_MAX_RANK) {
+    ALLOC(h->w2f, dt::chain_w2_frags_elems(V, r) * esz);
+    HIPB(dt::launch_pack_w2_frags((const uint16_t*)h->w2t, (uint16_t*)h->w2f, V, r, stream));
+  }
   ALLOC(h->chain_gu, (size_t)Bm * (3 * ds + r) * sizeof(float));
   ALLOC(h->chain_s, (size_t)Bm * ds * sizeof(float));
   ALLOC(h->chain_sop, (size_t)Bm * ds * esz);
@@ -515,6 +520,7 @@ dt_status dt_draft_chain(dt_handle* h, const dt_inputs* in, uint32_t flags, int3
   c.r = d.rank;
   c.bf16 = h->bf16;
   c.w2t = h->w2t;
+  c.w2f = h->w2f;
   c.wc = h->wc_rm;
   c.G = h->G;
   c.b_hh = h->b_hh;

@@ -145,7 +145,7 @@ constexpr int MT = 2;                 // 32-row tiles per wave
 constexpr int MROWS = 4 * MT * 32;    // rows per block
 constexpr int AROW = CHAIN_MAX_RANK + 8;  // bf16 per LDS row of a_hi / a_lo (padded)
 
-__global__ __launch_bounds__(CT) void chain_correct_mfma_kernel(const uint16_t* __restrict__ w2t,
+__global__ __launch_bounds__(CT) void chain_correct_mfma_kernel(const uint16_t* __restrict__ w2f,
                                                                 const float* __restrict__ base,
                                                                 const float* __restrict__ P,
                                                                 const float* __restrict__ gu, int B, int D, int d,
@@ -172,12 +172,16 @@ __global__ __launch_bounds__(CT) void chain_correct_mfma_kernel(const uint16_t* 
   const int vbase = blockIdx.x * MROWS + wv * MT * 32;
   uint64_t best = 0ull;
   uint4 q[2][CHAIN_MAX_RANK / 16];
+  // w2f: W2^T in fragment order (launch_pack_w2_frags): the 16-byte operand
+  // pieces of the 64 lanes for (32-row tile, 16-k step) are one contiguous
+  // 1 KB, so each load instruction moves eight whole 128-byte lines
+  const int ntile = (V + 31) / 32;
   auto load_tile = [&](int tile, uint4 (&dst)[CHAIN_MAX_RANK / 16]) {
-    const int vr = min(vbase + tile * 32 + fr, V - 1);
-    const uint16_t* row = w2t + (size_t)vr * r + fk;
+    const int tg = min((vbase >> 5) + tile, ntile - 1);
+    const uint4* src = reinterpret_cast<const uint4*>(w2f) + (size_t)tg * ks * 64 + lane;
 #pragma unroll
     for (int s = 0; s < CHAIN_MAX_RANK / 16; ++s)
-      if (s < ks) dst[s] = *reinterpret_cast<const uint4*>(row + 16 * s);
+      if (s < ks) dst[s] = src[s * 64];
   };
   load_tile(0, q[0]);
 #pragma unroll
@@ -300,6 +304,32 @@ __global__ void chain_init_kernel(const float* __restrict__ root, int n, float* 
   }
 }
 
+// W2^T [V, r] bf16 -> fragment order [ceil(V / 32)][r / 16][64 lanes][8]:
+// lane l of (tile t, step s) holds row 32 t + (l & 31), k 16 s + 8 (l >> 5)
+// .. + 7 (the v_mfma_f32_32x32x16_bf16 A-operand piece); rows past V zero.
+__global__ void pack_w2_frags_kernel(const uint16_t* __restrict__ w2t, uint16_t* __restrict__ out, int V, int r) {
+  const int ks = r / 16;
+  const size_t n = (size_t)((V + 31) / 32) * ks * 64;
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) {
+    const int l = (int)(i & 63);
+    const size_t ts = i >> 6;
+    const int st = (int)(ts % ks);
+    const size_t t = ts / ks;
+    const size_t row = t * 32 + (l & 31);
+    uint4 q = make_uint4(0, 0, 0, 0);
+    if (row < (size_t)V) q = *reinterpret_cast<const uint4*>(w2t + row * r + 16 * st + 8 * (l >> 5));
+    reinterpret_cast<uint4*>(out)[i] = q;
+  }
+}
+
+size_t chain_w2_frags_elems(int V, int r) { return (size_t)((V + 31) / 32) * 32 * r; }
+
+hipError_t launch_pack_w2_frags(const uint16_t* w2t, uint16_t* out, int V, int r, hipStream_t stream) {
+  if (r % 16 || r > CHAIN_MAX_RANK) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(pack_w2_frags_kernel, dim3(2048), dim3(256), 0, stream, w2t, out, V, r);
+  return hipGetLastError();
+}
+
 int chain_blocks(int V) { return (V + CT - 1) / CT; }
 int chain_mfma_blocks(int V) { return (V + MROWS - 1) / MROWS; }
 
@@ -355,9 +385,9 @@ hipError_t launch_chain(const ChainArgs& c, hipStream_t stream) {
 #define CHAIN_CORRECT(T, NB)                                                                                  \
   hipLaunchKernelGGL((chain_correct_kernel<T, NB>), dim3(nblk), dim3(CT), 0, stream, (const T*)c.w2t, c.base, \
                      c.P, c.gu, c.B, c.D, d, c.V, c.r, gstride, goff, c.part)
-    if (c.bf16 && c.r % 16 == 0) {
+    if (c.w2f) {
       hipLaunchKernelGGL(chain_correct_mfma_kernel, dim3(chain_mfma_blocks(c.V)), dim3(CT), 0, stream,
-                         (const uint16_t*)c.w2t, c.base, c.P, c.gu, c.B, c.D, d, c.V, c.r, gstride, goff, c.part);
+                         (const uint16_t*)c.w2f, c.base, c.P, c.gu, c.B, c.D, d, c.V, c.r, gstride, goff, c.part);
     } else if (c.bf16) {
       if (c.B <= 4) CHAIN_CORRECT(uint16_t, 4);
       else if (c.B <= 8) CHAIN_CORRECT(uint16_t, 8);
@@ -374,7 +404,7 @@ hipError_t launch_chain(const ChainArgs& c, hipStream_t stream) {
     if (e != hipSuccess) return e;
     // 3. the pick, then the state for the next position
     const int adv = d + 1 < c.D;
-    const int np = (c.bf16 && c.r % 16 == 0) ? chain_mfma_blocks(c.V) : nblk;
+    const int np = c.w2f ? chain_mfma_blocks(c.V) : nblk;
     if (c.bf16)
       hipLaunchKernelGGL(chain_pick_kernel<uint16_t>, dim3(c.B), dim3(CT), 0, stream, c.part, np, c.V, c.G, c.gu,
                          c.b_hh, gstride, c.ds, c.D, d, adv, c.s, (uint16_t*)c.s_op, c.tokens, c.logits);

@@ -60,6 +60,7 @@ constexpr int CHAIN_MAX_RANK = 256;
 struct ChainArgs {
   int B, D, V, ds, r, bf16;  // bf16: weights and the state operand in bf16
   const void* w2t;      // [V, r] (wdtype)
+  const void* w2f;      // bf16 W2^T in MFMA fragment order, or null (then the fp32-FMA kernel)
   const void* wc;       // [3 ds + r, ds] row-major: W_hh rows, then W1_S^T
   const float* G;       // [V, 3 ds] = E W_ih^T + b_ih
   const float* b_hh;    // [3 ds] or null
@@ -74,6 +75,8 @@ struct ChainArgs {
   float* logits;        // [B, D] or null
 };
 int chain_blocks(int V);
+size_t chain_w2_frags_elems(int V, int r);
+hipError_t launch_pack_w2_frags(const uint16_t* w2t, uint16_t* out, int V, int r, hipStream_t stream);
 hipError_t launch_chain(const ChainArgs& c, hipStream_t stream);
 // S <- GRU(S, E[t]) over tokens[b, 0..L-1] from c.root (zeros when null),
 // written to out [B, ds]; uses c's weights and workspaces (gu, s, s_op).
