@@ -43,7 +43,7 @@ def tree_kernel_bytes(spec) -> float:
     return float(spec.N) * (per_step_weights + spec.B * per_request)
 
 
-TREE_SOURCES = ["csrc/tree.hip", "csrc/kernels.h", "csrc/common.h"]
+TREE_SOURCES = ["csrc/tree.hip", "csrc/tree.h", "csrc/common.h"]
 
 
 def tree_source_hash() -> str:

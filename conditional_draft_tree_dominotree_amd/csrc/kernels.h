@@ -92,69 +92,7 @@ hipError_t launch_pack_node_tiles(const void* w_hh, const void* w1, int h, int d
                                   void* out, hipStream_t stream);
 hipError_t launch_fill_u32(uint32_t* p, uint32_t v, size_t n, hipStream_t stream);
 
-// ---- the tree builder (tree.hip)
-struct TreeArgs {
-  // shapes and parameters
-  int B, D, ds, r, M, k, N;
-  float T;
-  int fullv;
-  int act_bf16;
-  int n_workers;        // worker blocks; block ids [0, n_workers) are workers
-  int tiles_per_worker;
-  int n_tiles;          // (3 ds + r) / 16
-  // schedule (set by plan_tree)
-  int p;                // nodes a request may expand per step (exchange columns per request)
-  int kc;               // state elements a worker stages per phase (kp / kc phases)
-  int regw;             // 0: workers stage operands in LDS; register workers: 1 (1 tile per wave, 1
-                        // column block per block), 2 (2 tiles, 1 block), 3 (2 tiles, 2 blocks),
-                        // 4 (2 tiles, 4 blocks)
-  int ncbmax;           // register workers: 16-column blocks per step
-  int wadv;             // 1: the workers advance the GRU states of a step's nodes (register workers)
-  int xcap;             // node records per request (budget + root + speculation room)
-  int fcap;             // frontier entries per request
-  int qmax;             // frontier entries tested per pop round
-  int nslots;           // depth slots of W2 candidate rows in a controller's LDS
-  // read-only inputs
-  const void* tiles;       // packed [W_hh ; W1_S^T] tiles
-  const float* b_hh;       // [3 ds] or NULL
-  const float* G;          // [V, 3 ds]: W_ih E[v] + b_ih
-  const void* w2t;         // [V, r] (wdtype)
-  const float* P;          // [B, D, r]: H_d W1_H
-  const int32_t* cand_ids; // [B, D, M]
-  const float* cand_vals;  // [B, D, M]
-  const float* tail;       // [B, D]
-  const int32_t* tokrank;  // [B, D, M]
-  const float* root;       // [B, ds] or NULL
-  // write-once exchange slots, step-major: slot (t, b, j) = (t B + b) p + j
-  float* state;            // [slots, ds] fp32 GRU state of the node expanded in the slot
-  void* act;               // [slots, ds] its GEMM operand copy (wdtype)
-  float* gh;               // [slots, 3 ds]
-  float* u;                // [slots, r]
-  int32_t* ninfo;          // [steps][TREE_MAX_COLS][2]: token and parent slot of each node to advance
-  uint32_t* gflag;         // [16][64] worker group flags (states of a step advanced)
-  uint32_t* ready;         // [64] controller b: its start-up loads are done (the workers then load weights)
-  uint32_t* mbox_w;        // [n_workers][32] controller -> worker mailboxes (one line each)
-  uint32_t* mbox_c;        // [B][256] worker -> controller mailboxes
-  int* err;                // device error word
-  // outputs
-  int32_t *tokens, *parents, *depths, *n_nodes;
-  float* scores;
-  unsigned spin_limit;
-  uint32_t ebase;          // epochs of this launch: ebase + 1 .. ebase + tree_epoch_span(N) - 1
-};
-// Exchange columns a build may use per step (slots per step = B p <= this).
-constexpr int TREE_MAX_COLS = 512;
-constexpr int GFLAG_WORDS = 16 * 64 + 64;  // worker group flags and controller ready flags, before the
-                                            // worker mailboxes
-// Epochs a launch may use (at most N + 1 steps, the first post and the last).
-__host__ __device__ inline uint32_t tree_epoch_span(int N) { return (uint32_t)N + 8u; }
-constexpr uint32_t TREE_EPOCH_LIMIT = 1u << 27;  // mailbox words hold the epoch in 27 bits
-// Fills the schedule fields of `a` (p from `pops`, 0 = automatic) and returns
-// the dynamic LDS bytes the launch needs, or 0 if the shape cannot be served.
-// With register workers (allowed unless `lds_workers`) it also sets
-// n_workers, at most `max_workers`; otherwise n_workers and tiles_per_worker
-// are the caller's.
-size_t plan_tree(TreeArgs& a, int wdtype_bf16, int pops, int max_workers, int lds_workers);
-hipError_t launch_tree(const TreeArgs& a, int wdtype_bf16, size_t lds_bytes, hipStream_t stream);
-
 }  // namespace dt
+
+// the tree builder's arguments, schedule and launch (tree.hip)
+#include "tree.h"

@@ -49,7 +49,7 @@
 #include <algorithm>
 
 #include "common.h"
-#include "kernels.h"
+#include "tree.h"
 
 namespace dt {
 
