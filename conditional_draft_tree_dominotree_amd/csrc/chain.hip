@@ -8,12 +8,13 @@
 // Per position, three launches on the caller's stream:
 //   1. [W_hh S~ | W1_S^T S~] for the batch (the dense-product kernels), S~ the
 //      state as a matrix operand;
-//   2. chain_correct: one thread per vocabulary row; a = SiLU(P_d + W1_S^T S~)
-//      for every request sits in LDS as [j][b] (one 16-byte broadcast read
-//      serves four requests), the thread requests its whole W2^T row at once
-//      (32 x 16 bytes in registers for bf16) and keeps one accumulator per
-//      request; each block writes, per request, its best (corrected logit,
-//      token) composite;
+//   2. the correction of every token and, per block and request, the best
+//      (corrected logit, token) composite: with bf16 weights on the matrix
+//      cores (chain_correct_mfma_kernel, W2^T in fragment order, `a` split
+//      into two bf16 terms); with fp32 weights one thread per vocabulary row
+//      (chain_correct_kernel: a = SiLU(P_d + W1_S^T S~) for every request in
+//      LDS as [j][b], one 16-byte broadcast read serving four requests, the
+//      thread's W2^T row requested at once, one accumulator per request);
 //   3. chain_pick: one block per request reduces the block composites to the
 //      pick and advances the GRU state with G[pick] = E W_ih^T + b_ih (the
 //      handle's table) and the product of step 1.
