@@ -106,3 +106,53 @@ def test_wide_store_data_not_overwritten_next(asm, tmpl):
                 if _vregs(dst) & data:
                     bad.append((l, nxt))
     assert not bad, bad[:5]
+
+
+# ---- the dense-product and chain-head kernels
+
+CSRC = os.path.join(ROOT, "conditional_draft_tree_dominotree_amd", "csrc")
+
+
+def _compile(src, tmp_path_factory):
+    if not os.path.exists(HIPCC):
+        pytest.skip("hipcc not available")
+    out = tmp_path_factory.mktemp("codegen") / (os.path.basename(src) + ".s")
+    cmd = [HIPCC, "--offload-arch=gfx950", "-O3", "-std=c++17", "-Xclang", "-target-feature", "-Xclang",
+           "-packed-fp32-ops", "--cuda-device-only", "-S", "-o", str(out), os.path.join(CSRC, src)]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr[-2000:]
+    return out.read_text()
+
+
+def _body(asm_text, prefix):
+    lines = asm_text.split("\n")
+    label = re.compile(re.escape(prefix) + r"\w*:")
+    starts = [i for i, l in enumerate(lines) if label.match(l)]
+    assert starts, prefix
+    out = []
+    for s in starts:
+        name = lines[s].split(":")[0]
+        end = next(i for i in range(s, len(lines)) if "s_endpgm" in lines[i])
+        meta = re.search(re.escape(name) + r"\.private_seg_size, (\d+)", asm_text)
+        out.append((name, [l.strip() for l in lines[s:end]], int(meta.group(1)) if meta else None))
+    return out
+
+
+@pytest.mark.parametrize("src,prefix", [("gemm.hip", "_ZN2dt20gemm_bf16_big_kernel"),
+                                        ("chain.hip", "_ZN2dt25chain_correct_mfma_kernel"),
+                                        ("chain.hip", "_ZN2dt20chain_correct_kernel")])
+def test_dense_kernels_use_no_scratch(tmp_path_factory, src, prefix):
+    # a spill in these kernels costs a memory round trip per loop iteration
+    for name, body, priv in _body(_compile(src, tmp_path_factory), prefix):
+        assert not any(l.startswith("scratch_") for l in body), name
+        if priv is not None:
+            assert priv == 0, name
+
+
+def test_lm_gemm_waits_for_all_but_two_stages(tmp_path_factory):
+    # the LM-head GEMM's main loop waits for its oldest stage of operand
+    # loads only (two 8-instruction stages stay in flight), then the barrier
+    for name, body, _ in _body(_compile("gemm.hip", tmp_path_factory), "_ZN2dt20gemm_bf16_big_kernel"):
+        waits = [l for l in body if l.startswith("s_waitcnt vmcnt(16)")]
+        assert waits, name
+        assert sum(l.startswith("global_load_lds_dwordx4") for l in body) >= 16, name
