@@ -9,20 +9,26 @@
 // the correction's first projection (H_d is shared by every path: DominoTree
 // technical summary, Componenti Core 1).
 //
-// bf16, large outputs (the LM head H W_lm, and the fold E W_ih^T): a 256 x 256
-// block tile, 256 threads (2 x 2 waves of 128 x 128, sixteen 32 x 32
-// accumulator tiles per wave), v_mfma_f32_32x32x16_bf16.  Operands go from
-// global memory straight into a four-stage LDS ring (32 k per stage, three
-// stages in flight while the fourth is read), one barrier per stage.  Blocks
-// are mapped to tiles XCD by XCD, so the blocks on one XCD (and its L2) cover
-// a contiguous run of tiles, those that share a tile of the larger operand
-// together.  For the LM head, W_lm is pre-tiled once per handle and H per
-// call (a 4 MB re-layout) so that each stage of an operand tile is one
-// contiguous, already swizzled 16 KB piece: every wave load instruction then
-// moves eight whole 128-byte lines (measured 7 % faster than H row-major,
-// whose 64-byte row pieces take twice the requests).
+// bf16, large outputs with row-major operands (the fold E W_ih^T):
+// gemm_bf16_big_kernel, a 256 x 256 block tile, 256 threads (2 x 2 waves of
+// 128 x 128, sixteen 32 x 32 accumulator tiles per wave),
+// v_mfma_f32_32x32x16_bf16.  Operands go from global memory straight into a
+// four-stage LDS ring (32 k per stage, three stages in flight while the
+// fourth is read), one barrier per stage.  Blocks are mapped to tiles XCD by
+// XCD, so the blocks on one XCD (and its L2) cover a contiguous run of tiles,
+// those that share a tile of the larger operand together.
+// The LM head H W_lm: gemm_lm_half_kernel, the same pipeline on 128 x 256
+// tiles (four waves of 64 x 128, a three-stage ring of 24 KB) so that two
+// blocks share a CU, with both operands in a tiled order -- W_lm once per
+// handle, H per call (a 4 MB re-layout) -- in which each 32-k stage of a
+// 256-row operand block is one contiguous, already swizzled 16 KB piece:
+// every wave load instruction moves eight whole 128-byte lines.  Measured
+// against the 256 x 256 kernel on the same tiled operands, 7 % faster (two
+// independent load streams per CU), and that one 7 % faster than with H
+// row-major (whose 64-byte row pieces take twice the requests).
 // bf16, other shapes: a 128 x 128 block tile (2 x 2 waves of 64 x 64), 32 k
-// per stage.  fp32: one thread per output element (small shapes only).
+// per stage, or (few tiles) 32 x 32 tiles with sixteen waves splitting K.
+// fp32: one thread per output element (small shapes only).
 #include <algorithm>
 
 #include "common.h"
@@ -136,10 +142,6 @@ __device__ __forceinline__ void wait_vm() {
   __builtin_amdgcn_s_waitcnt(0x0F70 | (n & 15) | ((n >> 4) << 14));
 }
 
-// BTILED: Bt is in the tiled order of launch_pack_b_tiles ([N / 256][K / 32]
-// blocks of 256 rows x 32 k, swizzled, rows past N zero), so each stage of a
-// B tile is one contiguous 16 KB piece; otherwise Bt is row-major [N, K].
-template <bool ATILED, bool BTILED>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_bf16_big_kernel(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ Bt, const float* __restrict__ bias,
     float* __restrict__ C, int M, int N, int K, int ldc, int tm, int tiles, int per_xcd) {
@@ -162,30 +164,24 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   // row (their outputs are not stored).
   const int lr = lane >> 2, lk = 8 * ((lane & 3) ^ big_swz(lr));
   const int nk = K / BK;
-  const uint16_t* a_base = ATILED ? A + (size_t)(m0 / BT) * nk * BOPND + (4 * w) * 16 * BK + 8 * lane
-                                  : A + (size_t)m0 * K;
-  // tiled B: this tile's nk stage blocks, wave w's 4 KB of each, lane l's 16 bytes
-  const uint16_t* b_base = BTILED ? Bt + (size_t)(n0 / BT) * nk * BOPND + (4 * w) * 16 * BK + 8 * lane
-                                  : Bt + (size_t)n0 * K;
+  const uint16_t* a_base = A + (size_t)m0 * K;
+  const uint16_t* b_base = Bt + (size_t)n0 * K;
   uint32_t a_off[4], b_off[4];
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const int r = 16 * (4 * w + q) + lr;
-    a_off[q] = ATILED ? (uint32_t)(q * 16 * BK) : (uint32_t)((min(m0 + r, M - 1) - m0) * K + lk);
-    b_off[q] = BTILED ? (uint32_t)(q * 16 * BK) : (uint32_t)((min(n0 + r, N - 1) - n0) * K + lk);
+    a_off[q] = (uint32_t)((min(m0 + r, M - 1) - m0) * K + lk);
+    b_off[q] = (uint32_t)((min(n0 + r, N - 1) - n0) * K + lk);
   }
   auto issue = [&](int stage) {
     // the stages past the last one load the last k block again (uniform
     // wait counts; the buffer they fill is not read any more)
-    const int ks = min(stage, nk - 1);
-    const int k0 = ks * BK;
-    const int kb = BTILED ? ks * BOPND : k0;
-    const int ka = ATILED ? ks * BOPND : k0;
+    const int k0 = min(stage, nk - 1) * BK;
     uint16_t* dst = glds + (stage % BNS) * BSTAGE + (4 * w) * 16 * BK;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      __builtin_amdgcn_global_load_lds((glb_ptr)(a_base + a_off[q] + ka), (lds_ptr)(dst + q * 16 * BK), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds((glb_ptr)(b_base + b_off[q] + kb), (lds_ptr)(dst + BOPND + q * 16 * BK), 16,
+      __builtin_amdgcn_global_load_lds((glb_ptr)(a_base + a_off[q] + k0), (lds_ptr)(dst + q * 16 * BK), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((glb_ptr)(b_base + b_off[q] + k0), (lds_ptr)(dst + BOPND + q * 16 * BK), 16,
                                        0, 0);
     }
   };
@@ -346,10 +342,10 @@ hipError_t launch_gemm_bf16(const uint16_t* A, const int32_t* rows, const uint16
   const long big_tiles = (long)((N + BT - 1) / BT) * ((M + BT - 1) / BT);
   if (K % (2 * BK) == 0 && K >= 2 * BK && big_tiles >= 256 && (size_t)BT * K < (1u << 31)) {
     const int tm = (M + BT - 1) / BT, tiles = (int)big_tiles, per_xcd = (tiles + 7) / 8;
-    hipError_t e = hipFuncSetAttribute((const void*)(gemm_bf16_big_kernel<false, false>),
+    hipError_t e = hipFuncSetAttribute((const void*)gemm_bf16_big_kernel,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)BIG_LDS);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((gemm_bf16_big_kernel<false, false>), dim3(8 * per_xcd), dim3(256), BIG_LDS, stream, A, Bt,
+    hipLaunchKernelGGL(gemm_bf16_big_kernel, dim3(8 * per_xcd), dim3(256), BIG_LDS, stream, A, Bt,
                        bias, C, M, N, K, ldc, tm, tiles, per_xcd);
     return hipGetLastError();
   }
@@ -365,6 +361,116 @@ hipError_t launch_gemm_bf16(const uint16_t* A, const int32_t* rows, const uint16
 }
 
 bool gemm_b_tiles_ok(int N, int K) { return K >= 2 * BK && K % (2 * BK) == 0 && (size_t)BT * K < (1u << 31) && N > 0; }
+
+// The LM-head GEMM: 128 x 256 tiles (A rows x B rows), both operands in the
+// tiled order of launch_pack_b_tiles / pack_a_tiles_kernel, four waves of
+// 64 x 128, a three-stage ring of 24 KB stages (72 KB), two blocks per CU.
+constexpr int HM = 128;                      // A rows per tile
+constexpr int HNS = 3;                       // ring stages
+constexpr int HSTAGE = (HM + BT) * BK;       // bf16 per stage (A rows, then B rows)
+constexpr size_t HALF_LDS = (size_t)HNS * HSTAGE * sizeof(uint16_t);  // 73728 B
+
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void gemm_lm_half_kernel(
+    const uint16_t* __restrict__ At, const uint16_t* __restrict__ Bt, float* __restrict__ C, int M, int N, int K,
+    int ldc, int tm, int tiles, int per_xcd) {
+  extern __shared__ __attribute__((aligned(16))) uint16_t glds[];
+  const int t = (int)(blockIdx.x & 7) * per_xcd + (int)(blockIdx.x >> 3);
+  if (t >= tiles) return;
+  const int m0 = (t % tm) * HM, n0 = (t / tm) * BT;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = (w >> 1) * 64, wn = (w & 1) * 128;
+  const int nk = K / BK;
+  // A: the 128-row half of a 256-row tiled block (rows are contiguous and
+  // the swizzle depends on row & 15 only); wave w fills 16-row blocks 2w, 2w+1
+  const uint16_t* a_base = At + (size_t)(m0 / BT) * nk * BOPND + (size_t)(m0 % BT) * BK + (2 * w) * 16 * BK + 8 * lane;
+  const uint16_t* b_base = Bt + (size_t)(n0 / BT) * nk * BOPND + (4 * w) * 16 * BK + 8 * lane;
+  auto issue = [&](int stage) {
+    const int ks = min(stage, nk - 1);
+    uint16_t* dst = glds + (stage % HNS) * HSTAGE;
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+      __builtin_amdgcn_global_load_lds((glb_ptr)(a_base + (size_t)ks * BOPND + q * 16 * BK),
+                                       (lds_ptr)(dst + (2 * w + q) * 16 * BK), 16, 0, 0);
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      __builtin_amdgcn_global_load_lds((glb_ptr)(b_base + (size_t)ks * BOPND + q * 16 * BK),
+                                       (lds_ptr)(dst + HM * BK + (4 * w + q) * 16 * BK), 16, 0, 0);
+  };
+  const int fr = lane & 31;
+  const int p0 = 8 * ((lane >> 5) ^ big_swz(fr & 15)), p1 = p0 ^ 16;
+  auto frags = [&](int stage, bf16x8 (&af)[2][2], bf16x8 (&bf)[2][4]) {
+    const uint16_t* sa = glds + (stage % HNS) * HSTAGE;
+    const uint16_t* sb = sa + HM * BK;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+#pragma unroll
+      for (int x = 0; x < 2; ++x)
+        af[h][x] = *reinterpret_cast<const bf16x8*>(&sa[(wm + 32 * x + fr) * BK + (h ? p1 : p0)]);
+#pragma unroll
+      for (int y = 0; y < 4; ++y)
+        bf[h][y] = *reinterpret_cast<const bf16x8*>(&sb[(wn + 32 * y + fr) * BK + (h ? p1 : p0)]);
+    }
+  };
+  auto stage_ready = [&]() {
+    __builtin_amdgcn_sched_barrier(0);
+    wait_vm<6 * (HNS - 2)>();
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  floatx16 acc[2][4];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+#pragma unroll
+  for (int st = 0; st < HNS - 1; ++st) issue(st);
+  stage_ready();
+  issue(HNS - 1);
+  bf16x8 fa[2][2][2], fb[2][2][4];
+  frags(0, fa[0], fb[0]);
+  auto step = [&](int i, bf16x8 (&ca)[2][2], bf16x8 (&cb)[2][4], bf16x8 (&na)[2][2], bf16x8 (&nb)[2][4]) {
+#pragma unroll
+    for (int y = 0; y < 4; ++y) acc[0][y] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ca[0][0], cb[0][y], acc[0][y], 0, 0, 0);
+    stage_ready();
+    issue(i + HNS);
+    frags(i + 1, na, nb);
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int x = 0; x < 2; ++x)
+#pragma unroll
+        for (int y = 0; y < 4; ++y)
+          if (h || x) acc[x][y] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ca[h][x], cb[h][y], acc[x][y], 0, 0, 0);
+#pragma unroll
+    for (int g = 0; g < 6; ++g) {
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+    }
+  };
+  for (int i = 0; i < nk; i += 2) {
+    step(i, fa[0], fb[0], fa[1], fb[1]);
+    step(i + 1, fa[1], fb[1], fa[0], fb[0]);
+  }
+  wait_vm<0>();
+#pragma unroll
+  for (int y = 0; y < 4; ++y) {
+    const int col = n0 + wn + 32 * y + fr;
+    if (col >= N) continue;
+#pragma unroll
+    for (int x = 0; x < 2; ++x)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int row = m0 + wm + 32 * x + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+        if (row < M) C[(size_t)row * ldc + col] = acc[x][y][e];
+      }
+  }
+}
 
 // A [M, K] row-major into the same tile order as launch_pack_b_tiles' (block
 // (mt, s): rows 256 mt .. 256 mt + 255, k 32 s .. 32 s + 31, swizzled, rows
@@ -392,21 +498,17 @@ size_t gemm_a_tiles_elems(int M, int K) { return (size_t)((M + BT - 1) / BT) * B
 
 hipError_t launch_gemm_bf16_btiled(const uint16_t* A, const uint16_t* Btiled, float* C, int M, int N, int K,
                                    int ldc, uint16_t* a_tiles, hipStream_t stream) {
-  if (!gemm_b_tiles_ok(N, K) || M <= 0) return hipErrorInvalidValue;
-  const int tm = (M + BT - 1) / BT, tiles = tm * ((N + BT - 1) / BT), per_xcd = (tiles + 7) / 8;
-  const void* fn = a_tiles ? (const void*)gemm_bf16_big_kernel<true, true> : (const void*)gemm_bf16_big_kernel<false, true>;
-  hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)BIG_LDS);
+  if (!gemm_b_tiles_ok(N, K) || M <= 0 || !a_tiles) return hipErrorInvalidValue;
+  const int nk = K / BK;
+  const size_t n = (size_t)((M + BT - 1) / BT) * BT * nk;
+  hipLaunchKernelGGL(pack_a_tiles_kernel, dim3((unsigned)std::min<size_t>((n + 255) / 256, 4096)), dim3(256), 0,
+                     stream, A, a_tiles, M, K);
+  const int tm = (M + HM - 1) / HM, tiles = tm * ((N + BT - 1) / BT), per_xcd = (tiles + 7) / 8;
+  hipError_t e = hipFuncSetAttribute((const void*)gemm_lm_half_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                     (int)HALF_LDS);
   if (e != hipSuccess) return e;
-  if (a_tiles) {
-    const size_t n = (size_t)tm * BT * (K / BK);
-    hipLaunchKernelGGL(pack_a_tiles_kernel, dim3((unsigned)std::min<size_t>((n + 255) / 256, 4096)), dim3(256), 0,
-                       stream, A, a_tiles, M, K);
-    hipLaunchKernelGGL((gemm_bf16_big_kernel<true, true>), dim3(8 * per_xcd), dim3(256), BIG_LDS, stream, a_tiles,
-                       Btiled, (const float*)nullptr, C, M, N, K, ldc, tm, tiles, per_xcd);
-  } else {
-    hipLaunchKernelGGL((gemm_bf16_big_kernel<false, true>), dim3(8 * per_xcd), dim3(256), BIG_LDS, stream, A,
-                       Btiled, (const float*)nullptr, C, M, N, K, ldc, tm, tiles, per_xcd);
-  }
+  hipLaunchKernelGGL(gemm_lm_half_kernel, dim3(8 * per_xcd), dim3(256), HALF_LDS, stream, a_tiles, Btiled, C, M, N,
+                     K, ldc, tm, tiles, per_xcd);
   return hipGetLastError();
 }
 

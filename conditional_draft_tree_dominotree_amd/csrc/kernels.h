@@ -35,7 +35,7 @@ hipError_t launch_gemm_bf16(const uint16_t* A, const int32_t* rows, const uint16
 bool gemm_b_tiles_ok(int N, int K);
 size_t gemm_b_tiles_elems(int N, int K);
 hipError_t launch_pack_b_tiles(const uint16_t* W, uint16_t* out, int K, int N, hipStream_t stream);
-// a_tiles (gemm_a_tiles_elems(M, K) bf16, or NULL): A is first re-laid out
+// a_tiles (gemm_a_tiles_elems(M, K) bf16, required): A is first re-laid out
 // there in the same tile order, so both operands load as contiguous pieces.
 size_t gemm_a_tiles_elems(int M, int K);
 hipError_t launch_gemm_bf16_btiled(const uint16_t* A, const uint16_t* Btiled, float* C, int M, int N, int K,
