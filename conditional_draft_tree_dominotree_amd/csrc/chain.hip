@@ -155,6 +155,10 @@ __global__ __launch_bounds__(CT) void chain_correct_mfma_kernel(const uint16_t* 
   __shared__ __attribute__((aligned(16))) uint16_t ahi[32 * AROW];
   __shared__ __attribute__((aligned(16))) uint16_t alo[32 * AROW];
   __shared__ uint64_t wbest[CT / 64][32];
+  // per wave, the base logits of its current 32-row tile for every request,
+  // [b][v] with rows padded to 36 floats (16-byte reads of 32 requests at one
+  // v offset spread over the banks)
+  __shared__ __attribute__((aligned(16))) float bstage[CT / 64][32 * 36];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   for (int t = tid; t < 32 * r; t += CT) {
     const int b = t / r, j = t - b * r;
@@ -201,15 +205,45 @@ __global__ __launch_bounds__(CT) void chain_correct_mfma_kernel(const uint16_t* 
         acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bl, acc, 0, 0, 0);
       }
     }
-    // lane: request fr, rows 8 (e / 4) + 4 (lane >> 5) + (e % 4) of the tile
-    if (fr < B) {
-      const float* brow = base + ((size_t)fr * D + d) * V;
+    // the tile's base logits, read row by row (128 contiguous bytes per
+    // request): load i brings requests 8 i .. 8 i + 7, lane l request
+    // 8 i + l / 8, rows 4 (l % 8) .. + 3
+    const int v0 = vbase + tile * 32;
+    float* bs = bstage[wv];
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int v = vbase + tile * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
-        if (v < V) {
-          const uint64_t c = cand_pack(f32_key(brow[v] + acc[e]), (uint32_t)v);
-          best = c > best ? c : best;
+    for (int i = 0; i < 4; ++i) {
+      const int b = 8 * i + (lane >> 3), vv = v0 + 4 * (lane & 7);
+      if (8 * i < B) {
+        float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (b < B) {
+          const float* brow = base + ((size_t)b * D + d) * V;
+          if ((V & 3) == 0 && vv + 3 < V) {
+            x = *reinterpret_cast<const float4*>(brow + vv);  // 16-byte aligned: V % 4 == 0
+          } else {
+            x.x = vv < V ? brow[vv] : 0.f;
+            x.y = vv + 1 < V ? brow[vv + 1] : 0.f;
+            x.z = vv + 2 < V ? brow[vv + 2] : 0.f;
+            x.w = vv + 3 < V ? brow[vv + 3] : 0.f;
+          }
+        }
+        *reinterpret_cast<float4*>(&bs[b * 36 + 4 * (lane & 7)]) = x;
+      }
+    }
+    // lane: request fr, rows 8 (e / 4) + 4 (lane >> 5) + (e % 4) of the tile
+    // (the stage is this wave's own: its writes are visible to its reads)
+    if (fr < B) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const float4 bv = *reinterpret_cast<const float4*>(&bs[fr * 36 + 8 * g + 4 * (lane >> 5)]);
+        const float bb[4] = {bv.x, bv.y, bv.z, bv.w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int e = 4 * g + q;
+          const int v = v0 + 8 * g + 4 * (lane >> 5) + q;
+          if (v < V) {
+            const uint64_t c = cand_pack(f32_key(bb[q] + acc[e]), (uint32_t)v);
+            best = c > best ? c : best;
+          }
         }
       }
     }

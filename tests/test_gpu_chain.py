@@ -168,3 +168,18 @@ def test_small_fp32_batches(dev, B):
     tb.close()
     exact, ties = compare(spec, w, req, got, range(B))
     assert exact == B, (exact, ties)
+
+
+@pytest.mark.parametrize("B,V", [(5, 5003), (32, 4099)])
+def test_small_bf16_odd_vocab(dev, B, V):
+    # the matrix-core correction with a vocabulary that is neither a multiple
+    # of 4 (unaligned base rows) nor of the 256-row block, up to 32 requests
+    spec = synth.small(f"chain_bf16_{B}_{V}", group=800 + B, V=V, D=5, h=64, e=96, ds=128, r=64, M=8, k=2,
+                       N=10, B=B, wdtype="bf16", emb_std=0.5, root_std=0.5)
+    spec, w, req = synth.workload(spec)
+    tb = gu.make_builder(spec, w)
+    got = run_chain(tb, spec, req)
+    tb.close()
+    exact, ties = compare(spec, w, req, got, range(B))
+    assert exact + ties == B, (exact, ties)
+    assert exact >= B - 1, (exact, ties)
