@@ -315,6 +315,11 @@ def main():
             "frac_vs_measured_write_bw": achieved / fill_gbs,
         },
     }
+    traffic = res["roofline"]["traffic"]
+    if traffic is not None:
+        # what the kernel actually moves (the counter figure) per second: the
+        # builder is bound by its per-step latency chain, not by HBM
+        res["roofline"]["traffic_gbs"] = traffic / (tree_ms * 1e-3) / 1e9
     if base is None:
         # the LM head: a dense bf16 contraction, priced against the MFMA peak
         flops = 2.0 * spec.B * spec.D * spec.V * spec.h
