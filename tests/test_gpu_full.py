@@ -78,8 +78,9 @@ def test_q8b_b1(dev, q8b_builder):
 
 
 def test_q8b_b32(dev, q8b_builder):
+    # every request of the batch against the oracle (about 6 s of CPU)
     spec, w, req = synth.workload("q8b_b32")
-    _full_case(spec, w, req, q8b_builder, [0, 7, 19, 31])
+    _full_case(spec, w, req, q8b_builder, list(range(spec.B)))
 
 
 def test_q8b_b32_lds_workers(dev, q8b_builder, monkeypatch):
@@ -103,7 +104,7 @@ def test_q8b_lm_pipeline(dev, q8b_builder):
     spec, w, req = synth.workload("q8b_lm")
     got = gu.run(q8b_builder, spec, req)          # base logits from H W_lm on the GPU
     _check_structure(spec, got)
-    sample = [0, 31]
+    sample = [0, 9, 22, 31]
     base = np.zeros((spec.B, spec.D, spec.V), np.float32)
     for b in sample:
         base[b] = ref.lm_head_logits(req["hidden"][b], w["w_lm"], True)
