@@ -16,7 +16,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 DT_OK, DT_EINVAL, DT_EUNSUPPORTED, DT_ENOMEM, DT_EHIP, DT_EDEVICE = 0, -1, -2, -3, -4, -5
 DT_F32, DT_BF16 = 0, 1
 DT_NORM_TOPM, DT_NORM_FULLV = 0, 1
-DT_ACT_BF16, DT_VALIDATE, DT_TIMING = 1, 2, 4
+DT_ACT_BF16, DT_VALIDATE, DT_TIMING, DT_MARGINAL = 1, 2, 4, 8
 _STATUS = {0: "DT_OK", -1: "DT_EINVAL", -2: "DT_EUNSUPPORTED", -3: "DT_ENOMEM", -4: "DT_EHIP",
            -5: "DT_EDEVICE"}
 

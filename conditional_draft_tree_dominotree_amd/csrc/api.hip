@@ -143,7 +143,8 @@ dt_status check_params(const dt_params* p, int V, const dt_params* maxp) {
   if (!(p->temperature > 0.f) || !std::isfinite(p->temperature))
     return fail(DT_EINVAL, "temperature must be finite and > 0");
   if (p->norm != DT_NORM_TOPM && p->norm != DT_NORM_FULLV) return fail(DT_EINVAL, "unknown norm");
-  if (p->flags & ~(DT_ACT_BF16 | DT_VALIDATE | DT_TIMING)) return fail(DT_EINVAL, "unknown flags 0x%x", p->flags);
+  if (p->flags & ~(DT_ACT_BF16 | DT_VALIDATE | DT_TIMING | DT_MARGINAL))
+    return fail(DT_EINVAL, "unknown flags 0x%x", p->flags);
   if (maxp && (p->top_m > maxp->top_m || p->top_k > maxp->top_k || p->budget > maxp->budget))
     return fail(DT_EINVAL, "params exceed the handle's max_params");
   return DT_OK;
@@ -388,6 +389,7 @@ dt_status dt_build_trees(dt_handle* h, const dt_inputs* in, const dt_params* p, 
   a.T = p->temperature;
   a.fullv = p->norm == DT_NORM_FULLV;
   a.act_bf16 = (p->flags & DT_ACT_BF16) != 0;
+  a.marginal = (p->flags & DT_MARGINAL) != 0;
   a.n_tiles = h->n_tiles;
   a.tiles_per_worker = choose_tpw(h, B);
   a.n_workers = (h->n_tiles + a.tiles_per_worker - 1) / a.tiles_per_worker;

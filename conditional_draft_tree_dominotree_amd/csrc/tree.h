@@ -13,6 +13,7 @@ struct TreeArgs {
   float T;
   int fullv;
   int act_bf16;
+  int marginal;         // 1: no correction (dL = 0), the factorised scores of the base logits
   int n_workers;        // worker blocks; block ids [0, n_workers) are workers
   int tiles_per_worker;
   int n_tiles;          // (3 ds + r) / 16

@@ -1103,7 +1103,7 @@ __device__ __forceinline__ void ctl_expand(const TreeArgs& a, const CtlLds& c, i
       }
       const float dl = h == 0 ? acc[0] : h == 1 ? acc[1] : h == 2 ? acc[2] : acc[3];
       const int m = 4 * g + h;
-      if (valid) c.f->z[j * 64 + m] = (c.cand[c.f->ex_dep[j] * M + m].val + dl) / a.T + 0.0f;
+      if (valid) c.f->z[j * 64 + m] = (c.cand[c.f->ex_dep[j] * M + m].val + (a.marginal ? 0.f : dl)) / a.T + 0.0f;
     }
   } else {
     // candidates padded to a power of two so that the index splits are shifts
@@ -1145,7 +1145,7 @@ __device__ __forceinline__ void ctl_expand(const TreeArgs& a, const CtlLds& c, i
         }
       }
       for (int s = 1; s < tpc; s <<= 1) dl += __shfl_xor(dl, s);
-      if (valid && part == 0) c.f->z[j * 64 + m] = (c.cand[c.f->ex_dep[j] * M + m].val + dl) / a.T + 0.0f;
+      if (valid && part == 0) c.f->z[j * 64 + m] = (c.cand[c.f->ex_dep[j] * M + m].val + (a.marginal ? 0.f : dl)) / a.T + 0.0f;
     }
   }
   __syncthreads();

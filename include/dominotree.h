@@ -81,6 +81,10 @@ typedef enum { DT_NORM_TOPM = 0, DT_NORM_FULLV = 1 } dt_norm;
 #define DT_ACT_BF16 1u  /* round the GRU state to bf16 where it is a GEMM operand */
 #define DT_VALIDATE 2u  /* scan the base logits for NaN first (DT_EINVAL if any) */
 #define DT_TIMING 4u    /* record HIP events between the phases of the build (dt_phase_times) */
+#define DT_MARGINAL 8u  /* score with the base logits alone (dL = 0): the factorised, DDTree-style
+                           tree that the conditional correction is compared against
+                           ("Riassunto Tecnico: DominoTree", Definizione del Problema: scores
+                           that depend on the position only); the GRU still runs */
 
 /* Limits of this build (DT_EUNSUPPORTED beyond them). */
 #define DT_MAX_BATCH 32

@@ -121,3 +121,16 @@ def test_q8b_lm_pipeline(dev, q8b_builder):
     print(spec.name, gu.summarize(reps))
     for b, r in zip(sample, reps):
         assert r.ok, (b, r)
+
+
+def test_q8b_b32_marginal(dev, q8b_builder):
+    import conditional_draft_tree_dominotree_amd as pkg
+    spec, w, req = synth.workload("q8b_b32")
+    got = gu.run(q8b_builder, spec, req, flags=pkg.DT_ACT_BF16 | pkg.DT_MARGINAL)
+    _check_structure(spec, got)
+    w0 = dict(w)
+    w0["w2"] = np.zeros_like(w["w2"])
+    reps, _ = gu.compare(spec, w0, req, got, requests=[0, 13, 31])
+    print(spec.name, "marginal", gu.summarize(reps))
+    for b, r in zip([0, 13, 31], reps):
+        assert r.ok, (b, r)

@@ -142,3 +142,22 @@ def test_runs_are_bitwise_reproducible(dev):
     for key in a:
         np.testing.assert_array_equal(a[key], b[key], err_msg=key)
     tb.close()
+
+
+@pytest.mark.parametrize("name", ["base", "batch3_fullv_T05"])
+def test_marginal_flag_is_the_zero_correction_tree(dev, name):
+    # DT_MARGINAL scores with the base logits alone: the oracle's tree with
+    # W2 = 0 (itself pinned to an independent product-tree enumeration)
+    import conditional_draft_tree_dominotree_amd as pkg
+    kw = dict(SMALL)[name]
+    spec = synth.small(name, group=300 + len(name), **kw)
+    spec, w, req = synth.workload(spec)
+    tb = gu.make_builder(spec, w)
+    got = gu.run(tb, spec, req, flags=pkg.DT_MARGINAL)
+    tb.close()
+    w0 = dict(w)
+    w0["w2"] = np.zeros_like(w["w2"])
+    reps, trees = gu.compare(spec, w0, req, got)
+    print(name, "marginal", gu.summarize(reps))
+    _assert_ok(reps)
+    assert all(r.exact for r in reps)
