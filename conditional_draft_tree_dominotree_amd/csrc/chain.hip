@@ -160,18 +160,6 @@ __global__ __launch_bounds__(CT) void chain_correct_mfma_kernel(const uint16_t* 
   // v offset spread over the banks)
   __shared__ __attribute__((aligned(16))) float bstage[CT / 64][32 * 36];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  for (int t = tid; t < 32 * r; t += CT) {
-    const int b = t / r, j = t - b * r;
-    float v = 0.f;
-    if (b < B) {
-      const float u = P[((size_t)b * D + d) * r + j] + gu[(size_t)b * gstride + goff + j];
-      v = u / (1.f + expf(-u));  // SiLU
-    }
-    const uint16_t hi = f32_to_bf16(v);
-    ahi[b * AROW + j] = hi;
-    alo[b * AROW + j] = f32_to_bf16(v - bf16_to_f32(hi));
-  }
-  __syncthreads();
   const int fr = lane & 31, fk = 8 * (lane >> 5);
   const int ks = r / 16;  // 16-k steps
   const int vbase = blockIdx.x * MROWS + wv * MT * 32;
@@ -188,7 +176,20 @@ __global__ __launch_bounds__(CT) void chain_correct_mfma_kernel(const uint16_t* 
     for (int s = 0; s < CHAIN_MAX_RANK / 16; ++s)
       if (s < ks) dst[s] = src[s * 64];
   };
+  // the first tile's W2^T loads go out before `a` is built (they do not need it)
   load_tile(0, q[0]);
+  for (int t = tid; t < 32 * r; t += CT) {
+    const int b = t / r, j = t - b * r;
+    float v = 0.f;
+    if (b < B) {
+      const float u = P[((size_t)b * D + d) * r + j] + gu[(size_t)b * gstride + goff + j];
+      v = u / (1.f + expf(-u));  // SiLU
+    }
+    const uint16_t hi = f32_to_bf16(v);
+    ahi[b * AROW + j] = hi;
+    alo[b * AROW + j] = f32_to_bf16(v - bf16_to_f32(hi));
+  }
+  __syncthreads();
 #pragma unroll
   for (int tile = 0; tile < MT; ++tile) {
     if (tile + 1 < MT) load_tile(tile + 1, q[(tile + 1) & 1]);
