@@ -423,8 +423,9 @@ dt_status dt_build_trees(dt_handle* h, const dt_inputs* in, const dt_params* p, 
   a.spin_limit = 1u << 21;
   const char* pops_env = getenv("DT_POPS");
   const char* workers_env = getenv("DT_WORKERS");  // "lds": workers stage operands in LDS
+  const char* halves_env = getenv("DT_HALVES");    // 1 or 2: split of the batch between the workers' turns
   const size_t lds = dt::plan_tree(a, h->bf16, pops_env ? atoi(pops_env) : 0, std::min(h->n_cu - B, h->max_workers),
-                                   workers_env && !strcmp(workers_env, "lds"));
+                                   workers_env && !strcmp(workers_env, "lds"), halves_env ? atoi(halves_env) : 0);
   if (lds == 0 || lds > 160 * 1024) return fail(DT_EUNSUPPORTED, "no builder schedule fits this shape in LDS");
   if (a.n_workers + B > h->n_cu || a.n_workers > h->max_workers)
     return fail(DT_EUNSUPPORTED, "%d workers + %d requests exceed %d compute units", a.n_workers, B, h->n_cu);

@@ -23,7 +23,10 @@ struct TreeArgs {
   int regw;             // 0: workers stage operands in LDS; register workers: 1 (1 tile per wave, 1
                         // column block per block), 2 (2 tiles, 1 block), 3 (2 tiles, 2 blocks),
                         // 4 (2 tiles, 4 blocks)
-  int ncbmax;           // register workers: 16-column blocks per step
+  int ncbmax;           // register workers: 16-column blocks per step (per half of the batch)
+  int halves;           // register workers: 2 serve the requests [0, bh) and [bh, B) of a step in
+                        // turn, so that one half's products overlap the other half's scoring; else 1
+  int bh;               // requests in the first half (B when halves = 1)
   int wadv;             // 1: the workers advance the GRU states of a step's nodes (register workers)
   int xcap;             // node records per request (budget + root + speculation room)
   int fcap;             // frontier entries per request
@@ -46,7 +49,8 @@ struct TreeArgs {
   float* gh;               // [slots, 3 ds]
   float* u;                // [slots, r]
   int32_t* ninfo;          // [steps][TREE_MAX_COLS][2]: token and parent slot of each node to advance
-  uint32_t* gflag;         // [16][64] worker group flags (states of a step advanced)
+  uint32_t* gflag;         // [16][64] worker group flags: 2 epoch + half once a group's states of
+                           // that step and half of the batch are advanced
   uint32_t* ready;         // [64] controller b: its start-up loads are done (the workers then load weights)
   uint32_t* mbox_w;        // [n_workers][32] controller -> worker mailboxes (one line each)
   uint32_t* mbox_c;        // [B][256] worker -> controller mailboxes
@@ -69,7 +73,9 @@ constexpr uint32_t TREE_EPOCH_LIMIT = 1u << 27;  // mailbox words hold the epoch
 // With register workers (allowed unless `lds_workers`) it also sets
 // n_workers, at most `max_workers`; otherwise n_workers and tiles_per_worker
 // are the caller's.
-size_t plan_tree(TreeArgs& a, int wdtype_bf16, int pops, int max_workers, int lds_workers);
+// `halves`: 1 or 2 forces the split of the batch, 0 = automatic (2 for register
+// workers with at least 16 requests whose first half fills whole 16-column blocks).
+size_t plan_tree(TreeArgs& a, int wdtype_bf16, int pops, int max_workers, int lds_workers, int halves);
 hipError_t launch_tree(const TreeArgs& a, int wdtype_bf16, size_t lds_bytes, hipStream_t stream);
 
 }  // namespace dt

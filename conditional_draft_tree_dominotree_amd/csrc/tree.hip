@@ -389,16 +389,21 @@ __device__ __forceinline__ void worker_compute_f32(const TreeArgs& a, const floa
 // lists the step's columns (exchange slots, request-major) in coln and the
 // requests with work in reqs; misc[0] = columns (-1: a wait ran out),
 // misc[1] = requests.  Ends with a block barrier.
-__device__ __forceinline__ void worker_columns(const TreeArgs& a, int w, int t, int* coln, int* reqs, int* misc) {
+// The columns of the nodes that the requests [b0, b0 + nb) expand at step t:
+// waits for those requests' mailbox words, then lists their exchange slots in
+// coln and the requests with nodes in reqs; misc[0] = column count (-1: a wait
+// ran out; 0: every one of these requests is finished), misc[1] = request count.
+__device__ __forceinline__ void worker_columns(const TreeArgs& a, int w, int t, int b0, int nb, int* coln, int* reqs,
+                                               int* misc) {
   const int tid = threadIdx.x, lane = tid & 63;
   const uint32_t epoch = a.ebase + (uint32_t)t + 1u;
   if (tid < 64) {
-    const uint32_t* mybox = a.mbox_w + (size_t)w * 32;
-    const bool ok = wait_mbox(mybox, a.B, epoch << 5, a.err, a.spin_limit);
-    const int b = lane;
+    const uint32_t* mybox = a.mbox_w + (size_t)w * 32 + b0;
+    const bool ok = wait_mbox(mybox, nb, epoch << 5, a.err, a.spin_limit);
+    const int b = b0 + lane;
     uint32_t word = 0;
-    if (ok && b < a.B) word = ld_dev_u32(mybox + b);
-    const int e = (ok && b < a.B && (word & 31u) != MBOX_DONE_E) ? (int)(word & 31u) : 0;
+    if (ok && lane < nb) word = ld_dev_u32(mybox + lane);
+    const int e = (ok && lane < nb && (word & 31u) != MBOX_DONE_E) ? (int)(word & 31u) : 0;
     // exclusive prefix of e over the lanes
     int incl = e;
     for (int d = 1; d < 64; d <<= 1) {
@@ -464,7 +469,7 @@ __device__ __forceinline__ void worker_main(const TreeArgs& a, unsigned char* ld
 
   for (int t = a.root ? 0 : 1;; ++t) {  // zero roots: step 0 needs no product (set up by the controllers)
     const uint32_t epoch = a.ebase + (uint32_t)t + 1u;
-    worker_columns(a, w, t, coln, reqs, misc);
+    worker_columns(a, w, t, 0, a.B, coln, reqs, misc);
     const int ncols = misc[0], nreq = misc[1];
     if (ncols <= 0) return;  // a wait ran out, or every request is finished
     const int ncb = (ncols + 15) / 16;
@@ -666,20 +671,34 @@ __device__ __forceinline__ void worker_regs(const TreeArgs& a, unsigned char* ld
     for (int kb = 0; kb < RKB; ++kb) wa[i][kb] = src[kb * 64];
   }
 
-  for (int t = a.root ? 0 : 1;; ++t) {  // zero roots: step 0 needs no product (set up by the controllers)
+  // With two halves the block serves the requests [0, bh) and then [bh, B) of
+  // each step; a half whose requests are all finished is passed over.
+  bool done[2] = {false, a.halves < 2};
+  int t = a.root ? 0 : 1;  // zero roots: step 0 needs no product (set up by the controllers)
+  for (int h = 0;; h = (h + 1) % a.halves, t += h == 0) {
+    if (done[0] && done[1]) return;
+    if (done[h]) continue;
     const uint32_t epoch = a.ebase + (uint32_t)t + 1u;
-    worker_columns(a, w, t, coln, reqs, misc);
+    // group flags: 2 epoch + h, increasing over (step, half) and across launches
+    // whatever their number of halves
+    const uint32_t gepoch = 2u * epoch + (uint32_t)h;
+    worker_columns(a, w, t, h ? a.bh : 0, h ? a.B - a.bh : a.bh, coln, reqs, misc);
     const int ncols = misc[0], nreq = misc[1];
-    if (ncols <= 0) return;  // a wait ran out, or every request is finished
+    if (ncols < 0) return;  // a wait ran out
+    if (ncols == 0) {       // every request of this half is finished
+      done[h] = true;
+      __syncthreads();      // misc is read by every thread before wave 0 writes it again
+      continue;
+    }
     if (col0 < ncols) {
       if (a.wadv && t > 0) {
         // the group advances the states of its columns, then waits for all of it
         worker_advance(a, coln, t, col0, min(16 * CPB, ncols - col0), gq, ngq);
         stores_done();
         __syncthreads();
-        if (tid == 0) st_dev_u32(a.gflag + grp * 64 + gq, epoch);
+        if (tid == 0) st_dev_u32(a.gflag + grp * 64 + gq, gepoch);
         if (tid < 64) {
-          const bool ok = wait_mbox(a.gflag + grp * 64, ngq, epoch, a.err, a.spin_limit);
+          const bool ok = wait_mbox(a.gflag + grp * 64, ngq, gepoch, a.err, a.spin_limit);
           if (lane == 0) misc[2] = ok;
         }
         __syncthreads();
@@ -1929,7 +1948,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 // ---------------------------------------------------------------------------
 // host side: schedule and launch
 
-size_t plan_tree(TreeArgs& a, int wdtype_bf16, int pops, int max_workers, int lds_workers) {
+size_t plan_tree(TreeArgs& a, int wdtype_bf16, int pops, int max_workers, int lds_workers, int halves) {
   const int esz = wdtype_bf16 ? 2 : 4;
   const size_t lds_max = 160 * 1024;
   const int kp = k_padded(a.ds);
@@ -1940,16 +1959,23 @@ size_t plan_tree(TreeArgs& a, int wdtype_bf16, int pops, int max_workers, int ld
   const int lds_n_workers = a.n_workers;
   for (; p >= 1; --p) {
     const int cols = a.B * p;
-    const int ncb = (cols + 15) / 16;
-    // register workers: one tile per wave if that many blocks fit, else two
-    int regw = 0, n_workers = lds_n_workers;
-    if (wdtype_bf16 && a.ds == RKB * 32 && !lds_workers) {
+    // register workers: one tile per wave if that many blocks fit, else two.
+    // Two halves of the batch need the first half's columns to fill whole
+    // 16-column blocks: the halves' node tables then share no cache line, so
+    // a worker's reads of the first half's entries cannot cache the second's
+    // before its controllers have written them.
+    const bool regok = wdtype_bf16 && a.ds == RKB * 32 && !lds_workers;
+    const int bh2 = (a.B + 1) / 2;
+    const bool split = regok && a.B >= 2 && (bh2 * p) % 16 == 0 && (halves == 2 || (halves == 0 && a.B >= 16));
+    int regw = 0, n_workers = lds_n_workers, hv = 1, ncb = (cols + 15) / 16;
+    for (int hc = split ? 2 : 1; regok && hc >= 1 && !regw; --hc) {
+      const int ncb_h = ((hc == 2 ? bh2 : a.B) * p + 15) / 16;
       // (tiles per wave, column blocks per block): 1 = (1, 1), 2 = (2, 1), 3 = (2, 2), 4 = (2, 4)
       for (int m = 1; m <= 4 && !regw; ++m) {
         const int tw = m == 1 ? 1 : 2, cpb = m == 4 ? 4 : m == 3 ? 2 : 1;
         const int ngq = ((a.n_tiles + tw - 1) / tw + 3) / 4;  // blocks per column group (64 flags each)
-        const int nw = ngq * ((ncb + cpb - 1) / cpb);
-        if (nw <= max_workers && ngq <= 64) regw = m, n_workers = nw;
+        const int nw = ngq * ((ncb_h + cpb - 1) / cpb);
+        if (nw <= max_workers && ngq <= 64) regw = m, n_workers = nw, hv = hc, ncb = ncb_h;
       }
     }
     int kc = kp;
@@ -1977,6 +2003,8 @@ size_t plan_tree(TreeArgs& a, int wdtype_bf16, int pops, int max_workers, int ld
     a.kc = kc;
     a.regw = regw;
     a.ncbmax = ncb;
+    a.halves = hv;
+    a.bh = hv == 2 ? bh2 : a.B;
     a.wadv = regw ? 1 : 0;
     a.n_workers = n_workers;
     a.qmax = qmax;

@@ -83,6 +83,14 @@ def test_q8b_b32(dev, q8b_builder):
     _full_case(spec, w, req, q8b_builder, list(range(spec.B)))
 
 
+def test_q8b_b32_one_half(dev, q8b_builder, monkeypatch):
+    # the register workers serving the whole batch at each step (the default
+    # at 32 requests serves it in two halves)
+    monkeypatch.setenv("DT_HALVES", "1")
+    spec, w, req = synth.workload("q8b_b32")
+    _full_case(spec, w, req, q8b_builder, [0, 17, 31])
+
+
 def test_q8b_b32_lds_workers(dev, q8b_builder, monkeypatch):
     # the workers that stage operands in LDS (the schedule for d_s other than
     # 1024) at the full shape, on the same handle

@@ -161,3 +161,46 @@ def test_marginal_flag_is_the_zero_correction_tree(dev, name):
     print(name, "marginal", gu.summarize(reps))
     _assert_ok(reps)
     assert all(r.exact for r in reps)
+
+
+@pytest.mark.parametrize("B,root", [(2, True), (3, False), (5, True)])
+def test_bf16_register_workers_two_halves(dev, monkeypatch, B, root):
+    # the register workers serve the first ceil(B/2) requests of a step, then
+    # the rest (16 nodes per request per step, so the first half fills whole
+    # 16-column blocks); uneven halves, given and zero root states
+    monkeypatch.setenv("DT_HALVES", "2")
+    monkeypatch.setenv("DT_POPS", "16")
+    spec = synth.small(f"halves_b{B}", V=3000, D=7, h=64, e=96, ds=1024, r=64, M=16, k=4, N=80, B=B,
+                       wdtype="bf16", group=1200 + B, emb_std=0.5, biases=True,
+                       root_std=0.7 if root else 0.0)
+    spec, w, req = synth.workload(spec)
+    tb = gu.make_builder(spec, w)
+    got = gu.run(tb, spec, req)
+    reps, trees = gu.compare(spec, w, req, got)
+    print(gu.summarize(reps))
+    _assert_ok(reps)
+    gu.check_candidates(spec, trees, got, range(spec.B))
+    tb.close()
+
+
+def test_halves_alternate_on_one_handle(dev, monkeypatch):
+    # group flags carry 2 epoch + half in every launch, so a one-half build
+    # after a two-half build (and back) waits for its own flags; each column's
+    # product and state update do not depend on the split, so the trees are
+    # bitwise the same
+    monkeypatch.setenv("DT_POPS", "16")
+    spec = synth.small("halves_alt", V=3000, D=7, h=64, e=96, ds=1024, r=64, M=16, k=4, N=80, B=4,
+                       wdtype="bf16", group=1290, emb_std=0.5, biases=True, root_std=0.7)
+    spec, w, req = synth.workload(spec)
+    tb = gu.make_builder(spec, w)
+    outs = []
+    for hv in ("2", "1", "2", "1"):
+        monkeypatch.setenv("DT_HALVES", hv)
+        outs.append(gu.run(tb, spec, req))
+    reps, _ = gu.compare(spec, w, req, outs[0])
+    print(gu.summarize(reps))
+    _assert_ok(reps)
+    for o in outs[1:]:
+        for key in ("tokens", "parents", "depths", "scores", "n_nodes"):
+            np.testing.assert_array_equal(o[key], outs[0][key], err_msg=key)
+    tb.close()
