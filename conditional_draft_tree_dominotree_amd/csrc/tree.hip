@@ -1966,7 +1966,7 @@ size_t plan_tree(TreeArgs& a, int wdtype_bf16, int pops, int max_workers, int ld
     // before its controllers have written them.
     const bool regok = wdtype_bf16 && a.ds == RKB * 32 && !lds_workers;
     const int bh2 = (a.B + 1) / 2;
-    const bool split = regok && a.B >= 2 && (bh2 * p) % 16 == 0 && (halves == 2 || (halves == 0 && a.B >= 16));
+    const bool split = regok && a.B >= 2 && (bh2 * p) % 16 == 0 && (halves == 2 || halves == 0);
     int regw = 0, n_workers = lds_n_workers, hv = 1, ncb = (cols + 15) / 16;
     for (int hc = split ? 2 : 1; regok && hc >= 1 && !regw; --hc) {
       const int ncb_h = ((hc == 2 ? bh2 : a.B) * p + 15) / 16;
