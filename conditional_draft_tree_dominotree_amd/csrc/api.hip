@@ -339,9 +339,8 @@ dt_status dt_build_trees(dt_handle* h, const dt_inputs* in, const dt_params* p, 
   // a2: P = H W1_H (the path-independent half of W1 [H_d; S]) needs only the
   // hidden states.  Beside the LM-head GEMM (on the handle's side stream) it
   // costs nothing; with base logits given it runs first on the caller's
-  // stream (measured: beside the candidate selection the two contend for
-  // memory and P ends ~10 us after it; alone first it takes ~12 us and the
-  // selection ~10 us less)
+  // stream (measured: first is faster per round than on the side stream
+  // beside the whole candidate selection or beside its merge alone)
   MARK(0);
   const bool p_inline = in->base_logits != nullptr;
   hipStream_t ps = p_inline ? stream : h->side;
