@@ -7,11 +7,10 @@
 // comparison on the fp32 inputs, so it is exact; only the two LSE values are
 // rounded.
 //
-// Kernels.  topm_chunk: a grid of 256-thread blocks sized to fill the chip
-// walks the (row, chunk of 8192 tokens) items; each block reads an item once
-// from HBM into registers (32 values per thread) while it selects from the
-// previous one, so the loads of one item overlap the selection of the other.
-// Each wave finds the ceil(M/4)-th largest of its 64 per-thread maxima (a bit
+// Kernels.  topm_chunk: one 256-thread block per (row, chunk of 8192 tokens)
+// item; the block reads its item once from HBM into registers (32 values per
+// thread, 16-byte loads), and the several blocks resident on a CU overlap one
+// block's loads with another's selection.  Each wave finds the ceil(M/4)-th largest of its 64 per-thread maxima (a bit
 // search over ballots); the smallest of the four wave values bounds the
 // chunk's M-th largest value from below (at least M threads reach it), so the
 // keys at or above it -- typically a few more than M -- hold the chunk's
