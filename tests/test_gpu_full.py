@@ -142,3 +142,24 @@ def test_q8b_b32_marginal(dev, q8b_builder):
     print(spec.name, "marginal", gu.summarize(reps))
     for b, r in zip([0, 13, 31], reps):
         assert r.ok, (b, r)
+
+
+def test_q8b_b32_repeated_builds_bitwise(dev, q8b_builder):
+    # 200 back-to-back builds of the full batch (two halves per step): every
+    # decision is taken in a fixed order, so each build must return the first
+    # build's trees bit for bit; a race in the exchange between the halves
+    # would show up as a differing tree
+    import torch
+    spec, w, req = synth.workload("q8b_b32")
+    first = gu.run(q8b_builder, spec, req)
+    hidden, base = gu.to_dev(req["hidden"]), gu.to_dev(req["base"])
+    import conditional_draft_tree_dominotree_amd as pkg
+    out = q8b_builder.outputs(spec.B, spec.M, spec.N)
+    for i in range(200):
+        q8b_builder.build(hidden, base, None, top_m=spec.M, top_k=spec.k, budget=spec.N,
+                          temperature=spec.T, norm=pkg.DT_NORM_TOPM, flags=pkg.DT_ACT_BF16, out=out)
+        if i % 50 == 49:
+            torch.cuda.synchronize()
+            q8b_builder.sync_status()
+            for key in ("tokens", "parents", "depths", "scores", "n_nodes"):
+                np.testing.assert_array_equal(out[key].cpu().numpy(), first[key], err_msg=f"{key} build {i}")
