@@ -178,7 +178,14 @@ dt_status dt_create(dt_handle** h, const dt_dims* dims, const dt_weights* w,
  * Errors: DT_EINVAL (NULL pointers, batch out of range, params out of range
  * or above the handle's max_params, NaN logits under DT_VALIDATE, w_lm
  * missing with NULL base logits), DT_EUNSUPPORTED, DT_EHIP, DT_EDEVICE (a
- * previous build's device wait ran out). */
+ * previous build's device wait ran out).
+ * Schedule overrides, read from the environment at each call: DT_POPS (nodes a
+ * request expands per step, at most 16), DT_HALVES (1 or 2: the workers serve
+ * the batch whole or in two halves per step), DT_WORKERS=lds and
+ * DT_TILES_PER_WORKER (workers that stage operands in LDS).  They change how
+ * the work is scheduled, not what is computed: the trees are the same up to
+ * the rounding of the per-node products, whose summation order can depend on
+ * the worker layout. */
 dt_status dt_build_trees(dt_handle* h, const dt_inputs* in, const dt_params* p,
                          dt_outputs* out, void* stream);
 
