@@ -78,7 +78,7 @@ struct dt_handle {
   float* chain_gu = nullptr;     // chain head: [max_batch, 3 ds + r]
   float* chain_s = nullptr;      // [max_batch, ds]
   void* chain_sop = nullptr;     // [max_batch, ds] (wdtype)
-  uint64_t* chain_part = nullptr;  // [max_batch, chain_blocks(V)]
+  uint64_t* chain_part = nullptr;  // [max_batch, max(chain_blocks(V), chain_mfma_blocks(V))]
   size_t act_bytes = 0;
   uint32_t ebase = 0;  // epoch base of the next launch (mailboxes hold older epochs)
   hipStream_t side = nullptr;  // runs P = H W1_H beside the candidate selection
@@ -262,7 +262,7 @@ dt_status dt_create(dt_handle** out, const dt_dims* dims, const dt_weights* w, c
   ALLOC(h->chain_gu, (size_t)Bm * (3 * ds + r) * sizeof(float));
   ALLOC(h->chain_s, (size_t)Bm * ds * sizeof(float));
   ALLOC(h->chain_sop, (size_t)Bm * ds * esz);
-  ALLOC(h->chain_part, (size_t)Bm * dt::chain_blocks(V) * sizeof(uint64_t));
+  ALLOC(h->chain_part, (size_t)Bm * std::max(dt::chain_blocks(V), dt::chain_mfma_blocks(V)) * sizeof(uint64_t));
 
   // workspace for max_batch and max_params
   const int S = dt::topm_chunks(V);

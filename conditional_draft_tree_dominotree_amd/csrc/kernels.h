@@ -74,7 +74,8 @@ struct ChainArgs {
   int32_t* tokens;      // [B, D]
   float* logits;        // [B, D] or null
 };
-int chain_blocks(int V);
+int chain_blocks(int V);       // blocks of the fp32 correction (one vocabulary row per thread)
+int chain_mfma_blocks(int V);  // blocks of the bf16 MFMA correction
 size_t chain_w2_frags_elems(int V, int r);
 hipError_t launch_pack_w2_frags(const uint16_t* w2t, uint16_t* out, int V, int r, hipStream_t stream);
 hipError_t launch_chain(const ChainArgs& c, hipStream_t stream);
