@@ -171,24 +171,26 @@ __global__ __launch_bounds__(TOPM_THREADS) void topm_chunk_kernel(
   // NaN, no padding); else the exact path
   const bool fast = tau > 0x007FFFFFu;
   const float tau_f = fast ? key_f32(tau) : INFINITY;
-  // 2. compaction of the candidates: count, one LDS atomic per wave, write
-  int n = 0;
+  // 2. compaction of the candidates: the wave's count from ballots, one LDS
+  //    atomic per wave, then each element q's candidates written at the
+  //    wave's running position plus their rank among the lanes (the order in
+  //    sel does not matter: the keys are ranked by value below)
+  int wtot = 0;
 #pragma unroll
-  for (int q = 0; q < PER_THREAD; ++q) n += x[q] >= tau_f ? 1 : 0;
-  const int incl = wave_add_scan_incl(n);
-  const int wtot = __builtin_amdgcn_readlane(incl, 63);
+  for (int q = 0; q < PER_THREAD; ++q) wtot += (int)__popcll(__ballot(x[q] >= tau_f));
   int base = 0;
   if (lane == 0 && wtot > 0) base = atomicAdd(&L.sel_count, wtot);
-  int pos = __builtin_amdgcn_readfirstlane(base) + incl - n;
+  int pos = __builtin_amdgcn_readfirstlane(base);
   if (wtot > 0) {
 #pragma unroll
     for (int q = 0; q < PER_THREAD; ++q) {
       const bool h = x[q] >= tau_f;
-      if (__ballot(h)) {  // wave-uniform: most elements of a wave have no candidate
-        if (h) {
-          if (pos < FAST_CAP) L.sel[pos] = cand_pack(f32_key(x[q]), id0 + (uint32_t)off(q));
-          ++pos;
-        }
+      const unsigned long long hm = __ballot(h);
+      if (hm) {  // wave-uniform: most elements of a wave have no candidate
+        const int p = pos + (int)__builtin_amdgcn_mbcnt_hi((unsigned)(hm >> 32),
+                                                           __builtin_amdgcn_mbcnt_lo((unsigned)hm, 0u));
+        if (h && p < FAST_CAP) L.sel[p] = cand_pack(f32_key(x[q]), id0 + (uint32_t)off(q));
+        pos += (int)__popcll(hm);
       }
     }
   }
