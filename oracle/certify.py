@@ -2,23 +2,52 @@
 
 Only tests/, smoke() and bench.py's CPU-baseline leg use this module.
 
-Given a tree produced elsewhere (the GPU library) and the oracle's tree for
-the same request, `compare` reports:
-  * exact   -- tokens and parents equal node for node, in pop order;
-  * scores  -- max |score difference| over the nodes that match;
-  * near_tie -- at the first mismatch, the oracle had a competitor within
-               `tol` (a pop, a top-k boundary or a top-M boundary);
-  * certificate failures on the other tree, re-evaluated with the oracle's
-    arithmetic along its own paths:
-      - node 0 is the root; parents precede children; depth = parent + 1;
-        no duplicate (parent, token) pairs; n_nodes == N unless the frontier
-        is empty;
-      - each node's score equals its path score within tol;
-      - each node's token is within tol of its parent's top-k boundary;
-      - scores are non-increasing in pop order (within tol);
-      - no child left out of the tree beats the tree's worst node by more
-        than tol (the tree is a best-first prefix, up to tol).
-A certificate failure is a bug in one of the two implementations.
+The pages call DominoTree's builder lossless up to floating-point
+tie-breaking ("Riassunto Tecnico: DominoTree", Risultati Sperimentali) and
+bit-identical to its Python reference (Componenti Core 3).  This module turns
+that into a check of another builder's tree (the GPU library) against the
+oracle's tree for the same request.
+
+`compare` reports:
+  * exact      -- tokens and parents equal node for node, in pop order, and
+                  the same node count;
+  * max_dscore -- max |score difference| over the nodes before the first
+                  difference;
+  * near_tie   -- the decision that produced the first difference, when the
+                  oracle had a competitor within `tol` there ("pop" or
+                  "topk"; "topm" only for base logits computed by an LM head,
+                  see `_tie_at`), else "";
+  * census     -- how many of the oracle's own decisions had a runner-up
+                  within the tolerance (pops and top-k boundaries within
+                  `tol`; with computed logits also top-M boundaries within
+                  `tol_logit`).  With none, nothing excuses a difference and
+                  the tree must be exact (`must_be_exact`);
+  * failures   -- certificate clauses the other tree breaks, each tagged
+                  with its clause name in brackets, re-evaluated with the
+                  oracle's arithmetic along the other tree's own paths:
+      [root]     node 0 is the root record (token -1, parent -1, depth 0,
+                 score 0);
+      [count]    0 <= n_nodes <= N;
+      [order]    every parent precedes its child;
+      [depth]    depth = parent's depth + 1, at most D;
+      [dup]      no two nodes share (parent, token);
+      [expand]   every parent is expandable (the root, or depth < D and
+                 index < N);
+      [score]    each node's score equals its path score within tol;
+      [mono]     scores do not rise in pop order (by more than tol);
+      [cand]     each token is a candidate of its depth;
+      [topk]     each token is within tol of its parent's top-k boundary;
+      [budget]   when n_nodes < N (the frontier ran dry), every expanded
+                 node has all its children (its finite top-k) in the tree;
+      [frontier] no left-out child that leads its parent's first candidate
+                 after the top-k by at least tol beats the tree's worst node
+                 by more than tol (the tree is a best-first prefix, up to
+                 tol);
+    and the comparison's own clauses:
+      [dscore]   matched nodes' scores within tol of the oracle's;
+      [mismatch] a first difference that no near tie at that decision
+                 excuses.
+A failure is a bug in one of the two implementations.
 """
 from __future__ import annotations
 
@@ -39,18 +68,46 @@ class Report:
     near_tie: str                 # "" or the decision type that tied
     max_dscore: float             # over nodes matching the oracle's
     failures: list = field(default_factory=list)
+    census: dict = field(default_factory=dict)
 
     @property
     def ok(self) -> bool:
         return not self.failures and (self.exact or bool(self.near_tie))
+
+    @property
+    def must_be_exact(self) -> bool:
+        """No oracle decision had a runner-up within the tolerance."""
+        return sum(self.census.values()) == 0
+
+
+def census(otree: ref.Tree, tol: float, logits_computed: bool = False,
+           tol_logit: float = 1e-4) -> dict:
+    """Counts of the oracle's decisions whose runner-up was within tolerance.
+
+    pop:  pops whose next heap entry was within `tol` of the popped score;
+    topk: expanded nodes whose k-th and (k+1)-th corrected logits were within
+          `tol` (z units, the log-prob gap at the boundary);
+    topm: depths whose M-th and (M+1)-th base logits were within `tol_logit`,
+          counted only when the logits were computed (an LM head): given
+          logits are selected by pure comparisons on identical inputs.
+    """
+    n = otree.n_nodes
+    out = {"pop": sum(1 for m in otree.pop_margin[:n] if m < tol),
+           "topk": sum(1 for m in otree.topk_margin.values() if m < tol)}
+    if logits_computed:
+        out["topm"] = sum(1 for d in otree.depths_info if d.margin < tol_logit)
+    return out
 
 
 def evaluate(head, deps, hidden, root, tokens, parents, n: int, k: int, T: float,
              norm: str, N: int):
     """Oracle arithmetic along the given tree's own paths.
 
-    Returns per-node path scores, per-node expansions (for nodes the builder
-    expands: depth < D and index < N) and per-node states.
+    The tree's structure must already be valid (parents precede children).
+    Returns per-node path scores, the expansion of every node the builder
+    expands (the root, and nodes with depth < D and index < N) and per-node
+    depths.  A node whose parent has no expansion, or whose token is not a
+    candidate, scores nan or -inf and is not expanded.
     """
     D = len(deps)
     states = {0: np.asarray(root, dtype=np.float64)}
@@ -63,7 +120,7 @@ def evaluate(head, deps, hidden, root, tokens, parents, n: int, k: int, T: float
             tok = int(tokens[i])
             depth[i] = depth[p] + 1
             ex = exps.get(p)
-            if ex is None:      # parent not expandable: certificate reports it
+            if ex is None:      # parent not expandable: the certificate reports it
                 score[i] = math.nan
                 continue
             hit = np.nonzero(deps[depth[i] - 1].cand == tok)[0]
@@ -77,74 +134,104 @@ def evaluate(head, deps, hidden, root, tokens, parents, n: int, k: int, T: float
     return score, exps, depth
 
 
-def certify(head, deps, hidden, root, tokens, parents, depths, scores, n: int, k: int,
-            T: float, norm: str, N: int, tol: float) -> list:
+def _structure(tokens, parents, depths, scores, n: int, D: int, N: int) -> list:
+    """Clauses root, count, order, depth, dup, expand (no arithmetic)."""
     fails = []
-    D = len(deps)
     if int(tokens[0]) != -1 or int(parents[0]) != -1 or int(depths[0]) != 0 \
             or float(scores[0]) != 0.0:
-        fails.append("root record")
+        fails.append("[root] node 0 is not the root record")
+    if not 0 <= n <= N:
+        fails.append(f"[count] n_nodes {n} outside 0..{N}")
+        return fails
     seen = set()
     for i in range(1, n + 1):
         p = int(parents[i])
-        if not (0 <= p < i):
-            fails.append(f"node {i}: parent {p} does not precede it")
+        if not 0 <= p < i:
+            fails.append(f"[order] node {i}: parent {p} does not precede it")
             return fails
         if int(depths[i]) != int(depths[p]) + 1 or int(depths[i]) > D:
-            fails.append(f"node {i}: depth {depths[i]} vs parent depth {depths[p]}")
+            fails.append(f"[depth] node {i}: depth {depths[i]} vs parent depth {depths[p]}")
         if (p, int(tokens[i])) in seen:
-            fails.append(f"node {i}: duplicate child token {tokens[i]} of {p}")
+            fails.append(f"[dup] node {i}: duplicate child token {tokens[i]} of {p}")
         seen.add((p, int(tokens[i])))
         if p > 0 and (int(depths[p]) >= D or p >= N):
-            fails.append(f"node {i}: parent {p} is not expandable")
-    if fails:
-        return fails
-    sc, exps, _ = evaluate(head, deps, hidden, root, tokens, parents, n, k, T, norm, N)
+            fails.append(f"[expand] node {i}: parent {p} is not expandable")
+    return fails
+
+
+def _arithmetic(deps, tokens, parents, depths, scores, n: int, k: int, N: int, tol: float,
+                sc: dict, exps: dict) -> list:
+    """Clauses score, mono, cand, topk, budget, frontier on a valid structure."""
+    fails = []
     for i in range(1, n + 1):
         if not abs(float(scores[i]) - sc[i]) <= tol:
-            fails.append(f"node {i}: score {float(scores[i])!r} vs path score {sc[i]!r}")
+            fails.append(f"[score] node {i}: score {float(scores[i])!r} vs path score {sc[i]!r}")
         if i > 1 and float(scores[i]) > float(scores[i - 1]) + tol:
-            fails.append(f"node {i}: score rises in pop order")
+            fails.append(f"[mono] node {i}: score rises in pop order")
         p = int(parents[i])
-        ex = exps.get(p)
-        if ex is None:
-            fails.append(f"node {i}: parent {p} has no valid path")
-            continue
+        ex = exps[p]
         dep = deps[int(depths[i]) - 1]
-        m = int(np.nonzero(dep.cand == int(tokens[i]))[0][0]) \
-            if np.any(dep.cand == int(tokens[i])) else -1
-        if m < 0:
-            fails.append(f"node {i}: token {tokens[i]} not a candidate of depth {depths[i]}")
+        hit = np.nonzero(dep.cand == int(tokens[i]))[0]
+        if hit.size == 0:
+            fails.append(f"[cand] node {i}: token {tokens[i]} not a candidate of depth {depths[i]}")
             continue
         order = ref.rank_desc(ex.z, dep.cand)
         kth = ex.z[order[min(k, len(order)) - 1]]
-        if not ex.z[m] >= kth - tol:
-            fails.append(f"node {i}: token outside its parent's top-{k} by more than tol")
-    # frontier: legal children of expanded nodes that are not in the tree
+        if not ex.z[hit[0]] >= kth - tol:
+            fails.append(f"[topk] node {i}: token outside its parent's top-{k} by more than tol")
+    # children of expanded nodes that are not in the tree.  A builder that
+    # met a top-k boundary within tol may have pushed another candidate in
+    # place of one of the oracle's children, so only a child that leads the
+    # first candidate after the top-k by at least tol is required.
     in_tree = {(int(parents[i]), int(tokens[i])) for i in range(1, n + 1)}
+    kids_in = {}
+    for i in range(1, n + 1):
+        kids_in[int(parents[i])] = kids_in.get(int(parents[i]), 0) + 1
     worst = min((float(scores[i]) for i in range(1, n + 1)), default=math.inf)
     best_out = ref.NEG_INF
     for p, ex in exps.items():
         if p > n:
             continue
         dep = deps[int(depths[p])]
+        order = ref.rank_desc(ex.z, dep.cand)
+        next_z = ex.z[order[k]] if len(order) > k else ref.NEG_INF
         for m in ex.children:
-            if (p, int(dep.cand[m])) not in in_tree:
+            if (p, int(dep.cand[m])) not in in_tree and ex.z[m] - next_z >= tol:
                 best_out = max(best_out, sc[p] + float(ex.logp[m]))
-    if n < N and best_out != ref.NEG_INF:
-        fails.append(f"n_nodes {n} < budget {N} while the frontier is not empty")
+        if n < N and kids_in.get(p, 0) != len(ex.children):
+            fails.append(f"[budget] n_nodes {n} < budget {N} while node {p} has "
+                         f"{kids_in.get(p, 0)} of its {len(ex.children)} children")
     if n > 0 and best_out > worst + tol:
-        fails.append(f"a left-out child scores {best_out!r} > worst node {worst!r} + tol")
+        fails.append(f"[frontier] a left-out child scores {best_out!r} > worst node {worst!r} + tol")
     return fails
 
 
+def certify(head, deps, hidden, root, tokens, parents, depths, scores, n: int, k: int,
+            T: float, norm: str, N: int, tol: float) -> list:
+    """The certificate clauses (module doc) of one tree; returns the failures."""
+    fails = _structure(tokens, parents, depths, scores, n, len(deps), N)
+    if fails:
+        return fails
+    sc, exps, _ = evaluate(head, deps, hidden, root, tokens, parents, n, k, T, norm, N)
+    return _arithmetic(deps, tokens, parents, depths, scores, n, k, N, tol, sc, exps)
+
+
 def compare(otree: ref.Tree, head, hidden, root, other: dict, k: int, T: float,
-            norm: str, N: int, tol: float) -> Report:
-    """Compare another builder's tree with the oracle's (see module doc)."""
+            norm: str, N: int, tol: float, logits_computed: bool = False,
+            tol_logit: float = 1e-4) -> Report:
+    """Compare another builder's tree with the oracle's (see module doc).
+
+    `other` holds tokens, parents, depths, scores ([N + 1] each) and n_nodes.
+    `logits_computed`: the base logits came from an LM head on both sides
+    (each with its own rounding), so the top-M boundaries can tie too.
+    """
     n_o = otree.n_nodes
     n_x = int(other["n_nodes"])
     tok, par, dep, scs = other["tokens"], other["parents"], other["depths"], other["scores"]
-    L = min(n_o, n_x)
+    deps = otree.depths_info
+    cen = census(otree, tol, logits_computed, tol_logit)
+    fails = _structure(tok, par, dep, scs, n_x, len(deps), N)
+    L = max(0, min(n_o, n_x))
     first = -1
     maxd = 0.0
     for i in range(1, L + 1):
@@ -156,33 +243,60 @@ def compare(otree: ref.Tree, head, hidden, root, other: dict, k: int, T: float,
     if first < 0 and not exact:
         first = L + 1
     near = ""
-    if not exact:
-        near = _tie_at(otree, first, tol)
-    fails = certify(head, otree.depths_info, hidden, root, tok, par, dep, scs, n_x, k, T,
-                    norm, N, tol)
+    if not fails:
+        sc, exps, _ = evaluate(head, deps, hidden, root, tok, par, n_x, k, T, norm, N)
+        fails = _arithmetic(deps, tok, par, dep, scs, n_x, k, N, tol, sc, exps)
+        if not exact:
+            near = _tie_at(otree, tok, par, dep, n_x, first, sc, exps, tol, logits_computed,
+                           tol_logit)
     if not exact and not near:
-        fails.append(f"mismatch at node {first} with no oracle decision within tol")
+        fails.append(f"[mismatch] first difference at node {first} with no oracle decision "
+                     f"within tol there")
     if maxd > tol:
-        fails.append(f"matched-node score difference {maxd!r} > tol")
+        fails.append(f"[dscore] matched-node score difference {maxd!r} > tol")
     return Report(exact=exact, n_oracle=n_o, n_other=n_x, first_mismatch=first,
-                  near_tie=near, max_dscore=maxd, failures=fails)
+                  near_tie=near, max_dscore=maxd, failures=fails, census=cen)
 
 
-def _tie_at(otree: ref.Tree, first: int, tol: float) -> str:
-    """Which oracle decision at node `first` had a competitor within tol.
+def _tie_at(otree: ref.Tree, tokens, parents, depths, n_x: int, first: int, sc: dict,
+            exps: dict, tol: float, logits_computed: bool, tol_logit: float) -> str:
+    """The near tie that excuses the first difference, or "".
 
-    Every node before `first` matched, so the trees part at the pop that
-    produced node `first`: either the oracle's heap held an entry within tol
-    of the one it popped, or a node expanded earlier pushed a different child
-    set (a top-k boundary within tol), or the candidate sets differ (a top-M
-    boundary within tol, possible only when the base logits are computed).
+    Nodes 1..first-1 are the same in both trees, so both builders took the
+    same pops up to there and expanded the same nodes the same way (in the
+    oracle's arithmetic).  Let A be the oracle's node `first` and B the other
+    tree's.  The difference is excused only when the two are competitors
+    within the tolerance in the oracle's own arithmetic, |score(A) -
+    score(B)| < tol (B scored along its own path), and then by the decision
+    that separates them:
+      * "pop"  -- B is one of the oracle's children of its parent, so both
+                  were in the oracle's heap at this pop and the oracle's pop
+                  margin there is below tol;
+      * "topk" -- B is not one of them: B's parent (a node both trees share)
+                  had a top-k boundary within tol, where the other builder
+                  kept B instead;
+      * "topm" -- only for computed logits: B's token is not among the
+                  oracle's candidates of its depth, and that depth's top-M
+                  boundary was within tol_logit.
+    Differing node counts (one tree a prefix of the other) are never excused:
+    the count depends on no floating-point decision.
     """
-    if first - 1 < len(otree.pop_margin) and otree.pop_margin[first - 1] < tol:
-        return "pop"
-    for i, mg in otree.topk_margin.items():
-        if i < first and mg < tol:
-            return "topk"
-    for d in otree.depths_info:
-        if d.margin < tol:
+    n_o = otree.n_nodes
+    if first < 1 or first > n_o or first > n_x:
+        return ""
+    pb, tb = int(parents[first]), int(tokens[first])
+    db = int(depths[first])
+    dep = otree.depths_info[db - 1]
+    if not np.any(dep.cand == tb):
+        if logits_computed and dep.margin < tol_logit:
             return "topm"
-    return ""
+        return ""
+    if not abs(otree.scores[first] - sc[first]) < tol:
+        return ""
+    ex = exps.get(pb)
+    if ex is None:
+        return ""
+    kids = {int(dep.cand[m]) for m in ex.children}
+    if tb in kids:
+        return "pop" if otree.pop_margin[first - 1] < tol else ""
+    return "topk" if otree.topk_margin.get(pb, math.inf) < tol else ""
