@@ -1,10 +1,11 @@
 """ctypes binding of libdominotree.so (argument marshalling only).
 
-The functions dt_create / dt_build_trees / dt_sync_status / dt_phase_times /
-dt_destroy / dt_tree_attention_inputs / dt_last_error / dt_version mirror
-include/dominotree.h one to one; TreeBuilder and tree_attention_inputs wrap
-them for torch device tensors.  Every step of the
-build runs in the HIP library: when it is not built, loading fails loudly.
+The dt_* functions mirror include/dominotree.h one to one; TreeBuilder and
+tree_attention_inputs wrap them for torch device tensors and check every
+tensor's device, dtype, shape and layout against the handle's dimensions
+before a pointer reaches the library (a wrong size would make a kernel read
+past an allocation).  Every step of the build runs in the HIP library: when
+it is not built, loading fails loudly.
 """
 from __future__ import annotations
 
@@ -55,6 +56,11 @@ class Outputs(C.Structure):
                 ("cand_logits", C.c_void_p), ("lse", C.c_void_p)]
 
 
+class Schedule(C.Structure):
+    _fields_ = [("pops", C.c_int32), ("halves", C.c_int32), ("lds_workers", C.c_int32),
+                ("tiles_per_worker", C.c_int32)]
+
+
 class TreeView(C.Structure):
     _fields_ = [("batch", C.c_int32), ("cols", C.c_int32), ("parents", C.c_void_p),
                 ("depths", C.c_void_p), ("tokens", C.c_void_p), ("n_nodes", C.c_void_p),
@@ -67,7 +73,8 @@ class VerifyOutputs(C.Structure):
 
 
 EXPORTS = ["dt_create", "dt_build_trees", "dt_sync_status", "dt_phase_times", "dt_destroy",
-           "dt_last_error", "dt_version", "dt_tree_attention_inputs", "dt_draft_chain", "dt_fold_state"]
+           "dt_last_error", "dt_version", "dt_tree_attention_inputs", "dt_draft_chain", "dt_fold_state",
+           "dt_set_schedule", "dt_set_device_error"]
 _lib = None
 
 
@@ -107,6 +114,10 @@ def load_library():
     lib.dt_fold_state.restype = C.c_int
     lib.dt_fold_state.argtypes = [C.c_void_p, C.c_int32, C.c_int32, C.c_void_p, C.c_void_p, C.c_void_p,
                                   C.c_uint32, C.c_void_p]
+    lib.dt_set_schedule.restype = C.c_int
+    lib.dt_set_schedule.argtypes = [C.c_void_p, C.POINTER(Schedule)]
+    lib.dt_set_device_error.restype = C.c_int
+    lib.dt_set_device_error.argtypes = [C.c_void_p, C.c_int32, C.c_void_p]
     lib.dt_tree_attention_inputs.restype = C.c_int
     lib.dt_tree_attention_inputs.argtypes = [C.POINTER(TreeView), C.POINTER(VerifyOutputs), C.c_void_p]
     _lib = lib
@@ -169,6 +180,15 @@ def dt_fold_state(handle: int, batch: int, n_tokens: int, tokens: int, prev_stat
                                         C.c_void_p(stream)))
 
 
+def dt_set_schedule(handle: int, sched):
+    """sched: a Schedule, or None for the defaults."""
+    _check(load_library().dt_set_schedule(C.c_void_p(handle), None if sched is None else C.byref(sched)))
+
+
+def dt_set_device_error(handle: int, code: int, stream: int = 0):
+    _check(load_library().dt_set_device_error(C.c_void_p(handle), code, C.c_void_p(stream)))
+
+
 def dt_tree_attention_inputs(view: TreeView, out: VerifyOutputs, stream: int = 0):
     _check(load_library().dt_tree_attention_inputs(C.byref(view), C.byref(out), C.c_void_p(stream)))
 
@@ -181,11 +201,34 @@ def _ptr(t):
     return None if t is None else t.data_ptr()
 
 
+def _check_tensor(name, t, dtype, shape, device=None, optional=False, where=True):
+    """Refuse a tensor whose dtype, shape, layout or (with `where`) device the
+    library would misread (ValueError, before any pointer reaches the C ABI)."""
+    if t is None:
+        if optional:
+            return
+        raise ValueError(f"{name} is required")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if not where:
+        return
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, the handle on {device}")
+
+
 class TreeBuilder:
     """A handle plus caller-owned output tensors, for torch device tensors.
 
-    weights: dict with emb, w_ih, w_hh, w1, w2 (torch.float32 or torch.bfloat16,
-    contiguous, on the device) and optional b_ih, b_hh (float32) and w_lm.
+    weights: dict with emb [V, e], w_ih [3 d_s, e], w_hh [3 d_s, d_s],
+    w1 [h + d_s, r], w2 [r, V] (all torch.float32, or all torch.bfloat16),
+    optional b_ih, b_hh ([3 d_s] float32) and w_lm ([h, V], bf16); contiguous,
+    on one device.
     """
 
     def __init__(self, weights: dict, *, vocab, depths, hidden, emb_dim, state_dim, rank,
@@ -193,11 +236,25 @@ class TreeBuilder:
         import torch
         self.torch = torch
         w = {k: v for k, v in weights.items() if v is not None}
+        for k in ("emb", "w_ih", "w_hh", "w1", "w2"):
+            if k not in w:
+                raise ValueError(f"weight {k} is required")
         dt = w["w_ih"].dtype
+        if dt not in (torch.float32, torch.bfloat16):
+            raise ValueError(f"weights must be float32 or bfloat16, got {dt}")
         self.wdtype = DT_BF16 if dt == torch.bfloat16 else DT_F32
-        for k, v in w.items():
-            if not v.is_cuda or not v.is_contiguous():
-                raise ValueError(f"weight {k} must be a contiguous device tensor")
+        self.tdtype = dt
+        dev = w["w_ih"].device
+        V, h, e, ds, r = vocab, hidden, emb_dim, state_dim, rank
+        shapes = {"emb": (V, e), "w_ih": (3 * ds, e), "w_hh": (3 * ds, ds), "w1": (h + ds, r),
+                  "w2": (r, V), "w_lm": (h, V)}
+        for where in (False, True):   # every dtype and shape first, then the devices
+            for k, shp in shapes.items():
+                _check_tensor(f"weight {k}", w.get(k), dt, shp, dev, optional=k == "w_lm", where=where)
+            for k in ("b_ih", "b_hh"):
+                _check_tensor(f"weight {k}", w.get(k), torch.float32, (3 * ds,), dev, optional=True,
+                              where=where)
+        self.device = dev
         self._keep = w   # emb is referenced by the handle
         self.dims = Dims(vocab, depths, hidden, emb_dim, state_dim, rank, max_batch, self.wdtype)
         self.wts = Weights(_ptr(w["emb"]), _ptr(w["w_ih"]), _ptr(w["w_hh"]), _ptr(w.get("b_ih")),
@@ -219,7 +276,7 @@ class TreeBuilder:
 
     def outputs(self, batch: int, top_m: int, budget: int, candidates: bool = False) -> dict:
         torch = self.torch
-        dev = self._keep["w_ih"].device
+        dev = self.device
         o = {
             "tokens": torch.empty((batch, budget + 1), dtype=torch.int32, device=dev),
             "parents": torch.empty((batch, budget + 1), dtype=torch.int32, device=dev),
@@ -234,16 +291,40 @@ class TreeBuilder:
             o["lse"] = torch.empty((batch, D), dtype=torch.float32, device=dev)
         return o
 
+    def _check_inputs(self, hidden, base_logits, root_state):
+        torch = self.torch
+        d = self.dims
+        if hidden is None or hidden.dim() != 3:
+            raise ValueError("hidden must be [batch, depths, hidden]")
+        b = hidden.shape[0]
+        if not 1 <= b <= d.max_batch:
+            raise ValueError(f"batch {b} outside 1..{d.max_batch}")
+        for where in (False, True):
+            _check_tensor("hidden", hidden, self.tdtype, (b, d.depths, d.hidden), self.device, where=where)
+            _check_tensor("base_logits", base_logits, torch.float32, (b, d.depths, d.vocab), self.device,
+                          optional=True, where=where)
+            _check_tensor("root_state", root_state, torch.float32, (b, d.state_dim), self.device,
+                          optional=True, where=where)
+        return b
+
     def build(self, hidden, base_logits=None, root_state=None, *, top_m, top_k, budget,
               temperature=1.0, norm=DT_NORM_TOPM, flags=None, out=None, candidates=False):
         """Enqueue one build on the builder's stream; returns the output tensors."""
+        torch = self.torch
         if flags is None:
             flags = DT_ACT_BF16 if self.wdtype == DT_BF16 else 0
-        batch = hidden.shape[0]
-        for name, t in (("hidden", hidden), ("base_logits", base_logits), ("root_state", root_state)):
-            if t is not None and (not t.is_cuda or not t.is_contiguous()):
-                raise ValueError(f"{name} must be a contiguous device tensor")
+        batch = self._check_inputs(hidden, base_logits, root_state)
         o = out if out is not None else self.outputs(batch, top_m, budget, candidates)
+        for k in ("tokens", "parents", "depths"):
+            _check_tensor(f"output {k}", o.get(k), torch.int32, (batch, budget + 1), self.device)
+        _check_tensor("output scores", o.get("scores"), torch.float32, (batch, budget + 1), self.device)
+        _check_tensor("output n_nodes", o.get("n_nodes"), torch.int32, (batch,), self.device)
+        D = self.dims.depths
+        _check_tensor("output cand_ids", o.get("cand_ids"), torch.int32, (batch, D, top_m), self.device,
+                      optional=True)
+        _check_tensor("output cand_logits", o.get("cand_logits"), torch.float32, (batch, D, top_m),
+                      self.device, optional=True)
+        _check_tensor("output lse", o.get("lse"), torch.float32, (batch, D), self.device, optional=True)
         inp = Inputs(batch, _ptr(base_logits), _ptr(hidden), _ptr(root_state))
         prm = Params(top_m, top_k, budget, float(temperature), norm, flags)
         outs = Outputs(_ptr(o["tokens"]), _ptr(o["parents"]), _ptr(o["depths"]), _ptr(o["scores"]),
@@ -258,14 +339,13 @@ class TreeBuilder:
         torch = self.torch
         if flags is None:
             flags = DT_ACT_BF16 if self.wdtype == DT_BF16 else 0
-        for name, t in (("hidden", hidden), ("base_logits", base_logits), ("root_state", root_state)):
-            if t is not None and (not t.is_cuda or not t.is_contiguous()):
-                raise ValueError(f"{name} must be a contiguous device tensor")
-        b, D = hidden.shape[0], self.dims.depths
-        dev = self._keep["w_ih"].device
+        b = self._check_inputs(hidden, base_logits, root_state)
+        D = self.dims.depths
         o = out if out is not None else {
-            "tokens": torch.empty((b, D), dtype=torch.int32, device=dev),
-            "logits": torch.empty((b, D), dtype=torch.float32, device=dev)}
+            "tokens": torch.empty((b, D), dtype=torch.int32, device=self.device),
+            "logits": torch.empty((b, D), dtype=torch.float32, device=self.device)}
+        _check_tensor("output tokens", o.get("tokens"), torch.int32, (b, D), self.device)
+        _check_tensor("output logits", o.get("logits"), torch.float32, (b, D), self.device, optional=True)
         inp = Inputs(b, _ptr(base_logits), _ptr(hidden), _ptr(root_state))
         dt_draft_chain(self.handle, inp, flags, _ptr(o["tokens"]), _ptr(o.get("logits")),
                        self.stream.cuda_stream)
@@ -277,20 +357,32 @@ class TreeBuilder:
         torch = self.torch
         if flags is None:
             flags = DT_ACT_BF16 if self.wdtype == DT_BF16 else 0
-        for name, t in (("tokens", tokens), ("prev_state", prev_state)):
-            if t is not None and (not t.is_cuda or not t.is_contiguous()):
-                raise ValueError(f"{name} must be a contiguous device tensor")
-        if tokens.dtype != torch.int32:
-            raise ValueError("tokens must be int32")
+        if tokens is None or tokens.dim() != 2:
+            raise ValueError("tokens must be [batch, n_tokens]")
         b, L = tokens.shape
-        o = out if out is not None else torch.empty((b, self.dims.state_dim), dtype=torch.float32,
-                                                    device=tokens.device)
+        if not 1 <= b <= self.dims.max_batch:
+            raise ValueError(f"batch {b} outside 1..{self.dims.max_batch}")
+        ds = self.dims.state_dim
+        for where in (False, True):
+            _check_tensor("tokens", tokens, torch.int32, (b, L), self.device, where=where)
+            _check_tensor("prev_state", prev_state, torch.float32, (b, ds), self.device, optional=True,
+                          where=where)
+        o = out if out is not None else torch.empty((b, ds), dtype=torch.float32, device=self.device)
+        _check_tensor("state_out", o, torch.float32, (b, ds), self.device)
         dt_fold_state(self.handle, b, L, _ptr(tokens), _ptr(prev_state), _ptr(o), flags,
                       self.stream.cuda_stream)
         return o
 
     def sync_status(self):
         dt_sync_status(self.handle, self.stream.cuda_stream)
+
+    def set_schedule(self, pops=0, halves=0, lds_workers=0, tiles_per_worker=0):
+        """Schedule of the next builds (dt_set_schedule); all zeros: defaults."""
+        dt_set_schedule(self.handle, Schedule(pops, halves, lds_workers, tiles_per_worker))
+
+    def set_device_error(self, code=1):
+        """Test hook of the failure path (dt_set_device_error)."""
+        dt_set_device_error(self.handle, code, self.stream.cuda_stream)
 
     def phase_times(self) -> tuple:
         """Mean ms per phase (PHASES order: the LM head or P, candidates, the
@@ -306,12 +398,15 @@ def tree_attention_inputs(parents, depths, n_nodes, tokens=None, prefix_len=None
     [b, cols, ceil(cols / 32)] int32 (bit patterns of the uint32 words),
     positions [b, cols], tokens [b, cols] (when `tokens` is given) and bad [b]."""
     import torch
+    if parents is None or parents.dim() != 2:
+        raise ValueError("parents must be [batch, cols]")
     b, cols = parents.shape
-    for name, t in (("parents", parents), ("depths", depths), ("n_nodes", n_nodes),
-                    ("tokens", tokens), ("prefix_len", prefix_len), ("anchor", anchor)):
-        if t is not None and (not t.is_cuda or not t.is_contiguous() or t.dtype != torch.int32):
-            raise ValueError(f"{name} must be a contiguous int32 device tensor")
     dev = parents.device
+    for where in (False, True):
+        for name, t, shp, opt in (("parents", parents, (b, cols), False), ("depths", depths, (b, cols), False),
+                                  ("n_nodes", n_nodes, (b,), False), ("tokens", tokens, (b, cols), True),
+                                  ("prefix_len", prefix_len, (b,), True), ("anchor", anchor, (b,), True)):
+            _check_tensor(name, t, torch.int32, shp, dev, optional=opt, where=where)
     words = (cols + 31) // 32
     o = {"mask": torch.empty((b, cols, words), dtype=torch.int32, device=dev),
          "positions": torch.empty((b, cols), dtype=torch.int32, device=dev),

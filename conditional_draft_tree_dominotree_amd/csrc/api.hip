@@ -74,7 +74,9 @@ struct dt_handle {
   uint32_t* mbox_w = nullptr;  // group flags, then the worker mailboxes
   uint32_t* mbox_c = nullptr;
   int* err = nullptr;
+  int* err_host = nullptr;  // pinned mirror of err, set by a builder launch that ends with err set
   int* nanflag = nullptr;
+  dt_schedule sched{};      // schedule overrides (dt_set_schedule); zeros: defaults
   float* chain_gu = nullptr;     // chain head: [max_batch, 3 ds + r]
   float* chain_s = nullptr;      // [max_batch, ds]
   void* chain_sop = nullptr;     // [max_batch, ds] (wdtype)
@@ -115,6 +117,7 @@ void free_all(dt_handle* h) {
   if (h->fork_ev) (void)hipEventDestroy(h->fork_ev);
   if (h->join_ev) (void)hipEventDestroy(h->join_ev);
   if (h->side) (void)hipStreamDestroy(h->side);
+  if (h->err_host) (void)hipHostFree(h->err_host);
 }
 
 dt_status check_dims(const dt_dims* d) {
@@ -152,8 +155,7 @@ dt_status check_params(const dt_params* p, int V, const dt_params* maxp) {
 
 // tiles per worker: one per worker when the workers fit beside the controllers
 int choose_tpw(const dt_handle* h, int B) {
-  const char* env = getenv("DT_TILES_PER_WORKER");
-  if (env && atoi(env) > 0) return atoi(env);
+  if (h->sched.tiles_per_worker > 0) return h->sched.tiles_per_worker;
   const int avail = h->n_cu - B;
   int tpw = 1;
   while ((h->n_tiles + tpw - 1) / tpw > avail) ++tpw;
@@ -291,6 +293,8 @@ dt_status dt_create(dt_handle** out, const dt_dims* dims, const dt_weights* w, c
   ALLOC(h->err, 64);
   ALLOC(h->nanflag, 64);
   HIPB(hipMemsetAsync(h->err, 0, 64, stream));
+  HIPB(hipHostMalloc(reinterpret_cast<void**>(&h->err_host), 64, hipHostMallocCoherent));
+  *reinterpret_cast<volatile int*>(h->err_host) = 0;
   HIPB(hipMemsetAsync(h->mbox_w, 0, (dt::GFLAG_WORDS + (size_t)h->max_workers * 32) * sizeof(uint32_t), stream));
   HIPB(hipMemsetAsync(h->mbox_c, 0, (size_t)DT_MAX_BATCH * 256 * sizeof(uint32_t), stream));
   for (auto& set : h->ev)
@@ -319,6 +323,11 @@ dt_status dt_build_trees(dt_handle* h, const dt_inputs* in, const dt_params* p, 
   if (!in->base_logits && !h->wlm_t) return fail(DT_EINVAL, "no base logits and no LM head weights");
   if (h->bf16 && !(p->flags & DT_ACT_BF16))
     return fail(DT_EUNSUPPORTED, "bf16 weights need DT_ACT_BF16 (bf16 GEMM operands)");
+  // a finished launch that ended with the device error word set (the mirror
+  // is read without a synchronisation; dt_sync_status reports and clears it)
+  if (const int e = *reinterpret_cast<volatile int*>(h->err_host))
+    return fail(DT_EDEVICE, "a previous build's device wait ran out (error word %d); dt_sync_status resets the handle",
+                e);
 
   const int B = in->batch, D = d.depths, V = d.vocab, M = p->top_m, N = p->budget;
   const int rows = B * D;
@@ -414,17 +423,15 @@ dt_status dt_build_trees(dt_handle* h, const dt_inputs* in, const dt_params* p, 
   a.mbox_w = h->mbox_w + dt::GFLAG_WORDS;
   a.mbox_c = h->mbox_c;
   a.err = h->err;
+  a.err_host = h->err_host;
   a.tokens = out->tokens;
   a.parents = out->parents;
   a.depths = out->depths;
   a.scores = out->scores;
   a.n_nodes = out->n_nodes;
   a.spin_limit = 1u << 21;
-  const char* pops_env = getenv("DT_POPS");
-  const char* workers_env = getenv("DT_WORKERS");  // "lds": workers stage operands in LDS
-  const char* halves_env = getenv("DT_HALVES");    // 1 or 2: split of the batch between the workers' turns
-  const size_t lds = dt::plan_tree(a, h->bf16, pops_env ? atoi(pops_env) : 0, std::min(h->n_cu - B, h->max_workers),
-                                   workers_env && !strcmp(workers_env, "lds"), halves_env ? atoi(halves_env) : 0);
+  const size_t lds = dt::plan_tree(a, h->bf16, h->sched.pops, std::min(h->n_cu - B, h->max_workers),
+                                   h->sched.lds_workers, h->sched.halves);
   if (lds == 0 || lds > 160 * 1024) return fail(DT_EUNSUPPORTED, "no builder schedule fits this shape in LDS");
   if (a.n_workers + B > h->n_cu || a.n_workers > h->max_workers)
     return fail(DT_EUNSUPPORTED, "%d workers + %d requests exceed %d compute units", a.n_workers, B, h->n_cu);
@@ -471,7 +478,39 @@ dt_status dt_sync_status(dt_handle* h, void* stream_) {
   HIPCHK(hipStreamSynchronize(stream));
   int e = 0;
   HIPCHK(hipMemcpy(&e, h->err, sizeof(int), hipMemcpyDeviceToHost));
-  if (e) return fail(DT_EDEVICE, "a builder wait ran out (device error word %d)", e);
+  if (!e) e = *reinterpret_cast<volatile int*>(h->err_host);
+  if (!e) return DT_OK;
+  // reset: clear the error word and its mirror, and re-base the epochs on
+  // cleared mailboxes, so that the next build starts as on a new handle
+  HIPCHK(dt::launch_fill_u32(reinterpret_cast<uint32_t*>(h->err), 0u, 16, stream));
+  HIPCHK(dt::launch_fill_u32(h->mbox_w, 0u, dt::GFLAG_WORDS + (size_t)h->max_workers * 32, stream));
+  HIPCHK(dt::launch_fill_u32(h->mbox_c, 0u, (size_t)DT_MAX_BATCH * 256, stream));
+  HIPCHK(hipStreamSynchronize(stream));
+  h->ebase = 0;
+  *reinterpret_cast<volatile int*>(h->err_host) = 0;
+  return fail(DT_EDEVICE, "a builder wait ran out (device error word %d); the handle is reset", e);
+}
+
+dt_status dt_set_schedule(dt_handle* h, const dt_schedule* s) {
+  if (!h) return fail(DT_EINVAL, "h is NULL");
+  if (!s) {
+    h->sched = dt_schedule{};
+    return DT_OK;
+  }
+  if (s->pops < 0 || s->pops > 16) return fail(DT_EINVAL, "pops %d outside 0..16", s->pops);
+  if (s->halves < 0 || s->halves > 2) return fail(DT_EINVAL, "halves %d outside 0..2", s->halves);
+  if (s->lds_workers != 0 && s->lds_workers != 1) return fail(DT_EINVAL, "lds_workers must be 0 or 1");
+  if (s->tiles_per_worker < 0 || s->tiles_per_worker > 64)
+    return fail(DT_EINVAL, "tiles_per_worker %d outside 0..64", s->tiles_per_worker);
+  h->sched = *s;
+  return DT_OK;
+}
+
+dt_status dt_set_device_error(dt_handle* h, int32_t code, void* stream) {
+  if (!h) return fail(DT_EINVAL, "h is NULL");
+  if (code <= 0) return fail(DT_EINVAL, "code %d must be positive", code);
+  HIPCHK(dt::launch_fill_u32(reinterpret_cast<uint32_t*>(h->err), (uint32_t)code, 1,
+                             reinterpret_cast<hipStream_t>(stream)));
   return DT_OK;
 }
 

@@ -55,6 +55,7 @@ struct TreeArgs {
   uint32_t* mbox_w;        // [n_workers][32] controller -> worker mailboxes (one line each)
   uint32_t* mbox_c;        // [B][256] worker -> controller mailboxes
   int* err;                // device error word
+  int* err_host;           // pinned host mirror: a controller that ends with err set copies it there
   // outputs
   int32_t *tokens, *parents, *depths, *n_nodes;
   float* scores;

@@ -1923,6 +1923,15 @@ __device__ __forceinline__ void controller_main(const TreeArgs& a, unsigned char
     st_dev_u32(a.mbox_w + (size_t)w * 32 + b, mbox_word(a.ebase + tree_epoch_span(a.N) - 1, MBOX_DONE_E));
   stores_done();
   ctl_output(a, c, b, failed);
+  // a launch that ends with the error word set tells the host through the
+  // mirror, which the next build call reads without a synchronisation
+  if (tid == 0) {
+    const uint32_t e = ld_dev_u32(a.err);
+    if (e != 0) {
+      __hip_atomic_store(a.err_host, (int)e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+      __threadfence_system();
+    }
+  }
 }
 
 template <typename W>

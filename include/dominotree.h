@@ -52,9 +52,14 @@
  *
  * Errors: every entry point returns a dt_status; dt_last_error() gives the
  * calling thread's message for the last non-OK status.  Arguments are checked
- * on the host before anything is enqueued; device-side failures (a bounded
- * wait that ran out) are reported by the next dt_build_trees call on the
- * handle or by dt_sync_status().
+ * on the host before anything is enqueued.  A device-side failure (a bounded
+ * wait of the builder that ran out, or a broken invariant) sets the handle's
+ * device error word; the launch that sees it set at its end also sets a
+ * host-visible copy.  From then on dt_build_trees refuses with DT_EDEVICE
+ * (without a synchronisation, so once the failing build has finished), and
+ * dt_sync_status() reports DT_EDEVICE and resets the handle, after which
+ * builds work again.  The trees of a failed build are undefined (its
+ * n_nodes may hold -1).
  */
 #ifndef DOMINOTREE_H
 #define DOMINOTREE_H
@@ -71,7 +76,7 @@ typedef enum {
   DT_EUNSUPPORTED = -2, /* valid but beyond this build's limits */
   DT_ENOMEM = -3,       /* device allocation failed in dt_create */
   DT_EHIP = -4,         /* a HIP runtime call failed (message has the text) */
-  DT_EDEVICE = -5       /* a kernel's bounded wait ran out (device fault) */
+  DT_EDEVICE = -5       /* a builder's bounded wait ran out or an invariant broke on the device */
 } dt_status;
 
 typedef enum { DT_F32 = 0, DT_BF16 = 1 } dt_dtype;
@@ -167,7 +172,8 @@ dt_status dt_create(dt_handle** h, const dt_dims* dims, const dt_weights* w,
                     const dt_params* max_params, void* stream);
 
 /* Build the trees of one batch [DominoTree, 1, 2, 4].  Enqueues the kernels on
- * `stream` and returns: no host synchronisation and no allocation.  Results
+ * `stream` and returns: no host synchronisation and no allocation (except
+ * under DT_VALIDATE, which synchronises to read its NaN scan).  Results
  * are valid once the stream reaches this point.  P = H W1_H runs first on
  * `stream` when base logits are given; with the LM head it runs on a stream
  * the handle owns (default priority), forked from and joined back into
@@ -178,20 +184,46 @@ dt_status dt_create(dt_handle** h, const dt_dims* dims, const dt_weights* w,
  * Errors: DT_EINVAL (NULL pointers, batch out of range, params out of range
  * or above the handle's max_params, NaN logits under DT_VALIDATE, w_lm
  * missing with NULL base logits), DT_EUNSUPPORTED, DT_EHIP, DT_EDEVICE (a
- * previous build's device wait ran out).
- * Schedule overrides, read from the environment at each call: DT_POPS (nodes a
- * request expands per step, at most 16), DT_HALVES (1 or 2: the workers serve
- * the batch whole or in two halves per step), DT_WORKERS=lds and
- * DT_TILES_PER_WORKER (workers that stage operands in LDS).  They change how
- * the work is scheduled, not what is computed: the trees are the same up to
- * the rounding of the per-node products, whose summation order can depend on
- * the worker layout. */
+ * finished earlier build on the handle set the device error word; nothing is
+ * enqueued until dt_sync_status resets the handle). */
 dt_status dt_build_trees(dt_handle* h, const dt_inputs* in, const dt_params* p,
                          dt_outputs* out, void* stream);
 
 /* Synchronise `stream` and report a device-side failure of the handle's
- * builds so far (DT_EDEVICE) or DT_OK. */
+ * builds so far: DT_OK, or DT_EDEVICE after clearing the error word, its host
+ * copy and the builder's mailboxes (synchronising again), so that the next
+ * build runs as on a fresh handle.  Errors: DT_EINVAL (NULL h), DT_EHIP. */
 dt_status dt_sync_status(dt_handle* h, void* stream);
+
+/* Schedule of the tree builder.  These change how the work is spread over the
+ * GPU, not what is computed: the trees are the same up to the rounding of the
+ * per-node products, whose summation order can depend on the worker layout.
+ * Zero in a field keeps the default. */
+typedef struct {
+  int32_t pops;             /* nodes a request may expand per step, 0..16 (default: fill the 512
+                               exchange columns of a step, at most 16) */
+  int32_t halves;           /* 0 (default: two from 2 requests on where the first half fills whole
+                               16-column blocks), 1 (the workers serve the batch whole per step) or 2
+                               (in two halves, one half's products beside the other's scoring) */
+  int32_t lds_workers;      /* 1: workers that stage operands in LDS even where register-resident
+                               workers fit; 0: default */
+  int32_t tiles_per_worker; /* LDS-staging workers: weight tiles per worker block, 0..64 (default:
+                               one per worker when the workers fit beside the controllers) */
+} dt_schedule;
+
+/* Set the schedule the handle's next builds use (NULL restores the defaults).
+ * Host only; takes effect at the next dt_build_trees.  A schedule that does
+ * not fit a build's shape makes that build return DT_EUNSUPPORTED.
+ * Errors: DT_EINVAL (NULL h, a field out of range). */
+dt_status dt_set_schedule(dt_handle* h, const dt_schedule* s);
+
+/* For tests of the failure path: enqueue on `stream` a write of `code` (> 0)
+ * into the handle's device error word, as a builder wait that ran out would.
+ * Every wait of the next build then gives up at its next periodic check of
+ * the word instead of waiting for its bound, so the build ends promptly, and
+ * the error is reported as any device failure (see Errors above).
+ * Errors: DT_EINVAL (NULL h, code <= 0), DT_EHIP. */
+dt_status dt_set_device_error(dt_handle* h, int32_t code, void* stream);
 
 /* Mean durations, in milliseconds, of the phases of the builds made with
  * DT_TIMING since the previous call (at most the last 256 of them), measured

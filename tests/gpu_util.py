@@ -45,8 +45,10 @@ def oracle_trees(spec, w, req, requests=None, base=None):
     return ref.build_all(spec, w, req, requests_subset=requests, base=base)
 
 
-def compare(spec, w, req, got, requests=None, base=None, tol=None):
-    """certify.compare for each listed request; returns the reports."""
+def compare(spec, w, req, got, requests=None, base=None, tol=None, logits_computed=False):
+    """certify.compare for each listed request; returns the reports.
+
+    Also checks the padding past each request's n_nodes."""
     bf16 = spec.wdtype == "bf16"
     tol = tol if tol is not None else (TOL_BF16 if bf16 else TOL_F32)
     head = ref.make_head(w, bf16, spec.act_bf16)
@@ -58,8 +60,29 @@ def compare(spec, w, req, got, requests=None, base=None, tol=None):
         other = {k: got[k][b] for k in ("tokens", "parents", "depths", "scores")}
         other["n_nodes"] = int(got["n_nodes"][b])
         reps.append(certify.compare(ot, head, hid, req["root"][b], other, spec.k, spec.T,
-                                    spec.norm, spec.N, tol))
+                                    spec.norm, spec.N, tol, logits_computed=logits_computed))
+    check_padding(got, spec.N)
     return reps, trees
+
+
+def check_padding(got, N):
+    """Slots past n_nodes: token -1, parent -1, depth -1, score -inf."""
+    for b in range(got["n_nodes"].shape[0]):
+        n = int(got["n_nodes"][b])
+        assert 0 <= n <= N, (b, n)
+        for key, pad in (("tokens", -1), ("parents", -1), ("depths", -1)):
+            assert np.all(got[key][b, n + 1:N + 1] == pad), (b, key)
+        assert np.all(np.isneginf(got["scores"][b, n + 1:N + 1])), (b, "scores")
+
+
+def assert_parity(reps, ids=None):
+    """Every tree passes the certificate and is exact unless the oracle itself
+    met a decision within the tolerance (then only a difference excused by a
+    near tie at the decision that produced it is allowed)."""
+    ids = list(range(len(reps))) if ids is None else list(ids)
+    for b, r in zip(ids, reps):
+        assert r.ok, (b, r)
+        assert r.exact or not r.must_be_exact, (b, r)
 
 
 def check_candidates(spec, trees, got, requests, exact=True):
@@ -77,4 +100,11 @@ def summarize(reps):
     n_exact = sum(r.exact for r in reps)
     ties = [r.near_tie for r in reps if not r.exact]
     worst = max((r.max_dscore for r in reps), default=0.0)
-    return f"{n_exact}/{len(reps)} exact, near-ties {ties}, max|dscore| {worst:.3e}"
+    must = sum(r.must_be_exact for r in reps)
+    cen = {}
+    for r in reps:
+        for key, v in r.census.items():
+            cen[key] = cen.get(key, 0) + v
+    return (f"{n_exact}/{len(reps)} exact, near-ties {ties}, max|dscore| {worst:.3e}; "
+            f"census: {must}/{len(reps)} trees with no oracle decision within tol, "
+            f"decisions within tol {cen}")

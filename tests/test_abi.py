@@ -120,3 +120,98 @@ def test_chain_null_arguments_are_einval(lib):
 def test_fold_null_arguments_are_einval(lib):
     assert lib.dt_fold_state(None, 1, 1, None, None, None, 0, None) == binding.DT_EINVAL
     assert "required" in pkg.dt_last_error()
+
+
+def test_schedule_and_error_hook_null_arguments(lib):
+    s = binding.Schedule(0, 0, 0, 0)
+    assert lib.dt_set_schedule(None, ctypes.byref(s)) == binding.DT_EINVAL
+    assert lib.dt_set_device_error(None, 1, None) == binding.DT_EINVAL
+    assert "NULL" in pkg.dt_last_error()
+
+
+# ----------------------------------------------------------------------------
+# the torch layer refuses tensors the library would misread, before any
+# pointer reaches the C ABI (checked here with host tensors: dtype and shape
+# are checked before the device)
+
+torch = pytest.importorskip("torch")
+
+V, D, H, E, DS, R, BMAX = 64, 3, 16, 8, 4, 8, 4
+
+
+def _weights(dtype=torch.float32, **over):
+    w = {"emb": torch.zeros(V, E), "w_ih": torch.zeros(3 * DS, E), "w_hh": torch.zeros(3 * DS, DS),
+         "w1": torch.zeros(H + DS, R), "w2": torch.zeros(R, V)}
+    w = {k: v.to(dtype) for k, v in w.items()}
+    w.update(over)
+    return w
+
+
+def _builder_kwargs():
+    return dict(vocab=V, depths=D, hidden=H, emb_dim=E, state_dim=DS, rank=R, max_batch=BMAX,
+                max_top_m=4, max_top_k=2, max_budget=8)
+
+
+@pytest.mark.parametrize("over,msg", [
+    ({"w2": torch.zeros(R, V + 1)}, "shape"),
+    ({"w_hh": torch.zeros(3 * DS, DS, dtype=torch.bfloat16)}, "float32"),
+    ({"b_ih": torch.zeros(3 * DS, dtype=torch.bfloat16)}, "float32"),
+    ({"b_hh": torch.zeros(3 * DS + 1)}, "shape"),
+    ({"w_lm": torch.zeros(H, V - 1)}, "shape"),
+    ({"w1": torch.zeros(R, H + DS).t()}, "contiguous"),
+    ({}, "device"),
+])
+def test_builder_refuses_bad_weights(over, msg):
+    with pytest.raises(ValueError, match=msg):
+        binding.TreeBuilder(_weights(**over), **_builder_kwargs())
+
+
+def _unbound_builder():
+    # the argument checks of a builder, without a handle
+    tb = object.__new__(binding.TreeBuilder)
+    tb.torch = torch
+    tb.dims = binding.Dims(V, D, H, E, DS, R, BMAX, binding.DT_F32)
+    tb.tdtype = torch.float32
+    tb.wdtype = binding.DT_F32
+    tb.device = torch.device("cpu")
+    return tb
+
+
+@pytest.mark.parametrize("hidden,base,root,msg", [
+    (torch.zeros(2, D, H), torch.zeros(2, D, V, dtype=torch.bfloat16), None, "float32"),
+    (torch.zeros(2, D, H), torch.zeros(2, D, V - 1), None, "shape"),
+    (torch.zeros(2, D + 1, H), None, None, "shape"),
+    (torch.zeros(2, D, H, dtype=torch.bfloat16), None, None, "float32"),
+    (torch.zeros(2, D, H), None, torch.zeros(3, DS), "shape"),
+    (torch.zeros(BMAX + 1, D, H), None, None, "batch"),
+    (torch.zeros(2, H), None, None, "hidden"),
+    (torch.zeros(2, D, H), torch.zeros(2, D, V), None, "device"),
+])
+def test_build_refuses_bad_inputs(hidden, base, root, msg):
+    tb = _unbound_builder()
+    with pytest.raises(ValueError, match=msg):
+        tb.build(hidden, base, root, top_m=4, top_k=2, budget=8)
+    with pytest.raises(ValueError, match=msg):
+        tb.chain(hidden, base, root)
+
+
+def test_output_refusal():
+    # budget 8 needs 9 columns per request
+    with pytest.raises(ValueError, match="output tokens"):
+        binding._check_tensor("output tokens", torch.zeros(2, 8, dtype=torch.int32), torch.int32, (2, 9))
+
+
+def test_fold_refuses_bad_tokens():
+    tb = _unbound_builder()
+    with pytest.raises(ValueError, match="int32"):
+        tb.fold_state(torch.zeros(2, 5, dtype=torch.int64))
+    with pytest.raises(ValueError, match="shape"):
+        tb.fold_state(torch.zeros(2, 5, dtype=torch.int32), torch.zeros(2, DS + 1))
+
+
+def test_tree_attention_refuses_bad_shapes():
+    p = torch.zeros(2, 9, dtype=torch.int32)
+    with pytest.raises(ValueError, match="shape"):
+        pkg.tree_attention_inputs(p, torch.zeros(2, 8, dtype=torch.int32), torch.zeros(2, dtype=torch.int32))
+    with pytest.raises(ValueError, match="int32"):
+        pkg.tree_attention_inputs(p, p, torch.zeros(2, dtype=torch.int64))

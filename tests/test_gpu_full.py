@@ -60,8 +60,7 @@ def _full_case(spec, w, req, tb, sample):
     reps, trees = gu.compare(spec, w, req, got, requests=sample)
     gu.check_candidates(spec, trees, got, sample)
     print(spec.name, gu.summarize(reps))
-    for b, r in zip(sample, reps):
-        assert r.ok, (b, r)
+    gu.assert_parity(reps, sample)
     return got, reps
 
 
@@ -83,20 +82,26 @@ def test_q8b_b32(dev, q8b_builder):
     _full_case(spec, w, req, q8b_builder, list(range(spec.B)))
 
 
-def test_q8b_b32_one_half(dev, q8b_builder, monkeypatch):
+def test_q8b_b32_one_half(dev, q8b_builder):
     # the register workers serving the whole batch at each step (the default
     # at 32 requests serves it in two halves)
-    monkeypatch.setenv("DT_HALVES", "1")
-    spec, w, req = synth.workload("q8b_b32")
-    _full_case(spec, w, req, q8b_builder, [0, 17, 31])
+    q8b_builder.set_schedule(halves=1)
+    try:
+        spec, w, req = synth.workload("q8b_b32")
+        _full_case(spec, w, req, q8b_builder, [0, 17, 31])
+    finally:
+        q8b_builder.set_schedule()
 
 
-def test_q8b_b32_lds_workers(dev, q8b_builder, monkeypatch):
+def test_q8b_b32_lds_workers(dev, q8b_builder):
     # the workers that stage operands in LDS (the schedule for d_s other than
     # 1024) at the full shape, on the same handle
-    monkeypatch.setenv("DT_WORKERS", "lds")
-    spec, w, req = synth.workload("q8b_b32")
-    _full_case(spec, w, req, q8b_builder, [0, 31])
+    q8b_builder.set_schedule(lds_workers=1)
+    try:
+        spec, w, req = synth.workload("q8b_b32")
+        _full_case(spec, w, req, q8b_builder, [0, 31])
+    finally:
+        q8b_builder.set_schedule()
 
 
 def test_q8b_b32_fullv_and_smaller_batch_reuse_handle(dev, q8b_builder):
@@ -140,8 +145,7 @@ def test_q8b_b32_marginal(dev, q8b_builder):
     w0["w2"] = np.zeros_like(w["w2"])
     reps, _ = gu.compare(spec, w0, req, got, requests=[0, 13, 31])
     print(spec.name, "marginal", gu.summarize(reps))
-    for b, r in zip([0, 13, 31], reps):
-        assert r.ok, (b, r)
+    gu.assert_parity(reps, [0, 13, 31])
 
 
 def test_q8b_b32_repeated_builds_bitwise(dev, q8b_builder):

@@ -19,8 +19,7 @@ def dev():
 
 
 def _assert_ok(reps):
-    for i, r in enumerate(reps):
-        assert r.ok, (i, r)
+    gu.assert_parity(reps)
 
 
 def test_tiny_workload(dev):
@@ -164,17 +163,16 @@ def test_marginal_flag_is_the_zero_correction_tree(dev, name):
 
 
 @pytest.mark.parametrize("B,root", [(2, True), (3, False), (5, True)])
-def test_bf16_register_workers_two_halves(dev, monkeypatch, B, root):
+def test_bf16_register_workers_two_halves(dev, B, root):
     # the register workers serve the first ceil(B/2) requests of a step, then
     # the rest (16 nodes per request per step, so the first half fills whole
     # 16-column blocks); uneven halves, given and zero root states
-    monkeypatch.setenv("DT_HALVES", "2")
-    monkeypatch.setenv("DT_POPS", "16")
     spec = synth.small(f"halves_b{B}", V=3000, D=7, h=64, e=96, ds=1024, r=64, M=16, k=4, N=80, B=B,
                        wdtype="bf16", group=1200 + B, emb_std=0.5, biases=True,
                        root_std=0.7 if root else 0.0)
     spec, w, req = synth.workload(spec)
     tb = gu.make_builder(spec, w)
+    tb.set_schedule(halves=2, pops=16)
     got = gu.run(tb, spec, req)
     reps, trees = gu.compare(spec, w, req, got)
     print(gu.summarize(reps))
@@ -183,19 +181,18 @@ def test_bf16_register_workers_two_halves(dev, monkeypatch, B, root):
     tb.close()
 
 
-def test_halves_alternate_on_one_handle(dev, monkeypatch):
+def test_halves_alternate_on_one_handle(dev):
     # group flags carry 2 epoch + half in every launch, so a one-half build
     # after a two-half build (and back) waits for its own flags; each column's
     # product and state update do not depend on the split, so the trees are
     # bitwise the same
-    monkeypatch.setenv("DT_POPS", "16")
     spec = synth.small("halves_alt", V=3000, D=7, h=64, e=96, ds=1024, r=64, M=16, k=4, N=80, B=4,
                        wdtype="bf16", group=1290, emb_std=0.5, biases=True, root_std=0.7)
     spec, w, req = synth.workload(spec)
     tb = gu.make_builder(spec, w)
     outs = []
-    for hv in ("2", "1", "2", "1"):
-        monkeypatch.setenv("DT_HALVES", hv)
+    for hv in (2, 1, 2, 1):
+        tb.set_schedule(halves=hv, pops=16)
         outs.append(gu.run(tb, spec, req))
     reps, _ = gu.compare(spec, w, req, outs[0])
     print(gu.summarize(reps))
