@@ -74,7 +74,7 @@ class VerifyOutputs(C.Structure):
 
 EXPORTS = ["dt_create", "dt_build_trees", "dt_sync_status", "dt_phase_times", "dt_destroy",
            "dt_last_error", "dt_version", "dt_tree_attention_inputs", "dt_draft_chain", "dt_fold_state",
-           "dt_set_schedule", "dt_set_device_error"]
+           "dt_set_schedule", "dt_set_device_error", "dt_draft_chain_noalloc"]
 _lib = None
 
 
@@ -111,6 +111,9 @@ def load_library():
     lib.dt_draft_chain.restype = C.c_int
     lib.dt_draft_chain.argtypes = [C.c_void_p, C.POINTER(Inputs), C.c_uint32, C.c_void_p, C.c_void_p,
                                    C.c_void_p]
+    lib.dt_draft_chain_noalloc.restype = C.c_int
+    lib.dt_draft_chain_noalloc.argtypes = [C.c_void_p, C.POINTER(Inputs), C.c_uint32, C.c_void_p, C.c_void_p,
+                                           C.c_void_p]
     lib.dt_fold_state.restype = C.c_int
     lib.dt_fold_state.argtypes = [C.c_void_p, C.c_int32, C.c_int32, C.c_void_p, C.c_void_p, C.c_void_p,
                                   C.c_uint32, C.c_void_p]
@@ -171,6 +174,11 @@ def dt_destroy(handle: int):
 def dt_draft_chain(handle: int, inputs: Inputs, flags: int, tokens: int, logits, stream: int = 0):
     _check(load_library().dt_draft_chain(C.c_void_p(handle), C.byref(inputs), C.c_uint32(flags),
                                          C.c_void_p(tokens), C.c_void_p(logits), C.c_void_p(stream)))
+
+
+def dt_draft_chain_noalloc(handle: int, inputs: Inputs, flags: int, tokens: int, logits, stream: int = 0):
+    _check(load_library().dt_draft_chain_noalloc(C.c_void_p(handle), C.byref(inputs), C.c_uint32(flags),
+                                                 C.c_void_p(tokens), C.c_void_p(logits), C.c_void_p(stream)))
 
 
 def dt_fold_state(handle: int, batch: int, n_tokens: int, tokens: int, prev_state, state_out: int,

@@ -7,6 +7,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <string>
 
 #include "../../include/dominotree.h"
@@ -33,6 +34,38 @@ dt_status fail(dt_status s, const char* fmt, ...) {
   } while (0)
 
 inline int round_up(int x, int m) { return (x + m - 1) / m * m; }
+
+}  // namespace
+
+// Workspace of dt_draft_chain_noalloc: a file-scope device array, one copy per
+// GPU, held until the process ends.  Host code uses only the address that
+// hipGetSymbolAddress returns for the current device (scratch_setup), never
+// the array's name, which on the host is a stand-in and not a device address.
+static __device__ __align__(256) unsigned char scratch[DT_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int MAX_DEVICES = 64;
+std::mutex g_scratch_mu;
+unsigned char* g_scratch[MAX_DEVICES] = {};
+
+// Take the array's address on `device`, which must be current; once per device.
+dt_status scratch_setup(int device) {
+  if (device < 0 || device >= MAX_DEVICES) return fail(DT_EUNSUPPORTED, "device %d >= %d", device, MAX_DEVICES);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch[device]) return DT_OK;
+  void* p = nullptr;
+  const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+  if (e != hipSuccess || !p) return fail(DT_EHIP, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+  g_scratch[device] = static_cast<unsigned char*>(p);
+  return DT_OK;
+}
+
+unsigned char* scratch_of(int device) {
+  if (device < 0 || device >= MAX_DEVICES) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  return g_scratch[device];
+}
 
 }  // namespace
 
@@ -199,6 +232,10 @@ dt_status dt_create(dt_handle** out, const dt_dims* dims, const dt_weights* w, c
   if (hipGetDeviceProperties(&prop, h->device) != hipSuccess) return bail(fail(DT_EHIP, "no device properties"));
   h->n_cu = prop.multiProcessorCount;
   if (!prop.cooperativeLaunch) return bail(fail(DT_EUNSUPPORTED, "device lacks cooperative launch"));
+  {
+    const dt_status st = scratch_setup(h->device);  // the allocation-free entry point's workspace
+    if (st != DT_OK) return bail(st);
+  }
 
   const int V = dims->vocab, D = dims->depths, hd = dims->hidden, e = dims->emb_dim, ds = dims->state_dim,
             r = dims->rank, Bm = dims->max_batch;
@@ -522,8 +559,11 @@ dt_status dt_destroy(dt_handle* h) {
   return DT_OK;
 }
 
-dt_status dt_draft_chain(dt_handle* h, const dt_inputs* in, uint32_t flags, int32_t* tokens, float* logits,
-                         void* stream_) {
+}  // extern "C"
+
+namespace {
+
+dt_status chain_check(const dt_handle* h, const dt_inputs* in, uint32_t flags, const int32_t* tokens) {
   if (!h || !in || !tokens) return fail(DT_EINVAL, "h, in and tokens are required");
   const dt_dims& d = h->dims;
   if (in->batch < 1 || in->batch > d.max_batch)
@@ -536,27 +576,26 @@ dt_status dt_draft_chain(dt_handle* h, const dt_inputs* in, uint32_t flags, int3
   if (!h->bf16 && (flags & DT_ACT_BF16)) return fail(DT_EUNSUPPORTED, "DT_ACT_BF16 needs bf16 weights");
   if (d.rank > dt::CHAIN_MAX_RANK || d.rank % 8)
     return fail(DT_EUNSUPPORTED, "the chain head needs rank <= %d and a multiple of 8", dt::CHAIN_MAX_RANK);
-  hipStream_t stream = reinterpret_cast<hipStream_t>(stream_);
-  const int B = in->batch, D = d.depths, V = d.vocab, rows = B * D;
+  return DT_OK;
+}
+
+// The chain head on a given workspace (P [B D, r], gu [B, 3 ds + r], s [B, ds],
+// s_op [B, ds], part [B, chain blocks]): P = H W1_H, then the positions.
+dt_status chain_run(const dt_handle* h, const dt_inputs* in, const float* base, int32_t* tokens, float* logits,
+                    float* P, float* gu, float* s, void* s_op, uint64_t* part, hipStream_t stream) {
+  const dt_dims& d = h->dims;
+  const int rows = in->batch * d.depths;
   // P = H W1_H for every position (the path-independent half of W1 [H_d; S])
   if (h->bf16)
-    HIPCHK(dt::launch_gemm_bf16((const uint16_t*)in->hidden, nullptr, (const uint16_t*)h->w1h_t, nullptr, h->P,
-                                rows, d.rank, d.hidden, d.rank, stream));
+    HIPCHK(dt::launch_gemm_bf16((const uint16_t*)in->hidden, nullptr, (const uint16_t*)h->w1h_t, nullptr, P, rows,
+                                d.rank, d.hidden, d.rank, stream));
   else
-    HIPCHK(dt::launch_gemm_f32((const float*)in->hidden, nullptr, (const float*)h->w1h_t, nullptr, h->P, rows,
-                               d.rank, d.hidden, d.rank, stream));
-  if (!in->base_logits) {
-    if (h->wlm_tiled)
-      HIPCHK(dt::launch_gemm_bf16_btiled((const uint16_t*)in->hidden, (const uint16_t*)h->wlm_t, h->logits, rows, V,
-                                         d.hidden, V, h->a_tiles, stream));
-    else
-      HIPCHK(dt::launch_gemm_bf16((const uint16_t*)in->hidden, nullptr, (const uint16_t*)h->wlm_t, nullptr,
-                                  h->logits, rows, V, d.hidden, V, stream));
-  }
+    HIPCHK(dt::launch_gemm_f32((const float*)in->hidden, nullptr, (const float*)h->w1h_t, nullptr, P, rows, d.rank,
+                               d.hidden, d.rank, stream));
   dt::ChainArgs c{};
-  c.B = B;
-  c.D = D;
-  c.V = V;
+  c.B = in->batch;
+  c.D = d.depths;
+  c.V = d.vocab;
   c.ds = d.state_dim;
   c.r = d.rank;
   c.bf16 = h->bf16;
@@ -565,17 +604,71 @@ dt_status dt_draft_chain(dt_handle* h, const dt_inputs* in, uint32_t flags, int3
   c.wc = h->wc_rm;
   c.G = h->G;
   c.b_hh = h->b_hh;
-  c.base = in->base_logits ? in->base_logits : h->logits;
-  c.P = h->P;
+  c.base = base;
+  c.P = P;
   c.root = in->root_state;
-  c.gu = h->chain_gu;
-  c.s = h->chain_s;
-  c.s_op = h->chain_sop;
-  c.part = h->chain_part;
+  c.gu = gu;
+  c.s = s;
+  c.s_op = s_op;
+  c.part = part;
   c.tokens = tokens;
   c.logits = logits;
   HIPCHK(dt::launch_chain(c, stream));
   return DT_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+dt_status dt_draft_chain(dt_handle* h, const dt_inputs* in, uint32_t flags, int32_t* tokens, float* logits,
+                         void* stream_) {
+  dt_status st = chain_check(h, in, flags, tokens);
+  if (st != DT_OK) return st;
+  const dt_dims& d = h->dims;
+  hipStream_t stream = reinterpret_cast<hipStream_t>(stream_);
+  const int V = d.vocab, rows = in->batch * d.depths;
+  if (!in->base_logits) {
+    if (h->wlm_tiled)
+      HIPCHK(dt::launch_gemm_bf16_btiled((const uint16_t*)in->hidden, (const uint16_t*)h->wlm_t, h->logits, rows, V,
+                                         d.hidden, V, h->a_tiles, stream));
+    else
+      HIPCHK(dt::launch_gemm_bf16((const uint16_t*)in->hidden, nullptr, (const uint16_t*)h->wlm_t, nullptr,
+                                  h->logits, rows, V, d.hidden, V, stream));
+  }
+  return chain_run(h, in, in->base_logits ? in->base_logits : h->logits, tokens, logits, h->P, h->chain_gu,
+                   h->chain_s, h->chain_sop, h->chain_part, stream);
+}
+
+dt_status dt_draft_chain_noalloc(dt_handle* h, const dt_inputs* in, uint32_t flags, int32_t* tokens, float* logits,
+                                 void* stream_) {
+  dt_status st = chain_check(h, in, flags, tokens);
+  if (st != DT_OK) return st;
+  if (!in->base_logits)
+    return fail(DT_EINVAL, "dt_draft_chain_noalloc needs base logits (the LM head's logits do not fit its scratch)");
+  const dt_dims& d = h->dims;
+  const int B = in->batch;
+  // the workspace, carved from the device's scratch array in 256-byte pieces
+  const size_t a = 256;
+  auto piece = [a](size_t bytes) { return (bytes + a - 1) / a * a; };
+  const size_t p_bytes = piece((size_t)B * d.depths * d.rank * sizeof(float));
+  const size_t gu_bytes = piece((size_t)B * (3 * d.state_dim + d.rank) * sizeof(float));
+  const size_t s_bytes = piece((size_t)B * d.state_dim * sizeof(float));
+  const size_t sop_bytes = piece((size_t)B * d.state_dim * h->esz);
+  const size_t part_bytes =
+      piece((size_t)B * std::max(dt::chain_blocks(d.vocab), dt::chain_mfma_blocks(d.vocab)) * sizeof(uint64_t));
+  const size_t total = p_bytes + gu_bytes + s_bytes + sop_bytes + part_bytes;
+  if (total > DT_NOALLOC_SCRATCH_BYTES)
+    return fail(DT_EUNSUPPORTED, "batch %d needs %zu bytes of scratch, more than the %u the library holds", B, total,
+                (unsigned)DT_NOALLOC_SCRATCH_BYTES);
+  unsigned char* base = scratch_of(h->device);
+  if (!base) return fail(DT_EHIP, "no scratch address for device %d", h->device);
+  float* P = reinterpret_cast<float*>(base);
+  float* gu = reinterpret_cast<float*>(base + p_bytes);
+  float* s = reinterpret_cast<float*>(base + p_bytes + gu_bytes);
+  void* s_op = base + p_bytes + gu_bytes + s_bytes;
+  uint64_t* part = reinterpret_cast<uint64_t*>(base + p_bytes + gu_bytes + s_bytes + sop_bytes);
+  return chain_run(h, in, in->base_logits, tokens, logits, P, gu, s, s_op, part, reinterpret_cast<hipStream_t>(stream_));
 }
 
 dt_status dt_fold_state(dt_handle* h, int32_t batch, int32_t n_tokens, const int32_t* tokens,

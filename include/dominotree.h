@@ -255,6 +255,27 @@ dt_status dt_phase_times(dt_handle* h, float* ms, int n, int32_t* count);
 dt_status dt_draft_chain(dt_handle* h, const dt_inputs* in, uint32_t flags, int32_t* tokens, float* logits,
                          void* stream);
 
+/* ---- Allocation-free chain head ------------------------------------------
+ * For callers that cannot allocate device memory during a call: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Computes exactly what dt_draft_chain computes, with the same arguments,
+ * results and errors, but its per-call workspace (P = H W1_H for every
+ * position, the per-position products [W_hh S | W1_S^T S], the state and its
+ * operand copy, the block-wise best candidates) lives in a fixed device array
+ * of DT_NOALLOC_SCRATCH_BYTES that the library holds on each GPU until the
+ * process ends (its address is taken when the first handle is created on
+ * that GPU), instead of in the handle's workspace.  It calls no allocating
+ * routine.  Differences: in->base_logits is required (NULL gives DT_EINVAL:
+ * the LM head's logits do not fit the array), and a batch whose workspace
+ * exceeds the array gives DT_EUNSUPPORTED (the Qwen3-8B shape, d_s 1024,
+ * r 256, 15 positions, uses about 1.4 MB at batch 32).  Nothing in the array
+ * needs clearing: every value is written before it is read.  Every call on a
+ * GPU shares that GPU's array, whatever the handle, stream or thread: calls
+ * that overlap on one GPU race, so the caller serialises them. */
+#define DT_NOALLOC_SCRATCH_BYTES (4u << 20)
+dt_status dt_draft_chain_noalloc(dt_handle* h, const dt_inputs* in, uint32_t flags, int32_t* tokens,
+                                 float* logits, void* stream);
+
 /* ---- Folding committed tokens into the causal state ------------------------
  * The causal state before a draft block is the GRU over the tokens committed
  * so far [Domino, Method: S_{i-1} = GRU(embeddings of the tokens before i)].
