@@ -53,7 +53,8 @@ class Inputs(C.Structure):
 class Outputs(C.Structure):
     _fields_ = [("tokens", C.c_void_p), ("parents", C.c_void_p), ("depths", C.c_void_p),
                 ("scores", C.c_void_p), ("n_nodes", C.c_void_p), ("cand_ids", C.c_void_p),
-                ("cand_logits", C.c_void_p), ("lse", C.c_void_p)]
+                ("cand_logits", C.c_void_p), ("lse", C.c_void_p), ("stats", C.c_void_p),
+                ("logits", C.c_void_p)]
 
 
 class Schedule(C.Structure):
@@ -282,7 +283,8 @@ class TreeBuilder:
         except Exception:
             pass
 
-    def outputs(self, batch: int, top_m: int, budget: int, candidates: bool = False) -> dict:
+    def outputs(self, batch: int, top_m: int, budget: int, candidates: bool = False,
+                stats: bool = False, logits: bool = False) -> dict:
         torch = self.torch
         dev = self.device
         o = {
@@ -297,6 +299,10 @@ class TreeBuilder:
             o["cand_ids"] = torch.empty((batch, D, top_m), dtype=torch.int32, device=dev)
             o["cand_logits"] = torch.empty((batch, D, top_m), dtype=torch.float32, device=dev)
             o["lse"] = torch.empty((batch, D), dtype=torch.float32, device=dev)
+        if stats:
+            o["stats"] = torch.empty((batch, 2), dtype=torch.int32, device=dev)
+        if logits:
+            o["logits"] = torch.empty((batch, self.dims.depths, self.dims.vocab), dtype=torch.float32, device=dev)
         return o
 
     def _check_inputs(self, hidden, base_logits, root_state):
@@ -333,11 +339,14 @@ class TreeBuilder:
         _check_tensor("output cand_logits", o.get("cand_logits"), torch.float32, (batch, D, top_m),
                       self.device, optional=True)
         _check_tensor("output lse", o.get("lse"), torch.float32, (batch, D), self.device, optional=True)
+        _check_tensor("output stats", o.get("stats"), torch.int32, (batch, 2), self.device, optional=True)
+        _check_tensor("output logits", o.get("logits"), torch.float32, (batch, D, self.dims.vocab), self.device,
+                      optional=True)
         inp = Inputs(batch, _ptr(base_logits), _ptr(hidden), _ptr(root_state))
         prm = Params(top_m, top_k, budget, float(temperature), norm, flags)
         outs = Outputs(_ptr(o["tokens"]), _ptr(o["parents"]), _ptr(o["depths"]), _ptr(o["scores"]),
                        _ptr(o["n_nodes"]), _ptr(o.get("cand_ids")), _ptr(o.get("cand_logits")),
-                       _ptr(o.get("lse")))
+                       _ptr(o.get("lse")), _ptr(o.get("stats")), _ptr(o.get("logits")))
         dt_build_trees(self.handle, inp, prm, outs, self.stream.cuda_stream)
         return o
 

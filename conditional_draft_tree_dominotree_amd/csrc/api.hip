@@ -402,18 +402,20 @@ dt_status dt_build_trees(dt_handle* h, const dt_inputs* in, const dt_params* p, 
                                d.rank, d.hidden, d.rank, ps));
   if (!p_inline) HIPCHK(hipEventRecord(h->join_ev, h->side));
   // a0 (LM head, when no base logits are given), then a1: candidates and LSE
+  // the LM head's logits go to the caller's copy when one is asked for
+  float* lm_logits = out->logits ? out->logits : h->logits;
   if (!in->base_logits) {
     // L_base = H W_lm (Domino summary, 方法步骤详情), fp32 accumulate
     if (h->wlm_tiled)
-      HIPCHK(dt::launch_gemm_bf16_btiled((const uint16_t*)in->hidden, (const uint16_t*)h->wlm_t, h->logits, rows, V,
+      HIPCHK(dt::launch_gemm_bf16_btiled((const uint16_t*)in->hidden, (const uint16_t*)h->wlm_t, lm_logits, rows, V,
                                          d.hidden, V, h->a_tiles, stream));
     else
       HIPCHK(dt::launch_gemm_bf16((const uint16_t*)in->hidden, nullptr, (const uint16_t*)h->wlm_t, nullptr,
-                                  h->logits, rows, V, d.hidden, V, stream));
+                                  lm_logits, rows, V, d.hidden, V, stream));
   }
   MARK(1);
   {
-    const float* logits = in->base_logits ? in->base_logits : h->logits;
+    const float* logits = in->base_logits ? in->base_logits : lm_logits;
     HIPCHK(dt::launch_topm(logits, rows, V, M, p->temperature, h->chunk_cand, h->chunk_stat, h->cand_ids,
                            h->cand_vals, h->lse, h->tail, h->tokrank, out->cand_ids, out->cand_logits, out->lse,
                            stream));
@@ -466,6 +468,7 @@ dt_status dt_build_trees(dt_handle* h, const dt_inputs* in, const dt_params* p, 
   a.depths = out->depths;
   a.scores = out->scores;
   a.n_nodes = out->n_nodes;
+  a.stats = out->stats;
   a.spin_limit = 1u << 21;
   const size_t lds = dt::plan_tree(a, h->bf16, h->sched.pops, std::min(h->n_cu - B, h->max_workers),
                                    h->sched.lds_workers, h->sched.halves);

@@ -59,6 +59,7 @@ struct TreeArgs {
   // outputs
   int32_t *tokens, *parents, *depths, *n_nodes;
   float* scores;
+  int32_t* stats;          // [B, 2] or NULL: steps of the request's loop, nodes it expanded
   unsigned spin_limit;
   uint32_t ebase;          // epochs of this launch: ebase + 1 .. ebase + tree_epoch_span(N) - 1
 };

@@ -1875,8 +1875,11 @@ __device__ __forceinline__ void controller_main(const TreeArgs& a, unsigned char
   if (tid == 0) st_dev_u32(a.ready + b, a.ebase + 1);  // start-up loads done: workers may load weights
 
   bool failed = false;
+  int steps = 0, expanded = 0;
   for (int t = 0;; ++t) {
     const int e = c.f->misc[C_E];
+    steps = t + 1;
+    expanded += e;
     const uint32_t epoch = a.ebase + (uint32_t)t + 1u;
     if (tid < 64) {
       const bool ok = (t == 0 && !a.root) ||  // zero roots: step 0's products are set up above
@@ -1923,6 +1926,10 @@ __device__ __forceinline__ void controller_main(const TreeArgs& a, unsigned char
     st_dev_u32(a.mbox_w + (size_t)w * 32 + b, mbox_word(a.ebase + tree_epoch_span(a.N) - 1, MBOX_DONE_E));
   stores_done();
   ctl_output(a, c, b, failed);
+  if (a.stats && tid == 0) {
+    a.stats[2 * b] = steps;
+    a.stats[2 * b + 1] = expanded;
+  }
   // a launch that ends with the error word set tells the host through the
   // mirror, which the next build call reads without a synchronisation
   if (tid == 0) {

@@ -142,7 +142,7 @@ typedef struct {
 /* Outputs (device pointers, caller-owned, sized for the batch and budget).
  * Node 0 is the root: token -1, parent -1, depth 0, score 0.  Nodes 1..n are
  * in pop order; slots past n_nodes hold token -1, parent -1, depth -1,
- * score -inf.  The three cand_* / lse pointers are optional (NULL to skip):
+ * score -inf.  The cand_* / lse / stats / logits pointers are optional (NULL to skip):
  * the per-depth candidates (sorted), their base logits and the LSE of base/T
  * over the whole vocabulary. */
 typedef struct {
@@ -154,6 +154,10 @@ typedef struct {
   int32_t* cand_ids; /* [b, D, M] or NULL */
   float* cand_logits;/* [b, D, M] or NULL */
   float* lse;        /* [b, D] or NULL */
+  int32_t* stats;    /* [b, 2] or NULL: per request, the steps of the builder's loop and the
+                        nodes it expanded (several nodes per step, speculative ones included) */
+  float* logits;     /* [b, D, V] or NULL: a copy of the base logits the LM head computed
+                        (written only when inputs.base_logits is NULL) */
 } dt_outputs;
 
 typedef struct dt_handle dt_handle;

@@ -15,8 +15,11 @@ oracle's tree for the same request.
                   difference;
   * near_tie   -- the decision that produced the first difference, when the
                   oracle had a competitor within `tol` there ("pop" or
-                  "topk"; "topm" only for base logits computed by an LM head,
-                  see `_tie_at`), else "";
+                  "topk", see `_tie_at`), else "";
+  * topm_swaps -- depths where the other builder's candidate set differs from
+                  the oracle's at a top-M boundary within `tol_logit` (only
+                  for logits computed by an LM head on both sides; the tree is
+                  then compared with the oracle's tree on the other's sets);
   * census     -- how many of the oracle's own decisions had a runner-up
                   within the tolerance (pops and top-k boundaries within
                   `tol`; with computed logits also top-M boundaries within
@@ -69,6 +72,7 @@ class Report:
     max_dscore: float             # over nodes matching the oracle's
     failures: list = field(default_factory=list)
     census: dict = field(default_factory=dict)
+    topm_swaps: int = 0           # depths compared on the other's candidate set
 
     @property
     def ok(self) -> bool:
@@ -216,21 +220,67 @@ def certify(head, deps, hidden, root, tokens, parents, depths, scores, n: int, k
     return _arithmetic(deps, tokens, parents, depths, scores, n, k, N, tol, sc, exps)
 
 
+def _same_set(a, b) -> bool:
+    """Equal candidate sets (the order inside a set only numbers the slots)."""
+    return np.array_equal(np.sort(np.asarray(a, dtype=np.int64)), np.sort(np.asarray(b, dtype=np.int64)))
+
+
+def other_depths(otree: ref.Tree, base_rows, cand_other, T: float) -> list:
+    """The oracle's per-depth candidate records, with the other builder's
+    candidate set wherever it differs from the oracle's (a top-M boundary
+    that the two sides' own logits settled differently).  Values are the
+    oracle's logits at the other's ids; lse, margin as the oracle's; tail
+    over the tokens outside the other's set."""
+    out = []
+    for d, dep in enumerate(otree.depths_info):
+        ids = np.asarray(cand_other[d], dtype=np.int64)
+        if _same_set(ids, dep.cand):
+            out.append(dep)
+            continue
+        row = np.asarray(base_rows[d], dtype=np.float64)
+        rest = np.ones(row.shape[0], bool)
+        rest[ids] = False
+        out.append(ref.Depth(cand=ids, base=row[ids].copy(), lse=dep.lse,
+                             tail=ref.logsumexp(row[rest] / T), margin=dep.margin))
+    return out
+
+
 def compare(otree: ref.Tree, head, hidden, root, other: dict, k: int, T: float,
             norm: str, N: int, tol: float, logits_computed: bool = False,
-            tol_logit: float = 1e-4) -> Report:
+            tol_logit: float = 1e-4, cand_other=None, base_rows=None) -> Report:
     """Compare another builder's tree with the oracle's (see module doc).
 
     `other` holds tokens, parents, depths, scores ([N + 1] each) and n_nodes.
     `logits_computed`: the base logits came from an LM head on both sides
-    (each with its own rounding), so the top-M boundaries can tie too.
+    (each with its own rounding), so the top-M boundaries can tie too; then
+    `cand_other` ([D, M], the other builder's candidates) and `base_rows`
+    ([D, V], the oracle's logits) are checked: a depth whose candidate set
+    differs from the oracle's must have had its boundary within `tol_logit`
+    ([topm] otherwise).  Each set is then a valid choice, and the tree that
+    follows from it is unique up to pop and top-k ties, so the oracle builds
+    its tree again on the other's sets (`topm_swaps` counts such depths) and
+    the comparison proceeds against that tree.
     """
     n_o = otree.n_nodes
     n_x = int(other["n_nodes"])
     tok, par, dep, scs = other["tokens"], other["parents"], other["depths"], other["scores"]
     deps = otree.depths_info
     cen = census(otree, tol, logits_computed, tol_logit)
-    fails = _structure(tok, par, dep, scs, n_x, len(deps), N)
+    fails = []
+    swaps = 0
+    if cand_other is not None:
+        for d, od in enumerate(deps):
+            if not _same_set(cand_other[d], od.cand):
+                swaps += 1
+                if not (logits_computed and od.margin < tol_logit):
+                    fails.append(f"[topm] depth {d + 1}: candidate set differs with no boundary "
+                                 f"within tol_logit")
+        if swaps and not fails:
+            deps = other_depths(otree, base_rows, cand_other, T)
+            otree = ref.build_tree(head, np.asarray(base_rows), hidden, root, len(deps[0].cand), k, N,
+                                   T, norm, deps=deps)
+            n_o = otree.n_nodes
+    fails += _structure(tok, par, dep, scs, n_x, len(deps), N)
     L = max(0, min(n_o, n_x))
     first = -1
     maxd = 0.0
@@ -247,19 +297,18 @@ def compare(otree: ref.Tree, head, hidden, root, other: dict, k: int, T: float,
         sc, exps, _ = evaluate(head, deps, hidden, root, tok, par, n_x, k, T, norm, N)
         fails = _arithmetic(deps, tok, par, dep, scs, n_x, k, N, tol, sc, exps)
         if not exact:
-            near = _tie_at(otree, tok, par, dep, n_x, first, sc, exps, tol, logits_computed,
-                           tol_logit)
+            near = _tie_at(otree, tok, par, dep, n_x, first, sc, exps, tol)
     if not exact and not near:
         fails.append(f"[mismatch] first difference at node {first} with no oracle decision "
                      f"within tol there")
     if maxd > tol:
         fails.append(f"[dscore] matched-node score difference {maxd!r} > tol")
     return Report(exact=exact, n_oracle=n_o, n_other=n_x, first_mismatch=first,
-                  near_tie=near, max_dscore=maxd, failures=fails, census=cen)
+                  near_tie=near, max_dscore=maxd, failures=fails, census=cen, topm_swaps=swaps)
 
 
 def _tie_at(otree: ref.Tree, tokens, parents, depths, n_x: int, first: int, sc: dict,
-            exps: dict, tol: float, logits_computed: bool, tol_logit: float) -> str:
+            exps: dict, tol: float) -> str:
     """The near tie that excuses the first difference, or "".
 
     Nodes 1..first-1 are the same in both trees, so both builders took the
@@ -274,10 +323,8 @@ def _tie_at(otree: ref.Tree, tokens, parents, depths, n_x: int, first: int, sc: 
                   margin there is below tol;
       * "topk" -- B is not one of them: B's parent (a node both trees share)
                   had a top-k boundary within tol, where the other builder
-                  kept B instead;
-      * "topm" -- only for computed logits: B's token is not among the
-                  oracle's candidates of its depth, and that depth's top-M
-                  boundary was within tol_logit.
+                  kept B instead.
+    (A top-M boundary is settled before the tree is built: see `compare`.)
     Differing node counts (one tree a prefix of the other) are never excused:
     the count depends on no floating-point decision.
     """
@@ -287,11 +334,7 @@ def _tie_at(otree: ref.Tree, tokens, parents, depths, n_x: int, first: int, sc: 
     pb, tb = int(parents[first]), int(tokens[first])
     db = int(depths[first])
     dep = otree.depths_info[db - 1]
-    if not np.any(dep.cand == tb):
-        if logits_computed and dep.margin < tol_logit:
-            return "topm"
-        return ""
-    if not abs(otree.scores[first] - sc[first]) < tol:
+    if not np.any(dep.cand == tb) or not abs(otree.scores[first] - sc[first]) < tol:
         return ""
     ex = exps.get(pb)
     if ex is None:

@@ -269,15 +269,19 @@ class Tree:
 
 
 def build_tree(head: Head, base: np.ndarray, hidden: np.ndarray, root: np.ndarray,
-               M: int, k: int, N: int, T: float, norm: str = "topm") -> Tree:
+               M: int, k: int, N: int, T: float, norm: str = "topm", deps=None) -> Tree:
     """Best-first conditional tree for one request [DominoTree, Core 1, 2, 4].
 
     base   [D, V] base logits (fp32 values)
     hidden [D, h] backbone hidden states H_1..H_D (float64 values)
     root   [ds]   the root GRU state
+    deps   per-depth candidate records to use instead of selecting them from
+           `base` (a candidate set that another implementation's own rounding
+           of computed logits settled differently at a near tie)
     """
     D = base.shape[0]
-    deps = [candidates(base[d], M, T) for d in range(D)]
+    if deps is None:
+        deps = [candidates(base[d], M, T) for d in range(D)]
     t = Tree(depths_info=deps)
     t.tokens.append(-1)
     t.parents.append(-1)

@@ -35,8 +35,9 @@ def run(tb, spec, req, base=None, candidates=True, flags=None):
         base = req["base"]
     root = to_dev(req["root"]) if spec.root_std > 0 else None
     norm = pkg.DT_NORM_FULLV if spec.norm == "fullv" else pkg.DT_NORM_TOPM
+    o = tb.outputs(hidden.shape[0], spec.M, spec.N, candidates=candidates, stats=True)
     out = tb.build(hidden, to_dev(base), root, top_m=spec.M, top_k=spec.k, budget=spec.N,
-                   temperature=spec.T, norm=norm, candidates=candidates, flags=flags)
+                   temperature=spec.T, norm=norm, flags=flags, out=o)
     tb.sync_status()
     return {k: v.cpu().numpy() for k, v in out.items()}
 
@@ -59,10 +60,28 @@ def compare(spec, w, req, got, requests=None, base=None, tol=None, logits_comput
         hid = ref.hidden_values(req["hidden"][b], bf16)
         other = {k: got[k][b] for k in ("tokens", "parents", "depths", "scores")}
         other["n_nodes"] = int(got["n_nodes"][b])
+        extra = {}
+        if logits_computed:   # the GPU's candidate sets, checked against the oracle's margins
+            extra = dict(cand_other=got["cand_ids"][b], base_rows=base[b])
         reps.append(certify.compare(ot, head, hid, req["root"][b], other, spec.k, spec.T,
-                                    spec.norm, spec.N, tol, logits_computed=logits_computed))
+                                    spec.norm, spec.N, tol, logits_computed=logits_computed, **extra))
     check_padding(got, spec.N)
+    if "stats" in got:
+        check_stats(got, spec)
     return reps, trees
+
+
+def check_stats(got, spec):
+    """The builder's per-request stats: at least one step, at most N + 1 (each
+    step takes one of the N best nodes), at most 16 expansions per step, and
+    every expandable node of the tree (the root, depth < D and index < N)
+    expanded."""
+    for b in range(got["n_nodes"].shape[0]):
+        steps, expanded = (int(x) for x in got["stats"][b])
+        n = int(got["n_nodes"][b])
+        need = sum(1 for i in range(n + 1) if got["depths"][b, i] < spec.D and i < spec.N)
+        assert 1 <= steps <= spec.N + 1, (b, steps)
+        assert need <= expanded <= 16 * steps, (b, expanded, need, steps)
 
 
 def check_padding(got, N):
@@ -105,6 +124,7 @@ def summarize(reps):
     for r in reps:
         for key, v in r.census.items():
             cen[key] = cen.get(key, 0) + v
-    return (f"{n_exact}/{len(reps)} exact, near-ties {ties}, max|dscore| {worst:.3e}; "
+    swaps = sum(r.topm_swaps for r in reps)
+    return (f"{n_exact}/{len(reps)} exact, near-ties {ties}, top-M swaps {swaps}, max|dscore| {worst:.3e}; "
             f"census: {must}/{len(reps)} trees with no oracle decision within tol, "
             f"decisions within tol {cen}")

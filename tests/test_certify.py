@@ -241,3 +241,56 @@ def test_length_difference_is_never_excused(case77):
     o = dict(_other(t), n_nodes=N - 1)
     rep = _cmp(case77, o, tol=10.0)
     assert rep.near_tie == "" and not rep.ok
+
+
+def test_topm_near_tie_with_computed_logits():
+    # two builders whose own logits settle a depth-1 top-M boundary (within
+    # 1e-5 in the oracle's logits) differently: the other tree holds the
+    # (M+1)-th token where the oracle holds the M-th, and everything that
+    # follows from its own correction.  Accepted only for computed logits and
+    # a boundary within tol_logit, by comparison with the oracle's tree on the
+    # other's candidate sets.
+    spec = synth.small("s_topm", V=8, D=3, M=3, k=3, N=10, T=1.0, group=1990, norm="topm", wdtype="f32",
+                       biases=True, root_std=0.5)
+    spec, w, req = synth.workload(spec)
+    head = ref.make_head(w, False, False)
+    hid = req["hidden"][0].astype(np.float64)
+    root = req["root"][0]
+    base = req["base"][0].copy()
+    order = ref.rank_desc(base[0], np.arange(8))
+    a, b = int(order[2]), int(order[3])               # the M-th and (M+1)-th of depth 1
+    base[0, b] = base[0, a] - np.float32(1e-5)
+    other_base = base.copy()
+    other_base[0, b] = base[0, a] + np.float32(1e-5)  # the other side's logits swap them
+    t = ref.build_tree(head, base, hid, root, 3, 3, 10, 1.0)
+    x = ref.build_tree(head, other_base, hid, root, 3, 3, 10, 1.0)
+    assert t.tokens != x.tokens
+    other = _other(x)
+    cand_x = np.array([d.cand for d in x.depths_info])
+
+    def cmp(**kw):
+        return certify.compare(t, head, hid, root, other, 3, 1.0, "topm", 10, 1e-3, **kw)
+
+    rep = cmp(logits_computed=True, tol_logit=1e-4, cand_other=cand_x, base_rows=base)
+    assert rep.ok and rep.exact and rep.topm_swaps == 1 and rep.max_dscore < 1e-3, rep
+    assert rep.census.get("topm") == 1
+    # a boundary farther than tol_logit does not excuse it
+    rep = cmp(logits_computed=True, tol_logit=1e-6, cand_other=cand_x, base_rows=base)
+    assert not rep.ok and "topm" in _codes(rep)
+    # nor do given logits, where the sets must be equal
+    rep = cmp(logits_computed=False, cand_other=cand_x, base_rows=base)
+    assert not rep.ok and "topm" in _codes(rep)
+    # and without the other's candidate sets the trees simply differ
+    rep = cmp(logits_computed=True, tol_logit=1e-4)
+    assert not rep.ok
+
+
+def test_candidate_order_inside_a_set_is_not_a_swap():
+    # the same candidate set listed in another order (two values inside the
+    # set within the other side's rounding) is no top-M difference at all
+    head, hid, root, t = _case(77)
+    cand_x = np.array([d.cand for d in t.depths_info])
+    cand_x[0, [0, 1]] = cand_x[0, [1, 0]]
+    rep = certify.compare(t, head, hid, root, _other(t), K, T, "topm", N, 1e-4, logits_computed=False,
+                          cand_other=cand_x, base_rows=np.zeros((4, 8)))
+    assert rep.ok and rep.exact and rep.topm_swaps == 0

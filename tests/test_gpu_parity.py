@@ -201,3 +201,58 @@ def test_halves_alternate_on_one_handle(dev):
         for key in ("tokens", "parents", "depths", "scores", "n_nodes"):
             np.testing.assert_array_equal(o[key], outs[0][key], err_msg=key)
     tb.close()
+
+
+def test_golden_tie_tree_through_the_gpu(dev):
+    # the hand-worked tie fixture: equal logits, W2 = 0, every candidate
+    # log-prob is -ln 2; pops tie on score and depth and are ordered by token,
+    # then by the parent's index
+    import json
+    import math
+    import os
+    fx = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "hand_tree_ties.json")))
+    V, D = fx["V"], fx["D"]
+    spec = synth.small("golden_ties", V=V, D=D, h=8, e=8, ds=4, r=4, M=fx["M"], k=fx["k"], N=fx["N"],
+                       T=fx["T"], group=1600, logits="zipf")    # the drawn logits are replaced below
+    spec, w, req = synth.workload(spec)
+    w = dict(w, w2=np.zeros_like(w["w2"]))
+    base = np.array(fx["logits"], np.float32)[None]
+    tb = gu.make_builder(spec, w)
+    got = gu.run(tb, spec, req, base=base)
+    tb.close()
+    ex = fx["expected"]
+    assert got["tokens"][0].tolist() == ex["tokens"]
+    assert got["parents"][0].tolist() == ex["parents"]
+    assert got["depths"][0].tolist() == ex["depths"]
+    np.testing.assert_allclose(got["scores"][0], np.array(ex["scores_in_ln2"]) * math.log(2.0), rtol=0, atol=1e-6)
+
+
+@pytest.mark.parametrize("wdtype,ds,B,M,k,N", [("f32", 64, 1, 8, 8, 120), ("f32", 64, 3, 8, 4, 90),
+                                              ("bf16", 1024, 2, 8, 8, 150)])
+def test_long_exact_tie_groups(dev, wdtype, ds, B, M, k, N):
+    # W2 = 0 and every base logit equal: every child of a depth has the same
+    # log-prob, so each depth's nodes form one exact tie group across all
+    # parents (64 entries at depth 2 with k = 8, longer than a 32-entry pop
+    # batch), ordered only by token and then by the parent's order
+    spec = synth.small(f"longties_{wdtype}_{B}_{k}", V=96, D=4, h=64, e=96, ds=ds, r=64, M=M, k=k, N=N, B=B,
+                       wdtype=wdtype, group=1700 + B + k, emb_std=0.5, biases=True, root_std=0.5)
+    spec, w, req = synth.workload(spec)
+    w = dict(w, w2=np.zeros_like(w["w2"]))
+    base = np.zeros((B, spec.D, spec.V), np.float32)
+    tb = gu.make_builder(spec, w)
+    got = gu.run(tb, spec, req, base=base)
+    tb.close()
+    reps, trees = gu.compare(spec, w, req, got, base=base)
+    print(gu.summarize(reps))
+    gu.assert_parity(reps)
+    assert all(r.exact for r in reps)
+    for b, t in enumerate(trees):
+        np.testing.assert_allclose(got["scores"][b, :N + 1], np.array(t.scores), rtol=0, atol=1e-5)
+        # the largest group of equal (score, depth) really is longer than a
+        # pop batch and spans several parents
+        groups = {}
+        for i in range(1, N + 1):
+            groups.setdefault(t.depths[i], []).append(i)
+        big = max(groups.values(), key=len)
+        assert len(big) > 32 and len({t.parents[i] for i in big}) > 1
+        assert len({t.scores[i] for i in big}) == 1
