@@ -86,7 +86,9 @@ struct dt_handle {
   void* wlm_t = nullptr;    // W_lm^T: tiled for the LM-head GEMM (wlm_tiled) or [V, h]; or null
   bool wlm_tiled = false;
   uint16_t* a_tiles = nullptr;  // H in the LM-head GEMM's tile order (per call)
-  float* logits = nullptr;  // [max_batch, D, V] base logits computed by the LM head
+  float* logits = nullptr;  // [max_batch, D, V] base logits computed by the LM head (the chain head)
+  uint64_t* lm_lists = nullptr;  // LM head fused with the candidate selection: per-row lists and statistics
+  float2* lm_stats = nullptr;
   void* wc_rm = nullptr;    // [3 ds + r, ds] row-major [W_hh ; W1_S^T] (the chain head)
   void* w2f = nullptr;      // bf16 W2^T in the chain head's MFMA fragment order, or null
   int n_tiles = 0;
@@ -141,7 +143,8 @@ void free_all(dt_handle* h) {
                   h->chunk_cand, h->chunk_stat, h->cand_ids, h->cand_vals, h->tokrank, h->lse,
                   h->tail,    h->P,        h->state,    h->act,   h->gh,       h->u,
                   h->ninfo,   h->mbox_w,   h->mbox_c,   h->err,   h->nanflag, h->wc_rm,
-                  h->chain_gu, h->chain_s, h->chain_sop, h->chain_part, h->a_tiles, h->w2f};
+                  h->chain_gu, h->chain_s, h->chain_sop, h->chain_part, h->a_tiles, h->w2f, h->lm_lists,
+                  h->lm_stats};
   for (void* p : ptrs)
     if (p) (void)hipFree(p);
   for (auto& set : h->ev)
@@ -307,6 +310,11 @@ dt_status dt_create(dt_handle** out, const dt_dims* dims, const dt_weights* w, c
   const int S = dt::topm_chunks(V);
   const size_t rows = (size_t)Bm * D;
   if (h->wlm_t) ALLOC(h->logits, rows * V * sizeof(float));
+  if (h->wlm_tiled && dt::lm_topm_ok((int)rows, V, hd, M)) {
+    const size_t nl = (size_t)dt::lm_lists_per_row(V);
+    ALLOC(h->lm_lists, rows * nl * 8 * sizeof(uint64_t));
+    ALLOC(h->lm_stats, rows * nl * sizeof(float2));
+  }
   ALLOC(h->chunk_cand, rows * S * M * sizeof(uint64_t));
   ALLOC(h->chunk_stat, rows * S * sizeof(float4));
   ALLOC(h->cand_ids, rows * M * sizeof(int32_t));
@@ -402,19 +410,29 @@ dt_status dt_build_trees(dt_handle* h, const dt_inputs* in, const dt_params* p, 
                                d.rank, d.hidden, d.rank, ps));
   if (!p_inline) HIPCHK(hipEventRecord(h->join_ev, h->side));
   // a0 (LM head, when no base logits are given), then a1: candidates and LSE
-  // the LM head's logits go to the caller's copy when one is asked for
-  float* lm_logits = out->logits ? out->logits : h->logits;
-  if (!in->base_logits) {
-    // L_base = H W_lm (Domino summary, 方法步骤详情), fp32 accumulate
-    if (h->wlm_tiled)
-      HIPCHK(dt::launch_gemm_bf16_btiled((const uint16_t*)in->hidden, (const uint16_t*)h->wlm_t, lm_logits, rows, V,
-                                         d.hidden, V, h->a_tiles, stream));
-    else
-      HIPCHK(dt::launch_gemm_bf16((const uint16_t*)in->hidden, nullptr, (const uint16_t*)h->wlm_t, nullptr,
-                                  lm_logits, rows, V, d.hidden, V, stream));
-  }
-  MARK(1);
-  {
+  if (!in->base_logits && h->lm_lists) {
+    // L_base = H W_lm (Domino summary, 方法步骤详情), fp32 accumulate, with
+    // each depth's candidates taken in the GEMM's epilogue: the logits reach
+    // memory only when the caller asks for a copy
+    HIPCHK(dt::launch_lm_topm_gemm((const uint16_t*)in->hidden, (const uint16_t*)h->wlm_t, rows, V, d.hidden,
+                                   h->a_tiles, p->temperature, h->lm_lists, h->lm_stats, out->logits, stream));
+    MARK(1);
+    HIPCHK(dt::launch_lm_select(h->lm_lists, h->lm_stats, rows, V, d.hidden, M, p->temperature,
+                                (const uint16_t*)in->hidden, (const uint16_t*)h->wlm_t, h->cand_ids, h->cand_vals,
+                                h->lse, h->tail, h->tokrank, out->cand_ids, out->cand_logits, out->lse, out->logits,
+                                h->err, stream));
+  } else {
+    // the LM head's logits go to the caller's copy when one is asked for
+    float* lm_logits = out->logits ? out->logits : h->logits;
+    if (!in->base_logits) {
+      if (h->wlm_tiled)
+        HIPCHK(dt::launch_gemm_bf16_btiled((const uint16_t*)in->hidden, (const uint16_t*)h->wlm_t, lm_logits, rows,
+                                           V, d.hidden, V, h->a_tiles, stream));
+      else
+        HIPCHK(dt::launch_gemm_bf16((const uint16_t*)in->hidden, nullptr, (const uint16_t*)h->wlm_t, nullptr,
+                                    lm_logits, rows, V, d.hidden, V, stream));
+    }
+    MARK(1);
     const float* logits = in->base_logits ? in->base_logits : lm_logits;
     HIPCHK(dt::launch_topm(logits, rows, V, M, p->temperature, h->chunk_cand, h->chunk_stat, h->cand_ids,
                            h->cand_vals, h->lse, h->tail, h->tokrank, out->cand_ids, out->cand_logits, out->lse,

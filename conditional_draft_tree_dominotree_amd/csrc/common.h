@@ -167,6 +167,20 @@ __device__ __forceinline__ float block_sum(float v, float* red) {
   return r;
 }
 
+// Integer sums over a wave (every lane gets it) and over a 256-thread block
+// (`red` holds 4 ints; every thread must call it).
+__device__ __forceinline__ int wave_reduce_add(int v) {
+  for (int d = 32; d >= 1; d >>= 1) v += __shfl_xor(v, d);
+  return v;
+}
+__device__ __forceinline__ int block_reduce_add(int v, int* red) {
+  v = wave_reduce_add(v);
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  return red[0] + red[1] + red[2] + red[3];
+}
+
 // Suffix sums over the threads of a block in thread order:
 // returns sum of v over threads with a larger index (exclusive).
 template <int NT>

@@ -370,13 +370,11 @@ constexpr int HNS = 3;                       // ring stages
 constexpr int HSTAGE = (HM + BT) * BK;       // bf16 per stage (A rows, then B rows)
 constexpr size_t HALF_LDS = (size_t)HNS * HSTAGE * sizeof(uint16_t);  // 73728 B
 
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void gemm_lm_half_kernel(
-    const uint16_t* __restrict__ At, const uint16_t* __restrict__ Bt, float* __restrict__ C, int M, int N, int K,
-    int ldc, int tm, int tiles, int per_xcd) {
-  extern __shared__ __attribute__((aligned(16))) uint16_t glds[];
-  const int t = (int)(blockIdx.x & 7) * per_xcd + (int)(blockIdx.x >> 3);
-  if (t >= tiles) return;
-  const int m0 = (t % tm) * HM, n0 = (t / tm) * BT;
+// acc = the 128 x 256 tile (m0, n0) of At Bt^T.  Lane layout of acc[x][y]
+// (wave w: rows 64 (w >> 1) + 32 x, columns 128 (w & 1) + 32 y): column
+// (lane & 31), rows 8 (e / 4) + 4 (lane >> 5) + (e % 4) of element e.
+__device__ __forceinline__ void lm_mainloop(const uint16_t* __restrict__ At, const uint16_t* __restrict__ Bt, int K,
+                                            int m0, int n0, uint16_t* glds, floatx16 (&acc)[2][4]) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = (w >> 1) * 64, wn = (w & 1) * 128;
@@ -420,7 +418,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     asm volatile("" ::: "memory");
     __builtin_amdgcn_sched_barrier(0);
   };
-  floatx16 acc[2][4];
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -458,9 +455,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     step(i + 1, fa[1], fb[1], fa[0], fb[0]);
   }
   wait_vm<0>();
+}
+
+// Store a wave's share of the tile (rows < M, columns < N) into C.
+__device__ __forceinline__ void lm_store(const floatx16 (&acc)[2][4], float* __restrict__ C, int M, int N, int ldc,
+                                         int m0, int n0) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int wm = (w >> 1) * 64, wn = (w & 1) * 128;
 #pragma unroll
   for (int y = 0; y < 4; ++y) {
-    const int col = n0 + wn + 32 * y + fr;
+    const int col = n0 + wn + 32 * y + (lane & 31);
     if (col >= N) continue;
 #pragma unroll
     for (int x = 0; x < 2; ++x)
@@ -470,6 +474,474 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         if (row < M) C[(size_t)row * ldc + col] = acc[x][y][e];
       }
   }
+}
+
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void gemm_lm_half_kernel(
+    const uint16_t* __restrict__ At, const uint16_t* __restrict__ Bt, float* __restrict__ C, int M, int N, int K,
+    int ldc, int tm, int tiles, int per_xcd) {
+  extern __shared__ __attribute__((aligned(16))) uint16_t glds[];
+  const int t = (int)(blockIdx.x & 7) * per_xcd + (int)(blockIdx.x >> 3);
+  if (t >= tiles) return;
+  const int m0 = (t % tm) * HM, n0 = (t / tm) * BT;
+  floatx16 acc[2][4];
+  lm_mainloop(At, Bt, K, m0, n0, glds, acc);
+  lm_store(acc, C, M, N, ldc, m0, n0);
+}
+
+// ---------------------------------------------------------------------------
+// The LM head fused with the per-depth candidate selection.  Base logits are
+// the LM head applied to the draft block's hidden states (Domino summary,
+// 方法步骤详情), and the tree needs only each depth's top-M of them and their
+// log-sum-exp (DominoTree summary, Componenti Core 2).  So the GEMM's
+// epilogue keeps, for each row and each 128 columns of its tile (a list), the
+// LM_KT largest logits as (value, id) composites and the list's statistics
+// (its max m and the sum of exp((x - m) / T)); the logits need not reach
+// memory (41 MB of lists and statistics instead of 292 MB at 480 x 151936).
+// lm_select_kernel then merges a row's lists.  A list whose LM_KT-th key still
+// beats the row's M-th selected key may hold more of the row's top M than it
+// listed; the merge recomputes that list's 128 logits of the row (an fp32
+// dot product per column) and selects again.  At most ceil(M / LM_KT) lists can
+// be in that state (each has LM_KT keys above the M-th), and once they are
+// recomputed the M-th key can only rise, so one such round is enough.
+
+constexpr int LM_COLS = 128;            // columns per list (a wave's share of a tile)
+constexpr int LM_KT = 8;                // keys per list
+constexpr int LM_STRIDE = LM_COLS + 4;  // staged row stride (floats)
+constexpr int LM_POOL = 1024;           // merge: candidates ranked pairwise
+constexpr int LM_HEADS = 24;            // merge: list heads per lane kept in registers (nl <= 1536)
+constexpr int LM_REDO_CAP = 2 * (DT_TOPM_MAX + LM_KT - 1) / LM_KT;  // merge: lists recomputed at most
+
+static_assert(4 * 32 * LM_STRIDE * 4 <= (int)HALF_LDS, "the epilogue stages 32 rows per wave in the ring");
+
+// insert k into the descending list t (k above t's last entry)
+__device__ __forceinline__ void topk_insert(uint64_t (&t)[LM_KT], uint64_t k) {
+#pragma unroll
+  for (int i = LM_KT - 1; i > 0; --i) t[i] = k > t[i - 1] ? t[i - 1] : (k > t[i] ? k : t[i]);
+  t[0] = k > t[0] ? k : t[0];
+}
+
+// the LM_KT largest of two descending lists, descending (a bitonic merge)
+__device__ __forceinline__ void topk_merge(uint64_t (&a)[LM_KT], const uint64_t (&b)[LM_KT]) {
+#pragma unroll
+  for (int i = 0; i < LM_KT; ++i) a[i] = a[i] > b[LM_KT - 1 - i] ? a[i] : b[LM_KT - 1 - i];
+#pragma unroll
+  for (int d = LM_KT / 2; d >= 1; d >>= 1)
+#pragma unroll
+    for (int i = 0; i < LM_KT; ++i)
+      if ((i & d) == 0) {
+        const uint64_t x = a[i], y = a[i + d];
+        a[i] = x > y ? x : y;
+        a[i + d] = x > y ? y : x;
+      }
+}
+
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void gemm_lm_topk_kernel(
+    const uint16_t* __restrict__ At, const uint16_t* __restrict__ Bt, int M, int N, int K, int tm, int tiles,
+    int per_xcd, float l2t, int nl, uint64_t* __restrict__ lists, float2* __restrict__ stats, float* __restrict__ C,
+    int ldc) {
+  extern __shared__ __attribute__((aligned(16))) uint16_t glds[];
+  const int t = (int)(blockIdx.x & 7) * per_xcd + (int)(blockIdx.x >> 3);
+  if (t >= tiles) return;
+  const int m0 = (t % tm) * HM, n0 = (t / tm) * BT;
+  floatx16 acc[2][4];
+  lm_mainloop(At, Bt, K, m0, n0, glds, acc);
+  if (C) lm_store(acc, C, M, N, ldc, m0, n0);
+  __syncthreads();  // every wave is done with the ring: each stages its rows in a quarter of it
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int wm = (w >> 1) * 64, wn = (w & 1) * 128;
+  float* st = reinterpret_cast<float*>(glds) + w * 32 * LM_STRIDE;
+  const int lr = lane & 31, lh = lane >> 5;   // the row this lane scans, and which 64 of its columns
+  const int list = 2 * (n0 / BT) + (w & 1);
+  const int c0 = n0 + wn + 64 * lh;
+  const int ncol = min(64, N - c0);           // columns of this lane inside the matrix (may be <= 0)
+#pragma unroll
+  for (int x = 0; x < 2; ++x) {
+    // stage the wave's rows 32 x .. 32 x + 31 (row-major, LM_STRIDE floats a row)
+#pragma unroll
+    for (int y = 0; y < 4; ++y)
+#pragma unroll
+      for (int e = 0; e < 16; ++e)
+        st[(8 * (e >> 2) + 4 * lh + (e & 3)) * LM_STRIDE + 32 * y + lr] = acc[x][y][e];
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the wave's writes are in LDS (one wave: no barrier)
+    const float* srcf = st + lr * LM_STRIDE + 64 * lh;
+    const float4* src = reinterpret_cast<const float4*>(srcf);
+    // pass 1: the row's max over both lanes' columns, and a lower bound tau
+    // of its LM_KT-th largest value: the smallest of eight group maxima (the
+    // lane's four groups of 16 columns and its partner's), eight distinct
+    // values at or above it (-inf when a group is empty, at the matrix edge)
+    float g[4];
+#pragma unroll
+    for (int gi = 0; gi < 4; ++gi) {
+      g[gi] = -INFINITY;
+#pragma unroll
+      for (int q = 4 * gi; q < 4 * gi + 4; ++q) {
+        const float4 v = src[q];
+        if (4 * q < ncol) g[gi] = fmaxf(g[gi], v.x);
+        if (4 * q + 1 < ncol) g[gi] = fmaxf(g[gi], v.y);
+        if (4 * q + 2 < ncol) g[gi] = fmaxf(g[gi], v.z);
+        if (4 * q + 3 < ncol) g[gi] = fmaxf(g[gi], v.w);
+      }
+    }
+    float m = fmaxf(fmaxf(g[0], g[1]), fmaxf(g[2], g[3]));
+    float tau = fminf(fminf(g[0], g[1]), fminf(g[2], g[3]));
+    m = fmaxf(m, __shfl_xor(m, 32));
+    tau = fminf(tau, __shfl_xor(tau, 32));
+    // pass 2: every term of the sum relative to the row's max (the merge
+    // recomputes a listed term with the same expression), and the columns at
+    // or above tau
+    const float mb = m * l2t;
+    float s = 0.f;
+    uint64_t cmask = 0ull;
+    if (m > -INFINITY) {
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        const float4 v = src[q];
+        const float vv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          if (4 * q + j < ncol) {
+            s += __builtin_amdgcn_exp2f(__builtin_fmaf(vv[j], l2t, -mb));
+            if (vv[j] >= tau) cmask |= 1ull << (4 * q + j);
+          }
+        }
+      }
+    }
+    // pass 3: the candidates into the descending list
+    uint64_t top[LM_KT];
+#pragma unroll
+    for (int i = 0; i < LM_KT; ++i) top[i] = 0ull;
+    while (cmask) {
+      const int q = __builtin_ctzll(cmask);
+      cmask &= cmask - 1ull;
+      const uint64_t k = cand_pack(f32_key(srcf[q]), (uint32_t)(c0 + q));
+      if (k > top[LM_KT - 1]) topk_insert(top, k);
+    }
+    s += __shfl_xor(s, 32);
+    uint64_t other[LM_KT];
+#pragma unroll
+    for (int i = 0; i < LM_KT; ++i) other[i] = shfl_xor_u64(top[i], 32);
+    topk_merge(top, other);
+    const int row = m0 + wm + 32 * x + lr;
+    if (lh == 0 && row < M) {  // a list past the last column is written empty (m = -inf)
+      uint4* o = reinterpret_cast<uint4*>(lists + ((size_t)row * nl + list) * LM_KT);
+#pragma unroll
+      for (int i = 0; i < LM_KT; i += 2)
+        o[i / 2] = make_uint4((uint32_t)top[i], (uint32_t)(top[i] >> 32), (uint32_t)top[i + 1],
+                              (uint32_t)(top[i + 1] >> 32));
+      stats[(size_t)row * nl + list] = make_float2(m, s);
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the reads are done before the next rows overwrite them
+  }
+}
+
+// sum_k h[k] W_lm[k, col] in fp32, k ascending, from W_lm in the tiled order
+// of launch_pack_b_tiles (a column's 32 k of a stage are 64 contiguous bytes,
+// their four 16-byte pieces swizzled)
+__device__ __forceinline__ float wlm_dot(const uint16_t* __restrict__ Bt, int nk, int col, const float* h) {
+  const int nt = col / BT, r = col % BT, sw = big_swz(r & 15);
+  const uint16_t* base = Bt + (size_t)nt * nk * BOPND + (size_t)r * BK;
+  float acc = 0.f;
+  for (int st = 0; st < nk; ++st) {
+#pragma unroll
+    for (int c = 0; c < BK / 8; ++c) {
+      const uint4 q = *reinterpret_cast<const uint4*>(base + (size_t)st * BOPND + 8 * (c ^ sw));
+      const uint32_t wd[4] = {q.x, q.y, q.z, q.w};
+      const float* hk = h + st * BK + 8 * c;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        acc = __builtin_fmaf(hk[2 * e], __uint_as_float(wd[e] << 16), acc);
+        acc = __builtin_fmaf(hk[2 * e + 1], __uint_as_float(wd[e] & 0xFFFF0000u), acc);
+      }
+    }
+  }
+  return acc;
+}
+
+// One block per row: the row's M candidates (value desc, id asc), the LSE of
+// base / T over the whole row and over the tokens left out (tail), from its
+// nl lists.  lists_out/stat are read; `hidden` ([rows, K] bf16 row-major) and
+// Bt (W_lm tiled) serve the recomputation.  user_logits (optional) holds the
+// GEMM's logits; recomputed ones are written there too.
+__global__ __launch_bounds__(256) void lm_select_kernel(
+    const uint64_t* __restrict__ lists, const float2* __restrict__ stats, int nl, int M, float T, float l2t,
+    const uint16_t* __restrict__ hidden, const uint16_t* __restrict__ Bt, int K, int N,
+    int32_t* __restrict__ ids_out, float* __restrict__ vals_out, float* __restrict__ lse_out,
+    float* __restrict__ tail_out, int32_t* __restrict__ tokrank_out, int32_t* __restrict__ user_ids,
+    float* __restrict__ user_vals, float* __restrict__ user_lse, float* __restrict__ user_logits,
+    int* __restrict__ err) {
+  extern __shared__ float2 sst[];               // [nl] list statistics, [nl] lists' last keys, [nl] heads' value keys
+  __shared__ uint64_t pool[LM_POOL];            // candidates
+  __shared__ uint64_t best[DT_TOPM_MAX];        // the row's M, descending
+  __shared__ float redo_v[LM_REDO_CAP][LM_COLS];  // recomputed lists' logits
+  __shared__ int redo_l[LM_REDO_CAP];             // their list indices
+  __shared__ float hrow[8192];                  // the row's hidden state (recomputation)
+  __shared__ int npool, nredo, nnew, nbest;
+  __shared__ uint32_t bound;
+  __shared__ float red[4];
+  __shared__ int ired[4];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int row = blockIdx.x;
+  const uint64_t* L = lists + (size_t)row * nl * LM_KT;
+  uint64_t* lastk = reinterpret_cast<uint64_t*>(sst + nl);   // set for the lists read into the pool
+  uint32_t* hk = reinterpret_cast<uint32_t*>(lastk + nl);
+  // every thread's loads in flight together
+  for (int i0 = 0; i0 < nl; i0 += 256 * 8) {
+    float2 sv[8];
+    uint32_t hv[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int i = min(i0 + u * 256 + tid, nl - 1);   // clamped: valid addresses
+      sv[u] = stats[(size_t)row * nl + i];
+      hv[u] = (uint32_t)(L[(size_t)i * LM_KT] >> 32);
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int i = i0 + u * 256 + tid;
+      if (i < nl) {
+        sst[i] = sv[u];
+        hk[i] = hv[u];
+      }
+    }
+  }
+  if (tid == 0) nredo = 0;
+  __syncthreads();
+
+  // entry j of list t: the listed keys, or the recomputed values of a redone list
+  auto list_len = [&](int t, int& r) {
+    r = -1;
+    for (int q = 0; q < nredo; ++q)
+      if (redo_l[q] == t) r = q;
+    return r >= 0 ? LM_COLS : LM_KT;
+  };
+  auto entry = [&](int t, int r, int j) -> uint64_t {
+    if (r < 0) return L[(size_t)t * LM_KT + j];
+    const int col = t * LM_COLS + j;
+    return col < N ? cand_pack(f32_key(redo_v[r][j]), (uint32_t)col) : 0ull;
+  };
+
+  for (int round = 0;; ++round) {
+    // 1. a lower bound of the row's M-th value key: the M-th largest list head
+    //    (M distinct entries reach it); wave 0 finds it bit by bit
+    if (wv == 0) {
+      uint32_t p = 0;
+      if (nl <= 64 * LM_HEADS) {
+        // the heads in registers, counted with ballots
+        uint32_t hv[LM_HEADS];
+#pragma unroll
+        for (int j = 0; j < LM_HEADS; ++j) hv[j] = lane + 64 * j < nl ? hk[lane + 64 * j] : 0u;
+        for (int b = 31; b >= 0; --b) {
+          const uint32_t c = p | (1u << b);
+          int cnt = 0;
+#pragma unroll
+          for (int j = 0; j < LM_HEADS; ++j) cnt += (int)__popcll(__ballot(hv[j] >= c));
+          if (cnt >= M) p = c;
+        }
+      } else {
+        for (int b = 31; b >= 0; --b) {
+          const uint32_t c = p | (1u << b);
+          int cnt = 0;
+          for (int t = lane; t < nl; t += 64) cnt += hk[t] >= c;
+          cnt = wave_reduce_add(cnt);
+          if (cnt >= M) p = c;
+        }
+      }
+      if (lane == 0) {
+        bound = p;
+        npool = 0;
+      }
+    }
+    __syncthreads();
+    // 2. every entry at or above the bound (a list's 8 keys in four 16-byte
+    //    loads; a recomputed list's values from LDS)
+    const uint32_t bd = bound;
+    for (int t = tid; t < nl; t += 256) {
+      if (hk[t] < bd) continue;
+      int r;
+      const int len = list_len(t, r);
+      if (r < 0) {
+        const uint4* src = reinterpret_cast<const uint4*>(L + (size_t)t * LM_KT);
+        uint4 q[LM_KT / 2];
+#pragma unroll
+        for (int i = 0; i < LM_KT / 2; ++i) q[i] = src[i];
+        lastk[t] = (uint64_t)q[LM_KT / 2 - 1].w << 32 | q[LM_KT / 2 - 1].z;
+#pragma unroll
+        for (int i = 0; i < LM_KT; ++i) {
+          const uint64_t k = (i & 1) ? ((uint64_t)q[i / 2].w << 32 | q[i / 2].z) : ((uint64_t)q[i / 2].y << 32 | q[i / 2].x);
+          if (k != 0ull && cand_key(k) >= bd) {
+            const int slot = atomicAdd(&npool, 1);
+            if (slot < LM_POOL) pool[slot] = k;
+          }
+        }
+      } else {
+        for (int j = 0; j < len; ++j) {
+          const uint64_t k = entry(t, r, j);
+          if (k != 0ull && cand_key(k) >= bd) {
+            const int slot = atomicAdd(&npool, 1);
+            if (slot < LM_POOL) pool[slot] = k;
+          }
+        }
+      }
+    }
+    __syncthreads();
+    const int C = npool;
+    if (C <= LM_POOL) {
+      // 3. exact ranks among the candidates (composites are unique)
+      for (int i = tid; i < C; i += 256) {
+        const uint64_t k = pool[i];
+        int rk = 0;
+#pragma unroll 8
+        for (int j = 0; j < C; ++j) rk += pool[j] > k;
+        if (rk < M) best[rk] = k;
+      }
+      if (tid == 0) nbest = min(C, M);
+    } else {
+      // 3'. many entries at the bound (equal values): the M-th largest
+      //     composite bit by bit, then the entries at or above it
+      uint64_t p = 0;
+      for (int b = 63; b >= 0; --b) {
+        const uint64_t c = p | (1ull << b);
+        int cnt = 0;
+        for (int t = tid; t < nl; t += 256) {
+          int r;
+          const int len = list_len(t, r);
+          for (int j = 0; j < len; ++j) {
+            const uint64_t k = entry(t, r, j);
+            if (k >= c) ++cnt;
+            else if (r < 0) break;
+          }
+        }
+        cnt = block_reduce_add(cnt, ired);
+        if (cnt >= M) p = c;
+      }
+      if (tid == 0) npool = 0;
+      __syncthreads();
+      for (int t = tid; t < nl; t += 256) {
+        int r;
+        const int len = list_len(t, r);
+        for (int j = 0; j < len; ++j) {
+          const uint64_t k = entry(t, r, j);
+          if (k >= p && k != 0ull) {
+            const int slot = atomicAdd(&npool, 1);
+            if (slot < DT_TOPM_MAX) best[slot] = k;
+          } else if (r < 0) {
+            break;
+          }
+        }
+      }
+      __syncthreads();
+      if (wv == 0) {
+        uint64_t v = lane < min(npool, M) ? best[lane] : 0ull;
+        v = wave_sort_desc_u64(v);
+        if (lane < DT_TOPM_MAX) best[lane] = v;
+      }
+      if (tid == 0) nbest = min(npool, M);
+    }
+    __syncthreads();
+    // 4. lists not yet recomputed that may hold more of the row's M than they
+    //    listed: full, with their last key above the M-th
+    const uint64_t kth = nbest == M ? best[M - 1] : 0ull;
+    const int before = nredo;
+    if (tid == 0) nnew = 0;
+    __syncthreads();
+    for (int t = tid; t < nl; t += 256) {
+      // a list whose head is below the bound has no key above the M-th
+      if (hk[t] < bd || (uint64_t)hk[t] < (kth >> 32)) continue;
+      int r;
+      list_len(t, r);
+      if (r >= 0) continue;
+      const uint64_t last = lastk[t];   // read into the pool above: its head reached the bound
+      if (last != 0ull && last > kth) {
+        const int q = before + atomicAdd(&nnew, 1);
+        if (q < LM_REDO_CAP) redo_l[q] = t;
+      }
+    }
+    __syncthreads();
+    if (nnew == 0) break;
+    if (before + nnew > LM_REDO_CAP) {
+      // cannot happen: at most ceil(M / LM_KT) lists hold LM_KT keys above the
+      // M-th, and recomputing them lowers the M-th only by rounding
+      if (tid == 0) atomicOr(err, 16);
+      break;
+    }
+    // 5. recompute those lists' logits of the row (fp32 dot products, k in
+    //    order) and their statistics
+    if (before == 0)
+      for (int k = tid; k < K; k += 256) hrow[k] = bf16_to_f32(hidden[(size_t)row * K + k]);
+    __syncthreads();
+    const int nk = K / BK;
+    for (int i = tid; i < nnew * LM_COLS; i += 256) {
+      const int q = before + i / LM_COLS, j = i % LM_COLS, col = redo_l[q] * LM_COLS + j;
+      const float v = col < N ? wlm_dot(Bt, nk, col, hrow) : -INFINITY;
+      redo_v[q][j] = v;
+      if (user_logits && col < N) user_logits[(size_t)row * N + col] = v;
+    }
+    __syncthreads();
+    for (int q = before + wv; q < before + nnew; q += 4) {
+      const int t = redo_l[q];
+      float m = -INFINITY;
+      for (int j = lane; j < LM_COLS; j += 64)
+        if (t * LM_COLS + j < N) m = fmaxf(m, redo_v[q][j]);
+      m = wave_max(m);
+      float s = 0.f;
+      if (m > -INFINITY)
+        for (int j = lane; j < LM_COLS; j += 64)
+          if (t * LM_COLS + j < N) s += __builtin_amdgcn_exp2f(__builtin_fmaf(redo_v[q][j], l2t, -m * l2t));
+      s = wave_sum(s);
+      if (lane == 0) {
+        sst[t] = make_float2(m, s);
+        hk[t] = m > -INFINITY ? f32_key(m) : 0u;   // the recomputed list's head
+      }
+    }
+    if (tid == 0) nredo = before + nnew;
+    __syncthreads();
+  }
+
+  // 6. the LSE over the row and over the tokens left out
+  float mloc = -INFINITY;
+  for (int i = tid; i < nl; i += 256) mloc = fmaxf(mloc, sst[i].x);
+  const float mstar = block_max<256>(mloc, red);
+  float s_all = 0.f;
+  if (mstar > -INFINITY)
+    for (int i = tid; i < nl; i += 256)
+      if (sst[i].x > -INFINITY) s_all += sst[i].y * __builtin_amdgcn_exp2f((sst[i].x - mstar) * l2t);
+  float s_sel = 0.f;
+  const int nb = nbest;
+  if (mstar > -INFINITY && tid < nb) {
+    const uint64_t k = best[tid];
+    const float x = key_f32(cand_key(k));
+    const float mt = sst[(int)cand_id(k) / LM_COLS].x;
+    s_sel = __builtin_amdgcn_exp2f(__builtin_fmaf(x, l2t, -mt * l2t)) * __builtin_amdgcn_exp2f((mt - mstar) * l2t);
+  }
+  s_all = block_sum<256>(s_all, red);
+  s_sel = block_sum<256>(s_sel, red);
+  if (tid == 0) {
+    const float lse = (mstar > -INFINITY && s_all > 0.f) ? mstar / T + __logf(s_all) : -INFINITY;
+    const float st = fmaxf(s_all - s_sel, 0.f);
+    lse_out[row] = lse;
+    tail_out[row] = (mstar > -INFINITY && st > 0.f) ? mstar / T + __logf(st) : -INFINITY;
+    if (user_lse) user_lse[row] = lse;
+  }
+  // 7. the candidates and the rank of each one's token id among them
+  if (tid < M) {
+    const uint64_t k = tid < nb ? best[tid] : 0ull;
+    const int id = tid < nb ? (int)cand_id(k) : 0;
+    const float v = tid < nb ? key_f32(cand_key(k)) : -INFINITY;
+    ids_out[(size_t)row * M + tid] = id;
+    vals_out[(size_t)row * M + tid] = v;
+    if (user_ids) user_ids[(size_t)row * M + tid] = id;
+    if (user_vals) user_vals[(size_t)row * M + tid] = v;
+    int r = 0;
+#pragma unroll 8
+    for (int j = 0; j < nb; ++j) r += (int)cand_id(best[j]) < id;
+    tokrank_out[(size_t)row * M + tid] = r;
+  }
+}
+
+int lm_lists_per_row(int N) { return 2 * ((N + BT - 1) / BT); }
+
+bool lm_topm_ok(int M, int N, int K, int topM) {
+  return gemm_b_tiles_ok(N, K) && K <= 8192 && M > 0 && topM >= 1 && topM <= DT_TOPM_MAX &&
+         (size_t)lm_lists_per_row(N) * (sizeof(float2) + 8 + 4) <= 96 * 1024;
 }
 
 // A [M, K] row-major into the same tile order as launch_pack_b_tiles' (block
@@ -509,6 +981,34 @@ hipError_t launch_gemm_bf16_btiled(const uint16_t* A, const uint16_t* Btiled, fl
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(gemm_lm_half_kernel, dim3(8 * per_xcd), dim3(256), HALF_LDS, stream, a_tiles, Btiled, C, M, N,
                      K, ldc, tm, tiles, per_xcd);
+  return hipGetLastError();
+}
+
+hipError_t launch_lm_topm_gemm(const uint16_t* A, const uint16_t* Btiled, int M, int N, int K, uint16_t* a_tiles,
+                               float T, uint64_t* lists, float2* stats, float* user_logits, hipStream_t stream) {
+  if (!gemm_b_tiles_ok(N, K) || M <= 0 || !a_tiles || !lists || !stats) return hipErrorInvalidValue;
+  const int nk = K / BK;
+  const size_t n = (size_t)((M + BT - 1) / BT) * BT * nk;
+  hipLaunchKernelGGL(pack_a_tiles_kernel, dim3((unsigned)std::min<size_t>((n + 255) / 256, 4096)), dim3(256), 0,
+                     stream, A, a_tiles, M, K);
+  const int tm = (M + HM - 1) / HM, tiles = tm * ((N + BT - 1) / BT), per_xcd = (tiles + 7) / 8;
+  hipError_t e = hipFuncSetAttribute((const void*)gemm_lm_topk_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                     (int)HALF_LDS);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(gemm_lm_topk_kernel, dim3(8 * per_xcd), dim3(256), HALF_LDS, stream, a_tiles, Btiled, M, N, K,
+                     tm, tiles, per_xcd, 1.4426950408889634f / T, lm_lists_per_row(N), lists, stats, user_logits, N);
+  return hipGetLastError();
+}
+
+hipError_t launch_lm_select(const uint64_t* lists, const float2* stats, int rows, int N, int K, int topM, float T,
+                            const uint16_t* hidden, const uint16_t* Btiled, int32_t* ids, float* vals, float* lse,
+                            float* tail, int32_t* tokrank, int32_t* user_ids, float* user_vals, float* user_lse,
+                            float* user_logits, int* err, hipStream_t stream) {
+  if (!lm_topm_ok(rows, N, K, topM)) return hipErrorInvalidValue;
+  const int nl = lm_lists_per_row(N);
+  hipLaunchKernelGGL(lm_select_kernel, dim3(rows), dim3(256), (size_t)nl * (sizeof(float2) + 8 + 4), stream, lists, stats, nl,
+                     topM, T, 1.4426950408889634f / T, hidden, Btiled, K, N, ids, vals, lse, tail, tokrank, user_ids,
+                     user_vals, user_lse, user_logits, err);
   return hipGetLastError();
 }
 

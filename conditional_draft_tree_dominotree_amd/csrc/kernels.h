@@ -42,6 +42,22 @@ hipError_t launch_gemm_bf16_btiled(const uint16_t* A, const uint16_t* Btiled, fl
                                    int ldc, uint16_t* a_tiles, hipStream_t stream);
 hipError_t launch_gemm_f32(const float* A, const int32_t* rows, const float* Bt, const float* bias,
                            float* C, int M, int N, int K, int ldc, hipStream_t stream);
+// The LM head fused with the candidate selection (gemm.hip): the GEMM's
+// epilogue writes, per row and per 128 columns, the 8 largest logits as
+// (value, id) composites (lists [M, nl, 8]) and (max, sum of exp((x - max)/T))
+// (stats [M, nl]), nl = lm_lists_per_row(N); user_logits (optional, [M, N])
+// also gets the logits.  lm_select then gives each row's topM candidates,
+// their values, the LSE of logits/T, the tail LSE and the token-id ranks, as
+// launch_topm does; it reads A (bf16 [M, K]) and Btiled again only to
+// recompute a list that may hide candidates.  Needs lm_topm_ok.
+int lm_lists_per_row(int N);
+bool lm_topm_ok(int M, int N, int K, int topM);
+hipError_t launch_lm_topm_gemm(const uint16_t* A, const uint16_t* Btiled, int M, int N, int K, uint16_t* a_tiles,
+                               float T, uint64_t* lists, float2* stats, float* user_logits, hipStream_t stream);
+hipError_t launch_lm_select(const uint64_t* lists, const float2* stats, int rows, int N, int K, int topM, float T,
+                            const uint16_t* hidden, const uint16_t* Btiled, int32_t* ids, float* vals, float* lse,
+                            float* tail, int32_t* tokrank, int32_t* user_ids, float* user_vals, float* user_lse,
+                            float* user_logits, int* err, hipStream_t stream);
 
 // ---- tree-attention inputs (verify.hip)
 constexpr int DT_VERIFY_MAX_COLS = 1025;  // budget + 1 at the largest budget

@@ -140,6 +140,8 @@ def _body(asm_text, prefix):
 
 @pytest.mark.parametrize("src,prefix", [("gemm.hip", "_ZN2dt20gemm_bf16_big_kernel"),
                                         ("gemm.hip", "_ZN2dt19gemm_lm_half_kernel"),
+                                        ("gemm.hip", "_ZN2dt19gemm_lm_topk_kernel"),
+                                        ("gemm.hip", "_ZN2dt16lm_select_kernel"),
                                         ("chain.hip", "_ZN2dt25chain_correct_mfma_kernel"),
                                         ("chain.hip", "_ZN2dt20chain_correct_kernel")])
 def test_dense_kernels_use_no_scratch(tmp_path_factory, src, prefix):
@@ -150,7 +152,8 @@ def test_dense_kernels_use_no_scratch(tmp_path_factory, src, prefix):
             assert priv == 0, name
 
 
-@pytest.mark.parametrize("prefix,vm", [("_ZN2dt20gemm_bf16_big_kernel", 16), ("_ZN2dt19gemm_lm_half_kernel", 6)])
+@pytest.mark.parametrize("prefix,vm", [("_ZN2dt20gemm_bf16_big_kernel", 16), ("_ZN2dt19gemm_lm_half_kernel", 6),
+                                       ("_ZN2dt19gemm_lm_topk_kernel", 6)])
 def test_gemm_waits_for_its_oldest_stage_only(tmp_path_factory, prefix, vm):
     # the main loop waits for its oldest stage of operand loads only (the
     # later stages stay in flight: two of 8 loads, one of 6), then the barrier

@@ -256,3 +256,64 @@ def test_long_exact_tie_groups(dev, wdtype, ds, B, M, k, N):
         big = max(groups.values(), key=len)
         assert len(big) > 32 and len({t.parents[i] for i in big}) > 1
         assert len({t.scores[i] for i in big}) == 1
+
+
+@pytest.mark.parametrize("V,M,k,N,zero_rows,dup", [
+    (3000, 16, 4, 40, [(0, 1)], 0),          # one depth's hidden state zero: every logit 0
+    (1000, 64, 8, 60, [(0, 0), (0, 2)], 0),  # vocabulary ending inside a 256-column tile, M = 64
+    (5000, 8, 4, 30, [], 300),               # 300 equal W_lm columns: tie blocks across lists
+    (2050, 1, 1, 10, [(1, 3)], 0),           # M = 1, two requests
+])
+def test_lm_head_fused_selection_edge_cases(dev, V, M, k, N, zero_rows, dup):
+    # the LM head with the candidate selection in its epilogue: candidates,
+    # their logits and the LSE against the oracle's own LM head and
+    # selection, where equal logits force lists to be recomputed
+    from oracle import ref
+    B = 2 if any(b == 1 for b, _ in zero_rows) else 1
+    spec = synth.small(f"lmsel_{V}_{M}_{dup}", V=V, D=4, h=128, e=64, ds=64, r=32, M=M, k=k, N=N, B=B,
+                       wdtype="bf16", logits="lmhead", group=1800 + V + M, emb_std=0.5)
+    spec, w, req = synth.workload(spec)
+    w = dict(w)
+    req = dict(req)
+    hidden = req["hidden"].copy()
+    for b, d in zero_rows:
+        hidden[b, d] = 0
+    req["hidden"] = hidden
+    if dup:
+        # column 7 scaled up (its logits lead the rows where they are
+        # positive) and copied to 40 .. 40 + dup: ties that span lists
+        wl = w["w_lm"].copy()
+        wl[:, 7] = synth.bf16_bits(4.0 * synth.bits_to_f32(wl[:, 7]))
+        wl[:, 40:40 + dup] = wl[:, 7:8]
+        w["w_lm"] = wl
+    tb = gu.make_builder(spec, w)
+    import conditional_draft_tree_dominotree_amd as pkg
+    o = tb.outputs(B, M, N, candidates=True, stats=True, logits=True)
+    tb.build(gu.to_dev(hidden), None, None, top_m=M, top_k=k, budget=N, temperature=spec.T,
+             flags=pkg.DT_ACT_BF16, out=o)
+    tb.sync_status()
+    got = {key: v.cpu().numpy() for key, v in o.items()}
+    tb.close()
+    rows = hidden.reshape(B * spec.D, spec.h)
+    base = ref.lm_head_logits(rows, w["w_lm"], True).reshape(B, spec.D, V)
+    assert np.max(np.abs(got["logits"].astype(np.float64) - base)) < 1e-4
+    for b in range(B):
+        for d in range(spec.D):
+            dep = ref.candidates(base[b, d], M, spec.T)
+            ids, vals = got["cand_ids"][b, d], got["cand_logits"][b, d]
+            # the GPU's own logits at its candidates, in (value desc, id asc) order
+            np.testing.assert_array_equal(vals, got["logits"][b, d, ids])
+            assert all((vals[i] > vals[i + 1]) or (vals[i] == vals[i + 1] and ids[i] < ids[i + 1])
+                       for i in range(M - 1)), (b, d)
+            # and exactly the top M of those logits
+            gl = got["logits"][b, d]
+            order = np.lexsort((np.arange(V), -gl.astype(np.float64)))[:M]
+            np.testing.assert_array_equal(ids, order, err_msg=f"request {b} depth {d}")
+            if dep.margin >= 1e-4:
+                np.testing.assert_array_equal(np.sort(ids), np.sort(dep.cand))
+            assert abs(got["lse"][b, d] - dep.lse) <= 1e-4 * max(1.0, abs(dep.lse)), (b, d)
+            if (b, d) in zero_rows:
+                assert np.all(vals == 0) and np.array_equal(ids, np.arange(M))
+    reps, trees = gu.compare(spec, w, req, got, base=base, logits_computed=True)
+    print(gu.summarize(reps))
+    gu.assert_parity(reps)
