@@ -397,15 +397,18 @@ dt_status dt_build_trees(dt_handle* h, const dt_inputs* in, const dt_params* p, 
   // beside the whole candidate selection or beside its merge alone)
   MARK(0);
   const bool p_inline = in->base_logits != nullptr;
+  // bf16 with base logits given: P runs in extra blocks of the candidate
+  // selection's launch, beside it
+  const bool p_in_topm = p_inline && h->bf16;
   hipStream_t ps = p_inline ? stream : h->side;
   if (!p_inline) {
     HIPCHK(hipEventRecord(h->fork_ev, stream));
     HIPCHK(hipStreamWaitEvent(h->side, h->fork_ev, 0));
   }
-  if (h->bf16)
+  if (h->bf16 && !p_in_topm)
     HIPCHK(dt::launch_gemm_bf16((const uint16_t*)in->hidden, nullptr, (const uint16_t*)h->w1h_t, nullptr, h->P,
                                 rows, d.rank, d.hidden, d.rank, ps));
-  else
+  else if (!h->bf16)
     HIPCHK(dt::launch_gemm_f32((const float*)in->hidden, nullptr, (const float*)h->w1h_t, nullptr, h->P, rows,
                                d.rank, d.hidden, d.rank, ps));
   if (!p_inline) HIPCHK(hipEventRecord(h->join_ev, h->side));
@@ -436,7 +439,8 @@ dt_status dt_build_trees(dt_handle* h, const dt_inputs* in, const dt_params* p, 
     const float* logits = in->base_logits ? in->base_logits : lm_logits;
     HIPCHK(dt::launch_topm(logits, rows, V, M, p->temperature, h->chunk_cand, h->chunk_stat, h->cand_ids,
                            h->cand_vals, h->lse, h->tail, h->tokrank, out->cand_ids, out->cand_logits, out->lse,
-                           stream));
+                           stream, p_in_topm ? (const uint16_t*)in->hidden : nullptr, (const uint16_t*)h->w1h_t,
+                           h->P, d.rank, d.hidden));
   }
   // join: what P adds after the candidates are done
   MARK(2);
@@ -489,7 +493,7 @@ dt_status dt_build_trees(dt_handle* h, const dt_inputs* in, const dt_params* p, 
   a.stats = out->stats;
   a.spin_limit = 1u << 21;
   const size_t lds = dt::plan_tree(a, h->bf16, h->sched.pops, std::min(h->n_cu - B, h->max_workers),
-                                   h->sched.lds_workers, h->sched.halves);
+                                   h->sched.lds_workers, h->sched.halves, h->sched.advance == 2);
   if (lds == 0 || lds > 160 * 1024) return fail(DT_EUNSUPPORTED, "no builder schedule fits this shape in LDS");
   if (a.n_workers + B > h->n_cu || a.n_workers > h->max_workers)
     return fail(DT_EUNSUPPORTED, "%d workers + %d requests exceed %d compute units", a.n_workers, B, h->n_cu);
@@ -560,6 +564,7 @@ dt_status dt_set_schedule(dt_handle* h, const dt_schedule* s) {
   if (s->lds_workers != 0 && s->lds_workers != 1) return fail(DT_EINVAL, "lds_workers must be 0 or 1");
   if (s->tiles_per_worker < 0 || s->tiles_per_worker > 64)
     return fail(DT_EINVAL, "tiles_per_worker %d outside 0..64", s->tiles_per_worker);
+  if (s->advance < 0 || s->advance > 2) return fail(DT_EINVAL, "advance %d outside 0..2", s->advance);
   h->sched = *s;
   return DT_OK;
 }

@@ -13,10 +13,14 @@ namespace dt {
 inline int topm_chunks(int V) { return (V + TOPM_CHUNK - 1) / TOPM_CHUNK; }
 
 // ---- per-depth candidates (topm.hip)
+// With pA (bf16 [rows, pK]) given, the merge's launch also computes
+// pC [rows, pN] = pA pBt^T (pBt bf16 [pN, pK]) in extra blocks: the per-round
+// product P = H W1_H beside the candidate selection.
 hipError_t launch_topm(const float* logits, int rows, int V, int M, float T, uint64_t* chunk_cand,
                        float4* chunk_stat, int32_t* ids, float* vals, float* lse, float* tail,
                        int32_t* tokrank, int32_t* user_ids, float* user_vals, float* user_lse,
-                       hipStream_t stream);
+                       hipStream_t stream, const uint16_t* pA = nullptr, const uint16_t* pBt = nullptr,
+                       float* pC = nullptr, int pN = 0, int pK = 0);
 hipError_t launch_topm_merge(const uint64_t* chunk_cand, const float4* chunk_stat, int rows, int S,
                              int M, float T, int32_t* ids, float* vals, float* lse, float* tail,
                              int32_t* tokrank, int32_t* user_ids, float* user_vals, float* user_lse,

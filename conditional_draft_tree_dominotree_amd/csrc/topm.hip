@@ -131,6 +131,75 @@ __device__ __forceinline__ void chunk_load(const float* __restrict__ src, int le
   }
 }
 
+// The per-round product P = H W1_H (the path-independent half of the
+// correction's first projection: H_d is shared by every path, DominoTree
+// summary, Componenti Core 1), launched as extra blocks in front of the rows
+// of the candidate merge, whose few latency-bound blocks leave the CUs room
+// (in the chunk kernel its registers would cut that kernel's occupancy): one
+// 32 x 32 output tile per block, the four waves splitting K, each keeping the next 64-k step's
+// operand loads (16 bytes a lane, straight from memory) in flight over the
+// current step's MFMAs; the partial tiles are summed in LDS in a fixed order.
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+
+struct PArgs {
+  const uint16_t* A;   // H [M, K] bf16
+  const uint16_t* Bt;  // W1_H^T [N, K] bf16
+  float* C;            // P [M, N] fp32
+  int M, N, K;
+  int blocks;          // output tiles (0: no P blocks)
+};
+
+__device__ __forceinline__ uint4 p_load8(const uint16_t* base, int row, int rows, int k0, int kend, int K) {
+  if (row < rows && k0 < kend) return *reinterpret_cast<const uint4*>(base + (size_t)row * K + k0);
+  return make_uint4(0, 0, 0, 0);
+}
+
+__device__ __forceinline__ void p_tile(const PArgs& pa, int tile, float* part /* [4][1024] */) {
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tn = (pa.N + 31) / 32;
+  const int m0 = (tile / tn) * 32, n0 = (tile % tn) * 32;
+  const int K = pa.K;
+  const int kq = ((K + 15) / 16 + 3) / 4 * 16;  // k per wave, a multiple of 16
+  const int kb = w * kq, ke = min(K, kb + kq);
+  const int ar = m0 + (lane & 31), bc = n0 + (lane & 31), ko = 8 * (lane >> 5);
+  floatx16 acc;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) acc[e] = 0.f;
+  uint4 ca[4], cb[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    ca[q] = p_load8(pa.A, ar, pa.M, kb + 16 * q + ko, ke, K);
+    cb[q] = p_load8(pa.Bt, bc, pa.N, kb + 16 * q + ko, ke, K);
+  }
+  for (int k = kb; k < ke; k += 64) {
+    uint4 na[4], nb[4];  // the next step's operands (past ke: zeros, no access)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      na[q] = p_load8(pa.A, ar, pa.M, k + 64 + 16 * q + ko, ke, K);
+      nb[q] = p_load8(pa.Bt, bc, pa.N, k + 64 + 16 * q + ko, ke, K);
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(&ca[q]),
+                                                    *reinterpret_cast<const bf16x8*>(&cb[q]), acc, 0, 0, 0);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      ca[q] = na[q];
+      cb[q] = nb[q];
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < 16; ++e) part[w * 1024 + (8 * (e >> 2) + 4 * (lane >> 5) + (e & 3)) * 32 + (lane & 31)] = acc[e];
+  __syncthreads();
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int i = tid + 256 * u;
+    const float v = (part[i] + part[1024 + i]) + (part[2048 + i] + part[3072 + i]);
+    const int row = m0 + i / 32, col = n0 + i % 32;
+    if (row < pa.M && col < pa.N) pa.C[(size_t)row * pa.N + col] = v;
+  }
+}
+
 // One block per item.  The selection works on the fp32 values with float
 // compares (a key per element only for the few candidates): per element a
 // max, a compare with the threshold and one exp.
@@ -330,8 +399,12 @@ __global__ __launch_bounds__(TOPM_THREADS) void topm_merge_kernel(
     const uint64_t* __restrict__ cand, const float4* __restrict__ stat, int S, int M, float T,
     int32_t* __restrict__ ids_out, float* __restrict__ vals_out, float* __restrict__ lse_out,
     float* __restrict__ tail_out, int32_t* __restrict__ tokrank_out, int32_t* __restrict__ user_ids,
-    float* __restrict__ user_vals, float* __restrict__ user_lse) {
-  extern __shared__ uint64_t lists[];  // [S][M], then [MERGE_CAP] candidates
+    float* __restrict__ user_vals, float* __restrict__ user_lse, PArgs pa) {
+  extern __shared__ uint64_t lists[];  // [S][M], then [MERGE_CAP] candidates (P tiles: [4][1024] floats)
+  if ((int)blockIdx.x < pa.blocks) {
+    p_tile(pa, blockIdx.x, reinterpret_cast<float*>(lists));
+    return;
+  }
   __shared__ int cnt[DT_TOPM_MAX_CHUNKS];
   __shared__ float mc[DT_TOPM_MAX_CHUNKS], sc[DT_TOPM_MAX_CHUNKS], tc[DT_TOPM_MAX_CHUNKS];
   __shared__ int out_ids[DT_TOPM_MAX];
@@ -341,7 +414,7 @@ __global__ __launch_bounds__(TOPM_THREADS) void topm_merge_kernel(
   __shared__ uint64_t lbound, kth;
 
   const int tid = threadIdx.x;
-  const int row = blockIdx.x;
+  const int row = blockIdx.x - pa.blocks;
   uint64_t* cands = lists + (size_t)S * M;
   const uint64_t* src = cand + (size_t)row * S * M;
   for (int i = tid; i < S * M; i += TOPM_THREADS) lists[i] = src[i];
@@ -485,10 +558,15 @@ __global__ void nan_scan_kernel(const float* __restrict__ x, size_t n, int* __re
 hipError_t launch_topm(const float* logits, int rows, int V, int M, float T, uint64_t* chunk_cand,
                        float4* chunk_stat, int32_t* ids, float* vals, float* lse, float* tail,
                        int32_t* tokrank, int32_t* user_ids, float* user_vals, float* user_lse,
-                       hipStream_t stream) {
+                       hipStream_t stream, const uint16_t* pA, const uint16_t* pBt, float* pC, int pN, int pK) {
   const int S = topm_chunks(V);
   const int items = rows * S;
   if (items == 0) return hipSuccess;
+  PArgs pa{pA, pBt, pC, rows, pN, pK, 0};
+  if (pA) {
+    if (!pBt || !pC || pN < 1 || pK < 8 || pK % 8) return hipErrorInvalidValue;
+    pa.blocks = ((rows + 31) / 32) * ((pN + 31) / 32);
+  }
   const bool vec4 = (V % 4 == 0) && (reinterpret_cast<uintptr_t>(logits) % 16 == 0);
   if (vec4)
     hipLaunchKernelGGL(topm_chunk_kernel<true>, dim3(items), dim3(TOPM_THREADS), 0, stream, logits, V, S, M, T,
@@ -498,8 +576,10 @@ hipError_t launch_topm(const float* logits, int rows, int V, int M, float T, uin
                        chunk_cand, chunk_stat);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  return launch_topm_merge(chunk_cand, chunk_stat, rows, S, M, T, ids, vals, lse, tail, tokrank,
-                           user_ids, user_vals, user_lse, stream);
+  const size_t lds = std::max(((size_t)S * M + MERGE_CAP) * sizeof(uint64_t), pa.blocks ? 4 * 1024 * sizeof(float) : 0);
+  hipLaunchKernelGGL(topm_merge_kernel, dim3(pa.blocks + rows), dim3(TOPM_THREADS), lds, stream, chunk_cand,
+                     chunk_stat, S, M, T, ids, vals, lse, tail, tokrank, user_ids, user_vals, user_lse, pa);
+  return hipGetLastError();
 }
 
 hipError_t launch_topm_merge(const uint64_t* chunk_cand, const float4* chunk_stat, int rows, int S,
@@ -508,7 +588,7 @@ hipError_t launch_topm_merge(const uint64_t* chunk_cand, const float4* chunk_sta
                              hipStream_t stream) {
   const size_t lds = ((size_t)S * M + MERGE_CAP) * sizeof(uint64_t);
   hipLaunchKernelGGL(topm_merge_kernel, dim3(rows), dim3(TOPM_THREADS), lds, stream, chunk_cand,
-                     chunk_stat, S, M, T, ids, vals, lse, tail, tokrank, user_ids, user_vals, user_lse);
+                     chunk_stat, S, M, T, ids, vals, lse, tail, tokrank, user_ids, user_vals, user_lse, PArgs{});
   return hipGetLastError();
 }
 

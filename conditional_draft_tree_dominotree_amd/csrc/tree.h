@@ -77,7 +77,8 @@ constexpr uint32_t TREE_EPOCH_LIMIT = 1u << 27;  // mailbox words hold the epoch
 // are the caller's.
 // `halves`: 1 or 2 forces the split of the batch, 0 = automatic (2 for register
 // workers with at least 2 requests whose first half fills whole 16-column blocks).
-size_t plan_tree(TreeArgs& a, int wdtype_bf16, int pops, int max_workers, int lds_workers, int halves);
+size_t plan_tree(TreeArgs& a, int wdtype_bf16, int pops, int max_workers, int lds_workers, int halves,
+                 int ctl_advance);
 hipError_t launch_tree(const TreeArgs& a, int wdtype_bf16, size_t lds_bytes, hipStream_t stream);
 
 }  // namespace dt

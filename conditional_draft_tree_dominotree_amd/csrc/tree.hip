@@ -1964,7 +1964,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 // ---------------------------------------------------------------------------
 // host side: schedule and launch
 
-size_t plan_tree(TreeArgs& a, int wdtype_bf16, int pops, int max_workers, int lds_workers, int halves) {
+size_t plan_tree(TreeArgs& a, int wdtype_bf16, int pops, int max_workers, int lds_workers, int halves,
+                 int ctl_advance) {
   const int esz = wdtype_bf16 ? 2 : 4;
   const size_t lds_max = 160 * 1024;
   const int kp = k_padded(a.ds);
@@ -2021,7 +2022,7 @@ size_t plan_tree(TreeArgs& a, int wdtype_bf16, int pops, int max_workers, int ld
     a.ncbmax = ncb;
     a.halves = hv;
     a.bh = hv == 2 ? bh2 : a.B;
-    a.wadv = regw ? 1 : 0;
+    a.wadv = regw && !ctl_advance ? 1 : 0;
     a.n_workers = n_workers;
     a.qmax = qmax;
     a.xcap = xcap;

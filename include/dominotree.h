@@ -213,6 +213,9 @@ typedef struct {
                                workers fit; 0: default */
   int32_t tiles_per_worker; /* LDS-staging workers: weight tiles per worker block, 0..64 (default:
                                one per worker when the workers fit beside the controllers) */
+  int32_t advance;          /* who advances the GRU states of a step's nodes beside register-resident
+                               workers: 0 (default) or 1 the workers, 2 the controllers (the
+                               LDS-staging workers always leave it to the controllers) */
 } dt_schedule;
 
 /* Set the schedule the handle's next builds use (NULL restores the defaults).
