@@ -459,6 +459,7 @@ dt_status dt_build_trees(dt_handle* h, const dt_inputs* in, const dt_params* p, 
   a.fullv = p->norm == DT_NORM_FULLV;
   a.act_bf16 = (p->flags & DT_ACT_BF16) != 0;
   a.marginal = (p->flags & DT_MARGINAL) != 0;
+  a.dlfma = h->sched.dl;
   a.n_tiles = h->n_tiles;
   a.tiles_per_worker = choose_tpw(h, B);
   a.n_workers = (h->n_tiles + a.tiles_per_worker - 1) / a.tiles_per_worker;
@@ -508,7 +509,7 @@ dt_status dt_build_trees(dt_handle* h, const dt_inputs* in, const dt_params* p, 
   a.ebase = h->ebase;
   h->ebase += span;
   MARK(4);
-  HIPCHK(dt::launch_tree(a, h->bf16, lds, stream));
+  HIPCHK(dt::launch_tree(a, h->bf16, lds, stream, h->sched.launch == 1));
   MARK(5);
   if (timing) ++h->timed;
 #undef MARK
@@ -565,6 +566,8 @@ dt_status dt_set_schedule(dt_handle* h, const dt_schedule* s) {
   if (s->tiles_per_worker < 0 || s->tiles_per_worker > 64)
     return fail(DT_EINVAL, "tiles_per_worker %d outside 0..64", s->tiles_per_worker);
   if (s->advance < 0 || s->advance > 2) return fail(DT_EINVAL, "advance %d outside 0..2", s->advance);
+  if (s->dl != 0 && s->dl != 1) return fail(DT_EINVAL, "dl must be 0 or 1");
+  if (s->launch < 0 || s->launch > 1) return fail(DT_EINVAL, "launch %d outside 0..1", s->launch);
   h->sched = *s;
   return DT_OK;
 }

@@ -14,6 +14,7 @@ struct TreeArgs {
   int fullv;
   int act_bf16;
   int marginal;         // 1: no correction (dL = 0), the factorised scores of the base logits
+  int dlfma;            // 1: dL with vector FMAs even where the matrix cores could take it
   int n_workers;        // worker blocks; block ids [0, n_workers) are workers
   int tiles_per_worker;
   int n_tiles;          // (3 ds + r) / 16
@@ -79,6 +80,6 @@ constexpr uint32_t TREE_EPOCH_LIMIT = 1u << 27;  // mailbox words hold the epoch
 // workers with at least 2 requests whose first half fills whole 16-column blocks).
 size_t plan_tree(TreeArgs& a, int wdtype_bf16, int pops, int max_workers, int lds_workers, int halves,
                  int ctl_advance);
-hipError_t launch_tree(const TreeArgs& a, int wdtype_bf16, size_t lds_bytes, hipStream_t stream);
+hipError_t launch_tree(const TreeArgs& a, int wdtype_bf16, size_t lds_bytes, hipStream_t stream, bool plain);
 
 }  // namespace dt

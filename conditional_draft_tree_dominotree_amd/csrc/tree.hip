@@ -357,6 +357,8 @@ __device__ __forceinline__ void worker_epilogue_bf16(const TreeArgs& a, const in
             v[3] += bh[row0 + 3];
           }
           st_dev_f32x4(a.gh + slot * gh_stride(a.ds) + row0, v);
+        } else if (row0 >= ds3 && row0 + 3 < ds3 + a.r && (ds3 & 3) == 0 && (a.r & 3) == 0) {
+          st_dev_f32x4(a.u + slot * u_stride(a.r) + (row0 - ds3), s);
         } else {
           for (int q = 0; q < 4; ++q) worker_store_out(a, slot, row0 + q, s[q]);
         }
@@ -778,6 +780,9 @@ __device__ __forceinline__ void worker_regs(const TreeArgs& a, unsigned char* ld
                 o[3] += a.b_hh[row0 + 3];
               }
               st_dev_f32x4(a.gh + slot * gh_stride(a.ds) + row0, o);
+            } else if (row0 >= ds3 && row0 + 3 < ds3 + a.r && (ds3 & 3) == 0 && (a.r & 3) == 0) {
+              // W1_S rows: u, the rows the controller waits for first
+              st_dev_f32x4(a.u + slot * u_stride(a.r) + (row0 - ds3), sum);
             } else {
               for (int q = 0; q < 4; ++q) worker_store_out(a, slot, row0 + q, sum[q]);
             }
@@ -854,7 +859,8 @@ struct CtlLds {
   int* pn;              // [p*k] their insertion points in the frontier
   unsigned char* w2s;   // [nslots][M][r + pad] W2 rows of the candidates of each slot's depth
   float* ps;            // [nslots][r] P rows
-  float* av;            // [p][r] SiLU(u + P)
+  float* av;            // [p][r] SiLU(u + P); bf16 weights with r % 32 == 0: three bf16 pieces
+                        // [3][p][av_stride(r)] (hi, mid, lo) whose sum is SiLU(u + P)
 };
 
 enum { L_FIXED, L_CAND, L_TAIL, L_REC, L_RRANK, L_TREC, L_FRONT, L_NC, L_NCS, L_PN, L_W2S, L_PS, L_AV, L_COUNT };
@@ -862,6 +868,13 @@ enum { L_FIXED, L_CAND, L_TAIL, L_REC, L_RRANK, L_TREC, L_FRONT, L_NC, L_NCS, L_
 // elements per row of W2 candidate weights: r plus 16 bytes, so that the
 // rows of consecutive candidates start in different banks
 __host__ __device__ inline int w2s_stride(int r, int esz) { return r + 16 / esz; }
+// bf16 elements per node row of the activation pieces (bf16 weights): r plus
+// 16 bytes, so that the rows of the step's nodes start in different banks
+__host__ __device__ inline int av_stride(int r) { return r + 8; }
+// whether the expansions take dL on the matrix cores (bf16 weights)
+__host__ __device__ inline bool dl_on_mfma(const TreeArgs& a, int esz) {
+  return esz == 2 && (a.r & 31) == 0 && !a.marginal && !a.dlfma;
+}
 
 // byte offsets of the controller's arrays; returns the total
 __host__ __device__ inline size_t ctl_offsets(const TreeArgs& a, int esz, size_t* off) {
@@ -879,7 +892,7 @@ __host__ __device__ inline size_t ctl_offsets(const TreeArgs& a, int esz, size_t
   sz[L_PN] = 0;
   sz[L_W2S] = (size_t)a.nslots * a.M * w2s_stride(a.r, esz) * esz;
   sz[L_PS] = (size_t)a.nslots * a.r * 4;
-  sz[L_AV] = P * a.r * 4;
+  sz[L_AV] = dl_on_mfma(a, esz) ? (size_t)3 * P * av_stride(a.r) * 2 : P * a.r * 4;
   size_t o = 0;
   for (int i = 0; i < L_COUNT; ++i) {
     off[i] = o;
@@ -1061,10 +1074,54 @@ template <typename W>
 __device__ __forceinline__ void ctl_expand(const TreeArgs& a, const CtlLds& c, int b, int t, int e) {
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int M = a.M, r = a.r, k = a.k;
+  // dL on the matrix cores (bf16 weights; not needed for marginal scores)
+  const bool mf = dl_on_mfma(a, (int)sizeof(W));
   // a_j = SiLU(u_j + P_{d_j}); the u loads of all nodes are issued first
-  {
-    const int us = u_stride(r);
-    const float* ub = a.u + slot_of(a, t, b, 0) * us;  // the e slots are consecutive
+  const int us = u_stride(r);
+  const float* ub = a.u + slot_of(a, t, b, 0) * us;  // the e slots are consecutive
+  if (mf) {
+    // pairs of elements: item i is node i / (r / 2), elements 2 (i % (r / 2)) + 0, 1;
+    // a thread takes items tid, tid + NT, ..., eight of them a batch (their u
+    // loads issued together), and writes each piece of a pair as one word
+    uint32_t* avw = reinterpret_cast<uint32_t*>(c.av);
+    const int r2 = r >> 1, tot = e * r2, dj = NT / r2, dq = NT - dj * r2;
+    const size_t piece = (size_t)a.p * av_stride(r) / 2;  // words
+    int j = tid / r2, q = tid - j * r2;
+    for (int b0 = 0; b0 < tot; b0 += 8 * NT) {
+      float2 uv[8];
+      int jj[8], qq[8];
+#pragma unroll
+      for (int x = 0; x < 8; ++x) {
+        jj[x] = j;
+        qq[x] = q;
+        if (b0 + x * NT + tid < tot) uv[x] = *reinterpret_cast<const float2*>(ub + (size_t)j * us + 2 * q);
+        q += dq;
+        j += dj;
+        if (q >= r2) {
+          q -= r2;
+          ++j;
+        }
+      }
+      keep_batch();
+#pragma unroll
+      for (int x = 0; x < 8; ++x)
+        if (b0 + x * NT + tid < tot) {
+          const float2 pv = *reinterpret_cast<const float2*>(c.ps + c.f->ex_ws[jj[x]] * r + 2 * qq[x]);
+          const float x0 = uv[x].x + pv.x, x1 = uv[x].y + pv.y;
+          const float v0 = x0 * sigm(x0), v1 = x1 * sigm(x1);
+          // v = hi + mid + lo, each a bf16 (nearest even): the products with
+          // bf16 W2 are exact in fp32
+          const uint16_t h0 = f32_to_bf16(v0), h1 = f32_to_bf16(v1);
+          const float s0 = v0 - bf16_to_f32(h0), s1 = v1 - bf16_to_f32(h1);
+          const uint16_t m0 = f32_to_bf16(s0), m1 = f32_to_bf16(s1);
+          const uint16_t l0 = f32_to_bf16(s0 - bf16_to_f32(m0)), l1 = f32_to_bf16(s1 - bf16_to_f32(m1));
+          uint32_t* o = avw + (size_t)jj[x] * (av_stride(r) / 2) + qq[x];
+          o[0] = (uint32_t)h0 | ((uint32_t)h1 << 16);
+          o[piece] = (uint32_t)m0 | ((uint32_t)m1 << 16);
+          o[2 * piece] = (uint32_t)l0 | ((uint32_t)l1 << 16);
+        }
+    }
+  } else {
     for (int i = tid; i < r; i += NT) {
       float uv[PMAX];
 #pragma unroll
@@ -1080,11 +1137,88 @@ __device__ __forceinline__ void ctl_expand(const TreeArgs& a, const CtlLds& c, i
     }
   }
   __syncthreads();
-  // dL_{j,m} = W2[:, cand_m] . a_j.  bf16 rows: a quad of threads per (node,
-  // 4 candidates), thread h of the quad taking elements 32 i + 8 h .. + 7 of
-  // all four rows (each a_j read serves four rows; a quad reads 64 consecutive
-  // bytes of a row), combined in a fixed order.
-  if (sizeof(W) == 2 && (M & 3) == 0 && (r & 63) == 0) {
+  // dL_{j,m} = W2[:, cand_m] . a_j.
+  if (a.marginal) {
+    // the factorised scores: base logits alone
+    for (int i = tid; i < e * M; i += NT) {
+      const int j = i / M, m = i - j * M;
+      c.f->z[j * 64 + m] = c.cand[c.f->ex_dep[j] * M + m].val / a.T + 0.0f;
+    }
+  } else if (mf) {
+    // On the matrix cores: for each depth slot s in use, the slot's W2
+    // candidate rows [M x r] (A, 16 candidates a block) times the step's
+    // activations [r x 16] (B, column n node n, the columns of nodes of other
+    // slots zero), v_mfma_f32_16x16x32_bf16 over r in 32-k steps, one
+    // accumulator per piece.  Wave w takes the candidate block w % nrb and
+    // every (4 / nrb)-th slot in use from w / nrb on; a node's column thus
+    // sums the products of its own slot only and is written by one wave.
+    const int nrb = (M + 15) >> 4;  // 1..4
+    const int nkp = (NT / WAVE) / nrb;
+    const int rb = wv % nrb, part = wv / nrb;
+    const int n = lane & 15, kq = 8 * (lane >> 4);
+    const int wsn = n < e ? c.f->ex_ws[n] : -1;
+    uint32_t smask = 0;
+    for (int s = 0; s < a.nslots; ++s)
+      if (__ballot(wsn == s)) smask |= 1u << s;
+    const bool mine = wsn >= 0 && __popc(smask & ((1u << wsn) - 1u)) % nkp == part;
+    if (part < nkp) {  // nrb = 3 leaves wave 3 idle
+      // Operand rows past M (A) or of nodes past e (B) are read as they
+      // stand: they only reach output rows and columns that are not kept.
+      const uint16_t* avh = reinterpret_cast<const uint16_t*>(c.av);
+      const int piece = a.p * av_stride(r);
+      const int rs = w2s_stride(r, 2);
+      const uint16_t* arow = avh + (size_t)n * av_stride(r) + kq;
+      const uint16_t* w2b = reinterpret_cast<const uint16_t*>(c.w2s) + (size_t)min(rb * 16 + n, M - 1) * rs + kq;
+      float res[4] = {0.f, 0.f, 0.f, 0.f};
+      int si = 0;
+      for (uint32_t mm = smask; mm; mm &= mm - 1u, ++si) {
+        if (si % nkp != part) continue;
+        const int s = __ffs(mm) - 1;
+        const uint16_t* wrow = w2b + (size_t)s * M * rs;
+        floatx4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = acc0, acc2 = acc0;
+        // two operand sets, X for the even and Y for the odd 32-k steps: a
+        // set is read again while the other set's products run
+        bf16x8 xw, x0, x1, x2, yw, y0, y1, y2;
+        auto ld = [&](int k0, bf16x8& w, bf16x8& o0, bf16x8& o1, bf16x8& o2) {
+          w = *reinterpret_cast<const bf16x8*>(wrow + k0);
+          o0 = *reinterpret_cast<const bf16x8*>(arow + k0);
+          o1 = *reinterpret_cast<const bf16x8*>(arow + piece + k0);
+          o2 = *reinterpret_cast<const bf16x8*>(arow + 2 * piece + k0);
+        };
+        ld(0, xw, x0, x1, x2);
+        if (r > 32) ld(32, yw, y0, y1, y2);
+        for (int k0 = 0; k0 < r; k0 += 64) {
+          acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xw, x0, acc0, 0, 0, 0);
+          acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xw, x1, acc1, 0, 0, 0);
+          acc2 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xw, x2, acc2, 0, 0, 0);
+          if (k0 + 64 < r) ld(k0 + 64, xw, x0, x1, x2);
+          if (k0 + 32 < r) {
+            acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(yw, y0, acc0, 0, 0, 0);
+            acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(yw, y1, acc1, 0, 0, 0);
+            acc2 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(yw, y2, acc2, 0, 0, 0);
+            if (k0 + 96 < r) ld(k0 + 96, yw, y0, y1, y2);
+          }
+        }
+        if (wsn == s) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) res[q] = acc0[q] + (acc1[q] + acc2[q]);
+        }
+      }
+      // lane: node n, candidates rb 16 + 4 (lane >> 4) + q
+      if (mine) {
+        const int dep = c.f->ex_dep[n];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int mc = rb * 16 + 4 * (lane >> 4) + q;
+          if (mc < M) c.f->z[n * 64 + mc] = (c.cand[dep * M + mc].val + res[q]) / a.T + 0.0f;
+        }
+      }
+    }
+  } else if (sizeof(W) == 2 && (M & 3) == 0 && (r & 63) == 0) {
+    // bf16 rows: a quad of threads per (node,
+    // 4 candidates), thread h of the quad taking elements 32 i + 8 h .. + 7 of
+    // all four rows (each a_j read serves four rows; a quad reads 64 consecutive
+    // bytes of a row), combined in a fixed order.
     const int G4 = M >> 2;
     const int rs = w2s_stride(r, 2);
     for (int base = 0; base < e * G4 * 4; base += NT) {
@@ -1122,7 +1256,7 @@ __device__ __forceinline__ void ctl_expand(const TreeArgs& a, const CtlLds& c, i
       }
       const float dl = h == 0 ? acc[0] : h == 1 ? acc[1] : h == 2 ? acc[2] : acc[3];
       const int m = 4 * g + h;
-      if (valid) c.f->z[j * 64 + m] = (c.cand[c.f->ex_dep[j] * M + m].val + (a.marginal ? 0.f : dl)) / a.T + 0.0f;
+      if (valid) c.f->z[j * 64 + m] = (c.cand[c.f->ex_dep[j] * M + m].val + dl) / a.T + 0.0f;
     }
   } else {
     // candidates padded to a power of two so that the index splits are shifts
@@ -1164,7 +1298,7 @@ __device__ __forceinline__ void ctl_expand(const TreeArgs& a, const CtlLds& c, i
         }
       }
       for (int s = 1; s < tpc; s <<= 1) dl += __shfl_xor(dl, s);
-      if (valid && part == 0) c.f->z[j * 64 + m] = (c.cand[c.f->ex_dep[j] * M + m].val + (a.marginal ? 0.f : dl)) / a.T + 0.0f;
+      if (valid && part == 0) c.f->z[j * 64 + m] = (c.cand[c.f->ex_dep[j] * M + m].val + dl) / a.T + 0.0f;
     }
   }
   __syncthreads();
@@ -2038,12 +2172,13 @@ size_t plan_tree(TreeArgs& a, int wdtype_bf16, int pops, int max_workers, int ld
   return 0;
 }
 
-hipError_t launch_tree(const TreeArgs& a, int wdtype_bf16, size_t lds_bytes, hipStream_t stream) {
+hipError_t launch_tree(const TreeArgs& a, int wdtype_bf16, size_t lds_bytes, hipStream_t stream, bool plain) {
   void* args[] = {const_cast<TreeArgs*>(&a)};
   const dim3 grid(a.n_workers + a.B), block(NT);
   const void* fn = wdtype_bf16 ? (const void*)tree_kernel<uint16_t> : (const void*)tree_kernel<float>;
   hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_bytes);
   if (e != hipSuccess) return e;
+  if (plain) return hipLaunchKernel(fn, grid, block, args, lds_bytes, stream);
   return hipLaunchCooperativeKernel(fn, grid, block, args, (unsigned)lds_bytes, stream);
 }
 

@@ -216,6 +216,14 @@ typedef struct {
   int32_t advance;          /* who advances the GRU states of a step's nodes beside register-resident
                                workers: 0 (default) or 1 the workers, 2 the controllers (the
                                LDS-staging workers always leave it to the controllers) */
+  int32_t launch;           /* 0 (default): a cooperative launch, which guarantees that every block of
+                               the builder is resident at once (they wait on each other); 1: a plain
+                               launch, for callers that leave the GPU to the build: if other work kept
+                               some blocks from being resident, the bounded waits end the build with
+                               DT_EDEVICE */
+  int32_t dl;               /* the correction dL = W2[:, candidates]^T a of each expansion: 0 (default)
+                               on the matrix cores where the weights are bf16 and r is a multiple of
+                               32, else with vector FMAs; 1: always with vector FMAs */
 } dt_schedule;
 
 /* Set the schedule the handle's next builds use (NULL restores the defaults).

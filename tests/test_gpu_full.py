@@ -104,6 +104,17 @@ def test_q8b_b32_lds_workers(dev, q8b_builder):
         q8b_builder.set_schedule()
 
 
+def test_q8b_b32_fma_correction(dev, q8b_builder):
+    # the expansions' correction dL with vector FMAs instead of the matrix
+    # cores, at the full shape
+    q8b_builder.set_schedule(dl=1)
+    try:
+        spec, w, req = synth.workload("q8b_b32")
+        _full_case(spec, w, req, q8b_builder, [3, 30])
+    finally:
+        q8b_builder.set_schedule()
+
+
 def test_q8b_b32_fullv_and_smaller_batch_reuse_handle(dev, q8b_builder):
     # the same handle serves a smaller batch and the full-vocabulary normaliser
     spec, w, req = synth.workload("q8b_b32")

@@ -82,6 +82,25 @@ def test_small_bf16(dev, B, M, k, N, ds):
     tb.close()
 
 
+# the correction dL of an expansion: on the matrix cores (bf16, r a multiple of
+# 32; M = 40 leaves a ragged 16-candidate block and takes a wave per node in
+# the softmax) and with vector FMAs (r = 48; or forced by the schedule, which
+# takes the quad-per-four-candidates form at r = 64)
+@pytest.mark.parametrize("r,M,dl", [(96, 40, 0), (32, 16, 0), (48, 16, 0), (64, 16, 1), (64, 40, 1)])
+def test_bf16_correction_paths(dev, r, M, dl):
+    spec = synth.small(f"bf16_dl_{r}_{M}_{dl}", V=4000, D=7, h=64, e=96, ds=1024, r=r, M=M, k=4, N=48,
+                       B=6, wdtype="bf16", group=1700 + r + M + dl, emb_std=0.5)
+    spec, w, req = synth.workload(spec)
+    tb = gu.make_builder(spec, w)
+    tb.set_schedule(dl=dl)
+    got = gu.run(tb, spec, req)
+    reps, trees = gu.compare(spec, w, req, got)
+    print(f"r={r} M={M} dl={dl}", gu.summarize(reps))
+    _assert_ok(reps)
+    gu.check_candidates(spec, trees, got, range(spec.B))
+    tb.close()
+
+
 def test_bf16_register_workers_with_root_and_biases(dev):
     # a given root state: the workers compute step 0's products (with zero
     # roots the controllers set them up and the workers start at step 1)
