@@ -44,5 +44,36 @@ def build(verbose: bool = False) -> str:
     return OUT
 
 
+# host code under AddressSanitizer and UndefinedBehaviorSanitizer (the device
+# code is built as usual, without them); the library then needs the clang ASan
+# runtime preloaded into the process that loads it
+SANITIZE = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+            "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-fno-omit-frame-pointer"]
+
+
+def build_host_sanitized(out_dir: str) -> str:
+    """Compile every source with the host side sanitized (-O1 -g) into
+    out_dir/libdominotree_san.so; returns its path."""
+    os.makedirs(out_dir, exist_ok=True)
+    flags = [f if f != "-O3" else "-O1" for f in FLAGS] + ["-g", *SANITIZE]
+
+    def one(src: str) -> str:
+        obj = os.path.join(out_dir, src.replace(".hip", ".o"))
+        r = subprocess.run([HIPCC, *flags, "-c", os.path.join(CSRC, src), "-o", obj], capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr}")
+        return obj
+
+    jobs = min(len(SOURCES), max(1, min(16, len(os.sched_getaffinity(0)))))
+    with ThreadPoolExecutor(jobs) as ex:
+        objs = list(ex.map(one, SOURCES))
+    out = os.path.join(out_dir, "libdominotree_san.so")
+    r = subprocess.run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", out],
+                       capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed:\n{r.stderr}")
+    return out
+
+
 if __name__ == "__main__":
     build(verbose=True)
