@@ -76,7 +76,7 @@ class VerifyOutputs(C.Structure):
 
 EXPORTS = ["dt_create", "dt_build_trees", "dt_sync_status", "dt_phase_times", "dt_destroy",
            "dt_last_error", "dt_version", "dt_tree_attention_inputs", "dt_draft_chain", "dt_fold_state",
-           "dt_set_schedule", "dt_set_device_error", "dt_draft_chain_noalloc"]
+           "dt_set_schedule", "dt_set_device_error", "dt_draft_chain_noalloc", "dt_draft_chain_sample"]
 _lib = None
 
 
@@ -113,6 +113,9 @@ def load_library():
     lib.dt_draft_chain.restype = C.c_int
     lib.dt_draft_chain.argtypes = [C.c_void_p, C.POINTER(Inputs), C.c_uint32, C.c_void_p, C.c_void_p,
                                    C.c_void_p]
+    lib.dt_draft_chain_sample.restype = C.c_int
+    lib.dt_draft_chain_sample.argtypes = [C.c_void_p, C.POINTER(Inputs), C.c_uint32, C.c_float, C.c_uint64,
+                                          C.c_void_p, C.c_void_p, C.c_void_p]
     lib.dt_draft_chain_noalloc.restype = C.c_int
     lib.dt_draft_chain_noalloc.argtypes = [C.c_void_p, C.POINTER(Inputs), C.c_uint32, C.c_void_p, C.c_void_p,
                                            C.c_void_p]
@@ -176,6 +179,13 @@ def dt_destroy(handle: int):
 def dt_draft_chain(handle: int, inputs: Inputs, flags: int, tokens: int, logits, stream: int = 0):
     _check(load_library().dt_draft_chain(C.c_void_p(handle), C.byref(inputs), C.c_uint32(flags),
                                          C.c_void_p(tokens), C.c_void_p(logits), C.c_void_p(stream)))
+
+
+def dt_draft_chain_sample(handle: int, inputs: Inputs, flags: int, temperature: float, seed: int, tokens: int,
+                          logits, stream: int = 0):
+    _check(load_library().dt_draft_chain_sample(C.c_void_p(handle), C.byref(inputs), C.c_uint32(flags),
+                                                C.c_float(temperature), C.c_uint64(seed), C.c_void_p(tokens),
+                                                C.c_void_p(logits), C.c_void_p(stream)))
 
 
 def dt_draft_chain_noalloc(handle: int, inputs: Inputs, flags: int, tokens: int, logits, stream: int = 0):
@@ -351,9 +361,12 @@ class TreeBuilder:
         dt_build_trees(self.handle, inp, prm, outs, self.stream.cuda_stream)
         return o
 
-    def chain(self, hidden, base_logits=None, root_state=None, *, flags=None, out=None):
-        """Enqueue the greedy chain head (dt_draft_chain) on the builder's
-        stream; returns {"tokens": [b, D] int32, "logits": [b, D] float32}."""
+    def chain(self, hidden, base_logits=None, root_state=None, *, flags=None, out=None, temperature=None,
+              seed=0):
+        """Enqueue the chain head on the builder's stream: greedy
+        (dt_draft_chain) when temperature is None, else sampled at that
+        temperature with the given seed (dt_draft_chain_sample); returns
+        {"tokens": [b, D] int32, "logits": [b, D] float32}."""
         torch = self.torch
         if flags is None:
             flags = DT_ACT_BF16 if self.wdtype == DT_BF16 else 0
@@ -365,8 +378,12 @@ class TreeBuilder:
         _check_tensor("output tokens", o.get("tokens"), torch.int32, (b, D), self.device)
         _check_tensor("output logits", o.get("logits"), torch.float32, (b, D), self.device, optional=True)
         inp = Inputs(b, _ptr(base_logits), _ptr(hidden), _ptr(root_state))
-        dt_draft_chain(self.handle, inp, flags, _ptr(o["tokens"]), _ptr(o.get("logits")),
-                       self.stream.cuda_stream)
+        if temperature is None:
+            dt_draft_chain(self.handle, inp, flags, _ptr(o["tokens"]), _ptr(o.get("logits")),
+                           self.stream.cuda_stream)
+        else:
+            dt_draft_chain_sample(self.handle, inp, flags, float(temperature), int(seed), _ptr(o["tokens"]),
+                                  _ptr(o.get("logits")), self.stream.cuda_stream)
         return o
 
     def fold_state(self, tokens, prev_state=None, *, flags=None, out=None):

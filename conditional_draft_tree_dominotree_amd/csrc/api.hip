@@ -608,10 +608,18 @@ dt_status chain_check(const dt_handle* h, const dt_inputs* in, uint32_t flags, c
   return DT_OK;
 }
 
+// Sampling parameters of a chain (sample 0: the greedy pick)
+struct ChainDraw {
+  int sample = 0;
+  float temperature = 1.f;
+  uint64_t seed = 0;
+};
+
 // The chain head on a given workspace (P [B D, r], gu [B, 3 ds + r], s [B, ds],
 // s_op [B, ds], part [B, chain blocks]): P = H W1_H, then the positions.
 dt_status chain_run(const dt_handle* h, const dt_inputs* in, const float* base, int32_t* tokens, float* logits,
-                    float* P, float* gu, float* s, void* s_op, uint64_t* part, hipStream_t stream) {
+                    float* P, float* gu, float* s, void* s_op, uint64_t* part, hipStream_t stream,
+                    const ChainDraw& draw = ChainDraw{}) {
   const dt_dims& d = h->dims;
   const int rows = in->batch * d.depths;
   // P = H W1_H for every position (the path-independent half of W1 [H_d; S])
@@ -642,7 +650,28 @@ dt_status chain_run(const dt_handle* h, const dt_inputs* in, const float* base, 
   c.part = part;
   c.tokens = tokens;
   c.logits = logits;
+  c.sample = draw.sample;
+  c.temperature = draw.temperature;
+  c.key0 = (uint32_t)(draw.seed & 0xFFFFFFFFu);
+  c.key1 = (uint32_t)(draw.seed >> 32);
   HIPCHK(dt::launch_chain(c, stream));
+  return DT_OK;
+}
+
+// The base logits of a chain call: the caller's, or H W_lm into the handle's
+// logits workspace
+dt_status chain_base(dt_handle* h, const dt_inputs* in, hipStream_t stream, const float** base) {
+  const dt_dims& d = h->dims;
+  const int V = d.vocab, rows = in->batch * d.depths;
+  if (!in->base_logits) {
+    if (h->wlm_tiled)
+      HIPCHK(dt::launch_gemm_bf16_btiled((const uint16_t*)in->hidden, (const uint16_t*)h->wlm_t, h->logits, rows, V,
+                                         d.hidden, V, h->a_tiles, stream));
+    else
+      HIPCHK(dt::launch_gemm_bf16((const uint16_t*)in->hidden, nullptr, (const uint16_t*)h->wlm_t, nullptr,
+                                  h->logits, rows, V, d.hidden, V, stream));
+  }
+  *base = in->base_logits ? in->base_logits : h->logits;
   return DT_OK;
 }
 
@@ -654,19 +683,27 @@ dt_status dt_draft_chain(dt_handle* h, const dt_inputs* in, uint32_t flags, int3
                          void* stream_) {
   dt_status st = chain_check(h, in, flags, tokens);
   if (st != DT_OK) return st;
-  const dt_dims& d = h->dims;
   hipStream_t stream = reinterpret_cast<hipStream_t>(stream_);
-  const int V = d.vocab, rows = in->batch * d.depths;
-  if (!in->base_logits) {
-    if (h->wlm_tiled)
-      HIPCHK(dt::launch_gemm_bf16_btiled((const uint16_t*)in->hidden, (const uint16_t*)h->wlm_t, h->logits, rows, V,
-                                         d.hidden, V, h->a_tiles, stream));
-    else
-      HIPCHK(dt::launch_gemm_bf16((const uint16_t*)in->hidden, nullptr, (const uint16_t*)h->wlm_t, nullptr,
-                                  h->logits, rows, V, d.hidden, V, stream));
-  }
-  return chain_run(h, in, in->base_logits ? in->base_logits : h->logits, tokens, logits, h->P, h->chain_gu,
-                   h->chain_s, h->chain_sop, h->chain_part, stream);
+  const float* base = nullptr;
+  if ((st = chain_base(h, in, stream, &base)) != DT_OK) return st;
+  return chain_run(h, in, base, tokens, logits, h->P, h->chain_gu, h->chain_s, h->chain_sop, h->chain_part, stream);
+}
+
+dt_status dt_draft_chain_sample(dt_handle* h, const dt_inputs* in, uint32_t flags, float temperature, uint64_t seed,
+                                int32_t* tokens, float* logits, void* stream_) {
+  dt_status st = chain_check(h, in, flags, tokens);
+  if (st != DT_OK) return st;
+  if (!(temperature > 0.f) || !std::isfinite(temperature))
+    return fail(DT_EINVAL, "temperature %g is not positive and finite", (double)temperature);
+  hipStream_t stream = reinterpret_cast<hipStream_t>(stream_);
+  const float* base = nullptr;
+  if ((st = chain_base(h, in, stream, &base)) != DT_OK) return st;
+  ChainDraw draw;
+  draw.sample = 1;
+  draw.temperature = temperature;
+  draw.seed = seed;
+  return chain_run(h, in, base, tokens, logits, h->P, h->chain_gu, h->chain_s, h->chain_sop, h->chain_part, stream,
+                   draw);
 }
 
 dt_status dt_draft_chain_noalloc(dt_handle* h, const dt_inputs* in, uint32_t flags, int32_t* tokens, float* logits,

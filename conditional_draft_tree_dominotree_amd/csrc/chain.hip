@@ -1,9 +1,13 @@
-// Greedy Domino chain head over the whole vocabulary: for each draft position
+// Domino chain head over the whole vocabulary: for each draft position
 // d = 1..D, dL = W2 SiLU(W1 [H_d; S]) on every token, the pick
 // x_d = argmax(base_d + dL) (ties to the lowest id), then S <- GRU(S, E[x_d])
 // ("Domino：在投机解码中将因果建模与自回归草稿解耦", 核心方法 and 方法步骤详情:
 // the head corrects each position's block-parallel base logits with a GRU
-// state advanced from the previously drafted token).
+// state advanced from the previously drafted token, each token sampled from
+// the refined logits).  Sampled chains rank (base + dL) / T + g instead, g a
+// standard Gumbel variate per (request, position, token) from a seeded
+// Philox4x32-10 stream: the Gumbel-max rule draws x_d from
+// softmax((base + dL) / T).
 //
 // Per position, three launches on the caller's stream:
 //   1. [W_hh S~ | W1_S^T S~] for the batch (the dense-product kernels), S~ the
@@ -24,6 +28,39 @@
 namespace dt {
 
 constexpr int CT = 256;  // threads per block (one vocabulary row each)
+
+// Philox4x32-10 (Salmon, Moraes, Dror and Shaw, "Parallel random numbers: as
+// easy as 1, 2, 3", SC 2011): ten rounds, each multiplying words 0 and 2 by
+// the two round constants and forming (hi(M1 c2) ^ c1 ^ k0, lo(M1 c2),
+// hi(M0 c0) ^ c3 ^ k1, lo(M0 c0)); the key advances by the two Weyl
+// increments between rounds.
+__device__ __forceinline__ uint4 philox4x32_10(uint4 c, uint32_t k0, uint32_t k1) {
+#pragma unroll
+  for (int i = 0; i < 10; ++i) {
+    if (i) {
+      k0 += 0x9E3779B9u;
+      k1 += 0xBB67AE85u;
+    }
+    const uint32_t lo0 = 0xD2511F53u * c.x, hi0 = __umulhi(0xD2511F53u, c.x);
+    const uint32_t lo1 = 0xCD9E8D57u * c.z, hi1 = __umulhi(0xCD9E8D57u, c.z);
+    c = make_uint4(hi1 ^ c.y ^ k0, lo1, hi0 ^ c.w ^ k1, lo0);
+  }
+  return c;
+}
+
+// The noise of token v at position d of request row b is word v % 4 of
+// Philox4x32-10 at counter (v / 4, d, b, 0); u = (w / 2^9 + 1/2) / 2^23 (an
+// odd multiple of 2^-24 in (0, 1), exact in fp32) and g = -ln(-ln u).
+__device__ __forceinline__ uint4 chain_noise_words(int v4, int d, int b, uint32_t k0, uint32_t k1) {
+  return philox4x32_10(make_uint4((uint32_t)v4, (uint32_t)d, (uint32_t)b, 0u), k0, k1);
+}
+__device__ __forceinline__ float gumbel_of(uint32_t w) {
+  const float u = (float)(w >> 9) * 0x1p-23f + 0x1p-24f;
+  return -logf(-logf(u));
+}
+__device__ __forceinline__ uint32_t word_of(const uint4& w, int i) {
+  return i == 0 ? w.x : i == 1 ? w.y : i == 2 ? w.z : w.w;
+}
 
 // Row pieces of 8 elements held in registers at once: a whole bf16 row of
 // rank <= 256 (32 x 16 bytes; half of it with 32 requests), an fp32 row 64
@@ -64,7 +101,8 @@ __global__ __launch_bounds__(CT) void chain_correct_kernel(const T* __restrict__
                                                            const float* __restrict__ P,
                                                            const float* __restrict__ gu, int B, int D, int d,
                                                            int V, int r, int gstride, int goff,
-                                                           uint64_t* __restrict__ part) {
+                                                           uint64_t* __restrict__ part, int sample, float temp,
+                                                           uint32_t k0, uint32_t k1) {
   typedef typename RowPiece<T>::type Piece;
   // 32 accumulators leave room for half a bf16 row at a time
   constexpr int CH = (NB >= 32 && RowPiece<T>::CHUNK > 128) ? 128 : RowPiece<T>::CHUNK;
@@ -112,11 +150,13 @@ __global__ __launch_bounds__(CT) void chain_correct_kernel(const T* __restrict__
       }
     }
   }
-  // per request: the block's best (corrected logit desc, token asc)
+  // per request: the block's best (corrected logit desc, token asc; when
+  // sampling, the perturbed score)
 #pragma unroll
   for (int b = 0; b < NB; ++b) {
     if (b < B) {
-      const float z = base[((size_t)b * D + d) * V + vr] + acc[b];
+      float z = base[((size_t)b * D + d) * V + vr] + acc[b];
+      if (sample) z = z / temp + gumbel_of(word_of(chain_noise_words(vr >> 2, d, b, k0, k1), vr & 3));
       const uint64_t m = wave_max_u64(v < V ? cand_pack(f32_key(z), (uint32_t)v) : 0ull);
       if (lane == 0) wbest[wv][b] = m;
     }
@@ -151,7 +191,8 @@ __global__ __launch_bounds__(CT) void chain_correct_mfma_kernel(const uint16_t* 
                                                                 const float* __restrict__ P,
                                                                 const float* __restrict__ gu, int B, int D, int d,
                                                                 int V, int r, int gstride, int goff,
-                                                                uint64_t* __restrict__ part) {
+                                                                uint64_t* __restrict__ part, int sample,
+                                                                float temp, uint32_t k0, uint32_t k1) {
   __shared__ __attribute__((aligned(16))) uint16_t ahi[32 * AROW];
   __shared__ __attribute__((aligned(16))) uint16_t alo[32 * AROW];
   __shared__ uint64_t wbest[CT / 64][32];
@@ -237,12 +278,17 @@ __global__ __launch_bounds__(CT) void chain_correct_mfma_kernel(const uint16_t* 
       for (int g = 0; g < 4; ++g) {
         const float4 bv = *reinterpret_cast<const float4*>(&bs[fr * 36 + 8 * g + 4 * (lane >> 5)]);
         const float bb[4] = {bv.x, bv.y, bv.z, bv.w};
+        // the four rows are the tokens of one noise counter
+        uint4 nw = make_uint4(0u, 0u, 0u, 0u);
+        if (sample) nw = chain_noise_words((v0 + 8 * g + 4 * (lane >> 5)) >> 2, d, fr, k0, k1);
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const int e = 4 * g + q;
           const int v = v0 + 8 * g + 4 * (lane >> 5) + q;
           if (v < V) {
-            const uint64_t c = cand_pack(f32_key(bb[q] + acc[e]), (uint32_t)v);
+            float z = bb[q] + acc[e];
+            if (sample) z = z / temp + gumbel_of(word_of(nw, q));
+            const uint64_t c = cand_pack(f32_key(z), (uint32_t)v);
             best = c > best ? c : best;
           }
         }
@@ -285,15 +331,21 @@ __device__ __forceinline__ void gru_advance(const float* __restrict__ gi, const 
   }
 }
 
+// The pick of request b (one block each): the largest block composite; then,
+// for a sampled chain, the pick's corrected logit base + W2[:, x] . a
+// recomputed (the composite holds its perturbed score); then the state.
 template <typename T>
 __global__ __launch_bounds__(CT) void chain_pick_kernel(const uint64_t* __restrict__ part, int nblk, int V,
                                                         const float* __restrict__ G, const float* __restrict__ gu,
                                                         const float* __restrict__ b_hh, int gstride, int ds,
                                                         int D, int d, int advance, float* __restrict__ s,
                                                         T* __restrict__ s_op, int32_t* __restrict__ tokens,
-                                                        float* __restrict__ logits) {
+                                                        float* __restrict__ logits, int sample,
+                                                        const T* __restrict__ w2t, const float* __restrict__ base,
+                                                        const float* __restrict__ P, int r, int goff) {
   __shared__ uint64_t wm[CT / 64];
   __shared__ uint64_t pick;
+  __shared__ float wsum[CT / 64];
   const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   uint64_t m = 0ull;
   for (int i = tid; i < nblk; i += CT) {
@@ -308,9 +360,25 @@ __global__ __launch_bounds__(CT) void chain_pick_kernel(const uint64_t* __restri
     for (int w = 1; w < CT / 64; ++w) x = wm[w] > x ? wm[w] : x;
     pick = x;
     tokens[(size_t)b * D + d] = (int32_t)cand_id(x);
-    if (logits) logits[(size_t)b * D + d] = key_f32(cand_key(x));
+    if (logits && !sample) logits[(size_t)b * D + d] = key_f32(cand_key(x));
   }
   __syncthreads();
+  if (sample && logits) {
+    const size_t x = min(cand_id(pick), (uint32_t)(V - 1));
+    float acc = 0.f;
+    for (int j = tid; j < r; j += CT) {
+      const float u = P[((size_t)b * D + d) * r + j] + gu[(size_t)b * gstride + goff + j];
+      float w;
+      if constexpr (sizeof(T) == 2) w = bf16_to_f32(w2t[x * r + j]);
+      else w = w2t[x * r + j];
+      acc = fmaf(w, u / (1.f + expf(-u)), acc);
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) acc += __shfl_xor(acc, o);
+    if (lane == 0) wsum[wv] = acc;
+    __syncthreads();
+    if (tid == 0) logits[(size_t)b * D + d] = base[((size_t)b * D + d) * V + x] + ((wsum[0] + wsum[1]) + (wsum[2] + wsum[3]));
+  }
   if (!advance) return;
   gru_advance<T>(G + (size_t)min(cand_id(pick), (uint32_t)(V - 1)) * 3 * ds, gu + (size_t)b * gstride, b_hh, ds,
                  s + (size_t)b * ds, s_op + (size_t)b * ds, nullptr);
@@ -420,10 +488,12 @@ hipError_t launch_chain(const ChainArgs& c, hipStream_t stream) {
     // 2. corrected logits of every token, block-wise best per request
 #define CHAIN_CORRECT(T, NB)                                                                                  \
   hipLaunchKernelGGL((chain_correct_kernel<T, NB>), dim3(nblk), dim3(CT), 0, stream, (const T*)c.w2t, c.base, \
-                     c.P, c.gu, c.B, c.D, d, c.V, c.r, gstride, goff, c.part)
+                     c.P, c.gu, c.B, c.D, d, c.V, c.r, gstride, goff, c.part, c.sample, c.temperature, c.key0,  \
+                     c.key1)
     if (c.w2f) {
       hipLaunchKernelGGL(chain_correct_mfma_kernel, dim3(chain_mfma_blocks(c.V)), dim3(CT), 0, stream,
-                         (const uint16_t*)c.w2f, c.base, c.P, c.gu, c.B, c.D, d, c.V, c.r, gstride, goff, c.part);
+                         (const uint16_t*)c.w2f, c.base, c.P, c.gu, c.B, c.D, d, c.V, c.r, gstride, goff, c.part,
+                         c.sample, c.temperature, c.key0, c.key1);
     } else if (c.bf16) {
       if (c.B <= 4) CHAIN_CORRECT(uint16_t, 4);
       else if (c.B <= 8) CHAIN_CORRECT(uint16_t, 8);
@@ -443,10 +513,12 @@ hipError_t launch_chain(const ChainArgs& c, hipStream_t stream) {
     const int np = c.w2f ? chain_mfma_blocks(c.V) : nblk;
     if (c.bf16)
       hipLaunchKernelGGL(chain_pick_kernel<uint16_t>, dim3(c.B), dim3(CT), 0, stream, c.part, np, c.V, c.G, c.gu,
-                         c.b_hh, gstride, c.ds, c.D, d, adv, c.s, (uint16_t*)c.s_op, c.tokens, c.logits);
+                         c.b_hh, gstride, c.ds, c.D, d, adv, c.s, (uint16_t*)c.s_op, c.tokens, c.logits, c.sample,
+                         (const uint16_t*)c.w2t, c.base, c.P, c.r, goff);
     else
       hipLaunchKernelGGL(chain_pick_kernel<float>, dim3(c.B), dim3(CT), 0, stream, c.part, np, c.V, c.G, c.gu,
-                         c.b_hh, gstride, c.ds, c.D, d, adv, c.s, (float*)c.s_op, c.tokens, c.logits);
+                         c.b_hh, gstride, c.ds, c.D, d, adv, c.s, (float*)c.s_op, c.tokens, c.logits, c.sample,
+                         (const float*)c.w2t, c.base, c.P, c.r, goff);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

@@ -93,6 +93,12 @@ struct ChainArgs {
   uint64_t* part;       // [B, chain_blocks(V)] workspace
   int32_t* tokens;      // [B, D]
   float* logits;        // [B, D] or null
+  // sampling: each position's token drawn by the Gumbel-max rule at
+  // temperature `temperature`, the noise from Philox4x32-10 under key
+  // (key0, key1); 0: the greedy pick
+  int sample;
+  float temperature;
+  uint32_t key0, key1;
 };
 int chain_blocks(int V);       // blocks of the fp32 correction (one vocabulary row per thread)
 int chain_mfma_blocks(int V);  // blocks of the bf16 MFMA correction

@@ -270,6 +270,26 @@ dt_status dt_phase_times(dt_handle* h, float* ms, int n, int32_t* count);
 dt_status dt_draft_chain(dt_handle* h, const dt_inputs* in, uint32_t flags, int32_t* tokens, float* logits,
                          void* stream);
 
+/* ---- Sampled chain head --------------------------------------------------
+ * The chain with each draft token sampled from the refined logits at
+ * temperature T [Domino, Steps: at inference each draft token is sampled from
+ * the final logits l_i + c_i], i.e. from softmax((base_d + dL_d) / T), by the
+ * Gumbel-max rule:
+ *   x_d = argmax_v ((base_d + dL_d)_v / T + g_{b,d,v})   (ties to the lowest id),
+ *   g = -ln(-ln u),  u = (floor(w / 2^9) + 1/2) / 2^23,
+ *   w = word (v mod 4) of Philox4x32-10 (Salmon et al., SC 2011) at counter
+ *       (floor(v / 4), d, b, 0) under key (seed mod 2^32, floor(seed / 2^32)),
+ * with b the request's row in the call and d the 0-based position; then
+ * S <- GRU(S, E[x_d]) as in the greedy chain.  The seed fixes every draw:
+ * the same seed and inputs give the same tokens; use a new seed for each
+ * call that should draw afresh.  Arguments, workspace and outputs as for
+ * dt_draft_chain (logits: the corrected logit base + dL of each pick, not its
+ * perturbed score).
+ * Errors: as dt_draft_chain, and DT_EINVAL for a temperature that is not
+ * positive and finite (T = 0 is the greedy chain). */
+dt_status dt_draft_chain_sample(dt_handle* h, const dt_inputs* in, uint32_t flags, float temperature,
+                                uint64_t seed, int32_t* tokens, float* logits, void* stream);
+
 /* ---- Allocation-free chain head ------------------------------------------
  * For callers that cannot allocate device memory during a call: code under
  * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.

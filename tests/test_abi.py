@@ -115,6 +115,8 @@ def test_tree_attention_argument_errors(lib, view, out, code):
 def test_chain_null_arguments_are_einval(lib):
     assert lib.dt_draft_chain(None, None, 0, None, None, None) == binding.DT_EINVAL
     assert "required" in pkg.dt_last_error()
+    assert lib.dt_draft_chain_sample(None, None, 0, 1.0, 1, None, None, None) == binding.DT_EINVAL
+    assert "required" in pkg.dt_last_error()
 
 
 def test_fold_null_arguments_are_einval(lib):

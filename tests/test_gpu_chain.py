@@ -183,3 +183,97 @@ def test_small_bf16_odd_vocab(dev, B, V):
     exact, ties = compare(spec, w, req, got, range(B))
     assert exact + ties == B, (exact, ties)
     assert exact >= B - 1, (exact, ties)
+
+
+# ---- sampled chain (dt_draft_chain_sample) ---------------------------------
+
+def compare_sampled(spec, w, req, got, requests, T, seed, base=None):
+    """As compare(), against the oracle's Gumbel-max chain with the same seed:
+    a pick may differ only where the oracle's perturbed scores had a
+    runner-up within the float tolerance scaled by 1 / T."""
+    bf16 = spec.wdtype == "bf16"
+    tol = gu.TOL_BF16 if bf16 else gu.TOL_F32
+    head = ref.make_head(w, bf16, spec.act_bf16)
+    exact, ties = 0, 0
+    for b in requests:
+        hid = ref.hidden_values(req["hidden"][b], bf16)
+        bl = base[b] if base is not None else req["base"][b]
+        toks, logits, margins = chain.sampled_chain(head, bl, hid, req["root"][b], T, seed, b)
+        for d in range(spec.D):
+            if got["tokens"][b, d] != toks[d]:
+                assert margins[d] < tol / T + 1e-5, (b, d, got["tokens"][b, d], toks[d], margins[d])
+                ties += 1
+                break
+            assert abs(float(got["logits"][b, d]) - logits[d]) <= tol, (b, d, got["logits"][b, d], logits[d])
+        else:
+            exact += 1
+    return exact, ties
+
+
+def run_sampled(tb, spec, req, T, seed):
+    hidden = gu.to_dev(req["hidden"])
+    root = gu.to_dev(req["root"]) if spec.root_std > 0 else None
+    o = tb.chain(hidden, gu.to_dev(req["base"]), root, temperature=T, seed=seed)
+    tb.sync_status()
+    return {k: v.cpu().numpy() for k, v in o.items()}
+
+
+@pytest.mark.parametrize("T,seed", [(1.0, 7), (0.5, 2 ** 40 + 3)])
+def test_sampled_tiny(dev, T, seed):
+    spec, w, req = synth.workload("tiny")
+    tb = gu.make_builder(spec, w)
+    got = run_sampled(tb, spec, req, T, seed)
+    again = run_sampled(tb, spec, req, T, seed)
+    greedy = run_chain(tb, spec, req)
+    tb.close()
+    np.testing.assert_array_equal(got["tokens"], again["tokens"])
+    exact, ties = compare_sampled(spec, w, req, got, range(spec.B), T, seed)
+    assert exact == spec.B, (exact, ties)
+    assert not np.array_equal(got["tokens"], greedy["tokens"])
+
+
+@pytest.mark.parametrize("B,wdtype", [(9, "f32"), (32, "f32"), (5, "bf16"), (32, "bf16")])
+def test_sampled_small_batches(dev, B, wdtype):
+    # both correction kernels (fp32 rows; bf16 on the matrix cores), a
+    # vocabulary that is not a multiple of 4, random root states; the row
+    # index of each request keys its noise
+    bf16 = wdtype == "bf16"
+    kw = dict(h=64, e=96, ds=128, r=64, wdtype="bf16", emb_std=0.5) if bf16 else dict(h=32, e=24, ds=64, r=32)
+    spec = synth.small(f"chain_smp_{B}_{wdtype}", group=900 + B + 50 * bf16, V=4001, D=5, M=8, k=2, N=10, B=B,
+                       root_std=0.5, **kw)
+    spec, w, req = synth.workload(spec)
+    tb = gu.make_builder(spec, w)
+    got = run_sampled(tb, spec, req, 0.8, 1234)
+    other = run_sampled(tb, spec, req, 0.8, 1235)
+    tb.close()
+    exact, ties = compare_sampled(spec, w, req, got, range(B), 0.8, 1234)
+    print(f"B={B} {wdtype}: {exact}/{B} sampled chains exact, near-ties {ties}")
+    assert exact + ties == B and exact >= B - 1, (exact, ties)
+    assert not np.array_equal(got["tokens"], other["tokens"])
+
+
+def test_sampled_full_shape(dev):
+    spec, w, req = synth.workload("q8b_b32")
+    tb = gu.make_builder(spec, w)
+    got = run_sampled(tb, spec, req, 1.0, 99)
+    tb.close()
+    assert np.all((got["tokens"] >= 0) & (got["tokens"] < spec.V))
+    sample = [0, 13, 31]
+    exact, ties = compare_sampled(spec, w, req, got, sample, 1.0, 99)
+    print(f"q8b_b32 sampled: {exact}/{len(sample)} exact, near-ties {ties}")
+    assert exact + ties == len(sample)
+
+
+def test_sampled_refuses_bad_temperature(dev):
+    import torch
+
+    import conditional_draft_tree_dominotree_amd as pkg
+    spec, w, req = synth.workload("tiny")
+    tb = gu.make_builder(spec, w)
+    hidden, base = gu.to_dev(req["hidden"]), gu.to_dev(req["base"])
+    for T in (0.0, -1.0, float("inf"), float("nan")):
+        with pytest.raises(pkg.DtError) as ei:
+            tb.chain(hidden, base, temperature=T, seed=1)
+        assert ei.value.status == pkg.binding.DT_EINVAL
+    torch.cuda.synchronize()
+    tb.close()
