@@ -392,6 +392,40 @@ def main():
         torch.cuda.synchronize()
         tb.sync_status()
         chain_ms[f"batch_{cb}"] = c0.elapsed_time(c1) / args.steps
+    # the sampled chain (Gumbel-max at T = 1) for the whole batch
+    co = tb.chain(hidden, base, temperature=1.0, seed=1)
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    c0.record(stream)
+    for i in range(args.steps):
+        tb.chain(hidden, base, out=co, temperature=1.0, seed=2 + i)
+    c1.record(stream)
+    torch.cuda.synchronize()
+    tb.sync_status()
+    chain_ms[f"sampled_batch_{spec.B}"] = c0.elapsed_time(c1) / args.steps
+
+    def timed_rounds(extra=0):
+        for _ in range(2):
+            step(extra)
+        a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a0.record(stream)
+        for _ in range(args.steps):
+            step(extra)
+        a1.record(stream)
+        torch.cuda.synchronize()
+        tb.sync_status()
+        return a0.elapsed_time(a1) / args.steps
+
+    # ablations on the same builds (event time per round): the factorised
+    # tree (DT_MARGINAL: base logits alone, no per-node products), a plain
+    # instead of a cooperative launch, the correction dL with vector FMAs
+    ablations = {"marginal_round_ms": timed_rounds(pkg.DT_MARGINAL)}
+    for key, sched in (("plain_launch_round_ms", dict(launch=1)), ("fma_dl_round_ms", dict(dl=1))):
+        tb.set_schedule(**sched)
+        ablations[key] = timed_rounds()
+        tb.set_schedule()
+    step()
+    torch.cuda.synchronize()
+    tb.sync_status()
     n_nodes = out["n_nodes"].cpu().numpy()
     assert np.all(n_nodes == spec.N), n_nodes
 
@@ -427,6 +461,7 @@ def main():
         },
         "us_per_tree": wall_ms * 1e3 / spec.B,
         "round_ms_events": ev_ms,
+        "ablations": ablations,
         "phases_ms": {"lm_head_or_P": phases[0], "candidates": phases[1], "P_join": phases[2],
                       "builder_setup": phases[3], "tree_kernel": tree_ms, "builds_averaged": nb},
         "round_ms_distribution": dict(dist, rounds=ROUNDS),

@@ -496,6 +496,7 @@ dt_status dt_build_trees(dt_handle* h, const dt_inputs* in, const dt_params* p, 
   const size_t lds = dt::plan_tree(a, h->bf16, h->sched.pops, std::min(h->n_cu - B, h->max_workers),
                                    h->sched.lds_workers, h->sched.halves, h->sched.advance == 2);
   if (lds == 0 || lds > 160 * 1024) return fail(DT_EUNSUPPORTED, "no builder schedule fits this shape in LDS");
+  if (a.marginal) a.n_workers = 0;  // marginal scores need no per-node products: controllers only
   if (a.n_workers + B > h->n_cu || a.n_workers > h->max_workers)
     return fail(DT_EUNSUPPORTED, "%d workers + %d requests exceed %d compute units", a.n_workers, B, h->n_cu);
   MARK(3);

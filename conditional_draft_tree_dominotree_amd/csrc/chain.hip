@@ -96,13 +96,13 @@ struct RowPiece<float> {
 // One vocabulary row per thread (the grid covers V).  NB: requests handled,
 // a multiple of 4 and >= B.  The row's W2^T pieces are all requested before
 // the first is used, so a thread waits for memory once per chunk.
-template <typename T, int NB>
+template <typename T, int NB, bool SAMPLE>
 __global__ __launch_bounds__(CT) void chain_correct_kernel(const T* __restrict__ w2t, const float* __restrict__ base,
                                                            const float* __restrict__ P,
                                                            const float* __restrict__ gu, int B, int D, int d,
                                                            int V, int r, int gstride, int goff,
-                                                           uint64_t* __restrict__ part, int sample, float temp,
-                                                           uint32_t k0, uint32_t k1) {
+                                                           uint64_t* __restrict__ part, float temp, uint32_t k0,
+                                                           uint32_t k1) {
   typedef typename RowPiece<T>::type Piece;
   // 32 accumulators leave room for half a bf16 row at a time
   constexpr int CH = (NB >= 32 && RowPiece<T>::CHUNK > 128) ? 128 : RowPiece<T>::CHUNK;
@@ -156,7 +156,7 @@ __global__ __launch_bounds__(CT) void chain_correct_kernel(const T* __restrict__
   for (int b = 0; b < NB; ++b) {
     if (b < B) {
       float z = base[((size_t)b * D + d) * V + vr] + acc[b];
-      if (sample) z = z / temp + gumbel_of(word_of(chain_noise_words(vr >> 2, d, b, k0, k1), vr & 3));
+      if constexpr (SAMPLE) z = z / temp + gumbel_of(word_of(chain_noise_words(vr >> 2, d, b, k0, k1), vr & 3));
       const uint64_t m = wave_max_u64(v < V ? cand_pack(f32_key(z), (uint32_t)v) : 0ull);
       if (lane == 0) wbest[wv][b] = m;
     }
@@ -186,13 +186,14 @@ constexpr int MT = 2;                 // 32-row tiles per wave
 constexpr int MROWS = 4 * MT * 32;    // rows per block
 constexpr int AROW = CHAIN_MAX_RANK + 8;  // bf16 per LDS row of a_hi / a_lo (padded)
 
+template <bool SAMPLE>
 __global__ __launch_bounds__(CT) void chain_correct_mfma_kernel(const uint16_t* __restrict__ w2f,
                                                                 const float* __restrict__ base,
                                                                 const float* __restrict__ P,
                                                                 const float* __restrict__ gu, int B, int D, int d,
                                                                 int V, int r, int gstride, int goff,
-                                                                uint64_t* __restrict__ part, int sample,
-                                                                float temp, uint32_t k0, uint32_t k1) {
+                                                                uint64_t* __restrict__ part, float temp,
+                                                                uint32_t k0, uint32_t k1) {
   __shared__ __attribute__((aligned(16))) uint16_t ahi[32 * AROW];
   __shared__ __attribute__((aligned(16))) uint16_t alo[32 * AROW];
   __shared__ uint64_t wbest[CT / 64][32];
@@ -280,14 +281,14 @@ __global__ __launch_bounds__(CT) void chain_correct_mfma_kernel(const uint16_t* 
         const float bb[4] = {bv.x, bv.y, bv.z, bv.w};
         // the four rows are the tokens of one noise counter
         uint4 nw = make_uint4(0u, 0u, 0u, 0u);
-        if (sample) nw = chain_noise_words((v0 + 8 * g + 4 * (lane >> 5)) >> 2, d, fr, k0, k1);
+        if constexpr (SAMPLE) nw = chain_noise_words((v0 + 8 * g + 4 * (lane >> 5)) >> 2, d, fr, k0, k1);
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const int e = 4 * g + q;
           const int v = v0 + 8 * g + 4 * (lane >> 5) + q;
           if (v < V) {
             float z = bb[q] + acc[e];
-            if (sample) z = z / temp + gumbel_of(word_of(nw, q));
+            if constexpr (SAMPLE) z = z / temp + gumbel_of(word_of(nw, q));
             const uint64_t c = cand_pack(f32_key(z), (uint32_t)v);
             best = c > best ? c : best;
           }
@@ -486,14 +487,26 @@ hipError_t launch_chain(const ChainArgs& c, hipStream_t stream) {
                                  c.ds, gstride, stream);
     if (e != hipSuccess) return e;
     // 2. corrected logits of every token, block-wise best per request
-#define CHAIN_CORRECT(T, NB)                                                                                  \
-  hipLaunchKernelGGL((chain_correct_kernel<T, NB>), dim3(nblk), dim3(CT), 0, stream, (const T*)c.w2t, c.base, \
-                     c.P, c.gu, c.B, c.D, d, c.V, c.r, gstride, goff, c.part, c.sample, c.temperature, c.key0,  \
-                     c.key1)
+#define CHAIN_CORRECT(T, NB)                                                                                   \
+  do {                                                                                                         \
+    if (c.sample)                                                                                              \
+      hipLaunchKernelGGL((chain_correct_kernel<T, NB, true>), dim3(nblk), dim3(CT), 0, stream, (const T*)c.w2t, \
+                         c.base, c.P, c.gu, c.B, c.D, d, c.V, c.r, gstride, goff, c.part, c.temperature, c.key0, \
+                         c.key1);                                                                              \
+    else                                                                                                       \
+      hipLaunchKernelGGL((chain_correct_kernel<T, NB, false>), dim3(nblk), dim3(CT), 0, stream,                 \
+                         (const T*)c.w2t, c.base, c.P, c.gu, c.B, c.D, d, c.V, c.r, gstride, goff, c.part, 1.f, \
+                         0u, 0u);                                                                              \
+  } while (0)
     if (c.w2f) {
-      hipLaunchKernelGGL(chain_correct_mfma_kernel, dim3(chain_mfma_blocks(c.V)), dim3(CT), 0, stream,
-                         (const uint16_t*)c.w2f, c.base, c.P, c.gu, c.B, c.D, d, c.V, c.r, gstride, goff, c.part,
-                         c.sample, c.temperature, c.key0, c.key1);
+      if (c.sample)
+        hipLaunchKernelGGL(chain_correct_mfma_kernel<true>, dim3(chain_mfma_blocks(c.V)), dim3(CT), 0, stream,
+                           (const uint16_t*)c.w2f, c.base, c.P, c.gu, c.B, c.D, d, c.V, c.r, gstride, goff, c.part,
+                           c.temperature, c.key0, c.key1);
+      else
+        hipLaunchKernelGGL(chain_correct_mfma_kernel<false>, dim3(chain_mfma_blocks(c.V)), dim3(CT), 0, stream,
+                           (const uint16_t*)c.w2f, c.base, c.P, c.gu, c.B, c.D, d, c.V, c.r, gstride, goff, c.part,
+                           1.f, 0u, 0u);
     } else if (c.bf16) {
       if (c.B <= 4) CHAIN_CORRECT(uint16_t, 4);
       else if (c.B <= 8) CHAIN_CORRECT(uint16_t, 8);

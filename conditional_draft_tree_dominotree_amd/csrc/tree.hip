@@ -970,7 +970,7 @@ template <typename W>
 __device__ __forceinline__ void ctl_prefetch(const TreeArgs& a, const CtlLds& c, int b) {
   const int tid = threadIdx.x, M = a.M, r = a.r;
   const int nl = c.f->misc[C_NL];
-  if (nl == 0) return;
+  if (nl == 0 || a.marginal) return;  // marginal scores use neither W2 nor P
   const W* w2t = reinterpret_cast<const W*>(a.w2t);
   const int rs = w2s_stride(r, (int)sizeof(W));
   const int rows = nl * M;
@@ -1079,7 +1079,9 @@ __device__ __forceinline__ void ctl_expand(const TreeArgs& a, const CtlLds& c, i
   // a_j = SiLU(u_j + P_{d_j}); the u loads of all nodes are issued first
   const int us = u_stride(r);
   const float* ub = a.u + slot_of(a, t, b, 0) * us;  // the e slots are consecutive
-  if (mf) {
+  if (a.marginal) {
+    // no correction: no activations
+  } else if (mf) {
     // pairs of elements: item i is node i / (r / 2), elements 2 (i % (r / 2)) + 0, 1;
     // a thread takes items tid, tid + NT, ..., eight of them a batch (their u
     // loads issued together), and writes each piece of a pair as one word
@@ -1979,8 +1981,8 @@ __device__ __forceinline__ void controller_main(const TreeArgs& a, unsigned char
     c.f->ex_dep[0] = 0;
     c.f->misc[C_E] = 1;
   }
-  // root state and its GEMM operand copy
-  {
+  // root state and its GEMM operand copy (marginal scores need no states)
+  if (!a.marginal) {
     const int ds = a.ds;
     const size_t sl = slot_of(a, 0, b, 0);
     float* s0 = a.state + sl * st_stride(ds);
@@ -2034,7 +2036,9 @@ __device__ __forceinline__ void controller_main(const TreeArgs& a, unsigned char
       failed = true;
       break;
     }
-    if (a.wadv) {
+    if (a.marginal) {
+      // marginal scores: no states to advance (and no workers)
+    } else if (a.wadv) {
       // the workers advance the states: token and parent slot of each node
       if (tid < e2) {
         int xs = c.f->ex_src[tid];

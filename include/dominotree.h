@@ -89,7 +89,9 @@ typedef enum { DT_NORM_TOPM = 0, DT_NORM_FULLV = 1 } dt_norm;
 #define DT_MARGINAL 8u  /* score with the base logits alone (dL = 0): the factorised, DDTree-style
                            tree that the conditional correction is compared against
                            ("Riassunto Tecnico: DominoTree", Definizione del Problema: scores
-                           that depend on the position only); the GRU still runs */
+                           that depend on the position only); such a build computes no
+                           per-node products (no GRU states, no W1/W2 work): only the
+                           per-request blocks run */
 
 /* Limits of this build (DT_EUNSUPPORTED beyond them). */
 #define DT_MAX_BATCH 32

@@ -172,11 +172,32 @@ def test_marginal_flag_is_the_zero_correction_tree(dev, name):
     spec, w, req = synth.workload(spec)
     tb = gu.make_builder(spec, w)
     got = gu.run(tb, spec, req, flags=pkg.DT_MARGINAL)
+    # a conditional build on the same handle afterwards (the marginal build
+    # runs no workers; the exchange with them must still be in step)
+    cond = gu.run(tb, spec, req)
     tb.close()
     w0 = dict(w)
     w0["w2"] = np.zeros_like(w["w2"])
     reps, trees = gu.compare(spec, w0, req, got)
     print(name, "marginal", gu.summarize(reps))
+    _assert_ok(reps)
+    assert all(r.exact for r in reps)
+    reps, _ = gu.compare(spec, w, req, cond)
+    _assert_ok(reps)
+
+
+def test_marginal_with_root_state_bf16(dev):
+    # a given root state changes nothing in the marginal scores
+    import conditional_draft_tree_dominotree_amd as pkg
+    spec = synth.small("marginal_root", V=3000, D=6, h=64, e=96, ds=1024, r=64, M=16, k=4, N=50, B=6,
+                       wdtype="bf16", group=2201, emb_std=0.5, root_std=0.7)
+    spec, w, req = synth.workload(spec)
+    tb = gu.make_builder(spec, w)
+    got = gu.run(tb, spec, req, flags=pkg.DT_ACT_BF16 | pkg.DT_MARGINAL)
+    tb.close()
+    w0 = dict(w)
+    w0["w2"] = np.zeros_like(w["w2"])
+    reps, _ = gu.compare(spec, w0, req, got)
     _assert_ok(reps)
     assert all(r.exact for r in reps)
 
