@@ -10,8 +10,9 @@
 // Kernels.  topm_chunk: one 256-thread block per (row, chunk of 8192 tokens)
 // item; the block reads its item once from HBM into registers (32 values per
 // thread, 16-byte loads), and the several blocks resident on a CU overlap one
-// block's loads with another's selection.  Each wave finds the ceil(M/4)-th largest of its 64 per-thread maxima (a bit
-// search over ballots); the smallest of the four wave values bounds the
+// block's loads with another's selection.  Each wave bounds the ceil(M/4)-th
+// largest of its 64 per-thread maxima from below (a bit search over ballots,
+// to 16 key bits); the smallest of the four wave values bounds the
 // chunk's M-th largest value from below (at least M threads reach it), so the
 // keys at or above it -- typically a few more than M -- hold the chunk's
 // top-M; they are ranked exactly as (value desc, id asc) composites.  When
@@ -60,12 +61,14 @@ __device__ __forceinline__ uint32_t wave_max_key(uint32_t v) {
   return max(a, b);
 }
 
-// The m-th largest of the wave's 64 keys (1 <= m <= 64): the largest c with
-// at least m keys >= c, built bit by bit from the top.
+// A lower bound of the m-th largest of the wave's 64 keys (1 <= m <= 64):
+// the largest c whose low LOW bits are zero with at least m keys >= c, built
+// bit by bit from the top (LOW = 0: the m-th largest itself).
+template <int LOW>
 __device__ __forceinline__ uint32_t wave_kth_largest(uint32_t v, int m) {
   uint32_t p = 0;
 #pragma unroll
-  for (int b = 31; b >= 0; --b) {
+  for (int b = 31; b >= LOW; --b) {
     const uint32_t c = p | (1u << b);
     if ((int)__popcll(__ballot(v >= c)) >= m) p = c;
   }
@@ -203,29 +206,29 @@ __device__ __forceinline__ void p_tile(const PArgs& pa, int tile, float* part /*
 // One block per item.  The selection works on the fp32 values with float
 // compares (a key per element only for the few candidates): per element a
 // max, a compare with the threshold and one exp.
+// One item's selection from its values in registers (x, loaded by
+// chunk_load); uses L and ends with the block's LDS reads done.
 template <bool VEC4>
-__global__ __launch_bounds__(TOPM_THREADS) void topm_chunk_kernel(
-    const float* __restrict__ logits, int V, int S, int M, float T,
-    uint64_t* __restrict__ out_cand, float4* __restrict__ out_stat) {
-  __shared__ ChunkLds L;
+__device__ __forceinline__ void chunk_select(ChunkLds& L, const float* __restrict__ logits, int V, int S, int M,
+                                             float T, int item, float (&x)[PER_THREAD],
+                                             uint64_t* __restrict__ out_cand, float4* __restrict__ out_stat) {
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int item = blockIdx.x;
   const int row = item / S, c = item - row * S;
   const int c0 = c * TOPM_CHUNK, len = min(TOPM_CHUNK, V - c0), Mc = min(M, len);
   const float* src = logits + (size_t)row * (size_t)V + c0;
-  float x[PER_THREAD];
-  chunk_load<VEC4>(src, len, x);
   // element q of this thread is chunk element 4 tid + off(q)
   auto off = [](int q) { return (q >> 2) * (4 * TOPM_THREADS) + (q & 3); };
   const uint32_t id0 = (uint32_t)(c0 + 4 * tid);
-  // 1. threshold: in each wave the ceil(Mc/4)-th largest lane maximum; the
+  // 1. threshold: in each wave a lower bound of the ceil(Mc/4)-th largest
+  //    lane maximum, to 16 bits of its key (the sign, the exponent and the top
+  //    7 mantissa bits: half the search steps, a few more candidates); the
   //    smallest of the four bounds the chunk's Mc-th largest value from below
   //    (at least 4 ceil(Mc/4) >= Mc threads have a maximum at or above it)
   float vmax = x[0];
 #pragma unroll
   for (int q = 1; q < PER_THREAD; ++q) vmax = fmaxf(vmax, x[q]);  // NaN is dropped
   const uint32_t kmax = f32_key(vmax);
-  const uint32_t wbound = wave_kth_largest(kmax, (Mc + 3) >> 2);
+  const uint32_t wbound = wave_kth_largest<16>(kmax, (Mc + 3) >> 2);
   const uint32_t wtop = wave_max_key(kmax);
   if (lane == 0) {
     L.wb[wv] = wbound;
@@ -382,6 +385,26 @@ __global__ __launch_bounds__(TOPM_THREADS) void topm_chunk_kernel(
       out_stat[item] = make_float4(vm / T, tot, fmaxf(tot - s_sel, 0.f), __int_as_float(Mc));
     }
   }
+}
+
+
+__device__ __forceinline__ const float* chunk_src(const float* logits, int V, int S, int item, int* len) {
+  const int row = item / S, c = item - row * S;
+  *len = min(TOPM_CHUNK, V - c * TOPM_CHUNK);
+  return logits + (size_t)row * (size_t)V + (size_t)c * TOPM_CHUNK;
+}
+
+// One block per item.
+template <bool VEC4>
+__global__ __launch_bounds__(TOPM_THREADS) void topm_chunk_kernel(
+    const float* __restrict__ logits, int V, int S, int M, float T,
+    uint64_t* __restrict__ out_cand, float4* __restrict__ out_stat) {
+  __shared__ ChunkLds L;
+  int len;
+  const float* src = chunk_src(logits, V, S, blockIdx.x, &len);
+  float x[PER_THREAD];
+  chunk_load<VEC4>(src, len, x);
+  chunk_select<VEC4>(L, logits, V, S, M, T, blockIdx.x, x, out_cand, out_stat);
 }
 
 // Number of entries of a descending list greater than `key`.

@@ -176,14 +176,72 @@ __device__ __forceinline__ uint64_t key_with_parent(uint64_t k, int parent) {
 }
 
 // bounded wait until every word of one mailbox line is >= need; wave-uniform
+// Poll box[0..nwords) (nwords <= 64 Q) until every word is >= need.  Two
+// polls are in flight at a time: the next one is issued before the previous
+// one is examined, so a word that lands is seen about half a load latency
+// sooner than with polls issued one after the other.  The loads are
+// device-coherent (relaxed, agent scope); lanes past nwords re-read the last
+// word.  On success *word0, when given, receives what the deciding poll read
+// at box[min(lane, nwords - 1)].
+template <int Q>
+__device__ __forceinline__ bool wait_words(const uint32_t* box, int nwords, uint32_t need, const int* err,
+                                           unsigned limit, uint32_t* word0) {
+  const int lane = threadIdx.x & 63;
+  const uint32_t* p[Q];
+#pragma unroll
+  for (int q = 0; q < Q; ++q) p[q] = box + min(lane + 64 * q, nwords - 1);
+  uint32_t x[Q], y[Q];
+  auto issue = [&](uint32_t (&v)[Q]) {
+#pragma unroll
+    for (int q = 0; q < Q; ++q) v[q] = __hip_atomic_load(p[q], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  };
+  auto all_in = [&](const uint32_t (&v)[Q]) {
+    bool ok = true;
+#pragma unroll
+    for (int q = 0; q < Q; ++q) ok &= v[q] >= need;
+    return __all(ok);
+  };
+  issue(x);
+  unsigned it = 0;
+  while (true) {
+    __builtin_amdgcn_s_sleep(1);
+    issue(y);
+    if (all_in(x)) {
+      if (word0) *word0 = x[0];
+      break;
+    }
+    __builtin_amdgcn_s_sleep(1);
+    issue(x);
+    if (all_in(y)) {
+      if (word0) *word0 = y[0];
+      break;
+    }
+    if ((++it & 127) == 0) {
+      if (ld_dev_u32(err) != 0) return false;
+      if (2 * it > limit) {
+        if (lane == 0) atomicOr((int*)err, 1);
+        return false;
+      }
+    }
+  }
+  asm volatile("" ::: "memory");  // what the caller reads next stays after the poll that saw the words
+  return true;
+}
+
 __device__ __forceinline__ bool wait_mbox(const uint32_t* box, int nwords, uint32_t need, const int* err,
-                                          unsigned limit) {
+                                          unsigned limit, uint32_t* word0 = nullptr) {
+  if (nwords <= 0) return true;
+  if (nwords <= 64) return wait_words<1>(box, nwords, need, err, limit, word0);
+  if (nwords <= 256) return wait_words<4>(box, nwords, need, err, limit, word0);
   const int lane = threadIdx.x & 63;
   unsigned it = 0;
   while (true) {
     bool ok = true;
     for (int i = lane; i < nwords; i += 64) ok &= ld_dev_u32(box + i) >= need;
-    if (__all(ok)) return true;
+    if (__all(ok)) {
+      if (word0) *word0 = ld_dev_u32(box + min(lane, nwords - 1));
+      return true;
+    }
     if ((++it & 255) == 0) {
       if (ld_dev_u32(err) != 0) return false;
       if (it > limit) {
@@ -401,10 +459,9 @@ __device__ __forceinline__ void worker_columns(const TreeArgs& a, int w, int t, 
   const uint32_t epoch = a.ebase + (uint32_t)t + 1u;
   if (tid < 64) {
     const uint32_t* mybox = a.mbox_w + (size_t)w * 32 + b0;
-    const bool ok = wait_mbox(mybox, nb, epoch << 5, a.err, a.spin_limit);
-    const int b = b0 + lane;
     uint32_t word = 0;
-    if (ok && lane < nb) word = ld_dev_u32(mybox + lane);
+    const bool ok = wait_mbox(mybox, nb, epoch << 5, a.err, a.spin_limit, &word);
+    const int b = b0 + lane;
     const int e = (ok && lane < nb && (word & 31u) != MBOX_DONE_E) ? (int)(word & 31u) : 0;
     // exclusive prefix of e over the lanes
     int incl = e;
