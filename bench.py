@@ -251,7 +251,8 @@ def lm_head_leg(steps: int, warmup: int) -> dict:
         "nodes_per_s": spec.B * spec.N / (round_ms * 1e-3),
         "phases_ms": {"lm_head": phases[0], "candidates": phases[1], "P_join": phases[2],
                       "builder_setup": phases[3], "tree_kernel": phases[4], "builds_averaged": nb},
-        "roofline": {"kernel": "gemm_lm_half_kernel (H W_lm, with the per-call re-layout of H)", "bound": "mfma",
+        "roofline": {"kernel": "gemm_lm_topk_kernel (H W_lm with the per-list top-8 and LSE epilogue; the "
+                                "per-call re-layout of H included)", "bound": "mfma",
                      "achieved": tf, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": tf / BF16_PEAK_TFLOPS,
                      "traffic": None, "algorithmic_flops": flops},
     }
@@ -502,8 +503,8 @@ def main():
         # the LM head: a dense bf16 contraction, priced against the MFMA peak
         flops = 2.0 * spec.B * spec.D * spec.V * spec.h
         tf = flops / (phases[0] * 1e-3) / 1e12
-        res["roofline_lm_head"] = {"kernel": "gemm_lm_half_kernel (H W_lm)", "bound": "mfma", "achieved": tf,
-                                   "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+        res["roofline_lm_head"] = {"kernel": "gemm_lm_topk_kernel (H W_lm with the candidate epilogue)",
+                                   "bound": "mfma", "achieved": tf, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                                    "frac": tf / BF16_PEAK_TFLOPS, "traffic": None,
                                    "algorithmic_flops": flops}
     got = {k: v.cpu().numpy() for k, v in out.items()}
