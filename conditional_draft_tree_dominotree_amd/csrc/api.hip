@@ -322,7 +322,7 @@ dt_status dt_create(dt_handle** out, const dt_dims* dims, const dt_weights* w, c
   ALLOC(h->tokrank, rows * M * sizeof(int32_t));
   ALLOC(h->lse, rows * sizeof(float));
   ALLOC(h->tail, rows * sizeof(float));
-  ALLOC(h->P, rows * r * sizeof(float));
+  ALLOC(h->P, (size_t)dt::P_KSPLIT * rows * r * sizeof(float));  // partials of P (the candidate merge's)
   // exchange slots: at most N + 1 steps of at most TREE_MAX_COLS expanded nodes
   const size_t nodes = (size_t)(N + 1) * dt::TREE_MAX_COLS;
   ALLOC(h->state, nodes * round_up(ds, 32) * sizeof(float));
@@ -470,6 +470,8 @@ dt_status dt_build_trees(dt_handle* h, const dt_inputs* in, const dt_params* p, 
   a.G = h->G;
   a.w2t = h->w2t;
   a.P = h->P;
+  a.p_parts = p_in_topm ? dt::P_KSPLIT : 1;
+  a.p_stride = (size_t)rows * d.rank;
   a.cand_ids = h->cand_ids;
   a.cand_vals = h->cand_vals;
   a.tail = h->tail;

@@ -136,70 +136,95 @@ __device__ __forceinline__ void chunk_load(const float* __restrict__ src, int le
 
 // The per-round product P = H W1_H (the path-independent half of the
 // correction's first projection: H_d is shared by every path, DominoTree
-// summary, Componenti Core 1), launched as extra blocks in front of the rows
-// of the candidate merge, whose few latency-bound blocks leave the CUs room
-// (in the chunk kernel its registers would cut that kernel's occupancy): one
-// 32 x 32 output tile per block, the four waves splitting K, each keeping the next 64-k step's
-// operand loads (16 bytes a lane, straight from memory) in flight over the
-// current step's MFMAs; the partial tiles are summed in LDS in a fixed order.
+// summary, Componenti Core 1), launched as extra blocks behind the rows of
+// the candidate merge, whose latency-bound blocks leave the CUs room (in the
+// chunk kernel its registers would cut that kernel's occupancy).  K is split
+// P_KSPLIT ways over blocks: a block computes one 32 x 32 output tile over
+// its K share, its four waves splitting the share again (256 k each at
+// h = 4096), so that a wave issues the loads of its whole share at once
+// (16 bytes a lane, straight from memory, 16 rows x 64 bytes per load
+// instruction) and waits for memory about once: with only a 64-k step's
+// products (about 128 cycles) to cover each load, a wave walking a long K
+// share pays one memory latency per step.  The four waves' tiles are summed
+// in LDS in a fixed order and the block writes partial kz of P; the
+// consumer adds the P_KSPLIT partials in a fixed order.
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 
 struct PArgs {
   const uint16_t* A;   // H [M, K] bf16
   const uint16_t* Bt;  // W1_H^T [N, K] bf16
-  float* C;            // P [M, N] fp32
+  float* C;            // P partials [P_KSPLIT][M, N] fp32
   int M, N, K;
-  int blocks;          // output tiles (0: no P blocks)
+  int blocks;          // output tiles x P_KSPLIT (0: no P blocks)
 };
 
+// 8 bf16 of a row at k0, or zeros past the rows or past kend (K and kend
+// multiples of 8).  The load itself is unconditional, from a clamped address
+// that is always in bounds, so that the loads of a step carry no branch and
+// stay in flight together.
 __device__ __forceinline__ uint4 p_load8(const uint16_t* base, int row, int rows, int k0, int kend, int K) {
-  if (row < rows && k0 < kend) return *reinterpret_cast<const uint4*>(base + (size_t)row * K + k0);
-  return make_uint4(0, 0, 0, 0);
+  const uint32_t m = (row < rows && k0 < kend) ? 0xFFFFFFFFu : 0u;  // a mask, not a branch around the load
+  const uint4 v = *reinterpret_cast<const uint4*>(base + (size_t)min(row, rows - 1) * K + min(k0, kend - 8));
+  return make_uint4(v.x & m, v.y & m, v.z & m, v.w & m);
 }
 
-__device__ __forceinline__ void p_tile(const PArgs& pa, int tile, float* part /* [4][1024] */) {
+__device__ __forceinline__ void p_tile(const PArgs& pa, int blk, float* part /* [4][1024] */) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tile = blk / P_KSPLIT, kz = blk - tile * P_KSPLIT;
   const int tn = (pa.N + 31) / 32;
   const int m0 = (tile / tn) * 32, n0 = (tile % tn) * 32;
   const int K = pa.K;
-  const int kq = ((K + 15) / 16 + 3) / 4 * 16;  // k per wave, a multiple of 16
-  const int kb = w * kq, ke = min(K, kb + kq);
-  const int ar = m0 + (lane & 31), bc = n0 + (lane & 31), ko = 8 * (lane >> 5);
-  floatx16 acc;
+  constexpr int NS = 4;                                       // 64-k steps whose loads go out together
+  const int kblk = ((K + P_KSPLIT - 1) / P_KSPLIT + 255) / 256 * 256;  // k per block, a multiple of 4 x 64
+  const int kw = kblk / 4;                                    // k per wave, a multiple of 64
+  const int kb = min(K, kz * kblk + w * kw), ke = min(K, kb + kw);
+  // v_mfma_f32_16x16x32_bf16 on the four 16 x 16 quarters of the tile: lane
+  // l holds row (l & 15) at k 8 (l >> 4) of each 32-k half step
+  const int r16 = lane & 15, ko = 8 * (lane >> 4);
+  floatx4 acc[2][2];
 #pragma unroll
-  for (int e = 0; e < 16; ++e) acc[e] = 0.f;
-  uint4 ca[4], cb[4];
+  for (int i = 0; i < 2; ++i)
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    ca[q] = p_load8(pa.A, ar, pa.M, kb + 16 * q + ko, ke, K);
-    cb[q] = p_load8(pa.Bt, bc, pa.N, kb + 16 * q + ko, ke, K);
+    for (int j = 0; j < 2; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+  for (int k = kb; k < ke; k += 64 * NS) {
+    uint4 ra[NS][2][2], rb[NS][2][2];  // [step][row or column half][32-k half]
+#pragma unroll
+    for (int d = 0; d < NS; ++d)
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          ra[d][h][q] = p_load8(pa.A, m0 + 16 * h + r16, pa.M, k + 64 * d + 32 * q + ko, ke, K);
+          rb[d][h][q] = p_load8(pa.Bt, n0 + 16 * h + r16, pa.N, k + 64 * d + 32 * q + ko, ke, K);
+        }
+#pragma unroll
+    for (int d = 0; d < NS; ++d)
+#pragma unroll
+      for (int q = 0; q < 2; ++q)
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+          for (int j = 0; j < 2; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*reinterpret_cast<const bf16x8*>(&ra[d][i][q]),
+                                                                *reinterpret_cast<const bf16x8*>(&rb[d][j][q]),
+                                                                acc[i][j], 0, 0, 0);
   }
-  for (int k = kb; k < ke; k += 64) {
-    uint4 na[4], nb[4];  // the next step's operands (past ke: zeros, no access)
+  // lane: column (lane & 15), rows 4 (lane >> 4) + e of each quarter
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      na[q] = p_load8(pa.A, ar, pa.M, k + 64 + 16 * q + ko, ke, K);
-      nb[q] = p_load8(pa.Bt, bc, pa.N, k + 64 + 16 * q + ko, ke, K);
-    }
+  for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(&ca[q]),
-                                                    *reinterpret_cast<const bf16x8*>(&cb[q]), acc, 0, 0, 0);
+    for (int j = 0; j < 2; ++j)
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      ca[q] = na[q];
-      cb[q] = nb[q];
-    }
-  }
-#pragma unroll
-  for (int e = 0; e < 16; ++e) part[w * 1024 + (8 * (e >> 2) + 4 * (lane >> 5) + (e & 3)) * 32 + (lane & 31)] = acc[e];
+      for (int e = 0; e < 4; ++e)
+        part[w * 1024 + (16 * i + 4 * (lane >> 4) + e) * 32 + 16 * j + r16] = acc[i][j][e];
   __syncthreads();
+  float* C = pa.C + (size_t)kz * pa.M * pa.N;
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
     const int i = tid + 256 * u;
     const float v = (part[i] + part[1024 + i]) + (part[2048 + i] + part[3072 + i]);
     const int row = m0 + i / 32, col = n0 + i % 32;
-    if (row < pa.M && col < pa.N) pa.C[(size_t)row * pa.N + col] = v;
+    if (row < pa.M && col < pa.N) C[(size_t)row * pa.N + col] = v;
   }
 }
 
@@ -424,8 +449,9 @@ __global__ __launch_bounds__(TOPM_THREADS) void topm_merge_kernel(
     float* __restrict__ tail_out, int32_t* __restrict__ tokrank_out, int32_t* __restrict__ user_ids,
     float* __restrict__ user_vals, float* __restrict__ user_lse, PArgs pa) {
   extern __shared__ uint64_t lists[];  // [S][M], then [MERGE_CAP] candidates (P tiles: [4][1024] floats)
-  if ((int)blockIdx.x < pa.blocks) {
-    p_tile(pa, blockIdx.x, reinterpret_cast<float*>(lists));
+  const int nrows = (int)gridDim.x - pa.blocks;  // the rows' blocks first, then P's
+  if ((int)blockIdx.x >= nrows) {
+    p_tile(pa, (int)blockIdx.x - nrows, reinterpret_cast<float*>(lists));
     return;
   }
   __shared__ int cnt[DT_TOPM_MAX_CHUNKS];
@@ -437,7 +463,7 @@ __global__ __launch_bounds__(TOPM_THREADS) void topm_merge_kernel(
   __shared__ uint64_t lbound, kth;
 
   const int tid = threadIdx.x;
-  const int row = blockIdx.x - pa.blocks;
+  const int row = blockIdx.x;
   uint64_t* cands = lists + (size_t)S * M;
   const uint64_t* src = cand + (size_t)row * S * M;
   for (int i = tid; i < S * M; i += TOPM_THREADS) lists[i] = src[i];
@@ -588,7 +614,7 @@ hipError_t launch_topm(const float* logits, int rows, int V, int M, float T, uin
   PArgs pa{pA, pBt, pC, rows, pN, pK, 0};
   if (pA) {
     if (!pBt || !pC || pN < 1 || pK < 8 || pK % 8) return hipErrorInvalidValue;
-    pa.blocks = ((rows + 31) / 32) * ((pN + 31) / 32);
+    pa.blocks = ((rows + 31) / 32) * ((pN + 31) / 32) * P_KSPLIT;
   }
   const bool vec4 = (V % 4 == 0) && (reinterpret_cast<uintptr_t>(logits) % 16 == 0);
   if (vec4)

@@ -38,7 +38,9 @@ struct TreeArgs {
   const float* b_hh;       // [3 ds] or NULL
   const float* G;          // [V, 3 ds]: W_ih E[v] + b_ih
   const void* w2t;         // [V, r] (wdtype)
-  const float* P;          // [B, D, r]: H_d W1_H
+  const float* P;          // [p_parts][B, D, r]: H_d W1_H, the sum of p_parts partials
+  int p_parts;             // 1, or P_KSPLIT when P comes from the candidate merge's launch
+  size_t p_stride;         // floats between partials
   const int32_t* cand_ids; // [B, D, M]
   const float* cand_vals;  // [B, D, M]
   const float* tail;       // [B, D]

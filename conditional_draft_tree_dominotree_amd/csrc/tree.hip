@@ -1062,7 +1062,10 @@ __device__ __forceinline__ void ctl_prefetch(const TreeArgs& a, const CtlLds& c,
   }
   for (int i = tid; i < nl * r; i += NT) {
     const int s = c.f->lslots[i / r], j = i % r;
-    c.ps[(size_t)s * r + j] = a.P[((size_t)b * a.D + c.f->wdep[s]) * r + j];
+    const size_t idx = ((size_t)b * a.D + c.f->wdep[s]) * r + j;
+    float v = a.P[idx];
+    for (int q = 1; q < a.p_parts; ++q) v += a.P[q * a.p_stride + idx];  // partials in order
+    c.ps[(size_t)s * r + j] = v;
   }
 }
 
