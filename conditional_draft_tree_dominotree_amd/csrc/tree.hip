@@ -1150,13 +1150,17 @@ __device__ __forceinline__ void ctl_expand(const TreeArgs& a, const CtlLds& c, i
     const size_t piece = (size_t)a.p * av_stride(r) / 2;  // words
     int j = tid / r2, q = tid - j * r2;
     for (int b0 = 0; b0 < tot; b0 += 8 * NT) {
-      float2 uv[8];
-      int jj[8], qq[8];
+      // the batch's u loads, its depth-slot reads and its P reads each go out
+      // together: no load is conditional (an item past the end re-reads the
+      // last node's pair, which is in bounds, and is not stored), so none
+      // waits behind a branch
+      float2 uv[8], pv[8];
+      int jj[8], qq[8], ws[8];
 #pragma unroll
       for (int x = 0; x < 8; ++x) {
-        jj[x] = j;
+        jj[x] = min(j, e - 1);
         qq[x] = q;
-        if (b0 + x * NT + tid < tot) uv[x] = *reinterpret_cast<const float2*>(ub + (size_t)j * us + 2 * q);
+        uv[x] = *reinterpret_cast<const float2*>(ub + (size_t)jj[x] * us + 2 * q);
         q += dq;
         j += dj;
         if (q >= r2) {
@@ -1164,12 +1168,15 @@ __device__ __forceinline__ void ctl_expand(const TreeArgs& a, const CtlLds& c, i
           ++j;
         }
       }
+#pragma unroll
+      for (int x = 0; x < 8; ++x) ws[x] = c.f->ex_ws[jj[x]];
+#pragma unroll
+      for (int x = 0; x < 8; ++x) pv[x] = *reinterpret_cast<const float2*>(c.ps + ws[x] * r + 2 * qq[x]);
       keep_batch();
 #pragma unroll
       for (int x = 0; x < 8; ++x)
         if (b0 + x * NT + tid < tot) {
-          const float2 pv = *reinterpret_cast<const float2*>(c.ps + c.f->ex_ws[jj[x]] * r + 2 * qq[x]);
-          const float x0 = uv[x].x + pv.x, x1 = uv[x].y + pv.y;
+          const float x0 = uv[x].x + pv[x].x, x1 = uv[x].y + pv[x].y;
           const float v0 = x0 * sigm(x0), v1 = x1 * sigm(x1);
           // v = hi + mid + lo, each a bf16 (nearest even): the products with
           // bf16 W2 are exact in fp32
@@ -1661,10 +1668,19 @@ __device__ __forceinline__ int ctl_pop(const TreeArgs& a, const CtlLds& c, int b
       uint64_t fu = 0;
       if (j < Q) {
         fu = key_u(F[j]);
-        for (int y = s; y < nx; y += S) {
-          const uint64_t yu = key_u(c.rec[y].key);
-          cv += yu > fu;
-          tie |= yu == fu;
+        // eight records per batch, their LDS reads issued together (clamped
+        // indices: every read is of a valid record; past nx nothing counts)
+        for (int y0 = s; y0 < nx; y0 += 8 * S) {
+          uint64_t yk[8];
+#pragma unroll
+          for (int u = 0; u < 8; ++u) yk[u] = c.rec[min(y0 + u * S, nx - 1)].key;
+#pragma unroll
+          for (int u = 0; u < 8; ++u) {
+            const uint64_t yu = key_u(yk[u]);
+            const bool in = y0 + u * S < nx;
+            cv += in && yu > fu;
+            tie |= in && yu == fu;
+          }
         }
         if (tie) {  // equal keys: the parents' order decides
           const int fp = key_parent(F[j]);
