@@ -105,7 +105,8 @@ struct dt_handle {
   void* act = nullptr;
   float* gh = nullptr;
   float* u = nullptr;
-  int32_t* ninfo = nullptr;
+  uint64_t* ninfo = nullptr;
+  size_t ninfo_words = 0;      // 32-bit words of ninfo (for clearing)
   uint32_t* mbox_w = nullptr;  // group flags, then the worker mailboxes
   uint32_t* mbox_c = nullptr;
   int* err = nullptr;
@@ -331,7 +332,9 @@ dt_status dt_create(dt_handle** out, const dt_dims* dims, const dt_weights* w, c
   HIPB(hipMemsetAsync(h->act, 0, h->act_bytes, stream));
   ALLOC(h->gh, nodes * round_up(3 * ds, 32) * sizeof(float));
   ALLOC(h->u, nodes * round_up(r, 32) * sizeof(float));
-  ALLOC(h->ninfo, nodes * 2 * sizeof(int32_t));
+  ALLOC(h->ninfo, nodes * sizeof(uint64_t));
+  HIPB(hipMemsetAsync(h->ninfo, 0, nodes * sizeof(uint64_t), stream));
+  h->ninfo_words = nodes * 2;
   h->max_workers = h->n_cu;
   ALLOC(h->mbox_w, (dt::GFLAG_WORDS + (size_t)h->max_workers * 32) * sizeof(uint32_t));
   ALLOC(h->mbox_c, (size_t)DT_MAX_BATCH * 256 * sizeof(uint32_t));
@@ -507,6 +510,7 @@ dt_status dt_build_trees(dt_handle* h, const dt_inputs* in, const dt_params* p, 
   if (h->ebase + span >= dt::TREE_EPOCH_LIMIT) {
     HIPCHK(dt::launch_fill_u32(h->mbox_w, 0u, dt::GFLAG_WORDS + (size_t)h->max_workers * 32, stream));
     HIPCHK(dt::launch_fill_u32(h->mbox_c, 0u, (size_t)DT_MAX_BATCH * 256, stream));
+    HIPCHK(dt::launch_fill_u32(reinterpret_cast<uint32_t*>(h->ninfo), 0u, h->ninfo_words, stream));
     h->ebase = 0;
   }
   a.ebase = h->ebase;
@@ -551,6 +555,7 @@ dt_status dt_sync_status(dt_handle* h, void* stream_) {
   HIPCHK(dt::launch_fill_u32(reinterpret_cast<uint32_t*>(h->err), 0u, 16, stream));
   HIPCHK(dt::launch_fill_u32(h->mbox_w, 0u, dt::GFLAG_WORDS + (size_t)h->max_workers * 32, stream));
   HIPCHK(dt::launch_fill_u32(h->mbox_c, 0u, (size_t)DT_MAX_BATCH * 256, stream));
+  HIPCHK(dt::launch_fill_u32(reinterpret_cast<uint32_t*>(h->ninfo), 0u, h->ninfo_words, stream));
   HIPCHK(hipStreamSynchronize(stream));
   h->ebase = 0;
   *reinterpret_cast<volatile int*>(h->err_host) = 0;

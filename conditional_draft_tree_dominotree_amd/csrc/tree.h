@@ -51,7 +51,7 @@ struct TreeArgs {
   void* act;               // [slots, ds] its GEMM operand copy (wdtype)
   float* gh;               // [slots, 3 ds]
   float* u;                // [slots, r]
-  int32_t* ninfo;          // [steps][TREE_MAX_COLS][2]: token and parent slot of each node to advance
+  uint64_t* ninfo;         // [steps][TREE_MAX_COLS]: node entries (ninfo_entry) of the nodes to advance
   uint32_t* gflag;         // [16][64] worker group flags: 2 epoch + half once a group's states of
                            // that step and half of the batch are advanced
   uint32_t* ready;         // [64] controller b: its start-up loads are done (the workers then load weights)
@@ -72,7 +72,15 @@ constexpr int GFLAG_WORDS = 16 * 64 + 64;  // worker group flags and controller 
                                             // worker mailboxes
 // Epochs a launch may use (at most N + 1 steps, the first post and the last).
 __host__ __device__ inline uint32_t tree_epoch_span(int N) { return (uint32_t)N + 8u; }
-constexpr uint32_t TREE_EPOCH_LIMIT = 1u << 27;  // mailbox words hold the epoch in 27 bits
+// mailbox words hold the epoch in 27 bits, node entries in 24: epochs stay
+// below 2^24, and the mailboxes and node entries are cleared when they wrap
+constexpr uint32_t TREE_EPOCH_LIMIT = 1u << 24;
+// A node entry of the node table: the epoch of the step it is published for
+// (24 bits), the token (20 bits) and the parent's exchange slot (20 bits).  It
+// validates itself: a reader compares its epoch with the step's.
+__host__ __device__ inline uint64_t ninfo_entry(uint32_t epoch, uint32_t tok, uint32_t src) {
+  return ((uint64_t)(epoch & 0xFFFFFFu) << 40) | ((uint64_t)(tok & 0xFFFFFu) << 20) | (uint64_t)(src & 0xFFFFFu);
+}
 // Fills the schedule fields of `a` (p from `pops`, 0 = automatic) and returns
 // the dynamic LDS bytes the launch needs, or 0 if the shape cannot be served.
 // With register workers (allowed unless `lds_workers`) it also sets

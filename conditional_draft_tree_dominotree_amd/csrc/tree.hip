@@ -103,6 +103,9 @@ __device__ __forceinline__ void st_dev_act<float>(float* p, float v, int act_bf1
   st_dev_f32(p, act_bf16 ? bf16_to_f32(f32_to_bf16(v)) : v);
 }
 
+__device__ __forceinline__ void st_dev_u64(void* p, uint64_t v) {
+  asm volatile("global_store_dwordx2 %0, %1, off sc1" ::"v"(p), "v"(v) : "memory");
+}
 __device__ __forceinline__ void st_dev_u32x2(void* p, uint32_t lo, uint32_t hi) {
   typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
   u32x2 v = {lo, hi};
@@ -653,18 +656,40 @@ __device__ __forceinline__ void worker_advance(const TreeArgs& a, const int* col
   const int ds = a.ds, n4 = ds >> 2;
   const int items = nc * n4;
   const int slot0 = (int)slot_of(a, t, 0, 0);
-  const int32_t* info = a.ninfo + (size_t)t * TREE_MAX_COLS * 2;
+  const uint64_t* info = a.ninfo + (size_t)t * TREE_MAX_COLS;
+  const uint32_t ep = (a.ebase + (uint32_t)t + 1u) & 0xFFFFFFu;  // the epoch the entries carry
   for (int base = q * NT; base < items; base += nq * NT * WG) {
     int tok[WG], src[WG], sl[WG], qv[WG];
+    uint64_t en[WG];
 #pragma unroll
     for (int g = 0; g < WG; ++g) {  // clamped: every lane reads valid entries
       const int item = min(base + g * nq * NT + (int)threadIdx.x, items - 1);
       const int cc = item / n4;
       qv[g] = (item - cc * n4) * 4;
       sl[g] = coln[c0 + cc];
-      const int2 in = *reinterpret_cast<const int2*>(info + (size_t)(sl[g] - slot0) * 2);
-      tok[g] = in.x;
-      src[g] = in.y;
+      en[g] = __hip_atomic_load(info + (sl[g] - slot0), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    // an entry published after its mailbox word can still be in flight:
+    // read it again until it carries this step's epoch (bounded)
+    for (unsigned it = 0;; ++it) {
+      bool all = true;
+#pragma unroll
+      for (int g = 0; g < WG; ++g) all &= (uint32_t)(en[g] >> 40) == ep;
+      if (all) break;
+      if (it > a.spin_limit || ((it & 255) == 255 && ld_dev_u32(a.err) != 0)) {
+        if (it > a.spin_limit) atomicOr(a.err, 1);
+        break;  // the group's wait sees the error word and ends the turn
+      }
+      __builtin_amdgcn_s_sleep(1);
+#pragma unroll
+      for (int g = 0; g < WG; ++g)
+        if ((uint32_t)(en[g] >> 40) != ep)
+          en[g] = __hip_atomic_load(info + (sl[g] - slot0), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+#pragma unroll
+    for (int g = 0; g < WG; ++g) {
+      tok[g] = (int)((en[g] >> 20) & 0xFFFFFu);
+      src[g] = (int)(en[g] & 0xFFFFFu);
     }
     float4 ir[WG], iz[WG], in_[WG], hr[WG], hz[WG], hn[WG], sp[WG];
 #pragma unroll
@@ -2115,23 +2140,30 @@ __device__ __forceinline__ void controller_main(const TreeArgs& a, unsigned char
     if (a.marginal) {
       // marginal scores: no states to advance (and no workers)
     } else if (a.wadv) {
-      // the workers advance the states: token and parent slot of each node
-      if (tid < e2) {
-        int xs = c.f->ex_src[tid];
-        if (xs < 0) {  // every parent was expanded; the guard keeps addresses valid
-          atomicOr(a.err, 8);
-          xs = 0;
+      // the workers advance the states: wave 0 publishes each node's entry
+      // (token and parent slot; it carries the step's epoch, so the mailbox
+      // words need not wait for it to land) and then the mailbox words
+      if (tid < 64) {
+        if (tid < e2) {
+          int xs = c.f->ex_src[tid];
+          if (xs < 0) {  // every parent was expanded; the guard keeps addresses valid
+            atomicOr(a.err, 8);
+            xs = 0;
+          }
+          const size_t sl = slot_of(a, t + 1, b, tid) - slot_of(a, t + 1, 0, 0);
+          st_dev_u64(a.ninfo + (size_t)(t + 1) * TREE_MAX_COLS + sl,
+                     ninfo_entry(a.ebase + t + 2, (uint32_t)c.f->ex_tok[tid], (uint32_t)xs));
         }
-        const size_t sl = slot_of(a, t + 1, b, tid) - slot_of(a, t + 1, 0, 0);
-        st_dev_u32x2(a.ninfo + ((size_t)(t + 1) * TREE_MAX_COLS + sl) * 2, (uint32_t)c.f->ex_tok[tid], (uint32_t)xs);
+        for (int w = tid; w < a.n_workers; w += 64)
+          st_dev_u32(a.mbox_w + (size_t)w * 32 + b, mbox_word(a.ebase + t + 2, e2));
       }
     } else {
       ctl_advance<W>(a, c, b, t + 1, e2);
+      stores_done();
+      __syncthreads();
+      for (int w = tid; w < a.n_workers; w += NT)
+        st_dev_u32(a.mbox_w + (size_t)w * 32 + b, mbox_word(a.ebase + t + 2, e2));
     }
-    stores_done();
-    __syncthreads();
-    for (int w = tid; w < a.n_workers; w += NT)
-      st_dev_u32(a.mbox_w + (size_t)w * 32 + b, mbox_word(a.ebase + t + 2, e2));
     ctl_prefetch<W>(a, c, b);  // overlaps the workers' step
     __syncthreads();
   }
