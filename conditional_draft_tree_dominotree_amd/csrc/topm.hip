@@ -33,6 +33,13 @@ namespace dt {
 
 constexpr int TOPM_THREADS = 256;
 
+// A block barrier for LDS only: the block's LDS operations complete, then
+// s_barrier.  __syncthreads also waits for the block's outstanding global
+// memory operations (one counter covers loads and stores), which would wait
+// for loads meant to stay in flight across the barrier; the barriers here
+// order LDS accesses only (global results are read by later launches).
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 constexpr int PER_THREAD = TOPM_CHUNK / TOPM_THREADS;  // 32 values per thread
 constexpr int FAST_CAP = 512;                          // candidates the fast path ranks
 constexpr int MERGE_SUB = 320;   // merge: subset keys for the bound (S (M / S + 2) <= M + 2 S)
@@ -80,9 +87,9 @@ __device__ __forceinline__ uint32_t wave_kth_largest(uint32_t v, int m) {
 __device__ __forceinline__ int block_prefix_excl(int v, int* red, int* total) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int incl = wave_add_scan_incl(v);
-  __syncthreads();
+  lds_barrier();
   if (lane == 63) red[w] = incl;
-  __syncthreads();
+  lds_barrier();
   int before = 0, tot = 0;
 #pragma unroll
   for (int i = 0; i < TOPM_THREADS / 64; ++i) {
@@ -260,7 +267,7 @@ __device__ __forceinline__ void chunk_select(ChunkLds& L, const float* __restric
     L.wm[wv] = wtop;
   }
   if (tid == 0) L.sel_count = 0;
-  __syncthreads();
+  lds_barrier();
   const uint32_t tau = min(min(L.wb[0], L.wb[1]), min(L.wb[2], L.wb[3]));
   const uint32_t ktop = max(max(L.wm[0], L.wm[1]), max(L.wm[2], L.wm[3]));
   const float vm = ktop > 0x007FFFFFu ? key_f32(ktop) : -INFINITY;  // the chunk's largest value
@@ -272,9 +279,11 @@ __device__ __forceinline__ void chunk_select(ChunkLds& L, const float* __restric
   //    atomic per wave, then each element q's candidates written at the
   //    wave's running position plus their rank among the lanes (the order in
   //    sel does not matter: the keys are ranked by value below)
-  int wtot = 0;
+  // (the wave's count: each lane counts its own hits, one DPP scan adds them)
+  int hits = 0;
 #pragma unroll
-  for (int q = 0; q < PER_THREAD; ++q) wtot += (int)__popcll(__ballot(x[q] >= tau_f));
+  for (int q = 0; q < PER_THREAD; ++q) hits += x[q] >= tau_f;
+  const int wtot = __builtin_amdgcn_readlane(wave_add_scan_incl(hits), 63);
   int base = 0;
   if (lane == 0 && wtot > 0) base = atomicAdd(&L.sel_count, wtot);
   int pos = __builtin_amdgcn_readfirstlane(base);
@@ -304,7 +313,7 @@ __device__ __forceinline__ void chunk_select(ChunkLds& L, const float* __restric
   }
   s_all = wave_sum_dpp(s_all);
   if (lane == 0) L.ws[wv] = s_all;
-  __syncthreads();
+  lds_barrier();
   const int cnt = L.sel_count;
   if (fast && cnt <= FAST_CAP) {
     // 4. rank the candidates exactly (composite keys are unique)
@@ -319,11 +328,14 @@ __device__ __forceinline__ void chunk_select(ChunkLds& L, const float* __restric
     const ulonglong2* s2 = reinterpret_cast<const ulonglong2*>(L.sel);
     const int pairs = cnt >> 1;
     if (cnt <= TOPM_THREADS) {
-      for (int i = 0; i < pairs; ++i) {
-        const ulonglong2 o = s2[i];
-        rk[0] += (o.x > mine[0]) + (o.y > mine[0]);
+      // only the waves that hold candidates rank (typically just the first)
+      if (wv * 64 < cnt) {
+        for (int i = 0; i < pairs; ++i) {
+          const ulonglong2 o = s2[i];
+          rk[0] += (o.x > mine[0]) + (o.y > mine[0]);
+        }
+        if (cnt & 1) rk[0] += L.sel[cnt - 1] > mine[0];
       }
-      if (cnt & 1) rk[0] += L.sel[cnt - 1] > mine[0];
     } else {
       for (int i = 0; i < pairs; ++i) {
         const ulonglong2 o = s2[i];
@@ -351,26 +363,26 @@ __device__ __forceinline__ void chunk_select(ChunkLds& L, const float* __restric
     int need = Mc;
     for (int sh = 24; sh >= 0; sh -= 8) {
       hist[tid] = 0;
-      __syncthreads();
+      lds_barrier();
       for (int i = tid; i < len; i += TOPM_THREADS) {
         const uint32_t k = f32_key(src[i]);
         if ((k & pmask) == prefix) atomicAdd(&hist[(k >> sh) & 255u], 1u);
       }
-      __syncthreads();
+      lds_barrier();
       const int h = (int)hist[tid];
       const int above = block_suffix_excl<TOPM_THREADS>(h, L.wi);  // keys with a larger digit
       if (above < need && above + h >= need) {
         L.digit = tid;
         L.above = above;
       }
-      __syncthreads();
+      lds_barrier();
       need -= L.above;
       prefix |= (uint32_t)L.digit << sh;
       pmask |= 255u << sh;
     }
     const uint32_t kstar = prefix;
     if (tid == 0) L.sel_count = 0;
-    __syncthreads();
+    lds_barrier();
     for (int i = tid; i < len; i += TOPM_THREADS) {
       const uint32_t k = f32_key(src[i]);
       if (k > kstar) L.list[atomicAdd(&L.sel_count, 1)] = cand_pack(k, (uint32_t)(c0 + i));
@@ -386,14 +398,14 @@ __device__ __forceinline__ void chunk_select(ChunkLds& L, const float* __restric
       slot += took;
       left -= took;
     }
-    __syncthreads();
+    lds_barrier();
     if (wv == 0) {
       uint64_t v = lane < Mc ? L.list[lane] : 0ull;
       v = wave_sort_desc_u64(v);
       L.list[lane] = v;
     }
   }
-  __syncthreads();
+  lds_barrier();
   // 5. the list, zero padded to M, and the statistics (m = max / T, the
   //    chunk's sum of exp(x/T - m), the same sum over its tokens left out of
   //    the list as the chunk sum minus the listed terms -- the listed values
