@@ -418,9 +418,11 @@ def main():
 
     # ablations on the same builds (event time per round): the factorised
     # tree (DT_MARGINAL: base logits alone, no per-node products), a plain
-    # instead of a cooperative launch, the correction dL with vector FMAs
+    # instead of a cooperative launch, the correction dL with vector FMAs,
+    # the workers' group exchange device-wide instead of through their XCD's L2
     ablations = {"marginal_round_ms": timed_rounds(pkg.DT_MARGINAL)}
-    for key, sched in (("plain_launch_round_ms", dict(launch=1)), ("fma_dl_round_ms", dict(dl=1))):
+    for key, sched in (("plain_launch_round_ms", dict(launch=1)), ("fma_dl_round_ms", dict(dl=1)),
+                       ("device_exchange_round_ms", dict(exchange=1))):
         tb.set_schedule(**sched)
         ablations[key] = timed_rounds()
         tb.set_schedule()

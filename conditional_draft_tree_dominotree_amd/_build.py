@@ -52,10 +52,11 @@ SANITIZE = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=unde
 
 
 def build_host_sanitized(out_dir: str) -> str:
-    """Compile every source with the host side sanitized (-O1 -g) into
-    out_dir/libdominotree_san.so; returns its path."""
+    """Compile every source with the host side sanitized (-O1 -g; the device
+    side at -O3 as in the product build) into out_dir/libdominotree_san.so;
+    returns its path."""
     os.makedirs(out_dir, exist_ok=True)
-    flags = [f if f != "-O3" else "-O1" for f in FLAGS] + ["-g", *SANITIZE]
+    flags = [*FLAGS, "-Xarch_host", "-O1", "-Xarch_host", "-g", *SANITIZE]
 
     def one(src: str) -> str:
         obj = os.path.join(out_dir, src.replace(".hip", ".o"))

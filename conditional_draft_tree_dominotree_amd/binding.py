@@ -60,7 +60,7 @@ class Outputs(C.Structure):
 class Schedule(C.Structure):
     _fields_ = [("pops", C.c_int32), ("halves", C.c_int32), ("lds_workers", C.c_int32),
                 ("tiles_per_worker", C.c_int32), ("advance", C.c_int32), ("launch", C.c_int32),
-                ("dl", C.c_int32)]
+                ("dl", C.c_int32), ("exchange", C.c_int32)]
 
 
 class TreeView(C.Structure):
@@ -411,9 +411,11 @@ class TreeBuilder:
     def sync_status(self):
         dt_sync_status(self.handle, self.stream.cuda_stream)
 
-    def set_schedule(self, pops=0, halves=0, lds_workers=0, tiles_per_worker=0, advance=0, launch=0, dl=0):
+    def set_schedule(self, pops=0, halves=0, lds_workers=0, tiles_per_worker=0, advance=0, launch=0, dl=0,
+                     exchange=0):
         """Schedule of the next builds (dt_set_schedule); all zeros: defaults."""
-        dt_set_schedule(self.handle, Schedule(pops, halves, lds_workers, tiles_per_worker, advance, launch, dl))
+        dt_set_schedule(self.handle, Schedule(pops, halves, lds_workers, tiles_per_worker, advance, launch, dl,
+                                              exchange))
 
     def set_device_error(self, code=1):
         """Test hook of the failure path (dt_set_device_error)."""

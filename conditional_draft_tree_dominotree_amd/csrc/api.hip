@@ -487,6 +487,7 @@ dt_status dt_build_trees(dt_handle* h, const dt_inputs* in, const dt_params* p, 
   a.ninfo = h->ninfo;
   a.gflag = h->mbox_w;
   a.ready = h->mbox_w + 16 * 64;
+  a.xccw = h->mbox_w + 16 * 64 + 64;
   a.mbox_w = h->mbox_w + dt::GFLAG_WORDS;
   a.mbox_c = h->mbox_c;
   a.err = h->err;
@@ -499,7 +500,8 @@ dt_status dt_build_trees(dt_handle* h, const dt_inputs* in, const dt_params* p, 
   a.stats = out->stats;
   a.spin_limit = 1u << 21;
   const size_t lds = dt::plan_tree(a, h->bf16, h->sched.pops, std::min(h->n_cu - B, h->max_workers),
-                                   h->sched.lds_workers, h->sched.halves, h->sched.advance == 2);
+                                   h->sched.lds_workers, h->sched.halves, h->sched.advance == 2,
+                                   h->sched.exchange == 1);
   if (lds == 0 || lds > 160 * 1024) return fail(DT_EUNSUPPORTED, "no builder schedule fits this shape in LDS");
   if (a.marginal) a.n_workers = 0;  // marginal scores need no per-node products: controllers only
   if (a.n_workers + B > h->n_cu || a.n_workers > h->max_workers)
@@ -576,6 +578,7 @@ dt_status dt_set_schedule(dt_handle* h, const dt_schedule* s) {
   if (s->advance < 0 || s->advance > 2) return fail(DT_EINVAL, "advance %d outside 0..2", s->advance);
   if (s->dl != 0 && s->dl != 1) return fail(DT_EINVAL, "dl must be 0 or 1");
   if (s->launch < 0 || s->launch > 1) return fail(DT_EINVAL, "launch %d outside 0..1", s->launch);
+  if (s->exchange < 0 || s->exchange > 1) return fail(DT_EINVAL, "exchange %d outside 0..1", s->exchange);
   h->sched = *s;
   return DT_OK;
 }

@@ -29,6 +29,11 @@ struct TreeArgs {
                         // turn, so that one half's products overlap the other half's scoring; else 1
   int bh;               // requests in the first half (B when halves = 1)
   int wadv;             // 1: the workers advance the GRU states of a step's nodes (register workers)
+  int uw0, uwn;         // the workers [uw0, uw0 + uwn) hold the W1_S^T tiles: once they acknowledge a
+                        // step, its u rows are stored (all workers unless register workers)
+  int xlocal;           // register workers: 1 lets a column group whose blocks all run on one XCD
+                        // (checked at the launch's first exchange) exchange advanced states through
+                        // that XCD's L2 instead of device-wide
   int xcap;             // node records per request (budget + root + speculation room)
   int fcap;             // frontier entries per request
   int qmax;             // frontier entries tested per pop round
@@ -55,6 +60,7 @@ struct TreeArgs {
   uint32_t* gflag;         // [16][64] worker group flags: 2 epoch + half once a group's states of
                            // that step and half of the batch are advanced
   uint32_t* ready;         // [64] controller b: its start-up loads are done (the workers then load weights)
+  uint32_t* xccw;          // [256] worker w: the XCC (XCD) its block runs on, this launch
   uint32_t* mbox_w;        // [n_workers][32] controller -> worker mailboxes (one line each)
   uint32_t* mbox_c;        // [B][256] worker -> controller mailboxes
   int* err;                // device error word
@@ -68,8 +74,8 @@ struct TreeArgs {
 };
 // Exchange columns a build may use per step (slots per step = B p <= this).
 constexpr int TREE_MAX_COLS = 512;
-constexpr int GFLAG_WORDS = 16 * 64 + 64;  // worker group flags and controller ready flags, before the
-                                            // worker mailboxes
+constexpr int GFLAG_WORDS = 16 * 64 + 64 + 256;  // worker group flags, controller ready flags and the
+                                                  // workers' XCC words, before the worker mailboxes
 // Epochs a launch may use (at most N + 1 steps, the first post and the last).
 __host__ __device__ inline uint32_t tree_epoch_span(int N) { return (uint32_t)N + 8u; }
 // mailbox words hold the epoch in 27 bits, node entries in 24: epochs stay
@@ -88,8 +94,10 @@ __host__ __device__ inline uint64_t ninfo_entry(uint32_t epoch, uint32_t tok, ui
 // are the caller's.
 // `halves`: 1 or 2 forces the split of the batch, 0 = automatic (2 for register
 // workers with at least 2 requests whose first half fills whole 16-column blocks).
+// `device_exchange`: 1 keeps the register workers' group exchange device-wide
+// even where a group runs on one XCD.
 size_t plan_tree(TreeArgs& a, int wdtype_bf16, int pops, int max_workers, int lds_workers, int halves,
-                 int ctl_advance);
+                 int ctl_advance, int device_exchange);
 hipError_t launch_tree(const TreeArgs& a, int wdtype_bf16, size_t lds_bytes, hipStream_t stream, bool plain);
 
 }  // namespace dt

@@ -111,6 +111,20 @@ __device__ __forceinline__ void st_dev_u32x2(void* p, uint32_t lo, uint32_t hi) 
   u32x2 v = {lo, hi};
   asm volatile("global_store_dwordx2 %0, %1, off sc1" ::"v"(p), "v"(v) : "memory");
 }
+// Stores that stop at the XCD's L2 (sc0; no write-through), for exchanges
+// between blocks known to run on one XCD: such a block sees them with the
+// device-coherent loads (sc1) that bypass its L1, and with plain loads of lines
+// it has not read before.  Measured between two CUs of one XCD, a flag stored
+// this way is seen about 0.2 us sooner than one stored with sc1.
+__device__ __forceinline__ void st_l2_u32(void* p, uint32_t v) {
+  asm volatile("global_store_dword %0, %1, off sc0" ::"v"(p), "v"(v) : "memory");
+}
+__device__ __forceinline__ void st_l2_u32x2(void* p, uint32_t lo, uint32_t hi) {
+  typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+  u32x2 v = {lo, hi};
+  asm volatile("global_store_dwordx2 %0, %1, off sc0" ::"v"(p), "v"(v) : "memory");
+}
+
 
 // four consecutive operand values (the address is 8- or 16-byte aligned)
 template <typename W>
@@ -284,12 +298,26 @@ __device__ __forceinline__ void worker_store_out(const TreeArgs& a, size_t slot,
   }
 }
 
+// A uniform address as a scalar register pair (the base operand of the
+// batched loads): the compiler may keep uniform values in vector registers
+// where scalar registers are short.  The batches begin with s_nop 4: a vector
+// instruction that writes a scalar register (v_readfirstlane here, v_readlane
+// for a spilled one) needs five wait states before a memory instruction reads
+// that register as its address, and the compiler does not look inside asm.
+__device__ __forceinline__ const void* uniform_ptr(const void* p) {
+  const uint64_t v = (uint64_t)(uintptr_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return reinterpret_cast<const void*>((uintptr_t)(((uint64_t)hi << 32) | lo));
+}
+
 // Sixteen 16-byte loads from base + off[q] (byte offsets), issued back to back
 // and completed together.  One asm block, so that register pressure elsewhere
 // in the kernel cannot make the compiler wait after each load.
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ void load16_batch(const void* base, const unsigned (&off)[16], u32x4 (&v)[16]) {
   asm volatile(
+      "s_nop 4\n\t"  // the base may have been written by a vector instruction just before
       "global_load_dwordx4 %0, %16, %32\n\t"
       "global_load_dwordx4 %1, %17, %32\n\t"
       "global_load_dwordx4 %2, %18, %32\n\t"
@@ -311,7 +339,7 @@ __device__ __forceinline__ void load16_batch(const void* base, const unsigned (&
         "=&v"(v[8]), "=&v"(v[9]), "=&v"(v[10]), "=&v"(v[11]), "=&v"(v[12]), "=&v"(v[13]), "=&v"(v[14]), "=&v"(v[15])
       : "v"(off[0]), "v"(off[1]), "v"(off[2]), "v"(off[3]), "v"(off[4]), "v"(off[5]), "v"(off[6]), "v"(off[7]),
         "v"(off[8]), "v"(off[9]), "v"(off[10]), "v"(off[11]), "v"(off[12]), "v"(off[13]), "v"(off[14]), "v"(off[15]),
-        "s"(base)
+        "s"(uniform_ptr(base))
       : "memory");
 }
 
@@ -576,6 +604,7 @@ constexpr int RSTRIDE = RKB * 32 + 8;  // staged column stride (elements): 16-by
 // and completed together (one asm block, like load16_batch).
 __device__ __forceinline__ void load8_batch(const void* base, const unsigned (&off)[8], u32x4 (&v)[8]) {
   asm volatile(
+      "s_nop 4\n\t"  // as in load16_batch
       "global_load_dwordx4 %0, %8, %16\n\t"
       "global_load_dwordx4 %1, %9, %16\n\t"
       "global_load_dwordx4 %2, %10, %16\n\t"
@@ -587,7 +616,7 @@ __device__ __forceinline__ void load8_batch(const void* base, const unsigned (&o
       "s_waitcnt vmcnt(0)"
       : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3]), "=&v"(v[4]), "=&v"(v[5]), "=&v"(v[6]), "=&v"(v[7])
       : "v"(off[0]), "v"(off[1]), "v"(off[2]), "v"(off[3]), "v"(off[4]), "v"(off[5]), "v"(off[6]), "v"(off[7]),
-        "s"(base)
+        "s"(uniform_ptr(base))
       : "memory");
 }
 
@@ -650,15 +679,20 @@ __device__ __forceinline__ void lds_read8_b(const uint16_t* p, bf16x8 (&v)[8]) {
 // G[tok] and gh_x published by the workers at the parent's step.  The
 // group's nq blocks share the float4 items: block q takes items q NT + i +
 // k nq NT.  Token and parent slot come from the controller's node table.
+constexpr int WG = 3;  // advance items per thread in flight
 __device__ __forceinline__ void worker_advance(const TreeArgs& a, const int* coln, int t, int c0, int nc, int q,
-                                               int nq) {
-  constexpr int WG = 3;  // items per thread in flight
+                                               int nq, bool loc, floatx4 (&dv)[WG], float* (&dp)[WG]) {
   const int ds = a.ds, n4 = ds >> 2;
   const int items = nc * n4;
   const int slot0 = (int)slot_of(a, t, 0, 0);
   const uint64_t* info = a.ninfo + (size_t)t * TREE_MAX_COLS;
   const uint32_t ep = (a.ebase + (uint32_t)t + 1u) & 0xFFFFFFu;  // the epoch the entries carry
+#pragma unroll
+  for (int g = 0; g < WG; ++g) dp[g] = nullptr;
   for (int base = q * NT; base < items; base += nq * NT * WG) {
+    // the states of the last batch are stored after the group's exchange
+    // (later steps read them; the group needs only the operand copies now)
+    const bool last = base + nq * NT * WG >= items;
     int tok[WG], src[WG], sl[WG], qv[WG];
     uint64_t en[WG];
 #pragma unroll
@@ -720,8 +754,20 @@ __device__ __forceinline__ void worker_advance(const TreeArgs& a, const int* col
           const float ng = tanh_(a2[qq] + rg * b2[qq]);
           o[qq] = (1.0f - zg) * ng + zg * s0[qq];
         }
-        st_dev_f32x4(a.state + (size_t)sl[g] * st_stride(ds) + qv[g], o);
-        st_dev_act4<uint16_t>(reinterpret_cast<uint16_t*>(a.act) + (size_t)sl[g] * act_stride(ds) + qv[g], o, 1);
+        float* stp = a.state + (size_t)sl[g] * st_stride(ds) + qv[g];
+        if (last) {  // deferred: dv, dp
+          dv[g] = o;
+          dp[g] = stp;
+        } else {
+          st_dev_f32x4(stp, o);
+        }
+        uint16_t* ap = reinterpret_cast<uint16_t*>(a.act) + (size_t)sl[g] * act_stride(ds) + qv[g];
+        const uint32_t lo = (uint32_t)f32_to_bf16(o[0]) | ((uint32_t)f32_to_bf16(o[1]) << 16);
+        const uint32_t hi = (uint32_t)f32_to_bf16(o[2]) | ((uint32_t)f32_to_bf16(o[3]) << 16);
+        if (loc)
+          st_l2_u32x2(ap, lo, hi);
+        else
+          st_dev_u32x2(ap, lo, hi);
       }
     }
   }
@@ -742,6 +788,12 @@ __device__ __forceinline__ void worker_regs(const TreeArgs& a, unsigned char* ld
   const int col0 = (w % nb) * CPB * 16;  // first column of the block
   const int tile0 = ((w / nb) * 4 + wv) * TW;
   const int grp = w % nb, gq = w / nb, ngq = a.n_workers / nb;  // the blocks sharing these columns
+  // the group's exchange: -1 undecided (device-wide until the first one has
+  // shown whether every block of the group runs on this XCD), 0 device-wide,
+  // 1 through the XCD's L2
+  int xmode = a.xlocal ? -1 : 0;
+  const uint32_t xcc = __builtin_amdgcn_s_getreg(0xF814);  // HW_REG_XCC_ID
+  if (a.xlocal && tid == 0) st_dev_u32(a.xccw + w, xcc);  // drained before this block's first flag
 
   if (!worker_wait_ready(a, misc)) return;
   // this wave's A operands: tile rows (lane & 15), k 8 (lane >> 4) + 32 kb
@@ -777,15 +829,34 @@ __device__ __forceinline__ void worker_regs(const TreeArgs& a, unsigned char* ld
     if (col0 < ncols) {
       if (a.wadv && t > 0) {
         // the group advances the states of its columns, then waits for all of it
-        worker_advance(a, coln, t, col0, min(16 * CPB, ncols - col0), gq, ngq);
+        const bool loc = xmode == 1;
+        floatx4 sv[WG];
+        float* sp[WG];
+        worker_advance(a, coln, t, col0, min(16 * CPB, ncols - col0), gq, ngq, loc, sv, sp);
         stores_done();
         __syncthreads();
-        if (tid == 0) st_dev_u32(a.gflag + grp * 64 + gq, gepoch);
+        if (tid == 0) {
+          if (loc)
+            st_l2_u32(a.gflag + grp * 64 + gq, gepoch);
+          else
+            st_dev_u32(a.gflag + grp * 64 + gq, gepoch);
+        }
         if (tid < 64) {
           const bool ok = wait_mbox(a.gflag + grp * 64, ngq, gepoch, a.err, a.spin_limit);
           if (lane == 0) misc[2] = ok;
+          if (xmode < 0) {
+            // the first exchange: every block of the group wrote its XCC word
+            // before its flag; one XCD for all of them means one L2
+            const uint32_t x = lane < ngq ? ld_dev_u32(a.xccw + lane * nb + grp) : xcc;
+            const bool same = __all(x == xcc);
+            if (lane == 0) misc[3] = same;
+          }
         }
         __syncthreads();
+        if (xmode < 0) xmode = misc[3] ? 1 : 0;  // the same for every block of the group
+#pragma unroll
+        for (int g = 0; g < WG; ++g)
+          if (sp[g]) st_dev_f32x4(sp[g], sv[g]);
         if (!misc[2]) return;
       }
       // stage: thread piece tid + 256 q = column (tid >> 7) + 2 q, 16-byte piece tid & 127
@@ -823,12 +894,26 @@ __device__ __forceinline__ void worker_regs(const TreeArgs& a, unsigned char* ld
           for (int i = 0; i < TW; ++i)
 #pragma unroll
             for (int n = 0; n < NACC; ++n) acc[c][i][n] = floatx4{0.f, 0.f, 0.f, 0.f};
-        // groups of 8 / CPB k blocks: their B operands read in one batch
-        constexpr int KG = 8 / CPB;
+        // B operands four 16-byte reads at a time (KG k blocks of the CPB column
+        // blocks), in two register sets: the next group's reads are issued
+        // before this group's products, so LDS reads and MFMAs overlap
+        constexpr int KG = 4 / CPB, NG = RKB / KG;
+        bf16x8 bv[2][4];  // [set][c KG + q]: column block c, k block g KG + q
 #pragma unroll
-        for (int g = 0; g < RKB / KG; ++g) {
-          bf16x8 bv[8];  // [c KG + q]: column block c, k block g KG + q
-          lds_read8_b<CPB>(sb + g * KG * 32, bv);
+        for (int q = 0; q < KG; ++q)
+#pragma unroll
+          for (int c = 0; c < CPB; ++c)
+            bv[0][c * KG + q] = *reinterpret_cast<const bf16x8*>(sb + c * 16 * RSTRIDE + q * 32);
+#pragma unroll
+        for (int g = 0; g < NG; ++g) {
+          if (g + 1 < NG) {
+#pragma unroll
+            for (int q = 0; q < KG; ++q)
+#pragma unroll
+              for (int c = 0; c < CPB; ++c)
+                bv[(g + 1) & 1][c * KG + q] =
+                    *reinterpret_cast<const bf16x8*>(sb + c * 16 * RSTRIDE + ((g + 1) * KG + q) * 32);
+          }
 #pragma unroll
           for (int q = 0; q < KG; ++q) {
             const int kb = g * KG + q;
@@ -836,9 +921,13 @@ __device__ __forceinline__ void worker_regs(const TreeArgs& a, unsigned char* ld
             for (int c = 0; c < CPB; ++c)
 #pragma unroll
               for (int i = 0; i < TW; ++i)
-                acc[c][i][kb % NACC] =
-                    __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa[i][kb], bv[c * KG + q], acc[c][i][kb % NACC], 0, 0, 0);
+                acc[c][i][kb % NACC] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa[i][kb], bv[g & 1][c * KG + q],
+                                                                               acc[c][i][kb % NACC], 0, 0, 0);
           }
+          // the schedule: this group's reads of the next set, then its products
+          if (g == 0) __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+          if (g + 1 < NG) __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, 4 * TW, 0);
         }
         // lane holds column col, rows 4 (lane >> 4) + q of each tile
         const int ds3 = 3 * a.ds;
@@ -1155,6 +1244,81 @@ __device__ __forceinline__ void lds_read_keys32(const uint64_t* p, u32x4 (&v)[16
       : "memory");
 }
 
+// a = SiLU(u + P_d) of the step's e nodes as three bf16 pieces per element
+// (hi, mid, lo: each the nearest bf16 of what the previous ones leave, so their
+// sum is a to fp32 precision and each product with bf16 W2 is exact in fp32),
+// pairs of elements: item i is node i / (r / 2), elements 2 (i % (r / 2)) + 0,
+// 1; a thread takes items tid, tid + NT, ..., eight of them a batch, and
+// writes each piece of a pair as one word.
+__device__ __forceinline__ void ctl_silu_pieces(const TreeArgs& a, const CtlLds& c, int b, int t, int e) {
+  const int tid = threadIdx.x, r = a.r;
+  const int us = u_stride(r);
+  const float* ub = a.u + slot_of(a, t, b, 0) * us;  // the e slots are consecutive
+  uint32_t* avw = reinterpret_cast<uint32_t*>(c.av);
+  const int r2 = r >> 1, tot = e * r2, dj = NT / r2, dq = NT - dj * r2;
+  const size_t piece = (size_t)a.p * av_stride(r) / 2;  // words
+  int j = tid / r2, q = tid - j * r2;
+  for (int b0 = 0; b0 < tot; b0 += 8 * NT) {
+    // the batch's u loads, its depth-slot reads and its P reads each go out
+    // together: no load is conditional (an item past the end re-reads the
+    // last node's pair, which is in bounds, and is not stored), so none
+    // waits behind a branch
+    float2 uv[8], pv[8];
+    int jj[8], qq[8], ws[8];
+#pragma unroll
+    for (int x = 0; x < 8; ++x) {
+      jj[x] = min(j, e - 1);
+      qq[x] = q;
+      uv[x] = *reinterpret_cast<const float2*>(ub + (size_t)jj[x] * us + 2 * q);
+      q += dq;
+      j += dj;
+      if (q >= r2) {
+        q -= r2;
+        ++j;
+      }
+    }
+#pragma unroll
+    for (int x = 0; x < 8; ++x) ws[x] = c.f->ex_ws[jj[x]];
+#pragma unroll
+    for (int x = 0; x < 8; ++x) pv[x] = *reinterpret_cast<const float2*>(c.ps + ws[x] * r + 2 * qq[x]);
+    keep_batch();
+#pragma unroll
+    for (int x = 0; x < 8; ++x)
+      if (b0 + x * NT + tid < tot) {
+        const float x0 = uv[x].x + pv[x].x, x1 = uv[x].y + pv[x].y;
+        const float v0 = x0 * sigm(x0), v1 = x1 * sigm(x1);
+        const uint16_t h0 = f32_to_bf16(v0), h1 = f32_to_bf16(v1);
+        const float s0 = v0 - bf16_to_f32(h0), s1 = v1 - bf16_to_f32(h1);
+        const uint16_t m0 = f32_to_bf16(s0), m1 = f32_to_bf16(s1);
+        const uint16_t l0 = f32_to_bf16(s0 - bf16_to_f32(m0)), l1 = f32_to_bf16(s1 - bf16_to_f32(m1));
+        uint32_t* o = avw + (size_t)jj[x] * (av_stride(r) / 2) + qq[x];
+        o[0] = (uint32_t)h0 | ((uint32_t)h1 << 16);
+        o[piece] = (uint32_t)m0 | ((uint32_t)m1 << 16);
+        o[2 * piece] = (uint32_t)l0 | ((uint32_t)l1 << 16);
+      }
+  }
+}
+
+// a = SiLU(u + P_d) in fp32 (the vector-FMA correction), element i of every
+// node by thread i mod NT.
+__device__ __forceinline__ void ctl_silu_f32(const TreeArgs& a, const CtlLds& c, int b, int t, int e) {
+  const int tid = threadIdx.x, r = a.r;
+  const int us = u_stride(r);
+  const float* ub = a.u + slot_of(a, t, b, 0) * us;
+  for (int i = tid; i < r; i += NT) {
+    float uv[PMAX];
+#pragma unroll
+    for (int j = 0; j < PMAX; ++j) uv[j] = ub[(size_t)min(j, e - 1) * us + i];  // in bounds, no branch
+    keep_batch();
+#pragma unroll
+    for (int j = 0; j < PMAX; ++j)
+      if (j < e) {
+        const float x = uv[j] + c.ps[c.f->ex_ws[j] * r + i];
+        c.av[j * r + i] = x * sigm(x);
+      }
+  }
+}
+
 template <typename W>
 __device__ __forceinline__ void ctl_expand(const TreeArgs& a, const CtlLds& c, int b, int t, int e) {
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
@@ -1162,73 +1326,11 @@ __device__ __forceinline__ void ctl_expand(const TreeArgs& a, const CtlLds& c, i
   // dL on the matrix cores (bf16 weights; not needed for marginal scores)
   const bool mf = dl_on_mfma(a, (int)sizeof(W));
   // a_j = SiLU(u_j + P_{d_j}); the u loads of all nodes are issued first
-  const int us = u_stride(r);
-  const float* ub = a.u + slot_of(a, t, b, 0) * us;  // the e slots are consecutive
-  if (a.marginal) {
-    // no correction: no activations
-  } else if (mf) {
-    // pairs of elements: item i is node i / (r / 2), elements 2 (i % (r / 2)) + 0, 1;
-    // a thread takes items tid, tid + NT, ..., eight of them a batch (their u
-    // loads issued together), and writes each piece of a pair as one word
-    uint32_t* avw = reinterpret_cast<uint32_t*>(c.av);
-    const int r2 = r >> 1, tot = e * r2, dj = NT / r2, dq = NT - dj * r2;
-    const size_t piece = (size_t)a.p * av_stride(r) / 2;  // words
-    int j = tid / r2, q = tid - j * r2;
-    for (int b0 = 0; b0 < tot; b0 += 8 * NT) {
-      // the batch's u loads, its depth-slot reads and its P reads each go out
-      // together: no load is conditional (an item past the end re-reads the
-      // last node's pair, which is in bounds, and is not stored), so none
-      // waits behind a branch
-      float2 uv[8], pv[8];
-      int jj[8], qq[8], ws[8];
-#pragma unroll
-      for (int x = 0; x < 8; ++x) {
-        jj[x] = min(j, e - 1);
-        qq[x] = q;
-        uv[x] = *reinterpret_cast<const float2*>(ub + (size_t)jj[x] * us + 2 * q);
-        q += dq;
-        j += dj;
-        if (q >= r2) {
-          q -= r2;
-          ++j;
-        }
-      }
-#pragma unroll
-      for (int x = 0; x < 8; ++x) ws[x] = c.f->ex_ws[jj[x]];
-#pragma unroll
-      for (int x = 0; x < 8; ++x) pv[x] = *reinterpret_cast<const float2*>(c.ps + ws[x] * r + 2 * qq[x]);
-      keep_batch();
-#pragma unroll
-      for (int x = 0; x < 8; ++x)
-        if (b0 + x * NT + tid < tot) {
-          const float x0 = uv[x].x + pv[x].x, x1 = uv[x].y + pv[x].y;
-          const float v0 = x0 * sigm(x0), v1 = x1 * sigm(x1);
-          // v = hi + mid + lo, each a bf16 (nearest even): the products with
-          // bf16 W2 are exact in fp32
-          const uint16_t h0 = f32_to_bf16(v0), h1 = f32_to_bf16(v1);
-          const float s0 = v0 - bf16_to_f32(h0), s1 = v1 - bf16_to_f32(h1);
-          const uint16_t m0 = f32_to_bf16(s0), m1 = f32_to_bf16(s1);
-          const uint16_t l0 = f32_to_bf16(s0 - bf16_to_f32(m0)), l1 = f32_to_bf16(s1 - bf16_to_f32(m1));
-          uint32_t* o = avw + (size_t)jj[x] * (av_stride(r) / 2) + qq[x];
-          o[0] = (uint32_t)h0 | ((uint32_t)h1 << 16);
-          o[piece] = (uint32_t)m0 | ((uint32_t)m1 << 16);
-          o[2 * piece] = (uint32_t)l0 | ((uint32_t)l1 << 16);
-        }
-    }
-  } else {
-    for (int i = tid; i < r; i += NT) {
-      float uv[PMAX];
-#pragma unroll
-      for (int j = 0; j < PMAX; ++j)
-        if (j < e) uv[j] = ub[(size_t)j * us + i];
-      keep_batch();
-#pragma unroll
-      for (int j = 0; j < PMAX; ++j)
-        if (j < e) {
-          const float x = uv[j] + c.ps[c.f->ex_ws[j] * r + i];
-          c.av[j * r + i] = x * sigm(x);
-        }
-    }
+  if (!a.marginal) {
+    if (mf)
+      ctl_silu_pieces(a, c, b, t, e);
+    else
+      ctl_silu_f32(a, c, b, t, e);
   }
   __syncthreads();
   // dL_{j,m} = W2[:, cand_m] . a_j.
@@ -2118,9 +2220,15 @@ __device__ __forceinline__ void controller_main(const TreeArgs& a, unsigned char
     steps = t + 1;
     expanded += e;
     const uint32_t epoch = a.ebase + (uint32_t)t + 1u;
+    // the workers' acknowledgements of step t.  Scoring needs u alone: here
+    // only the workers holding the W1_S^T tiles are waited for; the others'
+    // (gh rows, which the next step's advance reads) are checked before the
+    // next publication, their words read while the step is scored.
+    const bool ack_wait = !(t == 0 && !a.root);  // zero roots: step 0's products are set up above
+    const uint32_t* box = a.mbox_c + (size_t)b * 256;
+    const int uwn = min(a.uwn, a.n_workers);
     if (tid < 64) {
-      const bool ok = (t == 0 && !a.root) ||  // zero roots: step 0's products are set up above
-                      wait_mbox(a.mbox_c + (size_t)b * 256, a.n_workers, epoch, a.err, a.spin_limit);
+      const bool ok = !ack_wait || wait_mbox(box + a.uw0, uwn, epoch, a.err, a.spin_limit);
       if (tid == 0) c.f->misc[C_OK] = ok;
     }
     __syncthreads();
@@ -2129,8 +2237,30 @@ __device__ __forceinline__ void controller_main(const TreeArgs& a, unsigned char
       break;
     }
     ctl_expand<W>(a, c, b, t, e);
+    const bool ack_rest = ack_wait && uwn < a.n_workers;
+    uint32_t acks[4];  // wave 0: every worker's word, read while merge and pop run
+    if (ack_rest && tid < 64) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        acks[q] = __hip_atomic_load(box + min(tid + 64 * q, a.n_workers - 1), __ATOMIC_RELAXED,
+                                    __HIP_MEMORY_SCOPE_AGENT);
+    }
     ctl_merge(a, c, e * a.k);
     const int e2 = ctl_pop(a, c, b, t);
+    if (ack_rest && e2 > 0) {
+      if (tid < 64) {
+        bool in = true;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) in &= acks[q] >= epoch;
+        const bool ok = __all(in) || wait_mbox(box, a.n_workers, epoch, a.err, a.spin_limit);
+        if (tid == 0 && !ok) c.f->misc[C_OK] = 0;
+      }
+      __syncthreads();
+      if (!c.f->misc[C_OK]) {
+        failed = true;
+        break;
+      }
+    }
     if (e2 == 0) break;
     if (t + 1 > a.N) {  // cannot happen: every step takes one of the N best nodes
       if (tid == 0) atomicOr(a.err, 2);
@@ -2211,7 +2341,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 // host side: schedule and launch
 
 size_t plan_tree(TreeArgs& a, int wdtype_bf16, int pops, int max_workers, int lds_workers, int halves,
-                 int ctl_advance) {
+                 int ctl_advance, int device_exchange) {
   const int esz = wdtype_bf16 ? 2 : 4;
   const size_t lds_max = 160 * 1024;
   const int kp = k_padded(a.ds);
@@ -2269,6 +2399,17 @@ size_t plan_tree(TreeArgs& a, int wdtype_bf16, int pops, int max_workers, int ld
     a.halves = hv;
     a.bh = hv == 2 ? bh2 : a.B;
     a.wadv = regw && !ctl_advance ? 1 : 0;
+    a.xlocal = a.wadv && !device_exchange ? 1 : 0;
+    // the blocks holding the W1_S^T tiles: block w has tile group w / nb
+    a.uw0 = 0;
+    a.uwn = n_workers;
+    if (regw) {
+      const int tw = regw == 1 ? 1 : 2, cpb = regw == 4 ? 4 : regw == 3 ? 2 : 1;
+      const int nbk = (ncb + cpb - 1) / cpb, tpb = 4 * tw;  // column groups, tiles per block
+      const int u0 = 3 * a.ds / 16, u1 = (3 * a.ds + a.r + 15) / 16;  // tiles [u0, u1) hold u rows
+      a.uw0 = (u0 / tpb) * nbk;
+      a.uwn = ((u1 - 1) / tpb - u0 / tpb + 1) * nbk;
+    }
     a.n_workers = n_workers;
     a.qmax = qmax;
     a.xcap = xcap;

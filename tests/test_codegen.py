@@ -108,6 +108,54 @@ def test_wide_store_data_not_overwritten_next(asm, tmpl):
     assert not bad, bad[:5]
 
 
+def _sregs(op):
+    m = re.match(r"s\[(\d+):(\d+)\]$", op)
+    if m:
+        return set(range(int(m.group(1)), int(m.group(2)) + 1))
+    m = re.match(r"s(\d+)$", op)
+    return {int(m.group(1))} if m else set()
+
+
+@pytest.mark.parametrize("tmpl", ["t", "f"])
+def test_asm_memory_base_not_written_by_valu_just_before(asm, tmpl):
+    # a vector instruction writing a scalar register needs five wait states
+    # before a memory instruction reads it as an address; the compiler's hazard
+    # check does not see into inline asm, so the asm must provide them
+    body = [l for l in _kernel(asm, tmpl)[0] if l and not l.startswith(".") and not l.endswith(":")]
+    inside, bad, checked = False, [], 0
+    for i, l in enumerate(body):
+        if l.startswith(";;#ASMSTART"):
+            inside = True
+            continue
+        if l.startswith(";;#ASMEND"):
+            inside = False
+            continue
+        if not inside or not l.startswith(("global_", "buffer_")):
+            continue
+        ops = [o.strip() for o in l.split(None, 1)[1].split(",")]
+        sbase = set().union(*[_sregs(o) for o in ops[2:3]]) if len(ops) > 2 else set()
+        if not sbase:
+            continue
+        checked += 1
+        waits, j = 0, i - 1
+        while j >= 0 and waits < 5:
+            prev = body[j]
+            j -= 1
+            if prev.startswith(";"):
+                continue
+            if prev.startswith("s_nop"):
+                waits += int(prev.split()[1]) + 1
+                continue
+            if prev.startswith("v_"):
+                dsts = [o.strip() for o in prev.split(None, 1)[1].split(",")[:2]]
+                if any(_sregs(d) & sbase for d in dsts):
+                    bad.append((prev, l))
+                    break
+            waits += 1
+    assert checked, "no asm memory instruction with a scalar base found"
+    assert not bad, bad[:5]
+
+
 # ---- the dense-product and chain-head kernels
 
 CSRC = os.path.join(ROOT, "conditional_draft_tree_dominotree_amd", "csrc")

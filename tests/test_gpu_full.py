@@ -115,6 +115,23 @@ def test_q8b_b32_fma_correction(dev, q8b_builder):
         q8b_builder.set_schedule()
 
 
+def test_q8b_b32_device_wide_exchange_same_trees(dev, q8b_builder):
+    # the column groups' state exchange through their XCD's L2 (the default
+    # where a group runs on one XCD) and device-wide move the same values in
+    # the same order: the trees are the same bit for bit
+    spec, w, req = synth.workload("q8b_b32")
+    local = gu.run(q8b_builder, spec, req)
+    q8b_builder.set_schedule(exchange=1)
+    try:
+        device = gu.run(q8b_builder, spec, req)
+    finally:
+        q8b_builder.set_schedule()
+    for key in ("tokens", "parents", "depths", "scores", "n_nodes"):
+        np.testing.assert_array_equal(local[key], device[key], err_msg=key)
+    reps, _ = gu.compare(spec, w, req, device, requests=[0, 31])
+    gu.assert_parity(reps, [0, 31])
+
+
 def test_q8b_b32_fullv_and_smaller_batch_reuse_handle(dev, q8b_builder):
     # the same handle serves a smaller batch and the full-vocabulary normaliser
     spec, w, req = synth.workload("q8b_b32")
