@@ -61,7 +61,8 @@ struct TreeArgs {
                            // that step and half of the batch are advanced
   uint32_t* ready;         // [64] controller b: its start-up loads are done (the workers then load weights)
   uint32_t* xccw;          // [256] worker w: the XCC (XCD) its block runs on, this launch
-  uint32_t* mbox_w;        // [n_workers][32] controller -> worker mailboxes (one line each)
+  uint32_t* mbox_w;        // [MBOX_REPL][32] controller -> worker mailbox words, one copy of a request's
+                           // word per line; worker w polls copy w % MBOX_REPL
   uint32_t* mbox_c;        // [B][256] worker -> controller mailboxes
   int* err;                // device error word
   int* err_host;           // pinned host mirror: a controller that ends with err set copies it there
@@ -72,6 +73,9 @@ struct TreeArgs {
   unsigned spin_limit;
   uint32_t ebase;          // epochs of this launch: ebase + 1 .. ebase + tree_epoch_span(N) - 1
 };
+// Copies of the controller -> worker mailbox line: each controller writes its
+// word into every copy, and the workers' polls spread over the copies.
+constexpr int MBOX_REPL = 8;
 // Exchange columns a build may use per step (slots per step = B p <= this).
 constexpr int TREE_MAX_COLS = 512;
 constexpr int GFLAG_WORDS = 16 * 64 + 64 + 256;  // worker group flags, controller ready flags and the

@@ -41,11 +41,14 @@
 //
 // Exchange between blocks: every published value is written once per launch
 // to its own 128-byte-aligned slot with device-scope (sc1) stores; after the
-// stores complete the producer raises a flag word in each consumer's mailbox
-// line (sc1 store); a consumer polls only its own mailbox line (sc1 loads)
-// and then reads the published slots.  Slots are never read before they are
-// published, so no cache holds a stale copy.  Every wait is bounded: when it
-// runs out the block sets the error word and leaves its loop.
+// stores complete the producer raises a flag word in its consumers' mailbox
+// lines (sc1 store; the controllers' words to the workers go to eight copies
+// of one line, each polled by an eighth of the workers); a consumer polls its
+// mailbox line (sc1 loads) and then reads the published slots.  Slots are
+// never read before they are published, so no cache holds a stale copy.
+// Blocks of one worker column group that run on one XCD pass the operand
+// copies and their group flags through that XCD's L2 instead.  Every wait is
+// bounded: when it runs out the block sets the error word and leaves its loop.
 #include <algorithm>
 
 #include "common.h"
@@ -489,7 +492,7 @@ __device__ __forceinline__ void worker_columns(const TreeArgs& a, int w, int t, 
   const int tid = threadIdx.x, lane = tid & 63;
   const uint32_t epoch = a.ebase + (uint32_t)t + 1u;
   if (tid < 64) {
-    const uint32_t* mybox = a.mbox_w + (size_t)w * 32 + b0;
+    const uint32_t* mybox = a.mbox_w + (size_t)(w % MBOX_REPL) * 32 + b0;
     uint32_t word = 0;
     const bool ok = wait_mbox(mybox, nb, epoch << 5, a.err, a.spin_limit, &word);
     const int b = b0 + lane;
@@ -1785,8 +1788,11 @@ __device__ __forceinline__ int ctl_pop(const TreeArgs& a, const CtlLds& c, int b
       }
     }
     if (Q <= 0) break;
-    // cnt[j] = records that precede entry j of the batch
-    {
+    // cnt[j] = records that precede entry j of the batch.  Entry j is out when
+    // cnt[j] + j >= N + 1; cnt[j] <= nx, so while nx + Q - 1 < N + 1 no entry
+    // of the batch can be out and the counts are not needed.
+    const bool counts = nx + Q - 1 >= N + 1;
+    if (counts) {
       int Qp = 1;
       while (Qp < Q) Qp <<= 1;
       const int S = min(64, 256 / Qp);
@@ -1817,8 +1823,8 @@ __device__ __forceinline__ int ctl_pop(const TreeArgs& a, const CtlLds& c, int b
       }
       for (int m = S >> 1; m >= 1; m >>= 1) cv += __shfl_xor(cv, m);
       if (j < Q && s == 0) c.f->cnt[j] = cv;
+      __syncthreads();
     }
-    __syncthreads();
     // wave 0, lane jj = the jj-th batch entry in the total order: the taken
     // entries are the longest prefix that is not out and fits the step
     if (tid < 64) {
@@ -1830,7 +1836,7 @@ __device__ __forceinline__ int ctl_pop(const TreeArgs& a, const CtlLds& c, int b
         // key order is the total order: everything on registers and ballots
         const int e0 = c.f->misc[C_E];
         const int nl0 = c.f->misc[C_NL];
-        const int cl = has ? c.f->cnt[lane] : 0;
+        const int cl = has && counts ? c.f->cnt[lane] : 0;
         int wdl = lane < a.nslots ? c.f->wdep[lane] : -1;  // lane s: slot s
         int wcl = lane < a.nslots ? c.f->wclaim[lane] : 0;
         const uint64_t key = fl;
@@ -1945,7 +1951,7 @@ __device__ __forceinline__ int ctl_pop(const TreeArgs& a, const CtlLds& c, int b
       const uint64_t key = has ? F[j] : 0ull;
       const int d = key_depth(key);
       const bool expd = has && d < D;
-      const bool out = has && c.f->cnt[j] + lane >= N + 1;
+      const bool out = has && counts && c.f->cnt[j] + lane >= N + 1;
       const int e0 = c.f->misc[C_E];
       // depth slots: a depth is new if no slot holds it and no earlier lane has it
       int held = 0, held_claimed = 0, nclaimed = 0;
@@ -2207,7 +2213,7 @@ __device__ __forceinline__ void controller_main(const TreeArgs& a, unsigned char
   stores_done();
   __syncthreads();
   if (a.root)
-    for (int w = tid; w < a.n_workers; w += NT) st_dev_u32(a.mbox_w + (size_t)w * 32 + b, mbox_word(a.ebase + 1, 1));
+    if (tid < MBOX_REPL) st_dev_u32(a.mbox_w + (size_t)tid * 32 + b, mbox_word(a.ebase + 1, 1));
   stores_done();
   ctl_prefetch<W>(a, c, b);
   __syncthreads();
@@ -2284,22 +2290,20 @@ __device__ __forceinline__ void controller_main(const TreeArgs& a, unsigned char
           st_dev_u64(a.ninfo + (size_t)(t + 1) * TREE_MAX_COLS + sl,
                      ninfo_entry(a.ebase + t + 2, (uint32_t)c.f->ex_tok[tid], (uint32_t)xs));
         }
-        for (int w = tid; w < a.n_workers; w += 64)
-          st_dev_u32(a.mbox_w + (size_t)w * 32 + b, mbox_word(a.ebase + t + 2, e2));
+        if (tid < MBOX_REPL) st_dev_u32(a.mbox_w + (size_t)tid * 32 + b, mbox_word(a.ebase + t + 2, e2));
       }
     } else {
       ctl_advance<W>(a, c, b, t + 1, e2);
       stores_done();
       __syncthreads();
-      for (int w = tid; w < a.n_workers; w += NT)
-        st_dev_u32(a.mbox_w + (size_t)w * 32 + b, mbox_word(a.ebase + t + 2, e2));
+      if (tid < MBOX_REPL) st_dev_u32(a.mbox_w + (size_t)tid * 32 + b, mbox_word(a.ebase + t + 2, e2));
     }
     ctl_prefetch<W>(a, c, b);  // overlaps the workers' step
     __syncthreads();
   }
   // release the workers from this request
-  for (int w = tid; w < a.n_workers; w += NT)
-    st_dev_u32(a.mbox_w + (size_t)w * 32 + b, mbox_word(a.ebase + tree_epoch_span(a.N) - 1, MBOX_DONE_E));
+  if (tid < MBOX_REPL)
+    st_dev_u32(a.mbox_w + (size_t)tid * 32 + b, mbox_word(a.ebase + tree_epoch_span(a.N) - 1, MBOX_DONE_E));
   stores_done();
   ctl_output(a, c, b, failed);
   if (a.stats && tid == 0) {
