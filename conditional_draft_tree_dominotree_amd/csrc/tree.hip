@@ -984,6 +984,7 @@ enum {
   C_NL,      // depth slots to load
   C_G,       // where the best entry of an over-long tie group came from
   C_NV,      // live new entries of a merge
+  C_TIE,     // the merge's cut after N + 1 entries falls inside a group of equal key_u
   C_MISC
 };
 
@@ -1611,7 +1612,10 @@ __device__ __forceinline__ void ctl_expand(const TreeArgs& a, const CtlLds& c, i
 // there.  Keys are unique.  First the live new entries are ranked among
 // themselves (S threads per entry), then each thread writes its share of the
 // merged order, found by a binary search on its first output's diagonal
-// (merge path).  Also resets the pop state of the step.
+// (merge path).  Only the first N + 1 merged entries are kept, unless the
+// next one has the same key_u as entry N: an entry with N + 1 entries of
+// greater key_u ahead of it could only be taken after all of them, with N + 1
+// records ahead, so it never is.  Also resets the pop state of the step.
 __device__ __forceinline__ void ctl_merge(const TreeArgs& a, const CtlLds& c, int nnew) {
   const int tid = threadIdx.x;
   const int fh = c.f->misc[C_FH], nf = c.f->misc[C_NF], fb = c.f->misc[C_FB];
@@ -1651,14 +1655,19 @@ __device__ __forceinline__ void ctl_merge(const TreeArgs& a, const CtlLds& c, in
       if ((tid & 63) == 0 && bl) atomicAdd(&c.f->misc[C_NV], __popcll(bl));
     }
   }
+  if (tid == 0) c.f->misc[C_TIE] = 0;
   __syncthreads();
   const int nv = c.f->misc[C_NV];
   const uint64_t* Nw = c.ncs;
-  {
-    // (k - 1) xcap + 1 bounds the frontier; the guard only keeps intact
-    const int total = min(na + nv, a.fcap);
-    const int L = (na + nv + NT - 1) / NT;
-    const int d0 = min(tid * L, total), d1 = min(d0 + L, total);
+  // (k - 1) xcap + 1 bounds the frontier; the guard only keeps intact
+  const int full = min(na + nv, a.fcap);
+  const int cut = min(full, a.N + 1);
+  int total = cut;
+  for (int pass = 0; pass < 2; ++pass) {
+    // outputs [o0, o1): the first N + 1, then (rarely) the rest
+    const int o0 = pass ? cut : 0, o1 = pass ? full : cut;
+    const int L = (o1 - o0 + NT - 1) / NT;
+    const int d0 = min(o0 + tid * L, o1), d1 = min(d0 + L, o1);
     if (d0 < d1) {
       // i old and d0 - i new entries precede output d0
       int lo = max(0, d0 - nv), hi = min(d0, na);
@@ -1669,9 +1678,11 @@ __device__ __forceinline__ void ctl_merge(const TreeArgs& a, const CtlLds& c, in
       }
       int i = lo, j = d0 - lo;
       uint64_t fi = i < na ? F[i] : 0ull, nj = j < nv ? Nw[j] : 0ull;
+      uint64_t last = 0ull;
       for (int d = d0; d < d1; ++d) {
         const bool old = j >= nv || (i < na && fi > nj);
-        O[d] = old ? fi : nj;
+        last = old ? fi : nj;
+        O[d] = last;
         if (old) {
           ++i;
           fi = i < na ? F[i] : 0ull;
@@ -1680,13 +1691,22 @@ __device__ __forceinline__ void ctl_merge(const TreeArgs& a, const CtlLds& c, in
           nj = j < nv ? Nw[j] : 0ull;
         }
       }
+      if (!pass && d1 == cut && cut < full) {
+        // the entry after the cut: does it share entry N's key_u?
+        const uint64_t nxt = (j >= nv || (i < na && fi > nj)) ? fi : nj;
+        if (key_u(nxt) == key_u(last)) c.f->misc[C_TIE] = 1;
+      }
     }
+    if (pass) break;
+    __syncthreads();
+    if (!c.f->misc[C_TIE]) break;
+    total = full;
   }
   if (tid == 0) {
     if (na + nv > a.fcap) atomicOr(a.err, 4);
     c.f->misc[C_FB] = 1 - fb;
     c.f->misc[C_FH] = 0;
-    c.f->misc[C_NF] = min(na + nv, a.fcap);
+    c.f->misc[C_NF] = total;
     c.f->misc[C_E] = 0;
     c.f->misc[C_STOP] = 0;
     c.f->misc[C_NL] = 0;

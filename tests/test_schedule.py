@@ -5,8 +5,9 @@ frontier entry only if fewer than N + 1 taken records precede it in the total
 order (score desc, depth asc, token asc, parent's order asc), compacts its
 record set when full, and ranks the records at the end.  This model follows
 the same schedule step for step (batches that do not end inside a group of
-equal keys, the acceptance test, pruning with tau, compaction, the recursive
-comparator for equal keys) on random trees with many exact ties, and checks
+equal keys, the acceptance test, pruning with tau, the frontier cut after N + 1
+entries outside a tie group, compaction, the recursive comparator for equal
+keys) on random trees with many exact ties, and checks
 that it returns exactly the tree of the one-node-at-a-time heap.  It shares no
 code with the kernel or with the oracle; the GPU parity tests check the kernel.
 """
@@ -67,6 +68,10 @@ def model_build(children, N, p, qmax, D):
             front = [f for f in front if f[0] >= tau]
             new = [f for f in new if f[0] >= tau]
         front = sorted(front + new, key=key, reverse=True)
+        # keep N + 1 entries unless entry N + 1 shares entry N's U: the rest
+        # have N + 1 entries of greater U ahead of them and are never taken
+        if len(front) > N + 1 and front[N + 1][0] != front[N][0]:
+            front = front[:N + 1]
         # pop
         ex = []
         stop = False
