@@ -29,8 +29,12 @@ struct TreeArgs {
                         // turn, so that one half's products overlap the other half's scoring; else 1
   int bh;               // requests in the first half (B when halves = 1)
   int wadv;             // 1: the workers advance the GRU states of a step's nodes (register workers)
-  int uw0, uwn;         // the workers [uw0, uw0 + uwn) hold the W1_S^T tiles: once they acknowledge a
-                        // step, its u rows are stored (all workers unless register workers)
+  int ncg, cpg;         // register workers: column groups and columns per group (16 per column block).
+                        // Column c of a half's p B_h columns is node c % p of the half's request c / p;
+                        // block w serves the columns [cpg g, cpg (g + 1)) of group g = w % ncg, with the
+                        // tile group w / ncg
+  int ugq0, ugq1;       // register workers: the tile groups [ugq0, ugq1] hold the W1_S^T tiles; once
+                        // they acknowledge a step, its u rows are stored
   int xlocal;           // register workers: 1 lets a column group whose blocks all run on one XCD
                         // (checked at the launch's first exchange) exchange advanced states through
                         // that XCD's L2 instead of device-wide

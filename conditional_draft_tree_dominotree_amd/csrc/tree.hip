@@ -195,21 +195,16 @@ __device__ __forceinline__ uint64_t key_with_parent(uint64_t k, int parent) {
   return (k & ~(2047ull << 10)) | ((uint64_t)parent << 10);
 }
 
-// bounded wait until every word of one mailbox line is >= need; wave-uniform
-// Poll box[0..nwords) (nwords <= 64 Q) until every word is >= need.  Two
-// polls are in flight at a time: the next one is issued before the previous
-// one is examined, so a word that lands is seen about half a load latency
-// sooner than with polls issued one after the other.  The loads are
-// device-coherent (relaxed, agent scope); lanes past nwords re-read the last
-// word.  On success *word0, when given, receives what the deciding poll read
-// at box[min(lane, nwords - 1)].
+// Bounded wait, wave-uniform: poll the words at p[0..Q) of every lane until
+// all are >= need.  Two polls are in flight at a time: the next one is issued
+// before the previous one is examined, so a word that lands is seen about half
+// a load latency sooner than with polls issued one after the other.  The loads
+// are device-coherent (relaxed, agent scope).  On success *word0, when given,
+// receives what the deciding poll read at p[0].
 template <int Q>
-__device__ __forceinline__ bool wait_words(const uint32_t* box, int nwords, uint32_t need, const int* err,
-                                           unsigned limit, uint32_t* word0) {
+__device__ __forceinline__ bool wait_ptrs(const uint32_t* const (&p)[Q], uint32_t need, const int* err,
+                                          unsigned limit, uint32_t* word0) {
   const int lane = threadIdx.x & 63;
-  const uint32_t* p[Q];
-#pragma unroll
-  for (int q = 0; q < Q; ++q) p[q] = box + min(lane + 64 * q, nwords - 1);
   uint32_t x[Q], y[Q];
   auto issue = [&](uint32_t (&v)[Q]) {
 #pragma unroll
@@ -246,6 +241,17 @@ __device__ __forceinline__ bool wait_words(const uint32_t* box, int nwords, uint
   }
   asm volatile("" ::: "memory");  // what the caller reads next stays after the poll that saw the words
   return true;
+}
+// The words box[0..nwords) (nwords <= 64 Q); lanes past nwords re-read the
+// last word; *word0 receives box[min(lane, nwords - 1)].
+template <int Q>
+__device__ __forceinline__ bool wait_words(const uint32_t* box, int nwords, uint32_t need, const int* err,
+                                           unsigned limit, uint32_t* word0) {
+  const int lane = threadIdx.x & 63;
+  const uint32_t* p[Q];
+#pragma unroll
+  for (int q = 0; q < Q; ++q) p[q] = box + min(lane + 64 * q, nwords - 1);
+  return wait_ptrs<Q>(p, need, err, limit, word0);
 }
 
 __device__ __forceinline__ bool wait_mbox(const uint32_t* box, int nwords, uint32_t need, const int* err,
@@ -509,6 +515,60 @@ __device__ __forceinline__ void worker_columns(const TreeArgs& a, int w, int t, 
     if (e > 0) reqs[__popcll(has & ((1ull << lane) - 1ull))] = b;
     if (lane == 63) misc[0] = ok ? incl : -1;
     if (lane == 0) misc[1] = __popcll(has);
+  }
+  __syncthreads();
+}
+
+// Register workers: the columns of block w's group at step t for the requests
+// [hb0, hb0 + hn) of a half.  Column c of the half is node c % p of request
+// hb0 + c / p, a column while that node exists.  The block waits for the words
+// of the requests its columns [col0, col0 + nc) (nc <= 64) cover, and no
+// others.  It writes coln[i] (i < nc): the slot staged for column col0 + i (a
+// present column's slot where the node does not exist), coln[64 + k]: the
+// slot of the k-th present column, reqs: the requests among those still
+// running; misc[0] = present columns (-1: a wait ran out), misc[1] = running
+// requests, misc[4] = 1 when every request of these columns is finished,
+// misc[6], misc[7] = the mask of present columns.
+__device__ __forceinline__ void worker_columns_fixed(const TreeArgs& a, int w, int t, int hb0, int hn, int col0,
+                                                     int nc, int* coln, int* reqs, int* misc) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int p = a.p;
+  const int c1 = min(col0 + nc, hn * p);
+  if (tid < 64) {
+    int nval = 0, nact = 0, fin = 1;
+    unsigned long long vm = 0;
+    bool ok = true;
+    if (col0 < c1) {
+      const uint32_t epoch = a.ebase + (uint32_t)t + 1u;
+      const int rb0 = col0 / p, nr = (c1 - 1) / p - rb0 + 1;  // <= nc <= 64
+      uint32_t word = 0;
+      ok = wait_mbox(a.mbox_w + (size_t)(w % MBOX_REPL) * 32 + hb0 + rb0, nr, epoch << 5, a.err, a.spin_limit,
+                     &word);
+      // a request still running expands at least one node this step
+      const bool live = ok && lane < nr && (word & 31u) != MBOX_DONE_E;
+      const int e = live ? (int)(word & 31u) : 0;
+      const unsigned long long act = __ballot(live);
+      fin = act == 0ull;
+      nact = __popcll(act);
+      if (live) reqs[__popcll(act & ((1ull << lane) - 1ull))] = hb0 + rb0 + lane;
+      // lane i: column col0 + i
+      const int c = col0 + lane;
+      const int er = __shfl(e, min(max(c / p - rb0, 0), 63));
+      const bool v = lane < nc && c < c1 && c % p < er;
+      const int s = v ? (int)slot_of(a, t, hb0 + c / p, c % p) : -1;
+      vm = __ballot(v);
+      nval = __popcll(vm);
+      const int s0 = __shfl(s, vm ? __ffsll((long long)vm) - 1 : 0);
+      if (lane < nc) coln[lane] = v ? s : s0;
+      if (v) coln[64 + __popcll(vm & ((1ull << lane) - 1ull))] = s;
+    }
+    if (lane == 0) {
+      misc[0] = ok ? nval : -1;
+      misc[1] = nact;
+      misc[4] = fin;
+      misc[6] = (int)(uint32_t)vm;
+      misc[7] = (int)(uint32_t)(vm >> 32);
+    }
   }
   __syncthreads();
 }
@@ -787,8 +847,8 @@ __device__ __forceinline__ void worker_regs(const TreeArgs& a, unsigned char* ld
   uint16_t* stage = reinterpret_cast<uint16_t*>(lds + REGW_STAGE_OFFSET);  // [16 CPB][RSTRIDE]
   const int kp = RKB * 32;
   const int as = act_stride(a.ds);
-  const int nb = (a.ncbmax + CPB - 1) / CPB;
-  const int col0 = (w % nb) * CPB * 16;  // first column of the block
+  const int nb = a.ncg;  // column groups
+  const int col0 = (w % nb) * CPB * 16;  // first column of the block (a.cpg = 16 CPB)
   const int tile0 = ((w / nb) * 4 + wv) * TW;
   const int grp = w % nb, gq = w / nb, ngq = a.n_workers / nb;  // the blocks sharing these columns
   // the group's exchange: -1 undecided (device-wide until the first one has
@@ -821,21 +881,24 @@ __device__ __forceinline__ void worker_regs(const TreeArgs& a, unsigned char* ld
     // group flags: 2 epoch + h, increasing over (step, half) and across launches
     // whatever their number of halves
     const uint32_t gepoch = 2u * epoch + (uint32_t)h;
-    worker_columns(a, w, t, h ? a.bh : 0, h ? a.B - a.bh : a.bh, coln, reqs, misc);
-    const int ncols = misc[0], nreq = misc[1];
-    if (ncols < 0) return;  // a wait ran out
-    if (ncols == 0) {       // every request of this half is finished
+    worker_columns_fixed(a, w, t, h ? a.bh : 0, h ? a.B - a.bh : a.bh, col0, 16 * CPB, coln, reqs, misc);
+    const int nval = misc[0], nreq = misc[1];
+    const unsigned long long vmask = (unsigned long long)(uint32_t)misc[6] | ((unsigned long long)(uint32_t)misc[7] << 32);
+    if (nval < 0) return;  // a wait ran out
+    if (misc[4]) {         // every request of these columns is finished
       done[h] = true;
-      __syncthreads();      // misc is read by every thread before wave 0 writes it again
+      __syncthreads();     // misc is read by every thread before wave 0 writes it again
       continue;
     }
-    if (col0 < ncols) {
+    if (nval > 0) {  // the same for every block of the group (it reads the same words)
+      floatx4 sv[WG];  // this block's last advanced states, stored once the operands are staged
+      float* sp[WG];
+#pragma unroll
+      for (int g = 0; g < WG; ++g) sp[g] = nullptr;
       if (a.wadv && t > 0) {
         // the group advances the states of its columns, then waits for all of it
         const bool loc = xmode == 1;
-        floatx4 sv[WG];
-        float* sp[WG];
-        worker_advance(a, coln, t, col0, min(16 * CPB, ncols - col0), gq, ngq, loc, sv, sp);
+        worker_advance(a, coln + 64, t, 0, nval, gq, ngq, loc, sv, sp);
         stores_done();
         __syncthreads();
         if (tid == 0) {
@@ -857,9 +920,6 @@ __device__ __forceinline__ void worker_regs(const TreeArgs& a, unsigned char* ld
         }
         __syncthreads();
         if (xmode < 0) xmode = misc[3] ? 1 : 0;  // the same for every block of the group
-#pragma unroll
-        for (int g = 0; g < WG; ++g)
-          if (sp[g]) st_dev_f32x4(sp[g], sv[g]);
         if (!misc[2]) return;
       }
       // stage: thread piece tid + 256 q = column (tid >> 7) + 2 q, 16-byte piece tid & 127
@@ -872,8 +932,8 @@ __device__ __forceinline__ void worker_regs(const TreeArgs& a, unsigned char* ld
         constexpr int NB = CPB == 1 ? 8 : 16;
         unsigned off[NB];
 #pragma unroll
-        for (int q = 0; q < NB; ++q) {
-          const int c = min(col0 + (tid >> 7) + 2 * (NB * h + q), ncols - 1);  // clamped: always a valid column
+        for (int q = 0; q < NB; ++q) {  // coln holds a present column's slot for every column
+          const int c = (tid >> 7) + 2 * (NB * h + q);
           off[q] = (unsigned)(((coln[c] - slot0) * as + pc * 8) * 2);
         }
         u32x4 v[NB];
@@ -883,6 +943,12 @@ __device__ __forceinline__ void worker_regs(const TreeArgs& a, unsigned char* ld
         for (int q = 0; q < NB; ++q)
           *reinterpret_cast<u32x4*>(stage + ((tid >> 7) + 2 * (NB * h + q)) * RSTRIDE + pc * 8) = v[q];
       }
+      // the states (read by later steps' advances) drain during the products
+      // and before the acknowledgement; stored earlier they would hold up the
+      // staging loads' wait
+#pragma unroll
+      for (int g = 0; g < WG; ++g)
+        if (sp[g]) st_dev_f32x4(sp[g], sv[g]);
       __syncthreads();
       if (tile0 < a.n_tiles) {
         // B operands: column (lane & 15) of each column block, k 8 (lane >> 4) + 32 kb
@@ -936,8 +1002,8 @@ __device__ __forceinline__ void worker_regs(const TreeArgs& a, unsigned char* ld
         const int ds3 = 3 * a.ds;
 #pragma unroll
         for (int c = 0; c < CPB; ++c) {
-          const int col = col0 + c * 16 + (lane & 15);
-          if (col >= ncols) continue;
+          const int col = c * 16 + (lane & 15);
+          if (!((vmask >> col) & 1ull)) continue;  // no node in this column
           const size_t slot = (size_t)coln[col];
 #pragma unroll
           for (int i = 0; i < TW; ++i) {
@@ -2179,6 +2245,24 @@ __device__ __forceinline__ void ctl_output(const TreeArgs& a, const CtlLds& c, i
   if (tid == 0) a.n_nodes[b] = failed ? -1 : n;
 }
 
+// Register workers: the acknowledgement words request b waits for, those of
+// the blocks of tile groups [q0, q1] in the column groups its p columns fall
+// in (block (q0 + i / ng) ncg + g0 + i % ng for word i); two per lane
+// (at most 128 words), lanes past the set re-reading its last word.
+__device__ __forceinline__ void ack_ptrs(const TreeArgs& a, const uint32_t* box, int b, int q0, int q1,
+                                         const uint32_t* (&p)[2]) {
+  const int lane = threadIdx.x & 63;
+  const int hb0 = (a.halves == 2 && b >= a.bh) ? a.bh : 0;
+  const int c0 = (b - hb0) * a.p;
+  const int g0 = c0 / a.cpg, ng = (c0 + a.p - 1) / a.cpg - g0 + 1;
+  const int n = (q1 - q0 + 1) * ng;
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int i = min(lane + 64 * q, n - 1);
+    p[q] = box + (size_t)(q0 + i / ng) * a.ncg + g0 + i % ng;
+  }
+}
+
 template <typename W>
 __device__ __forceinline__ void controller_main(const TreeArgs& a, unsigned char* lds) {
   const int b = blockIdx.x - a.n_workers;
@@ -2246,15 +2330,24 @@ __device__ __forceinline__ void controller_main(const TreeArgs& a, unsigned char
     steps = t + 1;
     expanded += e;
     const uint32_t epoch = a.ebase + (uint32_t)t + 1u;
-    // the workers' acknowledgements of step t.  Scoring needs u alone: here
-    // only the workers holding the W1_S^T tiles are waited for; the others'
+    // the workers' acknowledgements of step t.  Register workers: only the
+    // blocks of this request's column groups; scoring needs u alone, so here
+    // only the blocks holding the W1_S^T tiles are waited for, and the others'
     // (gh rows, which the next step's advance reads) are checked before the
-    // next publication, their words read while the step is scored.
+    // next publication, their words read while the step is scored.  Other
+    // workers: all of them, here.
     const bool ack_wait = !(t == 0 && !a.root);  // zero roots: step 0's products are set up above
+    const bool fixed = a.regw != 0 && a.n_workers > 0;
     const uint32_t* box = a.mbox_c + (size_t)b * 256;
-    const int uwn = min(a.uwn, a.n_workers);
     if (tid < 64) {
-      const bool ok = !ack_wait || wait_mbox(box + a.uw0, uwn, epoch, a.err, a.spin_limit);
+      bool ok = true;
+      if (ack_wait && fixed) {
+        const uint32_t* p[2];
+        ack_ptrs(a, box, b, a.ugq0, a.ugq1, p);
+        ok = wait_ptrs<2>(p, epoch, a.err, a.spin_limit, nullptr);
+      } else if (ack_wait) {
+        ok = wait_mbox(box, a.n_workers, epoch, a.err, a.spin_limit);
+      }
       if (tid == 0) c.f->misc[C_OK] = ok;
     }
     __syncthreads();
@@ -2263,22 +2356,20 @@ __device__ __forceinline__ void controller_main(const TreeArgs& a, unsigned char
       break;
     }
     ctl_expand<W>(a, c, b, t, e);
-    const bool ack_rest = ack_wait && uwn < a.n_workers;
-    uint32_t acks[4];  // wave 0: every worker's word, read while merge and pop run
+    const bool ack_rest = ack_wait && fixed;
+    const uint32_t* pr[2];
+    uint32_t acks[2];  // wave 0: the rest of the words, read while merge and pop run
     if (ack_rest && tid < 64) {
+      ack_ptrs(a, box, b, 0, a.n_workers / a.ncg - 1, pr);
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
-        acks[q] = __hip_atomic_load(box + min(tid + 64 * q, a.n_workers - 1), __ATOMIC_RELAXED,
-                                    __HIP_MEMORY_SCOPE_AGENT);
+      for (int q = 0; q < 2; ++q) acks[q] = __hip_atomic_load(pr[q], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     ctl_merge(a, c, e * a.k);
     const int e2 = ctl_pop(a, c, b, t);
     if (ack_rest && e2 > 0) {
       if (tid < 64) {
-        bool in = true;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) in &= acks[q] >= epoch;
-        const bool ok = __all(in) || wait_mbox(box, a.n_workers, epoch, a.err, a.spin_limit);
+        const bool ok = __all(acks[0] >= epoch && acks[1] >= epoch) ||
+                        wait_ptrs<2>(pr, epoch, a.err, a.spin_limit, nullptr);
         if (tid == 0 && !ok) c.f->misc[C_OK] = 0;
       }
       __syncthreads();
@@ -2424,15 +2515,19 @@ size_t plan_tree(TreeArgs& a, int wdtype_bf16, int pops, int max_workers, int ld
     a.bh = hv == 2 ? bh2 : a.B;
     a.wadv = regw && !ctl_advance ? 1 : 0;
     a.xlocal = a.wadv && !device_exchange ? 1 : 0;
-    // the blocks holding the W1_S^T tiles: block w has tile group w / nb
-    a.uw0 = 0;
-    a.uwn = n_workers;
+    // register workers: column groups, and the tile groups holding the W1_S^T
+    // tiles (block w has tile group w / ncg)
+    a.ncg = 1;
+    a.cpg = 16;
+    a.ugq0 = a.ugq1 = 0;
     if (regw) {
       const int tw = regw == 1 ? 1 : 2, cpb = regw == 4 ? 4 : regw == 3 ? 2 : 1;
-      const int nbk = (ncb + cpb - 1) / cpb, tpb = 4 * tw;  // column groups, tiles per block
+      const int tpb = 4 * tw;  // tiles per block
       const int u0 = 3 * a.ds / 16, u1 = (3 * a.ds + a.r + 15) / 16;  // tiles [u0, u1) hold u rows
-      a.uw0 = (u0 / tpb) * nbk;
-      a.uwn = ((u1 - 1) / tpb - u0 / tpb + 1) * nbk;
+      a.ncg = (ncb + cpb - 1) / cpb;
+      a.cpg = 16 * cpb;
+      a.ugq0 = u0 / tpb;
+      a.ugq1 = (u1 - 1) / tpb;
     }
     a.n_workers = n_workers;
     a.qmax = qmax;
