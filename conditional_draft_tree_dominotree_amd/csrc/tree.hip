@@ -1389,6 +1389,38 @@ __device__ __forceinline__ void ctl_silu_f32(const TreeArgs& a, const CtlLds& c,
   }
 }
 
+// Within each half-wave (32 lanes): how many other lanes hold a greater value
+// than this lane.  The lanes of the same row of 16 come from DPP rotations
+// (row_ror), those of the other row from one swizzle (lane ^ 16) and its
+// rotations: no LDS traffic.
+template <int R>
+__device__ __forceinline__ uint32_t row_ror_u32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x120 + R, 0xF, 0xF, false);
+}
+__device__ __forceinline__ int half_rank32(uint32_t v) {
+  int gt = 0;
+  auto acc = [&](uint32_t o) { gt += o > v; };
+#define DT_ROW_RORS(x)                                                                                          \
+  acc(row_ror_u32<1>(x)), acc(row_ror_u32<2>(x)), acc(row_ror_u32<3>(x)), acc(row_ror_u32<4>(x)),              \
+      acc(row_ror_u32<5>(x)), acc(row_ror_u32<6>(x)), acc(row_ror_u32<7>(x)), acc(row_ror_u32<8>(x)),          \
+      acc(row_ror_u32<9>(x)), acc(row_ror_u32<10>(x)), acc(row_ror_u32<11>(x)), acc(row_ror_u32<12>(x)),       \
+      acc(row_ror_u32<13>(x)), acc(row_ror_u32<14>(x)), acc(row_ror_u32<15>(x))
+  DT_ROW_RORS(v);
+  const uint32_t x = (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, 0x401F);  // lane ^ 16 within 32 lanes
+  acc(x);
+  DT_ROW_RORS(x);
+#undef DT_ROW_RORS
+  return gt;
+}
+// OR over each half-wave.
+__device__ __forceinline__ uint32_t half_or32(uint32_t v) {
+  v |= row_ror_u32<1>(v);
+  v |= row_ror_u32<2>(v);
+  v |= row_ror_u32<4>(v);
+  v |= row_ror_u32<8>(v);
+  return v | (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, 0x401F);
+}
+
 template <typename W>
 __device__ __forceinline__ void ctl_expand(const TreeArgs& a, const CtlLds& c, int b, int t, int e) {
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
@@ -1610,21 +1642,36 @@ __device__ __forceinline__ void ctl_expand(const TreeArgs& a, const CtlLds& c, i
         if (tl[u] > -INFINITY) se += __builtin_amdgcn_exp2f((tl[u] - mx) * L2E);
         lz[u] = live ? mx + __builtin_amdgcn_logf(se) * LN2 : -INFINITY;
       }
-      // ranks among each node's candidates: every lane compares its composite
-      // with the half-wave's others, rotated one lane at a time through the
-      // permute network (distinct lanes per read: no LDS bank conflicts)
-      uint64_t me[2];
+      // ranks among each node's candidates by (value desc, token asc): by the
+      // value keys alone (lanes past M hold 0, below every value) unless a
+      // half-wave holds equal values, then by the full composites, rotated
+      // one lane at a time through the permute network
+      int rank[2];
+      bool tie = false;
 #pragma unroll
-      for (int u = 0; u < 2; ++u) me[u] = has[u] ? cand_pack(f32_key(zv[u]), (uint32_t)idv[u]) : 0ull;
-      int rank[2] = {0, 0};
-#pragma unroll
-      for (int q = 1; q < 32; ++q) {
-        const int src = (((l32 + q) & 31) | (half << 5)) << 2;  // byte address of the source lane
+      for (int u = 0; u < 2; ++u) {
+        rank[u] = half_rank32(has[u] ? f32_key(zv[u]) : 0u);
+        // distinct values take the ranks 0 .. M - 1 once each; equal values
+        // share a rank and leave others unused
+        const uint32_t seen = half_or32(has[u] ? 1u << rank[u] : 0u);
+        tie |= node[u] && __popc(seen) != M;
+      }
+      if (__ballot(tie)) {
+        uint64_t me[2];
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
-          const uint32_t oh = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)(me[u] >> 32));
-          const uint32_t ol = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)(uint32_t)me[u]);
-          rank[u] += (((uint64_t)oh << 32) | ol) > me[u];  // lanes past M hold 0, which precedes nothing
+          me[u] = has[u] ? cand_pack(f32_key(zv[u]), (uint32_t)idv[u]) : 0ull;
+          rank[u] = 0;
+        }
+#pragma unroll
+        for (int q = 1; q < 32; ++q) {
+          const int src = (((l32 + q) & 31) | (half << 5)) << 2;  // byte address of the source lane
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            const uint32_t oh = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)(me[u] >> 32));
+            const uint32_t ol = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)(uint32_t)me[u]);
+            rank[u] += (((uint64_t)oh << 32) | ol) > me[u];  // lanes past M hold 0, which precedes nothing
+          }
         }
       }
 #pragma unroll
