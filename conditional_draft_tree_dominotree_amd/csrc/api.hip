@@ -166,6 +166,8 @@ dt_status check_dims(const dt_dims* d) {
   if (d->depths > DT_MAX_DEPTHS) return fail(DT_EUNSUPPORTED, "depths %d > %d", d->depths, DT_MAX_DEPTHS);
   if (d->vocab > DT_TOPM_MAX_CHUNKS * TOPM_CHUNK)
     return fail(DT_EUNSUPPORTED, "vocab %d > %d", d->vocab, DT_TOPM_MAX_CHUNKS * TOPM_CHUNK);
+  if (d->vocab > dt::NINFO_MAX_VOCAB)  // node entries hold tokens in 20 bits, beside two markers
+    return fail(DT_EUNSUPPORTED, "vocab %d > %d", d->vocab, dt::NINFO_MAX_VOCAB);
   if (d->wdtype == DT_BF16 && (d->emb_dim % 8 || d->hidden % 8))
     return fail(DT_EUNSUPPORTED, "bf16 weights need emb_dim and hidden multiples of 8");
   if (d->rank > 4096 || d->state_dim > 8192) return fail(DT_EUNSUPPORTED, "rank or state_dim too large");
@@ -332,9 +334,11 @@ dt_status dt_create(dt_handle** out, const dt_dims* dims, const dt_weights* w, c
   HIPB(hipMemsetAsync(h->act, 0, h->act_bytes, stream));
   ALLOC(h->gh, nodes * round_up(3 * ds, 32) * sizeof(float));
   ALLOC(h->u, nodes * round_up(r, 32) * sizeof(float));
-  ALLOC(h->ninfo, nodes * sizeof(uint64_t));
-  HIPB(hipMemsetAsync(h->ninfo, 0, nodes * sizeof(uint64_t), stream));
-  h->ninfo_words = nodes * 2;
+  // node entries: one more step than the slots (a finished request's last entries)
+  const size_t ninfo_n = nodes + dt::TREE_MAX_COLS;
+  ALLOC(h->ninfo, ninfo_n * sizeof(uint64_t));
+  HIPB(hipMemsetAsync(h->ninfo, 0, ninfo_n * sizeof(uint64_t), stream));
+  h->ninfo_words = ninfo_n * 2;
   h->max_workers = h->n_cu;
   ALLOC(h->mbox_w, (dt::GFLAG_WORDS + (size_t)h->max_workers * 32) * sizeof(uint32_t));
   ALLOC(h->mbox_c, (size_t)DT_MAX_BATCH * 256 * sizeof(uint32_t));

@@ -60,7 +60,7 @@ struct TreeArgs {
   void* act;               // [slots, ds] its GEMM operand copy (wdtype)
   float* gh;               // [slots, 3 ds]
   float* u;                // [slots, r]
-  uint64_t* ninfo;         // [steps][TREE_MAX_COLS]: node entries (ninfo_entry) of the nodes to advance
+  uint64_t* ninfo;         // [N + 2][TREE_MAX_COLS]: node entries (ninfo_entry) of each step's columns
   uint32_t* gflag;         // [16][64] worker group flags: 2 epoch + half once a group's states of
                            // that step and half of the batch are advanced
   uint32_t* ready;         // [64] controller b: its start-up loads are done (the workers then load weights)
@@ -95,6 +95,12 @@ constexpr uint32_t TREE_EPOCH_LIMIT = 1u << 24;
 __host__ __device__ inline uint64_t ninfo_entry(uint32_t epoch, uint32_t tok, uint32_t src) {
   return ((uint64_t)(epoch & 0xFFFFFFu) << 40) | ((uint64_t)(tok & 0xFFFFFu) << 20) | (uint64_t)(src & 0xFFFFFu);
 }
+// Token fields of entries that are not nodes.  With register workers a
+// controller writes an entry for each of its p columns of every step: the
+// node's, NINFO_NONE where it expands fewer than p nodes, and NINFO_DONE in
+// the step after its last (the request has finished).
+constexpr uint32_t NINFO_NONE = 0xFFFFFu, NINFO_DONE = 0xFFFFEu;
+constexpr int NINFO_MAX_VOCAB = 0xFFFFE;  // tokens stay below the markers
 // Fills the schedule fields of `a` (p from `pops`, 0 = automatic) and returns
 // the dynamic LDS bytes the launch needs, or 0 if the shape cannot be served.
 // With register workers (allowed unless `lds_workers`) it also sets

@@ -519,53 +519,95 @@ __device__ __forceinline__ void worker_columns(const TreeArgs& a, int w, int t, 
   __syncthreads();
 }
 
+// Poll, per lane, the node entry at p (lanes with poll false: none) until
+// every polled entry carries the step's 24-bit epoch ep; two polls in flight,
+// as in wait_ptrs.  False if the wait ran out or the error word is set.
+__device__ __forceinline__ bool wait_entries(const uint64_t* p, bool poll, uint32_t ep, const int* err,
+                                             unsigned limit, uint64_t& out) {
+  const int lane = threadIdx.x & 63;
+  auto in = [&](uint64_t v) { return !poll || (uint32_t)(v >> 40) == ep; };
+  uint64_t x = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT), y;
+  unsigned it = 0;
+  while (true) {
+    __builtin_amdgcn_s_sleep(1);
+    y = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (__all(in(x))) {
+      out = x;
+      break;
+    }
+    __builtin_amdgcn_s_sleep(1);
+    x = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (__all(in(y))) {
+      out = y;
+      break;
+    }
+    if ((++it & 127) == 0) {
+      if (ld_dev_u32(err) != 0) return false;
+      if (2 * it > limit) {
+        if (lane == 0) atomicOr((int*)err, 1);
+        return false;
+      }
+    }
+  }
+  asm volatile("" ::: "memory");
+  return true;
+}
+
 // Register workers: the columns of block w's group at step t for the requests
 // [hb0, hb0 + hn) of a half.  Column c of the half is node c % p of request
-// hb0 + c / p, a column while that node exists.  The block waits for the words
-// of the requests its columns [col0, col0 + nc) (nc <= 64) cover, and no
-// others.  It writes coln[i] (i < nc): the slot staged for column col0 + i (a
-// present column's slot where the node does not exist), coln[64 + k]: the
-// slot of the k-th present column, reqs: the requests among those still
-// running; misc[0] = present columns (-1: a wait ran out), misc[1] = running
-// requests, misc[4] = 1 when every request of these columns is finished,
+// hb0 + c / p; the block polls the node entries of its columns [col0, col0 +
+// nc) (nc <= 64) directly (no mailbox word first), except those of requests
+// it has seen finish (the lanes in fin, updated here).  It writes coln[i]
+// (i < nc): the slot staged for column col0 + i (a present column's slot where
+// there is no node), and for the k-th present column coln[64 + k] its slot,
+// coln[128 + k] its token, coln[192 + k] its parent's slot; reqs: the running
+// requests among these columns'.  misc[0] = present columns (-1: a wait ran
+// out), misc[1] = running requests, misc[4] = 1 when none is running,
 // misc[6], misc[7] = the mask of present columns.
-__device__ __forceinline__ void worker_columns_fixed(const TreeArgs& a, int w, int t, int hb0, int hn, int col0,
-                                                     int nc, int* coln, int* reqs, int* misc) {
+__device__ __forceinline__ void worker_columns_fixed(const TreeArgs& a, int t, int hb0, int hn, int col0, int nc,
+                                                     unsigned long long& fin, int* coln, int* reqs, int* misc) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int p = a.p;
   const int c1 = min(col0 + nc, hn * p);
   if (tid < 64) {
-    int nval = 0, nact = 0, fin = 1;
+    int nval = 0, nact = 0, none = 1;
     unsigned long long vm = 0;
     bool ok = true;
     if (col0 < c1) {
-      const uint32_t epoch = a.ebase + (uint32_t)t + 1u;
-      const int rb0 = col0 / p, nr = (c1 - 1) / p - rb0 + 1;  // <= nc <= 64
-      uint32_t word = 0;
-      ok = wait_mbox(a.mbox_w + (size_t)(w % MBOX_REPL) * 32 + hb0 + rb0, nr, epoch << 5, a.err, a.spin_limit,
-                     &word);
-      // a request still running expands at least one node this step
-      const bool live = ok && lane < nr && (word & 31u) != MBOX_DONE_E;
-      const int e = live ? (int)(word & 31u) : 0;
-      const unsigned long long act = __ballot(live);
-      fin = act == 0ull;
-      nact = __popcll(act);
-      if (live) reqs[__popcll(act & ((1ull << lane) - 1ull))] = hb0 + rb0 + lane;
-      // lane i: column col0 + i
+      const uint32_t ep = (a.ebase + (uint32_t)t + 1u) & 0xFFFFFFu;
+      const int rb0 = col0 / p;  // the first request (within the half) of these columns
       const int c = col0 + lane;
-      const int er = __shfl(e, min(max(c / p - rb0, 0), 63));
-      const bool v = lane < nc && c < c1 && c % p < er;
+      const bool col = lane < nc && c < c1;
+      const bool poll = col && !((fin >> lane) & 1ull);
+      const uint64_t* ptr = a.ninfo + (poll ? (size_t)t * TREE_MAX_COLS + (size_t)(hb0 + c / p) * p + c % p : 0);
+      uint64_t en = 0;
+      ok = wait_entries(ptr, poll, ep, a.err, a.spin_limit, en);
+      const uint32_t tok = (uint32_t)(en >> 20) & 0xFFFFFu, src = (uint32_t)en & 0xFFFFFu;
+      const bool done = col && (!poll || tok == NINFO_DONE);
+      fin |= __ballot(done);
+      const bool v = ok && poll && tok != NINFO_DONE && tok != NINFO_NONE;
+      // a request's first column among these: it lists the request if running
+      const bool first = col && (c % p == 0 || lane == 0);
+      const unsigned long long act = __ballot(ok && first && !done);
+      nact = __popcll(act);
+      none = act == 0ull;
+      if (ok && first && !done) reqs[__popcll(act & ((1ull << lane) - 1ull))] = hb0 + rb0 + (c / p - rb0);
       const int s = v ? (int)slot_of(a, t, hb0 + c / p, c % p) : -1;
       vm = __ballot(v);
       nval = __popcll(vm);
       const int s0 = __shfl(s, vm ? __ffsll((long long)vm) - 1 : 0);
       if (lane < nc) coln[lane] = v ? s : s0;
-      if (v) coln[64 + __popcll(vm & ((1ull << lane) - 1ull))] = s;
+      if (v) {
+        const int k = __popcll(vm & ((1ull << lane) - 1ull));
+        coln[64 + k] = s;
+        coln[128 + k] = (int)tok;
+        coln[192 + k] = (int)src;
+      }
     }
     if (lane == 0) {
       misc[0] = ok ? nval : -1;
       misc[1] = nact;
-      misc[4] = fin;
+      misc[4] = none;
       misc[6] = (int)(uint32_t)vm;
       misc[7] = (int)(uint32_t)(vm >> 32);
     }
@@ -737,19 +779,18 @@ __device__ __forceinline__ void lds_read8_b(const uint16_t* p, bf16x8 (&v)[8]) {
         : "memory");
 }
 
-// Advance the GRU states of columns [c0, c0 + nc) of step t (d_s = 1024,
-// bf16 operand copies): S_y = GRU(S_x, E[tok]) with W_ih E[tok] + b_ih =
-// G[tok] and gh_x published by the workers at the parent's step.  The
+// Advance the GRU states of nc columns (d_s = 1024, bf16 operand copies):
+// S_y = GRU(S_x, E[tok]) with W_ih E[tok] + b_ih = G[tok] and gh_x published
+// by the workers at the parent's step; column cc has slot cslot[cc], token
+// ctok[cc] and parent slot csrc[cc] (from the controller's node entries).  The
 // group's nq blocks share the float4 items: block q takes items q NT + i +
-// k nq NT.  Token and parent slot come from the controller's node table.
+// k nq NT.
 constexpr int WG = 3;  // advance items per thread in flight
-__device__ __forceinline__ void worker_advance(const TreeArgs& a, const int* coln, int t, int c0, int nc, int q,
-                                               int nq, bool loc, floatx4 (&dv)[WG], float* (&dp)[WG]) {
+__device__ __forceinline__ void worker_advance(const TreeArgs& a, const int* cslot, const int* ctok, const int* csrc,
+                                               int nc, int q, int nq, bool loc, floatx4 (&dv)[WG],
+                                               float* (&dp)[WG]) {
   const int ds = a.ds, n4 = ds >> 2;
   const int items = nc * n4;
-  const int slot0 = (int)slot_of(a, t, 0, 0);
-  const uint64_t* info = a.ninfo + (size_t)t * TREE_MAX_COLS;
-  const uint32_t ep = (a.ebase + (uint32_t)t + 1u) & 0xFFFFFFu;  // the epoch the entries carry
 #pragma unroll
   for (int g = 0; g < WG; ++g) dp[g] = nullptr;
   for (int base = q * NT; base < items; base += nq * NT * WG) {
@@ -757,36 +798,14 @@ __device__ __forceinline__ void worker_advance(const TreeArgs& a, const int* col
     // (later steps read them; the group needs only the operand copies now)
     const bool last = base + nq * NT * WG >= items;
     int tok[WG], src[WG], sl[WG], qv[WG];
-    uint64_t en[WG];
 #pragma unroll
-    for (int g = 0; g < WG; ++g) {  // clamped: every lane reads valid entries
+    for (int g = 0; g < WG; ++g) {  // clamped: every lane reads a present column
       const int item = min(base + g * nq * NT + (int)threadIdx.x, items - 1);
       const int cc = item / n4;
       qv[g] = (item - cc * n4) * 4;
-      sl[g] = coln[c0 + cc];
-      en[g] = __hip_atomic_load(info + (sl[g] - slot0), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-    // an entry published after its mailbox word can still be in flight:
-    // read it again until it carries this step's epoch (bounded)
-    for (unsigned it = 0;; ++it) {
-      bool all = true;
-#pragma unroll
-      for (int g = 0; g < WG; ++g) all &= (uint32_t)(en[g] >> 40) == ep;
-      if (all) break;
-      if (it > a.spin_limit || ((it & 255) == 255 && ld_dev_u32(a.err) != 0)) {
-        if (it > a.spin_limit) atomicOr(a.err, 1);
-        break;  // the group's wait sees the error word and ends the turn
-      }
-      __builtin_amdgcn_s_sleep(1);
-#pragma unroll
-      for (int g = 0; g < WG; ++g)
-        if ((uint32_t)(en[g] >> 40) != ep)
-          en[g] = __hip_atomic_load(info + (sl[g] - slot0), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-#pragma unroll
-    for (int g = 0; g < WG; ++g) {
-      tok[g] = (int)((en[g] >> 20) & 0xFFFFFu);
-      src[g] = (int)(en[g] & 0xFFFFFu);
+      sl[g] = cslot[cc];
+      tok[g] = ctok[cc];
+      src[g] = csrc[cc];
     }
     float4 ir[WG], iz[WG], in_[WG], hr[WG], hz[WG], hn[WG], sp[WG];
 #pragma unroll
@@ -873,6 +892,7 @@ __device__ __forceinline__ void worker_regs(const TreeArgs& a, unsigned char* ld
   // With two halves the block serves the requests [0, bh) and then [bh, B) of
   // each step; a half whose requests are all finished is passed over.
   bool done[2] = {false, a.halves < 2};
+  unsigned long long fin0 = 0ull, fin1 = 0ull;  // wave 0: columns whose request has finished, per half
   int t = a.root ? 0 : 1;  // zero roots: step 0 needs no product (set up by the controllers)
   for (int h = 0;; h = (h + 1) % a.halves, t += h == 0) {
     if (done[0] && done[1]) return;
@@ -881,7 +901,12 @@ __device__ __forceinline__ void worker_regs(const TreeArgs& a, unsigned char* ld
     // group flags: 2 epoch + h, increasing over (step, half) and across launches
     // whatever their number of halves
     const uint32_t gepoch = 2u * epoch + (uint32_t)h;
-    worker_columns_fixed(a, w, t, h ? a.bh : 0, h ? a.B - a.bh : a.bh, col0, 16 * CPB, coln, reqs, misc);
+    unsigned long long fin = h ? fin1 : fin0;
+    worker_columns_fixed(a, t, h ? a.bh : 0, h ? a.B - a.bh : a.bh, col0, 16 * CPB, fin, coln, reqs, misc);
+    if (h)
+      fin1 = fin;
+    else
+      fin0 = fin;
     const int nval = misc[0], nreq = misc[1];
     const unsigned long long vmask = (unsigned long long)(uint32_t)misc[6] | ((unsigned long long)(uint32_t)misc[7] << 32);
     if (nval < 0) return;  // a wait ran out
@@ -898,7 +923,7 @@ __device__ __forceinline__ void worker_regs(const TreeArgs& a, unsigned char* ld
       if (a.wadv && t > 0) {
         // the group advances the states of its columns, then waits for all of it
         const bool loc = xmode == 1;
-        worker_advance(a, coln + 64, t, 0, nval, gq, ngq, loc, sv, sp);
+        worker_advance(a, coln + 64, coln + 128, coln + 192, nval, gq, ngq, loc, sv, sp);
         stores_done();
         __syncthreads();
         if (tid == 0) {
@@ -2310,6 +2335,27 @@ __device__ __forceinline__ void ack_ptrs(const TreeArgs& a, const uint32_t* box,
   }
 }
 
+// Register workers: wave 0 writes the node entries of request b's p columns at
+// step ts: the e nodes' (token, parent slot), NINFO_NONE for the columns past
+// them, or NINFO_DONE for every column once the request has finished.
+__device__ __forceinline__ void ctl_entries(const TreeArgs& a, const CtlLds& c, int b, int ts, int e, bool done) {
+  const int tid = threadIdx.x;
+  if (tid < a.p) {
+    uint32_t tok = done ? NINFO_DONE : NINFO_NONE, src = 0;
+    if (!done && tid < e) {
+      int xs = c.f->ex_src[tid];
+      if (xs < 0) {  // every parent was expanded; the guard keeps addresses valid
+        atomicOr(a.err, 8);
+        xs = 0;
+      }
+      tok = (uint32_t)c.f->ex_tok[tid];
+      src = (uint32_t)xs;
+    }
+    st_dev_u64(a.ninfo + (size_t)ts * TREE_MAX_COLS + (size_t)b * a.p + tid,
+               ninfo_entry(a.ebase + (uint32_t)ts + 1u, tok, src));
+  }
+}
+
 template <typename W>
 __device__ __forceinline__ void controller_main(const TreeArgs& a, unsigned char* lds) {
   const int b = blockIdx.x - a.n_workers;
@@ -2363,8 +2409,14 @@ __device__ __forceinline__ void controller_main(const TreeArgs& a, unsigned char
   }
   stores_done();
   __syncthreads();
-  if (a.root)
-    if (tid < MBOX_REPL) st_dev_u32(a.mbox_w + (size_t)tid * 32 + b, mbox_word(a.ebase + 1, 1));
+  const bool regws = a.regw != 0 && a.n_workers > 0;  // register workers: node entries, not mailbox words
+  if (a.root) {  // step 0: the workers take the root's products (its state is set above)
+    if (regws) {
+      if (tid < a.p) st_dev_u64(a.ninfo + (size_t)b * a.p + tid, ninfo_entry(a.ebase + 1, tid ? NINFO_NONE : 0u, 0u));
+    } else if (tid < MBOX_REPL) {
+      st_dev_u32(a.mbox_w + (size_t)tid * 32 + b, mbox_word(a.ebase + 1, 1));
+    }
+  }
   stores_done();
   ctl_prefetch<W>(a, c, b);
   __syncthreads();
@@ -2434,34 +2486,30 @@ __device__ __forceinline__ void controller_main(const TreeArgs& a, unsigned char
     if (a.marginal) {
       // marginal scores: no states to advance (and no workers)
     } else if (a.wadv) {
-      // the workers advance the states: wave 0 publishes each node's entry
-      // (token and parent slot; it carries the step's epoch, so the mailbox
-      // words need not wait for it to land) and then the mailbox words
-      if (tid < 64) {
-        if (tid < e2) {
-          int xs = c.f->ex_src[tid];
-          if (xs < 0) {  // every parent was expanded; the guard keeps addresses valid
-            atomicOr(a.err, 8);
-            xs = 0;
-          }
-          const size_t sl = slot_of(a, t + 1, b, tid) - slot_of(a, t + 1, 0, 0);
-          st_dev_u64(a.ninfo + (size_t)(t + 1) * TREE_MAX_COLS + sl,
-                     ninfo_entry(a.ebase + t + 2, (uint32_t)c.f->ex_tok[tid], (uint32_t)xs));
-        }
-        if (tid < MBOX_REPL) st_dev_u32(a.mbox_w + (size_t)tid * 32 + b, mbox_word(a.ebase + t + 2, e2));
-      }
+      // the workers advance the states: the node entries (token and parent
+      // slot, carrying the step's epoch) are all they need
+      if (tid < 64) ctl_entries(a, c, b, t + 1, e2, false);
     } else {
       ctl_advance<W>(a, c, b, t + 1, e2);
       stores_done();
       __syncthreads();
-      if (tid < MBOX_REPL) st_dev_u32(a.mbox_w + (size_t)tid * 32 + b, mbox_word(a.ebase + t + 2, e2));
+      if (regws) {
+        if (tid < 64) ctl_entries(a, c, b, t + 1, e2, false);
+      } else if (tid < MBOX_REPL) {
+        st_dev_u32(a.mbox_w + (size_t)tid * 32 + b, mbox_word(a.ebase + t + 2, e2));
+      }
     }
     ctl_prefetch<W>(a, c, b);  // overlaps the workers' step
     __syncthreads();
   }
-  // release the workers from this request
-  if (tid < MBOX_REPL)
+  // release the workers from this request: register workers read it in the
+  // entries of the step after the last (a failed build's workers leave on
+  // the error word)
+  if (regws) {
+    if (!failed && tid < 64) ctl_entries(a, c, b, steps, 0, true);
+  } else if (tid < MBOX_REPL) {
     st_dev_u32(a.mbox_w + (size_t)tid * 32 + b, mbox_word(a.ebase + tree_epoch_span(a.N) - 1, MBOX_DONE_E));
+  }
   stores_done();
   ctl_output(a, c, b, failed);
   if (a.stats && tid == 0) {
