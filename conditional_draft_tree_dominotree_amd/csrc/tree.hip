@@ -1437,6 +1437,31 @@ __device__ __forceinline__ int half_rank32(uint32_t v) {
 #undef DT_ROW_RORS
   return gt;
 }
+// The same over the whole wave (64 lanes): the other row of this half by a
+// swizzle, the other half by one permute and its swizzle, each rotated.
+__device__ __forceinline__ int wave_rank32(uint32_t v) {
+  int gt = 0;
+  auto acc = [&](uint32_t o) { gt += o > v; };
+#define DT_ROW_RORS(x)                                                                                          \
+  acc(row_ror_u32<1>(x)), acc(row_ror_u32<2>(x)), acc(row_ror_u32<3>(x)), acc(row_ror_u32<4>(x)),              \
+      acc(row_ror_u32<5>(x)), acc(row_ror_u32<6>(x)), acc(row_ror_u32<7>(x)), acc(row_ror_u32<8>(x)),          \
+      acc(row_ror_u32<9>(x)), acc(row_ror_u32<10>(x)), acc(row_ror_u32<11>(x)), acc(row_ror_u32<12>(x)),       \
+      acc(row_ror_u32<13>(x)), acc(row_ror_u32<14>(x)), acc(row_ror_u32<15>(x))
+  DT_ROW_RORS(v);
+  const uint32_t x1 = (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, 0x401F);  // lane ^ 16
+  acc(x1);
+  DT_ROW_RORS(x1);
+  const int lane = threadIdx.x & 63;
+  const uint32_t x2 = (uint32_t)__builtin_amdgcn_ds_bpermute((lane ^ 32) << 2, (int)v);  // lane ^ 32
+  acc(x2);
+  DT_ROW_RORS(x2);
+  const uint32_t x3 = (uint32_t)__builtin_amdgcn_ds_swizzle((int)x2, 0x401F);  // lane ^ 48
+  acc(x3);
+  DT_ROW_RORS(x3);
+#undef DT_ROW_RORS
+  return gt;
+}
+
 // OR over each half-wave.
 __device__ __forceinline__ uint32_t half_or32(uint32_t v) {
   v |= row_ror_u32<1>(v);
@@ -1707,36 +1732,72 @@ __device__ __forceinline__ void ctl_expand(const TreeArgs& a, const CtlLds& c, i
           c.nc[(hw + 8 * u) * k + rank[u]] = ok ? make_key(yscore[u] + lp, dy[u] + 1, crk[u], y[u], l32) : 0ull;
       }
     }
-  } else
-  for (int j = wv; j < e; j += 4) {
-    const int y = c.f->ex_rec[j];
-    const int dy = c.f->ex_dep[j];
-    const float yscore = key_score(c.rec[y].key);
-    const bool has = lane < M;
-    const float zv = has ? c.f->z[j * 64 + lane] : -INFINITY;
-    const int idv = has ? c.cand[dy * M + lane].id : 0x7FFFFFFF;
-    float mx = wave_max_dpp(zv);
-    const float tl = a.fullv ? c.tailv[dy] : -INFINITY;
-    mx = fmaxf(mx, tl);
-    float lz = -INFINITY;
-    if (mx > -INFINITY) {
-      float se = wave_sum_dpp(has ? expf(zv - mx) : 0.f);
-      if (tl > -INFINITY) se += expf(tl - mx);
-      lz = mx + logf(se);
+  } else {
+    // one wave per node (M <= 64): nodes wv + 8 i and wv + 8 i + 4 at once, so
+    // that their latency chains overlap
+    for (int j0 = wv; j0 < e; j0 += 8) {
+      int jr[2], y[2], dy[2];
+      bool node[2], has[2];
+      float yscore[2], zv[2], tl[2];
+      int idv[2];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int j = j0 + 4 * u;
+        node[u] = j < e;
+        jr[u] = node[u] ? j : j0;  // a valid node of this wave for the reads
+        has[u] = node[u] && lane < M;
+        y[u] = c.f->ex_rec[jr[u]];
+        dy[u] = c.f->ex_dep[jr[u]];
+      }
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        yscore[u] = key_score(c.rec[y[u]].key);
+        zv[u] = has[u] ? c.f->z[jr[u] * 64 + lane] : -INFINITY;
+        idv[u] = has[u] ? c.cand[dy[u] * M + lane].id : 0x7FFFFFFF;
+        tl[u] = a.fullv ? c.tailv[dy[u]] : -INFINITY;
+      }
+      float lz[2];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const float mx = fmaxf(wave_max_dpp(zv[u]), tl[u]);
+        lz[u] = -INFINITY;
+        if (mx > -INFINITY) {
+          float se = wave_sum_dpp(has[u] ? expf(zv[u] - mx) : 0.f);
+          if (tl[u] > -INFINITY) se += expf(tl[u] - mx);
+          lz[u] = mx + logf(se);
+        }
+      }
+      // rank by (value desc, token asc): on the value keys alone (absent
+      // lanes 0, below every value) unless the ranks show equal values
+      // (distinct ones take the ranks 0 .. M - 1 once each, summing to
+      // M (M - 1) / 2; equal ones share a rank), then by the composite
+      // (value key, complemented id)
+      int rank[2];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) rank[u] = wave_rank32(has[u] ? f32_key(zv[u]) : 0u);
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        if (node[u] && wave_sum_dpp(has[u] ? (float)rank[u] : 0.f) != (float)(M * (M - 1) / 2)) {
+          const uint64_t me = has[u] ? cand_pack(f32_key(zv[u]), (uint32_t)idv[u]) : 0ull;
+          const uint32_t mlo = (uint32_t)me, mhi = (uint32_t)(me >> 32);
+          int rk = 0;
+          for (int q = 0; q < M; ++q) {
+            const uint64_t o = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)mhi, q) << 32) |
+                               (uint32_t)__builtin_amdgcn_readlane((int)mlo, q);
+            rk += o > me;
+          }
+          rank[u] = rk;
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const float lp = zv[u] - lz[u];
+        const bool ok = has[u] && isfinite(lp);
+        if (has[u] && rank[u] < k)
+          c.nc[jr[u] * k + rank[u]] =
+              ok ? make_key(yscore[u] + lp, dy[u] + 1, c.cand[dy[u] * M + lane].rank, y[u], lane) : 0ull;
+      }
     }
-    const float lp = zv - lz;
-    // rank by the composite (value key, complemented id); absent lanes are 0
-    const uint64_t me = has ? cand_pack(f32_key(zv), (uint32_t)idv) : 0ull;
-    const uint32_t mlo = (uint32_t)me, mhi = (uint32_t)(me >> 32);
-    int rank = 0;
-    for (int q = 0; q < M; ++q) {
-      const uint64_t o = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)mhi, q) << 32) |
-                         (uint32_t)__builtin_amdgcn_readlane((int)mlo, q);
-      rank += o > me;
-    }
-    const bool ok = has && isfinite(lp);
-    if (has && rank < k)
-      c.nc[j * k + rank] = ok ? make_key(yscore + lp, dy + 1, c.cand[dy * M + lane].rank, y, lane) : 0ull;
   }
   // zero the new keys past e k up to a multiple of 32 (the merge reads blocks of 32)
   for (int i = e * k + tid; i < (e * k + 31) / 32 * 32; i += NT) c.nc[i] = 0ull;
