@@ -50,6 +50,7 @@
 // copies and their group flags through that XCD's L2 instead.  Every wait is
 // bounded: when it runs out the block sets the error word and leaves its loop.
 #include <algorithm>
+#include <type_traits>
 
 #include "common.h"
 #include "tree.h"
@@ -86,6 +87,9 @@ __device__ __forceinline__ uint32_t ld_dev_u32(const void* p) {
   return v;
 }
 __device__ __forceinline__ void stores_done() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// A block barrier that waits only for this wave's LDS operations (a
+// __syncthreads also waits for its outstanding global loads and stores).
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 // Keeps the instruction scheduler from moving anything across this point.  Put
 // between the loads of a batch and their uses, so that every load of the
@@ -947,57 +951,58 @@ __device__ __forceinline__ void worker_regs(const TreeArgs& a, unsigned char* ld
         if (xmode < 0) xmode = misc[3] ? 1 : 0;  // the same for every block of the group
         if (!misc[2]) return;
       }
-      // stage: thread piece tid + 256 q = column (tid >> 7) + 2 q, 16-byte piece tid & 127
+      // stage the operands in two halves of k (16-byte pieces [0, 64) and
+      // [64, 128) of each column's 128): the second half's loads are in flight
+      // while the first half's products run.  Thread: piece tid & 63 of
+      // columns (tid >> 6) + 4 q.
       const int slot0 = (int)slot_of(a, t, 0, 0);
-      const int pc = tid & 127;
-      const uint16_t* base = reinterpret_cast<const uint16_t*>(a.act) + (size_t)slot0 * as;
-      // batches of up to 16 loads (32 columns), each completed before the next
+      const int ph = tid & 63;
+      const char* base = reinterpret_cast<const char*>(reinterpret_cast<const uint16_t*>(a.act) + (size_t)slot0 * as);
+      constexpr int NL = 4 * CPB;  // loads per thread and half
+      unsigned off[NL];
 #pragma unroll
-      for (int h = 0; h < (CPB + 1) / 2; ++h) {
-        constexpr int NB = CPB == 1 ? 8 : 16;
-        unsigned off[NB];
+      for (int q = 0; q < NL; ++q)  // coln holds a present column's slot for every column
+        off[q] = (unsigned)(((coln[(tid >> 6) + 4 * q] - slot0) * as + ph * 8) * 2);
+      u32x4 v[NL];
 #pragma unroll
-        for (int q = 0; q < NB; ++q) {  // coln holds a present column's slot for every column
-          const int c = (tid >> 7) + 2 * (NB * h + q);
-          off[q] = (unsigned)(((coln[c] - slot0) * as + pc * 8) * 2);
-        }
-        u32x4 v[NB];
-        if constexpr (NB == 8) load8_batch(base, off, v);
-        else load16_batch(base, off, v);
+      for (int q = 0; q < NL; ++q) v[q] = *reinterpret_cast<const u32x4*>(base + off[q]);
+      keep_batch();
 #pragma unroll
-        for (int q = 0; q < NB; ++q)
-          *reinterpret_cast<u32x4*>(stage + ((tid >> 7) + 2 * (NB * h + q)) * RSTRIDE + pc * 8) = v[q];
-      }
+      for (int q = 0; q < NL; ++q) *reinterpret_cast<u32x4*>(stage + ((tid >> 6) + 4 * q) * RSTRIDE + ph * 8) = v[q];
+#pragma unroll
+      for (int q = 0; q < NL; ++q) v[q] = *reinterpret_cast<const u32x4*>(base + off[q] + 64 * 16);
+      keep_batch();
       // the states (read by later steps' advances) drain during the products
-      // and before the acknowledgement; stored earlier they would hold up the
-      // staging loads' wait
+      // and before the acknowledgement
 #pragma unroll
       for (int g = 0; g < WG; ++g)
         if (sp[g]) st_dev_f32x4(sp[g], sv[g]);
-      __syncthreads();
-      if (tile0 < a.n_tiles) {
-        // B operands: column (lane & 15) of each column block, k 8 (lane >> 4) + 32 kb
-        const uint16_t* sb = stage + (lane & 15) * RSTRIDE + 8 * (lane >> 4);
-        // independent accumulation chains: two per (column block, tile) unless
-        // the column blocks give enough
-        constexpr int NACC = CPB >= 4 ? 1 : 2;
-        floatx4 acc[CPB][TW][NACC];
+      lds_barrier();  // the first half is staged (the second half's loads stay in flight)
+      // B operands: column (lane & 15) of each column block, k 8 (lane >> 4) + 32 kb
+      const uint16_t* sb = stage + (lane & 15) * RSTRIDE + 8 * (lane >> 4);
+      // independent accumulation chains: two per (column block, tile) unless
+      // the column blocks give enough
+      constexpr int NACC = CPB >= 4 ? 1 : 2;
+      floatx4 acc[CPB][TW][NACC];
 #pragma unroll
-        for (int c = 0; c < CPB; ++c)
+      for (int c = 0; c < CPB; ++c)
 #pragma unroll
-          for (int i = 0; i < TW; ++i)
+        for (int i = 0; i < TW; ++i)
 #pragma unroll
-            for (int n = 0; n < NACC; ++n) acc[c][i][n] = floatx4{0.f, 0.f, 0.f, 0.f};
-        // B operands four 16-byte reads at a time (KG k blocks of the CPB column
-        // blocks), in two register sets: the next group's reads are issued
-        // before this group's products, so LDS reads and MFMAs overlap
-        constexpr int KG = 4 / CPB, NG = RKB / KG;
-        bf16x8 bv[2][4];  // [set][c KG + q]: column block c, k block g KG + q
+          for (int n = 0; n < NACC; ++n) acc[c][i][n] = floatx4{0.f, 0.f, 0.f, 0.f};
+      // the products of k blocks [16 hk, 16 hk + 16): B operands four 16-byte
+      // reads at a time (KG k blocks of the CPB column blocks), in two register
+      // sets, the next group's reads issued before this group's products
+      constexpr int KG = 4 / CPB, NG = RKB / KG / 2;
+      auto products = [&](auto hkc) {
+        constexpr int hk = decltype(hkc)::value;
+        bf16x8 bv[2][4];  // [set][c KG + q]: column block c, k block 16 hk + g KG + q
+        const uint16_t* sbh = sb + hk * 16 * 32;
 #pragma unroll
         for (int q = 0; q < KG; ++q)
 #pragma unroll
           for (int c = 0; c < CPB; ++c)
-            bv[0][c * KG + q] = *reinterpret_cast<const bf16x8*>(sb + c * 16 * RSTRIDE + q * 32);
+            bv[0][c * KG + q] = *reinterpret_cast<const bf16x8*>(sbh + c * 16 * RSTRIDE + q * 32);
 #pragma unroll
         for (int g = 0; g < NG; ++g) {
           if (g + 1 < NG) {
@@ -1006,23 +1011,31 @@ __device__ __forceinline__ void worker_regs(const TreeArgs& a, unsigned char* ld
 #pragma unroll
               for (int c = 0; c < CPB; ++c)
                 bv[(g + 1) & 1][c * KG + q] =
-                    *reinterpret_cast<const bf16x8*>(sb + c * 16 * RSTRIDE + ((g + 1) * KG + q) * 32);
+                    *reinterpret_cast<const bf16x8*>(sbh + c * 16 * RSTRIDE + ((g + 1) * KG + q) * 32);
           }
 #pragma unroll
           for (int q = 0; q < KG; ++q) {
-            const int kb = g * KG + q;
+            const int kb = g * KG + q;  // within the half
 #pragma unroll
             for (int c = 0; c < CPB; ++c)
 #pragma unroll
               for (int i = 0; i < TW; ++i)
-                acc[c][i][kb % NACC] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa[i][kb], bv[g & 1][c * KG + q],
-                                                                               acc[c][i][kb % NACC], 0, 0, 0);
+                acc[c][i][kb % NACC] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                    wa[i][16 * hk + kb], bv[g & 1][c * KG + q], acc[c][i][kb % NACC], 0, 0, 0);
           }
           // the schedule: this group's reads of the next set, then its products
           if (g == 0) __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
           if (g + 1 < NG) __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
           __builtin_amdgcn_sched_group_barrier(0x008, 4 * TW, 0);
         }
+      };
+      if (tile0 < a.n_tiles) products(std::integral_constant<int, 0>{});
+#pragma unroll
+      for (int q = 0; q < NL; ++q)
+        *reinterpret_cast<u32x4*>(stage + ((tid >> 6) + 4 * q) * RSTRIDE + (64 + ph) * 8) = v[q];
+      lds_barrier();  // the second half is staged
+      if (tile0 < a.n_tiles) {
+        products(std::integral_constant<int, 1>{});
         // lane holds column col, rows 4 (lane >> 4) + q of each tile
         const int ds3 = 3 * a.ds;
 #pragma unroll
