@@ -166,8 +166,9 @@ dt_status check_dims(const dt_dims* d) {
   if (d->depths > DT_MAX_DEPTHS) return fail(DT_EUNSUPPORTED, "depths %d > %d", d->depths, DT_MAX_DEPTHS);
   if (d->vocab > DT_TOPM_MAX_CHUNKS * TOPM_CHUNK)
     return fail(DT_EUNSUPPORTED, "vocab %d > %d", d->vocab, DT_TOPM_MAX_CHUNKS * TOPM_CHUNK);
-  if (d->vocab > dt::NINFO_MAX_VOCAB)  // node entries hold tokens in 20 bits, beside two markers
-    return fail(DT_EUNSUPPORTED, "vocab %d > %d", d->vocab, dt::NINFO_MAX_VOCAB);
+  static_assert(DT_MAX_VOCAB == dt::NINFO_MAX_VOCAB, "the header's vocabulary limit is the node entries'");
+  if (d->vocab > DT_MAX_VOCAB)  // node entries hold tokens in 20 bits, beside two markers
+    return fail(DT_EUNSUPPORTED, "vocab %d > %d", d->vocab, DT_MAX_VOCAB);
   if (d->wdtype == DT_BF16 && (d->emb_dim % 8 || d->hidden % 8))
     return fail(DT_EUNSUPPORTED, "bf16 weights need emb_dim and hidden multiples of 8");
   if (d->rank > 4096 || d->state_dim > 8192) return fail(DT_EUNSUPPORTED, "rank or state_dim too large");

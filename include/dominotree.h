@@ -99,9 +99,10 @@ typedef enum { DT_NORM_TOPM = 0, DT_NORM_FULLV = 1 } dt_norm;
 #define DT_MAX_TOPM 64
 #define DT_MAX_BUDGET 1024
 #define DT_MAX_FRONTIER 4096 /* budget * (top_k - 1) + 1 */
+#define DT_MAX_VOCAB 1048574 /* 2^20 - 2: the builder's node entries hold a token in 20 bits */
 
 typedef struct {
-  int32_t vocab;     /* V */
+  int32_t vocab;     /* V, 1..DT_MAX_VOCAB */
   int32_t depths;    /* D = draft block size - 1 */
   int32_t hidden;    /* h: rows of H_d, rows of the H half of W1 */
   int32_t emb_dim;   /* e: embedding size (GRU input) */

@@ -51,6 +51,7 @@ def test_null_arguments_are_einval(lib):
 @pytest.mark.parametrize("dims,params,code", [
     ((0, 7, 8, 8, 8, 4, 1), (4, 2, 8, 1.0), binding.DT_EINVAL),          # vocab 0
     ((64, 7, 8, 8, 8, 4, 33), (4, 2, 8, 1.0), binding.DT_EUNSUPPORTED),  # batch > 32
+    ((1048575, 7, 8, 8, 8, 4, 1), (4, 2, 8, 1.0), binding.DT_EUNSUPPORTED),  # vocab > 2^20 - 2
     ((64, 40, 8, 8, 8, 4, 1), (4, 2, 8, 1.0), binding.DT_EUNSUPPORTED),  # depths > 31
     ((64, 7, 8, 8, 8, 4, 1), (0, 1, 8, 1.0), binding.DT_EINVAL),         # M = 0
     ((64, 7, 8, 8, 8, 4, 1), (65, 2, 8, 1.0), binding.DT_EINVAL),        # M > V
