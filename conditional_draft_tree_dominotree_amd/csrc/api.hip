@@ -27,6 +27,22 @@ dt_status fail(dt_status s, const char* fmt, ...) {
   return s;
 }
 
+// what the bits of the device error word mean (several may be set)
+std::string device_error_text(int e) {
+  static const char* const why[] = {
+      "a bounded wait ran out",                                // 1
+      "a request needed more steps than its budget allows",    // 2
+      "a frontier outgrew its capacity",                       // 4
+      "a node's parent had no state slot",                     // 8
+      "the LM head's candidate lists did not agree with the recomputed logits",  // 16
+  };
+  std::string s;
+  for (int b = 0; b < 5; ++b)
+    if (e & (1 << b)) s += (s.empty() ? "" : "; ") + std::string(why[b]);
+  if (e >> 5) s += (s.empty() ? "" : "; ") + std::string("unknown bits");
+  return s;
+}
+
 #define HIPCHK(expr)                                                                     \
   do {                                                                                   \
     hipError_t e_ = (expr);                                                              \
@@ -379,8 +395,8 @@ dt_status dt_build_trees(dt_handle* h, const dt_inputs* in, const dt_params* p, 
   // a finished launch that ended with the device error word set (the mirror
   // is read without a synchronisation; dt_sync_status reports and clears it)
   if (const int e = *reinterpret_cast<volatile int*>(h->err_host))
-    return fail(DT_EDEVICE, "a previous build's device wait ran out (error word %d); dt_sync_status resets the handle",
-                e);
+    return fail(DT_EDEVICE, "a previous build ended with a device error (word %d: %s); dt_sync_status resets the handle",
+                e, device_error_text(e).c_str());
 
   const int B = in->batch, D = d.depths, V = d.vocab, M = p->top_m, N = p->budget;
   const int rows = B * D;
@@ -566,7 +582,8 @@ dt_status dt_sync_status(dt_handle* h, void* stream_) {
   HIPCHK(hipStreamSynchronize(stream));
   h->ebase = 0;
   *reinterpret_cast<volatile int*>(h->err_host) = 0;
-  return fail(DT_EDEVICE, "a builder wait ran out (device error word %d); the handle is reset", e);
+  return fail(DT_EDEVICE, "a build ended with a device error (word %d: %s); the handle is reset", e,
+              device_error_text(e).c_str());
 }
 
 dt_status dt_set_schedule(dt_handle* h, const dt_schedule* s) {
