@@ -36,8 +36,8 @@ struct TreeArgs {
   int ugq0, ugq1;       // register workers: the tile groups [ugq0, ugq1] hold the W1_S^T tiles; once
                         // they acknowledge a step, its u rows are stored
   int xlocal;           // register workers: 1 lets a column group whose blocks all run on one XCD
-                        // (checked at the launch's first exchange) exchange advanced states through
-                        // that XCD's L2 instead of device-wide
+                        // (checked at the launch's first exchange) raise its group flags in that
+                        // XCD's L2 instead of device-wide
   int xcap;             // node records per request (budget + root + speculation room)
   int fcap;             // frontier entries per request
   int qmax;             // frontier entries tested per pop round

@@ -126,11 +126,6 @@ __device__ __forceinline__ void st_dev_u32x2(void* p, uint32_t lo, uint32_t hi) 
 __device__ __forceinline__ void st_l2_u32(void* p, uint32_t v) {
   asm volatile("global_store_dword %0, %1, off sc0" ::"v"(p), "v"(v) : "memory");
 }
-__device__ __forceinline__ void st_l2_u32x2(void* p, uint32_t lo, uint32_t hi) {
-  typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-  u32x2 v = {lo, hi};
-  asm volatile("global_store_dwordx2 %0, %1, off sc0" ::"v"(p), "v"(v) : "memory");
-}
 
 
 // four consecutive operand values (the address is 8- or 16-byte aligned)
@@ -791,7 +786,7 @@ __device__ __forceinline__ void lds_read8_b(const uint16_t* p, bf16x8 (&v)[8]) {
 // k nq NT.
 constexpr int WG = 3;  // advance items per thread in flight
 __device__ __forceinline__ void worker_advance(const TreeArgs& a, const int* cslot, const int* ctok, const int* csrc,
-                                               int nc, int q, int nq, bool loc, floatx4 (&dv)[WG],
+                                               int nc, int q, int nq, floatx4 (&dv)[WG],
                                                float* (&dp)[WG]) {
   const int ds = a.ds, n4 = ds >> 2;
   const int items = nc * n4;
@@ -850,10 +845,7 @@ __device__ __forceinline__ void worker_advance(const TreeArgs& a, const int* csl
         uint16_t* ap = reinterpret_cast<uint16_t*>(a.act) + (size_t)sl[g] * act_stride(ds) + qv[g];
         const uint32_t lo = (uint32_t)f32_to_bf16(o[0]) | ((uint32_t)f32_to_bf16(o[1]) << 16);
         const uint32_t hi = (uint32_t)f32_to_bf16(o[2]) | ((uint32_t)f32_to_bf16(o[3]) << 16);
-        if (loc)
-          st_l2_u32x2(ap, lo, hi);
-        else
-          st_dev_u32x2(ap, lo, hi);
+        st_dev_u32x2(ap, lo, hi);  // device-wide even within one XCD: measured faster than into the L2
       }
     }
   }
@@ -927,7 +919,7 @@ __device__ __forceinline__ void worker_regs(const TreeArgs& a, unsigned char* ld
       if (a.wadv && t > 0) {
         // the group advances the states of its columns, then waits for all of it
         const bool loc = xmode == 1;
-        worker_advance(a, coln + 64, coln + 128, coln + 192, nval, gq, ngq, loc, sv, sp);
+        worker_advance(a, coln + 64, coln + 128, coln + 192, nval, gq, ngq, sv, sp);
         stores_done();
         __syncthreads();
         if (tid == 0) {

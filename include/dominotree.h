@@ -227,10 +227,10 @@ typedef struct {
   int32_t dl;               /* the correction dL = W2[:, candidates]^T a of each expansion: 0 (default)
                                on the matrix cores where the weights are bf16 and r is a multiple of
                                32, else with vector FMAs; 1: always with vector FMAs */
-  int32_t exchange;         /* register-resident workers pass a step's advanced states to the other
-                               blocks of their column group: 0 (default) through the L2 of their XCD
-                               when the launch's first exchange finds the whole group on one XCD,
-                               else device-wide; 1: always device-wide */
+  int32_t exchange;         /* register-resident workers tell the other blocks of their column group
+                               that a step's advanced states are stored: 0 (default) with flags kept
+                               in the L2 of their XCD when the launch's first exchange finds the whole
+                               group on one XCD, else device-wide; 1: always device-wide */
 } dt_schedule;
 
 /* Set the schedule the handle's next builds use (NULL restores the defaults).
