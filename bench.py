@@ -417,11 +417,11 @@ def main():
         return a0.elapsed_time(a1) / args.steps
 
     # ablations on the same builds (event time per round): the factorised
-    # tree (DT_MARGINAL: base logits alone, no per-node products), a plain
-    # instead of a cooperative launch, the correction dL with vector FMAs,
+    # tree (DT_MARGINAL: base logits alone, no per-node products), a
+    # cooperative instead of a plain launch, the correction dL with vector FMAs,
     # the workers' group exchange device-wide instead of through their XCD's L2
     ablations = {"marginal_round_ms": timed_rounds(pkg.DT_MARGINAL)}
-    for key, sched in (("plain_launch_round_ms", dict(launch=1)), ("fma_dl_round_ms", dict(dl=1)),
+    for key, sched in (("cooperative_launch_round_ms", dict(launch=2)), ("fma_dl_round_ms", dict(dl=1)),
                        ("device_exchange_round_ms", dict(exchange=1))):
         tb.set_schedule(**sched)
         ablations[key] = timed_rounds()

@@ -539,7 +539,7 @@ dt_status dt_build_trees(dt_handle* h, const dt_inputs* in, const dt_params* p, 
   a.ebase = h->ebase;
   h->ebase += span;
   MARK(4);
-  HIPCHK(dt::launch_tree(a, h->bf16, lds, stream, h->sched.launch == 1));
+  HIPCHK(dt::launch_tree(a, h->bf16, lds, stream, h->sched.launch != 2));
   MARK(5);
   if (timing) ++h->timed;
 #undef MARK
@@ -599,7 +599,7 @@ dt_status dt_set_schedule(dt_handle* h, const dt_schedule* s) {
     return fail(DT_EINVAL, "tiles_per_worker %d outside 0..64", s->tiles_per_worker);
   if (s->advance < 0 || s->advance > 2) return fail(DT_EINVAL, "advance %d outside 0..2", s->advance);
   if (s->dl != 0 && s->dl != 1) return fail(DT_EINVAL, "dl must be 0 or 1");
-  if (s->launch < 0 || s->launch > 1) return fail(DT_EINVAL, "launch %d outside 0..1", s->launch);
+  if (s->launch < 0 || s->launch > 2) return fail(DT_EINVAL, "launch %d outside 0..2", s->launch);
   if (s->exchange < 0 || s->exchange > 1) return fail(DT_EINVAL, "exchange %d outside 0..1", s->exchange);
   h->sched = *s;
   return DT_OK;

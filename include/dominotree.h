@@ -219,11 +219,13 @@ typedef struct {
   int32_t advance;          /* who advances the GRU states of a step's nodes beside register-resident
                                workers: 0 (default) or 1 the workers, 2 the controllers (the
                                LDS-staging workers always leave it to the controllers) */
-  int32_t launch;           /* 0 (default): a cooperative launch, which guarantees that every block of
-                               the builder is resident at once (they wait on each other); 1: a plain
-                               launch, for callers that leave the GPU to the build: if other work kept
-                               some blocks from being resident, the bounded waits end the build with
-                               DT_EDEVICE */
+  int32_t launch;           /* the builder's blocks wait on each other, so all of them must be resident
+                               at once (one per compute unit, at most as many as the GPU has).
+                               0 (default) or 1: a plain launch, which has them all resident when the
+                               build does not share the GPU with other streams' kernels; if other work
+                               keeps some blocks waiting for a compute unit long enough, the bounded
+                               waits end the build with DT_EDEVICE.  2: a cooperative launch, which
+                               guarantees it, for callers that share the GPU (it costs about 20 us) */
   int32_t dl;               /* the correction dL = W2[:, candidates]^T a of each expansion: 0 (default)
                                on the matrix cores where the weights are bf16 and r is a multiple of
                                32, else with vector FMAs; 1: always with vector FMAs */

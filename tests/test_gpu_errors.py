@@ -66,7 +66,7 @@ def test_schedule_rejects_out_of_range(dev):
     spec, w, req = synth.workload("tiny")
     tb = gu.make_builder(spec, w)
     for kw in (dict(pops=17), dict(halves=3), dict(lds_workers=2), dict(tiles_per_worker=-1),
-               dict(dl=2), dict(exchange=2)):
+               dict(dl=2), dict(exchange=2), dict(launch=3)):
         with pytest.raises(pkg.DtError) as ei:
             tb.set_schedule(**kw)
         assert ei.value.status == pkg.binding.DT_EINVAL

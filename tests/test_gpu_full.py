@@ -132,6 +132,20 @@ def test_q8b_b32_device_wide_exchange_same_trees(dev, q8b_builder):
     gu.assert_parity(reps, [0, 31])
 
 
+def test_q8b_b32_cooperative_launch_same_trees(dev, q8b_builder):
+    # the cooperative launch (schedule launch = 2) runs the same kernel as
+    # the default plain launch: the same trees bit for bit
+    spec, w, req = synth.workload("q8b_b32")
+    plain = gu.run(q8b_builder, spec, req)
+    q8b_builder.set_schedule(launch=2)
+    try:
+        coop = gu.run(q8b_builder, spec, req)
+    finally:
+        q8b_builder.set_schedule()
+    for key in ("tokens", "parents", "depths", "scores", "n_nodes"):
+        np.testing.assert_array_equal(plain[key], coop[key], err_msg=key)
+
+
 def test_q8b_b32_fullv_and_smaller_batch_reuse_handle(dev, q8b_builder):
     # the same handle serves a smaller batch and the full-vocabulary normaliser
     spec, w, req = synth.workload("q8b_b32")
