@@ -146,6 +146,32 @@ def test_q8b_b32_cooperative_launch_same_trees(dev, q8b_builder):
         np.testing.assert_array_equal(plain[key], coop[key], err_msg=key)
 
 
+def test_q8b_b32_plain_launch_beside_another_streams_work(dev, q8b_builder):
+    # the default plain launch while another stream's matrix products hold
+    # the compute units: builder blocks that wait for a unit start once the
+    # products' blocks retire, well inside the bounded waits, and the trees
+    # are those of the idle GPU
+    import torch
+
+    import conditional_draft_tree_dominotree_amd as pkg
+    spec, w, req = synth.workload("q8b_b32")
+    want = gu.run(q8b_builder, spec, req)
+    hidden, base = gu.to_dev(req["hidden"]), gu.to_dev(req["base"])
+    out = q8b_builder.outputs(spec.B, spec.M, spec.N)
+    x = torch.randn(4096, 4096, device=dev)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    with torch.cuda.stream(side):
+        for _ in range(6):
+            x = torch.tanh(x @ x * 1e-3)
+    q8b_builder.build(hidden, base, None, top_m=spec.M, top_k=spec.k, budget=spec.N, temperature=spec.T,
+                      flags=pkg.DT_ACT_BF16, out=out)
+    torch.cuda.synchronize()
+    q8b_builder.sync_status()
+    for key in ("tokens", "parents", "depths", "scores", "n_nodes"):
+        np.testing.assert_array_equal(out[key].cpu().numpy(), want[key], err_msg=key)
+
+
 def test_q8b_b32_fullv_and_smaller_batch_reuse_handle(dev, q8b_builder):
     # the same handle serves a smaller batch and the full-vocabulary normaliser
     spec, w, req = synth.workload("q8b_b32")
