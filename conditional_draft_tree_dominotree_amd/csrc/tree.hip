@@ -1,4 +1,4 @@
-// The conditional best-first tree builder: one persistent cooperative kernel.
+// The conditional best-first tree builder: one persistent kernel.
 //
 // Method (DominoTree technical summary, Componenti Core 1, 2 and 4; Domino
 // summary, 核心方法): per request, repeatedly take the frontier node with the
@@ -23,32 +23,39 @@
 //     the output is X ranked by the total order, cut after N + 1 records.
 // Speculation changes how much work is done, never the result.
 //
-// Roles (blocks of 256 threads, one per CU, launched cooperatively so that all
-// are resident):
-//   * worker blocks [0, n_workers): each keeps `tiles_per_worker` 16-row tiles
-//     of the per-node product Wc = [W_hh ; W1_S^T] ((3 d_s + r) x d_s) in LDS
-//     for the whole launch.  Each step it multiplies its rows by the GEMM
-//     operand copies of the states expanded in that step (one column per
-//     expanded node) with MFMA, and publishes gh = W_hh S~ + b_hh and
-//     u = W1_S^T S~.
+// Roles (blocks of 256 threads, one per CU, all resident at once: they wait
+// on each other, so the grid never exceeds the GPU's CUs; a plain launch by
+// default, a cooperative one on request):
+//   * worker blocks [0, n_workers) keep tiles of the per-node product
+//     Wc = [W_hh ; W1_S^T] ((3 d_s + r) x d_s) for the whole launch: at
+//     d_s = 1024 in bf16 as MFMA operands in registers ("register workers"),
+//     otherwise `tiles_per_worker` 16-row tiles in LDS.  Each step they
+//     multiply their rows by the GEMM operand copies of the states expanded in
+//     that step (one column per expanded node) and publish
+//     gh = W_hh S~ + b_hh and u = W1_S^T S~.  Register workers own fixed
+//     columns (node c % p of a request of their column group), read each
+//     column's node (token, parent slot) from a node entry its controller
+//     writes, and advance those nodes' GRU states themselves from
+//     G[token] = W_ih E[token] + b_ih (a table folded once per handle) and the
+//     parents' gh before the product.
 //   * controller blocks [n_workers, n_workers + B): one per request.  It keeps
 //     the request's candidates, node records and sorted frontier in LDS;
 //     scores the children of the nodes expanded in the step
 //     (a = SiLU(u + P_d), dL on the M candidate columns of W2, log-softmax,
-//     top-k), merges them into the frontier, takes the next nodes, and
-//     advances their GRU states elementwise from G[token] = W_ih E[token] +
-//     b_ih (a table folded once per handle) and their parents' gh.
+//     top-k), merges them into the frontier, takes the next nodes and
+//     publishes them (node entries for register workers; beside LDS workers
+//     it advances their states itself and raises mailbox words).
 //
 // Exchange between blocks: every published value is written once per launch
 // to its own 128-byte-aligned slot with device-scope (sc1) stores; after the
-// stores complete the producer raises a flag word in its consumers' mailbox
-// lines (sc1 store; the controllers' words to the workers go to eight copies
-// of one line, each polled by an eighth of the workers); a consumer polls its
-// mailbox line (sc1 loads) and then reads the published slots.  Slots are
-// never read before they are published, so no cache holds a stale copy.
-// Blocks of one worker column group that run on one XCD pass the operand
-// copies and their group flags through that XCD's L2 instead.  Every wait is
-// bounded: when it runs out the block sets the error word and leaves its loop.
+// stores complete the producer raises a word its consumers poll with sc1
+// loads (a node entry carrying the step's epoch, an acknowledgement, a group
+// flag, or a mailbox word in eight copies of one line), and the consumer then
+// reads the published slots.  Slots are never read before they are
+// published, so no cache holds a stale copy.  The blocks of a register-worker
+// column group that run on one XCD raise their group flags in that XCD's L2
+// (sc0 stores).  Every wait is bounded: when it runs out the block sets the
+// error word and leaves its loop.
 #include <algorithm>
 #include <type_traits>
 
