@@ -92,7 +92,7 @@ def tree_kernel_flops(spec, nodes: float) -> float:
     return 2.0 * nodes * (3 * spec.ds + spec.r) * spec.ds
 
 
-TREE_SOURCES = ["csrc/tree.hip", "csrc/tree.h", "csrc/common.h"]
+TREE_SOURCES = ["csrc/tree.hip", "csrc/tree.h", "csrc/common.h", "csrc/kernels.h"]
 
 
 def tree_source_hash() -> str:

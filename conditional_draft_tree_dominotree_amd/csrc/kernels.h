@@ -18,7 +18,7 @@ inline int topm_chunks(int V) { return (V + TOPM_CHUNK - 1) / TOPM_CHUNK; }
 // product P = H W1_H beside the candidate selection.
 // P = H W1_H in the candidate merge's launch is written as P_KSPLIT partials
 // [P_KSPLIT][rows, pN] (pC), which the consumer adds in order
-constexpr int P_KSPLIT = 4;
+constexpr int P_KSPLIT = 2;
 hipError_t launch_topm(const float* logits, int rows, int V, int M, float T, uint64_t* chunk_cand,
                        float4* chunk_stat, int32_t* ids, float* vals, float* lse, float* tail,
                        int32_t* tokrank, int32_t* user_ids, float* user_vals, float* user_lse,

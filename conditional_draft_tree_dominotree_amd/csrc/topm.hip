@@ -153,14 +153,18 @@ __device__ __forceinline__ void chunk_load(const float* __restrict__ src, int le
 // the candidate merge, whose latency-bound blocks leave the CUs room (in the
 // chunk kernel its registers would cut that kernel's occupancy).  K is split
 // P_KSPLIT ways over blocks: a block computes one 32 x 32 output tile over
-// its K share, its four waves splitting the share again (256 k each at
-// h = 4096), so that a wave issues the loads of its whole share at once
+// its K share, its four waves splitting the share again (512 k each at
+// h = 4096 with two shares), so that a wave issues the loads of 256 k at once
 // (16 bytes a lane, straight from memory, 16 rows x 64 bytes per load
-// instruction) and waits for memory about once: with only a 64-k step's
-// products (about 128 cycles) to cover each load, a wave walking a long K
-// share pays one memory latency per step.  The four waves' tiles are summed
-// in LDS in a fixed order and the block writes partial kz of P; the
-// consumer adds the P_KSPLIT partials in a fixed order.
+// instruction) and waits for memory about once per 256 k: with only a 64-k
+// step's products (about 128 cycles) to cover each load, a wave walking its
+// share 64 k at a time would pay one memory latency per step.  The four
+// waves' tiles are summed in LDS in a fixed order and the block writes
+// partial kz of P; the consumer adds the P_KSPLIT partials in a fixed order.
+// Two shares rather than four or eight: the tree kernel's prefetch adds
+// fewer partials, and the launch stays as short (measured by the round: one
+// share 0.325, two 0.318, four 0.320, eight 0.336 ms at the Qwen3-8B shape
+// with 32 requests).
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 
 struct PArgs {
